@@ -1,0 +1,167 @@
+"""Seeded synthetic inputs for the sparse MoE layer forward.
+
+This module only draws random numbers and stores them in the layer's input
+formats (fp32, bf16 bits, affine 4-bit codes with bf16 scales/biases).  It
+holds none of the layer's arithmetic; both the GPU tests and the CPU oracle
+consume what it returns.
+
+Recipe (the pages fix the shapes, not the draws):
+  * NumPy PCG64, one independent stream per part of the layer: x from
+    ``[seed, 0, x_index]``, the router from ``[seed, 1]``, expert e (routed
+    first, then shared) from ``[seed, 2, e]``; so a layer's weights do not
+    depend on T, and the decode layer at T=1 and T=32 shares them.
+  * Weights ~ N(0, 1/fan_in) with fan_in = the reduction length (d_model for
+    router, gate and up; d_ff for down), drawn in stored (out-major) order:
+    gate [d_ff][d_model], up [d_ff][d_model], down [d_model][d_ff].
+  * x ~ N(0, 1) except for the tiny fp32 layer, where x ~ N(0, 1/d_model).
+  * bf16 storage rounds the fp32 draw to nearest-even (torch's cast).
+  * 4-bit storage, per group of 64 consecutive reduction columns of one row:
+    lo = min, hi = max, scale = bf16((hi - lo) / 15), bias = bf16(lo),
+    q = clamp(rint((w - bias) / scale), 0, 15) (ties to even), q = 0 where
+    scale == 0.  Eight codes per uint32, code m of a word at bits [4m, 4m+4)
+    holding column 8*word + m.
+  * Skewed routing: an additive router bias of -2.2 * ln(e + 1) on expert e,
+    i.e. twice the log of a Zipf(s = 1.1) weight of rank e + 1 (the Zipf
+    normaliser cancels in the softmax).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, replace
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class LayerSpec:
+    name: str
+    T: int
+    d_model: int
+    d_ff: int
+    n_experts: int
+    top_k: int
+    n_shared: int = 0
+    act: str = "bf16"            # "f32" | "bf16"
+    wfmt: str = "dense"          # "dense" | "q4"
+    group_size: int = 64
+    gate_up_fused: bool = False
+    swiglu_round_bf16: bool = False
+    renormalize: bool = True
+    router_bias: str = "none"    # "none" | "zipf"
+    x_scale: str = "unit"        # "unit" | "fan_in"
+    seed: int = 0
+
+    @property
+    def n_routed_rows(self) -> int:
+        return self.T * self.top_k
+
+    def with_(self, **kw) -> "LayerSpec":
+        return replace(self, **kw)
+
+
+# The five workloads: shapes, formats and seeds.
+CONFIGS = {
+    "tiny-f32": LayerSpec("tiny-f32", T=16, d_model=64, d_ff=128, n_experts=8, top_k=2,
+                          act="f32", wfmt="dense", x_scale="fan_in", seed=1),
+    "dense-bf16-t512": LayerSpec("dense-bf16-t512", T=512, d_model=2048, d_ff=5632, n_experts=8,
+                                 top_k=2, act="bf16", wfmt="dense", seed=2),
+    "q4-decode-t1": LayerSpec("q4-decode-t1", T=1, d_model=2048, d_ff=768, n_experts=128, top_k=8,
+                              wfmt="q4", seed=3),
+    "q4-decode-t32": LayerSpec("q4-decode-t32", T=32, d_model=2048, d_ff=768, n_experts=128,
+                               top_k=8, wfmt="q4", seed=3),
+    "q4-prefill-t2048": LayerSpec("q4-prefill-t2048", T=2048, d_model=2048, d_ff=512, n_experts=512,
+                                  top_k=10, wfmt="q4", gate_up_fused=True, swiglu_round_bf16=True,
+                                  seed=4),
+    "q4-skewed-t256": LayerSpec("q4-skewed-t256", T=256, d_model=2048, d_ff=1408, n_experts=64,
+                                top_k=6, n_shared=2, wfmt="q4", router_bias="zipf", seed=5),
+}
+
+
+def _rng(*key) -> np.random.Generator:
+    return np.random.default_rng(list(key))
+
+
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even, via torch."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def quantize_q4(w: np.ndarray, group: int = 64):
+    """Encode fp32 rows [N][K] as (uint32 [N][K/8], scales bf16 [N][K/g], biases bf16 [N][K/g])."""
+    N, K = w.shape
+    assert K % group == 0 and group % 8 == 0
+    wg = w.reshape(N, K // group, group).astype(np.float32)
+    lo = wg.min(axis=-1)
+    hi = wg.max(axis=-1)
+    s_bits = to_bf16_bits((hi - lo) / np.float32(15.0))
+    b_bits = to_bf16_bits(lo)
+    s = bf16_bits_to_f32(s_bits)[..., None]
+    b = bf16_bits_to_f32(b_bits)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.rint((wg - b) / s)
+    q = np.where(s == 0, 0.0, np.clip(q, 0, 15)).astype(np.uint32).reshape(N, K // 8, 8)
+    shifts = (np.arange(8, dtype=np.uint32) * 4)[None, None, :]
+    words = np.bitwise_or.reduce(q << shifts, axis=-1).astype(np.uint32)
+    return words, s_bits, b_bits
+
+
+def gen_x(spec: LayerSpec, x_index: int = 0, T: int | None = None) -> np.ndarray:
+    T = spec.T if T is None else T
+    std = 1.0 / math.sqrt(spec.d_model) if spec.x_scale == "fan_in" else 1.0
+    x = _rng(spec.seed, 0, x_index).standard_normal((T, spec.d_model), dtype=np.float32) * np.float32(std)
+    return x if spec.act == "f32" else to_bf16_bits(x)
+
+
+def gen_router(spec: LayerSpec):
+    w = _rng(spec.seed, 1).standard_normal((spec.d_model, spec.n_experts), dtype=np.float32)
+    w *= np.float32(1.0 / math.sqrt(spec.d_model))
+    w = w if spec.act == "f32" else to_bf16_bits(w)
+    bias = None
+    if spec.router_bias == "zipf":
+        bias = (-2.2 * np.log(np.arange(1, spec.n_experts + 1, dtype=np.float64))).astype(np.float32)
+    return w, bias
+
+
+def _store(spec: LayerSpec, w: np.ndarray):
+    if spec.wfmt == "q4":
+        q, s, b = quantize_q4(w, spec.group_size)
+        return {"w": q, "scales": s, "biases": b}
+    return {"w": w if spec.act == "f32" else to_bf16_bits(w)}
+
+
+def gen_expert(spec: LayerSpec, e: int) -> dict:
+    """Expert e (routed experts first, then shared) in stored form."""
+    r = _rng(spec.seed, 2, e)
+    D, F = spec.d_model, spec.d_ff
+    gate = r.standard_normal((F, D), dtype=np.float32) * np.float32(1.0 / math.sqrt(D))
+    up = r.standard_normal((F, D), dtype=np.float32) * np.float32(1.0 / math.sqrt(D))
+    down = r.standard_normal((D, F), dtype=np.float32) * np.float32(1.0 / math.sqrt(F))
+    out = {"down": _store(spec, down)}
+    if spec.gate_up_fused:
+        out["gate_up"] = _store(spec, np.concatenate([gate, up], axis=0))
+    else:
+        out["gate"] = _store(spec, gate)
+        out["up"] = _store(spec, up)
+    return out
+
+
+def gen_experts(spec: LayerSpec) -> dict:
+    """All experts (routed, then shared) stacked along a leading axis."""
+    n_all = spec.n_experts + spec.n_shared
+    parts = [gen_expert(spec, e) for e in range(n_all)]
+    out = {}
+    for proj in parts[0]:
+        out[proj] = {k: np.stack([p[proj][k] for p in parts]) for k in parts[0][proj]}
+    return out
+
+
+def gen_layer(spec: LayerSpec, x_index: int = 0, T: int | None = None) -> dict:
+    w_router, bias = gen_router(spec)
+    return {"spec": spec, "x": gen_x(spec, x_index, T), "w_router": w_router,
+            "router_bias": bias, "experts": gen_experts(spec)}

@@ -1,0 +1,95 @@
+"""NumPy fp64 brute force for small MoE layers (test helper).
+
+An independent restatement of the layer from its definition, used to pin the
+CPU oracle: every quantity is computed densely in float64 with NumPy's own
+matmul, so it shares no arithmetic path with the oracle's fp32 C loops.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from sparse_mixture_experts_amd.inputs import LayerSpec
+
+
+def bits_to_f64(h: np.ndarray) -> np.ndarray:
+    return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def widen(spec: LayerSpec, a: np.ndarray) -> np.ndarray:
+    return bits_to_f64(a) if spec.act == "bf16" else np.asarray(a, np.float32).astype(np.float64)
+
+
+def unpack_codes(words: np.ndarray) -> np.ndarray:
+    """uint32 [..., K/8] -> codes [..., K] (column 8*w + m is bits [4m, 4m+4) of word w)."""
+    sh = (np.arange(8, dtype=np.uint32) * 4)
+    codes = (words[..., None] >> sh) & np.uint32(0xF)
+    return codes.reshape(*words.shape[:-1], words.shape[-1] * 8)
+
+
+def dequant64(spec: LayerSpec, proj: dict) -> np.ndarray:
+    if spec.wfmt != "q4":
+        return widen(spec, proj["w"])
+    q = unpack_codes(proj["w"]).astype(np.float64)
+    g = spec.group_size
+    s = np.repeat(bits_to_f64(proj["scales"]), g, axis=-1)
+    b = np.repeat(bits_to_f64(proj["biases"]), g, axis=-1)
+    return s * q + b
+
+
+def weights64(spec: LayerSpec, experts: dict):
+    """(gate, up, down) as float64 [n_all][F][D], [n_all][F][D], [n_all][D][F]."""
+    F = spec.d_ff
+    if spec.gate_up_fused:
+        gu = dequant64(spec, experts["gate_up"])
+        gate, up = gu[:, :F, :], gu[:, F:, :]
+    else:
+        gate, up = dequant64(spec, experts["gate"]), dequant64(spec, experts["up"])
+    return gate, up, dequant64(spec, experts["down"])
+
+
+def bf16_round64(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 (ties to even), via float32 first."""
+    import torch
+    return torch.from_numpy(np.asarray(v, np.float64).astype(np.float32)).to(torch.bfloat16).to(
+        torch.float64).numpy()
+
+
+def expert_outputs64(spec: LayerSpec, x64: np.ndarray, W) -> np.ndarray:
+    """Every expert applied to every token: [T][n_all][D] float64."""
+    gate, up, down = W
+    g = np.einsum("td,efd->tef", x64, gate)
+    u = np.einsum("td,efd->tef", x64, up)
+    if spec.swiglu_round_bf16:
+        g, u = bf16_round64(g), bf16_round64(u)
+        s = bf16_round64(1.0 / (1.0 + np.exp(-g)))
+        a = bf16_round64(g * s)
+        h = bf16_round64(a * u)
+    else:
+        h = g / (1.0 + np.exp(-g)) * u
+    return np.einsum("tef,edf->ted", h, down)
+
+
+def logits64(spec: LayerSpec, x64: np.ndarray, wr64: np.ndarray, bias) -> np.ndarray:
+    l = x64 @ wr64
+    if bias is not None:
+        l = l + np.asarray(bias, np.float64)[None, :]
+    return l
+
+
+def softmax64(l: np.ndarray) -> np.ndarray:
+    m = l.max(axis=-1, keepdims=True)
+    e = np.exp(l - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def layer_dense_masked64(spec: LayerSpec, layer: dict, topk_idx: np.ndarray, topk_w: np.ndarray):
+    """Dense all-experts output, masked to the given top-k and weighted, plus shared experts."""
+    x64 = widen(spec, layer["x"])
+    O = expert_outputs64(spec, x64, weights64(spec, layer["experts"]))
+    T, E = x64.shape[0], spec.n_experts
+    mask = np.zeros((T, E), np.float64)
+    np.put_along_axis(mask, topk_idx.astype(np.int64), topk_w.astype(np.float64), axis=1)
+    y = np.einsum("te,ted->td", mask, O[:, :E, :])
+    if spec.n_shared:
+        y = y + O[:, E:, :].sum(axis=1)
+    return y

@@ -1,0 +1,62 @@
+"""Seeded generator: determinism, formats, and the load profile of the skewed layer."""
+import numpy as np
+
+import oracle
+import pins
+from sparse_mixture_experts_amd import inputs
+
+
+def test_deterministic_and_independent_streams():
+    spec = pins.SMALL["q4-fused-round"]
+    a, b = inputs.gen_layer(spec), inputs.gen_layer(spec)
+    assert np.array_equal(a["x"], b["x"]) and np.array_equal(a["w_router"], b["w_router"])
+    for p in a["experts"]:
+        for k in a["experts"][p]:
+            assert np.array_equal(a["experts"][p][k], b["experts"][p][k])
+    # weights do not depend on T; x rows are a prefix of a longer draw
+    c = inputs.gen_layer(spec.with_(T=3))
+    assert np.array_equal(c["experts"]["down"]["w"], a["experts"]["down"]["w"])
+    assert np.array_equal(c["x"], a["x"][:3])
+    assert not np.array_equal(inputs.gen_x(spec, 1), a["x"])
+
+
+def test_formats_and_shapes():
+    for name, spec in pins.SMALL.items():
+        L = inputs.gen_layer(spec)
+        n_all = spec.n_experts + spec.n_shared
+        assert L["x"].shape == (spec.T, spec.d_model)
+        assert L["x"].dtype == (np.float32 if spec.act == "f32" else np.uint16)
+        assert L["w_router"].shape == (spec.d_model, spec.n_experts)
+        ex = L["experts"]
+        if spec.wfmt == "q4":
+            assert ex["down"]["w"].shape == (n_all, spec.d_model, spec.d_ff // 8)
+            assert ex["down"]["w"].dtype == np.uint32
+            assert ex["down"]["scales"].shape == (n_all, spec.d_model, spec.d_ff // 64)
+        if spec.gate_up_fused:
+            assert ex["gate_up"]["w"].shape[1] == 2 * spec.d_ff and "gate" not in ex
+
+
+def test_quantizer_codes_and_bf16_cast():
+    rng = np.random.default_rng(1)
+    w = rng.standard_normal((4, 128)).astype(np.float32)
+    w[1, :64] = 0.5  # a constant group: scale 0, every code 0
+    q, s, b = inputs.quantize_q4(w)
+    codes = ((q[..., None] >> (np.arange(8, dtype=np.uint32) * 4)) & 15).reshape(4, 128)
+    assert codes.max() <= 15
+    assert s[1, 0] == 0 and np.all(codes[1, :64] == 0)
+    assert inputs.bf16_bits_to_f32(b[1, :1])[0] == 0.5
+    # columns of min and max in each group get codes 0 and 15 (or within one of it after bf16 rounding)
+    g = w[0, :64]
+    assert codes[0, np.argmin(g)] <= 1 and codes[0, np.argmax(g)] >= 14
+
+
+def test_skewed_layer_load_profile():
+    """A few experts get more than 64 rows, most get 0-2 (the skewed-load layer)."""
+    spec = inputs.CONFIGS["q4-skewed-t256"]
+    x = inputs.gen_x(spec)
+    w, bias = inputs.gen_router(spec)
+    idx, _ = oracle.route(pins.desc_of(spec), x, w, bias)
+    cnt = np.bincount(idx.reshape(-1), minlength=spec.n_experts)
+    assert 3 <= (cnt > 64).sum() <= 16
+    assert (cnt <= 2).sum() >= 32
+    assert cnt.sum() == spec.T * spec.top_k

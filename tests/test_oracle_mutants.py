@@ -1,0 +1,62 @@
+"""Planted mistakes in the oracle must fail at least one pin.
+
+Each mutant is a one-line edit of a copy of oracle/moe_oracle.c (a dropped
+term, a wrong sign, index or operand), compiled on the CPU into a temporary
+library; the pins of tests/pins.py then run against it and at least one must
+fail.  This shows that the pins would catch such a mistake in the oracle.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "moe_oracle.c")
+
+MUTANTS = {
+    "tie_break_flipped": ("  return a < b;\n}", "  return a > b;\n}"),
+    "router_bias_dropped": ("if (router_bias) acc = acc + router_bias[e];", "(void)router_bias;"),
+    "router_chunk_dropped": ("        acc = acc + p;", "        acc = p;"),
+    "renormalise_skipped": ("if (d->renormalize)\n", "if (0)\n"),
+    "softmax_wrong_index": ("w[j] = expf(l[idx[j]] - m) / z;", "w[j] = expf(l[j] - m) / z;"),
+    "nibble_order_reversed": ("(4 * (k % 8))", "(4 * (7 - k % 8))"),
+    "scale_bias_swapped": ("out[k] = s * (float)q + b;", "out[k] = b * (float)q + s;"),
+    "group_index_wrong": ("float s = oracle_bf16_to_f32(sc[k / G]);", "float s = oracle_bf16_to_f32(sc[0]);"),
+    "fused_up_reads_gate": ("oracle_dequant_row(d, &w->gate_up, e, F + n, 2 * F, D, row);",
+                            "oracle_dequant_row(d, &w->gate_up, e, n, 2 * F, D, row);"),
+    "separate_gate_reads_up": ("oracle_dequant_row(d, &w->gate, e, n, F, D, row);",
+                               "oracle_dequant_row(d, &w->up, e, n, F, D, row);"),
+    "silu_sign": ("static float silu(float g) { return g / (1.0f + expf(-g)); }",
+                  "static float silu(float g) { return g / (1.0f + expf(g)); }"),
+    "sigmoid_not_rounded": ("float s = round_bf16(sigmoid(g));", "float s = sigmoid(g);"),
+    "dispatch_unstable": ("return i < j ? -1 : (i > j);", "return i < j ? 1 : -(i > j);"),
+    "row_map_modulo": ("row_map[p] = order[p] / top_k;", "row_map[p] = order[p] % top_k;"),
+    "tile_off_floor": ("(cnt + tile_rows - 1) / tile_rows", "cnt / tile_rows"),
+    "shared_dropped": ("for (int32_t s = 0; s < d->n_shared; ++s) {", "for (int32_t s = 0; s < 0; ++s) {"),
+    "slot_weight_wrong": ("yr[m] = yr[m] + wt[j] * o[m];", "yr[m] = yr[m] + wt[0] * o[m];"),
+    "bf16_ties_away": ("u += 0x7fffu + lsb;", "u += 0x7fffu + 1u;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    mpath = tmp_path / "moe_oracle.c"
+    mpath.write_text(src.replace(old, new))
+    (tmp_path / "moe_oracle.h").write_text(open(SRC[:-2] + ".h").read())
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                    "-o", str(lib), str(mpath), "-lm"], check=True)
+    failed = []
+    with oracle.use_library(str(lib)):
+        for pname, fn, args in pins.ALL_PINS:
+            try:
+                fn(*args)
+            except AssertionError:
+                failed.append(pname)
+                break
+    assert failed, f"mutant {name} passed every pin"
