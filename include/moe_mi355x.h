@@ -1,0 +1,189 @@
+/*
+ * moe_mi355x.h -- C ABI of the sparse Mixture-of-Experts layer forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (per token t with row x[t] of length d_model):
+ *   1. route:    logits = x[t] . W_router (+ router_bias), softmax, top-k
+ *                experts with their weights, renormalised to sum to one;
+ *   2. dispatch: the T*k routed (token, slot) rows grouped by expert;
+ *   3. experts:  for each routed row, h = silu(x . Wg_e) * (x . Wu_e) and
+ *                y_e = h . Wd_e (SwiGLU expert FFN);
+ *   4. combine:  y[t] = sum_j w[t][j] * y_{e_j}(x[t]) + sum_s shared_s(x[t]).
+ * This is the layer of "perf(moe): fused MoE expert decode kernel" (lablup/
+ * mlxcel #275, section "What it does": out = sum_k score_k * down_k(silu(
+ * gate_k(x)) * up_k(x))), with the routing kernel contract of the PRD "5.5
+ * real sparse MoE kernels (Metal)" (section "Scope - in": routing_logits ->
+ * (top_k_indices, top_k_weights) with no host round trip; expert dispatch
+ * (tokens, expert_indices) -> grouped tokens; scatter-add combine) and the
+ * sorted-row route of DS4Server issue #112 (section "Current upstream
+ * route": sort_rows -> order, inv_order, row_map; gate/up SwiGLU reading
+ * rows in place through row_map; down on the sorted rows; unsort through
+ * inv_order).
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named as tensors are DEVICE pointers owned by the caller, 16-byte
+ *    aligned, to densely packed row-major arrays.  Descriptor/weight-table
+ *    structs and `bytes` out-parameters are HOST pointers.
+ *  - Each call validates everything on the host first; on any error it returns
+ *    a negative moe_status, enqueues nothing and leaves every output untouched.
+ *  - On success the work is only ENQUEUED on `stream` (a hipStream_t, NULL =
+ *    the default stream).  No call synchronises the host or copies device data
+ *    to the host; buffers must stay alive until the stream work completes.
+ *  - T == 0 is valid and enqueues nothing.
+ *  - The library allocates no device memory: scratch space comes from the
+ *    caller's workspace (`ws`, `ws_bytes`, sized by moe_workspace_size).
+ *  - Results are deterministic: no floating-point atomics anywhere, so two
+ *    identical calls give bitwise identical outputs.
+ *  - Calls that share a workspace must not run concurrently.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_E_INVALID = -1,     /* bad descriptor, size, pointer or alignment */
+  MOE_E_UNSUPPORTED = -2, /* a valid but unimplemented format (bits, group) */
+  MOE_E_WORKSPACE = -3,   /* ws_bytes below moe_workspace_size() */
+  MOE_E_HIP = -4          /* the HIP runtime reported a launch error */
+} moe_status;
+
+typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
+typedef enum { MOE_WF_DENSE = 0, MOE_WF_AFFINE_Q4 = 1 } moe_wformat;
+
+/*
+ * Layer shape and format.
+ *  d_model, d_ff  > 0; multiples of 64 when w_format is MOE_WF_AFFINE_Q4
+ *                 (the q4 group runs along both reduction dims), multiples of
+ *                 8 otherwise.
+ *  n_experts      routed experts E, 1..1024.
+ *  top_k          1..min(32, n_experts).
+ *  n_shared       always-on shared experts (weight 1.0, not renormalised), 0..8;
+ *                 their weights follow the E routed experts in every projection.
+ *  act_dtype      moe_dtype of x, W_router and dense expert weights.
+ *  w_format       moe_wformat of the expert weights.  MOE_WF_AFFINE_Q4 needs
+ *                 act_dtype == MOE_DT_BF16.
+ *  group_size     q4 group length along the reduction dim; only 64.
+ *  gate_up_fused  1: one [2*d_ff][d_model] matrix per expert whose rows are
+ *                 [gate | up]; 0: separate gate and up matrices.
+ *  swiglu_round_bf16  1: round gate and up to bf16, then sigmoid, g*s and
+ *                 (g*s)*u each rounded to bf16 (DS4Server #112, "Kernel
+ *                 contract", SwiGLU epilogue); needs act_dtype == BF16.
+ *  renormalize    1: the k selected weights are divided by their sum.
+ */
+typedef struct {
+  int32_t d_model, d_ff, n_experts, top_k, n_shared;
+  int32_t act_dtype, w_format, group_size;
+  int32_t gate_up_fused, swiglu_round_bf16, renormalize;
+} moe_layer_desc;
+
+/*
+ * One projection for all experts (routed 0..E-1, then shared E..E+S-1), out-
+ * major (the reduction dim contiguous):
+ *  dense: w = act_dtype [E+S][N][K]; scales = biases = NULL.
+ *  q4:    w = uint32 [E+S][N][K/8], column k of row n is bits [4*(k%8), +4)
+ *         of word k/8 (an unsigned code q in 0..15); scales, biases = bf16
+ *         [E+S][N][K/64]; the weight is scale*q + bias of its group ("affine"
+ *         4-bit, group 64, with bf16 scales and biases: "SwitchGLU: grouped-
+ *         expert Metal kernels" (ml-explore/mlx-lm #2044), "When it applies").
+ * gate, up: N = d_ff, K = d_model; gate_up: N = 2*d_ff, K = d_model;
+ * down: N = d_model, K = d_ff.
+ */
+typedef struct {
+  const void *w;
+  const void *scales;
+  const void *biases;
+} moe_proj;
+
+typedef struct {
+  const void *w_router;      /* [d_model][n_experts], act_dtype */
+  const float *router_bias;  /* [n_experts] fp32 added to the logits, or NULL */
+  moe_proj gate, up;         /* used when gate_up_fused == 0 */
+  moe_proj gate_up;          /* used when gate_up_fused == 1 */
+  moe_proj down;
+} moe_weights;
+
+/* Bytes of workspace that moe_dispatch, moe_expert_ffn and moe_forward need
+ * for this layer at T tokens (also valid for any smaller T).  Returns
+ * MOE_E_INVALID for a bad descriptor or T < 0. */
+int moe_workspace_size(const moe_layer_desc *desc, int32_t T, size_t *bytes);
+
+/*
+ * Router (step 1): topk_idx[T][k] int32 and topk_w[T][k] fp32 from x[T][d_model]
+ * and w_router[d_model][E] (+ router_bias[E] or NULL).  Logits use a fixed
+ * fp32 order: per (t, e), chunks of 64 consecutive columns, each chunk a
+ * sequential fma chain from +0, chunk sums added in ascending order from +0,
+ * bias added last.  Slot j holds the j-th largest logit (ties to the lower
+ * expert index); the weights are the fp32 softmax over all E logits, divided
+ * by their sum over the k slots when renormalize is set.  Needs no workspace.
+ */
+int moe_route(const moe_layer_desc *desc, int32_t T, const void *x,
+              const void *w_router, const float *router_bias,
+              int32_t *topk_idx, float *topk_w, void *stream);
+
+/*
+ * Dispatch (step 2, DS4Server #112 "Current upstream route", sort_rows, and
+ * "Kernel contract", per-expert tile/row prefix tables): for the N = T*k flat
+ * slots i = t*k + j with expert f[i] = topk_idx[i]:
+ *   order[N]      stable argsort of f (equal experts keep ascending i);
+ *   inv_order[N]  inverse permutation, inv_order[order[p]] = p;
+ *   row_map[N]    order[p] / k, the token whose row sorted position p reads;
+ *   expert_off[E+1]  first sorted position of each expert, expert_off[E] = N;
+ *   tile_off[E+1] prefix sum of ceil(count_e / tile_rows), tile_rows >= 1.
+ * All int32.  Every topk_idx entry must lie in [0, E); the kernel checks it
+ * and an out-of-range entry yields order = inv_order = row_map = -1 and
+ * expert_off[E] = -1 rather than an out-of-bounds write.
+ */
+int moe_dispatch(const moe_layer_desc *desc, int32_t T, const int32_t *topk_idx,
+                 int32_t tile_rows, int32_t *order, int32_t *inv_order,
+                 int32_t *row_map, int32_t *expert_off, int32_t *tile_off,
+                 void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Grouped expert FFN (step 3): for sorted routed row p < N (expert e with
+ * expert_off[e] <= p < expert_off[e+1], token row_map[p]) and shared row
+ * p = N + s*T + t (shared expert s, token t):
+ *   y_sorted[p][:] = down_e( SwiGLU( gate_e . x[token], up_e . x[token] ) ),
+ * fp32, y_sorted [N + n_shared*T][d_model].  row_map and expert_off are as
+ * moe_dispatch writes them.
+ */
+int moe_expert_ffn(const moe_layer_desc *desc, int32_t T, const void *x,
+                   const int32_t *row_map, const int32_t *expert_off,
+                   const moe_weights *w, float *y_sorted, void *ws,
+                   size_t ws_bytes, void *stream);
+
+/*
+ * Combine (step 4, DS4Server #112 "_scatter_unsort" through inv_order):
+ *   y[t][:] = sum_{j<k} topk_w[t][j] * y_sorted[inv_order[t*k+j]][:]
+ *             + sum_{s<n_shared} y_sorted[N + s*T + t][:],
+ * accumulated in fp32 in that order, then stored as out_dtype (moe_dtype;
+ * bf16 rounds to nearest even once).
+ */
+int moe_combine(const moe_layer_desc *desc, int32_t T, const float *y_sorted,
+                const int32_t *inv_order, const float *topk_w, void *y,
+                int32_t out_dtype, void *stream);
+
+/*
+ * The whole layer (steps 1-4) in one call, all on `stream`.  y[T][d_model] in
+ * out_dtype.  topk_idx_out[T][k] / topk_w_out[T][k] receive the routing when
+ * non-NULL.  Routing and dispatch results equal those of moe_route and
+ * moe_dispatch bit for bit.
+ */
+int moe_forward(const moe_layer_desc *desc, int32_t T, const void *x,
+                const moe_weights *w, void *y, int32_t out_dtype,
+                int32_t *topk_idx_out, float *topk_w_out, void *ws,
+                size_t ws_bytes, void *stream);
+
+/* A static, human-readable name of a moe_status value. */
+const char *moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,61 @@
+// device_common.h -- small device helpers for the gfx950 kernels: bf16
+// conversions, 4-bit unpacking and wave64 reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
+// The two bf16 values packed in a 32-bit word (element 0 in the low half).
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float round_bf16(float f) { return bf16_bits_to_f32(f32_to_bf16_bits(f)); }
+
+// Activation element i as fp32 (BF16: array of bf16 bits).
+template <bool BF16>
+__device__ __forceinline__ float load_act(const void *p, int64_t i) {
+  if constexpr (BF16) return bf16_bits_to_f32(static_cast<const uint16_t *>(p)[i]);
+  else return static_cast<const float *>(p)[i];
+}
+
+// Eight 4-bit codes of a word, as fp32 (code m -> out[m]).
+__device__ __forceinline__ void unpack_q4(uint32_t w, float out[8]) {
+#pragma unroll
+  for (int m = 0; m < 8; ++m) out[m] = float((w >> (4 * m)) & 0xfu);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+__device__ __forceinline__ float sigmoid_f32(float g) { return 1.0f / (1.0f + expf(-g)); }
+
+// SwiGLU of one (gate, up) pair.  With per-op rounding: gate and up rounded to
+// bf16, then sigmoid, g*s and (g*s)*u each rounded to bf16.
+__device__ __forceinline__ float swiglu(float g, float u, bool round_ops) {
+  if (!round_ops) return silu_f32(g) * u;
+  g = round_bf16(g);
+  u = round_bf16(u);
+  float s = round_bf16(sigmoid_f32(g));
+  float a = round_bf16(g * s);
+  return round_bf16(a * u);
+}
+
+}  // namespace moe

@@ -1,0 +1,237 @@
+// dispatch.hip -- groups the T*k routed rows by expert.
+//
+// DS4Server issue #112 ("Current upstream route", sort_rows): order is the
+// argsort of the flattened expert ids, inv_order its inverse, row_map =
+// order / k, and x is read in place through row_map instead of being copied;
+// "Kernel contract": per-expert row and tile prefix tables.  The PRD "5.5 real
+// sparse MoE kernels (Metal)" names this step ("Expert-dispatch ... the hard
+// part").
+//
+// A counting sort, stable and deterministic, in one workgroup:
+//   1. each wave owns a contiguous segment of slots and counts its experts
+//      with integer LDS atomics (order-independent);
+//   2. block scans give expert offsets, and every (wave, expert) pair gets the
+//      first position of its run: expert offset + counts of earlier waves;
+//   3. each wave walks its segment in slot order, 64 slots at a time; lanes
+//      that carry the same expert find each other with ballots over the bits
+//      of the expert id, so a slot's rank = base + number of earlier equal
+//      lanes, which is exactly the stable order.
+// The same kernel emits the work plan the expert kernels consume: the list of
+// experts with rows (plus the shared experts) and the list of row tiles.
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 512;
+
+// In-place exclusive scan of a[0..n) (LDS); returns the total to every thread.
+__device__ int block_exscan(int32_t *a, int n, int32_t *wave_tot) {
+  const int tid = threadIdx.x, nth = blockDim.x, lane = tid & 63, w = tid >> 6;
+  const int nw = nth / 64;
+  const int chunk = (n + nth - 1) / nth;
+  const int b = min(n, tid * chunk), e = min(n, b + chunk);
+  int s = 0;
+  for (int i = b; i < e; ++i) s += a[i];
+  int v = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) wave_tot[w] = v;
+  __syncthreads();
+  if (w == 0) {
+    const int wt = lane < nw ? wave_tot[lane] : 0;
+    int iv = wt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(iv, o, 64);
+      if (lane >= o) iv += u;
+    }
+    if (lane < nw) wave_tot[lane] = iv - wt;
+    if (lane == nw - 1) wave_tot[nw] = iv;
+  }
+  __syncthreads();
+  int run = wave_tot[w] + v - s;
+  for (int i = b; i < e; ++i) {
+    const int t = a[i];
+    a[i] = run;
+    run += t;
+  }
+  const int total = wave_tot[nw];
+  __syncthreads();
+  return total;
+}
+
+// Work plan from per-expert offsets/counts held in LDS.  act_flag and
+// tile_cnt are LDS scratch of length E.
+__device__ void emit_plan(const int32_t *off, const int32_t *cnt, int32_t *act_flag,
+                          int32_t *tile_cnt, int32_t *wave_tot, int E, int S, int N, int T,
+                          int32_t *counters, PlanItem *act_items, PlanItem *tiles) {
+  const int tid = threadIdx.x, nth = blockDim.x;
+  for (int e = tid; e < E; e += nth) {
+    act_flag[e] = cnt[e] > 0;
+    tile_cnt[e] = (cnt[e] + kTileRows - 1) / kTileRows;
+  }
+  __syncthreads();
+  const int n_act = block_exscan(act_flag, E, wave_tot);
+  const int n_tiles = block_exscan(tile_cnt, E, wave_tot);
+  for (int e = tid; e < E; e += nth) {
+    const int c = cnt[e];
+    if (c > 0) act_items[act_flag[e]] = PlanItem{e, off[e], c, 0};
+    for (int j = 0; j * kTileRows < c; ++j)
+      tiles[tile_cnt[e] + j] = PlanItem{e, off[e] + j * kTileRows, min(kTileRows, c - j * kTileRows), 0};
+  }
+  const int shared_tiles = (T + kTileRows - 1) / kTileRows;
+  for (int q = tid; q < S * shared_tiles; q += nth) {
+    const int s = q / shared_tiles, j = q % shared_tiles;
+    tiles[n_tiles + q] = PlanItem{E + s, N + s * T + j * kTileRows, min(kTileRows, T - j * kTileRows), 0};
+  }
+  for (int s = tid; s < S; s += nth) act_items[n_act + s] = PlanItem{E + s, N + s * T, T, 0};
+  if (tid == 0) {
+    counters[0] = n_act + S;
+    counters[1] = n_tiles + S * shared_tiles;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void dispatch_kernel(
+    const int32_t *__restrict__ f, int N, int K, int E, int S, int T, int tile_rows,
+    int32_t *__restrict__ order, int32_t *__restrict__ inv_order, int32_t *__restrict__ row_map,
+    int32_t *__restrict__ expert_off, int32_t *__restrict__ tile_off, int32_t *counters,
+    PlanItem *act_items, PlanItem *tiles) {
+  extern __shared__ int32_t lds[];
+  const int nw = blockDim.x / 64;
+  int32_t *cnt = lds;                 // [nw][E] per-wave counts, then run bases
+  int32_t *off = cnt + nw * E;        // [E] expert offsets
+  int32_t *tot = off + E;             // [E] expert counts
+  int32_t *utile = tot + E;           // [E] caller tile offsets
+  int32_t *scr0 = utile + E;          // [E] plan scratch
+  int32_t *scr1 = scr0 + E;           // [E] plan scratch
+  __shared__ int32_t wave_tot[17];
+  __shared__ int32_t bad;
+
+  const int tid = threadIdx.x, nth = blockDim.x, lane = tid & 63, w = tid >> 6;
+  for (int q = tid; q < nw * E; q += nth) cnt[q] = 0;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+
+  const int seg = (N + nw - 1) / nw;
+  const int i0 = min(N, w * seg), i1 = min(N, i0 + seg);
+  for (int i = i0 + lane; i < i1; i += 64) {
+    const int e = f[i];
+    if (unsigned(e) < unsigned(E)) atomicAdd(&cnt[w * E + e], 1);
+    else bad = 1;
+  }
+  __syncthreads();
+  if (bad) {
+    // Out-of-range expert id: an empty, in-bounds result with expert_off[E] = -1.
+    for (int i = tid; i < N; i += nth) order[i] = inv_order[i] = row_map[i] = -1;
+    for (int e = tid; e <= E; e += nth) {
+      expert_off[e] = e == E ? -1 : 0;
+      tile_off[e] = 0;
+    }
+    if (tid == 0) counters[0] = counters[1] = 0;
+    return;
+  }
+
+  for (int e = tid; e < E; e += nth) {
+    int c = 0;
+    for (int ww = 0; ww < nw; ++ww) c += cnt[ww * E + e];
+    tot[e] = c;
+    off[e] = c;
+    utile[e] = (c + tile_rows - 1) / tile_rows;
+  }
+  __syncthreads();
+  block_exscan(off, E, wave_tot);
+  const int n_utiles = block_exscan(utile, E, wave_tot);
+  for (int e = tid; e < E; e += nth) {
+    int run = off[e];
+    for (int ww = 0; ww < nw; ++ww) {
+      const int c = cnt[ww * E + e];
+      cnt[ww * E + e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+
+  // Stable ranks.  Each wave only touches its own row of bases.
+  volatile int32_t *base = cnt + w * E;
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 1;
+  const uint64_t lt_mask = lane ? (~0ull >> (64 - lane)) : 0ull;
+  for (int b0 = i0; b0 < i1; b0 += 64) {
+    const int i = b0 + lane;
+    const bool valid = i < i1;
+    const int e = valid ? f[i] : 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bal = __ballot(valid && bit);
+      peers &= bit ? bal : ~bal;
+    }
+    int pos = 0;
+    if (valid) {
+      pos = base[e] + __popcll(peers & lt_mask);
+      order[pos] = i;
+      inv_order[i] = pos;
+      row_map[pos] = i / K;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (valid && lane == 63 - __clzll(peers)) base[e] = base[e] + __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  for (int e = tid; e < E; e += nth) {
+    expert_off[e] = off[e];
+    tile_off[e] = utile[e];
+  }
+  if (tid == 0) {
+    expert_off[E] = N;
+    tile_off[E] = n_utiles;
+  }
+  __syncthreads();
+  emit_plan(off, tot, scr0, scr1, wave_tot, E, S, N, T, counters, act_items, tiles);
+}
+
+__global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *__restrict__ expert_off,
+                                                        int N, int E, int S, int T,
+                                                        int32_t *counters, PlanItem *act_items,
+                                                        PlanItem *tiles) {
+  extern __shared__ int32_t lds[];
+  int32_t *off = lds, *cnt = off + E, *scr0 = cnt + E, *scr1 = scr0 + E;
+  __shared__ int32_t wave_tot[17];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    // Clamp caller offsets into [0, N] so that a bad table cannot send the
+    // expert kernels outside the sorted rows.
+    const int a = min(max(expert_off[e], 0), N);
+    const int b = min(max(expert_off[e + 1], a), N);
+    off[e] = a;
+    cnt[e] = b - a;
+  }
+  __syncthreads();
+  emit_plan(off, cnt, scr0, scr1, wave_tot, E, S, N, T, counters, act_items, tiles);
+}
+
+}  // namespace
+
+void launch_dispatch(const moe_layer_desc *d, int32_t T, const int32_t *idx, int32_t tile_rows,
+                     int32_t *order, int32_t *inv_order, int32_t *row_map, int32_t *expert_off,
+                     int32_t *tile_off, int32_t *counters, PlanItem *act_items, PlanItem *tiles,
+                     void *stream) {
+  const int E = d->n_experts, nw = kThreads / 64;
+  const size_t lds = size_t(nw * E + 5 * E) * sizeof(int32_t);
+  hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kThreads), lds, static_cast<hipStream_t>(stream),
+                     idx, T * d->top_k, d->top_k, E, d->n_shared, T, tile_rows, order, inv_order,
+                     row_map, expert_off, tile_off, counters, act_items, tiles);
+}
+
+void launch_plan(const moe_layer_desc *d, int32_t T, const int32_t *expert_off, int32_t *counters,
+                 PlanItem *act_items, PlanItem *tiles, void *stream) {
+  const int E = d->n_experts;
+  const size_t lds = size_t(4 * E) * sizeof(int32_t);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), lds, static_cast<hipStream_t>(stream),
+                     expert_off, T * d->top_k, E, d->n_shared, T, counters, act_items, tiles);
+}
+
+}  // namespace moe

@@ -1,0 +1,252 @@
+// ffn_gemv.hip -- grouped expert FFN for few rows per expert (dequant-GEMV).
+//
+// "SwitchGLU: grouped-expert Metal kernels" (ml-explore/mlx-lm #2044),
+// section "What": slots are grouped by expert across tokens so each expert's
+// weights are read and dequantised once per group of rows instead of once
+// per (token, slot); gate and up are computed in one pass.  "perf(moe): fused
+// MoE expert decode kernel" (lablup/mlxcel #275), "What it does": affine
+// dequantisation inside the GEMV, SwiGLU, down projection.
+//
+// One workgroup takes one plan item (an expert and its sorted rows) and a
+// block of output columns.  Up to MR of the item's rows are staged in LDS;
+// each wave computes whole output columns: its 64 lanes split the reduction
+// dim into 8-element pieces (one 32-bit word of 4-bit codes, or 16/32 bytes
+// of dense weights, per lane and step, so a wave reads 256..2048 contiguous
+// bytes of a weight row per step), dequantises once, and applies the piece to
+// all staged rows; a butterfly sum finishes each dot product.
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+enum WFmt { W_F32 = 0, W_BF16 = 1, W_Q4 = 2 };
+constexpr int kMR = 8;        // rows per pass (register accumulators)
+constexpr int kNB = 16;       // output columns per workgroup (4 per wave)
+constexpr int kThreads = 256;
+
+// Weights k..k+7 of global row `row` (expert-major row index) of a [.][K] matrix.
+template <int WF>
+__device__ __forceinline__ void load_w8(const void *__restrict__ w, const uint16_t *__restrict__ sc,
+                                        const uint16_t *__restrict__ bi, int64_t row, int K, int k,
+                                        float out[8]) {
+  if constexpr (WF == W_F32) {
+    const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(w) + row * K + k);
+    const float4 a = p[0], b = p[1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  } else if constexpr (WF == W_BF16) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(w) + row * K + k);
+    out[0] = bf16_lo(u.x); out[1] = bf16_hi(u.x); out[2] = bf16_lo(u.y); out[3] = bf16_hi(u.y);
+    out[4] = bf16_lo(u.z); out[5] = bf16_hi(u.z); out[6] = bf16_lo(u.w); out[7] = bf16_hi(u.w);
+  } else {
+    const uint32_t q = static_cast<const uint32_t *>(w)[row * (K / 8) + k / 8];
+    const int64_t g = row * (K / kGroup) + k / kGroup;
+    const float s = bf16_bits_to_f32(sc[g]), b = bf16_bits_to_f32(bi[g]);
+    float c[8];
+    unpack_q4(q, c);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) out[m] = __builtin_fmaf(s, c[m], b);  // s*q is exact
+  }
+}
+
+// Eight staged activations (fp32 or bf16 bits in LDS) as fp32.
+template <bool BF16>
+__device__ __forceinline__ void lds_x8(const void *xs, int idx, float out[8]) {
+  if constexpr (BF16) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(xs) + idx);
+    out[0] = bf16_lo(u.x); out[1] = bf16_hi(u.x); out[2] = bf16_lo(u.y); out[3] = bf16_hi(u.y);
+    out[4] = bf16_lo(u.z); out[5] = bf16_hi(u.z); out[6] = bf16_lo(u.w); out[7] = bf16_hi(u.w);
+  } else {
+    const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(xs) + idx);
+    const float4 a = p[0], b = p[1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  }
+}
+
+// Stage `mr` rows of length K into LDS; row m comes from src row src_row(m).
+template <bool BF16, class RowOf>
+__device__ __forceinline__ void stage_rows(void *xs, const void *__restrict__ src, int mr, int K,
+                                           RowOf src_row) {
+  // 16-byte pieces: 8 bf16 or 4 fp32 elements.
+  constexpr int EPP = BF16 ? 8 : 4;
+  const int ppr = K / EPP;
+  for (int q = threadIdx.x; q < mr * ppr; q += blockDim.x) {
+    const int m = q / ppr, c = (q % ppr) * EPP;
+    const int64_t r = src_row(m);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r >= 0) v = *reinterpret_cast<const uint4 *>(static_cast<const char *>(src) + (r * K + c) * (BF16 ? 2 : 4));
+    *reinterpret_cast<uint4 *>(static_cast<char *>(xs) + (int64_t(m) * K + c) * (BF16 ? 2 : 4)) = v;
+  }
+}
+
+struct GateUpArgs {
+  const void *x;
+  const int32_t *row_map;
+  int T, N, D, F, E, fused, round_ops, MR;
+  const void *wg;
+  const uint16_t *sg, *bg;
+  const void *wu;
+  const uint16_t *su, *bu;
+  const int32_t *counters;
+  const PlanItem *items;
+  void *h;
+};
+
+template <bool BF16, int WF>
+__global__ __launch_bounds__(kThreads) void gateup_gemv_kernel(GateUpArgs a) {
+  extern __shared__ uint4 smem_v[];
+  void *xs = smem_v;
+  if (int(blockIdx.y) >= a.counters[0]) return;
+  const PlanItem it = a.items[blockIdx.y];
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int D = a.D, F = a.F;
+  for (int r0 = 0; r0 < it.rows; r0 += a.MR) {
+    const int mr = min(a.MR, it.rows - r0);
+    __syncthreads();
+    stage_rows<BF16>(xs, a.x, mr, D, [&](int m) -> int64_t {
+      const int p = it.row0 + r0 + m;
+      const int t = p < a.N ? a.row_map[p] : (p - a.N) % a.T;
+      return unsigned(t) < unsigned(a.T) ? int64_t(t) : int64_t(-1);
+    });
+    __syncthreads();
+    for (int nq = 0; nq < kNB / 4; ++nq) {
+      const int n = blockIdx.x * kNB + wave * (kNB / 4) + nq;
+      if (n >= F) break;
+      const int64_t rg = a.fused ? int64_t(it.expert) * 2 * F + n : int64_t(it.expert) * F + n;
+      const int64_t ru = a.fused ? rg + F : rg;
+      const void *wu = a.fused ? a.wg : a.wu;
+      const uint16_t *su = a.fused ? a.sg : a.su, *bu = a.fused ? a.bg : a.bu;
+      float ag[kMR], au[kMR];
+#pragma unroll
+      for (int m = 0; m < kMR; ++m) ag[m] = au[m] = 0.0f;
+      for (int k = lane * 8; k < D; k += 8 * kWave) {
+        float wg8[8], wu8[8];
+        load_w8<WF>(a.wg, a.sg, a.bg, rg, D, k, wg8);
+        load_w8<WF>(wu, su, bu, ru, D, k, wu8);
+#pragma unroll
+        for (int m = 0; m < kMR; ++m) {
+          if (m < mr) {
+            float xv[8];
+            lds_x8<BF16>(xs, m * D + k, xv);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              ag[m] += xv[u] * wg8[u];
+              au[m] += xv[u] * wu8[u];
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < kMR; ++m) {
+        if (m < mr) {
+          const float g = wave_sum(ag[m]), u = wave_sum(au[m]);
+          if (lane == 0) {
+            const float hv = swiglu(g, u, a.round_ops);
+            const int64_t o = int64_t(it.row0 + r0 + m) * F + n;
+            if constexpr (BF16) static_cast<uint16_t *>(a.h)[o] = uint16_t(f32_to_bf16_bits(hv));
+            else static_cast<float *>(a.h)[o] = hv;
+          }
+        }
+      }
+    }
+  }
+}
+
+struct DownArgs {
+  const void *h;
+  int D, F, MR;
+  const void *wd;
+  const uint16_t *sd, *bd;
+  const int32_t *counters;
+  const PlanItem *items;
+  float *y;
+};
+
+template <bool BF16, int WF>
+__global__ __launch_bounds__(kThreads) void down_gemv_kernel(DownArgs a) {
+  extern __shared__ uint4 smem_v[];
+  void *hs = smem_v;
+  if (int(blockIdx.y) >= a.counters[0]) return;
+  const PlanItem it = a.items[blockIdx.y];
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int D = a.D, F = a.F;
+  for (int r0 = 0; r0 < it.rows; r0 += a.MR) {
+    const int mr = min(a.MR, it.rows - r0);
+    __syncthreads();
+    stage_rows<BF16>(hs, a.h, mr, F, [&](int m) -> int64_t { return it.row0 + r0 + m; });
+    __syncthreads();
+    for (int nq = 0; nq < kNB / 4; ++nq) {
+      const int n = blockIdx.x * kNB + wave * (kNB / 4) + nq;
+      if (n >= D) break;
+      const int64_t rd = int64_t(it.expert) * D + n;
+      float acc[kMR];
+#pragma unroll
+      for (int m = 0; m < kMR; ++m) acc[m] = 0.0f;
+      for (int k = lane * 8; k < F; k += 8 * kWave) {
+        float w8[8];
+        load_w8<WF>(a.wd, a.sd, a.bd, rd, F, k, w8);
+#pragma unroll
+        for (int m = 0; m < kMR; ++m) {
+          if (m < mr) {
+            float hv[8];
+            lds_x8<BF16>(hs, m * F + k, hv);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc[m] += hv[u] * w8[u];
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < kMR; ++m) {
+        if (m < mr) {
+          const float v = wave_sum(acc[m]);
+          if (lane == 0) a.y[int64_t(it.row0 + r0 + m) * D + n] = v;
+        }
+      }
+    }
+  }
+}
+
+int rows_per_pass(int K, int esz) { return max(1, min(kMR, 65536 / (K * esz))); }
+
+template <bool BF16, int WF>
+void launch_gemv(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
+                 const moe_weights *w, const int32_t *counters, const PlanItem *items, void *h,
+                 float *y, hipStream_t s) {
+  const int D = d->d_model, F = d->d_ff, E = d->n_experts, S = d->n_shared;
+  const int N = T * d->top_k;
+  const int esz = BF16 ? 2 : 4;
+  const int max_items = min(E, N) + S;
+  const moe_proj &pg = d->gate_up_fused ? w->gate_up : w->gate;
+  GateUpArgs ga{x, row_map, T, N, D, F, E, d->gate_up_fused, d->swiglu_round_bf16,
+                rows_per_pass(D, esz), pg.w, static_cast<const uint16_t *>(pg.scales),
+                static_cast<const uint16_t *>(pg.biases), w->up.w,
+                static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases),
+                counters, items, h};
+  hipLaunchKernelGGL((gateup_gemv_kernel<BF16, WF>), dim3((F + kNB - 1) / kNB, max_items),
+                     dim3(kThreads), size_t(ga.MR) * D * esz, s, ga);
+  DownArgs da{h, D, F, rows_per_pass(F, esz), w->down.w, static_cast<const uint16_t *>(w->down.scales),
+              static_cast<const uint16_t *>(w->down.biases), counters, items, y};
+  hipLaunchKernelGGL((down_gemv_kernel<BF16, WF>), dim3((D + kNB - 1) / kNB, max_items),
+                     dim3(kThreads), size_t(da.MR) * F * esz, s, da);
+}
+
+}  // namespace
+
+void launch_expert_ffn(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
+                       const moe_weights *w, const int32_t *counters, const PlanItem *act_items,
+                       const PlanItem *tiles, int64_t max_tiles, void *h, float *y_sorted,
+                       void *stream) {
+  (void)tiles;
+  (void)max_tiles;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d->w_format == MOE_WF_AFFINE_Q4)
+    launch_gemv<true, W_Q4>(d, T, x, row_map, w, counters, act_items, h, y_sorted, s);
+  else if (d->act_dtype == MOE_DT_BF16)
+    launch_gemv<true, W_BF16>(d, T, x, row_map, w, counters, act_items, h, y_sorted, s);
+  else
+    launch_gemv<false, W_F32>(d, T, x, row_map, w, counters, act_items, h, y_sorted, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,145 @@
+// moe_api.cpp -- the C ABI entry points: validate on the host, carve the
+// caller's workspace, enqueue kernels on the caller's stream, never wait.
+//
+// One command stream per layer with no host wait between router and experts
+// is the point of "MoE Optimization COMPLETE" ("Optimization Technique": the
+// router result was read back on the CPU, costing a wait per layer); every
+// entry point here only enqueues.
+#include <hip/hip_runtime.h>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+int hip_status() {
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+template <class T>
+T *at(void *ws, size_t off) {
+  return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+int check_ws(const moe_layer_desc *d, int32_t T, const void *ws, size_t ws_bytes, Workspace *out) {
+  *out = workspace_layout(d, T);
+  if (validate_ptr(ws)) return MOE_E_INVALID;
+  if (ws_bytes < out->total) return MOE_E_WORKSPACE;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_E_INVALID: return "MOE_E_INVALID: invalid descriptor, size, pointer or alignment";
+    case MOE_E_UNSUPPORTED: return "MOE_E_UNSUPPORTED: unsupported weight format";
+    case MOE_E_WORKSPACE: return "MOE_E_WORKSPACE: workspace smaller than moe_workspace_size()";
+    case MOE_E_HIP: return "MOE_E_HIP: HIP launch error";
+    default: return "unknown moe_status";
+  }
+}
+
+int moe_workspace_size(const moe_layer_desc *desc, int32_t T, size_t *bytes) {
+  int s;
+  if ((s = validate_desc(desc)) || (s = validate_T(T))) return s;
+  if (!bytes) return MOE_E_INVALID;
+  *bytes = workspace_layout(desc, T).total;
+  return MOE_OK;
+}
+
+int moe_route(const moe_layer_desc *desc, int32_t T, const void *x, const void *w_router,
+              const float *router_bias, int32_t *topk_idx, float *topk_w, void *stream) {
+  int s;
+  if ((s = validate_desc(desc)) || (s = validate_T(T))) return s;
+  if ((s = validate_ptr(x)) || (s = validate_ptr(w_router)) || (s = validate_ptr(router_bias, true)) ||
+      (s = validate_ptr(topk_idx)) || (s = validate_ptr(topk_w)))
+    return s;
+  if (T == 0) return MOE_OK;
+  launch_route(desc, T, x, w_router, router_bias, topk_idx, topk_w, stream);
+  return hip_status();
+}
+
+int moe_dispatch(const moe_layer_desc *desc, int32_t T, const int32_t *topk_idx, int32_t tile_rows,
+                 int32_t *order, int32_t *inv_order, int32_t *row_map, int32_t *expert_off,
+                 int32_t *tile_off, void *ws, size_t ws_bytes, void *stream) {
+  int s;
+  if ((s = validate_desc(desc)) || (s = validate_T(T))) return s;
+  if (tile_rows < 1) return MOE_E_INVALID;
+  if ((s = validate_ptr(topk_idx)) || (s = validate_ptr(order)) || (s = validate_ptr(inv_order)) ||
+      (s = validate_ptr(row_map)) || (s = validate_ptr(expert_off)) || (s = validate_ptr(tile_off)))
+    return s;
+  Workspace L;
+  if ((s = check_ws(desc, T, ws, ws_bytes, &L))) return s;
+  if (T == 0) return MOE_OK;
+  launch_dispatch(desc, T, topk_idx, tile_rows, order, inv_order, row_map, expert_off, tile_off,
+                  at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles),
+                  stream);
+  return hip_status();
+}
+
+int moe_expert_ffn(const moe_layer_desc *desc, int32_t T, const void *x, const int32_t *row_map,
+                   const int32_t *expert_off, const moe_weights *w, float *y_sorted, void *ws,
+                   size_t ws_bytes, void *stream) {
+  int s;
+  if ((s = validate_desc(desc)) || (s = validate_T(T))) return s;
+  if ((s = validate_ptr(x)) || (s = validate_ptr(row_map)) || (s = validate_ptr(expert_off)) ||
+      (s = validate_ptr(y_sorted)))
+    return s;
+  if ((s = validate_weights(desc, w, false, true))) return s;
+  Workspace L;
+  if ((s = check_ws(desc, T, ws, ws_bytes, &L))) return s;
+  if (T == 0) return MOE_OK;
+  launch_plan(desc, T, expert_off, at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items),
+              at<PlanItem>(ws, L.tiles), stream);
+  launch_expert_ffn(desc, T, x, row_map, w, at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items),
+                    at<PlanItem>(ws, L.tiles), L.max_tiles, at<void>(ws, L.h), y_sorted, stream);
+  return hip_status();
+}
+
+int moe_combine(const moe_layer_desc *desc, int32_t T, const float *y_sorted, const int32_t *inv_order,
+                const float *topk_w, void *y, int32_t out_dtype, void *stream) {
+  int s;
+  if ((s = validate_desc(desc)) || (s = validate_T(T))) return s;
+  if (out_dtype != MOE_DT_F32 && out_dtype != MOE_DT_BF16) return MOE_E_INVALID;
+  if ((s = validate_ptr(y_sorted)) || (s = validate_ptr(inv_order)) || (s = validate_ptr(topk_w)) ||
+      (s = validate_ptr(y)))
+    return s;
+  if (T == 0) return MOE_OK;
+  launch_combine(desc, T, y_sorted, inv_order, topk_w, y, out_dtype, stream);
+  return hip_status();
+}
+
+int moe_forward(const moe_layer_desc *desc, int32_t T, const void *x, const moe_weights *w, void *y,
+                int32_t out_dtype, int32_t *topk_idx_out, float *topk_w_out, void *ws,
+                size_t ws_bytes, void *stream) {
+  int s;
+  if ((s = validate_desc(desc)) || (s = validate_T(T))) return s;
+  if (out_dtype != MOE_DT_F32 && out_dtype != MOE_DT_BF16) return MOE_E_INVALID;
+  if ((s = validate_ptr(x)) || (s = validate_ptr(y)) || (s = validate_ptr(topk_idx_out, true)) ||
+      (s = validate_ptr(topk_w_out, true)))
+    return s;
+  if ((s = validate_weights(desc, w, true, true))) return s;
+  Workspace L;
+  if ((s = check_ws(desc, T, ws, ws_bytes, &L))) return s;
+  if (T == 0) return MOE_OK;
+  int32_t *idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.topk_idx);
+  float *wt = topk_w_out ? topk_w_out : at<float>(ws, L.topk_w);
+  launch_route(desc, T, x, w->w_router, w->router_bias, idx, wt, stream);
+  launch_dispatch(desc, T, idx, kTileRows, at<int32_t>(ws, L.order), at<int32_t>(ws, L.inv_order),
+                  at<int32_t>(ws, L.row_map), at<int32_t>(ws, L.expert_off), at<int32_t>(ws, L.tile_off),
+                  at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles),
+                  stream);
+  launch_expert_ffn(desc, T, x, at<int32_t>(ws, L.row_map), w, at<int32_t>(ws, L.counters),
+                    at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles), L.max_tiles,
+                    at<void>(ws, L.h), at<float>(ws, L.y_sorted), stream);
+  launch_combine(desc, T, at<float>(ws, L.y_sorted), at<int32_t>(ws, L.inv_order), wt, y, out_dtype,
+                 stream);
+  return hip_status();
+}
+
+}  // extern "C"

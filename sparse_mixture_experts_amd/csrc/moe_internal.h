@@ -1,0 +1,77 @@
+// moe_internal.h -- host-side plumbing shared by the library's translation
+// units: descriptor validation, workspace layout and kernel launchers.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe_mi355x.h"
+
+namespace moe {
+
+// One unit of expert work: `rows` consecutive sorted rows starting at `row0`,
+// all routed to `expert` (shared experts have ids E..E+S-1).
+struct PlanItem {
+  int32_t expert, row0, rows, pad;
+};
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxShared = 8;
+constexpr int kGroup = 64;     // q4 group length
+constexpr int kTileRows = 64;  // rows per tile of the grouped MFMA kernels
+
+// Host-side checks (no HIP calls); return a moe_status.
+int validate_desc(const moe_layer_desc *d);
+int validate_T(int32_t T);
+int validate_ptr(const void *p, bool may_be_null = false);
+int validate_weights(const moe_layer_desc *d, const moe_weights *w, bool need_router,
+                     bool need_experts);
+
+inline int64_t act_bytes(const moe_layer_desc *d) { return d->act_dtype == MOE_DT_BF16 ? 2 : 4; }
+// Bytes per element of the SwiGLU intermediate h (bf16 for bf16 layers).
+inline int64_t h_bytes(const moe_layer_desc *d) { return d->act_dtype == MOE_DT_BF16 ? 2 : 4; }
+
+// Workspace carve-up.  Every section is 256-byte aligned.
+struct Workspace {
+  size_t topk_idx, topk_w;            // [N] int32 / f32 (moe_forward without caller buffers)
+  size_t order, inv_order, row_map;   // [N] int32
+  size_t expert_off, tile_off;        // [E+1] int32
+  size_t counters;                    // 64 int32: [0] active items, [1] tiles
+  size_t act_items;                   // [E+S] PlanItem
+  size_t tiles;                       // [max_tiles] PlanItem
+  size_t h;                           // [N+S*T][d_ff] h_bytes
+  size_t y_sorted;                    // [N+S*T][d_model] f32
+  size_t total;
+  int64_t max_tiles;
+};
+Workspace workspace_layout(const moe_layer_desc *d, int32_t T);
+
+// ---- launchers (defined next to their kernels; all asynchronous) ----------
+
+// Router: topk idx/w for T tokens.
+void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router,
+                  const float *bias, int32_t *idx, float *w, void *stream);
+
+// Dispatch: stable counting sort + prefix tables + the internal work plan.
+void launch_dispatch(const moe_layer_desc *d, int32_t T, const int32_t *idx, int32_t tile_rows,
+                     int32_t *order, int32_t *inv_order, int32_t *row_map, int32_t *expert_off,
+                     int32_t *tile_off, int32_t *counters, PlanItem *act_items, PlanItem *tiles,
+                     void *stream);
+
+// Work plan from caller-supplied expert offsets (standalone moe_expert_ffn).
+void launch_plan(const moe_layer_desc *d, int32_t T, const int32_t *expert_off, int32_t *counters,
+                 PlanItem *act_items, PlanItem *tiles, void *stream);
+
+// Expert FFN over the plan: y_sorted rows for all routed and shared rows.
+void launch_expert_ffn(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
+                       const moe_weights *w, const int32_t *counters, const PlanItem *act_items,
+                       const PlanItem *tiles, int64_t max_tiles, void *h, float *y_sorted,
+                       void *stream);
+
+// Combine.
+void launch_combine(const moe_layer_desc *d, int32_t T, const float *y_sorted,
+                    const int32_t *inv_order, const float *topk_w, void *y, int32_t out_dtype,
+                    void *stream);
+
+}  // namespace moe

@@ -1,0 +1,107 @@
+// moe_validate.cpp -- host-side argument checks and workspace layout.
+// No HIP calls here: everything in this file runs before anything is enqueued,
+// so an invalid call returns an error with no device work and no side effects.
+#include <algorithm>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static bool is_bool(int32_t v) { return v == 0 || v == 1; }
+
+int validate_desc(const moe_layer_desc *d) {
+  if (!d) return MOE_E_INVALID;
+  if (d->act_dtype != MOE_DT_F32 && d->act_dtype != MOE_DT_BF16) return MOE_E_INVALID;
+  if (d->w_format != MOE_WF_DENSE && d->w_format != MOE_WF_AFFINE_Q4) return MOE_E_INVALID;
+  if (!is_bool(d->gate_up_fused) || !is_bool(d->swiglu_round_bf16) || !is_bool(d->renormalize))
+    return MOE_E_INVALID;
+  if (d->d_model <= 0 || d->d_ff <= 0 || d->d_model > 16384 || d->d_ff > 16384) return MOE_E_INVALID;
+  if (d->n_experts < 1 || d->n_experts > kMaxExperts) return MOE_E_INVALID;
+  if (d->top_k < 1 || d->top_k > kMaxTopK || d->top_k > d->n_experts) return MOE_E_INVALID;
+  if (d->n_shared < 0 || d->n_shared > kMaxShared) return MOE_E_INVALID;
+  if (d->swiglu_round_bf16 && d->act_dtype != MOE_DT_BF16) return MOE_E_INVALID;
+  if (d->w_format == MOE_WF_AFFINE_Q4) {
+    // The q4 format carries bf16 scales/biases and feeds bf16 activations.
+    if (d->act_dtype != MOE_DT_BF16) return MOE_E_UNSUPPORTED;
+    if (d->group_size != kGroup) return MOE_E_UNSUPPORTED;
+    if (d->d_model % kGroup || d->d_ff % kGroup) return MOE_E_INVALID;
+  } else {
+    if (d->d_model % 8 || d->d_ff % 8) return MOE_E_INVALID;
+  }
+  return MOE_OK;
+}
+
+int validate_T(int32_t T) {
+  // T*k and the shared rows must stay far below 2^31 sorted rows.
+  if (T < 0 || T > (1 << 20)) return MOE_E_INVALID;
+  return MOE_OK;
+}
+
+int validate_ptr(const void *p, bool may_be_null) {
+  if (!p) return may_be_null ? MOE_OK : MOE_E_INVALID;
+  if (reinterpret_cast<uintptr_t>(p) % 16) return MOE_E_INVALID;
+  return MOE_OK;
+}
+
+static int validate_proj(const moe_layer_desc *d, const moe_proj &p) {
+  int s = validate_ptr(p.w);
+  if (s) return s;
+  if (d->w_format == MOE_WF_AFFINE_Q4) {
+    if ((s = validate_ptr(p.scales))) return s;
+    if ((s = validate_ptr(p.biases))) return s;
+  }
+  return MOE_OK;
+}
+
+int validate_weights(const moe_layer_desc *d, const moe_weights *w, bool need_router,
+                     bool need_experts) {
+  if (!w) return MOE_E_INVALID;
+  int s;
+  if (need_router) {
+    if ((s = validate_ptr(w->w_router))) return s;
+    if ((s = validate_ptr(w->router_bias, true))) return s;
+  }
+  if (need_experts) {
+    if (d->gate_up_fused) {
+      if ((s = validate_proj(d, w->gate_up))) return s;
+    } else {
+      if ((s = validate_proj(d, w->gate))) return s;
+      if ((s = validate_proj(d, w->up))) return s;
+    }
+    if ((s = validate_proj(d, w->down))) return s;
+  }
+  return MOE_OK;
+}
+
+static size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+Workspace workspace_layout(const moe_layer_desc *d, int32_t T) {
+  Workspace ws{};
+  const int64_t N = int64_t(T) * d->top_k;
+  const int64_t S = d->n_shared, E = d->n_experts;
+  const int64_t rows = N + S * T;
+  const int64_t tiles_per_shared = (T + kTileRows - 1) / kTileRows;
+  ws.max_tiles = (N + kTileRows - 1) / kTileRows + std::min<int64_t>(E, N) + S * tiles_per_shared + 1;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  ws.topk_idx = take(size_t(N) * 4);
+  ws.topk_w = take(size_t(N) * 4);
+  ws.order = take(size_t(N) * 4);
+  ws.inv_order = take(size_t(N) * 4);
+  ws.row_map = take(size_t(N) * 4);
+  ws.expert_off = take(size_t(E + 1) * 4);
+  ws.tile_off = take(size_t(E + 1) * 4);
+  ws.counters = take(64 * 4);
+  ws.act_items = take(size_t(E + S) * sizeof(PlanItem));
+  ws.tiles = take(size_t(ws.max_tiles) * sizeof(PlanItem));
+  ws.h = take(size_t(rows) * d->d_ff * h_bytes(d));
+  ws.y_sorted = take(size_t(rows) * d->d_model * 4);
+  ws.total = o;
+  return ws;
+}
+
+}  // namespace moe

@@ -26,7 +26,9 @@ Recipe (the pages fix the shapes, not the draws):
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import math
+import os
 from dataclasses import dataclass, replace
 
 import numpy as np
@@ -106,8 +108,9 @@ def quantize_q4(w: np.ndarray, group: int = 64):
     with np.errstate(divide="ignore", invalid="ignore"):
         q = np.rint((wg - b) / s)
     q = np.where(s == 0, 0.0, np.clip(q, 0, 15)).astype(np.uint32).reshape(N, K // 8, 8)
-    shifts = (np.arange(8, dtype=np.uint32) * 4)[None, None, :]
-    words = np.bitwise_or.reduce(q << shifts, axis=-1).astype(np.uint32)
+    words = q[..., 0].copy()
+    for m in range(1, 8):
+        words |= q[..., m] << np.uint32(4 * m)
     return words, s_bits, b_bits
 
 
@@ -151,13 +154,26 @@ def gen_expert(spec: LayerSpec, e: int) -> dict:
     return out
 
 
-def gen_experts(spec: LayerSpec) -> dict:
-    """All experts (routed, then shared) stacked along a leading axis."""
+def gen_experts(spec: LayerSpec, workers: int | None = None) -> dict:
+    """All experts (routed, then shared) stacked along a leading axis.
+    Experts are drawn from independent streams, so they are generated in
+    parallel threads with results identical to a sequential loop."""
     n_all = spec.n_experts + spec.n_shared
-    parts = [gen_expert(spec, e) for e in range(n_all)]
-    out = {}
-    for proj in parts[0]:
-        out[proj] = {k: np.stack([p[proj][k] for p in parts]) for k in parts[0][proj]}
+    first = gen_expert(spec, 0)
+    out = {proj: {k: np.empty((n_all,) + v.shape, v.dtype) for k, v in parts.items()}
+           for proj, parts in first.items()}
+
+    def fill(e, parts=None):
+        parts = parts if parts is not None else gen_expert(spec, e)
+        for proj, arrs in parts.items():
+            for k, v in arrs.items():
+                out[proj][k][e] = v
+
+    fill(0, first)
+    if workers is None:
+        workers = min(16, len(os.sched_getaffinity(0)))
+    with cf.ThreadPoolExecutor(max_workers=max(1, workers)) as ex:
+        list(ex.map(fill, range(1, n_all)))
     return out
 
 

@@ -1,0 +1,209 @@
+"""ctypes binding of the C ABI in include/moe_mi355x.h (libmoe_mi355x.so).
+
+Argument marshalling only: every function below passes device pointers of
+torch tensors (or raw integer addresses) and the stream straight to the C
+entry point of the same name, raises ``MoeError`` on a negative status and
+returns nothing else.  All work happens in the library's HIP kernels; there
+is no fallback of any kind, and a missing library raises at load time.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
+
+MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = 0, -1, -2, -3, -4
+MOE_DT_F32, MOE_DT_BF16 = 0, 1
+MOE_WF_DENSE, MOE_WF_AFFINE_Q4 = 0, 1
+
+EXPORTED = ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
+            "moe_forward", "moe_status_string")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        super().__init__(f"{fn}: {moe_status_string(status)} ({status})")
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "d_model", "d_ff", "n_experts", "top_k", "n_shared", "act_dtype", "w_format", "group_size",
+        "gate_up_fused", "swiglu_round_bf16", "renormalize")]
+
+
+class Proj(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("w_router", ctypes.c_void_p), ("router_bias", ctypes.c_void_p), ("gate", Proj),
+                ("up", Proj), ("gate_up", Proj), ("down", Proj)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FileNotFoundError(
+                f"{LIB_PATH} is missing: build it with `python -m sparse_mixture_experts_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        P = ctypes.POINTER
+        lib.moe_workspace_size.argtypes = [P(LayerDesc), i32, P(sz)]
+        lib.moe_route.argtypes = [P(LayerDesc), i32, vp, vp, vp, vp, vp, vp]
+        lib.moe_dispatch.argtypes = [P(LayerDesc), i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.moe_expert_ffn.argtypes = [P(LayerDesc), i32, vp, vp, vp, P(Weights), vp, vp, sz, vp]
+        lib.moe_combine.argtypes = [P(LayerDesc), i32, vp, vp, vp, vp, i32, vp]
+        lib.moe_forward.argtypes = [P(LayerDesc), i32, vp, P(Weights), vp, i32, vp, vp, vp, sz, vp]
+        lib.moe_status_string.argtypes = [ctypes.c_int]
+        lib.moe_status_string.restype = ctypes.c_char_p
+        for name in EXPORTED:
+            if name != "moe_status_string":
+                getattr(lib, name).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def moe_status_string(status: int) -> str:
+    return load().moe_status_string(int(status)).decode()
+
+
+def make_desc(d_model, d_ff, n_experts, top_k, n_shared=0, act="bf16", wfmt="dense", group_size=64,
+              gate_up_fused=False, swiglu_round_bf16=False, renormalize=True) -> LayerDesc:
+    return LayerDesc(d_model, d_ff, n_experts, top_k, n_shared,
+                     MOE_DT_BF16 if act == "bf16" else MOE_DT_F32,
+                     MOE_WF_AFFINE_Q4 if wfmt == "q4" else MOE_WF_DENSE, group_size,
+                     int(gate_up_fused), int(swiglu_round_bf16), int(renormalize))
+
+
+def desc_from_spec(spec) -> LayerDesc:
+    return make_desc(spec.d_model, spec.d_ff, spec.n_experts, spec.top_k, spec.n_shared, spec.act,
+                     spec.wfmt, spec.group_size, spec.gate_up_fused, spec.swiglu_round_bf16,
+                     spec.renormalize)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if isinstance(t, torch.Tensor):
+        if not t.is_contiguous():
+            raise ValueError("tensors passed to the MoE library must be contiguous")
+        return t.data_ptr()
+    raise TypeError(f"expected a torch tensor, an int address or None, got {type(t)}")
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _nbytes(ws):
+    if ws is None:
+        return 0
+    if isinstance(ws, torch.Tensor):
+        return ws.numel() * ws.element_size()
+    raise TypeError("workspace must be a torch tensor")
+
+
+def _check(status: int, fn: str):
+    if status != MOE_OK:
+        raise MoeError(status, fn)
+
+
+def moe_workspace_size(desc: LayerDesc, T: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().moe_workspace_size(ctypes.byref(desc), T, ctypes.byref(out)), "moe_workspace_size")
+    return out.value
+
+
+def moe_route(desc, T, x, w_router, router_bias, topk_idx, topk_w, stream=None):
+    _check(load().moe_route(ctypes.byref(desc), T, _ptr(x), _ptr(w_router), _ptr(router_bias),
+                            _ptr(topk_idx), _ptr(topk_w), _stream(stream)), "moe_route")
+
+
+def moe_dispatch(desc, T, topk_idx, tile_rows, order, inv_order, row_map, expert_off, tile_off, ws,
+                 stream=None):
+    _check(load().moe_dispatch(ctypes.byref(desc), T, _ptr(topk_idx), tile_rows, _ptr(order),
+                               _ptr(inv_order), _ptr(row_map), _ptr(expert_off), _ptr(tile_off),
+                               _ptr(ws), _nbytes(ws), _stream(stream)), "moe_dispatch")
+
+
+def moe_expert_ffn(desc, T, x, row_map, expert_off, weights, y_sorted, ws, stream=None):
+    _check(load().moe_expert_ffn(ctypes.byref(desc), T, _ptr(x), _ptr(row_map), _ptr(expert_off),
+                                 ctypes.byref(weights.c), _ptr(y_sorted), _ptr(ws), _nbytes(ws),
+                                 _stream(stream)), "moe_expert_ffn")
+
+
+def moe_combine(desc, T, y_sorted, inv_order, topk_w, y, out_dtype, stream=None):
+    _check(load().moe_combine(ctypes.byref(desc), T, _ptr(y_sorted), _ptr(inv_order), _ptr(topk_w),
+                              _ptr(y), out_dtype, _stream(stream)), "moe_combine")
+
+
+def moe_forward(desc, T, x, weights, y, out_dtype, topk_idx_out, topk_w_out, ws, stream=None):
+    _check(load().moe_forward(ctypes.byref(desc), T, _ptr(x), ctypes.byref(weights.c), _ptr(y), out_dtype,
+                              _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws), _nbytes(ws),
+                              _stream(stream)), "moe_forward")
+
+
+# ---- marshalling helpers ----------------------------------------------------
+
+def to_device(a: np.ndarray, device) -> torch.Tensor:
+    """A NumPy array as a device tensor with the matching element type
+    (uint16 bf16 bits -> torch.bfloat16, uint32 codes -> torch.int32)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    if a.dtype == np.uint32:
+        return torch.from_numpy(a.view(np.int32)).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+class DeviceWeights:
+    """Device copies of a layer's weights plus the C weight table pointing at them."""
+
+    def __init__(self, w_router: torch.Tensor, router_bias, experts: dict):
+        self.w_router, self.router_bias, self.experts = w_router, router_bias, experts
+
+        def proj(name):
+            p = experts.get(name)
+            if p is None:
+                return Proj(None, None, None)
+            return Proj(_ptr(p["w"]), _ptr(p.get("scales")), _ptr(p.get("biases")))
+
+        self.c = Weights(_ptr(w_router), _ptr(router_bias), proj("gate"), proj("up"), proj("gate_up"),
+                         proj("down"))
+
+    @classmethod
+    def from_layer(cls, layer: dict, device="cuda") -> "DeviceWeights":
+        experts = {name: {k: to_device(v, device) for k, v in p.items()} for name, p in layer["experts"].items()}
+        bias = None if layer["router_bias"] is None else to_device(layer["router_bias"], device)
+        return cls(to_device(layer["w_router"], device), bias, experts)
+
+    def clone(self) -> "DeviceWeights":
+        """A byte-identical copy at new device addresses."""
+        experts = {n: {k: v.clone() for k, v in p.items()} for n, p in self.experts.items()}
+        bias = None if self.router_bias is None else self.router_bias.clone()
+        return DeviceWeights(self.w_router.clone(), bias, experts)
+
+    def nbytes(self, experts=None) -> int:
+        """Bytes of all weights, or of the listed expert ids only."""
+        total = 0
+        for p in self.experts.values():
+            for v in p.values():
+                per = v.numel() * v.element_size() // v.shape[0]
+                total += per * (v.shape[0] if experts is None else len(experts))
+        return total

@@ -1,0 +1,129 @@
+"""C-ABI library on the CPU: it loads, exports every declared symbol, and its
+host-side validation rejects bad calls before touching the GPU.
+
+No compute call happens here: every call either fails validation (returns a
+negative status, enqueues nothing) or has T == 0 (valid, enqueues nothing).
+"""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from sparse_mixture_experts_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+A = 1 << 20  # a fake, 16-byte aligned device address; never dereferenced here
+
+
+def declared_symbols():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(moe_\w+)\s*\(", text))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIB_PATH):
+        from sparse_mixture_experts_amd import build
+        build.build(verbose=False)
+    return moe.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_symbols()
+    assert set(moe.EXPORTED) <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+
+
+def good():
+    return moe.make_desc(2048, 768, 128, 8, wfmt="q4")
+
+
+def weights():
+    p = moe.Proj(A, A, A)
+    return moe.Weights(A, None, p, p, moe.Proj(None, None, None), p)
+
+
+def ws_size(d, T):
+    return moe.moe_workspace_size(d, T)
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4):
+        assert moe.moe_status_string(s)
+    assert "unknown" in moe.moe_status_string(7)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("d_model", 0, moe.MOE_E_INVALID), ("d_model", 100, moe.MOE_E_INVALID),
+    ("d_ff", 96, moe.MOE_E_INVALID), ("n_experts", 0, moe.MOE_E_INVALID),
+    ("n_experts", 1025, moe.MOE_E_INVALID), ("top_k", 0, moe.MOE_E_INVALID),
+    ("top_k", 33, moe.MOE_E_INVALID), ("n_shared", -1, moe.MOE_E_INVALID),
+    ("n_shared", 9, moe.MOE_E_INVALID), ("act_dtype", 5, moe.MOE_E_INVALID),
+    ("w_format", 3, moe.MOE_E_INVALID), ("group_size", 32, moe.MOE_E_UNSUPPORTED),
+    ("group_size", 128, moe.MOE_E_UNSUPPORTED), ("act_dtype", moe.MOE_DT_F32, moe.MOE_E_UNSUPPORTED),
+    ("renormalize", 2, moe.MOE_E_INVALID), ("gate_up_fused", -1, moe.MOE_E_INVALID),
+])
+def test_descriptor_validation(lib, field, value, status):
+    d = good()
+    setattr(d, field, value)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_workspace_size(d, 4)
+    assert ei.value.status == status
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_route(d, 4, A, A, None, A, A, stream=0)
+    assert ei.value.status == status
+
+
+def test_top_k_above_experts_and_rounding_needs_bf16(lib):
+    d = moe.make_desc(64, 64, 4, 5, act="f32")
+    assert lib.moe_workspace_size(ctypes.byref(d), 1, ctypes.byref(ctypes.c_size_t())) == moe.MOE_E_INVALID
+    d = moe.make_desc(64, 64, 4, 2, act="f32", swiglu_round_bf16=True)
+    assert lib.moe_workspace_size(ctypes.byref(d), 1, ctypes.byref(ctypes.c_size_t())) == moe.MOE_E_INVALID
+
+
+def test_pointer_and_size_validation(lib):
+    d = good()
+    st = lambda f: pytest.raises(moe.MoeError)  # noqa: E731
+    with st(0):
+        moe.moe_route(d, -1, A, A, None, A, A, stream=0)
+    with st(0):
+        moe.moe_route(d, 4, None, A, None, A, A, stream=0)
+    with st(0):
+        moe.moe_route(d, 4, A + 4, A, None, A, A, stream=0)  # misaligned
+    with st(0):
+        moe.moe_combine(d, 4, A, A, A, A, 7, stream=0)  # bad out dtype
+    with st(0):
+        moe.moe_dispatch(d, 4, A, 0, A, A, A, A, A, None, stream=0)  # tile_rows 0
+
+
+def test_workspace_checks(lib):
+    d = good()
+    need = ws_size(d, 32)
+    assert need >= ws_size(d, 1) > 0
+    assert ws_size(d, 0) >= 0
+    r = lib.moe_forward(ctypes.byref(d), 32, A, ctypes.byref(weights()), A, 0, None, None, A, need - 1, None)
+    assert r == moe.MOE_E_WORKSPACE
+    r = lib.moe_expert_ffn(ctypes.byref(d), 32, A, A, A, ctypes.byref(weights()), A, A, 16, None)
+    assert r == moe.MOE_E_WORKSPACE
+    bad_w = weights()
+    bad_w.down = moe.Proj(A, None, A)  # q4 needs scales
+    r = lib.moe_forward(ctypes.byref(d), 32, A, ctypes.byref(bad_w), A, 0, None, None, A, need, None)
+    assert r == moe.MOE_E_INVALID
+
+
+def test_zero_tokens_is_a_no_op(lib):
+    d = good()
+    need = ws_size(d, 0)
+    assert lib.moe_route(ctypes.byref(d), 0, A, A, None, A, A, None) == moe.MOE_OK
+    assert lib.moe_dispatch(ctypes.byref(d), 0, A, 64, A, A, A, A, A, A, need, None) == moe.MOE_OK
+    assert lib.moe_expert_ffn(ctypes.byref(d), 0, A, A, A, ctypes.byref(weights()), A, A, need, None) == 0
+    assert lib.moe_combine(ctypes.byref(d), 0, A, A, A, A, 0, None) == moe.MOE_OK
+    assert lib.moe_forward(ctypes.byref(d), 0, A, ctypes.byref(weights()), A, 1, None, None, A, need,
+                           None) == moe.MOE_OK
