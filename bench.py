@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--sweep A,B] [--graph]
+
+A step is one whole layer forward (router, dispatch, expert FFN, combine)
+through the C ABI (moe_forward) over one batch of synthetic input that is
+already resident in HBM.  The headline workload is the 2048-token prefill
+chunk (T=2048, d_model=2048, d_ff=512, E=512, top-10, affine 4-bit g64, fused
+gate|up); the decode layer at T=1 and T=32 is measured in the same run and
+reported under "sweep".  Weight copies and x copies rotate from step to step
+so that the bytes between two reuses of the same buffer exceed the 256 MB
+Infinity Cache: every step streams its weights from HBM.
+
+Prints ONE JSON line on stdout (everything else goes to stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, TFLOP/s
+VALU_F32_PEAK_TFLOPS = 78.6     # fp32 FMA without packed instructions: 256 CU * 64 lanes * 2 * 2.4 GHz
+METRIC = "MoE layer routed rows/s at T=1/32/2048; % of HBM or MFMA roofline"
+ROTATE_BYTES = 1 << 30          # reuse distance of weight buffers
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """The few HIP runtime calls the benchmark needs for raw stream events."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+
+def workload_name(spec) -> str:
+    w = "affine 4-bit g64" if spec.wfmt == "q4" else f"dense {spec.act}"
+    extra = (", fused gate|up" if spec.gate_up_fused else "") + (
+        ", per-op bf16 SwiGLU" if spec.swiglu_round_bf16 else "") + (
+        f", {spec.n_shared} shared experts" if spec.n_shared else "") + (
+        ", Zipf-skewed router bias" if spec.router_bias == "zipf" else "")
+    return (f"{spec.name}: MoE layer forward T={spec.T} d_model={spec.d_model} d_ff={spec.d_ff} "
+            f"E={spec.n_experts} top-{spec.top_k}, {spec.act} activations, {w} experts{extra}")
+
+
+def expert_bytes(spec) -> int:
+    """Stored bytes of one expert's gate, up and down weights."""
+    n = 3 * spec.d_model * spec.d_ff
+    if spec.wfmt == "q4":
+        return n // 2 + (n // spec.group_size) * 4
+    return n * (2 if spec.act == "bf16" else 4)
+
+
+def accounting(spec, touched: int):
+    """Algorithmic bytes and FLOPs of one forward, and per kernel."""
+    T, D, F, E, K, S = spec.T, spec.d_model, spec.d_ff, spec.n_experts, spec.top_k, spec.n_shared
+    esz = 2 if spec.act == "bf16" else 4
+    N, R = T * K, T * K + S * T
+    eb = expert_bytes(spec)
+    gu_frac, down_frac = 2 / 3, 1 / 3
+    w_touched = (touched + S) * eb
+    router = D * E * esz
+    acc = {
+        "layer_bytes": w_touched + router + T * D * esz + T * D * esz,
+        "expert_flops": 2 * R * 3 * D * F,
+        "router_flops": 2 * T * D * E,
+        "kernels": {
+            "route": {"bound": "alu", "flops": 2 * T * D * E, "bytes": T * D * esz + router + N * 8},
+            "dispatch": {"bound": "hbm", "bytes": N * 4 * 4},
+            "gateup_gemv": {"bound": "hbm", "bytes": int(w_touched * gu_frac) + T * D * esz + R * F * esz},
+            "down_gemv": {"bound": "hbm", "bytes": int(w_touched * down_frac) + R * F * esz + R * D * 4},
+            "combine": {"bound": "hbm", "bytes": R * D * 4 + T * D * esz + N * 8},
+        },
+    }
+    return acc
+
+
+def run_config(name, steps, warmup, use_graph, hip):
+    import torch
+    from sparse_mixture_experts_amd import inputs, moe
+
+    spec = inputs.CONFIGS[name]
+    dev = "cuda:0"
+    t0 = time.time()
+    host = inputs.gen_layer(spec)
+    log(f"[{name}] generated in {time.time() - t0:.1f}s")
+    desc = moe.desc_from_spec(spec)
+    w0 = moe.DeviceWeights.from_layer(host, dev)
+    wbytes = w0.nbytes()
+    n_w = max(1, math.ceil(ROTATE_BYTES / max(1, wbytes)))
+    weights = [w0] + [w0.clone() for _ in range(n_w - 1)]
+    n_x = 8
+    xs = [moe.to_device(inputs.gen_x(spec, i), dev) for i in range(n_x)]
+    T = spec.T
+    out_dt = moe.MOE_DT_BF16 if spec.act == "bf16" else moe.MOE_DT_F32
+    y = torch.empty((T, spec.d_model), device=dev, dtype=torch.bfloat16 if out_dt == moe.MOE_DT_BF16 else torch.float32)
+    ws = torch.empty(moe.moe_workspace_size(desc, T), dtype=torch.uint8, device=dev)
+    idx = torch.empty((T, spec.top_k), dtype=torch.int32, device=dev)
+    wt = torch.empty((T, spec.top_k), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        moe.moe_forward(desc, T, xs[i % n_x], weights[i % n_w], y, out_dt, idx, wt, ws, stream)
+
+    # experts touched by each x (for the algorithmic byte count)
+    touched = []
+    for i in range(n_x):
+        step(i)
+        torch.cuda.synchronize()
+        touched.append(len(np.unique(idx.cpu().numpy())))
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    graph = None
+    if use_graph:
+        # one graph per (x, weights) pair in the rotation
+        graph = []
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            for i in range(n_x * n_w // math.gcd(n_x, n_w)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    moe.moe_forward(desc, T, xs[i % n_x], weights[i % n_w], y, out_dt, idx, wt, ws, cap)
+                graph.append(g)
+        stream.wait_stream(cap)
+        for g in graph[:2]:
+            g.replay()
+        torch.cuda.synchronize()
+
+    # timed region: K whole forwards
+    torch.cuda.synchronize()
+    ta = time.perf_counter()
+    for i in range(steps):
+        if graph:
+            graph[i % len(graph)].replay()
+        else:
+            step(i)
+    torch.cuda.synchronize()
+    tb = time.perf_counter()
+    ms = (tb - ta) * 1000.0 / steps
+
+    # per-kernel durations on the launch stream: events around every kernel
+    kernel_ms, names = {}, []
+    evs = [[hip.event() for _ in range(16)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        names = moe.moe_forward_timed(desc, T, xs[i % n_x], weights[i % n_w], y, out_dt, idx, wt, ws,
+                                      evs[i], stream)
+    torch.cuda.synchronize()
+    for j, nm in enumerate(names):
+        kernel_ms[nm] = sum(hip.elapsed_ms(evs[i][j], evs[i][j + 1]) for i in range(steps)) / steps
+    for row in evs:
+        for e in row:
+            hip.destroy(e)
+
+    avg_touched = sum(touched[i % n_x] for i in range(steps)) / steps
+    acc = accounting(spec, round(avg_touched))
+    rows = T * spec.top_k
+    res = {
+        "name": name, "spec": spec, "ms_per_step": ms, "rows_per_s": rows / (ms / 1e3),
+        "tokens_per_s": T / (ms / 1e3), "kernel_ms": kernel_ms, "acc": acc, "touched": avg_touched,
+        "weight_copies": n_w, "x_copies": n_x, "graph": bool(graph),
+    }
+    lb = acc["layer_bytes"]
+    res["layer_gbs"] = lb / (ms / 1e3) / 1e9
+    res["layer_hbm_frac"] = res["layer_gbs"] / HBM_PEAK_GBS
+    res["layer_mfma_frac"] = acc["expert_flops"] / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
+    log(f"[{name}] {ms * 1e3:.1f} us/step, {res['rows_per_s']:.4g} rows/s, layer {res['layer_gbs']:.0f} GB/s "
+        f"({100 * res['layer_hbm_frac']:.1f}% HBM), kernels(us): "
+        + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in kernel_ms.items()))
+    del weights, xs, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def roofline(res):
+    km = res["kernel_ms"]
+    dom = max(km, key=km.get)
+    kacc = res["acc"]["kernels"].get(dom)
+    t = km[dom] / 1e3
+    if kacc is None:
+        return {"kernel": dom, "bound": None, "achieved": None, "peak": None, "unit": None, "frac": None,
+                "traffic": None}
+    if kacc["bound"] == "alu":
+        a = kacc["flops"] / t / 1e12
+        return {"kernel": dom, "bound": "alu", "achieved": round(a, 3), "peak": VALU_F32_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(a / VALU_F32_PEAK_TFLOPS, 4), "traffic": None,
+                "avg_launch_us": round(km[dom] * 1e3, 2)}
+    a = kacc["bytes"] / t / 1e9
+    return {"kernel": dom, "bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None, "avg_launch_us": round(km[dom] * 1e3, 2),
+            "algorithmic_bytes_per_launch": kacc["bytes"]}
+
+
+def cpu_baseline(name, n_tokens):
+    """The oracle, as it stands, on the host cores over a bounded token sample."""
+    import oracle
+    from sparse_mixture_experts_amd import inputs
+
+    spec = inputs.CONFIGS[name]
+    host = inputs.gen_layer(spec)
+    d = oracle.Desc(spec.d_model, spec.d_ff, spec.n_experts, spec.top_k, spec.n_shared, spec.act == "bf16",
+                    spec.wfmt == "q4", spec.group_size, spec.gate_up_fused, spec.swiglu_round_bf16,
+                    spec.renormalize)
+    n = min(n_tokens, spec.T)
+    toks = np.linspace(0, spec.T - 1, n).astype(np.int32)
+    threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    _, _, _, used = oracle.forward(d, host["x"], host["w_router"], host["router_bias"], host["experts"],
+                                   tokens=toks, n_threads=threads)
+    dt = time.perf_counter() - t0
+    rows = n * spec.top_k
+    return {"value": round(rows / dt, 2), "unit": "routed rows/s", "cores": used, "kind": "oracle",
+            "sample": f"{n} of {spec.T} tokens ({rows} routed rows) of {name}, each routed and run through "
+                      f"its {spec.top_k} experts; {dt:.2f} s wall on {used} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="q4-prefill-t2048")
+    ap.add_argument("--sweep", default="q4-decode-t1,q4-decode-t32")
+    ap.add_argument("--graph", action="store_true", help="replay captured HIP graphs in the timed loop")
+    ap.add_argument("--cpu-tokens", type=int, default=96)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus "
+              f"{args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from sparse_mixture_experts_amd import moe
+    moe.load()
+    hip = Hip()
+
+    head = run_config(args.config, args.steps, args.warmup, args.graph, hip)
+    sweep = []
+    for name in [s for s in args.sweep.split(",") if s]:
+        r = run_config(name, args.steps, args.warmup, args.graph, hip)
+        sweep.append({
+            "workload": workload_name(r["spec"]), "value": round(r["rows_per_s"], 1), "unit": "routed rows/s",
+            "tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 5),
+            "layer_gbs": round(r["layer_gbs"], 1), "layer_hbm_frac": round(r["layer_hbm_frac"], 4),
+            "kernel_us": {k: round(v * 1e3, 2) for k, v in r["kernel_ms"].items()},
+            "roofline": roofline(r)})
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.config, args.cpu_tokens)
+        log(f"[cpu baseline] {cpu}")
+
+    spec = head["spec"]
+    line = {
+        "metric": METRIC, "value": round(head["rows_per_s"], 1), "unit": "routed rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded N(0,1/fan_in) weights quantised to affine 4-bit g64, N(0,1) bf16 x)",
+        "config": {"workload": workload_name(spec), "T": spec.T, "d_model": spec.d_model, "d_ff": spec.d_ff,
+                   "n_experts": spec.n_experts, "top_k": spec.top_k, "n_shared": spec.n_shared,
+                   "routed_rows": spec.T * spec.top_k, "weight_copies_rotated": head["weight_copies"],
+                   "graph_replay": head["graph"]},
+        "tokens_per_s": round(head["tokens_per_s"], 1),
+        "layer_roofline": {"algorithmic_bytes": head["acc"]["layer_bytes"], "gbs": round(head["layer_gbs"], 1),
+                           "hbm_frac": round(head["layer_hbm_frac"], 4),
+                           "expert_flops": head["acc"]["expert_flops"],
+                           "mfma_frac": round(head["layer_mfma_frac"], 4),
+                           "touched_experts": head["touched"]},
+        "kernel_us": {k: round(v * 1e3, 2) for k, v in head["kernel_ms"].items()},
+        "roofline": roofline(head),
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -180,6 +180,20 @@ int moe_forward(const moe_layer_desc *desc, int32_t T, const void *x,
                 int32_t *topk_idx_out, float *topk_w_out, void *ws,
                 size_t ws_bytes, void *stream);
 
+/*
+ * moe_forward for profiling: the same work, plus a stream event recorded
+ * before the first kernel (events[0]) and after each kernel i (events[i+1]),
+ * for as many as n_events events (hipEvent_t handles created by the caller).
+ * names (nullable, names_len bytes) receives the comma-separated kernel names
+ * in launch order, truncated to fit.  Kernel durations are the elapsed times
+ * between consecutive events.
+ */
+int moe_forward_timed(const moe_layer_desc *desc, int32_t T, const void *x,
+                      const moe_weights *w, void *y, int32_t out_dtype,
+                      int32_t *topk_idx_out, float *topk_w_out, void *ws,
+                      size_t ws_bytes, void *stream, void *const *events,
+                      int32_t n_events, char *names, size_t names_len);
+
 /* A static, human-readable name of a moe_status value. */
 const char *moe_status_string(int status);
 

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 
 void launch_combine(const moe_layer_desc *d, int32_t T, const float *y_sorted,
                     const int32_t *inv_order, const float *topk_w, void *y, int32_t out_dtype,
-                    void *stream) {
+                    void *stream, StageMarker *mk) {
   const int N = T * d->top_k;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (out_dtype == MOE_DT_BF16)
@@ -60,6 +60,7 @@ void launch_combine(const moe_layer_desc *d, int32_t T, const float *y_sorted,
   else
     hipLaunchKernelGGL(combine_kernel<false>, dim3(T), dim3(256), 0, s, y_sorted, inv_order, topk_w,
                        T, d->top_k, d->n_shared, N, d->d_model, y);
+  if (mk) mk->mark("combine");
 }
 
 }  // namespace moe

@@ -218,12 +218,13 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *__restric
 void launch_dispatch(const moe_layer_desc *d, int32_t T, const int32_t *idx, int32_t tile_rows,
                      int32_t *order, int32_t *inv_order, int32_t *row_map, int32_t *expert_off,
                      int32_t *tile_off, int32_t *counters, PlanItem *act_items, PlanItem *tiles,
-                     void *stream) {
+                     void *stream, StageMarker *mk) {
   const int E = d->n_experts, nw = kThreads / 64;
   const size_t lds = size_t(nw * E + 5 * E) * sizeof(int32_t);
   hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kThreads), lds, static_cast<hipStream_t>(stream),
                      idx, T * d->top_k, d->top_k, E, d->n_shared, T, tile_rows, order, inv_order,
                      row_map, expert_off, tile_off, counters, act_items, tiles);
+  if (mk) mk->mark("dispatch");
 }
 
 void launch_plan(const moe_layer_desc *d, int32_t T, const int32_t *expert_off, int32_t *counters,

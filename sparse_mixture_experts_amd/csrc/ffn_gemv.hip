@@ -213,7 +213,7 @@ int rows_per_pass(int K, int esz) { return max(1, min(kMR, 65536 / (K * esz))); 
 template <bool BF16, int WF>
 void launch_gemv(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
                  const moe_weights *w, const int32_t *counters, const PlanItem *items, void *h,
-                 float *y, hipStream_t s) {
+                 float *y, hipStream_t s, StageMarker *mk) {
   const int D = d->d_model, F = d->d_ff, E = d->n_experts, S = d->n_shared;
   const int N = T * d->top_k;
   const int esz = BF16 ? 2 : 4;
@@ -226,10 +226,12 @@ void launch_gemv(const moe_layer_desc *d, int32_t T, const void *x, const int32_
                 counters, items, h};
   hipLaunchKernelGGL((gateup_gemv_kernel<BF16, WF>), dim3((F + kNB - 1) / kNB, max_items),
                      dim3(kThreads), size_t(ga.MR) * D * esz, s, ga);
+  if (mk) mk->mark("gateup_gemv");
   DownArgs da{h, D, F, rows_per_pass(F, esz), w->down.w, static_cast<const uint16_t *>(w->down.scales),
               static_cast<const uint16_t *>(w->down.biases), counters, items, y};
   hipLaunchKernelGGL((down_gemv_kernel<BF16, WF>), dim3((D + kNB - 1) / kNB, max_items),
                      dim3(kThreads), size_t(da.MR) * F * esz, s, da);
+  if (mk) mk->mark("down_gemv");
 }
 
 }  // namespace
@@ -237,16 +239,16 @@ void launch_gemv(const moe_layer_desc *d, int32_t T, const void *x, const int32_
 void launch_expert_ffn(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
                        const moe_weights *w, const int32_t *counters, const PlanItem *act_items,
                        const PlanItem *tiles, int64_t max_tiles, void *h, float *y_sorted,
-                       void *stream) {
+                       void *stream, StageMarker *mk) {
   (void)tiles;
   (void)max_tiles;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d->w_format == MOE_WF_AFFINE_Q4)
-    launch_gemv<true, W_Q4>(d, T, x, row_map, w, counters, act_items, h, y_sorted, s);
+    launch_gemv<true, W_Q4>(d, T, x, row_map, w, counters, act_items, h, y_sorted, s, mk);
   else if (d->act_dtype == MOE_DT_BF16)
-    launch_gemv<true, W_BF16>(d, T, x, row_map, w, counters, act_items, h, y_sorted, s);
+    launch_gemv<true, W_BF16>(d, T, x, row_map, w, counters, act_items, h, y_sorted, s, mk);
   else
-    launch_gemv<false, W_F32>(d, T, x, row_map, w, counters, act_items, h, y_sorted, s);
+    launch_gemv<false, W_F32>(d, T, x, row_map, w, counters, act_items, h, y_sorted, s, mk);
 }
 
 }  // namespace moe

@@ -114,9 +114,9 @@ int moe_combine(const moe_layer_desc *desc, int32_t T, const float *y_sorted, co
   return hip_status();
 }
 
-int moe_forward(const moe_layer_desc *desc, int32_t T, const void *x, const moe_weights *w, void *y,
-                int32_t out_dtype, int32_t *topk_idx_out, float *topk_w_out, void *ws,
-                size_t ws_bytes, void *stream) {
+static int forward_impl(const moe_layer_desc *desc, int32_t T, const void *x, const moe_weights *w,
+                        void *y, int32_t out_dtype, int32_t *topk_idx_out, float *topk_w_out, void *ws,
+                        size_t ws_bytes, void *stream, StageMarker *mk) {
   int s;
   if ((s = validate_desc(desc)) || (s = validate_T(T))) return s;
   if (out_dtype != MOE_DT_F32 && out_dtype != MOE_DT_BF16) return MOE_E_INVALID;
@@ -127,19 +127,62 @@ int moe_forward(const moe_layer_desc *desc, int32_t T, const void *x, const moe_
   Workspace L;
   if ((s = check_ws(desc, T, ws, ws_bytes, &L))) return s;
   if (T == 0) return MOE_OK;
+  if (mk) mk->mark(nullptr);
   int32_t *idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.topk_idx);
   float *wt = topk_w_out ? topk_w_out : at<float>(ws, L.topk_w);
-  launch_route(desc, T, x, w->w_router, w->router_bias, idx, wt, stream);
+  launch_route(desc, T, x, w->w_router, w->router_bias, idx, wt, stream, mk);
   launch_dispatch(desc, T, idx, kTileRows, at<int32_t>(ws, L.order), at<int32_t>(ws, L.inv_order),
                   at<int32_t>(ws, L.row_map), at<int32_t>(ws, L.expert_off), at<int32_t>(ws, L.tile_off),
                   at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles),
-                  stream);
+                  stream, mk);
   launch_expert_ffn(desc, T, x, at<int32_t>(ws, L.row_map), w, at<int32_t>(ws, L.counters),
                     at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles), L.max_tiles,
-                    at<void>(ws, L.h), at<float>(ws, L.y_sorted), stream);
+                    at<void>(ws, L.h), at<float>(ws, L.y_sorted), stream, mk);
   launch_combine(desc, T, at<float>(ws, L.y_sorted), at<int32_t>(ws, L.inv_order), wt, y, out_dtype,
-                 stream);
+                 stream, mk);
   return hip_status();
+}
+
+int moe_forward(const moe_layer_desc *desc, int32_t T, const void *x, const moe_weights *w, void *y,
+                int32_t out_dtype, int32_t *topk_idx_out, float *topk_w_out, void *ws,
+                size_t ws_bytes, void *stream) {
+  return forward_impl(desc, T, x, w, y, out_dtype, topk_idx_out, topk_w_out, ws, ws_bytes, stream,
+                      nullptr);
+}
+
+namespace {
+// Records events[0] before the first kernel and events[i] after kernel i, and
+// collects the kernel names.
+struct EventMarker : StageMarker {
+  void *const *events;
+  int32_t n_events, used = 0;
+  hipStream_t stream;
+  char *names;
+  size_t names_len, pos = 0;
+  void mark(const char *stage) override {
+    if (used < n_events) (void)hipEventRecord(static_cast<hipEvent_t>(events[used]), stream);
+    ++used;
+    if (!stage || !names || names_len == 0) return;
+    for (const char *p = (pos ? "," : ""); *p && pos + 1 < names_len; ++p) names[pos++] = *p;
+    for (const char *p = stage; *p && pos + 1 < names_len; ++p) names[pos++] = *p;
+    names[pos] = 0;
+  }
+};
+}  // namespace
+
+int moe_forward_timed(const moe_layer_desc *desc, int32_t T, const void *x, const moe_weights *w,
+                      void *y, int32_t out_dtype, int32_t *topk_idx_out, float *topk_w_out, void *ws,
+                      size_t ws_bytes, void *stream, void *const *events, int32_t n_events,
+                      char *names, size_t names_len) {
+  if (n_events < 0 || (n_events > 0 && !events)) return MOE_E_INVALID;
+  if (names && names_len) names[0] = 0;
+  EventMarker mk;
+  mk.events = events;
+  mk.n_events = n_events;
+  mk.stream = static_cast<hipStream_t>(stream);
+  mk.names = names;
+  mk.names_len = names_len;
+  return forward_impl(desc, T, x, w, y, out_dtype, topk_idx_out, topk_w_out, ws, ws_bytes, stream, &mk);
 }
 
 }  // extern "C"

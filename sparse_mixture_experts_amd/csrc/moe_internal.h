@@ -47,17 +47,25 @@ struct Workspace {
 };
 Workspace workspace_layout(const moe_layer_desc *d, int32_t T);
 
+// Optional hook called after each kernel launch (profiling builds of the
+// forward pass record a stream event there).
+struct StageMarker {
+  virtual void mark(const char *stage) = 0;
+  virtual ~StageMarker() = default;
+};
+
 // ---- launchers (defined next to their kernels; all asynchronous) ----------
 
 // Router: topk idx/w for T tokens.
 void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router,
-                  const float *bias, int32_t *idx, float *w, void *stream);
+                  const float *bias, int32_t *idx, float *w, void *stream,
+                  StageMarker *mk = nullptr);
 
 // Dispatch: stable counting sort + prefix tables + the internal work plan.
 void launch_dispatch(const moe_layer_desc *d, int32_t T, const int32_t *idx, int32_t tile_rows,
                      int32_t *order, int32_t *inv_order, int32_t *row_map, int32_t *expert_off,
                      int32_t *tile_off, int32_t *counters, PlanItem *act_items, PlanItem *tiles,
-                     void *stream);
+                     void *stream, StageMarker *mk = nullptr);
 
 // Work plan from caller-supplied expert offsets (standalone moe_expert_ffn).
 void launch_plan(const moe_layer_desc *d, int32_t T, const int32_t *expert_off, int32_t *counters,
@@ -67,11 +75,11 @@ void launch_plan(const moe_layer_desc *d, int32_t T, const int32_t *expert_off, 
 void launch_expert_ffn(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
                        const moe_weights *w, const int32_t *counters, const PlanItem *act_items,
                        const PlanItem *tiles, int64_t max_tiles, void *h, float *y_sorted,
-                       void *stream);
+                       void *stream, StageMarker *mk = nullptr);
 
 // Combine.
 void launch_combine(const moe_layer_desc *d, int32_t T, const float *y_sorted,
                     const int32_t *inv_order, const float *topk_w, void *y, int32_t out_dtype,
-                    void *stream);
+                    void *stream, StageMarker *mk = nullptr);
 
 }  // namespace moe

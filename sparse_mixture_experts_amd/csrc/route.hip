@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ x,
 }  // namespace
 
 void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router,
-                  const float *bias, int32_t *idx, float *w, void *stream) {
+                  const float *bias, int32_t *idx, float *w, void *stream, StageMarker *mk) {
   const int E = d->n_experts;
   const int threads = E >= 256 ? 256 : ((E + kWave - 1) / kWave) * kWave;
   const dim3 grid((T + TT - 1) / TT);
@@ -139,6 +139,7 @@ void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void 
   else
     hipLaunchKernelGGL(route_kernel<false>, grid, dim3(threads), lds, s, x, w_router, bias, T,
                        d->d_model, E, d->top_k, d->renormalize, idx, w);
+  if (mk) mk->mark("route");
 }
 
 }  // namespace moe

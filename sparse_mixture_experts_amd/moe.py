@@ -22,7 +22,7 @@ MOE_DT_F32, MOE_DT_BF16 = 0, 1
 MOE_WF_DENSE, MOE_WF_AFFINE_Q4 = 0, 1
 
 EXPORTED = ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-            "moe_forward", "moe_status_string")
+            "moe_forward", "moe_forward_timed", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -64,6 +64,8 @@ def load() -> ctypes.CDLL:
         lib.moe_expert_ffn.argtypes = [P(LayerDesc), i32, vp, vp, vp, P(Weights), vp, vp, sz, vp]
         lib.moe_combine.argtypes = [P(LayerDesc), i32, vp, vp, vp, vp, i32, vp]
         lib.moe_forward.argtypes = [P(LayerDesc), i32, vp, P(Weights), vp, i32, vp, vp, vp, sz, vp]
+        lib.moe_forward_timed.argtypes = [P(LayerDesc), i32, vp, P(Weights), vp, i32, vp, vp, vp, sz, vp,
+                                          P(vp), i32, ctypes.c_char_p, sz]
         lib.moe_status_string.argtypes = [ctypes.c_int]
         lib.moe_status_string.restype = ctypes.c_char_p
         for name in EXPORTED:
@@ -157,6 +159,17 @@ def moe_forward(desc, T, x, weights, y, out_dtype, topk_idx_out, topk_w_out, ws,
     _check(load().moe_forward(ctypes.byref(desc), T, _ptr(x), ctypes.byref(weights.c), _ptr(y), out_dtype,
                               _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws), _nbytes(ws),
                               _stream(stream)), "moe_forward")
+
+
+def moe_forward_timed(desc, T, x, weights, y, out_dtype, topk_idx_out, topk_w_out, ws, events, stream=None):
+    """moe_forward recording `events` (raw hipEvent_t handles) around each kernel;
+    returns the kernel names in launch order."""
+    arr = (ctypes.c_void_p * len(events))(*events)
+    names = ctypes.create_string_buffer(512)
+    _check(load().moe_forward_timed(ctypes.byref(desc), T, _ptr(x), ctypes.byref(weights.c), _ptr(y), out_dtype,
+                                    _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws), _nbytes(ws), _stream(stream),
+                                    arr, len(events), names, 512), "moe_forward_timed")
+    return names.value.decode().split(",") if names.value else []
 
 
 # ---- marshalling helpers ----------------------------------------------------
