@@ -68,12 +68,12 @@ __device__ int block_exscan(int32_t *a, int n, int32_t *wave_tot) {
 // Work plan from per-expert offsets/counts held in LDS.  act_flag and
 // tile_cnt are LDS scratch of length E.
 __device__ void emit_plan(const int32_t *off, const int32_t *cnt, int32_t *act_flag,
-                          int32_t *tile_cnt, int32_t *wave_tot, int E, int S, int N, int T,
+                          int32_t *tile_cnt, int32_t *wave_tot, int E, int S, int N, int T, int tr,
                           int32_t *counters, PlanItem *act_items, PlanItem *tiles) {
   const int tid = threadIdx.x, nth = blockDim.x;
   for (int e = tid; e < E; e += nth) {
     act_flag[e] = cnt[e] > 0;
-    tile_cnt[e] = (cnt[e] + kTileRows - 1) / kTileRows;
+    tile_cnt[e] = (cnt[e] + tr - 1) / tr;
   }
   __syncthreads();
   const int n_act = block_exscan(act_flag, E, wave_tot);
@@ -81,13 +81,13 @@ __device__ void emit_plan(const int32_t *off, const int32_t *cnt, int32_t *act_f
   for (int e = tid; e < E; e += nth) {
     const int c = cnt[e];
     if (c > 0) act_items[act_flag[e]] = PlanItem{e, off[e], c, 0};
-    for (int j = 0; j * kTileRows < c; ++j)
-      tiles[tile_cnt[e] + j] = PlanItem{e, off[e] + j * kTileRows, min(kTileRows, c - j * kTileRows), 0};
+    for (int j = 0; j * tr < c; ++j)
+      tiles[tile_cnt[e] + j] = PlanItem{e, off[e] + j * tr, min(tr, c - j * tr), 0};
   }
-  const int shared_tiles = (T + kTileRows - 1) / kTileRows;
+  const int shared_tiles = (T + tr - 1) / tr;
   for (int q = tid; q < S * shared_tiles; q += nth) {
     const int s = q / shared_tiles, j = q % shared_tiles;
-    tiles[n_tiles + q] = PlanItem{E + s, N + s * T + j * kTileRows, min(kTileRows, T - j * kTileRows), 0};
+    tiles[n_tiles + q] = PlanItem{E + s, N + s * T + j * tr, min(tr, T - j * tr), 0};
   }
   for (int s = tid; s < S; s += nth) act_items[n_act + s] = PlanItem{E + s, N + s * T, T, 0};
   if (tid == 0) {
@@ -97,7 +97,7 @@ __device__ void emit_plan(const int32_t *off, const int32_t *cnt, int32_t *act_f
 }
 
 __global__ __launch_bounds__(kThreads) void dispatch_kernel(
-    const int32_t *__restrict__ f, int N, int K, int E, int S, int T, int tile_rows,
+    const int32_t *__restrict__ f, int N, int K, int E, int S, int T, int tile_rows, int tr,
     int32_t *__restrict__ order, int32_t *__restrict__ inv_order, int32_t *__restrict__ row_map,
     int32_t *__restrict__ expert_off, int32_t *__restrict__ tile_off, int32_t *counters,
     PlanItem *act_items, PlanItem *tiles) {
@@ -191,11 +191,11 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
     tile_off[E] = n_utiles;
   }
   __syncthreads();
-  emit_plan(off, tot, scr0, scr1, wave_tot, E, S, N, T, counters, act_items, tiles);
+  emit_plan(off, tot, scr0, scr1, wave_tot, E, S, N, T, tr, counters, act_items, tiles);
 }
 
 __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *__restrict__ expert_off,
-                                                        int N, int E, int S, int T,
+                                                        int N, int E, int S, int T, int tr,
                                                         int32_t *counters, PlanItem *act_items,
                                                         PlanItem *tiles) {
   extern __shared__ int32_t lds[];
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *__restric
     cnt[e] = b - a;
   }
   __syncthreads();
-  emit_plan(off, cnt, scr0, scr1, wave_tot, E, S, N, T, counters, act_items, tiles);
+  emit_plan(off, cnt, scr0, scr1, wave_tot, E, S, N, T, tr, counters, act_items, tiles);
 }
 
 }  // namespace
@@ -219,10 +219,11 @@ void launch_dispatch(const moe_layer_desc *d, int32_t T, const int32_t *idx, int
                      int32_t *order, int32_t *inv_order, int32_t *row_map, int32_t *expert_off,
                      int32_t *tile_off, int32_t *counters, PlanItem *act_items, PlanItem *tiles,
                      void *stream, StageMarker *mk) {
+  const int tr = plan_tile_rows(d, T);
   const int E = d->n_experts, nw = kThreads / 64;
   const size_t lds = size_t(nw * E + 5 * E) * sizeof(int32_t);
   hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kThreads), lds, static_cast<hipStream_t>(stream),
-                     idx, T * d->top_k, d->top_k, E, d->n_shared, T, tile_rows, order, inv_order,
+                     idx, T * d->top_k, d->top_k, E, d->n_shared, T, tile_rows, tr, order, inv_order,
                      row_map, expert_off, tile_off, counters, act_items, tiles);
   if (mk) mk->mark("dispatch");
 }
@@ -230,9 +231,10 @@ void launch_dispatch(const moe_layer_desc *d, int32_t T, const int32_t *idx, int
 void launch_plan(const moe_layer_desc *d, int32_t T, const int32_t *expert_off, int32_t *counters,
                  PlanItem *act_items, PlanItem *tiles, void *stream) {
   const int E = d->n_experts;
+  const int tr = plan_tile_rows(d, T);
   const size_t lds = size_t(4 * E) * sizeof(int32_t);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), lds, static_cast<hipStream_t>(stream),
-                     expert_off, T * d->top_k, E, d->n_shared, T, counters, act_items, tiles);
+                     expert_off, T * d->top_k, E, d->n_shared, T, tr, counters, act_items, tiles);
 }
 
 }  // namespace moe

@@ -131,7 +131,7 @@ static int forward_impl(const moe_layer_desc *desc, int32_t T, const void *x, co
   int32_t *idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.topk_idx);
   float *wt = topk_w_out ? topk_w_out : at<float>(ws, L.topk_w);
   launch_route(desc, T, x, w->w_router, w->router_bias, idx, wt, stream, mk);
-  launch_dispatch(desc, T, idx, kTileRows, at<int32_t>(ws, L.order), at<int32_t>(ws, L.inv_order),
+  launch_dispatch(desc, T, idx, 64, at<int32_t>(ws, L.order), at<int32_t>(ws, L.inv_order),
                   at<int32_t>(ws, L.row_map), at<int32_t>(ws, L.expert_off), at<int32_t>(ws, L.tile_off),
                   at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles),
                   stream, mk);

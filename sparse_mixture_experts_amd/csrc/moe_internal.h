@@ -19,7 +19,7 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxShared = 8;
 constexpr int kGroup = 64;     // q4 group length
-constexpr int kTileRows = 64;  // rows per tile of the grouped MFMA kernels
+constexpr int kMinTileRows = 16;  // smallest row tile of the grouped MFMA kernels
 
 // Host-side checks (no HIP calls); return a moe_status.
 int validate_desc(const moe_layer_desc *d);
@@ -76,6 +76,14 @@ void launch_expert_ffn(const moe_layer_desc *d, int32_t T, const void *x, const 
                        const moe_weights *w, const int32_t *counters, const PlanItem *act_items,
                        const PlanItem *tiles, int64_t max_tiles, void *h, float *y_sorted,
                        void *stream, StageMarker *mk = nullptr);
+
+// Row-tile height of the work plan for this layer and token count, and
+// whether the grouped MFMA kernels serve the layer (else dequant-GEMV).
+int plan_tile_rows(const moe_layer_desc *d, int32_t T);
+bool use_mfma(const moe_layer_desc *d);
+void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
+                            const moe_weights *w, const int32_t *counters, const PlanItem *tiles,
+                            int64_t max_tiles, void *h, float *y_sorted, void *stream, StageMarker *mk);
 
 // Combine.
 void launch_combine(const moe_layer_desc *d, int32_t T, const float *y_sorted,

@@ -80,8 +80,8 @@ Workspace workspace_layout(const moe_layer_desc *d, int32_t T) {
   const int64_t N = int64_t(T) * d->top_k;
   const int64_t S = d->n_shared, E = d->n_experts;
   const int64_t rows = N + S * T;
-  const int64_t tiles_per_shared = (T + kTileRows - 1) / kTileRows;
-  ws.max_tiles = (N + kTileRows - 1) / kTileRows + std::min<int64_t>(E, N) + S * tiles_per_shared + 1;
+  const int64_t tiles_per_shared = (T + kMinTileRows - 1) / kMinTileRows;
+  ws.max_tiles = (N + kMinTileRows - 1) / kMinTileRows + std::min<int64_t>(E, N) + S * tiles_per_shared + 1;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
