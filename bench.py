@@ -95,10 +95,13 @@ def accounting(spec, touched: int):
         "expert_flops": 2 * R * 3 * D * F,
         "router_flops": 2 * T * D * E,
         "kernels": {
-            "route": {"bound": "alu", "flops": 2 * T * D * E, "bytes": T * D * esz + router + N * 8},
+            "route_logits": {"bound": "alu", "flops": 2 * T * D * E, "bytes": T * D * esz + router + T * E * 4},
+            "route_select": {"bound": "hbm", "bytes": T * E * 4 + N * 8},
             "dispatch": {"bound": "hbm", "bytes": N * 4 * 4},
             "gateup_gemv": {"bound": "hbm", "bytes": int(w_touched * gu_frac) + T * D * esz + R * F * esz},
             "down_gemv": {"bound": "hbm", "bytes": int(w_touched * down_frac) + R * F * esz + R * D * 4},
+            "gateup_mfma": {"bound": "hbm", "bytes": int(w_touched * gu_frac) + T * D * esz + R * F * esz},
+            "down_mfma": {"bound": "hbm", "bytes": int(w_touched * down_frac) + R * F * esz + R * D * 4},
             "combine": {"bound": "hbm", "bytes": R * D * 4 + T * D * esz + N * 8},
         },
     }

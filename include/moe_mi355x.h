@@ -121,11 +121,13 @@ int moe_workspace_size(const moe_layer_desc *desc, int32_t T, size_t *bytes);
  * sequential fma chain from +0, chunk sums added in ascending order from +0,
  * bias added last.  Slot j holds the j-th largest logit (ties to the lower
  * expert index); the weights are the fp32 softmax over all E logits, divided
- * by their sum over the k slots when renormalize is set.  Needs no workspace.
+ * by their sum over the k slots when renormalize is set.  The logits live in
+ * the workspace (sized by moe_workspace_size); they are not an output.
  */
 int moe_route(const moe_layer_desc *desc, int32_t T, const void *x,
               const void *w_router, const float *router_bias,
-              int32_t *topk_idx, float *topk_w, void *stream);
+              int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+              void *stream);
 
 /*
  * Dispatch (step 2, DS4Server #112 "Current upstream route", sort_rows, and

@@ -16,17 +16,21 @@
 // the stores contiguous.
 //
 // Weight operands come straight from global memory into registers (every
-// weight element is used by exactly one lane): for affine 4-bit weights a lane
-// reads 2 words = 16 codes of one quantisation group per step and turns each
-// word into 8 bf16 values 128+q with one shift and one and-or per pair (the
-// bf16 with exponent 2^7 and the code as its low mantissa bits is exactly
-// 128+q).  The pairs come out as (q_j, q_{j+4}), so the activations are
-// staged in LDS with the same order inside every 8-element block.  Since
+// weight element is used by exactly one lane), one 64-element group ahead of
+// their use: for affine 4-bit weights a lane reads 2 words = 16 codes of one
+// quantisation group and turns each word into 8 bf16 values 128+q with one
+// shift and one and-or per pair (the bf16 with exponent 2^7 and the code as
+// its low mantissa bits is exactly 128+q).  The pairs come out as (q_j,
+// q_{j+4}), so the activations are staged in LDS with the same order inside
+// every 8-element block.  Since
 //   sum_k x_k (s q_k + b) = s * sum_k x_k (128 + q_k) + (b - 128 s) * sum_k x_k
 // per 64-element group, two MFMAs give D = sum x (128+q) for the group and
 // the fp32 epilogue of the group adds s*D + (b - 128 s)*X with X the group sum
-// of the activations (computed once per staged row).  Dense bf16 weights go
-// to the MFMA unchanged.
+// of the activations.  Dense bf16 weights go to the MFMA unchanged.
+//
+// Activations, group sums and scales are staged in LDS in slabs of 128
+// reduction elements, double buffered: the global loads of slab s+1 are in
+// flight in registers while slab s is multiplied.
 #include "device_common.h"
 #include "moe_internal.h"
 
@@ -37,11 +41,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;  // 4 waves
-constexpr int kKS = 256;       // reduction elements staged in LDS per slab
-constexpr int kPad = 8;        // bf16 padding per LDS row (bank spread)
-constexpr int kLdsRow = kKS + kPad;
-constexpr int kGroupsPerSlab = kKS / kGroup;
+constexpr int kThreads = 256;              // 4 waves
+constexpr int kNW = kThreads / kWave;
+constexpr int kNT = 4;                     // 16-row weight tiles per wave
+constexpr int kNRows = kNW * kNT * 16;     // weight rows per block (256)
+constexpr int kKS = 128;                   // reduction elements per slab
+constexpr int kGPS = kKS / kGroup;         // groups per slab (2)
+constexpr int kLdsRow = kKS + 8;           // padded LDS row (bf16): spreads rows over banks
+static_assert(kNRows == kThreads, "one scale row per thread");
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -57,15 +64,13 @@ __device__ __forceinline__ bf16x8 q4_word_to_bf16(uint32_t w) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Permutation of an 8-element block used for q4 activations: position p holds
-// element kPerm[p].
+// bf16 elements e0..e7 -> e0,e4,e1,e5,e2,e6,e3,e7 (the order of q4_word_to_bf16).
 __device__ __forceinline__ uint4 permute8(uint4 v) {
-  // elements (bf16) e0..e7 packed as v.x = e0|e1<<16, ...; want e0,e4,e1,e5,e2,e6,e3,e7
   uint4 r;
-  r.x = (v.x & 0xffffu) | (v.z << 16);            // e0, e4
-  r.y = (v.x >> 16) | (v.z & 0xffff0000u);        // e1, e5
-  r.z = (v.y & 0xffffu) | (v.w << 16);            // e2, e6
-  r.w = (v.y >> 16) | (v.w & 0xffff0000u);        // e3, e7
+  r.x = (v.x & 0xffffu) | (v.z << 16);
+  r.y = (v.x >> 16) | (v.z & 0xffff0000u);
+  r.z = (v.y & 0xffffu) | (v.w << 16);
+  r.w = (v.y >> 16) | (v.w & 0xffff0000u);
   return r;
 }
 
@@ -90,158 +95,241 @@ struct GemmArgs {
   void *out;                // gate/up: h bf16 [rows][F]; down: y fp32 [rows][D]
 };
 
-// Shared-memory layout of one slab.
-template <int RB, int NROWS>
-struct Smem {
-  uint16_t a[RB * 16][kLdsRow];           // activations (bf16 bits), q4 order inside 8-blocks
-  float xg[kGroupsPerSlab][RB * 16];      // group sums of the activations
-  float2 sb[kGroupsPerSlab][NROWS];       // (scale, bias - 128*scale) per weight row and group
+template <int RB>
+struct Slab {
+  uint16_t a[RB * 16][kLdsRow];   // activations (bf16 bits), q4 order inside 8-blocks
+  float xg[kGPS][RB * 16];        // group sums of the activations
+  float2 sb[kGPS][kNRows];        // (scale, bias - 128*scale) per weight row and group
 };
 
-// Token row of tile row m (gate/up), or -1 for padding / out-of-range.
-__device__ __forceinline__ int64_t act_row(const GemmArgs &a, const PlanItem &t, int m, bool gateup) {
-  if (m >= t.rows) return -1;
-  const int p = t.row0 + m;
-  if (!gateup) return p;
-  const int tok = p < a.N ? a.row_map[p] : (p - a.N) % a.T;
-  return unsigned(tok) < unsigned(a.T) ? int64_t(tok) : int64_t(-1);
-}
+// Per-lane weight data of one group: q4 -> one uint2 per tile; dense -> 2 uint4.
+template <bool Q4>
+struct WGroup;
+template <>
+struct WGroup<true> { uint2 w[kNT]; };
+template <>
+struct WGroup<false> { uint4 w[kNT][2]; };
 
-// GATEUP: true -> gate/up projection with SwiGLU epilogue writing h;
-//         false -> down projection writing fp32 y rows.
-// Q4: affine 4-bit weights; otherwise dense bf16.
-// RB: 16-row blocks per tile; NT: 16-row weight tiles per wave (gate/up: NT/2
-// gate tiles followed by the NT/2 up tiles of the same columns).
-template <bool GATEUP, bool Q4, int RB, int NT>
+// GATEUP: gate/up projection with SwiGLU epilogue writing h, else down
+// projection writing fp32 y rows.  Q4: affine 4-bit weights, else dense bf16.
+// RB: 16-row blocks per tile.  Each wave owns kNT weight tiles of 16 rows; for
+// gate/up the first kNT/2 are gate rows and the last kNT/2 the up rows of the
+// same output columns.
+template <bool GATEUP, bool Q4, int RB>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
-  constexpr int NW = kThreads / kWave;
-  constexpr int NROWS = NW * NT * 16;  // weight rows (incl. up rows) per block
-  __shared__ Smem<RB, NROWS> sm;
+  constexpr int NTH = GATEUP ? kNT / 2 : kNT;  // output-column tiles per wave
+  constexpr int TPR = 16 / RB;                 // staging threads per activation row
+  constexpr int PPT = RB;                      // 8-element pieces per staging thread
+  static_assert(RB * 16 * TPR == kThreads, "staging covers the slab");
+  __shared__ Slab<RB> sm[2];
 
-  if (int(blockIdx.y) >= a.counters[1]) return;
-  const PlanItem tile = a.tiles[blockIdx.y];
+  // XCD-aware order.  Workgroups go to the 8 XCDs round-robin by linear id;
+  // the W = tiles * column-blocks work items of this call are cut into 8
+  // contiguous ranges, one per XCD, so the column blocks of a tile (which
+  // stage the same activation rows) share an L2 and every XCD gets an equal
+  // share.  Linear ids past the 8 ranges exit.
+  const int nbx = gridDim.x;
+  const int total = nbx * gridDim.y;
+  const int work = a.counters[1] * nbx;
+  const int lin = blockIdx.y * nbx + blockIdx.x;
+  const int per = (work + 7) / 8;
+  int item = lin;
+  if (8 * per <= total) {
+    const int slot = lin / 8;
+    if (slot >= per) return;
+    item = (lin % 8) * per + slot;
+  }
+  if (item >= work) return;
+  const int tile_id = item / nbx, bx = item % nbx;
+  const PlanItem tile = a.tiles[tile_id];
+
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+  const int lr = lane & 15, lg = lane >> 4;  // operand row / reduction block of this lane
   const int K = a.K, KW = K / 8, G = K / kGroup;
+  const int nslab = (K + kKS - 1) / kKS;
   const int rb_count = (tile.rows + 15) / 16;
-  constexpr int NTH = GATEUP ? NT / 2 : NT;
-  // First output column of this wave.
-  const int col0 = (blockIdx.x * NW + wave) * NTH * 16;
+  const int col0 = (bx * kNW + wave) * NTH * 16;  // first output column of this wave
+  const bool col_ok = col0 < a.n_out;              // whole wave in or out (n_out % 64 == 0)
 
-  // Global weight row (expert-major) of weight tile `nt` row r (0..15).
-  auto wrow = [&](int nt, int r) -> int64_t {
-    const int c = col0 + (nt % NTH) * 16 + r;
-    if (!GATEUP) return int64_t(tile.expert) * a.n_out + c;
-    const bool up = nt >= NTH;
-    if (a.fused) return int64_t(tile.expert) * 2 * a.n_out + (up ? a.n_out : 0) + c;
-    return int64_t(tile.expert) * a.n_out + c;
+  auto wrow_of = [&](int col, bool up) -> int64_t {
+    if (!GATEUP) return int64_t(tile.expert) * a.n_out + col;
+    if (a.fused) return int64_t(tile.expert) * 2 * a.n_out + (up ? a.n_out : 0) + col;
+    return int64_t(tile.expert) * a.n_out + col;
   };
-  auto wbase = [&](int nt) -> const void * { return (GATEUP && !a.fused && nt >= NTH) ? a.w1 : a.w0; };
-  auto sbase = [&](int nt) -> const uint16_t * { return (GATEUP && !a.fused && nt >= NTH) ? a.s1 : a.s0; };
-  auto bbase = [&](int nt) -> const uint16_t * { return (GATEUP && !a.fused && nt >= NTH) ? a.b1 : a.b0; };
-  const bool col_ok = col0 < a.n_out;  // whole wave in or out (n_out % 16 == 0)
+  auto wsrc = [&](bool up) -> const void * { return (GATEUP && !a.fused && up) ? a.w1 : a.w0; };
+  auto ssrc = [&](bool up) -> const uint16_t * { return (GATEUP && !a.fused && up) ? a.s1 : a.s0; };
+  auto bsrc = [&](bool up) -> const uint16_t * { return (GATEUP && !a.fused && up) ? a.b1 : a.b0; };
 
-  f32x4 acc[NT][RB];
+  // Every global load below is issued unconditionally, from a clamped and
+  // always valid address (unused data is discarded with a select): loads that
+  // sit on only one side of a branch make the compiler wait for all
+  // outstanding loads at the join, which would drain the prefetch pipeline.
+  const int col_c = col_ok ? col0 : a.n_out - NTH * 16;  // in-range columns for idle waves
+
+  // This lane's weight row (operand A row lr) of each tile.
+  int64_t wr[kNT];
+  const void *wp[kNT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+  for (int nt = 0; nt < kNT; ++nt) {
+    const bool up = GATEUP && nt >= NTH;
+    wr[nt] = wrow_of(col_c + (nt % NTH) * 16 + lr, up);
+    wp[nt] = wsrc(up);
+  }
+  auto load_group = [&](int g, WGroup<Q4> &dst) {
+    g = min(g, G - 1);
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      if constexpr (Q4) {
+        dst.w[nt] = *reinterpret_cast<const uint2 *>(static_cast<const uint32_t *>(wp[nt]) + wr[nt] * KW + g * 8 + lg * 2);
+      } else {
+        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(wp[nt]) + wr[nt] * K + g * kGroup + lg * 16);
+        dst.w[nt][0] = p[0];
+        dst.w[nt][1] = p[1];
+      }
+    }
+  };
+
+  // ---- staging: thread -> (row m, pieces j*PPT..+PPT of the slab) ----
+  const int sm_row = tid / TPR, sj = tid % TPR;
+  int64_t src_row = -1;
+  if (sm_row < tile.rows) {
+    const int p = tile.row0 + sm_row;
+    if (!GATEUP) {
+      src_row = p;
+    } else {
+      const int tok = p < a.N ? a.row_map[p] : (p - a.N) % a.T;
+      src_row = unsigned(tok) < unsigned(a.T) ? tok : -1;
+    }
+  }
+  const int64_t src_row_c = src_row >= 0 ? src_row : (GATEUP ? 0 : tile.row0);
+  // scale row of this thread (one weight row of the block per thread)
+  const int s_w = tid / (kNT * 16), s_nt = (tid / 16) % kNT, s_r = tid % 16;
+  const int s_col = (bx * kNW + s_w) * NTH * 16 + (s_nt % NTH) * 16 + s_r;
+  const bool s_up = GATEUP && s_nt >= NTH;
+  const bool s_ok = s_col < a.n_out;
+  const int64_t s_wrow = wrow_of(s_ok ? s_col : a.n_out - 1, s_up);
+
+  uint4 stg[PPT];
+  uint16_t sraw[kGPS][2];
+  auto stage_load = [&](int s) {
+    s = min(s, nslab - 1);
+    const int k0 = s * kKS;
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) {
+      const int k = k0 + (sj * PPT + p) * 8;
+      const uint4 v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.act) + src_row_c * K +
+                                                       min(k, K - 8));
+      const bool ok = src_row >= 0 && k < K;
+      stg[p] = make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+    }
+    if constexpr (Q4) {
+#pragma unroll
+      for (int g = 0; g < kGPS; ++g) {
+        const int gg = s * kGPS + g;
+        const bool ok = s_ok && gg < G;
+        const int64_t at = s_wrow * G + min(gg, G - 1);
+        const uint16_t sv = ssrc(s_up)[at], bv = bsrc(s_up)[at];
+        sraw[g][0] = ok ? sv : uint16_t(0);
+        sraw[g][1] = ok ? bv : uint16_t(0);
+      }
+    }
+  };
+  auto stage_write = [&](int buf) {
+    Slab<RB> &S = sm[buf];
+    float xs = 0.f;
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) {
+      if constexpr (Q4) xs += sum8_bf16(stg[p]);
+      *reinterpret_cast<uint4 *>(&S.a[sm_row][(sj * PPT + p) * 8]) = Q4 ? permute8(stg[p]) : stg[p];
+    }
+    if constexpr (Q4) {
+      // group sum over the 8 / PPT threads of one group, fixed tree order
+#pragma unroll
+      for (int o = 1; o < 8 / PPT; o <<= 1) xs += __shfl_xor(xs, o, kWave);
+      const int kk = sj * PPT * 8;
+      if (kk % kGroup == 0) S.xg[kk / kGroup][sm_row] = xs;
+#pragma unroll
+      for (int g = 0; g < kGPS; ++g) {
+        const float sc = bf16_bits_to_f32(sraw[g][0]), bi = bf16_bits_to_f32(sraw[g][1]);
+        S.sb[g][tid] = make_float2(sc, __builtin_fmaf(-128.0f, sc, bi));
+      }
+    }
+  };
+
+  f32x4 acc[kNT][RB];
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) acc[nt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int lr = lane & 15, lg = lane >> 4;  // operand row / reduction block of this lane
-
-  for (int k0 = 0; k0 < K; k0 += kKS) {
-    const int ks = min(kKS, K - k0);
-    __syncthreads();
-    // Stage activations: 16-byte pieces of 8 bf16.
-    for (int q = tid; q < RB * 16 * (kKS / 8); q += kThreads) {
-      const int m = q / (kKS / 8), c8 = q % (kKS / 8);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      const int64_t r = (c8 * 8 < ks) ? act_row(a, tile, m, GATEUP) : -1;
-      if (r >= 0) v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.act) + r * K + k0 + c8 * 8);
-      if (Q4) v = permute8(v);
-      *reinterpret_cast<uint4 *>(&sm.a[m][c8 * 8]) = v;
-    }
-    if (Q4) {
-      // Scales and (bias - 128*scale) of this slab's groups, one weight row per thread.
-      for (int r = tid; r < NROWS; r += kThreads) {
-        // row r belongs to wave r / (NT*16), weight tile (r / 16) % NT
-        const int rw = r / (NT * 16), nt = (r / 16) % NT, rr = r % 16;
-        const int c = (blockIdx.x * NW + rw) * NTH * 16 + (nt % NTH) * 16 + rr;
-        int64_t wr;
-        if (!GATEUP) wr = int64_t(tile.expert) * a.n_out + c;
-        else if (a.fused) wr = int64_t(tile.expert) * 2 * a.n_out + (nt >= NTH ? a.n_out : 0) + c;
-        else wr = int64_t(tile.expert) * a.n_out + c;
-        const int g0 = k0 / kGroup;
-        for (int g = 0; g < kGroupsPerSlab; ++g) {
-          float2 v = make_float2(0.f, 0.f);
-          if (c < a.n_out && g0 + g < G) {
-            const float s = bf16_bits_to_f32(sbase(nt)[wr * G + g0 + g]);
-            const float b = bf16_bits_to_f32(bbase(nt)[wr * G + g0 + g]);
-            v = make_float2(s, __builtin_fmaf(-128.0f, s, b));
-          }
-          sm.sb[g][r] = v;
-        }
-      }
-    }
-    __syncthreads();
-    if (Q4) {
-      // Group sums of the staged activations (fixed order: deterministic).
-      for (int q = tid; q < RB * 16 * kGroupsPerSlab; q += kThreads) {
-        const int m = q % (RB * 16), g = q / (RB * 16);
-        float s = 0.f;
+  auto compute_group = [&](const Slab<RB> &S, int gi, const WGroup<Q4> &wg) {
+    bf16x8 bx[2][RB];
 #pragma unroll
-        for (int j = 0; j < kGroup / 8; ++j) s += sum8_bf16(*reinterpret_cast<const uint4 *>(&sm.a[m][g * kGroup + j * 8]));
-        sm.xg[g][m] = s;
-      }
-      __syncthreads();
-    }
-    if (!col_ok) continue;
-
-    for (int g = 0; g < ks / kGroup; ++g) {
-      const int kg = k0 + g * kGroup;  // first reduction element of the group
-      // Activation operands of the two MFMAs of this group, per row block.
-      bf16x8 bx[2][RB];
+    for (int rb = 0; rb < RB; ++rb)
+      if (rb < rb_count)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        if (rb < rb_count) {
+        for (int j = 0; j < 2; ++j)
+          bx[j][rb] = *reinterpret_cast<const bf16x8 *>(&S.a[rb * 16 + lr][gi * kGroup + lg * 16 + j * 8]);
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            bx[j][rb] = *reinterpret_cast<const bf16x8 *>(&sm.a[rb * 16 + lr][g * kGroup + lg * 16 + j * 8]);
-        }
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int64_t wr = wrow(nt, lr);
-        bf16x8 aw[2];
-        if constexpr (Q4) {
-          const uint2 w2 = *reinterpret_cast<const uint2 *>(static_cast<const uint32_t *>(wbase(nt)) + wr * KW + kg / 8 + lg * 2);
-          aw[0] = q4_word_to_bf16(w2.x);
-          aw[1] = q4_word_to_bf16(w2.y);
-        } else {
-          const uint16_t *p = static_cast<const uint16_t *>(wbase(nt)) + wr * K + kg + lg * 16;
-          aw[0] = *reinterpret_cast<const bf16x8 *>(p);
-          aw[1] = *reinterpret_cast<const bf16x8 *>(p + 8);
-        }
+    for (int nt = 0; nt < kNT; ++nt) {
+      bf16x8 aw[2];
+      if constexpr (Q4) {
+        aw[0] = q4_word_to_bf16(wg.w[nt].x);
+        aw[1] = q4_word_to_bf16(wg.w[nt].y);
         float2 sbv[4];
-        if constexpr (Q4) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sbv[i] = sm.sb[g][(wave * NT + nt) * 16 + lg * 4 + i];
-        }
+        for (int i = 0; i < 4; ++i) sbv[i] = S.sb[gi][(wave * kNT + nt) * 16 + lg * 4 + i];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           if (rb < rb_count) {
-            if constexpr (Q4) {
-              f32x4 d = mfma16(aw[0], bx[0][rb], f32x4{0.f, 0.f, 0.f, 0.f});
-              d = mfma16(aw[1], bx[1][rb], d);
-              const float xs = sm.xg[g][rb * 16 + lr];
+            f32x4 d = mfma16(aw[0], bx[0][rb], f32x4{0.f, 0.f, 0.f, 0.f});
+            d = mfma16(aw[1], bx[1][rb], d);
+            const float xs = S.xg[gi][rb * 16 + lr];
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                acc[nt][rb][i] = __builtin_fmaf(sbv[i].y, xs, __builtin_fmaf(sbv[i].x, d[i], acc[nt][rb][i]));
-            } else {
-              acc[nt][rb] = mfma16(aw[0], bx[0][rb], acc[nt][rb]);
-              acc[nt][rb] = mfma16(aw[1], bx[1][rb], acc[nt][rb]);
-            }
+            for (int i = 0; i < 4; ++i)
+              acc[nt][rb][i] = __builtin_fmaf(sbv[i].y, xs, __builtin_fmaf(sbv[i].x, d[i], acc[nt][rb][i]));
           }
         }
+      } else {
+        aw[0] = __builtin_bit_cast(bf16x8, wg.w[nt][0]);
+        aw[1] = __builtin_bit_cast(bf16x8, wg.w[nt][1]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          if (rb < rb_count) {
+            acc[nt][rb] = mfma16(aw[0], bx[0][rb], acc[nt][rb]);
+            acc[nt][rb] = mfma16(aw[1], bx[1][rb], acc[nt][rb]);
+          }
+        }
+      }
+    }
+  };
+
+  // ---- pipelined main loop ----
+  // Weights run PD groups ahead in a ring of register buffers (4-bit groups
+  // are small, so more of them are kept in flight); the activation slab s+1
+  // is loaded during the first group of slab s and written to the other LDS
+  // buffer after its last group.
+  constexpr int PD = Q4 ? 4 : 2;
+  static_assert(PD % kGPS == 0, "ring covers whole slabs");
+  WGroup<Q4> wb[PD];
+  stage_load(0);
+  stage_write(0);
+#pragma unroll
+  for (int u = 0; u < PD; ++u) load_group(u, wb[u]);
+  __syncthreads();
+  // Steps past the last group (when G is not a multiple of PD) only keep the
+  // barrier pattern; their loads are clamped repeats and their compute is skipped.
+  for (int g0 = 0; g0 < G; g0 += PD) {
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {
+      const int g = g0 + u;
+      const int s = g / kGPS, gi = g % kGPS, buf = s & 1;
+      if (gi == 0) stage_load(s + 1);
+      if (col_ok && g < G) compute_group(sm[buf], gi, wb[u]);
+      load_group(g + PD, wb[u]);
+      if (gi == kGPS - 1) {
+        stage_write(buf ^ 1);
+        __syncthreads();
       }
     }
   }
@@ -260,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
         uint32_t hb[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16_bits(swiglu(acc[nt][rb][i], acc[nt + NTH][rb][i], a.round_ops));
-        uint2 o = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+        const uint2 o = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
         *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + row * a.n_out + c) = o;
       } else {
         *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + row * a.n_out + c) =
@@ -270,12 +358,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   }
 }
 
-template <bool GATEUP, bool Q4, int RB, int NT>
+template <bool GATEUP, bool Q4, int RB>
 void launch_one(const GemmArgs &ga, int64_t max_tiles, hipStream_t s) {
-  constexpr int NTH = GATEUP ? NT / 2 : NT;
-  const int cols_per_block = (kThreads / kWave) * NTH * 16;
+  constexpr int NTH = GATEUP ? kNT / 2 : kNT;
+  const int cols_per_block = kNW * NTH * 16;
   const dim3 grid((ga.n_out + cols_per_block - 1) / cols_per_block, unsigned(max_tiles));
-  hipLaunchKernelGGL((grouped_gemm_kernel<GATEUP, Q4, RB, NT>), grid, dim3(kThreads), 0, s, ga);
+  hipLaunchKernelGGL((grouped_gemm_kernel<GATEUP, Q4, RB>), grid, dim3(kThreads), 0, s, ga);
 }
 
 }  // namespace
@@ -308,18 +396,18 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
               w->down.w, static_cast<const uint16_t *>(w->down.scales), static_cast<const uint16_t *>(w->down.biases),
               nullptr, nullptr, nullptr, counters, tiles, y_sorted};
   if (tr == 16) {
-    if (q4) launch_one<true, true, 1, 4>(gu, max_tiles, s);
-    else launch_one<true, false, 1, 4>(gu, max_tiles, s);
+    if (q4) launch_one<true, true, 1>(gu, max_tiles, s);
+    else launch_one<true, false, 1>(gu, max_tiles, s);
     if (mk) mk->mark("gateup_mfma");
-    if (q4) launch_one<false, true, 1, 4>(dn, max_tiles, s);
-    else launch_one<false, false, 1, 4>(dn, max_tiles, s);
+    if (q4) launch_one<false, true, 1>(dn, max_tiles, s);
+    else launch_one<false, false, 1>(dn, max_tiles, s);
     if (mk) mk->mark("down_mfma");
   } else {
-    if (q4) launch_one<true, true, 4, 4>(gu, max_tiles, s);
-    else launch_one<true, false, 4, 4>(gu, max_tiles, s);
+    if (q4) launch_one<true, true, 4>(gu, max_tiles, s);
+    else launch_one<true, false, 4>(gu, max_tiles, s);
     if (mk) mk->mark("gateup_mfma");
-    if (q4) launch_one<false, true, 4, 4>(dn, max_tiles, s);
-    else launch_one<false, false, 4, 4>(dn, max_tiles, s);
+    if (q4) launch_one<false, true, 4>(dn, max_tiles, s);
+    else launch_one<false, false, 4>(dn, max_tiles, s);
     if (mk) mk->mark("down_mfma");
   }
 }

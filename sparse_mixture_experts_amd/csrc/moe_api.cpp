@@ -53,14 +53,17 @@ int moe_workspace_size(const moe_layer_desc *desc, int32_t T, size_t *bytes) {
 }
 
 int moe_route(const moe_layer_desc *desc, int32_t T, const void *x, const void *w_router,
-              const float *router_bias, int32_t *topk_idx, float *topk_w, void *stream) {
+              const float *router_bias, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+              void *stream) {
   int s;
   if ((s = validate_desc(desc)) || (s = validate_T(T))) return s;
   if ((s = validate_ptr(x)) || (s = validate_ptr(w_router)) || (s = validate_ptr(router_bias, true)) ||
       (s = validate_ptr(topk_idx)) || (s = validate_ptr(topk_w)))
     return s;
+  Workspace L;
+  if ((s = check_ws(desc, T, ws, ws_bytes, &L))) return s;
   if (T == 0) return MOE_OK;
-  launch_route(desc, T, x, w_router, router_bias, topk_idx, topk_w, stream);
+  launch_route(desc, T, x, w_router, router_bias, topk_idx, topk_w, at<float>(ws, L.route), stream);
   return hip_status();
 }
 
@@ -130,7 +133,7 @@ static int forward_impl(const moe_layer_desc *desc, int32_t T, const void *x, co
   if (mk) mk->mark(nullptr);
   int32_t *idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.topk_idx);
   float *wt = topk_w_out ? topk_w_out : at<float>(ws, L.topk_w);
-  launch_route(desc, T, x, w->w_router, w->router_bias, idx, wt, stream, mk);
+  launch_route(desc, T, x, w->w_router, w->router_bias, idx, wt, at<float>(ws, L.route), stream, mk);
   launch_dispatch(desc, T, idx, 64, at<int32_t>(ws, L.order), at<int32_t>(ws, L.inv_order),
                   at<int32_t>(ws, L.row_map), at<int32_t>(ws, L.expert_off), at<int32_t>(ws, L.tile_off),
                   at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles),

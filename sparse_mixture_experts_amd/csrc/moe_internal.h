@@ -35,6 +35,7 @@ inline int64_t h_bytes(const moe_layer_desc *d) { return d->act_dtype == MOE_DT_
 // Workspace carve-up.  Every section is 256-byte aligned.
 struct Workspace {
   size_t topk_idx, topk_w;            // [N] int32 / f32 (moe_forward without caller buffers)
+  size_t route;                       // router logits / chunk partials (f32)
   size_t order, inv_order, row_map;   // [N] int32
   size_t expert_off, tile_off;        // [E+1] int32
   size_t counters;                    // 64 int32: [0] active items, [1] tiles
@@ -56,9 +57,10 @@ struct StageMarker {
 
 // ---- launchers (defined next to their kernels; all asynchronous) ----------
 
-// Router: topk idx/w for T tokens.
+// Router: topk idx/w for T tokens; scratch holds route_scratch_floats floats.
+int64_t route_scratch_floats(const moe_layer_desc *d, int32_t T);
 void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router,
-                  const float *bias, int32_t *idx, float *w, void *stream,
+                  const float *bias, int32_t *idx, float *w, float *scratch, void *stream,
                   StageMarker *mk = nullptr);
 
 // Dispatch: stable counting sort + prefix tables + the internal work plan.

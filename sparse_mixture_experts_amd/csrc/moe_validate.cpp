@@ -90,6 +90,7 @@ Workspace workspace_layout(const moe_layer_desc *d, int32_t T) {
   };
   ws.topk_idx = take(size_t(N) * 4);
   ws.topk_w = take(size_t(N) * 4);
+  ws.route = take(size_t(route_scratch_floats(d, T)) * 4);
   ws.order = take(size_t(N) * 4);
   ws.inv_order = take(size_t(N) * 4);
   ws.row_map = take(size_t(N) * 4);

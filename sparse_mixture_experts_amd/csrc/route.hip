@@ -10,136 +10,259 @@
 // bit: for each (token, expert) the reduction over d runs in chunks of 64
 // consecutive columns; a chunk is a sequential fma chain starting at +0, the
 // chunk partials are added in ascending order to an accumulator starting at
-// +0, and the bias is added last.  Each lane owns one expert and TT tokens,
-// so the fma chains of one lane are independent and keep the VALU busy; the
-// router column reads are coalesced across lanes (W_router is [d][E]).
+// +0, and the bias is added last.
+//
+// The chunk partials are independent, so they are computed in parallel:
+// kernel 1 gives each thread one chunk of 8 experts for TT tokens (8*TT
+// independent fma chains; one 16-byte router load per column feeds 8*TT fmas;
+// the token columns come from LDS as fp32).  When one workgroup holds every
+// chunk of its (token, expert) block (large T), it adds the partials in chunk
+// order from LDS and writes logits; for small T the chunks are spread over
+// more workgroups to spread the router-weight reads over many CUs, and the
+// raw partials go to a small global buffer.  Kernel 2 takes one wave per
+// token: it adds any remaining partials in chunk order, then selects the top-k
+// with a butterfly argmax per slot and computes the fp32 softmax weights.
+#include <algorithm>
+
 #include "device_common.h"
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int TT = 8;      // tokens per workgroup
-constexpr int SLAB = 512;  // columns of x staged in LDS at a time (multiple of 64)
+constexpr int kThreads = 256;
+constexpr int kChunk = 64;
 
 // (v, e) ranks before (bv, be): larger logit first, ties to the lower index.
 __device__ __forceinline__ bool ranks_before(float v, int e, float bv, int be) {
   return v > bv || (v == bv && e < be);
 }
 
+// Eight consecutive router weights as fp32.
 template <bool BF16>
-__global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ x,
-                                                    const void *__restrict__ wr,
-                                                    const float *__restrict__ bias, int T, int D,
-                                                    int E, int K, int renorm,
-                                                    int32_t *__restrict__ idx_out,
-                                                    float *__restrict__ w_out) {
-  __shared__ float xs[SLAB][TT];
-  extern __shared__ float logits[];  // [TT][E]
+__device__ __forceinline__ void load_w8(const void *w, int64_t i, float o[8]) {
+  if constexpr (BF16) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(w) + i);
+    o[0] = bf16_lo(u.x); o[1] = bf16_hi(u.x); o[2] = bf16_lo(u.y); o[3] = bf16_hi(u.y);
+    o[4] = bf16_lo(u.z); o[5] = bf16_hi(u.z); o[6] = bf16_lo(u.w); o[7] = bf16_hi(u.w);
+  } else {
+    const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(w) + i);
+    const float4 a = p[0], b = p[1];
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
+}
 
-  const int t0 = blockIdx.x * TT;
+// Chunk partials.  Block (tb, eb, cb): tokens tb*TT.., experts eb*EPB.., chunks
+// cb*CPB..; thread = (chunk lane tid / EO, expert octet tid % EO).
+// FULL: the block holds all chunks -> logits[T][E]; else partials[C][T][E].
+template <bool BF16, int TT, int CPB>
+__global__ __launch_bounds__(kThreads) void route_partials_kernel(
+    const void *__restrict__ x, const void *__restrict__ wr, const float *__restrict__ bias, int T, int D,
+    int E, int full, float *__restrict__ out) {
+  constexpr int EO = kThreads / CPB;  // expert octets per block
+  constexpr int EPB = EO * 8;         // experts per block
+  extern __shared__ float lds[];
+  float *xs = lds;    // [CPB*64][TT] token columns
+  float *part = lds;  // [CPB][TT][EPB] chunk partials, overlaying xs once it is consumed
+
+  const int tid = threadIdx.x, cl = tid / EO, eo = tid % EO;
+  const int t0 = blockIdx.x * TT, e0 = blockIdx.y * EPB, c0 = blockIdx.z * CPB;
+  const int C = (D + kChunk - 1) / kChunk;
   const int nt = min(TT, T - t0);
-  const int tid = threadIdx.x;
+  const int kbeg = c0 * kChunk, kend = min(D, (c0 + CPB) * kChunk);
 
-  for (int eg = 0; eg < E; eg += blockDim.x) {
-    const int e = eg + tid;
-    const bool active = e < E;
-    float acc[TT];
-#pragma unroll
-    for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
-    for (int s0 = 0; s0 < D; s0 += SLAB) {
-      const int s1 = min(s0 + SLAB, D);
-      __syncthreads();
-      for (int q = tid; q < TT * SLAB; q += blockDim.x) {
-        const int t = q / SLAB, c = q % SLAB;
-        float v = 0.0f;
-        if (t < nt && s0 + c < s1) v = load_act<BF16>(x, int64_t(t0 + t) * D + s0 + c);
-        xs[c][t] = v;
-      }
-      __syncthreads();
-      if (active) {
-        for (int c0 = s0; c0 < s1; c0 += 64) {
-          const int c1 = min(c0 + 64, s1);
-          float p[TT];
-#pragma unroll
-          for (int t = 0; t < TT; ++t) p[t] = 0.0f;
-          for (int i = c0; i < c1; ++i) {
-            const float w = load_act<BF16>(wr, int64_t(i) * E + e);
-#pragma unroll
-            for (int t = 0; t < TT; ++t) p[t] = __builtin_fmaf(xs[i - s0][t], w, p[t]);
-          }
-#pragma unroll
-          for (int t = 0; t < TT; ++t) acc[t] = acc[t] + p[t];
-        }
-      }
-    }
-    if (active) {
-#pragma unroll
-      for (int t = 0; t < TT; ++t) logits[t * E + e] = bias ? acc[t] + bias[e] : acc[t];
-    }
+  for (int q = tid; q < (kend - kbeg) * TT; q += kThreads) {
+    const int k = q / TT, t = q % TT;
+    xs[q] = t < nt ? load_act<BF16>(x, int64_t(t0 + t) * D + kbeg + k) : 0.0f;
   }
   __syncthreads();
 
-  // Selection and weights: one wave per token.  After each butterfly argmax
-  // every lane holds the same winner, so lane j keeps the winner of round j.
-  const int wave = tid / kWave, lane = lane_id(), nwaves = blockDim.x / kWave;
-  for (int t = wave; t < nt; t += nwaves) {
-    const float *l = logits + t * E;
-    uint32_t taken = 0;  // bit m: expert lane + 64*m already selected
-    int my_e = 0;
-    float my_l = 0.0f, top = 0.0f;
-    for (int j = 0; j < K; ++j) {
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
-      for (int m = 0, e = lane; e < E; ++m, e += kWave) {
-        if ((taken >> m) & 1u) continue;
-        const float v = l[e];
-        if (ranks_before(v, e, bv, be)) { bv = v; be = e; }
+  const int c = c0 + cl;
+  const int e = e0 + eo * 8;
+  const bool active = c < C && e < E;
+  float p[TT][8];
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[t][j] = 0.0f;
+  if (active) {
+    const int kc = c * kChunk, n = min(D, kc + kChunk) - kc;
+    // 8 router columns of 8 experts are loaded before they are used, so the
+    // loads of a step overlap each other; experts past E read as 0.
+    const bool vec = (E % 8) == 0;
+    for (int k8 = 0; k8 < n; k8 += 8) {
+      float w[8][8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t base = int64_t(kc + k8 + u) * E + e;
+        if (k8 + u < n && vec) {
+          load_w8<BF16>(wr, base, w[u]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) w[u][j] = (k8 + u < n && e + j < E) ? load_act<BF16>(wr, base + j) : 0.0f;
+        }
       }
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, kWave);
-        const int oe = __shfl_xor(be, o, kWave);
-        if (ranks_before(ov, oe, bv, be)) { bv = ov; be = oe; }
+      for (int u = 0; u < 8; ++u) {
+        if (k8 + u < n) {
+          const float *xk = xs + (kc + k8 + u - kbeg) * TT;
+#pragma unroll
+          for (int t = 0; t < TT; ++t) {
+            const float xv = xk[t];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p[t][j] = __builtin_fmaf(xv, w[u][j], p[t][j]);
+          }
+        }
       }
-      if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
-      if (j == 0) top = bv;
-      if (lane == j) { my_e = be; my_l = bv; }
     }
-    // fp32 softmax over all E logits (the top-1 logit is the maximum).
-    float z = 0.0f;
-    for (int e = lane; e < E; e += kWave) z += expf(l[e] - top);
-    z = wave_sum(z);
-    const float p = expf(my_l - top) / z;
-    float w = p;
-    if (renorm) {
-      float psum = 0.0f;
-      for (int j = 0; j < K; ++j) psum = psum + __shfl(p, j, kWave);
-      w = p / psum;
+  }
+  __syncthreads();  // everyone is done with xs, which part overlays
+  if (active) {
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) part[(cl * TT + t) * EPB + eo * 8 + j] = p[t][j];
+  }
+  __syncthreads();
+
+  if (full) {
+    // All chunks are here: chunk-ordered sum, then the bias.
+    for (int q = tid; q < TT * EPB; q += kThreads) {
+      const int t = q / EPB, el = q % EPB;
+      if (t >= nt || e0 + el >= E) continue;
+      float acc = 0.0f;
+      for (int cc = 0; cc < C; ++cc) acc = acc + part[(cc * TT + t) * EPB + el];
+      if (bias) acc = acc + bias[e0 + el];
+      out[int64_t(t0 + t) * E + e0 + el] = acc;
     }
-    if (lane < K) {
-      idx_out[int64_t(t0 + t) * K + lane] = my_e;
-      w_out[int64_t(t0 + t) * K + lane] = w;
+  } else {
+    for (int q = tid; q < CPB * TT * EPB; q += kThreads) {
+      const int cc = q / (TT * EPB), t = (q / EPB) % TT, el = q % EPB;
+      if (c0 + cc >= C || t >= nt || e0 + el >= E) continue;
+      out[(int64_t(c0 + cc) * T + t0 + t) * E + e0 + el] = part[q];
     }
   }
 }
 
+// One wave per token: logits (summing chunk partials when n_chunks > 0),
+// top-k, softmax.  Each lane keeps the logits of experts lane + 64*m.
+__global__ __launch_bounds__(kThreads) void route_select_kernel(const float *__restrict__ in, int n_chunks,
+                                                                const float *__restrict__ bias, int T, int E,
+                                                                int K, int renorm, int32_t *__restrict__ idx_out,
+                                                                float *__restrict__ w_out) {
+  constexpr int kMaxPerLane = kMaxExperts / kWave;
+  const int t = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+  const int lane = lane_id();
+  if (t >= T) return;
+  float l[kMaxPerLane];
+#pragma unroll
+  for (int m = 0; m < kMaxPerLane; ++m) {
+    const int e = lane + kWave * m;
+    float v = -INFINITY;
+    if (e < E) {
+      if (n_chunks == 0) {
+        v = in[int64_t(t) * E + e];
+      } else {
+        // Issue 16 partial loads at a time, then add them in chunk order.
+        float acc = 0.0f;
+        for (int c0 = 0; c0 < n_chunks; c0 += 16) {
+          float pv[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) pv[u] = c0 + u < n_chunks ? in[(int64_t(c0 + u) * T + t) * E + e] : 0.0f;
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            if (c0 + u < n_chunks) acc = acc + pv[u];
+        }
+        if (bias) acc = acc + bias[e];
+        v = acc;
+      }
+    }
+    l[m] = v;
+  }
+  uint32_t taken = 0;
+  int my_e = 0;
+  float my_l = 0.0f, top = 0.0f;
+  for (int j = 0; j < K; ++j) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int m = 0; m < kMaxPerLane; ++m) {
+      const int e = lane + kWave * m;
+      if (e < E && !((taken >> m) & 1u) && ranks_before(l[m], e, bv, be)) { bv = l[m]; be = e; }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oe = __shfl_xor(be, o, kWave);
+      if (ranks_before(ov, oe, bv, be)) { bv = ov; be = oe; }
+    }
+    if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
+    if (j == 0) top = bv;
+    if (lane == j) { my_e = be; my_l = bv; }
+  }
+  // fp32 softmax over all E logits (the top-1 logit is the maximum).
+  float z = 0.0f;
+#pragma unroll
+  for (int m = 0; m < kMaxPerLane; ++m)
+    if (lane + kWave * m < E) z += expf(l[m] - top);
+  z = wave_sum(z);
+  const float p = expf(my_l - top) / z;
+  float w = p;
+  if (renorm) {
+    float psum = 0.0f;
+    for (int j = 0; j < K; ++j) psum = psum + __shfl(p, j, kWave);
+    w = p / psum;
+  }
+  if (lane < K) {
+    idx_out[int64_t(t) * K + lane] = my_e;
+    w_out[int64_t(t) * K + lane] = w;
+  }
+}
+
+// Returns true when one block held every chunk (the output is logits).
+template <bool BF16, int TT, int CPB>
+bool launch_partials(const void *x, const void *wr, const float *bias, int T, int D, int E, float *out,
+                     hipStream_t s) {
+  constexpr int EPB = (kThreads / CPB) * 8;
+  const int C = (D + kChunk - 1) / kChunk;
+  const dim3 grid((T + TT - 1) / TT, (E + EPB - 1) / EPB, (C + CPB - 1) / CPB);
+  const int full = grid.z == 1;
+  const size_t lds = std::max(size_t(CPB) * kChunk * TT, size_t(CPB) * TT * EPB) * sizeof(float);
+  hipLaunchKernelGGL((route_partials_kernel<BF16, TT, CPB>), grid, dim3(kThreads), lds, s, x, wr, bias, T, D,
+                     E, full, out);
+  return full;
+}
+
 }  // namespace
 
+int64_t route_scratch_floats(const moe_layer_desc *d, int32_t T) {
+  const int64_t C = (d->d_model + kChunk - 1) / kChunk;
+  return std::max<int64_t>(int64_t(T) * d->n_experts, C * T * d->n_experts);
+}
+
 void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router,
-                  const float *bias, int32_t *idx, float *w, void *stream, StageMarker *mk) {
-  const int E = d->n_experts;
-  const int threads = E >= 256 ? 256 : ((E + kWave - 1) / kWave) * kWave;
-  const dim3 grid((T + TT - 1) / TT);
-  const size_t lds = size_t(TT) * E * sizeof(float);
+                  const float *bias, int32_t *idx, float *w, float *scratch, void *stream, StageMarker *mk) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (d->act_dtype == MOE_DT_BF16)
-    hipLaunchKernelGGL(route_kernel<true>, grid, dim3(threads), lds, s, x, w_router, bias, T,
-                       d->d_model, E, d->top_k, d->renormalize, idx, w);
-  else
-    hipLaunchKernelGGL(route_kernel<false>, grid, dim3(threads), lds, s, x, w_router, bias, T,
-                       d->d_model, E, d->top_k, d->renormalize, idx, w);
-  if (mk) mk->mark("route");
+  const int D = d->d_model, E = d->n_experts;
+  const int C = (D + kChunk - 1) / kChunk;
+  const bool bf16 = d->act_dtype == MOE_DT_BF16;
+  // Large T: 8 tokens per block with every chunk of the block on chip.
+  // Small T (or d_model > 2048): one token per block, 2 chunks per block, the
+  // partials summed by the selection kernel.
+  bool full;
+  if (T >= 64 && C <= 32) {
+    full = bf16 ? launch_partials<true, 8, 32>(x, w_router, bias, T, D, E, scratch, s)
+                : launch_partials<false, 8, 32>(x, w_router, bias, T, D, E, scratch, s);
+  } else {
+    full = bf16 ? launch_partials<true, 1, 2>(x, w_router, bias, T, D, E, scratch, s)
+                : launch_partials<false, 1, 2>(x, w_router, bias, T, D, E, scratch, s);
+  }
+  const int n_chunks = full ? 0 : C;
+  if (mk) mk->mark("route_logits");
+  const int wpb = kThreads / kWave;
+  hipLaunchKernelGGL(route_select_kernel, dim3((T + wpb - 1) / wpb), dim3(kThreads), 0, s, scratch, n_chunks,
+                     bias, T, E, d->top_k, d->renormalize, idx, w);
+  if (mk) mk->mark("route_select");
 }
 
 }  // namespace moe

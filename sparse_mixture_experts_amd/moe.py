@@ -59,7 +59,7 @@ def load() -> ctypes.CDLL:
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         P = ctypes.POINTER
         lib.moe_workspace_size.argtypes = [P(LayerDesc), i32, P(sz)]
-        lib.moe_route.argtypes = [P(LayerDesc), i32, vp, vp, vp, vp, vp, vp]
+        lib.moe_route.argtypes = [P(LayerDesc), i32, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.moe_dispatch.argtypes = [P(LayerDesc), i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.moe_expert_ffn.argtypes = [P(LayerDesc), i32, vp, vp, vp, P(Weights), vp, vp, sz, vp]
         lib.moe_combine.argtypes = [P(LayerDesc), i32, vp, vp, vp, vp, i32, vp]
@@ -132,9 +132,9 @@ def moe_workspace_size(desc: LayerDesc, T: int) -> int:
     return out.value
 
 
-def moe_route(desc, T, x, w_router, router_bias, topk_idx, topk_w, stream=None):
+def moe_route(desc, T, x, w_router, router_bias, topk_idx, topk_w, ws, stream=None):
     _check(load().moe_route(ctypes.byref(desc), T, _ptr(x), _ptr(w_router), _ptr(router_bias),
-                            _ptr(topk_idx), _ptr(topk_w), _stream(stream)), "moe_route")
+                            _ptr(topk_idx), _ptr(topk_w), _ptr(ws), _nbytes(ws), _stream(stream)), "moe_route")
 
 
 def moe_dispatch(desc, T, topk_idx, tile_rows, order, inv_order, row_map, expert_off, tile_off, ws,

@@ -29,7 +29,7 @@ class GpuLayer:
     def route(self):
         idx = torch.empty((self.T, self.spec.top_k), dtype=torch.int32, device=DEV)
         w = torch.empty((self.T, self.spec.top_k), dtype=torch.float32, device=DEV)
-        moe.moe_route(self.desc, self.T, self.x, self.w.w_router, self.w.router_bias, idx, w)
+        moe.moe_route(self.desc, self.T, self.x, self.w.w_router, self.w.router_bias, idx, w, self.ws)
         torch.cuda.synchronize()
         return idx.cpu().numpy(), w.cpu().numpy()
 

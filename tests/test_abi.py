@@ -77,7 +77,7 @@ def test_descriptor_validation(lib, field, value, status):
         moe.moe_workspace_size(d, 4)
     assert ei.value.status == status
     with pytest.raises(moe.MoeError) as ei:
-        moe.moe_route(d, 4, A, A, None, A, A, stream=0)
+        moe.moe_route(d, 4, A, A, None, A, A, None, stream=0)
     assert ei.value.status == status
 
 
@@ -92,11 +92,11 @@ def test_pointer_and_size_validation(lib):
     d = good()
     st = lambda f: pytest.raises(moe.MoeError)  # noqa: E731
     with st(0):
-        moe.moe_route(d, -1, A, A, None, A, A, stream=0)
+        moe.moe_route(d, -1, A, A, None, A, A, None, stream=0)
     with st(0):
-        moe.moe_route(d, 4, None, A, None, A, A, stream=0)
+        moe.moe_route(d, 4, None, A, None, A, A, None, stream=0)
     with st(0):
-        moe.moe_route(d, 4, A + 4, A, None, A, A, stream=0)  # misaligned
+        moe.moe_route(d, 4, A + 4, A, None, A, A, None, stream=0)  # misaligned
     with st(0):
         moe.moe_combine(d, 4, A, A, A, A, 7, stream=0)  # bad out dtype
     with st(0):
@@ -121,7 +121,7 @@ def test_workspace_checks(lib):
 def test_zero_tokens_is_a_no_op(lib):
     d = good()
     need = ws_size(d, 0)
-    assert lib.moe_route(ctypes.byref(d), 0, A, A, None, A, A, None) == moe.MOE_OK
+    assert lib.moe_route(ctypes.byref(d), 0, A, A, None, A, A, A, need, None) == moe.MOE_OK
     assert lib.moe_dispatch(ctypes.byref(d), 0, A, 64, A, A, A, A, A, A, need, None) == moe.MOE_OK
     assert lib.moe_expert_ffn(ctypes.byref(d), 0, A, A, A, ctypes.byref(weights()), A, A, need, None) == 0
     assert lib.moe_combine(ctypes.byref(d), 0, A, A, A, A, 0, None) == moe.MOE_OK
