@@ -25,6 +25,8 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 512;
+constexpr int kBatch = 8;   // slots per lane loaded together (long segments)
+constexpr int kCache = 48;  // slots per lane kept in registers (segments up to 3072)
 
 // In-place exclusive scan of a[0..n) (LDS); returns the total to every thread.
 __device__ int block_exscan(int32_t *a, int n, int32_t *wave_tot) {
@@ -119,10 +121,39 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
 
   const int seg = (N + nw - 1) / nw;
   const int i0 = min(N, w * seg), i1 = min(N, i0 + seg);
-  for (int i = i0 + lane; i < i1; i += 64) {
-    const int e = f[i];
-    if (unsigned(e) < unsigned(E)) atomicAdd(&cnt[w * E + e], 1);
-    else bad = 1;
+  // When a wave's segment fits (up to 64*kCache slots), its expert ids are
+  // read once, all loads in flight together, and kept in registers for both
+  // passes; otherwise they are read kBatch per lane at a time in each pass.
+  const bool cached = (i1 - i0) <= 64 * kCache;
+  int cache[kCache];
+  if (cached) {
+#pragma unroll
+    for (int u = 0; u < kCache; ++u) {
+      const int i = i0 + u * 64 + lane;
+      cache[u] = i < i1 ? f[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kCache; ++u) {
+      if (i0 + u * 64 + lane >= i1) continue;
+      const int e = cache[u];
+      if (unsigned(e) < unsigned(E)) atomicAdd(&cnt[w * E + e], 1);
+      else bad = 1;
+    }
+  }
+  for (int b0 = cached ? i1 : i0; b0 < i1; b0 += kBatch * 64) {
+    int ev[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = b0 + u * 64 + lane;
+      ev[u] = i < i1 ? f[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (b0 + u * 64 + lane >= i1) continue;
+      const int e = ev[u];
+      if (unsigned(e) < unsigned(E)) atomicAdd(&cnt[w * E + e], 1);
+      else bad = 1;
+    }
   }
   __syncthreads();
   if (bad) {
@@ -160,19 +191,17 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
   volatile int32_t *base = cnt + w * E;
   const int nbits = E > 1 ? 32 - __clz(E - 1) : 1;
   const uint64_t lt_mask = lane ? (~0ull >> (64 - lane)) : 0ull;
-  for (int b0 = i0; b0 < i1; b0 += 64) {
-    const int i = b0 + lane;
-    const bool valid = i < i1;
-    const int e = valid ? f[i] : 0;
+  // 64 consecutive slots (slot i in this lane, expert e): lanes carrying the
+  // same expert find each other bit by bit, rank = run base + earlier peers.
+  auto rank_step = [&](int i, bool valid, int e) {
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;
       const uint64_t bal = __ballot(valid && bit);
       peers &= bit ? bal : ~bal;
     }
-    int pos = 0;
     if (valid) {
-      pos = base[e] + __popcll(peers & lt_mask);
+      const int pos = base[e] + __popcll(peers & lt_mask);
       order[pos] = i;
       inv_order[i] = pos;
       row_map[pos] = i / K;
@@ -180,6 +209,27 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
     __builtin_amdgcn_wave_barrier();
     if (valid && lane == 63 - __clzll(peers)) base[e] = base[e] + __popcll(peers);
     __builtin_amdgcn_wave_barrier();
+  };
+  if (cached) {
+#pragma unroll
+    for (int u = 0; u < kCache; ++u) {
+      if (i0 + u * 64 >= i1) break;
+      const int i = i0 + u * 64 + lane;
+      rank_step(i, i < i1, cache[u]);
+    }
+  }
+  for (int bb = cached ? i1 : i0; bb < i1; bb += kBatch * 64) {
+    int ev[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = bb + u * 64 + lane;
+      ev[u] = i < i1 ? f[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = bb + u * 64 + lane;
+      rank_step(i, i < i1, ev[u]);
+    }
   }
 
   for (int e = tid; e < E; e += nth) {

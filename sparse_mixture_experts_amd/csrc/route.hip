@@ -33,6 +33,14 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChunk = 64;
 
+constexpr int kXsPad = 8;
+
+// LDS index of staged column k (relative to the block's first column), token t.
+template <int TT>
+__device__ __forceinline__ int xs_at(int k, int t) {
+  return (k / kChunk) * (kChunk * TT + kXsPad) + (k % kChunk) * TT + t;
+}
+
 // (v, e) ranks before (bv, be): larger logit first, ties to the lower index.
 __device__ __forceinline__ bool ranks_before(float v, int e, float bv, int be) {
   return v > bv || (v == bv && e < be);
@@ -62,7 +70,10 @@ __global__ __launch_bounds__(kThreads) void route_partials_kernel(
   constexpr int EO = kThreads / CPB;  // expert octets per block
   constexpr int EPB = EO * 8;         // experts per block
   extern __shared__ float lds[];
-  float *xs = lds;    // [CPB*64][TT] token columns
+  // xs: token columns, [CPB][64 + pad][TT]: each chunk's block is padded by 8
+  // floats so that the chunk lanes of a wave, which read 64 columns apart,
+  // hit different LDS banks.
+  float *xs = lds;
   float *part = lds;  // [CPB][TT][EPB] chunk partials, overlaying xs once it is consumed
 
   const int tid = threadIdx.x, cl = tid / EO, eo = tid % EO;
@@ -73,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void route_partials_kernel(
 
   for (int q = tid; q < (kend - kbeg) * TT; q += kThreads) {
     const int k = q / TT, t = q % TT;
-    xs[q] = t < nt ? load_act<BF16>(x, int64_t(t0 + t) * D + kbeg + k) : 0.0f;
+    xs[xs_at<TT>(k, t)] = t < nt ? load_act<BF16>(x, int64_t(t0 + t) * D + kbeg + k) : 0.0f;
   }
   __syncthreads();
 
@@ -105,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void route_partials_kernel(
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (k8 + u < n) {
-          const float *xk = xs + (kc + k8 + u - kbeg) * TT;
+          const float *xk = xs + xs_at<TT>(kc + k8 + u - kbeg, 0);
 #pragma unroll
           for (int t = 0; t < TT; ++t) {
             const float xv = xk[t];
@@ -227,7 +238,16 @@ bool launch_partials(const void *x, const void *wr, const float *bias, int T, in
   const int C = (D + kChunk - 1) / kChunk;
   const dim3 grid((T + TT - 1) / TT, (E + EPB - 1) / EPB, (C + CPB - 1) / CPB);
   const int full = grid.z == 1;
-  const size_t lds = std::max(size_t(CPB) * kChunk * TT, size_t(CPB) * TT * EPB) * sizeof(float);
+  const size_t lds = std::max(size_t(CPB) * (kChunk * TT + kXsPad), size_t(CPB) * TT * EPB) * sizeof(float);
+  if (lds > 64 * 1024) {
+    // Above the default dynamic-LDS limit (gfx950 has 160 KB per CU): raise it
+    // once per process for this kernel.
+    static const bool raised = [&] {
+      return hipFuncSetAttribute(reinterpret_cast<const void *>(&route_partials_kernel<BF16, TT, CPB>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) == hipSuccess;
+    }();
+    (void)raised;
+  }
   hipLaunchKernelGGL((route_partials_kernel<BF16, TT, CPB>), grid, dim3(kThreads), lds, s, x, wr, bias, T, D,
                      E, full, out);
   return full;
