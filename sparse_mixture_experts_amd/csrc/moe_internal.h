@@ -59,6 +59,11 @@ struct StageMarker {
 
 // Router: topk idx/w for T tokens; scratch holds route_scratch_floats floats.
 int64_t route_scratch_floats(const moe_layer_desc *d, int32_t T);
+// Matrix-core router with exact recomputation of the candidates (large T).
+bool route_mfma_applies(const moe_layer_desc *d, int32_t T);
+int64_t route_mfma_scratch_floats(const moe_layer_desc *d, int32_t T);
+void launch_route_mfma(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router, const float *bias,
+                       int32_t *idx, float *w, float *scratch, void *stream, StageMarker *mk);
 void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router,
                   const float *bias, int32_t *idx, float *w, float *scratch, void *stream,
                   StageMarker *mk = nullptr);

@@ -257,11 +257,17 @@ bool launch_partials(const void *x, const void *wr, const float *bias, int T, in
 
 int64_t route_scratch_floats(const moe_layer_desc *d, int32_t T) {
   const int64_t C = (d->d_model + kChunk - 1) / kChunk;
-  return std::max<int64_t>(int64_t(T) * d->n_experts, C * T * d->n_experts);
+  int64_t n = std::max<int64_t>(int64_t(T) * d->n_experts, C * T * d->n_experts);
+  if (route_mfma_applies(d, T)) n = std::max(n, route_mfma_scratch_floats(d, T));
+  return n;
 }
 
 void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router,
                   const float *bias, int32_t *idx, float *w, float *scratch, void *stream, StageMarker *mk) {
+  if (route_mfma_applies(d, T)) {
+    launch_route_mfma(d, T, x, w_router, bias, idx, w, scratch, stream, mk);
+    return;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int D = d->d_model, E = d->n_experts;
   const int C = (D + kChunk - 1) / kChunk;

@@ -1,0 +1,398 @@
+// route_mfma.hip -- router for many tokens: matrix-core logits, certified by
+// exact recomputation of the few experts that can still reach the top-k.
+//
+// The top-k experts and their order must equal those of the fixed fp32
+// logit order (64-column chunks, each a sequential fma chain from +0, chunk
+// partials added in ascending order, bias last).  Computing every logit that
+// way costs 2*T*d*E fp32 fmas on the vector units.  Instead:
+//   1. the router weight is transposed to [E][d] (its columns become
+//      contiguous rows) and the per-expert squared norms are formed;
+//   2. L~ = x . W + bias on the bf16 matrix cores (exact bf16 products, fp32
+//      sums: two MFMAs per 64-column chunk from zero, chunk results added in
+//      fp32);
+//   3. per token, with B = gamma * ||x_t|| * max_e ||W_e|| + gamma * max|bias|
+//      a bound on |L~ - L| for every expert (Cauchy-Schwarz bounds the sum of
+//      |x_i W_ie|; gamma covers the rounding of both summation orders), every
+//      expert whose true logit can reach the top-k satisfies L~ >= L~_(k) - 2B
+//      (the k-th order statistic moves by at most B).  Only those candidates
+//      are recomputed in the fixed order, and the top-k is chosen among them
+//      exactly (larger logit first, lower index on ties).  When more than 64
+//      experts are candidates (near-ties, e.g. x = 0), every expert of that
+//      token is recomputed.
+// Softmax weights use the recomputed logits of the selected experts; with
+// renormalisation the all-expert denominator cancels, so L~ may stand in for
+// the non-candidates there.  ("MoE Optimization COMPLETE", "Mega Kernel
+// Architecture": router matmul, softmax and top-K all on the GPU.)
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 64;
+constexpr int kMaxCand = 64;
+
+__device__ __forceinline__ bool ranks_before(float v, int e, float bv, int be) {
+  return v > bv || (v == bv && e < be);
+}
+
+// ---- 1. transpose W [d][E] -> WT [E][d] and squared-norm partials ---------
+// Block (eb, kb): experts eb*64.., columns kb*256..; normp[kb][e] = sum of
+// squares of W[kb*256 .. +256][e].
+__global__ __launch_bounds__(kThreads) void router_transpose_kernel(const uint16_t *__restrict__ w, int D, int E,
+                                                                    uint16_t *__restrict__ wt,
+                                                                    float *__restrict__ normp) {
+  __shared__ uint16_t tile[64][256 + 8];
+  const int tid = threadIdx.x;
+  const int e0 = blockIdx.x * 64, k0 = blockIdx.y * 256;
+  {
+    const int k = k0 + tid;  // one router row per thread, 64 experts
+    if (k < D && e0 + 64 <= E && E % 8 == 0) {
+#pragma unroll
+      for (int j8 = 0; j8 < 8; ++j8) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(w + int64_t(k) * E + e0 + j8 * 8);
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          tile[j8 * 8 + 2 * h][tid] = uint16_t(u[h] & 0xffffu);
+          tile[j8 * 8 + 2 * h + 1][tid] = uint16_t(u[h] >> 16);
+        }
+      }
+    } else {
+      for (int j = 0; j < 64; ++j) {
+        const int e = e0 + j;
+        tile[j][tid] = (k < D && e < E) ? w[int64_t(k) * E + e] : uint16_t(0);
+      }
+    }
+  }
+  __syncthreads();
+  const int el = tid / 4, q = tid % 4;  // expert row, quarter of the 256 columns
+  const int e = e0 + el;
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(&tile[el][q * 64 + c * 8]);
+    const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                        bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(f[i], f[i], ss);
+    const int k = k0 + q * 64 + c * 8;
+    if (e < E && k < D) *reinterpret_cast<uint4 *>(wt + int64_t(e) * D + k) = v;
+  }
+  ss += __shfl_xor(ss, 1, kWave);
+  ss += __shfl_xor(ss, 2, kWave);
+  if (q == 0 && e < E) normp[int64_t(blockIdx.y) * E + e] = ss;
+}
+
+// ---- 2. L~ = x . W + bias on MFMA ------------------------------------------
+// Block tile 64 experts x 64 tokens; wave (we, wt) owns 32 x 32 = 2 x 2 MFMA
+// tiles.  Operand A = WT rows (experts), operand B = x rows (tokens); a lane's
+// 4 results are 4 consecutive experts of one token.
+// The blocks of the first token tile also add up the squared-norm partials of
+// their 64 experts: normp[n_kb][e] -> normp[n_kb + 0 * E + e] (the row after
+// the partials).
+__global__ __launch_bounds__(kThreads) void router_mfma_kernel(const uint16_t *__restrict__ x,
+                                                               const uint16_t *__restrict__ wt,
+                                                               const float *__restrict__ bias,
+                                                               float *__restrict__ normp, int n_kb, int T, int D,
+                                                               int E, float *__restrict__ lt) {
+  __shared__ uint16_t sa[64][kChunk + 8];
+  __shared__ uint16_t sb[64][kChunk + 8];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+  const int lr = lane & 15, lg = lane >> 4;
+  const int e0 = blockIdx.x * 64, t0 = blockIdx.y * 64;
+  if (blockIdx.y == 0 && tid < 64 && e0 + tid < E) {
+    float s = 0.f;
+    for (int kb = 0; kb < n_kb; ++kb) s += normp[int64_t(kb) * E + e0 + tid];
+    normp[int64_t(n_kb) * E + e0 + tid] = s;
+  }
+  const int we = wave / 2, wtk = wave % 2;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // staging: thread -> (row tid / 4, 16 columns (tid % 4) * 16) of both tiles
+  const int sr = tid / 4, sc = (tid % 4) * 16;
+  const int ea = min(e0 + sr, E - 1), tb = min(t0 + sr, T - 1);
+  const bool oka = e0 + sr < E, okb = t0 + sr < T;
+  for (int k0 = 0; k0 < D; k0 += kChunk) {
+    const uint4 *pa = reinterpret_cast<const uint4 *>(wt + int64_t(ea) * D + k0 + sc);
+    const uint4 *pb = reinterpret_cast<const uint4 *>(x + int64_t(tb) * D + k0 + sc);
+    const uint4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
+    auto keep = [](bool ok, uint4 v) {
+      return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+    };
+    __syncthreads();
+    *reinterpret_cast<uint4 *>(&sa[sr][sc]) = keep(oka, a0);
+    *reinterpret_cast<uint4 *>(&sa[sr][sc + 8]) = keep(oka, a1);
+    *reinterpret_cast<uint4 *>(&sb[sr][sc]) = keep(okb, b0);
+    *reinterpret_cast<uint4 *>(&sb[sr][sc + 8]) = keep(okb, b1);
+    __syncthreads();
+    bf16x8 av[2][2], bv[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        av[i][j] = *reinterpret_cast<const bf16x8 *>(&sa[we * 32 + i * 16 + lr][lg * 16 + j * 8]);
+        bv[i][j] = *reinterpret_cast<const bf16x8 *>(&sb[wtk * 32 + i * 16 + lr][lg * 16 + j * 8]);
+      }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i][0], bv[j][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i][1], bv[j][1], d, 0, 0, 0);
+        acc[i][j] += d;
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int t = t0 + wtk * 32 + j * 16 + lr;
+      const int eb = e0 + we * 32 + i * 16 + lg * 4;
+      const f32x4 v = acc[i][j];
+      if (t < T) {
+        if (eb + 0 < E) lt[int64_t(t) * E + eb + 0] = v[0] + (bias ? bias[eb + 0] : 0.0f);
+        if (eb + 1 < E) lt[int64_t(t) * E + eb + 1] = v[1] + (bias ? bias[eb + 1] : 0.0f);
+        if (eb + 2 < E) lt[int64_t(t) * E + eb + 2] = v[2] + (bias ? bias[eb + 2] : 0.0f);
+        if (eb + 3 < E) lt[int64_t(t) * E + eb + 3] = v[3] + (bias ? bias[eb + 3] : 0.0f);
+      }
+    }
+}
+
+// ---- 3. candidates, exact recomputation, selection -------------------------
+struct CertArgs {
+  const uint16_t *x, *wt;
+  const float *bias, *lt, *wnorm;
+  int T, D, E, K;
+  float gamma;
+  int32_t *idx_out;
+  float *w_out;
+};
+
+// One wave per token.
+__global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
+  constexpr int kPerLane = kMaxExperts / kWave;
+  __shared__ float s_l[kThreads / kWave][kMaxExperts];   // recomputed logits by list position
+  __shared__ int32_t s_e[kThreads / kWave][kMaxExperts]; // expert id by list position
+  const int wv = threadIdx.x / kWave, lane = lane_id();
+  const int t = blockIdx.x * (kThreads / kWave) + wv;
+  if (t >= a.T) return;
+  const int E = a.E, D = a.D, K = a.K, C = D / kChunk;
+
+  // L~ row, ||x_t||, max_e ||W_e||, max |bias|
+  float lv[kPerLane];
+#pragma unroll
+  for (int m = 0; m < kPerLane; ++m) {
+    const int e = lane + kWave * m;
+    lv[m] = e < E ? a.lt[int64_t(t) * E + e] : -INFINITY;
+  }
+  float xs = 0.f;
+  for (int k = lane * 8; k < D; k += kWave * 8) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(a.x + int64_t(t) * D + k);
+    const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                        bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xs = __builtin_fmaf(f[i], f[i], xs);
+  }
+  xs = wave_sum(xs);
+  float wn = 0.f, bmax = 0.f;
+  for (int e = lane; e < E; e += kWave) {
+    wn = fmaxf(wn, a.wnorm[e]);
+    if (a.bias) bmax = fmaxf(bmax, fabsf(a.bias[e]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    wn = fmaxf(wn, __shfl_xor(wn, o, kWave));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, o, kWave));
+  }
+  const float bound = a.gamma * (sqrtf(xs) * sqrtf(wn) * 1.001f + bmax);
+
+  // k-th largest L~ value
+  float vk = 0.f;
+  {
+    uint32_t taken = 0;
+    for (int j = 0; j < K; ++j) {
+      float bv = -INFINITY;
+      int be = 0x7fffffff;
+#pragma unroll
+      for (int m = 0; m < kPerLane; ++m) {
+        const int e = lane + kWave * m;
+        if (e < E && !((taken >> m) & 1u) && ranks_before(lv[m], e, bv, be)) { bv = lv[m]; be = e; }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, kWave);
+        const int oe = __shfl_xor(be, o, kWave);
+        if (ranks_before(ov, oe, bv, be)) { bv = ov; be = oe; }
+      }
+      if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
+      vk = bv;
+    }
+  }
+  const float thr = vk - 2.0f * bound;
+
+  // candidate list (all experts when too many)
+  int n = 0;
+#pragma unroll
+  for (int m = 0; m < kPerLane; ++m) {
+    const int e = lane + kWave * m;
+    const bool c = e < E && lv[m] >= thr;
+    n += __popcll(__ballot(c));
+  }
+  const bool all = n > kMaxCand;
+  int pos[kPerLane];
+  {
+    int base = 0;
+    const uint64_t lt_mask = lane ? (~0ull >> (64 - lane)) : 0ull;
+#pragma unroll
+    for (int m = 0; m < kPerLane; ++m) {
+      const int e = lane + kWave * m;
+      const bool c = e < E && (all || lv[m] >= thr);
+      const uint64_t b = __ballot(c);
+      pos[m] = c ? base + __popcll(b & lt_mask) : -1;
+      if (c) s_e[wv][pos[m]] = e;
+      base += __popcll(b);
+    }
+    n = base;
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // exact logits of the listed experts: lane = (slot, chunk); slots = 64 / C
+  const int slots = C <= kWave ? kWave / C : 1;
+  const int slot = lane / C, ch = lane % C;
+  uint32_t xw[32];  // this lane's x chunk as packed bf16 (64 values)
+  if (slot < slots) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(a.x + int64_t(t) * D + ch * kChunk + q * 8);
+      xw[4 * q] = v.x; xw[4 * q + 1] = v.y; xw[4 * q + 2] = v.z; xw[4 * q + 3] = v.w;
+    }
+  }
+  for (int p0 = 0; p0 < n; p0 += slots) {
+    const int p = p0 + slot;
+    float part = 0.f;
+    if (slot < slots && p < n) {
+      const int e = s_e[wv][p];
+      const uint16_t *wr = a.wt + int64_t(e) * D + ch * kChunk;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(wr + q * 8);
+        const uint32_t wv4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          part = __builtin_fmaf(bf16_lo(xw[4 * q + h]), bf16_lo(wv4[h]), part);
+          part = __builtin_fmaf(bf16_hi(xw[4 * q + h]), bf16_hi(wv4[h]), part);
+        }
+      }
+    }
+    // chunk partials of each slot added in chunk order
+    float acc = 0.f;
+    for (int c = 0; c < C; ++c) acc = acc + __shfl(part, slot * C + c, kWave);
+    if (slot < slots && ch == 0 && p < n) {
+      const int e = s_e[wv][p];
+      s_l[wv][p] = a.bias ? acc + a.bias[e] : acc;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // top-k over the list
+  int my_e = 0;
+  float my_l = 0.f, top = 0.f;
+  {
+    uint32_t taken = 0;  // bit q: list entry lane + 64*q taken
+    const int nq = (n + kWave - 1) / kWave;
+    for (int j = 0; j < K; ++j) {
+      float bv = -INFINITY;
+      int be = 0x7fffffff;
+      for (int q = 0; q < nq; ++q) {
+        const int p = lane + kWave * q;
+        if (p < n && !((taken >> q) & 1u)) {
+          const float v = s_l[wv][p];
+          const int e = s_e[wv][p];
+          if (ranks_before(v, e, bv, be)) { bv = v; be = e; }
+        }
+      }
+      int bp = -1;
+      for (int q = 0; q < nq; ++q) {
+        const int p = lane + kWave * q;
+        if (p < n && s_e[wv][p] == be) bp = p;
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, kWave);
+        const int oe = __shfl_xor(be, o, kWave);
+        const int op = __shfl_xor(bp, o, kWave);
+        if (ranks_before(ov, oe, bv, be)) { bv = ov; be = oe; bp = op; }
+      }
+      if ((bp & (kWave - 1)) == lane) taken |= 1u << (bp / kWave);
+      if (j == 0) top = bv;
+      if (lane == j) { my_e = be; my_l = bv; }
+    }
+  }
+
+  // softmax: recomputed logits where listed, L~ elsewhere (cancels when renormalised)
+  float z = 0.f;
+#pragma unroll
+  for (int m = 0; m < kPerLane; ++m) {
+    const int e = lane + kWave * m;
+    if (e < E) z += expf((pos[m] >= 0 ? s_l[wv][pos[m]] : lv[m]) - top);
+  }
+  z = wave_sum(z);
+  const float pj = expf(my_l - top) / z;
+  float psum = 0.f;
+  for (int j = 0; j < K; ++j) psum = psum + __shfl(pj, j, kWave);
+  if (lane < K) {
+    a.idx_out[int64_t(t) * K + lane] = my_e;
+    a.w_out[int64_t(t) * K + lane] = pj / psum;
+  }
+}
+
+}  // namespace
+
+bool route_mfma_applies(const moe_layer_desc *d, int32_t T) {
+  return d->act_dtype == MOE_DT_BF16 && d->renormalize && d->d_model % kChunk == 0 &&
+         d->d_model <= kWave * kChunk && T >= 64;
+}
+
+// Scratch: L~ [T][E] f32, then WT [E][D] bf16, then norm partials [D/256][E]
+// f32, each part starting on a 16-byte boundary (offsets in floats).
+static int64_t align4(int64_t v) { return (v + 3) & ~int64_t(3); }
+
+int64_t route_mfma_scratch_floats(const moe_layer_desc *d, int32_t T) {
+  const int64_t E = d->n_experts, D = d->d_model, nkb = (D + 255) / 256;
+  return align4(int64_t(T) * E) + align4((E * D + 1) / 2) + (nkb + 1) * E;
+}
+
+void launch_route_mfma(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router, const float *bias,
+                       int32_t *idx, float *w, float *scratch, void *stream, StageMarker *mk) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int D = d->d_model, E = d->n_experts, nkb = (D + 255) / 256, C = D / kChunk;
+  float *lt = scratch;
+  const int64_t o_wt = align4(int64_t(T) * E), o_np = o_wt + align4((int64_t(E) * D + 1) / 2);
+  uint16_t *wt = reinterpret_cast<uint16_t *>(scratch + o_wt);
+  float *normp = scratch + o_np;
+  hipLaunchKernelGGL(router_transpose_kernel, dim3((E + 63) / 64, nkb), dim3(kThreads), 0, s,
+                     static_cast<const uint16_t *>(w_router), D, E, wt, normp);
+  hipLaunchKernelGGL(router_mfma_kernel, dim3((E + 63) / 64, (T + 63) / 64), dim3(kThreads), 0, s,
+                     static_cast<const uint16_t *>(x), wt, bias, normp, nkb, T, D, E, lt);
+  if (mk) mk->mark("route_mfma");
+  // |L~ - L| <= gamma * S: two MFMAs per chunk counted as 128 sequential
+  // roundings, C chunk additions, and the fixed order's 64 + C + 1 roundings,
+  // with a margin: (256 + 2C) units of 2^-24.
+  const float gamma = float(256 + 2 * C) * 5.9604645e-8f;
+  CertArgs ca{static_cast<const uint16_t *>(x), wt, bias, lt, normp + int64_t(nkb) * E, T, D, E, d->top_k, gamma,
+              idx, w};
+  const int wpb = kThreads / kWave;
+  hipLaunchKernelGGL(router_certify_kernel, dim3((T + wpb - 1) / wpb), dim3(kThreads), 0, s, ca);
+  if (mk) mk->mark("route_certify");
+}
+
+}  // namespace moe

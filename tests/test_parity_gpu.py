@@ -189,3 +189,24 @@ def test_zero_input_gives_zero_output():
     y, idx, _ = g.forward()
     assert torch.all(y == 0).item()
     _layers.clear()  # the cached device layer no longer holds the generated x
+
+
+@pytest.mark.parametrize("T", [9, 96])
+def test_route_exact_ties_and_zero_rows(T):
+    """Duplicated router columns tie exactly and zero rows tie everywhere: the
+    lower expert index must win, on both the small-T and the large-T router."""
+    spec = LayerSpec("ties", T=T, d_model=256, d_ff=64, n_experts=16, top_k=4, seed=31)
+    L = inputs.gen_layer(spec)
+    w = L["w_router"].copy()
+    w[:, 5] = w[:, 2]
+    w[:, 9] = w[:, 2]
+    w[:, 15] = w[:, 0]
+    L["w_router"] = w
+    x = L["x"].copy()
+    x[::7] = 0  # every 7th token: all logits 0
+    L["x"] = x
+    g = GpuLayer(L)
+    idx, wt = g.route()
+    ridx, rw = oracle.route(pins.desc_of(spec), L["x"], L["w_router"], None)
+    assert np.array_equal(idx, ridx)
+    assert np.max(np.abs(wt - rw)) <= 1e-6
