@@ -1,4 +1,4 @@
-// ffn_mfma.hip -- grouped expert GEMMs on the bf16 matrix cores (MFMA).
+// ffn_mfma.hip -- grouped expert GEMMs on the matrix cores (MFMA).
 //
 // The sorted-row route of DS4Server issue #112 ("Current upstream route",
 // "Kernel contract"): workgroups own a tile of one expert's sorted rows; the
@@ -8,29 +8,34 @@
 // expert means each expert's weights are read and dequantised once per tile
 // ("SwitchGLU: grouped-expert Metal kernels", section "What").
 //
-// gfx950 mapping.  One v_mfma_f32_16x16x32_bf16 multiplies a 16x32 weight
-// block (operand A: 16 weight rows n) by a 32x16 activation block (operand B:
-// 16 token rows m).  A lane holds row/column l%16 and the 8 reduction elements
-// 8*(l/16)..+8 of its operand; its 4 results are rows n = 4*(l/16)+i of
-// column m = l%16, i.e. 4 consecutive outputs of one token row, which makes
-// the stores contiguous.
+// gfx950 mapping.  One v_mfma_f32_16x16x32_{f16,bf16} multiplies a 16x32
+// weight block (operand A: 16 weight rows n) by a 32x16 activation block
+// (operand B: 16 token rows m).  A lane holds row/column l%16 and the 8
+// reduction elements 8*(l/16)..+8 of its operand; its 4 results are rows
+// n = 4*(l/16)+i of column m = l%16, i.e. 4 consecutive outputs of one token
+// row, which makes the stores contiguous.
 //
 // Weight operands come straight from global memory into registers (every
-// weight element is used by exactly one lane), one 64-element group ahead of
-// their use: for affine 4-bit weights a lane reads 2 words = 16 codes of one
-// quantisation group and turns each word into 8 bf16 values 128+q with one
-// shift and one and-or per pair (the bf16 with exponent 2^7 and the code as
-// its low mantissa bits is exactly 128+q).  The pairs come out as (q_j,
-// q_{j+4}), so the activations are staged in LDS with the same order inside
-// every 8-element block.  Since
-//   sum_k x_k (s q_k + b) = s * sum_k x_k (128 + q_k) + (b - 128 s) * sum_k x_k
-// per 64-element group, two MFMAs give D = sum x (128+q) for the group and
-// the fp32 epilogue of the group adds s*D + (b - 128 s)*X with X the group sum
-// of the activations.  Dense bf16 weights go to the MFMA unchanged.
+// weight element is used by exactly one lane), several 64-element groups
+// ahead of their use.  Affine 4-bit weights are dequantised in registers to
+// fp16 with packed math: for each pair of codes the word is shifted and
+// masked into two fp16 values 1024+q (exponent 2^10, the code in the low
+// mantissa bits), 1024 is subtracted exactly, and one v_pk_fma_f16 gives
+// s*q + b for both.  The pairs come out as (q_j, q_{j+4}) of a word, so the
+// activations are staged in LDS with the same order inside every 8-element
+// block.  Activations (x or h, bf16) are converted to fp16 when staged.
 //
-// Activations, group sums and scales are staged in LDS in slabs of 128
-// reduction elements, double buffered: the global loads of slab s+1 are in
-// flight in registers while slab s is multiplied.
+// fp16 has the range of neither bf16 nor the scales, so every staged row gets
+// an exponent: activation rows whose largest |value| in the slab reaches 2^15
+// are scaled down by a power of two, as are weight rows whose |s|*15 + |b|
+// does; a slab in which any row was scaled multiplies the MFMA results by the
+// exact power-of-two product before accumulating (the common case, no row
+// scaled, accumulates in the MFMA directly).  Dense bf16 weights go to a bf16
+// MFMA unchanged.
+//
+// Activations and scales are staged in LDS in slabs of 128 reduction
+// elements, double buffered: the global loads of slab s+1 are in flight in
+// registers while slab s is multiplied.
 #include "device_common.h"
 #include "moe_internal.h"
 
@@ -38,6 +43,8 @@ namespace moe {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -47,24 +54,29 @@ constexpr int kNT = 4;                     // 16-row weight tiles per wave
 constexpr int kNRows = kNW * kNT * 16;     // weight rows per block (256)
 constexpr int kKS = 128;                   // reduction elements per slab
 constexpr int kGPS = kKS / kGroup;         // groups per slab (2)
-constexpr int kLdsRow = kKS + 8;           // padded LDS row (bf16): spreads rows over banks
+constexpr int kLdsRow = kKS + 8;           // padded LDS row (16-bit elements): spreads rows over banks
 static_assert(kNRows == kThreads, "one scale row per thread");
 
-__device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-
-// 8 codes of a word -> 8 bf16 (128 + q) in the order q0,q4,q1,q5,q2,q6,q3,q7.
-__device__ __forceinline__ bf16x8 q4_word_to_bf16(uint32_t w) {
-  u32x4 r;
-  r[0] = (w & 0x000f000fu) | 0x43004300u;
-  r[1] = ((w >> 4) & 0x000f000fu) | 0x43004300u;
-  r[2] = ((w >> 8) & 0x000f000fu) | 0x43004300u;
-  r[3] = ((w >> 12) & 0x000f000fu) | 0x43004300u;
-  return __builtin_bit_cast(bf16x8, r);
+__device__ __forceinline__ f32x4 mfma_f16(const f16x8 &a, const f16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// bf16 elements e0..e7 -> e0,e4,e1,e5,e2,e6,e3,e7 (the order of q4_word_to_bf16).
+// 8 codes of a word -> 8 fp16 weights s*q + b in the order q0,q4,q1,q5,q2,q6,q3,q7.
+__device__ __forceinline__ f16x8 q4_word_to_f16(uint32_t w, h2 s2, h2 b2) {
+  const h2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  h2 r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const h2 q = __builtin_bit_cast(h2, ((w >> (4 * j)) & 0x000f000fu) | 0x64006400u) - k1024;
+    r[j] = __builtin_elementwise_fma(q, s2, b2);
+  }
+  return __builtin_bit_cast(f16x8, r);
+}
+
+// 16-bit elements e0..e7 -> e0,e4,e1,e5,e2,e6,e3,e7 (the order of q4_word_to_f16).
 __device__ __forceinline__ uint4 permute8(uint4 v) {
   uint4 r;
   r.x = (v.x & 0xffffu) | (v.z << 16);
@@ -74,9 +86,30 @@ __device__ __forceinline__ uint4 permute8(uint4 v) {
   return r;
 }
 
-__device__ __forceinline__ float sum8_bf16(uint4 v) {
-  return ((bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y))) +
-         ((bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w)));
+// Power-of-two exponent that brings a nonnegative magnitude below 2^15.
+__device__ __forceinline__ int f16_shift(float mag) {
+  const int ex = int((__float_as_uint(mag) >> 23) & 0xffu) - 127;  // floor(log2(mag)) for normal mag
+  return ex >= 15 ? ex - 14 : 0;
+}
+__device__ __forceinline__ float pow2(int e) { return __uint_as_float(uint32_t(127 + e) << 23); }
+
+// Eight bf16 values scaled by 2^-sh as packed fp16 (two per word).
+__device__ __forceinline__ uint4 bf16x8_to_f16(uint4 v, int sh) {
+  const float m = pow2(-sh);
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const h2 p = {(_Float16)(bf16_lo(u[i]) * m), (_Float16)(bf16_hi(u[i]) * m)};
+    o[i] = __builtin_bit_cast(uint32_t, p);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__device__ __forceinline__ float absmax8_bf16(uint4 v) {
+  const float a = fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))), fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y))));
+  const float b = fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))), fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w))));
+  return fmaxf(a, b);
 }
 
 struct GemmArgs {
@@ -97,9 +130,10 @@ struct GemmArgs {
 
 template <int RB>
 struct Slab {
-  uint16_t a[RB * 16][kLdsRow];   // activations (bf16 bits), q4 order inside 8-blocks
-  float xg[kGPS][RB * 16];        // group sums of the activations
-  float2 sb[kGPS][kNRows];        // (scale, bias - 128*scale) per weight row and group
+  uint16_t a[RB * 16][kLdsRow];   // activations: bf16 (dense) or fp16 in q4 order (q4)
+  uint2 sb[kGPS][kNRows];         // q4: (s,s) and (b,b) as packed fp16, per weight row and group
+  int8_t ash[RB * 16];            // q4: activation row shifts
+  int8_t wsh[kNRows];             // q4: weight row shifts
 };
 
 // Per-lane weight data of one group: q4 -> one uint2 per tile; dense -> 2 uint4.
@@ -111,10 +145,10 @@ template <>
 struct WGroup<false> { uint4 w[kNT][2]; };
 
 // GATEUP: gate/up projection with SwiGLU epilogue writing h, else down
-// projection writing fp32 y rows.  Q4: affine 4-bit weights, else dense bf16.
-// RB: 16-row blocks per tile.  Each wave owns kNT weight tiles of 16 rows; for
-// gate/up the first kNT/2 are gate rows and the last kNT/2 the up rows of the
-// same output columns.
+// projection writing fp32 y rows.  Q4: affine 4-bit weights (fp16 MFMA),
+// else dense bf16 (bf16 MFMA).  RB: 16-row blocks per tile.  Each wave owns
+// kNT weight tiles of 16 rows; for gate/up the first kNT/2 are gate rows and
+// the last kNT/2 the up rows of the same output columns.
 template <bool GATEUP, bool Q4, int RB>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   constexpr int NTH = GATEUP ? kNT / 2 : kNT;  // output-column tiles per wave
@@ -234,26 +268,44 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
       }
     }
   };
-  auto stage_write = [&](int buf) {
+  // Writes the staged slab to LDS buffer `buf`; returns nonzero when a row of
+  // it needed a power-of-two shift to fit fp16.
+  auto stage_write = [&](int buf) -> int {
     Slab<RB> &S = sm[buf];
-    float xs = 0.f;
-#pragma unroll
-    for (int p = 0; p < PPT; ++p) {
-      if constexpr (Q4) xs += sum8_bf16(stg[p]);
-      *reinterpret_cast<uint4 *>(&S.a[sm_row][(sj * PPT + p) * 8]) = Q4 ? permute8(stg[p]) : stg[p];
-    }
+    int flag = 0;
     if constexpr (Q4) {
-      // group sum over the 8 / PPT threads of one group, fixed tree order
+      float mx = 0.f;
 #pragma unroll
-      for (int o = 1; o < 8 / PPT; o <<= 1) xs += __shfl_xor(xs, o, kWave);
-      const int kk = sj * PPT * 8;
-      if (kk % kGroup == 0) S.xg[kk / kGroup][sm_row] = xs;
+      for (int p = 0; p < PPT; ++p) mx = fmaxf(mx, absmax8_bf16(stg[p]));
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+      const int sh = f16_shift(mx);
+#pragma unroll
+      for (int p = 0; p < PPT; ++p)
+        *reinterpret_cast<uint4 *>(&S.a[sm_row][(sj * PPT + p) * 8]) = permute8(bf16x8_to_f16(stg[p], sh));
+      if (sj == 0) S.ash[sm_row] = int8_t(sh);
+      float sv[kGPS], bv[kGPS], wm = 0.f;
 #pragma unroll
       for (int g = 0; g < kGPS; ++g) {
-        const float sc = bf16_bits_to_f32(sraw[g][0]), bi = bf16_bits_to_f32(sraw[g][1]);
-        S.sb[g][tid] = make_float2(sc, __builtin_fmaf(-128.0f, sc, bi));
+        sv[g] = bf16_bits_to_f32(sraw[g][0]);
+        bv[g] = bf16_bits_to_f32(sraw[g][1]);
+        wm = fmaxf(wm, __builtin_fmaf(15.0f, fabsf(sv[g]), fabsf(bv[g])));
       }
+      const int wsh = f16_shift(wm);
+      const float m = pow2(-wsh);
+#pragma unroll
+      for (int g = 0; g < kGPS; ++g) {
+        const _Float16 sh16 = (_Float16)(sv[g] * m), bh16 = (_Float16)(bv[g] * m);
+        const h2 s2 = {sh16, sh16}, b2 = {bh16, bh16};
+        S.sb[g][tid] = make_uint2(__builtin_bit_cast(uint32_t, s2), __builtin_bit_cast(uint32_t, b2));
+      }
+      S.wsh[tid] = int8_t(wsh);
+      flag = sh | wsh;
+    } else {
+#pragma unroll
+      for (int p = 0; p < PPT; ++p) *reinterpret_cast<uint4 *>(&S.a[sm_row][(sj * PPT + p) * 8]) = stg[p];
     }
+    return flag;
   };
 
   f32x4 acc[kNT][RB];
@@ -262,42 +314,61 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) acc[nt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // A slab in which some row was shifted: the accumulators are brought to the
+  // slab's scale (times 2^-(activation shift + weight shift) of each output)
+  // before its groups accumulate, and back (times 2^+shift) after, both exact.
+  auto rescale = [&](const Slab<RB> &S, int sign) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int ash = S.ash[rb * 16 + lr];
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[nt][rb][i] *= pow2(sign * (ash + S.wsh[(wave * kNT + nt) * 16 + lg * 4 + i]));
+    }
+  };
+
   auto compute_group = [&](const Slab<RB> &S, int gi, const WGroup<Q4> &wg) {
-    bf16x8 bx[2][RB];
+    if constexpr (Q4) {
+      f16x8 bx[2][RB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      if (rb < rb_count)
+      for (int rb = 0; rb < RB; ++rb)
+        if (rb < rb_count)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          bx[j][rb] = *reinterpret_cast<const bf16x8 *>(&S.a[rb * 16 + lr][gi * kGroup + lg * 16 + j * 8]);
+          for (int j = 0; j < 2; ++j)
+            bx[j][rb] = *reinterpret_cast<const f16x8 *>(&S.a[rb * 16 + lr][gi * kGroup + lg * 16 + j * 8]);
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-      bf16x8 aw[2];
-      if constexpr (Q4) {
-        aw[0] = q4_word_to_bf16(wg.w[nt].x);
-        aw[1] = q4_word_to_bf16(wg.w[nt].y);
-        float2 sbv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sbv[i] = S.sb[gi][(wave * kNT + nt) * 16 + lg * 4 + i];
+      for (int nt = 0; nt < kNT; ++nt) {
+        const uint2 sbv = S.sb[gi][(wave * kNT + nt) * 16 + lr];
+        const h2 s2 = __builtin_bit_cast(h2, sbv.x), b2 = __builtin_bit_cast(h2, sbv.y);
+        const f16x8 aw0 = q4_word_to_f16(wg.w[nt].x, s2, b2);
+        const f16x8 aw1 = q4_word_to_f16(wg.w[nt].y, s2, b2);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           if (rb < rb_count) {
-            f32x4 d = mfma16(aw[0], bx[0][rb], f32x4{0.f, 0.f, 0.f, 0.f});
-            d = mfma16(aw[1], bx[1][rb], d);
-            const float xs = S.xg[gi][rb * 16 + lr];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[nt][rb][i] = __builtin_fmaf(sbv[i].y, xs, __builtin_fmaf(sbv[i].x, d[i], acc[nt][rb][i]));
+            acc[nt][rb] = mfma_f16(aw0, bx[0][rb], acc[nt][rb]);
+            acc[nt][rb] = mfma_f16(aw1, bx[1][rb], acc[nt][rb]);
           }
         }
-      } else {
-        aw[0] = __builtin_bit_cast(bf16x8, wg.w[nt][0]);
-        aw[1] = __builtin_bit_cast(bf16x8, wg.w[nt][1]);
+      }
+    } else {
+      bf16x8 bx[2][RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        if (rb < rb_count)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            bx[j][rb] = *reinterpret_cast<const bf16x8 *>(&S.a[rb * 16 + lr][gi * kGroup + lg * 16 + j * 8]);
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        const bf16x8 aw0 = __builtin_bit_cast(bf16x8, wg.w[nt][0]);
+        const bf16x8 aw1 = __builtin_bit_cast(bf16x8, wg.w[nt][1]);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           if (rb < rb_count) {
-            acc[nt][rb] = mfma16(aw[0], bx[0][rb], acc[nt][rb]);
-            acc[nt][rb] = mfma16(aw[1], bx[1][rb], acc[nt][rb]);
+            acc[nt][rb] = mfma_bf16(aw0, bx[0][rb], acc[nt][rb]);
+            acc[nt][rb] = mfma_bf16(aw1, bx[1][rb], acc[nt][rb]);
           }
         }
       }
@@ -308,28 +379,29 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   // Weights run PD groups ahead in a ring of register buffers (4-bit groups
   // are small, so more of them are kept in flight); the activation slab s+1
   // is loaded during the first group of slab s and written to the other LDS
-  // buffer after its last group.
+  // buffer after its last group.  Steps past the last group (when G is not a
+  // multiple of PD) only keep the barrier pattern; their loads are clamped
+  // repeats and their compute is skipped.
   constexpr int PD = Q4 ? 4 : 2;
   static_assert(PD % kGPS == 0, "ring covers whole slabs");
   WGroup<Q4> wb[PD];
   stage_load(0);
-  stage_write(0);
+  const int f0 = stage_write(0);
 #pragma unroll
   for (int u = 0; u < PD; ++u) load_group(u, wb[u]);
-  __syncthreads();
-  // Steps past the last group (when G is not a multiple of PD) only keep the
-  // barrier pattern; their loads are clamped repeats and their compute is skipped.
+  int slow = __syncthreads_or(f0);
   for (int g0 = 0; g0 < G; g0 += PD) {
 #pragma unroll
     for (int u = 0; u < PD; ++u) {
       const int g = g0 + u;
       const int s = g / kGPS, gi = g % kGPS, buf = s & 1;
       if (gi == 0) stage_load(s + 1);
+      if (Q4 && slow && gi == 0 && col_ok) rescale(sm[buf], -1);
       if (col_ok && g < G) compute_group(sm[buf], gi, wb[u]);
       load_group(g + PD, wb[u]);
       if (gi == kGPS - 1) {
-        stage_write(buf ^ 1);
-        __syncthreads();
+        if (Q4 && slow && col_ok) rescale(sm[buf], +1);
+        slow = __syncthreads_or(stage_write(buf ^ 1));
       }
     }
   }
