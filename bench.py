@@ -82,7 +82,12 @@ def expert_bytes(spec) -> int:
 
 
 def accounting(spec, touched: int):
-    """Algorithmic bytes and FLOPs of one forward, and per kernel."""
+    """Algorithmic bytes and FLOPs of one forward, and per kernel.
+
+    Bytes count each tensor a kernel must read or write once: weights of the
+    experts the batch touches (plus shared experts), activations, the routed
+    intermediate h, the f32 expert outputs and the small index tables.
+    """
     T, D, F, E, K, S = spec.T, spec.d_model, spec.d_ff, spec.n_experts, spec.top_k, spec.n_shared
     esz = 2 if spec.act == "bf16" else 4
     N, R = T * K, T * K + S * T
@@ -90,18 +95,24 @@ def accounting(spec, touched: int):
     gu_frac, down_frac = 2 / 3, 1 / 3
     w_touched = (touched + S) * eb
     router = D * E * esz
+    gateup = {"bound": "hbm", "bytes": int(w_touched * gu_frac) + T * D * esz + R * F * esz,
+              "flops": 2 * R * 2 * D * F}
+    down = {"bound": "hbm", "bytes": int(w_touched * down_frac) + R * F * esz + R * D * 4, "flops": 2 * R * D * F}
     acc = {
         "layer_bytes": w_touched + router + T * D * esz + T * D * esz,
         "expert_flops": 2 * R * 3 * D * F,
         "router_flops": 2 * T * D * E,
         "kernels": {
+            # VALU router: canonical-order logits (fp32 FMA chains), then top-k
             "route_logits": {"bound": "alu", "flops": 2 * T * D * E, "bytes": T * D * esz + router + T * E * 4},
             "route_select": {"bound": "hbm", "bytes": T * E * 4 + N * 8},
+            # matrix-core router: W transposed (read + write + read), x read, logits written
+            "route_mfma": {"bound": "hbm", "bytes": 3 * router + T * D * esz + T * E * 4, "flops": 2 * T * D * E},
+            # certification: logits and x read, the k winners written
+            "route_certify": {"bound": "hbm", "bytes": T * E * 4 + T * D * esz + N * 8},
             "dispatch": {"bound": "hbm", "bytes": N * 4 * 4},
-            "gateup_gemv": {"bound": "hbm", "bytes": int(w_touched * gu_frac) + T * D * esz + R * F * esz},
-            "down_gemv": {"bound": "hbm", "bytes": int(w_touched * down_frac) + R * F * esz + R * D * 4},
-            "gateup_mfma": {"bound": "hbm", "bytes": int(w_touched * gu_frac) + T * D * esz + R * F * esz},
-            "down_mfma": {"bound": "hbm", "bytes": int(w_touched * down_frac) + R * F * esz + R * D * 4},
+            "gateup_gemv": gateup, "down_gemv": down,
+            "gateup_mfma": gateup, "down_mfma": down,
             "combine": {"bound": "hbm", "bytes": R * D * 4 + T * D * esz + N * 8},
         },
     }
@@ -208,8 +219,73 @@ def run_config(name, steps, warmup, use_graph, hip):
     return res
 
 
+def path_dtype(spec) -> str:
+    """Arithmetic type of the expert contractions (they dominate the step).
+
+    4-bit weights are expanded to fp16 and the bf16 activations are staged as
+    fp16 scaled by powers of two, so those products run on fp16 matrix cores;
+    dense bf16 layers use bf16 matrix cores; f32 layers use fp32 FMA.  All of
+    them accumulate in fp32.
+    """
+    if spec.act != "bf16":
+        return "f32"
+    return "fp16" if spec.wfmt == "q4" else "bf16"
+
+
+STAGE_SOURCES = {
+    "route_logits": "route.hip", "route_select": "route.hip", "route_mfma": "route_mfma.hip",
+    "route_certify": "route_mfma.hip", "dispatch": "dispatch.hip", "gateup_gemv": "ffn_gemv.hip",
+    "down_gemv": "ffn_gemv.hip", "gateup_mfma": "ffn_mfma.hip", "down_mfma": "ffn_mfma.hip",
+    "combine": "combine.hip",
+}
+
+
+def kernel_sources_digest(kernel: str) -> str:
+    """SHA-256 over the source of the stage's kernels and the shared device
+    headers (stamps the traffic counters taken for that stage)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in [STAGE_SOURCES[kernel], "device_common.h", "moe_internal.h"]:
+        with open(os.path.join(ROOT, "sparse_mixture_experts_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(config: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the FETCH_SIZE/WRITE_SIZE counter
+    summary stored for `config`, each counter scaled by what it reads for a
+    copy kernel of known size.  None when no summary exists or the kernel
+    sources changed after the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    k = rec.get("kernels", {}).get(kernel)
+    if k is None or k.get("sources_sha256") != kernel_sources_digest(kernel):
+        return None
+    cal = rec["copy_calibration"]
+    f_fetch = cal["fetch_kib"] * 1024.0 / cal["bytes"]
+    f_write = cal["write_kib"] * 1024.0 / cal["bytes"]
+    return int(k["fetch_kib"] * 1024.0 / f_fetch + k["write_kib"] * 1024.0 / f_write)
+
+
+def calibrate_copy(mib: int):
+    """Copy kernel of known size for scaling the traffic counters: 3 launches
+    of dst.copy_(src) over `mib` MiB."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+
+
 def roofline(res):
     km = res["kernel_ms"]
+    traffic = measured_traffic(res["name"], max(km, key=km.get))
     dom = max(km, key=km.get)
     kacc = res["acc"]["kernels"].get(dom)
     t = km[dom] / 1e3
@@ -219,11 +295,11 @@ def roofline(res):
     if kacc["bound"] == "alu":
         a = kacc["flops"] / t / 1e12
         return {"kernel": dom, "bound": "alu", "achieved": round(a, 3), "peak": VALU_F32_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(a / VALU_F32_PEAK_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(a / VALU_F32_PEAK_TFLOPS, 4), "traffic": traffic,
                 "avg_launch_us": round(km[dom] * 1e3, 2)}
     a = kacc["bytes"] / t / 1e9
     return {"kernel": dom, "bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None, "avg_launch_us": round(km[dom] * 1e3, 2),
+            "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic, "avg_launch_us": round(km[dom] * 1e3, 2),
             "algorithmic_bytes_per_launch": kacc["bytes"]}
 
 
@@ -260,6 +336,8 @@ def main():
     ap.add_argument("--graph", action="store_true", help="replay captured HIP graphs in the timed loop")
     ap.add_argument("--cpu-tokens", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a device copy of MIB MiB (scale for the HBM traffic counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -270,6 +348,9 @@ def main():
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     from sparse_mixture_experts_amd import moe
     moe.load()
     hip = Hip()
@@ -294,7 +375,7 @@ def main():
     line = {
         "metric": METRIC, "value": round(head["rows_per_s"], 1), "unit": "routed rows/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": path_dtype(spec),
         "data": "synthetic (seeded N(0,1/fan_in) weights quantised to affine 4-bit g64, N(0,1) bf16 x)",
         "config": {"workload": workload_name(spec), "T": spec.T, "d_model": spec.d_model, "d_ff": spec.d_ff,
                    "n_experts": spec.n_experts, "top_k": spec.top_k, "n_shared": spec.n_shared,

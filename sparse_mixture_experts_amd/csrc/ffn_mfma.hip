@@ -382,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   // buffer after its last group.  Steps past the last group (when G is not a
   // multiple of PD) only keep the barrier pattern; their loads are clamped
   // repeats and their compute is skipped.
-  constexpr int PD = Q4 ? 4 : 2;
+  constexpr int PD = 2;
   static_assert(PD % kGPS == 0, "ring covers whole slabs");
   WGroup<Q4> wb[PD];
   stage_load(0);
