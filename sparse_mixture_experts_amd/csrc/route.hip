@@ -256,8 +256,12 @@ bool launch_partials(const void *x, const void *wr, const float *bias, int T, in
 }  // namespace
 
 int64_t route_scratch_floats(const moe_layer_desc *d, int32_t T) {
+  // Covers every T' <= T: the one-token kernel keeps all chunk partials on
+  // chip when C <= 2; otherwise it writes C partials per (token, expert),
+  // which happens below 64 tokens, or at any T when C > 32.
   const int64_t C = (d->d_model + kChunk - 1) / kChunk;
-  int64_t n = std::max<int64_t>(int64_t(T) * d->n_experts, C * T * d->n_experts);
+  const int64_t t_split = C <= 2 ? 0 : (C <= 32 ? std::min<int64_t>(T, 63) : int64_t(T));
+  int64_t n = std::max<int64_t>(int64_t(T) * d->n_experts, C * t_split * d->n_experts);
   if (route_mfma_applies(d, T)) n = std::max(n, route_mfma_scratch_floats(d, T));
   return n;
 }
