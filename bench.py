@@ -111,6 +111,8 @@ def accounting(spec, touched: int):
             # certification: logits and x read, the k winners written
             "route_certify": {"bound": "hbm", "bytes": T * E * 4 + T * D * esz + N * 8},
             "dispatch": {"bound": "hbm", "bytes": N * 4 * 4},
+            # fp16 copy of x for the 4-bit GEMMs: x read, copy and token exponents written
+            "x_f16": {"bound": "hbm", "bytes": 2 * T * D * esz + T},
             "gateup_gemv": gateup, "down_gemv": down,
             "gateup_mfma": gateup, "down_mfma": down,
             "combine": {"bound": "hbm", "bytes": R * D * 4 + T * D * esz + N * 8},
@@ -234,7 +236,7 @@ def path_dtype(spec) -> str:
 
 STAGE_SOURCES = {
     "route_logits": "route.hip", "route_select": "route.hip", "route_mfma": "route_mfma.hip",
-    "route_certify": "route_mfma.hip", "dispatch": "dispatch.hip", "gateup_gemv": "ffn_gemv.hip",
+    "route_certify": "route_mfma.hip", "dispatch": "dispatch.hip", "x_f16": "ffn_mfma.hip", "gateup_gemv": "ffn_gemv.hip",
     "down_gemv": "ffn_gemv.hip", "gateup_mfma": "ffn_mfma.hip", "down_mfma": "ffn_mfma.hip",
     "combine": "combine.hip",
 }

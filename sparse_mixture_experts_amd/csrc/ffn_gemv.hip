@@ -238,12 +238,13 @@ void launch_gemv(const moe_layer_desc *d, int32_t T, const void *x, const int32_
 
 void launch_expert_ffn(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
                        const moe_weights *w, const int32_t *counters, const PlanItem *act_items,
-                       const PlanItem *tiles, int64_t max_tiles, void *h, float *y_sorted,
+                       const PlanItem *tiles, int64_t max_tiles, const FfnScratch &sc, float *y_sorted,
                        void *stream, StageMarker *mk) {
   if (use_mfma(d)) {
-    launch_expert_ffn_mfma(d, T, x, row_map, w, counters, tiles, max_tiles, h, y_sorted, stream, mk);
+    launch_expert_ffn_mfma(d, T, x, row_map, w, counters, tiles, max_tiles, sc, y_sorted, stream, mk);
     return;
   }
+  void *h = sc.h;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d->w_format == MOE_WF_AFFINE_Q4)
     launch_gemv<true, W_Q4>(d, T, x, row_map, w, counters, act_items, h, y_sorted, s, mk);

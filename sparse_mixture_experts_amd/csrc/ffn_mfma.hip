@@ -16,26 +16,32 @@
 // row, which makes the stores contiguous.
 //
 // Weight operands come straight from global memory into registers (every
-// weight element is used by exactly one lane), several 64-element groups
-// ahead of their use.  Affine 4-bit weights are dequantised in registers to
-// fp16 with packed math: for each pair of codes the word is shifted and
-// masked into two fp16 values 1024+q (exponent 2^10, the code in the low
-// mantissa bits), 1024 is subtracted exactly, and one v_pk_fma_f16 gives
-// s*q + b for both.  The pairs come out as (q_j, q_{j+4}) of a word, so the
-// activations are staged in LDS with the same order inside every 8-element
-// block.  Activations (x or h, bf16) are converted to fp16 when staged.
+// weight element is used by exactly one lane), a group ahead of their use.
+// Affine 4-bit weights are dequantised in registers to fp16 with packed
+// math: for each pair of codes the word is shifted and masked into two fp16
+// values 1024+q (exponent 2^10, the code in the low mantissa bits), 1024 is
+// subtracted exactly, and one v_pk_fma_f16 gives s*q + b for both.  The pairs
+// come out as (q_j, q_{j+4}) of a word, so the activations are stored with
+// the same order inside every 8-element block.
 //
-// fp16 has the range of neither bf16 nor the scales, so every staged row gets
-// an exponent: activation rows whose largest |value| in the slab reaches 2^15
-// are scaled down by a power of two, as are weight rows whose |s|*15 + |b|
-// does; a slab in which any row was scaled multiplies the MFMA results by the
-// exact power-of-two product before accumulating (the common case, no row
-// scaled, accumulates in the MFMA directly).  Dense bf16 weights go to a bf16
-// MFMA unchanged.
+// 4-bit layers keep their activations in fp16 end to end: a small kernel
+// converts x once per token (not once per expert tile) and the gate/up
+// epilogue writes h as fp16, both already in that permuted order, so the
+// GEMMs' LDS staging is a plain copy.  fp16 has the range of neither bf16
+// nor the scales, so values carry power-of-two exponents, used only where
+// needed: one per token row of x (undone in the gate/up epilogue), one per
+// (row, 128-column block) of h, and one per (weight row, slab) for scales
+// whose |s|*15 + |b| is at least 2^15 or below 2^-10.  The main loop runs
+// without any rescaling; if a slab of the tile carries an h or weight
+// exponent, the tile starts over in a loop that brings the accumulators to
+// each such slab's scale and back (exact power-of-two multiplies).  Dense
+// bf16 weights go to a bf16 MFMA unchanged.
 //
 // Activations and scales are staged in LDS in slabs of 128 reduction
 // elements, double buffered: the global loads of slab s+1 are in flight in
 // registers while slab s is multiplied.
+#include <type_traits>
+
 #include "device_common.h"
 #include "moe_internal.h"
 
@@ -54,8 +60,11 @@ constexpr int kNT = 4;                     // 16-row weight tiles per wave
 constexpr int kNRows = kNW * kNT * 16;     // weight rows per block (256)
 constexpr int kKS = 128;                   // reduction elements per slab
 constexpr int kGPS = kKS / kGroup;         // groups per slab (2)
+constexpr int kSteps = kKS / 32;           // MFMA reduction steps per slab (4)
+constexpr int kPieces = kKS / 8;           // 16-byte activation pieces per row and slab (16)
 constexpr int kLdsRow = kKS + 8;           // padded LDS row (16-bit elements): spreads rows over banks
 static_assert(kNRows == kThreads, "one scale row per thread");
+static_assert(kKS == 32 * 4, "a lane's 4 reduction blocks of 32 span the slab");
 
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -86,10 +95,15 @@ __device__ __forceinline__ uint4 permute8(uint4 v) {
   return r;
 }
 
-// Power-of-two exponent that brings a nonnegative magnitude below 2^15.
+// Power-of-two exponent e for a nonnegative magnitude, nonzero only when
+// needed: mag * 2^-e lies below 2^15 (fp16 range with headroom), and
+// magnitudes below 2^-10 (whose small elements would fall into fp16
+// subnormals) are brought to [1, 2).  Zero needs no exponent.
 __device__ __forceinline__ int f16_shift(float mag) {
   const int ex = int((__float_as_uint(mag) >> 23) & 0xffu) - 127;  // floor(log2(mag)) for normal mag
-  return ex >= 15 ? ex - 14 : 0;
+  if (ex >= 15) return ex - 14;
+  if (mag > 0.f && ex < -10) return max(ex, -100);
+  return 0;
 }
 __device__ __forceinline__ float pow2(int e) { return __uint_as_float(uint32_t(127 + e) << 23); }
 
@@ -112,8 +126,31 @@ __device__ __forceinline__ float absmax8_bf16(uint4 v) {
   return fmaxf(a, b);
 }
 
+// x [T][D] bf16 -> fp16 copy for the 4-bit GEMMs.  One wave per token row:
+// the row's largest |x| gives its exponent e (f16_shift); the row is stored
+// as fp16 x * 2^-e in the staging order of q4_word_to_f16 (every 8-element
+// block permuted).  bf16 -> fp16 is exact for values in fp16's normal range.
+__global__ __launch_bounds__(256) void act_f16_kernel(const uint16_t *x, int T, int D, uint16_t *x16,
+                                                      int8_t *xsh) {
+  const int t = blockIdx.x * (256 / kWave) + int(threadIdx.x) / kWave, lane = lane_id();
+  if (t >= T) return;  // whole waves
+  const uint4 *src = reinterpret_cast<const uint4 *>(x + int64_t(t) * D);
+  uint4 *dst = reinterpret_cast<uint4 *>(x16 + int64_t(t) * D);
+  const int P = D / 8;
+  float mx = 0.f;
+  for (int p = lane; p < P; p += kWave) mx = fmaxf(mx, absmax8_bf16(src[p]));
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  const int sh = f16_shift(mx);
+  for (int p = lane; p < P; p += kWave) dst[p] = permute8(bf16x8_to_f16(src[p], sh));
+  if (lane == 0) xsh[t] = int8_t(sh);
+}
+
 struct GemmArgs {
-  const void *act;          // gate/up: x [T][D]; down: h [rows][F] (bf16)
+  const void *act;          // gate/up: x [T][K] (bf16; fp16 copy for 4-bit); down: h [rows][K]
+  const int8_t *act_sh;     // 4-bit: gate/up token exponents [T]; down h exponents [rows][nblk]
+  int8_t *out_sh;           // 4-bit gate/up: h exponents [rows][nblk]
+  int nblk;                 // h exponent blocks per row
   const int32_t *row_map;   // gate/up only
   int T, N, K;              // token count, routed rows, reduction length
   int n_out;                // output columns of the projection (F for gate/up, D for down)
@@ -125,37 +162,50 @@ struct GemmArgs {
   const uint16_t *s1, *b1;
   const int32_t *counters;  // [1] = number of tiles
   const PlanItem *tiles;
-  void *out;                // gate/up: h bf16 [rows][F]; down: y fp32 [rows][D]
+  void *out;                // gate/up: h [rows][F] (bf16, or fp16 for 4-bit); down: y fp32 [rows][D]
 };
 
 template <int RB>
 struct Slab {
   uint16_t a[RB * 16][kLdsRow];   // activations: bf16 (dense) or fp16 in q4 order (q4)
   uint2 sb[kGPS][kNRows];         // q4: (s,s) and (b,b) as packed fp16, per weight row and group
-  int8_t ash[RB * 16];            // q4: activation row shifts
-  int8_t wsh[kNRows];             // q4: weight row shifts
+  int8_t ash[RB * 16];            // q4 down: h exponents of the slab's rows
+  int8_t wsh[kNRows];             // q4: weight row exponents
 };
 
-// Per-lane weight data of one group: q4 -> one uint2 per tile; dense -> 2 uint4.
+// Per-lane weight data of one slab: 4-bit -> one uint4 (4 words, 32 codes)
+// per tile; dense -> four uint4 (32 bf16) per tile.
 template <bool Q4>
-struct WGroup;
+struct WSlab;
 template <>
-struct WGroup<true> { uint2 w[kNT]; };
+struct WSlab<true> { uint4 w[kNT]; };
 template <>
-struct WGroup<false> { uint4 w[kNT][2]; };
+struct WSlab<false> { uint4 w[kNT][kSteps]; };
 
 // GATEUP: gate/up projection with SwiGLU epilogue writing h, else down
 // projection writing fp32 y rows.  Q4: affine 4-bit weights (fp16 MFMA),
 // else dense bf16 (bf16 MFMA).  RB: 16-row blocks per tile.  Each wave owns
 // kNT weight tiles of 16 rows; for gate/up the first kNT/2 are gate rows and
 // the last kNT/2 the up rows of the same output columns.
+//
+// Reduction order inside a slab of 128: lane (lr, lg) of an operand holds
+// the 32 slab elements 32*lg .. 32*lg+31 (4-bit: words 4*lg .. 4*lg+3 of the
+// row's slab, one contiguous 16-byte load), and MFMA step j multiplies the 8
+// elements 32*lg + 8*j .. +7 of both operands.  Both operands use the same
+// order, so every step sums over a fixed quarter of the slab and the four
+// steps cover it.  Lanes lg = 0, 1 hold the slab's first group, lg = 2, 3 its
+// second.
 template <bool GATEUP, bool Q4, int RB>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
-  constexpr int NTH = GATEUP ? kNT / 2 : kNT;  // output-column tiles per wave
-  constexpr int TPR = 16 / RB;                 // staging threads per activation row
-  constexpr int PPT = RB;                      // 8-element pieces per staging thread
-  static_assert(RB * 16 * TPR == kThreads, "staging covers the slab");
+  constexpr int NTH = GATEUP ? kNT / 2 : kNT;   // output-column tiles per wave
+  constexpr int kRowsPerPass = kThreads / kPieces;  // activation rows staged per pass (16)
+  constexpr int PPT = RB * 16 / kRowsPerPass;     // staging passes (pieces per thread)
+  static_assert(PPT * kRowsPerPass == RB * 16, "staging covers the slab");
+  static_assert(!GATEUP || kNW * NTH * 16 == kHBlock, "a gate/up block writes one h exponent block");
+  static_assert(kKS == kHBlock, "a down slab reads one h exponent block");
   __shared__ Slab<RB> sm[2];
+  __shared__ float rmax[GATEUP && Q4 ? kNW : 1][RB * 16];  // gate/up 4-bit epilogue: row maxima per wave
+  __shared__ int8_t rsh[RB * 16];                         // gate/up 4-bit: token exponents of the rows
 
   // XCD-aware order.  Workgroups go to the 8 XCDs round-robin by linear id;
   // the W = tiles * column-blocks work items of this call are cut into 8
@@ -178,10 +228,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   const PlanItem tile = a.tiles[tile_id];
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
-  const int lr = lane & 15, lg = lane >> 4;  // operand row / reduction block of this lane
+  const int lr = lane & 15, lg = lane >> 4;  // operand row / reduction quarter of this lane
   const int K = a.K, KW = K / 8, G = K / kGroup;
   const int nslab = (K + kKS - 1) / kKS;
-  const int rb_count = (tile.rows + 15) / 16;
   const int col0 = (bx * kNW + wave) * NTH * 16;  // first output column of this wave
   const bool col_ok = col0 < a.n_out;              // whole wave in or out (n_out % 64 == 0)
 
@@ -201,41 +250,60 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   const int col_c = col_ok ? col0 : a.n_out - NTH * 16;  // in-range columns for idle waves
 
   // This lane's weight row (operand A row lr) of each tile.
-  int64_t wr[kNT];
   const void *wp[kNT];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
     const bool up = GATEUP && nt >= NTH;
-    wr[nt] = wrow_of(col_c + (nt % NTH) * 16 + lr, up);
-    wp[nt] = wsrc(up);
+    const int64_t wr = wrow_of(col_c + (nt % NTH) * 16 + lr, up);
+    wp[nt] = Q4 ? static_cast<const void *>(static_cast<const uint32_t *>(wsrc(up)) + wr * KW)
+                : static_cast<const void *>(static_cast<const uint16_t *>(wsrc(up)) + wr * K);
   }
-  auto load_group = [&](int g, WGroup<Q4> &dst) {
-    g = min(g, G - 1);
+  // Slab s of this lane's rows.  The last slab may hold a single group
+  // (K = 64 mod 128): its second half is read from a clamped address and
+  // multiplied by zero scales (4-bit) or zeroed activations (dense).
+  auto load_slab = [&](int s, WSlab<Q4> &dst) {
+    s = min(s, nslab - 1);
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
       if constexpr (Q4) {
-        dst.w[nt] = *reinterpret_cast<const uint2 *>(static_cast<const uint32_t *>(wp[nt]) + wr[nt] * KW + g * 8 + lg * 2);
+        const int w = min(s * (kKS / 8) + lg * 4, KW - 4);
+        dst.w[nt] = *reinterpret_cast<const uint4 *>(static_cast<const uint32_t *>(wp[nt]) + w);
       } else {
-        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(wp[nt]) + wr[nt] * K + g * kGroup + lg * 16);
-        dst.w[nt][0] = p[0];
-        dst.w[nt][1] = p[1];
+#pragma unroll
+        for (int j = 0; j < kSteps; ++j) {
+          const int k = min(s * kKS + lg * 32 + j * 8, K - 8);
+          dst.w[nt][j] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(wp[nt]) + k);
+        }
       }
     }
   };
 
-  // ---- staging: thread -> (row m, pieces j*PPT..+PPT of the slab) ----
-  const int sm_row = tid / TPR, sj = tid % TPR;
-  int64_t src_row = -1;
-  if (sm_row < tile.rows) {
-    const int p = tile.row0 + sm_row;
-    if (!GATEUP) {
-      src_row = p;
-    } else {
-      const int tok = p < a.N ? a.row_map[p] : (p - a.N) % a.T;
-      src_row = unsigned(tok) < unsigned(a.T) ? tok : -1;
+  // ---- staging: pass p of thread tid -> row p*16 + tid/16, piece tid%16 ----
+  // (16 consecutive lanes read one row's 256 contiguous bytes of the slab.)
+  const int piece = tid % kPieces;
+  int src_row[PPT];       // source row, -1 past the tile (or for an invalid token)
+  int64_t src_off[PPT];   // element offset of a valid source row
+#pragma unroll
+  for (int p = 0; p < PPT; ++p) {
+    const int m = p * kRowsPerPass + tid / kPieces;
+    int r = -1;
+    if (m < tile.rows) {
+      const int q = tile.row0 + m;
+      if (!GATEUP) {
+        r = q;
+      } else {
+        const int tok = q < a.N ? a.row_map[q] : (q - a.N) % a.T;
+        r = unsigned(tok) < unsigned(a.T) ? tok : -1;
+      }
+    }
+    src_row[p] = r;
+    // Rows past the tile (and invalid tokens) read a valid row; their results
+    // are never stored.
+    src_off[p] = int64_t(r >= 0 ? r : (GATEUP ? 0 : tile.row0)) * K;
+    if constexpr (GATEUP && Q4) {
+      if (piece == 0) rsh[m] = a.act_sh[src_off[p] / K];  // visible after the first barrier
     }
   }
-  const int64_t src_row_c = src_row >= 0 ? src_row : (GATEUP ? 0 : tile.row0);
   // scale row of this thread (one weight row of the block per thread)
   const int s_w = tid / (kNT * 16), s_nt = (tid / 16) % kNT, s_r = tid % 16;
   const int s_col = (bx * kNW + s_w) * NTH * 16 + (s_nt % NTH) * 16 + s_r;
@@ -245,16 +313,21 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
 
   uint4 stg[PPT];
   uint16_t sraw[kGPS][2];
+  int stg_sh[PPT];  // q4 down: h exponents of the staged rows' slab
   auto stage_load = [&](int s) {
     s = min(s, nslab - 1);
-    const int k0 = s * kKS;
+    const int k = s * kKS + piece * 8;
 #pragma unroll
     for (int p = 0; p < PPT; ++p) {
-      const int k = k0 + (sj * PPT + p) * 8;
-      const uint4 v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.act) + src_row_c * K +
+      const uint4 v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.act) + src_off[p] +
                                                        min(k, K - 8));
-      const bool ok = src_row >= 0 && k < K;
-      stg[p] = make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+      if constexpr (Q4) {
+        stg[p] = v;  // pieces past K meet zero scales
+      } else {
+        const bool ok = src_row[p] >= 0 && k < K;
+        stg[p] = make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+      }
+      if constexpr (Q4 && !GATEUP) stg_sh[p] = a.act_sh[(src_off[p] / K) * a.nblk + s];
     }
     if constexpr (Q4) {
 #pragma unroll
@@ -268,22 +341,22 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
       }
     }
   };
-  // Writes the staged slab to LDS buffer `buf`; returns nonzero when a row of
-  // it needed a power-of-two shift to fit fp16.
+  // Writes the staged slab to LDS buffer `buf`; returns nonzero when the slab
+  // carries an exponent (h rows of the down projection, or weight rows).
   auto stage_write = [&](int buf) -> int {
     Slab<RB> &S = sm[buf];
     int flag = 0;
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) {
+      const int m = p * kRowsPerPass + tid / kPieces;
+      *reinterpret_cast<uint4 *>(&S.a[m][piece * 8]) = stg[p];
+      if constexpr (Q4 && !GATEUP) {
+        const int sh = src_row[p] >= 0 ? stg_sh[p] : 0;
+        if (piece == 0) S.ash[m] = int8_t(sh);
+        flag |= sh;
+      }
+    }
     if constexpr (Q4) {
-      float mx = 0.f;
-#pragma unroll
-      for (int p = 0; p < PPT; ++p) mx = fmaxf(mx, absmax8_bf16(stg[p]));
-#pragma unroll
-      for (int o = 1; o < TPR; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-      const int sh = f16_shift(mx);
-#pragma unroll
-      for (int p = 0; p < PPT; ++p)
-        *reinterpret_cast<uint4 *>(&S.a[sm_row][(sj * PPT + p) * 8]) = permute8(bf16x8_to_f16(stg[p], sh));
-      if (sj == 0) S.ash[sm_row] = int8_t(sh);
       float sv[kGPS], bv[kGPS], wm = 0.f;
 #pragma unroll
       for (int g = 0; g < kGPS; ++g) {
@@ -300,27 +373,27 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
         S.sb[g][tid] = make_uint2(__builtin_bit_cast(uint32_t, s2), __builtin_bit_cast(uint32_t, b2));
       }
       S.wsh[tid] = int8_t(wsh);
-      flag = sh | wsh;
-    } else {
-#pragma unroll
-      for (int p = 0; p < PPT; ++p) *reinterpret_cast<uint4 *>(&S.a[sm_row][(sj * PPT + p) * 8]) = stg[p];
+      flag |= wsh;
     }
     return flag;
   };
 
   f32x4 acc[kNT][RB];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int nt = 0; nt < kNT; ++nt)
+    for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) acc[nt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rb = 0; rb < RB; ++rb) acc[nt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  zero_acc();
 
-  // A slab in which some row was shifted: the accumulators are brought to the
-  // slab's scale (times 2^-(activation shift + weight shift) of each output)
-  // before its groups accumulate, and back (times 2^+shift) after, both exact.
+  // A slab that carries exponents: the accumulators are brought to the slab's
+  // scale (times 2^-(h exponent + weight exponent) of each output) before its
+  // steps accumulate, and back after, both exact.
   auto rescale = [&](const Slab<RB> &S, int sign) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const int ash = S.ash[rb * 16 + lr];
+      const int ash = GATEUP ? 0 : int(S.ash[rb * 16 + lr]);
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
@@ -329,81 +402,148 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     }
   };
 
-  auto compute_group = [&](const Slab<RB> &S, int gi, const WGroup<Q4> &wg) {
+  // One slab of every tile of this wave, in kSteps MFMA steps.  Row blocks
+  // past the tile's rows are multiplied too (their results are never
+  // stored), which keeps the body free of branches.
+  auto compute_slab = [&](const Slab<RB> &S, const WSlab<Q4> &ws) {
     if constexpr (Q4) {
-      f16x8 bx[2][RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        if (rb < rb_count)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            bx[j][rb] = *reinterpret_cast<const f16x8 *>(&S.a[rb * 16 + lr][gi * kGroup + lg * 16 + j * 8]);
+      h2 s2[kNT], b2[kNT];
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
-        const uint2 sbv = S.sb[gi][(wave * kNT + nt) * 16 + lr];
-        const h2 s2 = __builtin_bit_cast(h2, sbv.x), b2 = __builtin_bit_cast(h2, sbv.y);
-        const f16x8 aw0 = q4_word_to_f16(wg.w[nt].x, s2, b2);
-        const f16x8 aw1 = q4_word_to_f16(wg.w[nt].y, s2, b2);
+        const uint2 v = S.sb[lg >> 1][(wave * kNT + nt) * 16 + lr];
+        s2[nt] = __builtin_bit_cast(h2, v.x);
+        b2[nt] = __builtin_bit_cast(h2, v.y);
+      }
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          if (rb < rb_count) {
-            acc[nt][rb] = mfma_f16(aw0, bx[0][rb], acc[nt][rb]);
-            acc[nt][rb] = mfma_f16(aw1, bx[1][rb], acc[nt][rb]);
-          }
+      for (int j = 0; j < kSteps; ++j) {
+        f16x8 bx[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          bx[rb] = *reinterpret_cast<const f16x8 *>(&S.a[rb * 16 + lr][lg * 32 + j * 8]);
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+          const uint32_t wd = j == 0 ? ws.w[nt].x : j == 1 ? ws.w[nt].y : j == 2 ? ws.w[nt].z : ws.w[nt].w;
+          const f16x8 aw = q4_word_to_f16(wd, s2[nt], b2[nt]);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) acc[nt][rb] = mfma_f16(aw, bx[rb], acc[nt][rb]);
         }
       }
     } else {
-      bf16x8 bx[2][RB];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        if (rb < rb_count)
+      for (int j = 0; j < kSteps; ++j) {
+        bf16x8 bx[RB];
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            bx[j][rb] = *reinterpret_cast<const bf16x8 *>(&S.a[rb * 16 + lr][gi * kGroup + lg * 16 + j * 8]);
+        for (int rb = 0; rb < RB; ++rb)
+          bx[rb] = *reinterpret_cast<const bf16x8 *>(&S.a[rb * 16 + lr][lg * 32 + j * 8]);
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        const bf16x8 aw0 = __builtin_bit_cast(bf16x8, wg.w[nt][0]);
-        const bf16x8 aw1 = __builtin_bit_cast(bf16x8, wg.w[nt][1]);
+        for (int nt = 0; nt < kNT; ++nt) {
+          const bf16x8 aw = __builtin_bit_cast(bf16x8, ws.w[nt][j]);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          if (rb < rb_count) {
-            acc[nt][rb] = mfma_bf16(aw0, bx[0][rb], acc[nt][rb]);
-            acc[nt][rb] = mfma_bf16(aw1, bx[1][rb], acc[nt][rb]);
-          }
+          for (int rb = 0; rb < RB; ++rb) acc[nt][rb] = mfma_bf16(aw, bx[rb], acc[nt][rb]);
         }
       }
     }
   };
 
   // ---- pipelined main loop ----
-  // Weights run PD groups ahead in a ring of register buffers (4-bit groups
-  // are small, so more of them are kept in flight); the activation slab s+1
-  // is loaded during the first group of slab s and written to the other LDS
-  // buffer after its last group.  Steps past the last group (when G is not a
-  // multiple of PD) only keep the barrier pattern; their loads are clamped
-  // repeats and their compute is skipped.
-  constexpr int PD = 2;
-  static_assert(PD % kGPS == 0, "ring covers whole slabs");
-  WGroup<Q4> wb[PD];
-  stage_load(0);
-  const int f0 = stage_write(0);
+  // Weights run PDS slabs ahead in a ring of register buffers (two slabs for
+  // 4-bit weights; dense slabs are four times larger, so one); the
+  // activation slab s+1 is loaded before slab s is multiplied and written to
+  // the other LDS buffer after it, and the barrier there also reports
+  // whether slab s+1 carries exponents.  Steps past the last slab only keep
+  // the barrier pattern; their loads are clamped repeats.  SLOW = false: no
+  // rescaling, and the loop gives up (returns true) before the first slab
+  // with exponents; SLOW = true: rescales around every such slab.
+  constexpr int PDS = Q4 ? 2 : 1;
+  auto run = [&](auto slow_tag) __attribute__((always_inline)) -> bool {
+    constexpr bool SLOW = decltype(slow_tag)::value;
+    WSlab<Q4> wb[PDS];
+    stage_load(0);
+    const int f0 = stage_write(0);
 #pragma unroll
-  for (int u = 0; u < PD; ++u) load_group(u, wb[u]);
-  int slow = __syncthreads_or(f0);
-  for (int g0 = 0; g0 < G; g0 += PD) {
+    for (int u = 0; u < PDS; ++u) load_slab(u, wb[u]);
+    int flag = __syncthreads_or(f0);
+    if (!SLOW && flag) return true;
+    for (int s0 = 0; s0 < nslab; s0 += PDS) {
 #pragma unroll
-    for (int u = 0; u < PD; ++u) {
-      const int g = g0 + u;
-      const int s = g / kGPS, gi = g % kGPS, buf = s & 1;
-      if (gi == 0) stage_load(s + 1);
-      if (Q4 && slow && gi == 0 && col_ok) rescale(sm[buf], -1);
-      if (col_ok && g < G) compute_group(sm[buf], gi, wb[u]);
-      load_group(g + PD, wb[u]);
-      if (gi == kGPS - 1) {
-        if (Q4 && slow && col_ok) rescale(sm[buf], +1);
-        slow = __syncthreads_or(stage_write(buf ^ 1));
+      for (int u = 0; u < PDS; ++u) {
+        const int s = s0 + u, buf = s & 1;
+        stage_load(s + 1);
+        if (SLOW && flag && col_ok) rescale(sm[buf], -1);
+        if (col_ok && s < nslab) compute_slab(sm[buf], wb[u]);
+        load_slab(s + PDS, wb[u]);
+        if (SLOW && flag && col_ok) rescale(sm[buf], +1);
+        flag = __syncthreads_or(stage_write(buf ^ 1));
+        if (!SLOW && flag) return true;
       }
     }
+    return false;
+  };
+  if (run(std::false_type{})) {
+    if constexpr (Q4) {
+      // Every wave left the fast loop at the same barrier, after its last
+      // read of the slab buffers.
+      zero_acc();
+      run(std::true_type{});
+    }
+  }
+
+  if constexpr (GATEUP && Q4) {
+    // SwiGLU on the true gate/up values (the token exponent undone), then h as
+    // fp16 with one exponent per (row, this block's 128 columns), in the
+    // permuted staging order.  Lane (lr, lg) holds columns c..c+3,
+    // c = col0 + nt*16 + 4*lg, of row m = rb*16 + lr: the lanes lg and lg^1
+    // hold the two halves of an 8-column block and swap a pair of values so
+    // that each stores 4 contiguous permuted elements.
+    float hv[RB][NTH][4];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float xs = pow2(rsh[rb * 16 + lr]);
+      float mx = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NTH; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = swiglu(acc[nt][rb][i] * xs, acc[nt + NTH][rb][i] * xs, a.round_ops);
+          hv[rb][nt][i] = col_ok ? v : 0.f;
+          mx = fmaxf(mx, fabsf(hv[rb][nt][i]));
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      if (lg == 0) rmax[wave][rb * 16 + lr] = mx;
+    }
+    __syncthreads();
+    if (!col_ok) return;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int m = rb * 16 + lr;
+      float mx = rmax[0][m];
+#pragma unroll
+      for (int w = 1; w < kNW; ++w) mx = fmaxf(mx, rmax[w][m]);
+      const int sh = f16_shift(mx);
+      const float sc = pow2(-sh);
+      const int64_t row = tile.row0 + m;
+#pragma unroll
+      for (int nt = 0; nt < NTH; ++nt) {
+        const h2 v01 = {(_Float16)(hv[rb][nt][0] * sc), (_Float16)(hv[rb][nt][1] * sc)};
+        const h2 v23 = {(_Float16)(hv[rb][nt][2] * sc), (_Float16)(hv[rb][nt][3] * sc)};
+        const uint32_t u01 = __builtin_bit_cast(uint32_t, v01), u23 = __builtin_bit_cast(uint32_t, v23);
+        const bool hi = lg & 1;  // this lane holds elements 4..7 of the block
+        const uint32_t recv = __shfl_xor(hi ? u01 : u23, 16, kWave);
+        uint2 o;
+        if (!hi) {  // e0,e4,e1,e5 (recv = e4,e5)
+          o.x = (u01 & 0xffffu) | (recv << 16);
+          o.y = (u01 >> 16) | (recv & 0xffff0000u);
+        } else {    // e2,e6,e3,e7 (recv = e2,e3; own e4,e5 | e6,e7)
+          o.x = (recv & 0xffffu) | (u23 << 16);
+          o.y = (recv >> 16) | (u23 & 0xffff0000u);
+        }
+        const int c = col0 + nt * 16 + lg * 4;
+        if (m < tile.rows) *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + row * a.n_out + c) = o;
+      }
+      if (wave == 0 && lg == 0 && m < tile.rows) a.out_sh[row * a.nblk + bx] = int8_t(sh);
+    }
+    return;
   }
   if (!col_ok) return;
 
@@ -455,16 +595,24 @@ int plan_tile_rows(const moe_layer_desc *d, int32_t T) {
 
 void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
                             const moe_weights *w, const int32_t *counters, const PlanItem *tiles,
-                            int64_t max_tiles, void *h, float *y_sorted, void *stream, StageMarker *mk) {
+                            int64_t max_tiles, const FfnScratch &sc, float *y_sorted, void *stream,
+                            StageMarker *mk) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool q4 = d->w_format == MOE_WF_AFFINE_Q4;
   const int tr = plan_tile_rows(d, T);
+  const int nblk = (d->d_ff + kHBlock - 1) / kHBlock;
+  if (q4) {
+    hipLaunchKernelGGL(act_f16_kernel, dim3((T + 3) / 4), dim3(256), 0, s, static_cast<const uint16_t *>(x), T,
+                       d->d_model, static_cast<uint16_t *>(sc.x16), sc.xsh);
+    if (mk) mk->mark("x_f16");
+  }
   const moe_proj &pg = d->gate_up_fused ? w->gate_up : w->gate;
-  GemmArgs gu{x, row_map, T, T * d->top_k, d->d_model, d->d_ff, d->gate_up_fused, d->swiglu_round_bf16,
+  GemmArgs gu{q4 ? sc.x16 : x, sc.xsh, sc.hsh, nblk, row_map, T, T * d->top_k, d->d_model, d->d_ff,
+              d->gate_up_fused, d->swiglu_round_bf16,
               pg.w, static_cast<const uint16_t *>(pg.scales), static_cast<const uint16_t *>(pg.biases),
               w->up.w, static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases),
-              counters, tiles, h};
-  GemmArgs dn{h, nullptr, T, T * d->top_k, d->d_ff, d->d_model, 0, 0,
+              counters, tiles, sc.h};
+  GemmArgs dn{sc.h, sc.hsh, nullptr, nblk, nullptr, T, T * d->top_k, d->d_ff, d->d_model, 0, 0,
               w->down.w, static_cast<const uint16_t *>(w->down.scales), static_cast<const uint16_t *>(w->down.biases),
               nullptr, nullptr, nullptr, counters, tiles, y_sorted};
   if (tr == 16) {

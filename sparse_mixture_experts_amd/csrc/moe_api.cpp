@@ -22,6 +22,10 @@ T *at(void *ws, size_t off) {
   return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
 }
 
+FfnScratch ffn_scratch(void *ws, const Workspace &L) {
+  return FfnScratch{at<void>(ws, L.h), at<int8_t>(ws, L.hsh), at<void>(ws, L.x16), at<int8_t>(ws, L.xsh)};
+}
+
 int check_ws(const moe_layer_desc *d, int32_t T, const void *ws, size_t ws_bytes, Workspace *out) {
   *out = workspace_layout(d, T);
   if (validate_ptr(ws)) return MOE_E_INVALID;
@@ -100,7 +104,7 @@ int moe_expert_ffn(const moe_layer_desc *desc, int32_t T, const void *x, const i
   launch_plan(desc, T, expert_off, at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items),
               at<PlanItem>(ws, L.tiles), stream);
   launch_expert_ffn(desc, T, x, row_map, w, at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items),
-                    at<PlanItem>(ws, L.tiles), L.max_tiles, at<void>(ws, L.h), y_sorted, stream);
+                    at<PlanItem>(ws, L.tiles), L.max_tiles, ffn_scratch(ws, L), y_sorted, stream);
   return hip_status();
 }
 
@@ -140,7 +144,7 @@ static int forward_impl(const moe_layer_desc *desc, int32_t T, const void *x, co
                   stream, mk);
   launch_expert_ffn(desc, T, x, at<int32_t>(ws, L.row_map), w, at<int32_t>(ws, L.counters),
                     at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles), L.max_tiles,
-                    at<void>(ws, L.h), at<float>(ws, L.y_sorted), stream, mk);
+                    ffn_scratch(ws, L), at<float>(ws, L.y_sorted), stream, mk);
   launch_combine(desc, T, at<float>(ws, L.y_sorted), at<int32_t>(ws, L.inv_order), wt, y, out_dtype,
                  stream, mk);
   return hip_status();

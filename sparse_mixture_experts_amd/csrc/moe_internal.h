@@ -42,6 +42,8 @@ struct Workspace {
   size_t act_items;                   // [E+S] PlanItem
   size_t tiles;                       // [max_tiles] PlanItem
   size_t h;                           // [N+S*T][d_ff] h_bytes
+  size_t hsh;                         // [N+S*T][ceil(d_ff/128)] int8 (4-bit layers)
+  size_t x16, xsh;                    // [T][d_model] fp16, [T] int8 (4-bit layers)
   size_t y_sorted;                    // [N+S*T][d_model] f32
   size_t total;
   int64_t max_tiles;
@@ -78,10 +80,22 @@ void launch_dispatch(const moe_layer_desc *d, int32_t T, const int32_t *idx, int
 void launch_plan(const moe_layer_desc *d, int32_t T, const int32_t *expert_off, int32_t *counters,
                  PlanItem *act_items, PlanItem *tiles, void *stream);
 
+// Intermediate buffers of the expert FFN (all in the workspace).  h holds
+// the SwiGLU rows; on the 4-bit matrix-core path h is fp16 with a power-of-two
+// exponent per (row, 128-column block) in hsh, and x16/xsh hold the fp16 copy
+// of x with one exponent per token.
+struct FfnScratch {
+  void *h;
+  int8_t *hsh;
+  void *x16;
+  int8_t *xsh;
+};
+constexpr int kHBlock = 128;  // h columns per exponent block
+
 // Expert FFN over the plan: y_sorted rows for all routed and shared rows.
 void launch_expert_ffn(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
                        const moe_weights *w, const int32_t *counters, const PlanItem *act_items,
-                       const PlanItem *tiles, int64_t max_tiles, void *h, float *y_sorted,
+                       const PlanItem *tiles, int64_t max_tiles, const FfnScratch &sc, float *y_sorted,
                        void *stream, StageMarker *mk = nullptr);
 
 // Row-tile height of the work plan for this layer and token count, and
@@ -90,7 +104,8 @@ int plan_tile_rows(const moe_layer_desc *d, int32_t T);
 bool use_mfma(const moe_layer_desc *d);
 void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
                             const moe_weights *w, const int32_t *counters, const PlanItem *tiles,
-                            int64_t max_tiles, void *h, float *y_sorted, void *stream, StageMarker *mk);
+                            int64_t max_tiles, const FfnScratch &sc, float *y_sorted, void *stream,
+                            StageMarker *mk);
 
 // Combine.
 void launch_combine(const moe_layer_desc *d, int32_t T, const float *y_sorted,

@@ -100,6 +100,10 @@ Workspace workspace_layout(const moe_layer_desc *d, int32_t T) {
   ws.act_items = take(size_t(E + S) * sizeof(PlanItem));
   ws.tiles = take(size_t(ws.max_tiles) * sizeof(PlanItem));
   ws.h = take(size_t(rows) * d->d_ff * h_bytes(d));
+  const bool q4 = d->w_format == MOE_WF_AFFINE_Q4;
+  ws.hsh = take(q4 ? size_t(rows) * ((d->d_ff + kHBlock - 1) / kHBlock) : 0);
+  ws.x16 = take(q4 ? size_t(T) * d->d_model * 2 : 0);
+  ws.xsh = take(q4 ? size_t(T) : 0);
   ws.y_sorted = take(size_t(rows) * d->d_model * 4);
   ws.total = o;
   return ws;
