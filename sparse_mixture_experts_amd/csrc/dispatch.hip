@@ -18,6 +18,8 @@
 //      lanes, which is exactly the stable order.
 // The same kernel emits the work plan the expert kernels consume: the list of
 // experts with rows (plus the shared experts) and the list of row tiles.
+#include <algorithm>
+
 #include "device_common.h"
 #include "moe_internal.h"
 
@@ -27,6 +29,13 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kBatch = 8;   // slots per lane loaded together (long segments)
 constexpr int kCache = 48;  // slots per lane kept in registers (segments up to 3072)
+// Up to this many slots the whole dispatch runs in one workgroup; above it,
+// in workgroups of dispatch_segment(N) slots (at most 256 workgroups).
+constexpr int kSingleBlockMax = 4096;
+inline int64_t dispatch_segment(int64_t N) {
+  const int64_t per = (N + 255) / 256;
+  return std::max<int64_t>(1024, (per + 255) / 256 * 256);
+}
 
 // In-place exclusive scan of a[0..n) (LDS); returns the total to every thread.
 __device__ int block_exscan(int32_t *a, int n, int32_t *wave_tot) {
@@ -98,6 +107,126 @@ __device__ void emit_plan(const int32_t *off, const int32_t *cnt, int32_t *act_f
   }
 }
 
+// One wave's segment [i0, i1) of the flat slots: its expert ids, read once
+// and kept in registers when the segment fits (all loads in flight
+// together), otherwise re-read kBatch per lane at a time by each pass.
+struct Segment {
+  int i0, i1;
+  bool cached;
+  int cache[kCache];
+};
+
+__device__ __forceinline__ void seg_load(const int32_t *__restrict__ f, int i0, int i1, Segment &sg) {
+  const int lane = threadIdx.x & 63;
+  sg.i0 = i0;
+  sg.i1 = i1;
+  sg.cached = (i1 - i0) <= 64 * kCache;
+  if (sg.cached) {
+#pragma unroll
+    for (int u = 0; u < kCache; ++u) {
+      const int i = i0 + u * 64 + lane;
+      sg.cache[u] = i < i1 ? f[i] : 0;
+    }
+  }
+}
+
+// Adds the segment's expert counts into cnt[E] (LDS, integer atomics, so the
+// result does not depend on their order); sets *bad for an id outside [0, E).
+__device__ __forceinline__ void seg_count(const int32_t *__restrict__ f, const Segment &sg, int E, int32_t *cnt,
+                                          int32_t *bad) {
+  const int lane = threadIdx.x & 63;
+  if (sg.cached) {
+#pragma unroll
+    for (int u = 0; u < kCache; ++u) {
+      if (sg.i0 + u * 64 + lane >= sg.i1) continue;
+      const int e = sg.cache[u];
+      if (unsigned(e) < unsigned(E)) atomicAdd(&cnt[e], 1);
+      else *bad = 1;
+    }
+    return;
+  }
+  for (int b0 = sg.i0; b0 < sg.i1; b0 += kBatch * 64) {
+    int ev[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = b0 + u * 64 + lane;
+      ev[u] = i < sg.i1 ? f[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (b0 + u * 64 + lane >= sg.i1) continue;
+      const int e = ev[u];
+      if (unsigned(e) < unsigned(E)) atomicAdd(&cnt[e], 1);
+      else *bad = 1;
+    }
+  }
+}
+
+// Stable positions of the segment's slots, given base[e] = the first position
+// of this wave's run of expert e (LDS, advanced in place).  The wave walks
+// its segment in slot order, 64 slots at a time; lanes that carry the same
+// expert find each other with ballots over the bits of the expert id, and a
+// slot's position = base + number of earlier equal lanes.
+__device__ __forceinline__ void seg_rank(const int32_t *__restrict__ f, const Segment &sg, int K, int E,
+                                         volatile int32_t *base, int32_t *__restrict__ order,
+                                         int32_t *__restrict__ inv_order, int32_t *__restrict__ row_map) {
+  const int lane = threadIdx.x & 63;
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 1;
+  const uint64_t lt_mask = lane ? (~0ull >> (64 - lane)) : 0ull;
+  auto rank_step = [&](int i, bool valid, int e) {
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bal = __ballot(valid && bit);
+      peers &= bit ? bal : ~bal;
+    }
+    if (valid) {
+      const int pos = base[e] + __popcll(peers & lt_mask);
+      order[pos] = i;
+      inv_order[i] = pos;
+      row_map[pos] = i / K;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (valid && lane == 63 - __clzll(peers)) base[e] = base[e] + __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+  };
+  if (sg.cached) {
+#pragma unroll
+    for (int u = 0; u < kCache; ++u) {
+      if (sg.i0 + u * 64 >= sg.i1) break;
+      const int i = sg.i0 + u * 64 + lane;
+      rank_step(i, i < sg.i1, sg.cache[u]);
+    }
+    return;
+  }
+  for (int bb = sg.i0; bb < sg.i1; bb += kBatch * 64) {
+    int ev[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = bb + u * 64 + lane;
+      ev[u] = i < sg.i1 ? f[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = bb + u * 64 + lane;
+      rank_step(i, i < sg.i1, ev[u]);
+    }
+  }
+}
+
+// Out-of-range expert id: an empty, in-bounds result with expert_off[E] = -1.
+__device__ void write_bad(int N, int E, int32_t *order, int32_t *inv_order, int32_t *row_map,
+                          int32_t *expert_off, int32_t *tile_off, int32_t *counters) {
+  const int tid = threadIdx.x, nth = blockDim.x;
+  for (int i = tid; i < N; i += nth) order[i] = inv_order[i] = row_map[i] = -1;
+  for (int e = tid; e <= E; e += nth) {
+    expert_off[e] = e == E ? -1 : 0;
+    tile_off[e] = 0;
+  }
+  if (tid == 0) counters[0] = counters[1] = 0;
+}
+
+// Whole dispatch in one workgroup (small N).
 __global__ __launch_bounds__(kThreads) void dispatch_kernel(
     const int32_t *__restrict__ f, int N, int K, int E, int S, int T, int tile_rows, int tr,
     int32_t *__restrict__ order, int32_t *__restrict__ inv_order, int32_t *__restrict__ row_map,
@@ -114,56 +243,19 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
   __shared__ int32_t wave_tot[17];
   __shared__ int32_t bad;
 
-  const int tid = threadIdx.x, nth = blockDim.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, nth = blockDim.x, w = tid >> 6;
   for (int q = tid; q < nw * E; q += nth) cnt[q] = 0;
   if (tid == 0) bad = 0;
   __syncthreads();
 
   const int seg = (N + nw - 1) / nw;
   const int i0 = min(N, w * seg), i1 = min(N, i0 + seg);
-  // When a wave's segment fits (up to 64*kCache slots), its expert ids are
-  // read once, all loads in flight together, and kept in registers for both
-  // passes; otherwise they are read kBatch per lane at a time in each pass.
-  const bool cached = (i1 - i0) <= 64 * kCache;
-  int cache[kCache];
-  if (cached) {
-#pragma unroll
-    for (int u = 0; u < kCache; ++u) {
-      const int i = i0 + u * 64 + lane;
-      cache[u] = i < i1 ? f[i] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < kCache; ++u) {
-      if (i0 + u * 64 + lane >= i1) continue;
-      const int e = cache[u];
-      if (unsigned(e) < unsigned(E)) atomicAdd(&cnt[w * E + e], 1);
-      else bad = 1;
-    }
-  }
-  for (int b0 = cached ? i1 : i0; b0 < i1; b0 += kBatch * 64) {
-    int ev[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int i = b0 + u * 64 + lane;
-      ev[u] = i < i1 ? f[i] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      if (b0 + u * 64 + lane >= i1) continue;
-      const int e = ev[u];
-      if (unsigned(e) < unsigned(E)) atomicAdd(&cnt[w * E + e], 1);
-      else bad = 1;
-    }
-  }
+  Segment sg;
+  seg_load(f, i0, i1, sg);
+  seg_count(f, sg, E, cnt + w * E, &bad);
   __syncthreads();
   if (bad) {
-    // Out-of-range expert id: an empty, in-bounds result with expert_off[E] = -1.
-    for (int i = tid; i < N; i += nth) order[i] = inv_order[i] = row_map[i] = -1;
-    for (int e = tid; e <= E; e += nth) {
-      expert_off[e] = e == E ? -1 : 0;
-      tile_off[e] = 0;
-    }
-    if (tid == 0) counters[0] = counters[1] = 0;
+    write_bad(N, E, order, inv_order, row_map, expert_off, tile_off, counters);
     return;
   }
 
@@ -186,51 +278,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
     }
   }
   __syncthreads();
-
-  // Stable ranks.  Each wave only touches its own row of bases.
-  volatile int32_t *base = cnt + w * E;
-  const int nbits = E > 1 ? 32 - __clz(E - 1) : 1;
-  const uint64_t lt_mask = lane ? (~0ull >> (64 - lane)) : 0ull;
-  // 64 consecutive slots (slot i in this lane, expert e): lanes carrying the
-  // same expert find each other bit by bit, rank = run base + earlier peers.
-  auto rank_step = [&](int i, bool valid, int e) {
-    uint64_t peers = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t bal = __ballot(valid && bit);
-      peers &= bit ? bal : ~bal;
-    }
-    if (valid) {
-      const int pos = base[e] + __popcll(peers & lt_mask);
-      order[pos] = i;
-      inv_order[i] = pos;
-      row_map[pos] = i / K;
-    }
-    __builtin_amdgcn_wave_barrier();
-    if (valid && lane == 63 - __clzll(peers)) base[e] = base[e] + __popcll(peers);
-    __builtin_amdgcn_wave_barrier();
-  };
-  if (cached) {
-#pragma unroll
-    for (int u = 0; u < kCache; ++u) {
-      if (i0 + u * 64 >= i1) break;
-      const int i = i0 + u * 64 + lane;
-      rank_step(i, i < i1, cache[u]);
-    }
-  }
-  for (int bb = cached ? i1 : i0; bb < i1; bb += kBatch * 64) {
-    int ev[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int i = bb + u * 64 + lane;
-      ev[u] = i < i1 ? f[i] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int i = bb + u * 64 + lane;
-      rank_step(i, i < i1, ev[u]);
-    }
-  }
+  seg_rank(f, sg, K, E, cnt + w * E, order, inv_order, row_map);
 
   for (int e = tid; e < E; e += nth) {
     expert_off[e] = off[e];
@@ -242,6 +290,129 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
   }
   __syncthreads();
   emit_plan(off, tot, scr0, scr1, wave_tot, E, S, N, T, tr, counters, act_items, tiles);
+}
+
+// ---- many workgroups (large N): count, scan, rank ----
+// Workgroup b owns slots [b*seg, (b+1)*seg), cut into one contiguous part
+// per wave, so slot order = (workgroup, wave, lane) order and the ranks stay
+// stable.  blk[b][0..E) holds the workgroup's expert counts, then (after the
+// scan) the first position of its run of each expert; blk[b][E] flags an
+// out-of-range id.
+
+constexpr int kMbThreads = 256;
+constexpr int kMbWaves = kMbThreads / 64;
+constexpr int kScanThreads = 1024;
+
+__device__ __forceinline__ void mb_segment(int N, int seg, int &i0, int &i1) {
+  const int b0 = blockIdx.x * seg, b1 = min(N, b0 + seg);
+  const int wseg = (b1 - b0 + kMbWaves - 1) / kMbWaves, w = threadIdx.x >> 6;
+  i0 = min(b1, b0 + w * wseg);
+  i1 = min(b1, i0 + wseg);
+}
+
+__global__ __launch_bounds__(kMbThreads) void dispatch_count_kernel(const int32_t *__restrict__ f, int N, int E,
+                                                                    int seg, int32_t *__restrict__ blk) {
+  extern __shared__ int32_t lds[];  // [kMbWaves][E]
+  __shared__ int32_t bad;
+  const int tid = threadIdx.x, w = tid >> 6;
+  for (int q = tid; q < kMbWaves * E; q += kMbThreads) lds[q] = 0;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  int i0, i1;
+  mb_segment(N, seg, i0, i1);
+  Segment sg;
+  seg_load(f, i0, i1, sg);
+  seg_count(f, sg, E, lds + w * E, &bad);
+  __syncthreads();
+  int32_t *row = blk + int64_t(blockIdx.x) * (E + 1);
+  for (int e = tid; e < E; e += kMbThreads) {
+    int c = 0;
+#pragma unroll
+    for (int ww = 0; ww < kMbWaves; ++ww) c += lds[ww * E + e];
+    row[e] = c;
+  }
+  if (tid == 0) row[E] = bad;
+}
+
+__global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
+    int32_t *__restrict__ blk, int B, int N, int E, int S, int T, int tile_rows, int tr,
+    int32_t *__restrict__ order, int32_t *__restrict__ inv_order, int32_t *__restrict__ row_map,
+    int32_t *__restrict__ expert_off, int32_t *__restrict__ tile_off, int32_t *counters, PlanItem *act_items,
+    PlanItem *tiles) {
+  extern __shared__ int32_t lds[];
+  int32_t *off = lds, *tot = off + E, *utile = tot + E, *scr0 = utile + E, *scr1 = scr0 + E;
+  __shared__ int32_t wave_tot[17];
+  __shared__ int32_t bad;
+  const int tid = threadIdx.x;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  for (int b = tid; b < B; b += kScanThreads)
+    if (blk[int64_t(b) * (E + 1) + E]) bad = 1;
+  __syncthreads();
+  if (bad) {
+    write_bad(N, E, order, inv_order, row_map, expert_off, tile_off, counters);
+    if (tid == 0) counters[2] = 1;  // tells the rank kernel to leave the -1 in place
+    return;
+  }
+  for (int e = tid; e < E; e += kScanThreads) {
+    int c = 0;
+    for (int b = 0; b < B; ++b) c += blk[int64_t(b) * (E + 1) + e];
+    tot[e] = c;
+    off[e] = c;
+    utile[e] = (c + tile_rows - 1) / tile_rows;
+  }
+  __syncthreads();
+  block_exscan(off, E, wave_tot);
+  const int n_utiles = block_exscan(utile, E, wave_tot);
+  for (int e = tid; e < E; e += kScanThreads) {
+    int run = off[e];
+    for (int b = 0; b < B; ++b) {
+      int32_t *p = blk + int64_t(b) * (E + 1) + e;
+      const int c = *p;
+      *p = run;
+      run += c;
+    }
+    expert_off[e] = off[e];
+    tile_off[e] = utile[e];
+  }
+  if (tid == 0) {
+    expert_off[E] = N;
+    tile_off[E] = n_utiles;
+    counters[2] = 0;
+  }
+  __syncthreads();
+  emit_plan(off, tot, scr0, scr1, wave_tot, E, S, N, T, tr, counters, act_items, tiles);
+}
+
+__global__ __launch_bounds__(kMbThreads) void dispatch_rank_kernel(
+    const int32_t *__restrict__ f, int N, int K, int E, int seg, const int32_t *__restrict__ blk,
+    const int32_t *counters, int32_t *__restrict__ order, int32_t *__restrict__ inv_order,
+    int32_t *__restrict__ row_map) {
+  if (counters[2]) return;  // out-of-range id: the scan kernel wrote the -1 result
+  extern __shared__ int32_t lds[];  // [kMbWaves][E] counts, then run bases
+  __shared__ int32_t bad;
+  const int tid = threadIdx.x, w = tid >> 6;
+  for (int q = tid; q < kMbWaves * E; q += kMbThreads) lds[q] = 0;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  int i0, i1;
+  mb_segment(N, seg, i0, i1);
+  Segment sg;
+  seg_load(f, i0, i1, sg);
+  seg_count(f, sg, E, lds + w * E, &bad);
+  __syncthreads();
+  const int32_t *row = blk + int64_t(blockIdx.x) * (E + 1);
+  for (int e = tid; e < E; e += kMbThreads) {
+    int run = row[e];
+#pragma unroll
+    for (int ww = 0; ww < kMbWaves; ++ww) {
+      const int c = lds[ww * E + e];
+      lds[ww * E + e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  seg_rank(f, sg, K, E, lds + w * E, order, inv_order, row_map);
 }
 
 __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *__restrict__ expert_off,
@@ -265,16 +436,37 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *__restric
 
 }  // namespace
 
+int64_t dispatch_scratch_ints(const moe_layer_desc *d, int32_t T) {
+  const int64_t N = int64_t(T) * d->top_k;
+  if (N <= kSingleBlockMax) return 0;
+  const int64_t seg = dispatch_segment(N);
+  return ((N + seg - 1) / seg) * (d->n_experts + 1);
+}
+
 void launch_dispatch(const moe_layer_desc *d, int32_t T, const int32_t *idx, int32_t tile_rows,
                      int32_t *order, int32_t *inv_order, int32_t *row_map, int32_t *expert_off,
                      int32_t *tile_off, int32_t *counters, PlanItem *act_items, PlanItem *tiles,
-                     void *stream, StageMarker *mk) {
+                     int32_t *scratch, void *stream, StageMarker *mk) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
   const int tr = plan_tile_rows(d, T);
-  const int E = d->n_experts, nw = kThreads / 64;
-  const size_t lds = size_t(nw * E + 5 * E) * sizeof(int32_t);
-  hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kThreads), lds, static_cast<hipStream_t>(stream),
-                     idx, T * d->top_k, d->top_k, E, d->n_shared, T, tile_rows, tr, order, inv_order,
-                     row_map, expert_off, tile_off, counters, act_items, tiles);
+  const int E = d->n_experts, N = T * d->top_k;
+  if (N <= kSingleBlockMax) {
+    const int nw = kThreads / 64;
+    const size_t lds = size_t(nw * E + 5 * E) * sizeof(int32_t);
+    hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kThreads), lds, s, idx, N, d->top_k, E, d->n_shared, T,
+                       tile_rows, tr, order, inv_order, row_map, expert_off, tile_off, counters, act_items, tiles);
+  } else {
+    // Scattered writes of order and row_map are spread over many CUs.
+    const int seg = int(dispatch_segment(N));
+    const int B = (N + seg - 1) / seg;
+    const size_t lds_w = size_t(kMbWaves) * E * sizeof(int32_t);
+    hipLaunchKernelGGL(dispatch_count_kernel, dim3(B), dim3(kMbThreads), lds_w, s, idx, N, E, seg, scratch);
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), size_t(5 * E) * sizeof(int32_t), s,
+                       scratch, B, N, E, d->n_shared, T, tile_rows, tr, order, inv_order, row_map, expert_off,
+                       tile_off, counters, act_items, tiles);
+    hipLaunchKernelGGL(dispatch_rank_kernel, dim3(B), dim3(kMbThreads), lds_w, s, idx, N, d->top_k, E, seg,
+                       scratch, counters, order, inv_order, row_map);
+  }
   if (mk) mk->mark("dispatch");
 }
 

@@ -85,7 +85,7 @@ int moe_dispatch(const moe_layer_desc *desc, int32_t T, const int32_t *topk_idx,
   if (T == 0) return MOE_OK;
   launch_dispatch(desc, T, topk_idx, tile_rows, order, inv_order, row_map, expert_off, tile_off,
                   at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles),
-                  stream);
+                  at<int32_t>(ws, L.dsp), stream);
   return hip_status();
 }
 
@@ -141,7 +141,7 @@ static int forward_impl(const moe_layer_desc *desc, int32_t T, const void *x, co
   launch_dispatch(desc, T, idx, 64, at<int32_t>(ws, L.order), at<int32_t>(ws, L.inv_order),
                   at<int32_t>(ws, L.row_map), at<int32_t>(ws, L.expert_off), at<int32_t>(ws, L.tile_off),
                   at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles),
-                  stream, mk);
+                  at<int32_t>(ws, L.dsp), stream, mk);
   launch_expert_ffn(desc, T, x, at<int32_t>(ws, L.row_map), w, at<int32_t>(ws, L.counters),
                     at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles), L.max_tiles,
                     ffn_scratch(ws, L), at<float>(ws, L.y_sorted), stream, mk);

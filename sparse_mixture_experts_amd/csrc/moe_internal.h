@@ -38,7 +38,8 @@ struct Workspace {
   size_t route;                       // router logits / chunk partials (f32)
   size_t order, inv_order, row_map;   // [N] int32
   size_t expert_off, tile_off;        // [E+1] int32
-  size_t counters;                    // 64 int32: [0] active items, [1] tiles
+  size_t counters;                    // 64 int32: [0] active items, [1] tiles, [2] dispatch error
+  size_t dsp;                         // dispatch scratch (dispatch_scratch_ints)
   size_t act_items;                   // [E+S] PlanItem
   size_t tiles;                       // [max_tiles] PlanItem
   size_t h;                           // [N+S*T][d_ff] h_bytes
@@ -71,10 +72,12 @@ void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void 
                   StageMarker *mk = nullptr);
 
 // Dispatch: stable counting sort + prefix tables + the internal work plan.
+// scratch holds dispatch_scratch_ints ints (per-workgroup counts for large N).
+int64_t dispatch_scratch_ints(const moe_layer_desc *d, int32_t T);
 void launch_dispatch(const moe_layer_desc *d, int32_t T, const int32_t *idx, int32_t tile_rows,
                      int32_t *order, int32_t *inv_order, int32_t *row_map, int32_t *expert_off,
                      int32_t *tile_off, int32_t *counters, PlanItem *act_items, PlanItem *tiles,
-                     void *stream, StageMarker *mk = nullptr);
+                     int32_t *scratch, void *stream, StageMarker *mk = nullptr);
 
 // Work plan from caller-supplied expert offsets (standalone moe_expert_ffn).
 void launch_plan(const moe_layer_desc *d, int32_t T, const int32_t *expert_off, int32_t *counters,

@@ -97,6 +97,7 @@ Workspace workspace_layout(const moe_layer_desc *d, int32_t T) {
   ws.expert_off = take(size_t(E + 1) * 4);
   ws.tile_off = take(size_t(E + 1) * 4);
   ws.counters = take(64 * 4);
+  ws.dsp = take(size_t(dispatch_scratch_ints(d, T)) * 4);
   ws.act_items = take(size_t(E + S) * sizeof(PlanItem));
   ws.tiles = take(size_t(ws.max_tiles) * sizeof(PlanItem));
   ws.h = take(size_t(rows) * d->d_ff * h_bytes(d));

@@ -155,40 +155,89 @@ __global__ __launch_bounds__(kThreads) void route_partials_kernel(
   }
 }
 
+// Chunk partials for small T: one wave per (64 experts, one chunk, TT
+// tokens), lane = expert.  Each lane runs the chunk's fma chain for its
+// expert and TT tokens; a wave's router loads are coalesced (64 consecutive
+// experts of one column) and the token values, staged in LDS, are the same
+// for every lane.  Output partials[C][T][E] (no bias).
+template <bool BF16, int TT>
+__global__ __launch_bounds__(kWave) void route_chunk_kernel(const void *__restrict__ x, const void *__restrict__ wr,
+                                                            int T, int D, int E, float *__restrict__ out) {
+  __shared__ float xs[kChunk][TT];
+  const int lane = threadIdx.x, e = blockIdx.x * kWave + lane, c = blockIdx.y, t0 = blockIdx.z * TT;
+  const int kc = c * kChunk, n = min(kChunk, D - kc), nt = min(TT, T - t0);
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+    xs[lane][t] = (lane < n && t < nt) ? load_act<BF16>(x, int64_t(t0 + t) * D + kc + lane) : 0.0f;
+  __syncthreads();
+  const int ec = min(e, E - 1);
+  float p[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) p[t] = 0.0f;
+  for (int i0 = 0; i0 < n; i0 += 16) {
+    float w[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) w[u] = i0 + u < n ? load_act<BF16>(wr, int64_t(kc + i0 + u) * E + ec) : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (i0 + u < n) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) p[t] = __builtin_fmaf(xs[i0 + u][t], w[u], p[t]);
+      }
+    }
+  }
+  if (e < E) {
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+      if (t < nt) out[(int64_t(c) * T + t0 + t) * E + e] = p[t];
+  }
+}
+
 // One wave per token: logits (summing chunk partials when n_chunks > 0),
-// top-k, softmax.  Each lane keeps the logits of experts lane + 64*m.
+// top-k, softmax.  Each lane keeps the logits of experts lane + 64*m, m < MPL.
+template <int MPL>
 __global__ __launch_bounds__(kThreads) void route_select_kernel(const float *__restrict__ in, int n_chunks,
                                                                 const float *__restrict__ bias, int T, int E,
                                                                 int K, int renorm, int32_t *__restrict__ idx_out,
                                                                 float *__restrict__ w_out) {
-  constexpr int kMaxPerLane = kMaxExperts / kWave;
+  // chunk partials per load batch: about 32 loads in flight per lane
+  constexpr int CB = MPL >= 32 ? 1 : 32 / MPL;
   const int t = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
   const int lane = lane_id();
   if (t >= T) return;
-  float l[kMaxPerLane];
+  float l[MPL];
+  if (n_chunks == 0) {
 #pragma unroll
-  for (int m = 0; m < kMaxPerLane; ++m) {
-    const int e = lane + kWave * m;
-    float v = -INFINITY;
-    if (e < E) {
-      if (n_chunks == 0) {
-        v = in[int64_t(t) * E + e];
-      } else {
-        // Issue 16 partial loads at a time, then add them in chunk order.
-        float acc = 0.0f;
-        for (int c0 = 0; c0 < n_chunks; c0 += 16) {
-          float pv[16];
-#pragma unroll
-          for (int u = 0; u < 16; ++u) pv[u] = c0 + u < n_chunks ? in[(int64_t(c0 + u) * T + t) * E + e] : 0.0f;
-#pragma unroll
-          for (int u = 0; u < 16; ++u)
-            if (c0 + u < n_chunks) acc = acc + pv[u];
-        }
-        if (bias) acc = acc + bias[e];
-        v = acc;
-      }
+    for (int m = 0; m < MPL; ++m) {
+      const int e = lane + kWave * m;
+      l[m] = e < E ? in[int64_t(t) * E + e] : -INFINITY;
     }
-    l[m] = v;
+  } else {
+    float acc[MPL];
+#pragma unroll
+    for (int m = 0; m < MPL; ++m) acc[m] = 0.0f;
+    for (int c0 = 0; c0 < n_chunks; c0 += CB) {
+      float pv[CB][MPL];
+#pragma unroll
+      for (int u = 0; u < CB; ++u)
+#pragma unroll
+        for (int m = 0; m < MPL; ++m) {
+          const int e = min(lane + kWave * m, E - 1), c = min(c0 + u, n_chunks - 1);
+          pv[u][m] = in[(int64_t(c) * T + t) * E + e];
+        }
+      // chunk order
+#pragma unroll
+      for (int u = 0; u < CB; ++u)
+        if (c0 + u < n_chunks) {
+#pragma unroll
+          for (int m = 0; m < MPL; ++m) acc[m] = acc[m] + pv[u][m];
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MPL; ++m) {
+      const int e = lane + kWave * m;
+      l[m] = e < E ? (bias ? acc[m] + bias[e] : acc[m]) : -INFINITY;
+    }
   }
   uint32_t taken = 0;
   int my_e = 0;
@@ -197,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(const float *__r
     float bv = -INFINITY;
     int be = 0x7fffffff;
 #pragma unroll
-    for (int m = 0; m < kMaxPerLane; ++m) {
+    for (int m = 0; m < MPL; ++m) {
       const int e = lane + kWave * m;
       if (e < E && !((taken >> m) & 1u) && ranks_before(l[m], e, bv, be)) { bv = l[m]; be = e; }
     }
@@ -214,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(const float *__r
   // fp32 softmax over all E logits (the top-1 logit is the maximum).
   float z = 0.0f;
 #pragma unroll
-  for (int m = 0; m < kMaxPerLane; ++m)
+  for (int m = 0; m < MPL; ++m)
     if (lane + kWave * m < E) z += expf(l[m] - top);
   z = wave_sum(z);
   const float p = expf(my_l - top) / z;
@@ -228,6 +277,16 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(const float *__r
     idx_out[int64_t(t) * K + lane] = my_e;
     w_out[int64_t(t) * K + lane] = w;
   }
+}
+
+void launch_select(const float *in, int n_chunks, const float *bias, int T, int E, int K, int renorm,
+                   int32_t *idx, float *w, hipStream_t s) {
+  const dim3 grid((T + kThreads / kWave - 1) / (kThreads / kWave)), block(kThreads);
+  if (E <= 64) hipLaunchKernelGGL(route_select_kernel<1>, grid, block, 0, s, in, n_chunks, bias, T, E, K, renorm, idx, w);
+  else if (E <= 128) hipLaunchKernelGGL(route_select_kernel<2>, grid, block, 0, s, in, n_chunks, bias, T, E, K, renorm, idx, w);
+  else if (E <= 256) hipLaunchKernelGGL(route_select_kernel<4>, grid, block, 0, s, in, n_chunks, bias, T, E, K, renorm, idx, w);
+  else if (E <= 512) hipLaunchKernelGGL(route_select_kernel<8>, grid, block, 0, s, in, n_chunks, bias, T, E, K, renorm, idx, w);
+  else hipLaunchKernelGGL(route_select_kernel<16>, grid, block, 0, s, in, n_chunks, bias, T, E, K, renorm, idx, w);
 }
 
 // Returns true when one block held every chunk (the output is logits).
@@ -256,11 +315,10 @@ bool launch_partials(const void *x, const void *wr, const float *bias, int T, in
 }  // namespace
 
 int64_t route_scratch_floats(const moe_layer_desc *d, int32_t T) {
-  // Covers every T' <= T: the one-token kernel keeps all chunk partials on
-  // chip when C <= 2; otherwise it writes C partials per (token, expert),
-  // which happens below 64 tokens, or at any T when C > 32.
+  // Covers every T' <= T: below 64 tokens (and at any T when C > 32) the
+  // chunk partials, C per (token, expert), go through the workspace.
   const int64_t C = (d->d_model + kChunk - 1) / kChunk;
-  const int64_t t_split = C <= 2 ? 0 : (C <= 32 ? std::min<int64_t>(T, 63) : int64_t(T));
+  const int64_t t_split = C <= 32 ? std::min<int64_t>(T, 63) : int64_t(T);
   int64_t n = std::max<int64_t>(int64_t(T) * d->n_experts, C * t_split * d->n_experts);
   if (route_mfma_applies(d, T)) n = std::max(n, route_mfma_scratch_floats(d, T));
   return n;
@@ -277,21 +335,25 @@ void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void 
   const int C = (D + kChunk - 1) / kChunk;
   const bool bf16 = d->act_dtype == MOE_DT_BF16;
   // Large T: 8 tokens per block with every chunk of the block on chip.
-  // Small T (or d_model > 2048): one token per block, 2 chunks per block, the
-  // partials summed by the selection kernel.
-  bool full;
-  if (T >= 64 && C <= 32) {
-    full = bf16 ? launch_partials<true, 8, 32>(x, w_router, bias, T, D, E, scratch, s)
-                : launch_partials<false, 8, 32>(x, w_router, bias, T, D, E, scratch, s);
+  // Small T: one wave per (64 experts, chunk, 8 tokens) for many parallel
+  // fma chains, the partials summed by the selection kernel.  Large T with
+  // d_model > 2048: one token per block, 2 chunks per block.
+  int n_chunks = C;
+  if (T < 64) {
+    const dim3 grid((E + kWave - 1) / kWave, C, (T + 7) / 8);
+    if (bf16) hipLaunchKernelGGL((route_chunk_kernel<true, 8>), grid, dim3(kWave), 0, s, x, w_router, T, D, E, scratch);
+    else hipLaunchKernelGGL((route_chunk_kernel<false, 8>), grid, dim3(kWave), 0, s, x, w_router, T, D, E, scratch);
+  } else if (C <= 32) {
+    if (bf16) launch_partials<true, 8, 32>(x, w_router, bias, T, D, E, scratch, s);
+    else launch_partials<false, 8, 32>(x, w_router, bias, T, D, E, scratch, s);
+    n_chunks = 0;
   } else {
-    full = bf16 ? launch_partials<true, 1, 2>(x, w_router, bias, T, D, E, scratch, s)
-                : launch_partials<false, 1, 2>(x, w_router, bias, T, D, E, scratch, s);
+    const bool full = bf16 ? launch_partials<true, 1, 2>(x, w_router, bias, T, D, E, scratch, s)
+                           : launch_partials<false, 1, 2>(x, w_router, bias, T, D, E, scratch, s);
+    n_chunks = full ? 0 : C;
   }
-  const int n_chunks = full ? 0 : C;
   if (mk) mk->mark("route_logits");
-  const int wpb = kThreads / kWave;
-  hipLaunchKernelGGL(route_select_kernel, dim3((T + wpb - 1) / wpb), dim3(kThreads), 0, s, scratch, n_chunks,
-                     bias, T, E, d->top_k, d->renormalize, idx, w);
+  launch_select(scratch, n_chunks, bias, T, E, d->top_k, d->renormalize, idx, w, s);
   if (mk) mk->mark("route_select");
 }
 

@@ -105,6 +105,31 @@ def test_dispatch_edge_cases():
     assert got["expert_off"][E] == -1 and np.all(got["order"] == -1) and np.all(got["expert_off"][:E] == 0)
 
 
+def test_dispatch_many_workgroups():
+    """Above 4096 slots the sort runs over many workgroups: ragged segments,
+    one expert taking every row, segments too long for the register cache,
+    and an out-of-range id."""
+    _, g = get("mid-q4-decode")
+    E = g.spec.n_experts
+    rng = np.random.default_rng(11)
+    zipf = np.minimum(rng.zipf(1.3, (9000, 8)) - 1, E - 1).astype(np.int32)
+    cases = [rng.integers(0, E, (513, 8), dtype=np.int32),       # 4104 slots: just past one workgroup
+             np.full((700, 8), 3, np.int32),                      # every row to one expert
+             zipf,                                               # heavy skew
+             rng.integers(0, E, (400_000, 8), dtype=np.int32)]    # 3.2M slots: uncached segments
+    for idx in cases:
+        for tr in (1, 64):
+            got = g.dispatch(idx, tr)
+            ref = oracle.dispatch(idx, E, tr)
+            for k in ref:
+                assert np.array_equal(got[k], ref[k]), (k, idx.shape, tr)
+    bad = rng.integers(0, E, (2000, 8), dtype=np.int32)
+    bad[1500, 5] = -1  # out of range, in a later workgroup
+    got = g.dispatch(bad, 64)
+    assert got["expert_off"][E] == -1 and np.all(got["order"] == -1) and np.all(got["row_map"] == -1)
+    assert np.all(got["inv_order"] == -1) and np.all(got["expert_off"][:E] == 0)
+
+
 @pytest.mark.parametrize("name", list(MID))
 def test_expert_ffn(name):
     L, g = get(name)
