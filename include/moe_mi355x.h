@@ -89,7 +89,8 @@ typedef struct {
  *  dense: w = act_dtype [E+S][N][K]; scales = biases = NULL.
  *  q4:    w = uint32 [E+S][N][K/8], column k of row n is bits [4*(k%8), +4)
  *         of word k/8 (an unsigned code q in 0..15); scales, biases = bf16
- *         [E+S][N][K/64]; the weight is scale*q + bias of its group ("affine"
+ *         [E+S][K/64][N] (group-major: one group's values for consecutive
+ *         rows are contiguous); the weight is scale*q + bias of its group ("affine"
  *         4-bit, group 64, with bf16 scales and biases: "SwitchGLU: grouped-
  *         expert Metal kernels" (ml-explore/mlx-lm #2044), "When it applies").
  * gate, up: N = d_ff, K = d_model; gate_up: N = 2*d_ff, K = d_model;

@@ -8,7 +8,8 @@ package never imports it.
 
 Arrays: activations and dense weights are ``float32`` or ``uint16`` holding
 bf16 bits; q4 weights are ``uint32`` words with eight 4-bit codes each (code m
-of a word sits at bits [4m, 4m+4)), scales/biases ``uint16`` bf16 bits.
+of a word sits at bits [4m, 4m+4)), scales/biases ``uint16`` bf16 bits stored
+group-major ([..][K/64][N]).
 """
 from __future__ import annotations
 

@@ -202,12 +202,13 @@ void oracle_dequant_row(const oracle_desc *d, const oracle_proj *p, int32_t e,
   }
   const int32_t G = d->group_size;
   const uint32_t *wq = (const uint32_t *)p->w + ((int64_t)e * N + n) * (K / 8);
-  const uint16_t *sc = p->scales + ((int64_t)e * N + n) * (K / G);
-  const uint16_t *bi = p->biases + ((int64_t)e * N + n) * (K / G);
+  /* scales/biases are group-major: [expert][group][row] */
+  const uint16_t *sc = p->scales + (int64_t)e * (K / G) * N + n;
+  const uint16_t *bi = p->biases + (int64_t)e * (K / G) * N + n;
   for (int32_t k = 0; k < K; ++k) {
     uint32_t q = (wq[k / 8] >> (4 * (k % 8))) & 0xfu;
-    float s = oracle_bf16_to_f32(sc[k / G]);
-    float b = oracle_bf16_to_f32(bi[k / G]);
+    float s = oracle_bf16_to_f32(sc[(int64_t)(k / G) * N]);
+    float b = oracle_bf16_to_f32(bi[(int64_t)(k / G) * N]);
     out[k] = s * (float)q + b;
   }
 }

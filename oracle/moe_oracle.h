@@ -50,7 +50,7 @@ typedef struct {
 /* One projection for all experts (routed first, then shared).  Dense:
  * w = [n_all][N][K] in the activation dtype.  q4: w = uint32 [n_all][N][K/8]
  * (eight 4-bit codes per word, code m at bits [4m, 4m+4) holds column
- * 8*word+m), scales/biases = bf16 bits [n_all][N][K/group]. */
+ * 8*word+m), scales/biases = bf16 bits [n_all][K/group][N] (group-major). */
 typedef struct {
   const void *w;
   const uint16_t *scales;

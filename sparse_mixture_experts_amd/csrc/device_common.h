@@ -1,5 +1,5 @@
 // device_common.h -- small device helpers for the gfx950 kernels: bf16
-// conversions, 4-bit unpacking and wave64 reductions.
+// conversions and wave64 reductions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,12 +28,6 @@ template <bool BF16>
 __device__ __forceinline__ float load_act(const void *p, int64_t i) {
   if constexpr (BF16) return bf16_bits_to_f32(static_cast<const uint16_t *>(p)[i]);
   else return static_cast<const float *>(p)[i];
-}
-
-// Eight 4-bit codes of a word, as fp32 (code m -> out[m]).
-__device__ __forceinline__ void unpack_q4(uint32_t w, float out[8]) {
-#pragma unroll
-  for (int m = 0; m < 8; ++m) out[m] = float((w >> (4 * m)) & 0xfu);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -1,11 +1,14 @@
-// ffn_gemv.hip -- grouped expert FFN for few rows per expert (dequant-GEMV).
+// ffn_gemv.hip -- grouped expert FFN on the vector units, for the layers the
+// matrix-core kernels do not take: fp32 activations, or dense bf16 layers
+// whose d_model or d_ff is not a multiple of 64.  (4-bit layers always have
+// bf16 activations and 64-multiple dims, so they always run on the matrix
+// cores.)
 //
 // "SwitchGLU: grouped-expert Metal kernels" (ml-explore/mlx-lm #2044),
 // section "What": slots are grouped by expert across tokens so each expert's
-// weights are read and dequantised once per group of rows instead of once
-// per (token, slot); gate and up are computed in one pass.  "perf(moe): fused
-// MoE expert decode kernel" (lablup/mlxcel #275), "What it does": affine
-// dequantisation inside the GEMV, SwiGLU, down projection.
+// weights are read once per group of rows instead of once per (token, slot);
+// gate and up are computed in one pass.  "perf(moe): fused MoE expert decode
+// kernel" (lablup/mlxcel #275), "What it does": SwiGLU, down projection.
 //
 // One workgroup takes one plan item (an expert and its sorted rows) and a
 // block of output columns.  Up to MR of the item's rows are staged in LDS;
@@ -20,7 +23,7 @@
 namespace moe {
 namespace {
 
-enum WFmt { W_F32 = 0, W_BF16 = 1, W_Q4 = 2 };
+enum WFmt { W_F32 = 0, W_BF16 = 1 };
 constexpr int kMR = 8;        // rows per pass (register accumulators)
 constexpr int kNB = 16;       // output columns per workgroup (4 per wave)
 constexpr int kThreads = 256;
@@ -35,18 +38,10 @@ __device__ __forceinline__ void load_w8(const void *__restrict__ w, const uint16
     const float4 a = p[0], b = p[1];
     out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
     out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
-  } else if constexpr (WF == W_BF16) {
+  } else {
     const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(w) + row * K + k);
     out[0] = bf16_lo(u.x); out[1] = bf16_hi(u.x); out[2] = bf16_lo(u.y); out[3] = bf16_hi(u.y);
     out[4] = bf16_lo(u.z); out[5] = bf16_hi(u.z); out[6] = bf16_lo(u.w); out[7] = bf16_hi(u.w);
-  } else {
-    const uint32_t q = static_cast<const uint32_t *>(w)[row * (K / 8) + k / 8];
-    const int64_t g = row * (K / kGroup) + k / kGroup;
-    const float s = bf16_bits_to_f32(sc[g]), b = bf16_bits_to_f32(bi[g]);
-    float c[8];
-    unpack_q4(q, c);
-#pragma unroll
-    for (int m = 0; m < 8; ++m) out[m] = __builtin_fmaf(s, c[m], b);  // s*q is exact
   }
 }
 
@@ -246,9 +241,7 @@ void launch_expert_ffn(const moe_layer_desc *d, int32_t T, const void *x, const 
   }
   void *h = sc.h;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (d->w_format == MOE_WF_AFFINE_Q4)
-    launch_gemv<true, W_Q4>(d, T, x, row_map, w, counters, act_items, h, y_sorted, s, mk);
-  else if (d->act_dtype == MOE_DT_BF16)
+  if (d->act_dtype == MOE_DT_BF16)
     launch_gemv<true, W_BF16>(d, T, x, row_map, w, counters, act_items, h, y_sorted, s, mk);
   else
     launch_gemv<false, W_F32>(d, T, x, row_map, w, counters, act_items, h, y_sorted, s, mk);

@@ -309,7 +309,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   const int s_col = (bx * kNW + s_w) * NTH * 16 + (s_nt % NTH) * 16 + s_r;
   const bool s_up = GATEUP && s_nt >= NTH;
   const bool s_ok = s_col < a.n_out;
-  const int64_t s_wrow = wrow_of(s_ok ? s_col : a.n_out - 1, s_up);
+  // Scales and biases are group-major, [expert][group][row of the expert's
+  // matrix], so a wave's loads of one group cover consecutive rows.
+  const int s_nre = (GATEUP && a.fused) ? 2 * a.n_out : a.n_out;  // rows of one expert's matrix
+  const int s_rin = (GATEUP && a.fused && s_up ? a.n_out : 0) + (s_ok ? s_col : a.n_out - 1);
+  const int64_t s_base = int64_t(tile.expert) * G * s_nre + s_rin;
 
   uint4 stg[PPT];
   uint16_t sraw[kGPS][2];
@@ -334,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
       for (int g = 0; g < kGPS; ++g) {
         const int gg = s * kGPS + g;
         const bool ok = s_ok && gg < G;
-        const int64_t at = s_wrow * G + min(gg, G - 1);
+        const int64_t at = s_base + int64_t(min(gg, G - 1)) * s_nre;
         const uint16_t sv = ssrc(s_up)[at], bv = bsrc(s_up)[at];
         sraw[g][0] = ok ? sv : uint16_t(0);
         sraw[g][1] = ok ? bv : uint16_t(0);

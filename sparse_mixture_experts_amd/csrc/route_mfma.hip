@@ -100,8 +100,8 @@ __global__ __launch_bounds__(kThreads) void router_mfma_kernel(const uint16_t *_
                                                                const float *__restrict__ bias,
                                                                float *__restrict__ normp, int n_kb, int T, int D,
                                                                int E, float *__restrict__ lt) {
-  __shared__ uint16_t sa[64][kChunk + 8];
-  __shared__ uint16_t sb[64][kChunk + 8];
+  __shared__ uint16_t sa[2][64][kChunk + 8];
+  __shared__ uint16_t sb[2][64][kChunk + 8];
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
   const int lr = lane & 15, lg = lane >> 4;
   const int e0 = blockIdx.x * 64, t0 = blockIdx.y * 64;
@@ -117,30 +117,46 @@ __global__ __launch_bounds__(kThreads) void router_mfma_kernel(const uint16_t *_
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // staging: thread -> (row tid / 4, 16 columns (tid % 4) * 16) of both tiles
+  // staging: thread -> (row tid / 4, 16 columns (tid % 4) * 16) of both
+  // tiles.  Chunk c+2 is loaded into registers while chunk c is multiplied
+  // from one LDS buffer and chunk c+1 is written to the other.
   const int sr = tid / 4, sc = (tid % 4) * 16;
   const int ea = min(e0 + sr, E - 1), tb = min(t0 + sr, T - 1);
   const bool oka = e0 + sr < E, okb = t0 + sr < T;
-  for (int k0 = 0; k0 < D; k0 += kChunk) {
+  const int C = D / kChunk;
+  auto keep = [](bool ok, uint4 v) {
+    return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+  };
+  struct Stage { uint4 a0, a1, b0, b1; };
+  auto load = [&](int c, Stage &st) {
+    const int k0 = min(c, C - 1) * kChunk;
     const uint4 *pa = reinterpret_cast<const uint4 *>(wt + int64_t(ea) * D + k0 + sc);
     const uint4 *pb = reinterpret_cast<const uint4 *>(x + int64_t(tb) * D + k0 + sc);
-    const uint4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
-    auto keep = [](bool ok, uint4 v) {
-      return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
-    };
-    __syncthreads();
-    *reinterpret_cast<uint4 *>(&sa[sr][sc]) = keep(oka, a0);
-    *reinterpret_cast<uint4 *>(&sa[sr][sc + 8]) = keep(oka, a1);
-    *reinterpret_cast<uint4 *>(&sb[sr][sc]) = keep(okb, b0);
-    *reinterpret_cast<uint4 *>(&sb[sr][sc + 8]) = keep(okb, b1);
-    __syncthreads();
+    st.a0 = pa[0]; st.a1 = pa[1]; st.b0 = pb[0]; st.b1 = pb[1];
+  };
+  auto store = [&](int buf, const Stage &st) {
+    *reinterpret_cast<uint4 *>(&sa[buf][sr][sc]) = keep(oka, st.a0);
+    *reinterpret_cast<uint4 *>(&sa[buf][sr][sc + 8]) = keep(oka, st.a1);
+    *reinterpret_cast<uint4 *>(&sb[buf][sr][sc]) = keep(okb, st.b0);
+    *reinterpret_cast<uint4 *>(&sb[buf][sr][sc + 8]) = keep(okb, st.b1);
+  };
+  Stage ring[2];
+  load(0, ring[0]);
+  load(1, ring[1]);
+  store(0, ring[0]);
+  load(2, ring[0]);
+  __syncthreads();
+  // chunk c from LDS buffer buf; then chunk c+1 (held in nx) to the other
+  // buffer, whose last readers (chunk c-1) are past the previous barrier, and
+  // chunk c+3 into nx.
+  auto step = [&](int c, int buf, Stage &nx) {
     bf16x8 av[2][2], bv[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        av[i][j] = *reinterpret_cast<const bf16x8 *>(&sa[we * 32 + i * 16 + lr][lg * 16 + j * 8]);
-        bv[i][j] = *reinterpret_cast<const bf16x8 *>(&sb[wtk * 32 + i * 16 + lr][lg * 16 + j * 8]);
+        av[i][j] = *reinterpret_cast<const bf16x8 *>(&sa[buf][we * 32 + i * 16 + lr][lg * 16 + j * 8]);
+        bv[i][j] = *reinterpret_cast<const bf16x8 *>(&sb[buf][wtk * 32 + i * 16 + lr][lg * 16 + j * 8]);
       }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -150,6 +166,13 @@ __global__ __launch_bounds__(kThreads) void router_mfma_kernel(const uint16_t *_
         d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i][1], bv[j][1], d, 0, 0, 0);
         acc[i][j] += d;
       }
+    store(buf ^ 1, nx);
+    load(c + 3, nx);
+    __syncthreads();
+  };
+  for (int c = 0; c < C; c += 2) {
+    step(c, 0, ring[1]);
+    if (c + 1 < C) step(c + 1, 1, ring[0]);
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -177,20 +200,23 @@ struct CertArgs {
   float *w_out;
 };
 
-// One wave per token.
+// One wave per token; each lane keeps L~ of experts lane + 64*m, m < MPL.
+template <int MPL>
 __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
-  constexpr int kPerLane = kMaxExperts / kWave;
-  __shared__ float s_l[kThreads / kWave][kMaxExperts];   // recomputed logits by list position
-  __shared__ int32_t s_e[kThreads / kWave][kMaxExperts]; // expert id by list position
+  constexpr int kNW = kThreads / kWave;
+  constexpr int kBatch = 32;  // candidates recomputed per batch
+  __shared__ float s_l[kNW][MPL * kWave];          // recomputed logits by list position
+  __shared__ int32_t s_e[kNW][MPL * kWave];        // expert id by list position
+  __shared__ float s_part[kNW][kBatch][kWave + 1];  // chunk partials of a batch (C <= 64)
   const int wv = threadIdx.x / kWave, lane = lane_id();
-  const int t = blockIdx.x * (kThreads / kWave) + wv;
-  if (t >= a.T) return;
+  const int t = blockIdx.x * kNW + wv;
+  if (t >= a.T) return;  // whole waves
   const int E = a.E, D = a.D, K = a.K, C = D / kChunk;
 
   // L~ row, ||x_t||, max_e ||W_e||, max |bias|
-  float lv[kPerLane];
+  float lv[MPL];
 #pragma unroll
-  for (int m = 0; m < kPerLane; ++m) {
+  for (int m = 0; m < MPL; ++m) {
     const int e = lane + kWave * m;
     lv[m] = e < E ? a.lt[int64_t(t) * E + e] : -INFINITY;
   }
@@ -223,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
       float bv = -INFINITY;
       int be = 0x7fffffff;
 #pragma unroll
-      for (int m = 0; m < kPerLane; ++m) {
+      for (int m = 0; m < MPL; ++m) {
         const int e = lane + kWave * m;
         if (e < E && !((taken >> m) & 1u) && ranks_before(lv[m], e, bv, be)) { bv = lv[m]; be = e; }
       }
@@ -242,18 +268,17 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
   // candidate list (all experts when too many)
   int n = 0;
 #pragma unroll
-  for (int m = 0; m < kPerLane; ++m) {
+  for (int m = 0; m < MPL; ++m) {
     const int e = lane + kWave * m;
-    const bool c = e < E && lv[m] >= thr;
-    n += __popcll(__ballot(c));
+    n += __popcll(__ballot(e < E && lv[m] >= thr));
   }
   const bool all = n > kMaxCand;
-  int pos[kPerLane];
+  int pos[MPL];
   {
     int base = 0;
     const uint64_t lt_mask = lane ? (~0ull >> (64 - lane)) : 0ull;
 #pragma unroll
-    for (int m = 0; m < kPerLane; ++m) {
+    for (int m = 0; m < MPL; ++m) {
       const int e = lane + kWave * m;
       const bool c = e < E && (all || lv[m] >= thr);
       const uint64_t b = __ballot(c);
@@ -265,43 +290,54 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
   }
   __builtin_amdgcn_wave_barrier();
 
-  // exact logits of the listed experts: lane = (slot, chunk); slots = 64 / C
-  const int slots = C <= kWave ? kWave / C : 1;
+  // Exact logits of the listed experts, kBatch at a time.  Lane (slot, ch)
+  // runs the 64-long fma chain of chunk ch for candidates slot, slot+slots,
+  // ... (two chains at a time); then lane p adds candidate p's C chunk
+  // partials in chunk order.
+  const int slots = kWave / C;
   const int slot = lane / C, ch = lane % C;
+  const bool lane_on = slot < slots;
   uint32_t xw[32];  // this lane's x chunk as packed bf16 (64 values)
-  if (slot < slots) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(a.x + int64_t(t) * D + ch * kChunk + q * 8);
+    xw[4 * q] = v.x; xw[4 * q + 1] = v.y; xw[4 * q + 2] = v.z; xw[4 * q + 3] = v.w;
+  }
+  auto chain = [&](const uint16_t *wr) -> float {
+    float part = 0.f;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(a.x + int64_t(t) * D + ch * kChunk + q * 8);
-      xw[4 * q] = v.x; xw[4 * q + 1] = v.y; xw[4 * q + 2] = v.z; xw[4 * q + 3] = v.w;
-    }
-  }
-  for (int p0 = 0; p0 < n; p0 += slots) {
-    const int p = p0 + slot;
-    float part = 0.f;
-    if (slot < slots && p < n) {
-      const int e = s_e[wv][p];
-      const uint16_t *wr = a.wt + int64_t(e) * D + ch * kChunk;
+      const uint4 v = *reinterpret_cast<const uint4 *>(wr + q * 8);
+      const uint32_t wv4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(wr + q * 8);
-        const uint32_t wv4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          part = __builtin_fmaf(bf16_lo(xw[4 * q + h]), bf16_lo(wv4[h]), part);
-          part = __builtin_fmaf(bf16_hi(xw[4 * q + h]), bf16_hi(wv4[h]), part);
-        }
+      for (int h = 0; h < 4; ++h) {
+        part = __builtin_fmaf(bf16_lo(xw[4 * q + h]), bf16_lo(wv4[h]), part);
+        part = __builtin_fmaf(bf16_hi(xw[4 * q + h]), bf16_hi(wv4[h]), part);
       }
     }
-    // chunk partials of each slot added in chunk order
-    float acc = 0.f;
-    for (int c = 0; c < C; ++c) acc = acc + __shfl(part, slot * C + c, kWave);
-    if (slot < slots && ch == 0 && p < n) {
-      const int e = s_e[wv][p];
-      s_l[wv][p] = a.bias ? acc + a.bias[e] : acc;
+    return part;
+  };
+  for (int b0 = 0; b0 < n; b0 += kBatch) {
+    const int nb = min(kBatch, n - b0);
+    for (int r = slot; r < nb; r += 2 * slots) {
+      const int r2 = r + slots;
+      const int e1 = s_e[wv][b0 + r], e2 = s_e[wv][b0 + min(r2, nb - 1)];
+      const float p1 = chain(a.wt + int64_t(e1) * D + ch * kChunk);
+      const float p2 = chain(a.wt + int64_t(e2) * D + ch * kChunk);
+      if (lane_on) {
+        s_part[wv][r][ch] = p1;
+        if (r2 < nb) s_part[wv][r2][ch] = p2;
+      }
     }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < nb) {
+      float acc = 0.f;
+      for (int c = 0; c < C; ++c) acc = acc + s_part[wv][lane][c];
+      const int e = s_e[wv][b0 + lane];
+      s_l[wv][b0 + lane] = a.bias ? acc + a.bias[e] : acc;
+    }
+    __builtin_amdgcn_wave_barrier();
   }
-  __builtin_amdgcn_wave_barrier();
 
   // top-k over the list
   int my_e = 0;
@@ -311,19 +347,14 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
     const int nq = (n + kWave - 1) / kWave;
     for (int j = 0; j < K; ++j) {
       float bv = -INFINITY;
-      int be = 0x7fffffff;
+      int be = 0x7fffffff, bp = -1;
       for (int q = 0; q < nq; ++q) {
         const int p = lane + kWave * q;
         if (p < n && !((taken >> q) & 1u)) {
           const float v = s_l[wv][p];
           const int e = s_e[wv][p];
-          if (ranks_before(v, e, bv, be)) { bv = v; be = e; }
+          if (ranks_before(v, e, bv, be)) { bv = v; be = e; bp = p; }
         }
-      }
-      int bp = -1;
-      for (int q = 0; q < nq; ++q) {
-        const int p = lane + kWave * q;
-        if (p < n && s_e[wv][p] == be) bp = p;
       }
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) {
@@ -341,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
   // softmax: recomputed logits where listed, L~ elsewhere (cancels when renormalised)
   float z = 0.f;
 #pragma unroll
-  for (int m = 0; m < kPerLane; ++m) {
+  for (int m = 0; m < MPL; ++m) {
     const int e = lane + kWave * m;
     if (e < E) z += expf((pos[m] >= 0 ? s_l[wv][pos[m]] : lv[m]) - top);
   }
@@ -390,8 +421,12 @@ void launch_route_mfma(const moe_layer_desc *d, int32_t T, const void *x, const 
   const float gamma = float(256 + 2 * C) * 5.9604645e-8f;
   CertArgs ca{static_cast<const uint16_t *>(x), wt, bias, lt, normp + int64_t(nkb) * E, T, D, E, d->top_k, gamma,
               idx, w};
-  const int wpb = kThreads / kWave;
-  hipLaunchKernelGGL(router_certify_kernel, dim3((T + wpb - 1) / wpb), dim3(kThreads), 0, s, ca);
+  const dim3 grid((T + kThreads / kWave - 1) / (kThreads / kWave)), block(kThreads);
+  if (E <= 64) hipLaunchKernelGGL(router_certify_kernel<1>, grid, block, 0, s, ca);
+  else if (E <= 128) hipLaunchKernelGGL(router_certify_kernel<2>, grid, block, 0, s, ca);
+  else if (E <= 256) hipLaunchKernelGGL(router_certify_kernel<4>, grid, block, 0, s, ca);
+  else if (E <= 512) hipLaunchKernelGGL(router_certify_kernel<8>, grid, block, 0, s, ca);
+  else hipLaunchKernelGGL(router_certify_kernel<16>, grid, block, 0, s, ca);
   if (mk) mk->mark("route_certify");
 }
 

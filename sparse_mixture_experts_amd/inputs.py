@@ -19,7 +19,9 @@ Recipe (the pages fix the shapes, not the draws):
     lo = min, hi = max, scale = bf16((hi - lo) / 15), bias = bf16(lo),
     q = clamp(rint((w - bias) / scale), 0, 15) (ties to even), q = 0 where
     scale == 0.  Eight codes per uint32, code m of a word at bits [4m, 4m+4)
-    holding column 8*word + m.
+    holding column 8*word + m.  Codes are stored row-major [N][K/8]; scales
+    and biases group-major [K/64][N] (the scales of one group for
+    consecutive rows are contiguous).
   * Skewed routing: an additive router bias of -2.2 * ln(e + 1) on expert e,
     i.e. twice the log of a Zipf(s = 1.1) weight of rank e + 1 (the Zipf
     normaliser cancels in the softmax).
@@ -134,7 +136,7 @@ def gen_router(spec: LayerSpec):
 def _store(spec: LayerSpec, w: np.ndarray):
     if spec.wfmt == "q4":
         q, s, b = quantize_q4(w, spec.group_size)
-        return {"w": q, "scales": s, "biases": b}
+        return {"w": q, "scales": np.ascontiguousarray(s.T), "biases": np.ascontiguousarray(b.T)}
     return {"w": w if spec.act == "f32" else to_bf16_bits(w)}
 
 

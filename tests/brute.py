@@ -31,8 +31,9 @@ def dequant64(spec: LayerSpec, proj: dict) -> np.ndarray:
         return widen(spec, proj["w"])
     q = unpack_codes(proj["w"]).astype(np.float64)
     g = spec.group_size
-    s = np.repeat(bits_to_f64(proj["scales"]), g, axis=-1)
-    b = np.repeat(bits_to_f64(proj["biases"]), g, axis=-1)
+    # scales/biases are stored group-major [..., K/g, N]
+    s = np.repeat(np.swapaxes(bits_to_f64(proj["scales"]), -1, -2), g, axis=-1)
+    b = np.repeat(np.swapaxes(bits_to_f64(proj["biases"]), -1, -2), g, axis=-1)
     return s * q + b
 
 

@@ -212,8 +212,8 @@ def pin_dequant():
     N, K = spec.d_ff, spec.d_model
     raw = inputs._rng(spec.seed, 2, 3).standard_normal((N, K), dtype=np.float32) / np.float32(math.sqrt(K))
     codes = brute.unpack_codes(proj["w"][3])
-    s = brute.bits_to_f64(proj["scales"][3])
-    b = brute.bits_to_f64(proj["biases"][3])
+    s = brute.bits_to_f64(proj["scales"][3]).T  # stored [K/64][N]
+    b = brute.bits_to_f64(proj["biases"][3]).T
     for n in (0, 1, N // 2, N - 1):
         row = oracle.dequant_row(d, proj, 3, n, N, K)
         sg, bg = np.repeat(s[n], 64), np.repeat(b[n], 64)

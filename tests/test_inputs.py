@@ -31,7 +31,7 @@ def test_formats_and_shapes():
         if spec.wfmt == "q4":
             assert ex["down"]["w"].shape == (n_all, spec.d_model, spec.d_ff // 8)
             assert ex["down"]["w"].dtype == np.uint32
-            assert ex["down"]["scales"].shape == (n_all, spec.d_model, spec.d_ff // 64)
+            assert ex["down"]["scales"].shape == (n_all, spec.d_ff // 64, spec.d_model)
         if spec.gate_up_fused:
             assert ex["gate_up"]["w"].shape[1] == 2 * spec.d_ff and "gate" not in ex
 

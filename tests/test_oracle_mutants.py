@@ -23,7 +23,7 @@ MUTANTS = {
     "softmax_wrong_index": ("w[j] = expf(l[idx[j]] - m) / z;", "w[j] = expf(l[j] - m) / z;"),
     "nibble_order_reversed": ("(4 * (k % 8))", "(4 * (7 - k % 8))"),
     "scale_bias_swapped": ("out[k] = s * (float)q + b;", "out[k] = b * (float)q + s;"),
-    "group_index_wrong": ("float s = oracle_bf16_to_f32(sc[k / G]);", "float s = oracle_bf16_to_f32(sc[0]);"),
+    "group_index_wrong": ("float s = oracle_bf16_to_f32(sc[(int64_t)(k / G) * N]);", "float s = oracle_bf16_to_f32(sc[0]);"),
     "fused_up_reads_gate": ("oracle_dequant_row(d, &w->gate_up, e, F + n, 2 * F, D, row);",
                             "oracle_dequant_row(d, &w->gate_up, e, n, 2 * F, D, row);"),
     "separate_gate_reads_up": ("oracle_dequant_row(d, &w->gate, e, n, F, D, row);",

@@ -253,7 +253,7 @@ def test_fp16_range_shifts():
         for k in ("scales", "biases"):
             v = L["experts"][proj][k].astype(np.uint32)
             nz = (v & 0x7f80) != 0
-            v[2, :5][nz[2, :5]] += 16 << 7  # expert 2: first 5 rows times 2^16
+            v[2, :, :5][nz[2, :, :5]] += 16 << 7  # expert 2: first 5 rows times 2^16 (stored [G][N])
             L["experts"][proj][k] = v.astype(np.uint16)
     g = GpuLayer(L)
     y, idx, _ = g.forward()
