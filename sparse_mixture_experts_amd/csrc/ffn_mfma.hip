@@ -74,14 +74,21 @@ __device__ __forceinline__ f32x4 mfma_f16(const f16x8 &a, const f16x8 &b, const 
 }
 
 // 8 codes of a word -> 8 fp16 weights s*q + b in the order q0,q4,q1,q5,q2,q6,q3,q7.
-__device__ __forceinline__ f16x8 q4_word_to_f16(uint32_t w, h2 s2, h2 b2) {
+// Codes 0/4 and 2/6 (after a shift by 8) sit in mantissa bits 0-3 of the two
+// halves: OR-ing the fp16 exponent of 1024 gives 1024 + q.  Codes 1/5 and
+// 3/7 sit in bits 4-7: the same OR gives 1024 + 16q, used with s/16.  Both
+// subtractions of 1024 are exact, and each fma rounds s*q + b once.  `magic`
+// holds 0x64006400 in a register so that every mask-and-or is one
+// v_and_or_b32 with a single literal.
+__device__ __forceinline__ f16x8 q4_word_to_f16(uint32_t w, h2 s2, h2 s2_16, h2 b2, uint32_t magic) {
   const h2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  const uint32_t w8 = w >> 8;
+  const uint32_t c[4] = {(w & 0x000f000fu) | magic, (w & 0x00f000f0u) | magic, (w8 & 0x000f000fu) | magic,
+                         (w8 & 0x00f000f0u) | magic};
   h2 r[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const h2 q = __builtin_bit_cast(h2, ((w >> (4 * j)) & 0x000f000fu) | 0x64006400u) - k1024;
-    r[j] = __builtin_elementwise_fma(q, s2, b2);
-  }
+  for (int j = 0; j < 4; ++j)
+    r[j] = __builtin_elementwise_fma(__builtin_bit_cast(h2, c[j]) - k1024, (j & 1) ? s2_16 : s2, b2);
   return __builtin_bit_cast(f16x8, r);
 }
 
@@ -382,6 +389,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     return flag;
   };
 
+  uint32_t magic = 0x64006400u;  // fp16 exponent of 1024 in both halves
+  asm volatile("" : "+v"(magic));  // kept in a register (see q4_word_to_f16)
   f32x4 acc[kNT][RB];
   auto zero_acc = [&]() {
 #pragma unroll
@@ -411,11 +420,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   // stored), which keeps the body free of branches.
   auto compute_slab = [&](const Slab<RB> &S, const WSlab<Q4> &ws) {
     if constexpr (Q4) {
-      h2 s2[kNT], b2[kNT];
+      const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+      h2 s2[kNT], s2_16[kNT], b2[kNT];
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
         const uint2 v = S.sb[lg >> 1][(wave * kNT + nt) * 16 + lr];
         s2[nt] = __builtin_bit_cast(h2, v.x);
+        s2_16[nt] = s2[nt] * sixteenth;
         b2[nt] = __builtin_bit_cast(h2, v.y);
       }
 #pragma unroll
@@ -427,7 +438,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
           const uint32_t wd = j == 0 ? ws.w[nt].x : j == 1 ? ws.w[nt].y : j == 2 ? ws.w[nt].z : ws.w[nt].w;
-          const f16x8 aw = q4_word_to_f16(wd, s2[nt], b2[nt]);
+          const f16x8 aw = q4_word_to_f16(wd, s2[nt], s2_16[nt], b2[nt], magic);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) acc[nt][rb] = mfma_f16(aw, bx[rb], acc[nt][rb]);
         }
