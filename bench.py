@@ -95,9 +95,11 @@ def accounting(spec, touched: int):
     gu_frac, down_frac = 2 / 3, 1 / 3
     w_touched = (touched + S) * eb
     router = D * E * esz
+    # expert outputs: bf16 where the matrix-core kernels write them, else fp32
+    ysz = 2 if spec.act == "bf16" and D % 64 == 0 and F % 64 == 0 else 4
     gateup = {"bound": "hbm", "bytes": int(w_touched * gu_frac) + T * D * esz + R * F * esz,
               "flops": 2 * R * 2 * D * F}
-    down = {"bound": "hbm", "bytes": int(w_touched * down_frac) + R * F * esz + R * D * 4, "flops": 2 * R * D * F}
+    down = {"bound": "hbm", "bytes": int(w_touched * down_frac) + R * F * esz + R * D * ysz, "flops": 2 * R * D * F}
     acc = {
         "layer_bytes": w_touched + router + T * D * esz + T * D * esz,
         "expert_flops": 2 * R * 3 * D * F,
@@ -115,7 +117,7 @@ def accounting(spec, touched: int):
             "x_f16": {"bound": "hbm", "bytes": 2 * T * D * esz + T},
             "gateup_gemv": gateup, "down_gemv": down,
             "gateup_mfma": gateup, "down_mfma": down,
-            "combine": {"bound": "hbm", "bytes": R * D * 4 + T * D * esz + N * 8},
+            "combine": {"bound": "hbm", "bytes": R * D * ysz + T * D * esz + N * 8},
         },
     }
     return acc

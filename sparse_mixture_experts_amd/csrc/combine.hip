@@ -11,55 +11,88 @@
 namespace moe {
 namespace {
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ ys,
-                                                      const int32_t *__restrict__ inv,
-                                                      const float *__restrict__ w, int T, int K,
-                                                      int S, int N, int D, void *__restrict__ y) {
+constexpr int kThreads = 256;
+constexpr int kCols = 8;  // columns per thread (one 16-byte bf16 load, two fp32 ones)
+
+// Eight consecutive expert-output values as fp32.
+template <bool YS_BF16>
+__device__ __forceinline__ void load8(const void *ys, int64_t i, float v[8]) {
+  if constexpr (YS_BF16) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(ys) + i);
+    v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+    v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z); v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+  } else {
+    const float4 *q = reinterpret_cast<const float4 *>(static_cast<const float *>(ys) + i);
+    const float4 a = q[0], b = q[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+// Block (t, cb): token t, columns cb*256*8 ..; each thread 8 columns.  All
+// slot rows of a thread are loaded before they are summed (slot order).
+template <bool YS_BF16, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const void *__restrict__ ys,
+                                                           const int32_t *__restrict__ inv,
+                                                           const float *__restrict__ w, int T, int K, int S,
+                                                           int N, int D, void *__restrict__ y) {
   const int t = blockIdx.x;
-  for (int c = threadIdx.x * 4; c < D; c += blockDim.x * 4) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < K; ++j) {
+  const int c = (blockIdx.y * kThreads + threadIdx.x) * kCols;
+  if (c >= D) return;
+  float acc[kCols];
+#pragma unroll
+  for (int i = 0; i < kCols; ++i) acc[i] = 0.f;
+  for (int j0 = 0; j0 < K; j0 += 8) {
+    float v[8][kCols], wj[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = min(j0 + u, K - 1);
       const int p = inv[int64_t(t) * K + j];
-      if (unsigned(p) >= unsigned(N)) continue;
-      const float wj = w[int64_t(t) * K + j];
-      const float4 v = *reinterpret_cast<const float4 *>(ys + int64_t(p) * D + c);
-      acc.x += wj * v.x;
-      acc.y += wj * v.y;
-      acc.z += wj * v.z;
-      acc.w += wj * v.w;
+      const bool ok = j0 + u < K && unsigned(p) < unsigned(N);
+      wj[u] = ok ? w[int64_t(t) * K + j] : 0.f;
+      load8<YS_BF16>(ys, int64_t(ok ? p : 0) * D + c, v[u]);
     }
-    for (int s = 0; s < S; ++s) {
-      const float4 v = *reinterpret_cast<const float4 *>(ys + (int64_t(N) + int64_t(s) * T + t) * D + c);
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
-    }
-    if constexpr (OUT_BF16) {
-      uint2 o;
-      o.x = f32_to_bf16_bits(acc.x) | (f32_to_bf16_bits(acc.y) << 16);
-      o.y = f32_to_bf16_bits(acc.z) | (f32_to_bf16_bits(acc.w) << 16);
-      *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(y) + int64_t(t) * D + c) = o;
-    } else {
-      *reinterpret_cast<float4 *>(static_cast<float *>(y) + int64_t(t) * D + c) = acc;
-    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < K) {
+#pragma unroll
+        for (int i = 0; i < kCols; ++i) acc[i] += wj[u] * v[u][i];
+      }
+  }
+  for (int s = 0; s < S; ++s) {
+    float v[kCols];
+    load8<YS_BF16>(ys, (int64_t(N) + int64_t(s) * T + t) * D + c, v);
+#pragma unroll
+    for (int i = 0; i < kCols; ++i) acc[i] += v[i];
+  }
+  if constexpr (OUT_BF16) {
+    uint4 o;
+    o.x = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
+    o.y = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
+    o.z = f32_to_bf16_bits(acc[4]) | (f32_to_bf16_bits(acc[5]) << 16);
+    o.w = f32_to_bf16_bits(acc[6]) | (f32_to_bf16_bits(acc[7]) << 16);
+    *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(y) + int64_t(t) * D + c) = o;
+  } else {
+    float4 *q = reinterpret_cast<float4 *>(static_cast<float *>(y) + int64_t(t) * D + c);
+    q[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    q[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
   }
 }
 
 }  // namespace
 
-void launch_combine(const moe_layer_desc *d, int32_t T, const float *y_sorted,
+void launch_combine(const moe_layer_desc *d, int32_t T, const void *y_sorted, bool ys_bf16,
                     const int32_t *inv_order, const float *topk_w, void *y, int32_t out_dtype,
                     void *stream, StageMarker *mk) {
-  const int N = T * d->top_k;
+  const int N = T * d->top_k, D = d->d_model;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (out_dtype == MOE_DT_BF16)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(T), dim3(256), 0, s, y_sorted, inv_order, topk_w, T,
-                       d->top_k, d->n_shared, N, d->d_model, y);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(T), dim3(256), 0, s, y_sorted, inv_order, topk_w,
-                       T, d->top_k, d->n_shared, N, d->d_model, y);
+  const dim3 grid(T, (D + kThreads * kCols - 1) / (kThreads * kCols));
+  const bool ob = out_dtype == MOE_DT_BF16;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, y_sorted, inv_order, topk_w, T, d->top_k, d->n_shared,
+                       N, D, y);
+  };
+  if (ys_bf16) ob ? go(combine_kernel<true, true>) : go(combine_kernel<true, false>);
+  else ob ? go(combine_kernel<false, true>) : go(combine_kernel<false, false>);
   if (mk) mk->mark("combine");
 }
 

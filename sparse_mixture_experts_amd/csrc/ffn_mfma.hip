@@ -169,7 +169,8 @@ struct GemmArgs {
   const uint16_t *s1, *b1;
   const int32_t *counters;  // [1] = number of tiles
   const PlanItem *tiles;
-  void *out;                // gate/up: h [rows][F] (bf16, or fp16 for 4-bit); down: y fp32 [rows][D]
+  void *out;                // gate/up: h [rows][F] (bf16, or fp16 for 4-bit); down: y [rows][D]
+  int out_bf16;             // down: y rows as bf16 (else fp32)
 };
 
 template <int RB>
@@ -577,6 +578,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
         for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16_bits(swiglu(acc[nt][rb][i], acc[nt + NTH][rb][i], a.round_ops));
         const uint2 o = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
         *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + row * a.n_out + c) = o;
+      } else if (a.out_bf16) {
+        const uint2 o = make_uint2(f32_to_bf16_bits(acc[nt][rb][0]) | (f32_to_bf16_bits(acc[nt][rb][1]) << 16),
+                                   f32_to_bf16_bits(acc[nt][rb][2]) | (f32_to_bf16_bits(acc[nt][rb][3]) << 16));
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + row * a.n_out + c) = o;
       } else {
         *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + row * a.n_out + c) =
             make_float4(acc[nt][rb][0], acc[nt][rb][1], acc[nt][rb][2], acc[nt][rb][3]);
@@ -610,7 +615,7 @@ int plan_tile_rows(const moe_layer_desc *d, int32_t T) {
 
 void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
                             const moe_weights *w, const int32_t *counters, const PlanItem *tiles,
-                            int64_t max_tiles, const FfnScratch &sc, float *y_sorted, void *stream,
+                            int64_t max_tiles, const FfnScratch &sc, void *y_sorted, bool ys_bf16, void *stream,
                             StageMarker *mk) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool q4 = d->w_format == MOE_WF_AFFINE_Q4;
@@ -626,10 +631,10 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
               d->gate_up_fused, d->swiglu_round_bf16,
               pg.w, static_cast<const uint16_t *>(pg.scales), static_cast<const uint16_t *>(pg.biases),
               w->up.w, static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases),
-              counters, tiles, sc.h};
+              counters, tiles, sc.h, 0};
   GemmArgs dn{sc.h, sc.hsh, nullptr, nblk, nullptr, T, T * d->top_k, d->d_ff, d->d_model, 0, 0,
               w->down.w, static_cast<const uint16_t *>(w->down.scales), static_cast<const uint16_t *>(w->down.biases),
-              nullptr, nullptr, nullptr, counters, tiles, y_sorted};
+              nullptr, nullptr, nullptr, counters, tiles, y_sorted, ys_bf16};
   if (tr == 16) {
     if (q4) launch_one<true, true, 1>(gu, max_tiles, s);
     else launch_one<true, false, 1>(gu, max_tiles, s);

@@ -104,7 +104,7 @@ int moe_expert_ffn(const moe_layer_desc *desc, int32_t T, const void *x, const i
   launch_plan(desc, T, expert_off, at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items),
               at<PlanItem>(ws, L.tiles), stream);
   launch_expert_ffn(desc, T, x, row_map, w, at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items),
-                    at<PlanItem>(ws, L.tiles), L.max_tiles, ffn_scratch(ws, L), y_sorted, stream);
+                    at<PlanItem>(ws, L.tiles), L.max_tiles, ffn_scratch(ws, L), y_sorted, false, stream);
   return hip_status();
 }
 
@@ -117,7 +117,7 @@ int moe_combine(const moe_layer_desc *desc, int32_t T, const float *y_sorted, co
       (s = validate_ptr(y)))
     return s;
   if (T == 0) return MOE_OK;
-  launch_combine(desc, T, y_sorted, inv_order, topk_w, y, out_dtype, stream);
+  launch_combine(desc, T, y_sorted, false, inv_order, topk_w, y, out_dtype, stream);
   return hip_status();
 }
 
@@ -144,8 +144,8 @@ static int forward_impl(const moe_layer_desc *desc, int32_t T, const void *x, co
                   at<int32_t>(ws, L.dsp), stream, mk);
   launch_expert_ffn(desc, T, x, at<int32_t>(ws, L.row_map), w, at<int32_t>(ws, L.counters),
                     at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles), L.max_tiles,
-                    ffn_scratch(ws, L), at<float>(ws, L.y_sorted), stream, mk);
-  launch_combine(desc, T, at<float>(ws, L.y_sorted), at<int32_t>(ws, L.inv_order), wt, y, out_dtype,
+                    ffn_scratch(ws, L), at<void>(ws, L.y_sorted), ys_bytes(desc) == 2, stream, mk);
+  launch_combine(desc, T, at<void>(ws, L.y_sorted), ys_bytes(desc) == 2, at<int32_t>(ws, L.inv_order), wt, y, out_dtype,
                  stream, mk);
   return hip_status();
 }

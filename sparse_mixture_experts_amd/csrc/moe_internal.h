@@ -31,6 +31,10 @@ int validate_weights(const moe_layer_desc *d, const moe_weights *w, bool need_ro
 inline int64_t act_bytes(const moe_layer_desc *d) { return d->act_dtype == MOE_DT_BF16 ? 2 : 4; }
 // Bytes per element of the SwiGLU intermediate h (bf16 for bf16 layers).
 inline int64_t h_bytes(const moe_layer_desc *d) { return d->act_dtype == MOE_DT_BF16 ? 2 : 4; }
+bool use_mfma(const moe_layer_desc *d);
+// Bytes per element of the workspace copy of the expert outputs: bf16 where
+// the matrix-core kernels write them, fp32 on the vector-unit path.
+inline int64_t ys_bytes(const moe_layer_desc *d) { return use_mfma(d) ? 2 : 4; }
 
 // Workspace carve-up.  Every section is 256-byte aligned.
 struct Workspace {
@@ -45,7 +49,7 @@ struct Workspace {
   size_t h;                           // [N+S*T][d_ff] h_bytes
   size_t hsh;                         // [N+S*T][ceil(d_ff/128)] int8 (4-bit layers)
   size_t x16, xsh;                    // [T][d_model] fp16, [T] int8 (4-bit layers)
-  size_t y_sorted;                    // [N+S*T][d_model] f32
+  size_t y_sorted;                    // [N+S*T][d_model] ys_bytes
   size_t total;
   int64_t max_tiles;
 };
@@ -98,20 +102,19 @@ constexpr int kHBlock = 128;  // h columns per exponent block
 // Expert FFN over the plan: y_sorted rows for all routed and shared rows.
 void launch_expert_ffn(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
                        const moe_weights *w, const int32_t *counters, const PlanItem *act_items,
-                       const PlanItem *tiles, int64_t max_tiles, const FfnScratch &sc, float *y_sorted,
-                       void *stream, StageMarker *mk = nullptr);
+                       const PlanItem *tiles, int64_t max_tiles, const FfnScratch &sc, void *y_sorted,
+                       bool ys_bf16, void *stream, StageMarker *mk = nullptr);
 
 // Row-tile height of the work plan for this layer and token count, and
 // whether the grouped MFMA kernels serve the layer (else dequant-GEMV).
 int plan_tile_rows(const moe_layer_desc *d, int32_t T);
-bool use_mfma(const moe_layer_desc *d);
 void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
                             const moe_weights *w, const int32_t *counters, const PlanItem *tiles,
-                            int64_t max_tiles, const FfnScratch &sc, float *y_sorted, void *stream,
+                            int64_t max_tiles, const FfnScratch &sc, void *y_sorted, bool ys_bf16, void *stream,
                             StageMarker *mk);
 
 // Combine.
-void launch_combine(const moe_layer_desc *d, int32_t T, const float *y_sorted,
+void launch_combine(const moe_layer_desc *d, int32_t T, const void *y_sorted, bool ys_bf16,
                     const int32_t *inv_order, const float *topk_w, void *y, int32_t out_dtype,
                     void *stream, StageMarker *mk = nullptr);
 

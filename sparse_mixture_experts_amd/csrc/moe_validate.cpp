@@ -105,7 +105,7 @@ Workspace workspace_layout(const moe_layer_desc *d, int32_t T) {
   ws.hsh = take(q4 ? size_t(rows) * ((d->d_ff + kHBlock - 1) / kHBlock) : 0);
   ws.x16 = take(q4 ? size_t(T) * d->d_model * 2 : 0);
   ws.xsh = take(q4 ? size_t(T) : 0);
-  ws.y_sorted = take(size_t(rows) * d->d_model * 4);
+  ws.y_sorted = take(size_t(rows) * d->d_model * ys_bytes(d));
   ws.total = o;
   return ws;
 }
