@@ -295,13 +295,11 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
 // ---- many workgroups (large N): count, scan, rank ----
 // Workgroup b owns slots [b*seg, (b+1)*seg), cut into one contiguous part
 // per wave, so slot order = (workgroup, wave, lane) order and the ranks stay
-// stable.  blk[b][0..E) holds the workgroup's expert counts, then (after the
-// scan) the first position of its run of each expert; blk[b][E] flags an
-// out-of-range id.
+// stable.  blk[b][0..E) holds the workgroup's expert counts; blk[b][E] flags
+// an out-of-range id.
 
 constexpr int kMbThreads = 256;
 constexpr int kMbWaves = kMbThreads / 64;
-constexpr int kScanThreads = 1024;
 
 __device__ __forceinline__ void mb_segment(int N, int seg, int &i0, int &i1) {
   const int b0 = blockIdx.x * seg, b1 = min(N, b0 + seg);
@@ -334,85 +332,107 @@ __global__ __launch_bounds__(kMbThreads) void dispatch_count_kernel(const int32_
   if (tid == 0) row[E] = bad;
 }
 
-__global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
-    int32_t *__restrict__ blk, int B, int N, int E, int S, int T, int tile_rows, int tr,
-    int32_t *__restrict__ order, int32_t *__restrict__ inv_order, int32_t *__restrict__ row_map,
-    int32_t *__restrict__ expert_off, int32_t *__restrict__ tile_off, int32_t *counters, PlanItem *act_items,
-    PlanItem *tiles) {
+// Each workgroup also forms the global tables it needs from blk: per expert
+// the total over all workgroups (whose exclusive scan gives expert_off) and
+// the sum over earlier workgroups (the start of this workgroup's run), so no
+// separate scan pass is needed; workgroup 0 writes expert_off, tile_off and
+// the work plan.
+__global__ __launch_bounds__(kMbThreads) void dispatch_rank_kernel(
+    const int32_t *__restrict__ f, int N, int K, int E, int S, int T, int seg, int B, int tile_rows, int tr,
+    const int32_t *__restrict__ blk, int32_t *__restrict__ order, int32_t *__restrict__ inv_order,
+    int32_t *__restrict__ row_map, int32_t *__restrict__ expert_off, int32_t *__restrict__ tile_off,
+    int32_t *counters, PlanItem *act_items, PlanItem *tiles) {
   extern __shared__ int32_t lds[];
-  int32_t *off = lds, *tot = off + E, *utile = tot + E, *scr0 = utile + E, *scr1 = scr0 + E;
+  int32_t *cw = lds;                  // [kMbWaves][E] wave counts, then wave run starts
+  int32_t *off = cw + kMbWaves * E;   // [E] expert offsets
+  int32_t *tot = off + E;             // [E] expert counts
+  int32_t *utile = tot + E;           // [E] caller tile offsets
+  int32_t *pre = utile + E;           // [E] rows of each expert in earlier workgroups; plan scratch later
+  int32_t *scr1 = pre + E;            // [E] plan scratch
   __shared__ int32_t wave_tot[17];
   __shared__ int32_t bad;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, b = blockIdx.x;
+
+  int i0, i1;
+  mb_segment(N, seg, i0, i1);
+  Segment sg;
+  seg_load(f, i0, i1, sg);
+  for (int q = tid; q < kMbWaves * E; q += kMbThreads) cw[q] = 0;
   if (tid == 0) bad = 0;
+  // column sums of blk, 8 workgroups x up to 4 experts per thread in flight
+  constexpr int kEPT = kMaxExperts / kMbThreads;
+  int ctot[kEPT], cpre[kEPT];
+#pragma unroll
+  for (int i = 0; i < kEPT; ++i) ctot[i] = cpre[i] = 0;
+  for (int b0 = 0; b0 < B; b0 += 8) {
+    int v[kEPT][8];
+#pragma unroll
+    for (int i = 0; i < kEPT; ++i)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = min(tid + i * kMbThreads, E - 1);
+        v[i][u] = blk[int64_t(min(b0 + u, B - 1)) * (E + 1) + e];
+      }
+#pragma unroll
+    for (int i = 0; i < kEPT; ++i)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (b0 + u < B) {
+          ctot[i] += v[i][u];
+          if (b0 + u < b) cpre[i] += v[i][u];
+        }
+  }
   __syncthreads();
-  for (int b = tid; b < B; b += kScanThreads)
-    if (blk[int64_t(b) * (E + 1) + E]) bad = 1;
+  for (int q = tid; q < B; q += kMbThreads)
+    if (blk[int64_t(q) * (E + 1) + E]) bad = 1;
+#pragma unroll
+  for (int i = 0; i < kEPT; ++i) {
+    const int e = tid + i * kMbThreads;
+    if (e < E) {
+      tot[e] = off[e] = ctot[i];
+      pre[e] = cpre[i];
+      utile[e] = (ctot[i] + tile_rows - 1) / tile_rows;
+    }
+  }
   __syncthreads();
   if (bad) {
-    write_bad(N, E, order, inv_order, row_map, expert_off, tile_off, counters);
-    if (tid == 0) counters[2] = 1;  // tells the rank kernel to leave the -1 in place
+    // Out-of-range expert id: the -1 result (each workgroup its own positions).
+    const int p0 = b * seg, p1 = min(N, p0 + seg);
+    for (int i = p0 + tid; i < p1; i += kMbThreads) order[i] = inv_order[i] = row_map[i] = -1;
+    if (b == 0) {
+      for (int e = tid; e <= E; e += kMbThreads) {
+        expert_off[e] = e == E ? -1 : 0;
+        tile_off[e] = 0;
+      }
+      if (tid == 0) counters[0] = counters[1] = 0;
+    }
     return;
   }
-  for (int e = tid; e < E; e += kScanThreads) {
-    int c = 0;
-    for (int b = 0; b < B; ++b) c += blk[int64_t(b) * (E + 1) + e];
-    tot[e] = c;
-    off[e] = c;
-    utile[e] = (c + tile_rows - 1) / tile_rows;
-  }
-  __syncthreads();
+  seg_count(f, sg, E, cw + w * E, &bad);
   block_exscan(off, E, wave_tot);
   const int n_utiles = block_exscan(utile, E, wave_tot);
-  for (int e = tid; e < E; e += kScanThreads) {
-    int run = off[e];
-    for (int b = 0; b < B; ++b) {
-      int32_t *p = blk + int64_t(b) * (E + 1) + e;
-      const int c = *p;
-      *p = run;
+  for (int e = tid; e < E; e += kMbThreads) {
+    int run = off[e] + pre[e];
+#pragma unroll
+    for (int ww = 0; ww < kMbWaves; ++ww) {
+      const int c = cw[ww * E + e];
+      cw[ww * E + e] = run;
       run += c;
     }
+  }
+  __syncthreads();
+  seg_rank(f, sg, K, E, cw + w * E, order, inv_order, row_map);
+  if (b != 0) return;
+  for (int e = tid; e < E; e += kMbThreads) {
     expert_off[e] = off[e];
     tile_off[e] = utile[e];
   }
   if (tid == 0) {
     expert_off[E] = N;
     tile_off[E] = n_utiles;
-    counters[2] = 0;
   }
   __syncthreads();
-  emit_plan(off, tot, scr0, scr1, wave_tot, E, S, N, T, tr, counters, act_items, tiles);
-}
-
-__global__ __launch_bounds__(kMbThreads) void dispatch_rank_kernel(
-    const int32_t *__restrict__ f, int N, int K, int E, int seg, const int32_t *__restrict__ blk,
-    const int32_t *counters, int32_t *__restrict__ order, int32_t *__restrict__ inv_order,
-    int32_t *__restrict__ row_map) {
-  if (counters[2]) return;  // out-of-range id: the scan kernel wrote the -1 result
-  extern __shared__ int32_t lds[];  // [kMbWaves][E] counts, then run bases
-  __shared__ int32_t bad;
-  const int tid = threadIdx.x, w = tid >> 6;
-  for (int q = tid; q < kMbWaves * E; q += kMbThreads) lds[q] = 0;
-  if (tid == 0) bad = 0;
-  __syncthreads();
-  int i0, i1;
-  mb_segment(N, seg, i0, i1);
-  Segment sg;
-  seg_load(f, i0, i1, sg);
-  seg_count(f, sg, E, lds + w * E, &bad);
-  __syncthreads();
-  const int32_t *row = blk + int64_t(blockIdx.x) * (E + 1);
-  for (int e = tid; e < E; e += kMbThreads) {
-    int run = row[e];
-#pragma unroll
-    for (int ww = 0; ww < kMbWaves; ++ww) {
-      const int c = lds[ww * E + e];
-      lds[ww * E + e] = run;
-      run += c;
-    }
-  }
-  __syncthreads();
-  seg_rank(f, sg, K, E, lds + w * E, order, inv_order, row_map);
+  emit_plan(off, tot, pre, scr1, wave_tot, E, S, N, T, tr, counters, act_items, tiles);
 }
 
 __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *__restrict__ expert_off,
@@ -461,11 +481,9 @@ void launch_dispatch(const moe_layer_desc *d, int32_t T, const int32_t *idx, int
     const int B = (N + seg - 1) / seg;
     const size_t lds_w = size_t(kMbWaves) * E * sizeof(int32_t);
     hipLaunchKernelGGL(dispatch_count_kernel, dim3(B), dim3(kMbThreads), lds_w, s, idx, N, E, seg, scratch);
-    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), size_t(5 * E) * sizeof(int32_t), s,
-                       scratch, B, N, E, d->n_shared, T, tile_rows, tr, order, inv_order, row_map, expert_off,
-                       tile_off, counters, act_items, tiles);
-    hipLaunchKernelGGL(dispatch_rank_kernel, dim3(B), dim3(kMbThreads), lds_w, s, idx, N, d->top_k, E, seg,
-                       scratch, counters, order, inv_order, row_map);
+    hipLaunchKernelGGL(dispatch_rank_kernel, dim3(B), dim3(kMbThreads), lds_w + size_t(5 * E) * sizeof(int32_t), s,
+                       idx, N, d->top_k, E, d->n_shared, T, seg, B, tile_rows, tr, scratch, order, inv_order, row_map,
+                       expert_off, tile_off, counters, act_items, tiles);
   }
   if (mk) mk->mark("dispatch");
 }

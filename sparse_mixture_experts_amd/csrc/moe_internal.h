@@ -42,7 +42,7 @@ struct Workspace {
   size_t route;                       // router logits / chunk partials (f32)
   size_t order, inv_order, row_map;   // [N] int32
   size_t expert_off, tile_off;        // [E+1] int32
-  size_t counters;                    // 64 int32: [0] active items, [1] tiles, [2] dispatch error
+  size_t counters;                    // 64 int32: [0] active items, [1] tiles
   size_t dsp;                         // dispatch scratch (dispatch_scratch_ints)
   size_t act_items;                   // [E+S] PlanItem
   size_t tiles;                       // [max_tiles] PlanItem

@@ -89,19 +89,19 @@ __global__ __launch_bounds__(kThreads) void router_transpose_kernel(const uint16
 }
 
 // ---- 2. L~ = x . W + bias on MFMA ------------------------------------------
-// Block tile 64 experts x 64 tokens; wave (we, wt) owns 32 x 32 = 2 x 2 MFMA
-// tiles.  Operand A = WT rows (experts), operand B = x rows (tokens); a lane's
-// 4 results are 4 consecutive experts of one token.
+// Block tile 64 experts x 64 tokens, 8 waves; wave (we, wt) owns 32 experts x
+// 16 tokens = 2 MFMA tiles.  Operand A = WT rows (experts), operand B = x rows
+// (tokens); a lane's 4 results are 4 consecutive experts of one token.
 // The blocks of the first token tile also add up the squared-norm partials of
 // their 64 experts: normp[n_kb][e] -> normp[n_kb + 0 * E + e] (the row after
 // the partials).
-__global__ __launch_bounds__(kThreads) void router_mfma_kernel(const uint16_t *__restrict__ x,
-                                                               const uint16_t *__restrict__ wt,
-                                                               const float *__restrict__ bias,
-                                                               float *__restrict__ normp, int n_kb, int T, int D,
-                                                               int E, float *__restrict__ lt) {
-  __shared__ uint16_t sa[2][64][kChunk + 8];
-  __shared__ uint16_t sb[2][64][kChunk + 8];
+constexpr int kMfThreads = 512;
+__global__ __launch_bounds__(kMfThreads) void router_mfma_kernel(const uint16_t *__restrict__ x,
+                                                                 const uint16_t *__restrict__ wt,
+                                                                 const float *__restrict__ bias,
+                                                                 float *__restrict__ normp, int n_kb, int T,
+                                                                 int D, int E, float *__restrict__ lt) {
+  __shared__ uint16_t sab[2][2][64][kChunk + 8];  // [buffer][expert tile, token tile][row][col]
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
   const int lr = lane & 15, lg = lane >> 4;
   const int e0 = blockIdx.x * 64, t0 = blockIdx.y * 64;
@@ -110,35 +110,31 @@ __global__ __launch_bounds__(kThreads) void router_mfma_kernel(const uint16_t *_
     for (int kb = 0; kb < n_kb; ++kb) s += normp[int64_t(kb) * E + e0 + tid];
     normp[int64_t(n_kb) * E + e0 + tid] = s;
   }
-  const int we = wave / 2, wtk = wave % 2;
-  f32x4 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int we = wave / 4, wtk = wave % 4;
+  f32x4 acc[2];
+  acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // staging: thread -> (row tid / 4, 16 columns (tid % 4) * 16) of both
-  // tiles.  Chunk c+2 is loaded into registers while chunk c is multiplied
-  // from one LDS buffer and chunk c+1 is written to the other.
-  const int sr = tid / 4, sc = (tid % 4) * 16;
-  const int ea = min(e0 + sr, E - 1), tb = min(t0 + sr, T - 1);
-  const bool oka = e0 + sr < E, okb = t0 + sr < T;
+  // staging: threads 0..255 fill the expert tile, 256..511 the token tile;
+  // thread -> (row (tid % 256) / 4, 16 columns (tid % 4) * 16).  Chunk c+2 is
+  // loaded into registers while chunk c is multiplied from one LDS buffer and
+  // chunk c+1 is written to the other.
+  const int which = tid / 256;  // 0: experts, 1: tokens
+  const int sr = (tid % 256) / 4, sc = (tid % 4) * 16;
+  const int64_t src = which == 0 ? int64_t(min(e0 + sr, E - 1)) * D : int64_t(min(t0 + sr, T - 1)) * D;
+  const uint16_t *sbase = which == 0 ? wt : x;
+  const bool ok = which == 0 ? e0 + sr < E : t0 + sr < T;
   const int C = D / kChunk;
-  auto keep = [](bool ok, uint4 v) {
-    return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+  struct Stage { uint4 v0, v1; };
+  auto load = [&](int c, Stage &st) __attribute__((always_inline)) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(sbase + src + min(c, C - 1) * kChunk + sc);
+    st.v0 = p[0];
+    st.v1 = p[1];
   };
-  struct Stage { uint4 a0, a1, b0, b1; };
-  auto load = [&](int c, Stage &st) {
-    const int k0 = min(c, C - 1) * kChunk;
-    const uint4 *pa = reinterpret_cast<const uint4 *>(wt + int64_t(ea) * D + k0 + sc);
-    const uint4 *pb = reinterpret_cast<const uint4 *>(x + int64_t(tb) * D + k0 + sc);
-    st.a0 = pa[0]; st.a1 = pa[1]; st.b0 = pb[0]; st.b1 = pb[1];
-  };
-  auto store = [&](int buf, const Stage &st) {
-    *reinterpret_cast<uint4 *>(&sa[buf][sr][sc]) = keep(oka, st.a0);
-    *reinterpret_cast<uint4 *>(&sa[buf][sr][sc + 8]) = keep(oka, st.a1);
-    *reinterpret_cast<uint4 *>(&sb[buf][sr][sc]) = keep(okb, st.b0);
-    *reinterpret_cast<uint4 *>(&sb[buf][sr][sc + 8]) = keep(okb, st.b1);
+  auto store = [&](int buf, const Stage &st) __attribute__((always_inline)) {
+    // per-component select: a select of whole uint4 values goes through scratch
+    auto keep = [&](uint4 v) { return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u); };
+    *reinterpret_cast<uint4 *>(&sab[buf][which][sr][sc]) = keep(st.v0);
+    *reinterpret_cast<uint4 *>(&sab[buf][which][sr][sc + 8]) = keep(st.v1);
   };
   Stage ring[2];
   load(0, ring[0]);
@@ -149,23 +145,22 @@ __global__ __launch_bounds__(kThreads) void router_mfma_kernel(const uint16_t *_
   // chunk c from LDS buffer buf; then chunk c+1 (held in nx) to the other
   // buffer, whose last readers (chunk c-1) are past the previous barrier, and
   // chunk c+3 into nx.
-  auto step = [&](int c, int buf, Stage &nx) {
-    bf16x8 av[2][2], bv[2][2];
+  auto step = [&](int c, int buf, Stage &nx) __attribute__((always_inline)) {
+    bf16x8 av[2][2], bv[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        av[i][j] = *reinterpret_cast<const bf16x8 *>(&sa[buf][we * 32 + i * 16 + lr][lg * 16 + j * 8]);
-        bv[i][j] = *reinterpret_cast<const bf16x8 *>(&sb[buf][wtk * 32 + i * 16 + lr][lg * 16 + j * 8]);
-      }
+      for (int j = 0; j < 2; ++j)
+        av[i][j] = *reinterpret_cast<const bf16x8 *>(&sab[buf][0][we * 32 + i * 16 + lr][lg * 16 + j * 8]);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 2; ++j)
+      bv[j] = *reinterpret_cast<const bf16x8 *>(&sab[buf][1][wtk * 16 + lr][lg * 16 + j * 8]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i][0], bv[j][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i][1], bv[j][1], d, 0, 0, 0);
-        acc[i][j] += d;
-      }
+    for (int i = 0; i < 2; ++i) {
+      f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i][0], bv[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i][1], bv[1], d, 0, 0, 0);
+      acc[i] += d;
+    }
     store(buf ^ 1, nx);
     load(c + 3, nx);
     __syncthreads();
@@ -174,20 +169,17 @@ __global__ __launch_bounds__(kThreads) void router_mfma_kernel(const uint16_t *_
     step(c, 0, ring[1]);
     if (c + 1 < C) step(c + 1, 1, ring[0]);
   }
+  const int t = t0 + wtk * 16 + lr;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 2; ++i) {
+    const int eb = e0 + we * 32 + i * 16 + lg * 4;
+    const f32x4 v = acc[i];
+    if (t < T) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int t = t0 + wtk * 32 + j * 16 + lr;
-      const int eb = e0 + we * 32 + i * 16 + lg * 4;
-      const f32x4 v = acc[i][j];
-      if (t < T) {
-        if (eb + 0 < E) lt[int64_t(t) * E + eb + 0] = v[0] + (bias ? bias[eb + 0] : 0.0f);
-        if (eb + 1 < E) lt[int64_t(t) * E + eb + 1] = v[1] + (bias ? bias[eb + 1] : 0.0f);
-        if (eb + 2 < E) lt[int64_t(t) * E + eb + 2] = v[2] + (bias ? bias[eb + 2] : 0.0f);
-        if (eb + 3 < E) lt[int64_t(t) * E + eb + 3] = v[3] + (bias ? bias[eb + 3] : 0.0f);
-      }
+      for (int q = 0; q < 4; ++q)
+        if (eb + q < E) lt[int64_t(t) * E + eb + q] = v[q] + (bias ? bias[eb + q] : 0.0f);
     }
+  }
 }
 
 // ---- 3. candidates, exact recomputation, selection -------------------------
@@ -220,17 +212,31 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
     const int e = lane + kWave * m;
     lv[m] = e < E ? a.lt[int64_t(t) * E + e] : -INFINITY;
   }
+  // ||x_t||^2: d <= 64 * 64 gives at most 8 pieces of 8 per lane, all loaded together
   float xs = 0.f;
-  for (int k = lane * 8; k < D; k += kWave * 8) {
-    const uint4 v = *reinterpret_cast<const uint4 *>(a.x + int64_t(t) * D + k);
-    const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                        bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+  {
+    uint4 xv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xs = __builtin_fmaf(f[i], f[i], xs);
+    for (int q = 0; q < 8; ++q) {
+      const int k = min((q * kWave + lane) * 8, D - 8);
+      xv[q] = *reinterpret_cast<const uint4 *>(a.x + int64_t(t) * D + k);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if ((q * kWave + lane) * 8 < D) {
+        const uint4 v = xv[q];
+        const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                            bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xs = __builtin_fmaf(f[i], f[i], xs);
+      }
+    }
   }
   xs = wave_sum(xs);
   float wn = 0.f, bmax = 0.f;
-  for (int e = lane; e < E; e += kWave) {
+#pragma unroll
+  for (int m = 0; m < MPL; ++m) {
+    const int e = min(lane + kWave * m, E - 1);  // repeats of expert E-1 do not change a max
     wn = fmaxf(wn, a.wnorm[e]);
     if (a.bias) bmax = fmaxf(bmax, fabsf(a.bias[e]));
   }
@@ -303,12 +309,18 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
     const uint4 v = *reinterpret_cast<const uint4 *>(a.x + int64_t(t) * D + ch * kChunk + q * 8);
     xw[4 * q] = v.x; xw[4 * q + 1] = v.y; xw[4 * q + 2] = v.z; xw[4 * q + 3] = v.w;
   }
-  auto chain = [&](const uint16_t *wr) -> float {
+  // Lane (slot, ch) takes candidates slot, slot + slots, ...; the router row
+  // chunk of the next one is loaded while the current chain runs.
+  auto load_row = [&](int e, uint4 (&v)[8]) {
+    const uint4 *wr = reinterpret_cast<const uint4 *>(a.wt + int64_t(e) * D + ch * kChunk);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = wr[q];
+  };
+  auto chain = [&](const uint4 (&v)[8]) -> float {
     float part = 0.f;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(wr + q * 8);
-      const uint32_t wv4[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t wv4[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         part = __builtin_fmaf(bf16_lo(xw[4 * q + h]), bf16_lo(wv4[h]), part);
@@ -319,15 +331,18 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
   };
   for (int b0 = 0; b0 < n; b0 += kBatch) {
     const int nb = min(kBatch, n - b0);
-    for (int r = slot; r < nb; r += 2 * slots) {
-      const int r2 = r + slots;
-      const int e1 = s_e[wv][b0 + r], e2 = s_e[wv][b0 + min(r2, nb - 1)];
-      const float p1 = chain(a.wt + int64_t(e1) * D + ch * kChunk);
-      const float p2 = chain(a.wt + int64_t(e2) * D + ch * kChunk);
-      if (lane_on) {
-        s_part[wv][r][ch] = p1;
-        if (r2 < nb) s_part[wv][r2][ch] = p2;
-      }
+    uint4 va[8], vb[8];
+    int r = slot;
+    load_row(s_e[wv][b0 + min(r, nb - 1)], va);
+    // two candidates per turn, alternating buffers (no dynamic register indexing)
+    for (; r < nb; r += 2 * slots) {
+      load_row(s_e[wv][b0 + min(r + slots, nb - 1)], vb);
+      const float pa = chain(va);
+      if (lane_on) s_part[wv][r][ch] = pa;
+      if (r + slots >= nb) break;
+      load_row(s_e[wv][b0 + min(r + 2 * slots, nb - 1)], va);
+      const float pb = chain(vb);
+      if (lane_on) s_part[wv][r + slots][ch] = pb;
     }
     __builtin_amdgcn_wave_barrier();
     if (lane < nb) {
@@ -412,7 +427,7 @@ void launch_route_mfma(const moe_layer_desc *d, int32_t T, const void *x, const 
   float *normp = scratch + o_np;
   hipLaunchKernelGGL(router_transpose_kernel, dim3((E + 63) / 64, nkb), dim3(kThreads), 0, s,
                      static_cast<const uint16_t *>(w_router), D, E, wt, normp);
-  hipLaunchKernelGGL(router_mfma_kernel, dim3((E + 63) / 64, (T + 63) / 64), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL(router_mfma_kernel, dim3((E + 63) / 64, (T + 63) / 64), dim3(kMfThreads), 0, s,
                      static_cast<const uint16_t *>(x), wt, bias, normp, nkb, T, D, E, lt);
   if (mk) mk->mark("route_mfma");
   // |L~ - L| <= gamma * S: two MFMAs per chunk counted as 128 sequential
