@@ -38,8 +38,12 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
-__device__ __forceinline__ float sigmoid_f32(float g) { return 1.0f / (1.0f + expf(-g)); }
+// Sigmoid and SiLU on the hardware exp2 and reciprocal (a few ulp of fp32;
+// the per-op bf16 rounding that follows in the rounded SwiGLU hides them).
+__device__ __forceinline__ float sigmoid_f32(float g) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504f));
+}
+__device__ __forceinline__ float silu_f32(float g) { return g * sigmoid_f32(g); }
 
 // SwiGLU of one (gate, up) pair.  With per-op rounding: gate and up rounded to
 // bf16, then sigmoid, g*s and (g*s)*u each rounded to bf16.

@@ -514,6 +514,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     float hv[RB][NTH][4];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
+      if (rb * 16 >= tile.rows) break;  // row blocks past the tile (uniform)
       const float xs = pow2(rsh[rb * 16 + lr]);
       float mx = 0.f;
 #pragma unroll
@@ -532,6 +533,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     if (!col_ok) return;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
+      if (rb * 16 >= tile.rows) break;
       const int m = rb * 16 + lr;
       float mx = rmax[0][m];
 #pragma unroll
