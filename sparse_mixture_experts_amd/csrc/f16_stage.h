@@ -1,0 +1,100 @@
+// f16_stage.h -- the fp16 staging format of the 4-bit matrix-core GEMMs.
+//
+// Activations of 4-bit layers are multiplied as fp16.  A row is stored as
+// fp16 x * 2^-e with one power-of-two exponent e per row (f16_shift), and
+// every 8-element block permuted to e0,e4,e1,e5,e2,e6,e3,e7, the order in
+// which the GEMMs expand a word of eight 4-bit codes.  bf16 -> fp16 is exact
+// for values in fp16's normal range.
+#pragma once
+
+#include "device_common.h"
+
+namespace moe {
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// 16-bit elements e0..e7 -> e0,e4,e1,e5,e2,e6,e3,e7 (the order of q4_word_to_f16).
+__device__ __forceinline__ uint4 permute8(uint4 v) {
+  uint4 r;
+  r.x = (v.x & 0xffffu) | (v.z << 16);
+  r.y = (v.x >> 16) | (v.z & 0xffff0000u);
+  r.z = (v.y & 0xffffu) | (v.w << 16);
+  r.w = (v.y >> 16) | (v.w & 0xffff0000u);
+  return r;
+}
+
+// Power-of-two exponent e for a nonnegative magnitude, nonzero only when
+// needed: mag * 2^-e lies below 2^15 (fp16 range with headroom), and
+// magnitudes below 2^-10 (whose small elements would fall into fp16
+// subnormals) are brought to [1, 2).  Zero needs no exponent.
+__device__ __forceinline__ int f16_shift(float mag) {
+  const int ex = int((__float_as_uint(mag) >> 23) & 0xffu) - 127;  // floor(log2(mag)) for normal mag
+  if (ex >= 15) return ex - 14;
+  if (mag > 0.f && ex < -10) return max(ex, -100);
+  return 0;
+}
+__device__ __forceinline__ float pow2(int e) { return __uint_as_float(uint32_t(127 + e) << 23); }
+
+// Eight bf16 values scaled by 2^-sh as packed fp16 (two per word).
+__device__ __forceinline__ uint4 bf16x8_to_f16(uint4 v, int sh) {
+  const float m = pow2(-sh);
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2_t p = {(_Float16)(bf16_lo(u[i]) * m), (_Float16)(bf16_hi(u[i]) * m)};
+    o[i] = __builtin_bit_cast(uint32_t, p);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__device__ __forceinline__ float absmax8_bf16(uint4 v) {
+  const float a = fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))), fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y))));
+  const float b = fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))), fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w))));
+  return fmaxf(a, b);
+}
+
+// One wave converts row x[0..D) (bf16, D a multiple of 8) to out[0..D) in
+// the staging format and writes its exponent to *sh_out (lane 0).
+__device__ __forceinline__ void row_to_f16(const uint16_t *x, int D, uint16_t *out, int8_t *sh_out) {
+  const int lane = lane_id();
+  const uint4 *src = reinterpret_cast<const uint4 *>(x);
+  uint4 *dst = reinterpret_cast<uint4 *>(out);
+  const int P = D / 8;
+  float mx = 0.f;
+  for (int p = lane; p < P; p += kWave) mx = fmaxf(mx, absmax8_bf16(src[p]));
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  const int sh = f16_shift(mx);
+  for (int p = lane; p < P; p += kWave) dst[p] = permute8(bf16x8_to_f16(src[p], sh));
+  if (lane == 0) *sh_out = int8_t(sh);
+}
+
+// The same conversion split in two phases for kernels that already hold one
+// wave per token (d <= 4096: at most 8 pieces of 8 per lane): row_f16_load
+// issues the loads early, row_f16_store converts and stores them later.
+constexpr int kRowF16MaxD = kWave * 8 * 8;
+struct RowF16 {
+  uint4 v[8];
+};
+__device__ __forceinline__ void row_f16_load(const uint16_t *x, int D, RowF16 &r) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int q = 0; q < 8; ++q) r.v[q] = reinterpret_cast<const uint4 *>(x)[min(q * kWave + lane, D / 8 - 1)];
+}
+__device__ __forceinline__ void row_f16_store(const RowF16 &r, int D, uint16_t *out, int8_t *sh_out) {
+  const int lane = lane_id();
+  float mx = 0.f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    if ((q * kWave + lane) * 8 < D) mx = fmaxf(mx, absmax8_bf16(r.v[q]));
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  const int sh = f16_shift(mx);
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    if ((q * kWave + lane) * 8 < D) reinterpret_cast<uint4 *>(out)[q * kWave + lane] = permute8(bf16x8_to_f16(r.v[q], sh));
+  if (lane == 0) *sh_out = int8_t(sh);
+}
+
+}  // namespace moe

@@ -43,6 +43,7 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "f16_stage.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -92,65 +93,12 @@ __device__ __forceinline__ f16x8 q4_word_to_f16(uint32_t w, h2 s2, h2 s2_16, h2 
   return __builtin_bit_cast(f16x8, r);
 }
 
-// 16-bit elements e0..e7 -> e0,e4,e1,e5,e2,e6,e3,e7 (the order of q4_word_to_f16).
-__device__ __forceinline__ uint4 permute8(uint4 v) {
-  uint4 r;
-  r.x = (v.x & 0xffffu) | (v.z << 16);
-  r.y = (v.x >> 16) | (v.z & 0xffff0000u);
-  r.z = (v.y & 0xffffu) | (v.w << 16);
-  r.w = (v.y >> 16) | (v.w & 0xffff0000u);
-  return r;
-}
-
-// Power-of-two exponent e for a nonnegative magnitude, nonzero only when
-// needed: mag * 2^-e lies below 2^15 (fp16 range with headroom), and
-// magnitudes below 2^-10 (whose small elements would fall into fp16
-// subnormals) are brought to [1, 2).  Zero needs no exponent.
-__device__ __forceinline__ int f16_shift(float mag) {
-  const int ex = int((__float_as_uint(mag) >> 23) & 0xffu) - 127;  // floor(log2(mag)) for normal mag
-  if (ex >= 15) return ex - 14;
-  if (mag > 0.f && ex < -10) return max(ex, -100);
-  return 0;
-}
-__device__ __forceinline__ float pow2(int e) { return __uint_as_float(uint32_t(127 + e) << 23); }
-
-// Eight bf16 values scaled by 2^-sh as packed fp16 (two per word).
-__device__ __forceinline__ uint4 bf16x8_to_f16(uint4 v, int sh) {
-  const float m = pow2(-sh);
-  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-  uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const h2 p = {(_Float16)(bf16_lo(u[i]) * m), (_Float16)(bf16_hi(u[i]) * m)};
-    o[i] = __builtin_bit_cast(uint32_t, p);
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
-}
-
-__device__ __forceinline__ float absmax8_bf16(uint4 v) {
-  const float a = fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))), fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y))));
-  const float b = fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))), fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w))));
-  return fmaxf(a, b);
-}
-
-// x [T][D] bf16 -> fp16 copy for the 4-bit GEMMs.  One wave per token row:
-// the row's largest |x| gives its exponent e (f16_shift); the row is stored
-// as fp16 x * 2^-e in the staging order of q4_word_to_f16 (every 8-element
-// block permuted).  bf16 -> fp16 is exact for values in fp16's normal range.
+// x [T][D] bf16 -> fp16 staging copy (row_to_f16), one wave per token.
 __global__ __launch_bounds__(256) void act_f16_kernel(const uint16_t *x, int T, int D, uint16_t *x16,
                                                       int8_t *xsh) {
-  const int t = blockIdx.x * (256 / kWave) + int(threadIdx.x) / kWave, lane = lane_id();
+  const int t = blockIdx.x * (256 / kWave) + int(threadIdx.x) / kWave;
   if (t >= T) return;  // whole waves
-  const uint4 *src = reinterpret_cast<const uint4 *>(x + int64_t(t) * D);
-  uint4 *dst = reinterpret_cast<uint4 *>(x16 + int64_t(t) * D);
-  const int P = D / 8;
-  float mx = 0.f;
-  for (int p = lane; p < P; p += kWave) mx = fmaxf(mx, absmax8_bf16(src[p]));
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-  const int sh = f16_shift(mx);
-  for (int p = lane; p < P; p += kWave) dst[p] = permute8(bf16x8_to_f16(src[p], sh));
-  if (lane == 0) xsh[t] = int8_t(sh);
+  row_to_f16(x + int64_t(t) * D, D, x16 + int64_t(t) * D, xsh + t);
 }
 
 struct GemmArgs {
@@ -623,7 +571,7 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
   const bool q4 = d->w_format == MOE_WF_AFFINE_Q4;
   const int tr = plan_tile_rows(d, T);
   const int nblk = (d->d_ff + kHBlock - 1) / kHBlock;
-  if (q4) {
+  if (q4 && !sc.x16_ready) {
     hipLaunchKernelGGL(act_f16_kernel, dim3((T + 3) / 4), dim3(256), 0, s, static_cast<const uint16_t *>(x), T,
                        d->d_model, static_cast<uint16_t *>(sc.x16), sc.xsh);
     if (mk) mk->mark("x_f16");

@@ -22,8 +22,9 @@ T *at(void *ws, size_t off) {
   return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
 }
 
-FfnScratch ffn_scratch(void *ws, const Workspace &L) {
-  return FfnScratch{at<void>(ws, L.h), at<int8_t>(ws, L.hsh), at<void>(ws, L.x16), at<int8_t>(ws, L.xsh)};
+FfnScratch ffn_scratch(void *ws, const Workspace &L, bool x16_ready) {
+  return FfnScratch{at<void>(ws, L.h), at<int8_t>(ws, L.hsh), at<void>(ws, L.x16), at<int8_t>(ws, L.xsh),
+                    x16_ready};
 }
 
 int check_ws(const moe_layer_desc *d, int32_t T, const void *ws, size_t ws_bytes, Workspace *out) {
@@ -67,7 +68,8 @@ int moe_route(const moe_layer_desc *desc, int32_t T, const void *x, const void *
   Workspace L;
   if ((s = check_ws(desc, T, ws, ws_bytes, &L))) return s;
   if (T == 0) return MOE_OK;
-  launch_route(desc, T, x, w_router, router_bias, topk_idx, topk_w, at<float>(ws, L.route), stream);
+  launch_route(desc, T, x, w_router, router_bias, topk_idx, topk_w, at<float>(ws, L.route), nullptr, nullptr,
+               stream);
   return hip_status();
 }
 
@@ -104,7 +106,7 @@ int moe_expert_ffn(const moe_layer_desc *desc, int32_t T, const void *x, const i
   launch_plan(desc, T, expert_off, at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items),
               at<PlanItem>(ws, L.tiles), stream);
   launch_expert_ffn(desc, T, x, row_map, w, at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items),
-                    at<PlanItem>(ws, L.tiles), L.max_tiles, ffn_scratch(ws, L), y_sorted, false, stream);
+                    at<PlanItem>(ws, L.tiles), L.max_tiles, ffn_scratch(ws, L, false), y_sorted, false, stream);
   return hip_status();
 }
 
@@ -137,14 +139,16 @@ static int forward_impl(const moe_layer_desc *desc, int32_t T, const void *x, co
   if (mk) mk->mark(nullptr);
   int32_t *idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.topk_idx);
   float *wt = topk_w_out ? topk_w_out : at<float>(ws, L.topk_w);
-  launch_route(desc, T, x, w->w_router, w->router_bias, idx, wt, at<float>(ws, L.route), stream, mk);
+  const bool x16_ready = route_writes_x16(desc);
+  launch_route(desc, T, x, w->w_router, w->router_bias, idx, wt, at<float>(ws, L.route), at<void>(ws, L.x16),
+               at<int8_t>(ws, L.xsh), stream, mk);
   launch_dispatch(desc, T, idx, 64, at<int32_t>(ws, L.order), at<int32_t>(ws, L.inv_order),
                   at<int32_t>(ws, L.row_map), at<int32_t>(ws, L.expert_off), at<int32_t>(ws, L.tile_off),
                   at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles),
                   at<int32_t>(ws, L.dsp), stream, mk);
   launch_expert_ffn(desc, T, x, at<int32_t>(ws, L.row_map), w, at<int32_t>(ws, L.counters),
                     at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles), L.max_tiles,
-                    ffn_scratch(ws, L), at<void>(ws, L.y_sorted), ys_bytes(desc) == 2, stream, mk);
+                    ffn_scratch(ws, L, x16_ready), at<void>(ws, L.y_sorted), ys_bytes(desc) == 2, stream, mk);
   launch_combine(desc, T, at<void>(ws, L.y_sorted), ys_bytes(desc) == 2, at<int32_t>(ws, L.inv_order), wt, y, out_dtype,
                  stream, mk);
   return hip_status();

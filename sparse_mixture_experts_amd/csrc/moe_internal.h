@@ -70,10 +70,14 @@ int64_t route_scratch_floats(const moe_layer_desc *d, int32_t T);
 bool route_mfma_applies(const moe_layer_desc *d, int32_t T);
 int64_t route_mfma_scratch_floats(const moe_layer_desc *d, int32_t T);
 void launch_route_mfma(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router, const float *bias,
-                       int32_t *idx, float *w, float *scratch, void *stream, StageMarker *mk);
+                       int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh, void *stream,
+                       StageMarker *mk);
+// x16/xsh (nullable): the router's per-token kernel also writes the fp16
+// staging copy of x for the 4-bit GEMMs when route_writes_x16 holds.
+bool route_writes_x16(const moe_layer_desc *d);
 void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router,
-                  const float *bias, int32_t *idx, float *w, float *scratch, void *stream,
-                  StageMarker *mk = nullptr);
+                  const float *bias, int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh,
+                  void *stream, StageMarker *mk = nullptr);
 
 // Dispatch: stable counting sort + prefix tables + the internal work plan.
 // scratch holds dispatch_scratch_ints ints (per-workgroup counts for large N).
@@ -96,6 +100,7 @@ struct FfnScratch {
   int8_t *hsh;
   void *x16;
   int8_t *xsh;
+  bool x16_ready;  // x16/xsh already written (by the router)
 };
 constexpr int kHBlock = 128;  // h columns per exponent block
 

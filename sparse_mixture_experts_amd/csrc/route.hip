@@ -25,6 +25,7 @@
 #include <algorithm>
 
 #include "device_common.h"
+#include "f16_stage.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -174,16 +175,15 @@ __global__ __launch_bounds__(kWave) void route_chunk_kernel(const void *__restri
   float p[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t) p[t] = 0.0f;
-  for (int i0 = 0; i0 < n; i0 += 16) {
-    float w[16];
+  // the whole chunk's router column is loaded at once (one memory round trip)
+  float w[kChunk];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) w[u] = i0 + u < n ? load_act<BF16>(wr, int64_t(kc + i0 + u) * E + ec) : 0.0f;
+  for (int u = 0; u < kChunk; ++u) w[u] = load_act<BF16>(wr, int64_t(kc + min(u, n - 1)) * E + ec);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      if (i0 + u < n) {
+  for (int u = 0; u < kChunk; ++u) {
+    if (u < n) {
 #pragma unroll
-        for (int t = 0; t < TT; ++t) p[t] = __builtin_fmaf(xs[i0 + u][t], w[u], p[t]);
-      }
+      for (int t = 0; t < TT; ++t) p[t] = __builtin_fmaf(xs[u][t], w[u], p[t]);
     }
   }
   if (e < E) {
@@ -195,16 +195,21 @@ __global__ __launch_bounds__(kWave) void route_chunk_kernel(const void *__restri
 
 // One wave per token: logits (summing chunk partials when n_chunks > 0),
 // top-k, softmax.  Each lane keeps the logits of experts lane + 64*m, m < MPL.
+// With x16 set (4-bit layers, d <= 4096), the wave also writes the token's
+// fp16 staging row for the expert GEMMs; its loads go out with the others.
 template <int MPL>
 __global__ __launch_bounds__(kThreads) void route_select_kernel(const float *__restrict__ in, int n_chunks,
                                                                 const float *__restrict__ bias, int T, int E,
                                                                 int K, int renorm, int32_t *__restrict__ idx_out,
-                                                                float *__restrict__ w_out) {
-  // chunk partials per load batch: about 32 loads in flight per lane
-  constexpr int CB = MPL >= 32 ? 1 : 32 / MPL;
+                                                                float *__restrict__ w_out, const uint16_t *x, int D,
+                                                                uint16_t *x16, int8_t *xsh) {
+  // chunk partials per load batch: about 64 loads in flight per lane
+  constexpr int CB = MPL >= 64 ? 1 : 64 / MPL;
   const int t = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
   const int lane = lane_id();
   if (t >= T) return;
+  RowF16 xr;
+  if (x16) row_f16_load(x + int64_t(t) * D, D, xr);
   float l[MPL];
   if (n_chunks == 0) {
 #pragma unroll
@@ -277,16 +282,22 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(const float *__r
     idx_out[int64_t(t) * K + lane] = my_e;
     w_out[int64_t(t) * K + lane] = w;
   }
+  if (x16) row_f16_store(xr, D, x16 + int64_t(t) * D, xsh + t);
 }
 
 void launch_select(const float *in, int n_chunks, const float *bias, int T, int E, int K, int renorm,
-                   int32_t *idx, float *w, hipStream_t s) {
+                   int32_t *idx, float *w, const void *x, int D, void *x16, int8_t *xsh, hipStream_t s) {
   const dim3 grid((T + kThreads / kWave - 1) / (kThreads / kWave)), block(kThreads);
-  if (E <= 64) hipLaunchKernelGGL(route_select_kernel<1>, grid, block, 0, s, in, n_chunks, bias, T, E, K, renorm, idx, w);
-  else if (E <= 128) hipLaunchKernelGGL(route_select_kernel<2>, grid, block, 0, s, in, n_chunks, bias, T, E, K, renorm, idx, w);
-  else if (E <= 256) hipLaunchKernelGGL(route_select_kernel<4>, grid, block, 0, s, in, n_chunks, bias, T, E, K, renorm, idx, w);
-  else if (E <= 512) hipLaunchKernelGGL(route_select_kernel<8>, grid, block, 0, s, in, n_chunks, bias, T, E, K, renorm, idx, w);
-  else hipLaunchKernelGGL(route_select_kernel<16>, grid, block, 0, s, in, n_chunks, bias, T, E, K, renorm, idx, w);
+  const uint16_t *xb = static_cast<const uint16_t *>(x);
+  uint16_t *xo = static_cast<uint16_t *>(x16);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, s, in, n_chunks, bias, T, E, K, renorm, idx, w, xb, D, xo, xsh);
+  };
+  if (E <= 64) go(route_select_kernel<1>);
+  else if (E <= 128) go(route_select_kernel<2>);
+  else if (E <= 256) go(route_select_kernel<4>);
+  else if (E <= 512) go(route_select_kernel<8>);
+  else go(route_select_kernel<16>);
 }
 
 // Returns true when one block held every chunk (the output is logits).
@@ -324,10 +335,16 @@ int64_t route_scratch_floats(const moe_layer_desc *d, int32_t T) {
   return n;
 }
 
+bool route_writes_x16(const moe_layer_desc *d) {
+  return d->w_format == MOE_WF_AFFINE_Q4 && d->d_model <= kRowF16MaxD;
+}
+
 void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router,
-                  const float *bias, int32_t *idx, float *w, float *scratch, void *stream, StageMarker *mk) {
+                  const float *bias, int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh,
+                  void *stream, StageMarker *mk) {
+  if (!route_writes_x16(d)) x16 = nullptr, xsh = nullptr;
   if (route_mfma_applies(d, T)) {
-    launch_route_mfma(d, T, x, w_router, bias, idx, w, scratch, stream, mk);
+    launch_route_mfma(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, stream, mk);
     return;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -353,7 +370,7 @@ void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void 
     n_chunks = full ? 0 : C;
   }
   if (mk) mk->mark("route_logits");
-  launch_select(scratch, n_chunks, bias, T, E, d->top_k, d->renormalize, idx, w, s);
+  launch_select(scratch, n_chunks, bias, T, E, d->top_k, d->renormalize, idx, w, x, D, x16, xsh, s);
   if (mk) mk->mark("route_select");
 }
 

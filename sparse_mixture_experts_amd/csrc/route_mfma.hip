@@ -24,6 +24,7 @@
 // the non-candidates there.  ("MoE Optimization COMPLETE", "Mega Kernel
 // Architecture": router matmul, softmax and top-K all on the GPU.)
 #include "device_common.h"
+#include "f16_stage.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -190,6 +191,8 @@ struct CertArgs {
   float gamma;
   int32_t *idx_out;
   float *w_out;
+  uint16_t *x16;  // nullable: fp16 staging copy of x for the 4-bit GEMMs
+  int8_t *xsh;
 };
 
 // One wave per token; each lane keeps L~ of experts lane + 64*m, m < MPL.
@@ -212,19 +215,16 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
     const int e = lane + kWave * m;
     lv[m] = e < E ? a.lt[int64_t(t) * E + e] : -INFINITY;
   }
-  // ||x_t||^2: d <= 64 * 64 gives at most 8 pieces of 8 per lane, all loaded together
+  // ||x_t||^2: d <= 64 * 64 gives at most 8 pieces of 8 per lane, all loaded
+  // together; the same registers give the fp16 staging row when asked.
   float xs = 0.f;
+  RowF16 xr;
+  row_f16_load(a.x + int64_t(t) * D, D, xr);
   {
-    uint4 xv[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int k = min((q * kWave + lane) * 8, D - 8);
-      xv[q] = *reinterpret_cast<const uint4 *>(a.x + int64_t(t) * D + k);
-    }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       if ((q * kWave + lane) * 8 < D) {
-        const uint4 v = xv[q];
+        const uint4 v = xr.v[q];
         const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                             bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
 #pragma unroll
@@ -233,6 +233,7 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
     }
   }
   xs = wave_sum(xs);
+  if (a.x16) row_f16_store(xr, D, a.x16 + int64_t(t) * D, a.xsh + t);  // xr dies here
   float wn = 0.f, bmax = 0.f;
 #pragma unroll
   for (int m = 0; m < MPL; ++m) {
@@ -418,7 +419,8 @@ int64_t route_mfma_scratch_floats(const moe_layer_desc *d, int32_t T) {
 }
 
 void launch_route_mfma(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router, const float *bias,
-                       int32_t *idx, float *w, float *scratch, void *stream, StageMarker *mk) {
+                       int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh, void *stream,
+                       StageMarker *mk) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int D = d->d_model, E = d->n_experts, nkb = (D + 255) / 256, C = D / kChunk;
   float *lt = scratch;
@@ -435,7 +437,7 @@ void launch_route_mfma(const moe_layer_desc *d, int32_t T, const void *x, const 
   // with a margin: (256 + 2C) units of 2^-24.
   const float gamma = float(256 + 2 * C) * 5.9604645e-8f;
   CertArgs ca{static_cast<const uint16_t *>(x), wt, bias, lt, normp + int64_t(nkb) * E, T, D, E, d->top_k, gamma,
-              idx, w};
+              idx, w, static_cast<uint16_t *>(x16), xsh};
   const dim3 grid((T + kThreads / kWave - 1) / (kThreads / kWave)), block(kThreads);
   if (E <= 64) hipLaunchKernelGGL(router_certify_kernel<1>, grid, block, 0, s, ca);
   else if (E <= 128) hipLaunchKernelGGL(router_certify_kernel<2>, grid, block, 0, s, ca);
