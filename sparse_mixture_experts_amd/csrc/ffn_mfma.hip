@@ -540,12 +540,235 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   }
 }
 
+// ---- decode tiles (at most 16 rows of an expert, K <= 2048) ----------------
+// One wave owns 16 weight rows and loads all of their codes and scales at
+// once (one memory round trip), while the workgroup stages the tile's
+// activation rows in LDS once; then the wave runs its K/32 MFMA steps with
+// no further barrier.  Exponents are per row over the whole K (weights: the
+// row's largest 15|s| + |b|; activations: the token's x exponent, or the h
+// row's largest value), so they are undone once in the epilogue.
+// gate/up: a wave's rows are 8 gate rows and the 8 up rows of the same
+// columns (the SwiGLU pairs sit 32 lanes apart in the MFMA result), h is
+// written as bf16.  down: 16 output columns, h read as bf16.
+constexpr int kDecMaxK = 2048;
+
+struct DecArgs {
+  const void *act;          // gate/up: fp16 staging copy of x [T][K]; down: h bf16 [rows][K]
+  const int8_t *act_sh;     // gate/up: token exponents [T]
+  const int32_t *row_map;   // gate/up only
+  int T, N, K, n_out, fused, round_ops;
+  const uint32_t *w0;       // gate (or gate_up) / down codes
+  const uint16_t *s0, *b0;
+  const uint32_t *w1;       // up codes (separate layout)
+  const uint16_t *s1, *b1;
+  const int32_t *counters;
+  const PlanItem *tiles;
+  void *out;                // gate/up: h bf16 [rows][F]; down: y [rows][D]
+  int out_bf16;
+};
+
+template <bool GATEUP, int kMaxSlabs>
+__global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecArgs a) {
+  constexpr int CPW = GATEUP ? 8 : 16;           // output columns per wave
+  extern __shared__ uint16_t xs[];               // [16][K + 8] activation rows, fp16 staging order
+  __shared__ uint32_t rmax_bits[16];             // down: row maxima of |h| (as float bits)
+
+  const int nbx = gridDim.x;
+  const int total = nbx * gridDim.y;
+  const int work = a.counters[1] * nbx;
+  const int lin = blockIdx.y * nbx + blockIdx.x;
+  const int per = (work + 7) / 8;
+  int item = lin;
+  if (8 * per <= total) {
+    const int slot = lin / 8;
+    if (slot >= per) return;
+    item = (lin % 8) * per + slot;
+  }
+  if (item >= work) return;
+  const int tile_id = item / nbx, bx = item % nbx;
+  const PlanItem tile = a.tiles[tile_id];
+
+  const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+  const int lr = lane & 15, lg = lane >> 4;
+  const int K = a.K, KW = K / 8, G = K / kGroup, nslab = (K + kKS - 1) / kKS;
+  // LDS rows hold whole slabs (K rounded up to 128, the tail zeroed) plus a
+  // pad that spreads the 16 rows over banks.
+  const int KR = nslab * kKS, XR = KR + 8;
+  const int col0 = (bx * kNW + wave) * CPW;
+  const bool col_ok = col0 < a.n_out;
+  const int colc = col_ok ? col0 : a.n_out - CPW;
+
+  // ---- this lane's weight row: codes and scales for the whole K ----
+  const bool up = GATEUP && lr >= 8;
+  const int rcol = colc + (GATEUP ? (lr & 7) : lr);
+  const int nre = (GATEUP && a.fused) ? 2 * a.n_out : a.n_out;  // rows of one expert's matrix
+  const int rin = (GATEUP && a.fused && up ? a.n_out : 0) + rcol;
+  const bool second = GATEUP && !a.fused && up;
+  const uint32_t *wrow = (second ? a.w1 : a.w0) + (int64_t(tile.expert) * nre + rin) * KW;
+  const uint16_t *sp = (second ? a.s1 : a.s0) + int64_t(tile.expert) * G * nre + rin;
+  const uint16_t *bp = (second ? a.b1 : a.b0) + int64_t(tile.expert) * G * nre + rin;
+  uint4 wq[kMaxSlabs];
+  uint16_t sr[kMaxSlabs], br[kMaxSlabs];
+#pragma unroll
+  for (int s = 0; s < kMaxSlabs; ++s) {
+    const int sc = min(s, nslab - 1);
+    wq[s] = *reinterpret_cast<const uint4 *>(wrow + min(sc * (kKS / 8) + lg * 4, KW - 4));
+    const int g = min(2 * sc + (lg >> 1), G - 1);
+    const bool ok = s < nslab && 2 * sc + (lg >> 1) < G;
+    const uint16_t sv = sp[int64_t(g) * nre], bv = bp[int64_t(g) * nre];
+    sr[s] = ok ? sv : uint16_t(0);
+    br[s] = ok ? bv : uint16_t(0);
+  }
+
+  // ---- stage the tile's activation rows (fp16 staging order) ----
+  const int P = K / 8;  // 16-byte pieces per row
+  if (tid < 16) rmax_bits[tid] = 0u;
+  for (int q = tid; q < 16 * (KR - K) / 8; q += kThreads) {
+    const int nz = (KR - K) / 8;
+    *reinterpret_cast<uint4 *>(&xs[(q / nz) * XR + K + (q % nz) * 8]) = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();
+  // Only the tile's own rows are staged: MFMA result column m depends only
+  // on activation row m, and the columns of rows past the tile are never
+  // stored, whatever those LDS rows hold.
+  const int nrow = min(tile.rows, 16);
+  if constexpr (GATEUP) {
+    for (int q = tid; q < nrow * P; q += kThreads) {
+      const int m = q / P, pc = q % P;
+      const int p = tile.row0 + m;
+      const int tok = p < a.N ? a.row_map[p] : (p - a.N) % a.T;
+      const int tk = unsigned(tok) < unsigned(a.T) ? tok : 0;
+      *reinterpret_cast<uint4 *>(&xs[m * XR + pc * 8]) =
+          reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.act) + int64_t(tk) * K)[pc];
+    }
+  } else {
+    // h rows (bf16): row maxima first, then fp16 with one exponent per row
+    // (the second pass re-reads the rows, now in cache)
+    for (int q0 = 0; q0 < nrow * P; q0 += 4 * kThreads) {
+      uint4 hv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = min(q0 + tid + i * kThreads, nrow * P - 1);
+        const int m = q / P, pc = q % P;
+        const int p = tile.row0 + m;
+        hv[i] = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.act) + int64_t(p) * K)[pc];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = q0 + tid + i * kThreads;
+        if (q < nrow * P) atomicMax(&rmax_bits[q / P], __float_as_uint(absmax8_bf16(hv[i])));
+      }
+    }
+    __syncthreads();
+    for (int q = tid; q < nrow * P; q += kThreads) {
+      const int m = q / P, pc = q % P;
+      const int p = tile.row0 + m;
+      const uint4 v = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.act) + int64_t(p) * K)[pc];
+      *reinterpret_cast<uint4 *>(&xs[m * XR + pc * 8]) = permute8(bf16x8_to_f16(v, f16_shift(__uint_as_float(rmax_bits[m]))));
+    }
+  }
+
+  // ---- weight row exponent over the whole K, fp16 scales ----
+  float wm = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxSlabs; ++s)
+    wm = fmaxf(wm, __builtin_fmaf(15.0f, fabsf(bf16_bits_to_f32(sr[s])), fabsf(bf16_bits_to_f32(br[s]))));
+  wm = fmaxf(wm, __shfl_xor(wm, 16, kWave));
+  wm = fmaxf(wm, __shfl_xor(wm, 32, kWave));
+  const int wsh = f16_shift(wm);  // exponent of weight row lr
+  const float wmul = pow2(-wsh);
+  __syncthreads();  // activation rows staged
+
+  uint32_t magic = 0x64006400u;
+  asm volatile("" : "+v"(magic));
+  const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kMaxSlabs; ++s) {
+    if (s < nslab) {
+      const _Float16 s16 = (_Float16)(bf16_bits_to_f32(sr[s]) * wmul), b16 = (_Float16)(bf16_bits_to_f32(br[s]) * wmul);
+      const h2 s2 = {s16, s16}, b2 = {b16, b16};
+      const h2 s2_16 = s2 * sixteenth;
+      const uint32_t wd[4] = {wq[s].x, wq[s].y, wq[s].z, wq[s].w};
+#pragma unroll
+      for (int j = 0; j < kSteps; ++j) {
+        const f16x8 bxv = *reinterpret_cast<const f16x8 *>(&xs[lr * XR + s * kKS + lg * 32 + j * 8]);
+        acc = mfma_f16(q4_word_to_f16(wd[j], s2, s2_16, b2, magic), bxv, acc);
+      }
+    }
+  }
+
+  // ---- epilogue: lane holds weight rows 4*lg + i of token row m = lr ----
+  // true value = acc * 2^(weight row exponent + activation row exponent)
+  const int m = lr;
+  int ash;
+  if constexpr (GATEUP) {
+    const int p = tile.row0 + min(m, tile.rows - 1);
+    const int tok = p < a.N ? a.row_map[p] : (p - a.N) % a.T;
+    ash = a.act_sh[unsigned(tok) < unsigned(a.T) ? tok : 0];
+  } else {
+    ash = f16_shift(__uint_as_float(rmax_bits[m]));
+  }
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int we = __shfl(wsh, 4 * lg + i, kWave);  // exponent of weight row 4*lg+i (held by lane lr = 4*lg+i)
+    v[i] = acc[i] * pow2(we + ash);
+  }
+  const int64_t row = tile.row0 + m;
+  if constexpr (GATEUP) {
+    float u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = __shfl_xor(v[i], 32, kWave);  // up rows 8 + 4*lg + i
+    if (col_ok && lg < 2 && m < tile.rows) {
+      uint32_t hb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16_bits(swiglu(v[i], u[i], a.round_ops));
+      *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + row * a.n_out + col0 + 4 * lg) =
+          make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+    }
+  } else if (col_ok && m < tile.rows) {
+    const int c = col0 + 4 * lg;
+    if (a.out_bf16) {
+      *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + row * a.n_out + c) =
+          make_uint2(f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+                     f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16));
+    } else {
+      *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + row * a.n_out + c) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
 template <bool GATEUP, bool Q4, int RB>
 void launch_one(const GemmArgs &ga, int64_t max_tiles, hipStream_t s) {
   constexpr int NTH = GATEUP ? kNT / 2 : kNT;
   const int cols_per_block = kNW * NTH * 16;
   const dim3 grid((ga.n_out + cols_per_block - 1) / cols_per_block, unsigned(max_tiles));
   hipLaunchKernelGGL((grouped_gemm_kernel<GATEUP, Q4, RB>), grid, dim3(kThreads), 0, s, ga);
+}
+
+template <bool GATEUP, int MS>
+void launch_decode_ms(const DecArgs &da, int64_t max_tiles, hipStream_t s) {
+  constexpr int CPW = GATEUP ? 8 : 16;
+  const int cols_per_block = kNW * CPW;
+  const size_t lds = size_t(16) * ((da.K + kKS - 1) / kKS * kKS + 8) * sizeof(uint16_t);
+  if (lds > 64 * 1024) {
+    // above the default dynamic-LDS limit (gfx950 has 160 KB per CU): raise it once
+    static const bool raised = [] {
+      return hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_gemm_kernel<GATEUP, MS>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 int(16 * (MS * kKS + 8) * sizeof(uint16_t))) == hipSuccess;
+    }();
+    (void)raised;
+  }
+  const dim3 grid((da.n_out + cols_per_block - 1) / cols_per_block, unsigned(max_tiles));
+  hipLaunchKernelGGL((decode_gemm_kernel<GATEUP, MS>), grid, dim3(kThreads), lds, s, da);
+}
+// K <= 1024: 8 slabs of registers; K <= 2048: 16.
+template <bool GATEUP>
+void launch_decode(const DecArgs &da, int64_t max_tiles, hipStream_t s) {
+  if (da.K <= 8 * kKS) launch_decode_ms<GATEUP, 8>(da, max_tiles, s);
+  else launch_decode_ms<GATEUP, 16>(da, max_tiles, s);
 }
 
 }  // namespace
@@ -585,7 +808,23 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
   GemmArgs dn{sc.h, sc.hsh, nullptr, nblk, nullptr, T, T * d->top_k, d->d_ff, d->d_model, 0, 0,
               w->down.w, static_cast<const uint16_t *>(w->down.scales), static_cast<const uint16_t *>(w->down.biases),
               nullptr, nullptr, nullptr, counters, tiles, y_sorted, ys_bf16};
-  if (tr == 16) {
+  if (tr == 16 && q4 && int64_t(T) * d->top_k <= d->n_experts && d->d_model <= kDecMaxK && d->d_ff <= kDecMaxK) {
+    // at most one routed row per expert on average: whole-K loads per wave
+    // (one memory round trip), h as bf16 between the two projections
+    DecArgs dg{q4 ? sc.x16 : x, sc.xsh, row_map, T, T * d->top_k, d->d_model, d->d_ff, d->gate_up_fused,
+               d->swiglu_round_bf16, static_cast<const uint32_t *>(pg.w), static_cast<const uint16_t *>(pg.scales),
+               static_cast<const uint16_t *>(pg.biases), static_cast<const uint32_t *>(w->up.w),
+               static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases), counters,
+               tiles, sc.h, 0};
+    DecArgs dd{sc.h, nullptr, nullptr, T, T * d->top_k, d->d_ff, d->d_model, 0, 0,
+               static_cast<const uint32_t *>(w->down.w), static_cast<const uint16_t *>(w->down.scales),
+               static_cast<const uint16_t *>(w->down.biases), nullptr, nullptr, nullptr, counters, tiles, y_sorted,
+               ys_bf16};
+    launch_decode<true>(dg, max_tiles, s);
+    if (mk) mk->mark("gateup_mfma");
+    launch_decode<false>(dd, max_tiles, s);
+    if (mk) mk->mark("down_mfma");
+  } else if (tr == 16) {
     if (q4) launch_one<true, true, 1>(gu, max_tiles, s);
     else launch_one<true, false, 1>(gu, max_tiles, s);
     if (mk) mk->mark("gateup_mfma");

@@ -35,6 +35,11 @@ MID = {
                                     top_k=3, n_shared=2, wfmt="q4", router_bias="zipf", seed=25),
     "mid-q4-decode": LayerSpec("mid-q4-decode", T=3, d_model=512, d_ff=256, n_experts=64, top_k=8,
                                wfmt="q4", seed=26),
+    # decode-sized tiles with reduction lengths of 64 mod 128, fused gate|up,
+    # per-op rounding and a shared expert
+    "mid-q4-decode-fused": LayerSpec("mid-q4-decode-fused", T=5, d_model=320, d_ff=192, n_experts=32,
+                                     top_k=4, n_shared=1, wfmt="q4", gate_up_fused=True,
+                                     swiglu_round_bf16=True, router_bias="zipf", seed=30),
     "mid-bf16-norenorm": LayerSpec("mid-bf16-norenorm", T=20, d_model=192, d_ff=64, n_experts=5, top_k=3,
                                    renormalize=False, seed=27),
     "mid-soft-routing": LayerSpec("mid-soft-routing", T=9, d_model=128, d_ff=64, n_experts=4, top_k=4,
@@ -237,14 +242,15 @@ def test_route_exact_ties_and_zero_rows(T):
     assert np.max(np.abs(wt - rw)) <= 1e-6
 
 
-def test_fp16_range_shifts():
+@pytest.mark.parametrize("T", [80, 6])
+def test_fp16_range_shifts(T):
     """Activations beyond the fp16 range (|x| up to 2^20) and 4-bit scales and
     biases beyond it (x 2^16) take the power-of-two shifted path of the fp16
     MFMA kernels in both projections; each token must still match the oracle
     to the tolerance, relative to that token's own largest output (a few
     columns carry almost all of the output here, so the usual RMS yardstick
     would measure bf16 rounding of h relative to a much smaller number)."""
-    spec = LayerSpec("big", T=80, d_model=256, d_ff=128, n_experts=8, top_k=2, wfmt="q4", seed=41)
+    spec = LayerSpec("big", T=T, d_model=256, d_ff=128, n_experts=8, top_k=2, wfmt="q4", seed=41)
     L = inputs.gen_layer(spec)
     x = L["x"].astype(np.uint32)
     x[3::9] += 20 << 7          # those rows times 2^20 (bf16 exponent field)
