@@ -338,7 +338,8 @@ def main():
     ap.add_argument("--config", default="q4-prefill-t2048")
     ap.add_argument("--sweep", default="q4-decode-t1,q4-decode-t32")
     ap.add_argument("--graph", action="store_true", help="replay captured HIP graphs in the timed loop")
-    ap.add_argument("--cpu-tokens", type=int, default=96)
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
+                    help="tokens of the headline workload the oracle runs for cpu_baseline (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a device copy of MIB MiB (scale for the HBM traffic counters)")
