@@ -97,6 +97,8 @@ def accounting(spec, touched: int):
     router = D * E * esz
     # expert outputs: bf16 where the matrix-core kernels write them, else fp32
     ysz = 2 if spec.act == "bf16" and D % 64 == 0 and F % 64 == 0 else 4
+    # the router's per-token kernel writes the fp16 staging copy of x (and reads x) for 4-bit layers
+    x16_bytes = (T * D * 2 + T) if spec.wfmt == "q4" and D <= 4096 else 0
     gateup = {"bound": "hbm", "bytes": int(w_touched * gu_frac) + T * D * esz + R * F * esz,
               "flops": 2 * R * 2 * D * F}
     down = {"bound": "hbm", "bytes": int(w_touched * down_frac) + R * F * esz + R * D * ysz, "flops": 2 * R * D * F}
@@ -107,11 +109,12 @@ def accounting(spec, touched: int):
         "kernels": {
             # VALU router: canonical-order logits (fp32 FMA chains), then top-k
             "route_logits": {"bound": "alu", "flops": 2 * T * D * E, "bytes": T * D * esz + router + T * E * 4},
-            "route_select": {"bound": "hbm", "bytes": T * E * 4 + N * 8},
+            "route_select": {"bound": "hbm", "bytes": T * E * 4 + N * 8 + x16_bytes},
             # matrix-core router: W transposed (read + write + read), x read, logits written
             "route_mfma": {"bound": "hbm", "bytes": 3 * router + T * D * esz + T * E * 4, "flops": 2 * T * D * E},
-            # certification: logits and x read, the k winners written
-            "route_certify": {"bound": "hbm", "bytes": T * E * 4 + T * D * esz + N * 8},
+            # certification: logits and x read, the k winners written (and the
+            # fp16 staging copy of x for 4-bit layers)
+            "route_certify": {"bound": "hbm", "bytes": T * E * 4 + T * D * esz + N * 8 + x16_bytes},
             "dispatch": {"bound": "hbm", "bytes": N * 4 * 4},
             # fp16 copy of x for the 4-bit GEMMs: x read, copy and token exponents written
             "x_f16": {"bound": "hbm", "bytes": 2 * T * D * esz + T},
