@@ -116,6 +116,8 @@ def accounting(spec, touched: int):
             # fp16 staging copy of x for 4-bit layers)
             "route_certify": {"bound": "hbm", "bytes": T * E * 4 + T * D * esz + N * 8 + x16_bytes},
             "dispatch": {"bound": "hbm", "bytes": N * 4 * 4},
+            # selection with the dispatch of a handful of slots folded in
+            "route_select_dispatch": {"bound": "hbm", "bytes": T * E * 4 + N * 8 + x16_bytes + N * 4 * 4},
             # fp16 copy of x for the 4-bit GEMMs: x read, copy and token exponents written
             "x_f16": {"bound": "hbm", "bytes": 2 * T * D * esz + T},
             "gateup_gemv": gateup, "down_gemv": down,
@@ -241,18 +243,21 @@ def path_dtype(spec) -> str:
 
 STAGE_SOURCES = {
     "route_logits": "route.hip", "route_select": "route.hip", "route_mfma": "route_mfma.hip",
-    "route_certify": "route_mfma.hip", "dispatch": "dispatch.hip", "x_f16": "ffn_mfma.hip", "gateup_gemv": "ffn_gemv.hip",
+    "route_certify": "route_mfma.hip", "route_select_dispatch": "route.hip", "dispatch": "dispatch.hip", "x_f16": "ffn_mfma.hip", "gateup_gemv": "ffn_gemv.hip",
     "down_gemv": "ffn_gemv.hip", "gateup_mfma": "ffn_mfma.hip", "down_mfma": "ffn_mfma.hip",
     "combine": "combine.hip",
 }
 
 
 def kernel_sources_digest(kernel: str) -> str:
-    """SHA-256 over the source of the stage's kernels and the shared device
-    headers (stamps the traffic counters taken for that stage)."""
+    """SHA-256 over the source of the stage's kernels and every header of the
+    library (stamps the traffic counters taken for that stage)."""
+    import glob
     import hashlib
     h = hashlib.sha256()
-    for f in [STAGE_SOURCES[kernel], "device_common.h", "moe_internal.h"]:
+    csrc = os.path.join(ROOT, "sparse_mixture_experts_amd", "csrc")
+    headers = sorted(os.path.basename(p) for p in glob.glob(os.path.join(csrc, "*.h")))
+    for f in [STAGE_SOURCES[kernel]] + headers:
         with open(os.path.join(ROOT, "sparse_mixture_experts_amd", "csrc", f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()

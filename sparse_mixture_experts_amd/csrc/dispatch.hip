@@ -21,6 +21,7 @@
 #include <algorithm>
 
 #include "device_common.h"
+#include "dispatch_tiny.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -435,6 +436,16 @@ __global__ __launch_bounds__(kMbThreads) void dispatch_rank_kernel(
   emit_plan(off, tot, pre, scr1, wave_tot, E, S, N, T, tr, counters, act_items, tiles);
 }
 
+// At most 128 slots: one wave does it all.
+__global__ __launch_bounds__(kWave) void dispatch_tiny_kernel(
+    const int32_t *__restrict__ f, int N, int K, int E, int S, int T, int tile_rows, int tr, int32_t *order,
+    int32_t *inv_order, int32_t *row_map, int32_t *expert_off, int32_t *tile_off, int32_t *counters,
+    PlanItem *act_items, PlanItem *tiles) {
+  __shared__ int32_t cnt[kMaxExperts];
+  tiny_dispatch(f, N, K, E, S, T, tile_rows, tr, order, inv_order, row_map, expert_off, tile_off, counters,
+                act_items, tiles, cnt);
+}
+
 __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *__restrict__ expert_off,
                                                         int N, int E, int S, int T, int tr,
                                                         int32_t *counters, PlanItem *act_items,
@@ -470,7 +481,10 @@ void launch_dispatch(const moe_layer_desc *d, int32_t T, const int32_t *idx, int
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int tr = plan_tile_rows(d, T);
   const int E = d->n_experts, N = T * d->top_k;
-  if (N <= kSingleBlockMax) {
+  if (N <= kTinyMaxN) {
+    hipLaunchKernelGGL(dispatch_tiny_kernel, dim3(1), dim3(kWave), 0, s, idx, N, d->top_k, E, d->n_shared, T,
+                       tile_rows, tr, order, inv_order, row_map, expert_off, tile_off, counters, act_items, tiles);
+  } else if (N <= kSingleBlockMax) {
     const int nw = kThreads / 64;
     const size_t lds = size_t(nw * E + 5 * E) * sizeof(int32_t);
     hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kThreads), lds, s, idx, N, d->top_k, E, d->n_shared, T,

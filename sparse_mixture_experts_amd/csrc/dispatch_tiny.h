@@ -1,0 +1,126 @@
+// dispatch_tiny.h -- the dispatch of a handful of routed rows in one wave.
+//
+// The same outputs as the workgroup dispatch (DS4Server issue #112, "Current
+// upstream route": order, inv_order, row_map; "Kernel contract": per-expert
+// row and tile prefix tables; plus the internal work plan) for N <= 128 flat
+// slots, computed by a single wave so that no workgroup barrier or second
+// kernel is needed: used by the dispatch entry point for small N and by the
+// router's selection kernel when every token of the call is in one
+// workgroup (decode).
+#pragma once
+
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kTinyMaxN = 2 * kWave;
+
+// f: the N expert ids (flat slot i = t*K + j), global or LDS.  cnt: LDS
+// scratch of E ints owned by this wave.  tile_rows: the caller's tile_off
+// granularity; tr: the row-tile height of the internal plan.
+__device__ __forceinline__ void tiny_dispatch(const int32_t *f, int N, int K, int E, int S, int T, int tile_rows,
+                                              int tr, int32_t *order, int32_t *inv_order, int32_t *row_map,
+                                              int32_t *expert_off, int32_t *tile_off, int32_t *counters,
+                                              PlanItem *act_items, PlanItem *tiles, int32_t *cnt) {
+  const int lane = lane_id();
+  const int e0 = lane < N ? f[lane] : 0, e1 = lane + kWave < N ? f[lane + kWave] : 0;
+  const bool bad = (lane < N && unsigned(e0) >= unsigned(E)) || (lane + kWave < N && unsigned(e1) >= unsigned(E));
+  if (__ballot(bad)) {
+    // Out-of-range expert id: an empty, in-bounds result with expert_off[E] = -1.
+    for (int i = lane; i < N; i += kWave) order[i] = inv_order[i] = row_map[i] = -1;
+    for (int e = lane; e <= E; e += kWave) {
+      expert_off[e] = e == E ? -1 : 0;
+      tile_off[e] = 0;
+    }
+    if (lane == 0) counters[0] = counters[1] = 0;
+    return;
+  }
+  for (int e = lane; e < E; e += kWave) cnt[e] = 0;
+  __builtin_amdgcn_wave_barrier();
+  if (lane < N) atomicAdd(&cnt[e0], 1);
+  if (lane + kWave < N) atomicAdd(&cnt[e1], 1);
+  __builtin_amdgcn_wave_barrier();
+
+  // Each lane owns a contiguous run of experts; exclusive scans of the rows,
+  // caller tiles, plan tiles and active experts of the runs.
+  const int chunk = (E + kWave - 1) / kWave;
+  const int b = min(E, lane * chunk), b1 = min(E, b + chunk);
+  int rs = 0, us = 0, ps = 0, as = 0;
+  for (int e = b; e < b1; ++e) {
+    const int c = cnt[e];
+    rs += c;
+    us += (c + tile_rows - 1) / tile_rows;
+    ps += (c + tr - 1) / tr;
+    as += c > 0;
+  }
+  int rx = rs, ux = us, px = ps, ax = as;  // inclusive scans
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int r2 = __shfl_up(rx, o, kWave), u2 = __shfl_up(ux, o, kWave);
+    const int p2 = __shfl_up(px, o, kWave), a2 = __shfl_up(ax, o, kWave);
+    if (lane >= o) {
+      rx += r2;
+      ux += u2;
+      px += p2;
+      ax += a2;
+    }
+  }
+  const int n_utiles = __shfl(ux, kWave - 1, kWave), n_ptiles = __shfl(px, kWave - 1, kWave);
+  const int n_act = __shfl(ax, kWave - 1, kWave);
+  int r = rx - rs, u = ux - us, pt = px - ps, ac = ax - as;  // exclusive bases of this lane's run
+  for (int e = b; e < b1; ++e) {
+    const int c = cnt[e];
+    expert_off[e] = r;
+    tile_off[e] = u;
+    if (c > 0) {
+      act_items[ac++] = PlanItem{e, r, c, 0};
+      for (int j = 0; j * tr < c; ++j) tiles[pt++] = PlanItem{e, r + j * tr, min(tr, c - j * tr), 0};
+    }
+    cnt[e] = r;  // run start of expert e, advanced by the ranking below
+    r += c;
+    u += (c + tile_rows - 1) / tile_rows;
+  }
+  const int shared_tiles = (T + tr - 1) / tr;
+  for (int q = lane; q < S * shared_tiles; q += kWave) {
+    const int s = q / shared_tiles, j = q % shared_tiles;
+    tiles[n_ptiles + q] = PlanItem{E + s, N + s * T + j * tr, min(tr, T - j * tr), 0};
+  }
+  for (int s = lane; s < S; s += kWave) act_items[n_act + s] = PlanItem{E + s, N + s * T, T, 0};
+  if (lane == 0) {
+    expert_off[E] = N;
+    tile_off[E] = n_utiles;
+    counters[0] = n_act + S;
+    counters[1] = n_ptiles + S * shared_tiles;
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // Stable positions, 64 slots at a time: lanes with the same expert find each
+  // other with ballots over the bits of the id.
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 1;
+  const uint64_t lt_mask = lane ? (~0ull >> (kWave - lane)) : 0ull;
+  volatile int32_t *base = cnt;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int i = half * kWave + lane;
+    const bool valid = i < N;
+    const int e = half ? e1 : e0;
+    uint64_t peers = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool on = (e >> bit) & 1;
+      const uint64_t bal = __ballot(valid && on);
+      peers &= on ? bal : ~bal;
+    }
+    if (valid) {
+      const int pos = base[e] + __popcll(peers & lt_mask);
+      order[pos] = i;
+      inv_order[i] = pos;
+      row_map[pos] = i / K;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (valid && lane == 63 - __clzll(peers)) base[e] = base[e] + __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+}  // namespace moe

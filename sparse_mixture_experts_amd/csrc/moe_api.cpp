@@ -69,7 +69,7 @@ int moe_route(const moe_layer_desc *desc, int32_t T, const void *x, const void *
   if ((s = check_ws(desc, T, ws, ws_bytes, &L))) return s;
   if (T == 0) return MOE_OK;
   launch_route(desc, T, x, w_router, router_bias, topk_idx, topk_w, at<float>(ws, L.route), nullptr, nullptr,
-               stream);
+               FusedDispatch{}, stream);
   return hip_status();
 }
 
@@ -140,12 +140,15 @@ static int forward_impl(const moe_layer_desc *desc, int32_t T, const void *x, co
   int32_t *idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.topk_idx);
   float *wt = topk_w_out ? topk_w_out : at<float>(ws, L.topk_w);
   const bool x16_ready = route_writes_x16(desc);
+  const FusedDispatch dsp{at<int32_t>(ws, L.order), at<int32_t>(ws, L.inv_order), at<int32_t>(ws, L.row_map),
+                          at<int32_t>(ws, L.expert_off), at<int32_t>(ws, L.tile_off), at<int32_t>(ws, L.counters),
+                          at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles), 64,
+                          plan_tile_rows(desc, T), desc->n_shared};
   launch_route(desc, T, x, w->w_router, w->router_bias, idx, wt, at<float>(ws, L.route), at<void>(ws, L.x16),
-               at<int8_t>(ws, L.xsh), stream, mk);
-  launch_dispatch(desc, T, idx, 64, at<int32_t>(ws, L.order), at<int32_t>(ws, L.inv_order),
-                  at<int32_t>(ws, L.row_map), at<int32_t>(ws, L.expert_off), at<int32_t>(ws, L.tile_off),
-                  at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles),
-                  at<int32_t>(ws, L.dsp), stream, mk);
+               at<int8_t>(ws, L.xsh), dsp, stream, mk);
+  if (!route_fuses_dispatch(desc, T))
+    launch_dispatch(desc, T, idx, 64, dsp.order, dsp.inv_order, dsp.row_map, dsp.expert_off, dsp.tile_off,
+                    dsp.counters, dsp.act_items, dsp.tiles, at<int32_t>(ws, L.dsp), stream, mk);
   launch_expert_ffn(desc, T, x, at<int32_t>(ws, L.row_map), w, at<int32_t>(ws, L.counters),
                     at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles), L.max_tiles,
                     ffn_scratch(ws, L, x16_ready), at<void>(ws, L.y_sorted), ys_bytes(desc) == 2, stream, mk);

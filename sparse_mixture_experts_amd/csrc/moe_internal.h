@@ -72,12 +72,21 @@ int64_t route_mfma_scratch_floats(const moe_layer_desc *d, int32_t T);
 void launch_route_mfma(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router, const float *bias,
                        int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh, void *stream,
                        StageMarker *mk);
+// Outputs of a dispatch that the router's selection kernel performs itself
+// (order == nullptr: none).
+struct FusedDispatch {
+  int32_t *order, *inv_order, *row_map, *expert_off, *tile_off, *counters;
+  PlanItem *act_items, *tiles;
+  int tile_rows, tr, S;
+};
 // x16/xsh (nullable): the router's per-token kernel also writes the fp16
-// staging copy of x for the 4-bit GEMMs when route_writes_x16 holds.
+// staging copy of x for the 4-bit GEMMs when route_writes_x16 holds.  With
+// dsp.order set and route_fuses_dispatch true it also does the dispatch.
 bool route_writes_x16(const moe_layer_desc *d);
+bool route_fuses_dispatch(const moe_layer_desc *d, int32_t T);
 void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router,
                   const float *bias, int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh,
-                  void *stream, StageMarker *mk = nullptr);
+                  const FusedDispatch &dsp, void *stream, StageMarker *mk = nullptr);
 
 // Dispatch: stable counting sort + prefix tables + the internal work plan.
 // scratch holds dispatch_scratch_ints ints (per-workgroup counts for large N).

@@ -25,6 +25,7 @@
 #include <algorithm>
 
 #include "device_common.h"
+#include "dispatch_tiny.h"
 #include "f16_stage.h"
 #include "moe_internal.h"
 
@@ -195,19 +196,15 @@ __global__ __launch_bounds__(kWave) void route_chunk_kernel(const void *__restri
 
 // One wave per token: logits (summing chunk partials when n_chunks > 0),
 // top-k, softmax.  Each lane keeps the logits of experts lane + 64*m, m < MPL.
-// With x16 set (4-bit layers, d <= 4096), the wave also writes the token's
-// fp16 staging row for the expert GEMMs; its loads go out with the others.
+// The per-token part of the selection kernel (one wave).
 template <int MPL>
-__global__ __launch_bounds__(kThreads) void route_select_kernel(const float *__restrict__ in, int n_chunks,
-                                                                const float *__restrict__ bias, int T, int E,
-                                                                int K, int renorm, int32_t *__restrict__ idx_out,
-                                                                float *__restrict__ w_out, const uint16_t *x, int D,
-                                                                uint16_t *x16, int8_t *xsh) {
+__device__ __forceinline__ void select_token(int t, const float *__restrict__ in, int n_chunks,
+                                             const float *__restrict__ bias, int T, int E, int K, int renorm,
+                                             int32_t *__restrict__ idx_out, float *__restrict__ w_out,
+                                             const uint16_t *x, int D, uint16_t *x16, int8_t *xsh, int32_t *s_f) {
   // chunk partials per load batch: about 64 loads in flight per lane
   constexpr int CB = MPL >= 64 ? 1 : 64 / MPL;
-  const int t = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
   const int lane = lane_id();
-  if (t >= T) return;
   RowF16 xr;
   if (x16) row_f16_load(x + int64_t(t) * D, D, xr);
   float l[MPL];
@@ -281,17 +278,42 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(const float *__r
   if (lane < K) {
     idx_out[int64_t(t) * K + lane] = my_e;
     w_out[int64_t(t) * K + lane] = w;
+    if (s_f) s_f[t * K + lane] = my_e;
   }
   if (x16) row_f16_store(xr, D, x16 + int64_t(t) * D, xsh + t);
 }
 
+// With x16 set (4-bit layers, d <= 4096), the wave also writes the token's
+// fp16 staging row for the expert GEMMs; its loads go out with the others.
+// With dsp.order set (all tokens in this one workgroup, T*k <= 128), the
+// selected ids also go to LDS and wave 0 then performs the dispatch.
+template <int MPL>
+__global__ __launch_bounds__(kThreads) void route_select_kernel(const float *__restrict__ in, int n_chunks,
+                                                                const float *__restrict__ bias, int T, int E,
+                                                                int K, int renorm, int32_t *__restrict__ idx_out,
+                                                                float *__restrict__ w_out, const uint16_t *x, int D,
+                                                                uint16_t *x16, int8_t *xsh, FusedDispatch dsp) {
+  __shared__ int32_t s_f[kTinyMaxN];
+  __shared__ int32_t s_cnt[kMaxExperts];
+  const int t = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+  if (t < T) select_token<MPL>(t, in, n_chunks, bias, T, E, K, renorm, idx_out, w_out, x, D, x16, xsh,
+                               dsp.order ? s_f : nullptr);
+  if (dsp.order) {
+    __syncthreads();
+    if (threadIdx.x < kWave)
+      tiny_dispatch(s_f, T * K, K, E, dsp.S, T, dsp.tile_rows, dsp.tr, dsp.order, dsp.inv_order, dsp.row_map,
+                    dsp.expert_off, dsp.tile_off, dsp.counters, dsp.act_items, dsp.tiles, s_cnt);
+  }
+}
+
 void launch_select(const float *in, int n_chunks, const float *bias, int T, int E, int K, int renorm,
-                   int32_t *idx, float *w, const void *x, int D, void *x16, int8_t *xsh, hipStream_t s) {
+                   int32_t *idx, float *w, const void *x, int D, void *x16, int8_t *xsh, const FusedDispatch &dsp,
+                   hipStream_t s) {
   const dim3 grid((T + kThreads / kWave - 1) / (kThreads / kWave)), block(kThreads);
   const uint16_t *xb = static_cast<const uint16_t *>(x);
   uint16_t *xo = static_cast<uint16_t *>(x16);
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, block, 0, s, in, n_chunks, bias, T, E, K, renorm, idx, w, xb, D, xo, xsh);
+    hipLaunchKernelGGL(kern, grid, block, 0, s, in, n_chunks, bias, T, E, K, renorm, idx, w, xb, D, xo, xsh, dsp);
   };
   if (E <= 64) go(route_select_kernel<1>);
   else if (E <= 128) go(route_select_kernel<2>);
@@ -339,10 +361,16 @@ bool route_writes_x16(const moe_layer_desc *d) {
   return d->w_format == MOE_WF_AFFINE_Q4 && d->d_model <= kRowF16MaxD;
 }
 
+bool route_fuses_dispatch(const moe_layer_desc *d, int32_t T) {
+  return T <= kThreads / kWave && int64_t(T) * d->top_k <= kTinyMaxN && !route_mfma_applies(d, T);
+}
+
 void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router,
                   const float *bias, int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh,
-                  void *stream, StageMarker *mk) {
+                  const FusedDispatch &dsp_in, void *stream, StageMarker *mk) {
   if (!route_writes_x16(d)) x16 = nullptr, xsh = nullptr;
+  FusedDispatch dsp = dsp_in;
+  if (!route_fuses_dispatch(d, T)) dsp.order = nullptr;
   if (route_mfma_applies(d, T)) {
     launch_route_mfma(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, stream, mk);
     return;
@@ -370,8 +398,8 @@ void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void 
     n_chunks = full ? 0 : C;
   }
   if (mk) mk->mark("route_logits");
-  launch_select(scratch, n_chunks, bias, T, E, d->top_k, d->renormalize, idx, w, x, D, x16, xsh, s);
-  if (mk) mk->mark("route_select");
+  launch_select(scratch, n_chunks, bias, T, E, d->top_k, d->renormalize, idx, w, x, D, x16, xsh, dsp, s);
+  if (mk) mk->mark(dsp.order ? "route_select_dispatch" : "route_select");
 }
 
 }  // namespace moe

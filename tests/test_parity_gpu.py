@@ -97,7 +97,11 @@ def test_dispatch_edge_cases():
     cases = [np.zeros((50, 8), np.int32) + 5,                             # one expert gets every row
              np.full((1, 8), E - 1, np.int32),
              rng.integers(0, E, (1000, 8), dtype=np.int32),               # duplicates within a token
-             np.arange(8, dtype=np.int32).reshape(1, 8)]
+             np.arange(8, dtype=np.int32).reshape(1, 8),
+             rng.integers(0, E, (16, 8), dtype=np.int32),                 # 128 slots: the one-wave dispatch
+             rng.integers(0, 3, (16, 8), dtype=np.int32),                 # ... with heavy repeats
+             rng.integers(0, E, (17, 8), dtype=np.int32),                 # 136 slots: one workgroup
+             rng.integers(0, E, (3, 8), dtype=np.int32)]
     for idx in cases:
         for tr in (1, 64, 1000):
             got = g.dispatch(idx, tr)
