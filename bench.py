@@ -64,9 +64,10 @@ class Hip:
 
 
 def workload_name(spec) -> str:
-    w = "affine 4-bit g64" if spec.wfmt == "q4" else f"dense {spec.act}"
+    w = f"affine {spec.bits}-bit g{spec.group_size}" if spec.quantized else f"dense {spec.act}"
     extra = (", fused gate|up" if spec.gate_up_fused else "") + (
-        ", per-op bf16 SwiGLU" if spec.swiglu_round_bf16 else "") + (
+        ", GeGLU (tanh-GELU gate)" if spec.activation == "geglu" else "") + (
+        ", per-op bf16 GLU rounding" if spec.swiglu_round_bf16 else "") + (
         f", {spec.n_shared} shared experts" if spec.n_shared else "") + (
         ", Zipf-skewed router bias" if spec.router_bias == "zipf" else "")
     return (f"{spec.name}: MoE layer forward T={spec.T} d_model={spec.d_model} d_ff={spec.d_ff} "
@@ -76,8 +77,8 @@ def workload_name(spec) -> str:
 def expert_bytes(spec) -> int:
     """Stored bytes of one expert's gate, up and down weights."""
     n = 3 * spec.d_model * spec.d_ff
-    if spec.wfmt == "q4":
-        return n // 2 + (n // spec.group_size) * 4
+    if spec.quantized:
+        return n * spec.bits // 8 + (n // spec.group_size) * 4
     return n * (2 if spec.act == "bf16" else 4)
 
 
@@ -98,7 +99,7 @@ def accounting(spec, touched: int):
     # expert outputs: bf16 where the matrix-core kernels write them, else fp32
     ysz = 2 if spec.act == "bf16" and D % 64 == 0 and F % 64 == 0 else 4
     # the router's per-token kernel writes the fp16 staging copy of x (and reads x) for 4-bit layers
-    x16_bytes = (T * D * 2 + T) if spec.wfmt == "q4" and D <= 4096 else 0
+    x16_bytes = (T * D * 2 + T) if spec.quantized and D <= 4096 else 0
     gateup = {"bound": "hbm", "bytes": int(w_touched * gu_frac) + T * D * esz + R * F * esz,
               "flops": 2 * R * 2 * D * F}
     down = {"bound": "hbm", "bytes": int(w_touched * down_frac) + R * F * esz + R * D * ysz, "flops": 2 * R * D * F}
@@ -238,7 +239,7 @@ def path_dtype(spec) -> str:
     """
     if spec.act != "bf16":
         return "f32"
-    return "fp16" if spec.wfmt == "q4" else "bf16"
+    return "fp16" if spec.quantized else "bf16"
 
 
 STAGE_SOURCES = {
@@ -323,8 +324,8 @@ def cpu_baseline(name, n_tokens):
     spec = inputs.CONFIGS[name]
     host = inputs.gen_layer(spec)
     d = oracle.Desc(spec.d_model, spec.d_ff, spec.n_experts, spec.top_k, spec.n_shared, spec.act == "bf16",
-                    spec.wfmt == "q4", spec.group_size, spec.gate_up_fused, spec.swiglu_round_bf16,
-                    spec.renormalize)
+                    spec.quantized, spec.group_size, spec.gate_up_fused, spec.swiglu_round_bf16,
+                    spec.renormalize, spec.bits, int(spec.activation == "geglu"))
     n = min(n_tokens, spec.T)
     toks = np.linspace(0, spec.T - 1, n).astype(np.int32)
     threads = len(os.sched_getaffinity(0))

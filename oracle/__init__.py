@@ -38,7 +38,7 @@ def build() -> str:
 class _Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d_model", "d_ff", "n_experts", "top_k", "n_shared", "act_bf16", "w_q4",
-        "group_size", "gate_up_fused", "swiglu_round_bf16", "renormalize")]
+        "group_size", "gate_up_fused", "swiglu_round_bf16", "renormalize", "w_bits", "activation")]
 
 
 class _Proj(ctypes.Structure):
@@ -105,11 +105,14 @@ class Desc:
     gate_up_fused: bool = False
     swiglu_round_bf16: bool = False
     renormalize: bool = True
+    w_bits: int = 4           # affine code width (4 or 8) when w_q4
+    activation: int = 0       # 0: SwiGLU, 1: GeGLU (tanh-GELU)
 
     def _c(self) -> _Desc:
         return _Desc(self.d_model, self.d_ff, self.n_experts, self.top_k, self.n_shared,
                      int(self.act_bf16), int(self.w_q4), self.group_size,
-                     int(self.gate_up_fused), int(self.swiglu_round_bf16), int(self.renormalize))
+                     int(self.gate_up_fused), int(self.swiglu_round_bf16), int(self.renormalize),
+                     int(self.w_bits), int(self.activation))
 
 
 def _ptr(a):

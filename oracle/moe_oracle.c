@@ -186,12 +186,13 @@ void oracle_dispatch(int32_t T, int32_t top_k, int32_t n_experts,
 }
 
 /*
- * Explicit dequantisation of one weight row.  Affine 4-bit ("perf(moe):
+ * Explicit dequantisation of one weight row.  Affine 4- or 8-bit ("perf(moe):
  * fused MoE expert decode kernel", section "Multi-bit handling": affine,
- * power-of-two bits, shift-unpack; DS4Server #112 "Kernel contract": biases
- * present, group 64): w = scale * q + bias, q the unsigned code of the
- * column, scale/bias the bf16 pair of the column's group.  The product of a
- * bf16 scale and a 4-bit code is exact in fp32, so only the addition rounds.
+ * power-of-two bits 4/8, shift-unpack; DS4Server #112, "Native implementation
+ * scope": biases present, 4 or 8 bits, group 32/64/128): w = scale * q + bias,
+ * q the unsigned code of the column, scale/bias the bf16 pair of the column's
+ * group.  The product of a bf16 scale and a code of at most 8 bits is exact in
+ * fp32, so only the addition rounds.
  */
 void oracle_dequant_row(const oracle_desc *d, const oracle_proj *p, int32_t e,
                         int32_t n, int32_t N, int32_t K, float *out) {
@@ -201,12 +202,15 @@ void oracle_dequant_row(const oracle_desc *d, const oracle_proj *p, int32_t e,
     return;
   }
   const int32_t G = d->group_size;
-  const uint32_t *wq = (const uint32_t *)p->w + ((int64_t)e * N + n) * (K / 8);
+  const int32_t bits = d->w_bits ? d->w_bits : 4;
+  const int32_t per = 32 / bits;              /* codes per word */
+  const uint32_t mask = (1u << bits) - 1u;
+  const uint32_t *wq = (const uint32_t *)p->w + ((int64_t)e * N + n) * (K / per);
   /* scales/biases are group-major: [expert][group][row] */
   const uint16_t *sc = p->scales + (int64_t)e * (K / G) * N + n;
   const uint16_t *bi = p->biases + (int64_t)e * (K / G) * N + n;
   for (int32_t k = 0; k < K; ++k) {
-    uint32_t q = (wq[k / 8] >> (4 * (k % 8))) & 0xfu;
+    uint32_t q = (wq[k / per] >> (bits * (k % per))) & mask;
     float s = oracle_bf16_to_f32(sc[(int64_t)(k / G) * N]);
     float b = oracle_bf16_to_f32(bi[(int64_t)(k / G) * N]);
     out[k] = s * (float)q + b;
@@ -215,6 +219,11 @@ void oracle_dequant_row(const oracle_desc *d, const oracle_proj *p, int32_t e,
 
 static float silu(float g) { return g / (1.0f + expf(-g)); }
 static float sigmoid(float g) { return 1.0f / (1.0f + expf(-g)); }
+/* tanh approximation of GELU: 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))) */
+static float gelu_tanh(float g) {
+  const float c = 0.7978845608028654f;
+  return 0.5f * g * (1.0f + tanhf(c * (g + 0.044715f * g * g * g)));
+}
 
 /*
  * One expert on one token (e may name a shared expert: e >= E).
@@ -223,6 +232,9 @@ static float sigmoid(float g) { return 1.0f / (1.0f + expf(-g)); }
  * "Kernel contract", SwiGLU epilogue: accumulators rounded to the activation
  * dtype, then sigmoid and each multiply rounded as separate ops):
  *   g, u <- bf16(g), bf16(u); s = bf16(sigmoid(g)); a = bf16(g*s); h = bf16(a*u).
+ * GeGLU ("SwitchGLU: grouped-expert Metal kernels", "When it applies":
+ * SwiGLU or tanh-GELU GLU): h = gelu_tanh(g) * u; with per-op rounding
+ *   g, u <- bf16(g), bf16(u); a = bf16(gelu_tanh(g)); h = bf16(a*u).
  * down: out[m] = sum_n h[n] * Wd[m][n], fp32, n ascending.
  * The fused [gate | up] matrix holds gate in rows 0..d_ff-1 and up in rows
  * d_ff..2*d_ff-1.
@@ -248,7 +260,15 @@ void oracle_expert_apply(const oracle_desc *d, const oracle_experts *w,
     else
       oracle_dequant_row(d, &w->up, e, n, F, D, row);
     for (int32_t k = 0; k < D; ++k) u = u + xr[k] * row[k];
-    if (d->swiglu_round_bf16) {
+    if (d->activation == 1) {
+      if (d->swiglu_round_bf16) {
+        g = round_bf16(g);
+        u = round_bf16(u);
+        h[n] = round_bf16(round_bf16(gelu_tanh(g)) * u);
+      } else {
+        h[n] = gelu_tanh(g) * u;
+      }
+    } else if (d->swiglu_round_bf16) {
       g = round_bf16(g);
       u = round_bf16(u);
       float s = round_bf16(sigmoid(g));

@@ -40,17 +40,20 @@ typedef struct {
   int32_t top_k;             /* experts selected per token */
   int32_t n_shared;          /* always-on shared experts, weight 1.0 */
   int32_t act_bf16;          /* 0: x, W_router, dense weights are fp32; 1: bf16 */
-  int32_t w_q4;              /* 0: dense weights in the activation dtype; 1: affine 4-bit */
-  int32_t group_size;        /* q4 group length along the reduction dim (64) */
+  int32_t w_q4;              /* 0: dense weights in the activation dtype; 1: affine quantised */
+  int32_t group_size;        /* quantisation group length along the reduction dim (32, 64, 128) */
   int32_t gate_up_fused;     /* 1: one [2*d_ff][d] matrix per expert, rows = [gate | up] */
-  int32_t swiglu_round_bf16; /* 1: per-op bf16 rounding in the SwiGLU epilogue */
+  int32_t swiglu_round_bf16; /* 1: per-op bf16 rounding in the gated epilogue */
   int32_t renormalize;       /* 1: selected weights renormalised to sum to one */
+  int32_t w_bits;            /* affine code width: 4 or 8 */
+  int32_t activation;        /* 0: SwiGLU (silu(g) * u); 1: GeGLU with tanh-GELU (gelu(g) * u) */
 } oracle_desc;
 
 /* One projection for all experts (routed first, then shared).  Dense:
- * w = [n_all][N][K] in the activation dtype.  q4: w = uint32 [n_all][N][K/8]
- * (eight 4-bit codes per word, code m at bits [4m, 4m+4) holds column
- * 8*word+m), scales/biases = bf16 bits [n_all][K/group][N] (group-major). */
+ * w = [n_all][N][K] in the activation dtype.  Affine b-bit (b = 4 or 8):
+ * w = uint32 [n_all][N][K*b/32] (32/b codes per word, code m at bits
+ * [b*m, b*m+b) holds column (32/b)*word+m), scales/biases = bf16 bits
+ * [n_all][K/group][N] (group-major). */
 typedef struct {
   const void *w;
   const uint16_t *scales;

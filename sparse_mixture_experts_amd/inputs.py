@@ -15,13 +15,14 @@ Recipe (the pages fix the shapes, not the draws):
     gate [d_ff][d_model], up [d_ff][d_model], down [d_model][d_ff].
   * x ~ N(0, 1) except for the tiny fp32 layer, where x ~ N(0, 1/d_model).
   * bf16 storage rounds the fp32 draw to nearest-even (torch's cast).
-  * 4-bit storage, per group of 64 consecutive reduction columns of one row:
-    lo = min, hi = max, scale = bf16((hi - lo) / 15), bias = bf16(lo),
-    q = clamp(rint((w - bias) / scale), 0, 15) (ties to even), q = 0 where
-    scale == 0.  Eight codes per uint32, code m of a word at bits [4m, 4m+4)
-    holding column 8*word + m.  Codes are stored row-major [N][K/8]; scales
-    and biases group-major [K/64][N] (the scales of one group for
-    consecutive rows are contiguous).
+  * b-bit affine storage (b = 4 or 8), per group of g (32, 64 or 128)
+    consecutive reduction columns of one row: lo = min, hi = max,
+    scale = bf16((hi - lo) / (2^b - 1)), bias = bf16(lo),
+    q = clamp(rint((w - bias) / scale), 0, 2^b - 1) (ties to even), q = 0
+    where scale == 0.  32/b codes per uint32, code m of a word at bits
+    [b*m, b*m + b) holding column (32/b)*word + m.  Codes are stored
+    row-major [N][K*b/32]; scales and biases group-major [K/g][N] (the
+    scales of one group for consecutive rows are contiguous).
   * Skewed routing: an additive router bias of -2.2 * ln(e + 1) on expert e,
     i.e. twice the log of a Zipf(s = 1.1) weight of rank e + 1 (the Zipf
     normaliser cancels in the softmax).
@@ -47,7 +48,7 @@ class LayerSpec:
     top_k: int
     n_shared: int = 0
     act: str = "bf16"            # "f32" | "bf16"
-    wfmt: str = "dense"          # "dense" | "q4"
+    wfmt: str = "dense"          # "dense" | "q4" | "q8" (affine 4- or 8-bit codes)
     group_size: int = 64
     gate_up_fused: bool = False
     swiglu_round_bf16: bool = False
@@ -55,6 +56,15 @@ class LayerSpec:
     router_bias: str = "none"    # "none" | "zipf"
     x_scale: str = "unit"        # "unit" | "fan_in"
     seed: int = 0
+    activation: str = "swiglu"   # "swiglu" | "geglu" (tanh-GELU gate)
+
+    @property
+    def quantized(self) -> bool:
+        return self.wfmt in ("q4", "q8")
+
+    @property
+    def bits(self) -> int:
+        return 8 if self.wfmt == "q8" else 4
 
     @property
     def n_routed_rows(self) -> int:
@@ -96,24 +106,31 @@ def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
     return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def quantize_q4(w: np.ndarray, group: int = 64):
-    """Encode fp32 rows [N][K] as (uint32 [N][K/8], scales bf16 [N][K/g], biases bf16 [N][K/g])."""
+def quantize_affine(w: np.ndarray, group: int = 64, bits: int = 4):
+    """Encode fp32 rows [N][K] as (uint32 [N][K*bits/32], scales bf16 [N][K/g], biases bf16 [N][K/g])."""
     N, K = w.shape
-    assert K % group == 0 and group % 8 == 0
+    per = 32 // bits
+    top = float((1 << bits) - 1)
+    assert K % group == 0 and group % per == 0
     wg = w.reshape(N, K // group, group).astype(np.float32)
     lo = wg.min(axis=-1)
     hi = wg.max(axis=-1)
-    s_bits = to_bf16_bits((hi - lo) / np.float32(15.0))
+    s_bits = to_bf16_bits((hi - lo) / np.float32(top))
     b_bits = to_bf16_bits(lo)
     s = bf16_bits_to_f32(s_bits)[..., None]
     b = bf16_bits_to_f32(b_bits)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
         q = np.rint((wg - b) / s)
-    q = np.where(s == 0, 0.0, np.clip(q, 0, 15)).astype(np.uint32).reshape(N, K // 8, 8)
+    q = np.where(s == 0, 0.0, np.clip(q, 0, top)).astype(np.uint32).reshape(N, K // per, per)
     words = q[..., 0].copy()
-    for m in range(1, 8):
-        words |= q[..., m] << np.uint32(4 * m)
+    for m in range(1, per):
+        words |= q[..., m] << np.uint32(bits * m)
     return words, s_bits, b_bits
+
+
+def quantize_q4(w: np.ndarray, group: int = 64):
+    """Affine 4-bit encoding of fp32 rows [N][K] (see quantize_affine)."""
+    return quantize_affine(w, group, 4)
 
 
 def gen_x(spec: LayerSpec, x_index: int = 0, T: int | None = None) -> np.ndarray:
@@ -134,8 +151,8 @@ def gen_router(spec: LayerSpec):
 
 
 def _store(spec: LayerSpec, w: np.ndarray):
-    if spec.wfmt == "q4":
-        q, s, b = quantize_q4(w, spec.group_size)
+    if spec.quantized:
+        q, s, b = quantize_affine(w, spec.group_size, spec.bits)
         return {"w": q, "scales": np.ascontiguousarray(s.T), "biases": np.ascontiguousarray(b.T)}
     return {"w": w if spec.act == "f32" else to_bf16_bits(w)}
 

@@ -19,17 +19,18 @@ def widen(spec: LayerSpec, a: np.ndarray) -> np.ndarray:
     return bits_to_f64(a) if spec.act == "bf16" else np.asarray(a, np.float32).astype(np.float64)
 
 
-def unpack_codes(words: np.ndarray) -> np.ndarray:
-    """uint32 [..., K/8] -> codes [..., K] (column 8*w + m is bits [4m, 4m+4) of word w)."""
-    sh = (np.arange(8, dtype=np.uint32) * 4)
-    codes = (words[..., None] >> sh) & np.uint32(0xF)
-    return codes.reshape(*words.shape[:-1], words.shape[-1] * 8)
+def unpack_codes(words: np.ndarray, bits: int = 4) -> np.ndarray:
+    """uint32 [..., K*b/32] -> codes [..., K] (column (32/b)*w + m is bits [b*m, b*m + b) of word w)."""
+    per = 32 // bits
+    sh = (np.arange(per, dtype=np.uint32) * bits)
+    codes = (words[..., None] >> sh) & np.uint32((1 << bits) - 1)
+    return codes.reshape(*words.shape[:-1], words.shape[-1] * per)
 
 
 def dequant64(spec: LayerSpec, proj: dict) -> np.ndarray:
-    if spec.wfmt != "q4":
+    if not spec.quantized:
         return widen(spec, proj["w"])
-    q = unpack_codes(proj["w"]).astype(np.float64)
+    q = unpack_codes(proj["w"], spec.bits).astype(np.float64)
     g = spec.group_size
     # scales/biases are stored group-major [..., K/g, N]
     s = np.repeat(np.swapaxes(bits_to_f64(proj["scales"]), -1, -2), g, axis=-1)
@@ -55,12 +56,24 @@ def bf16_round64(v: np.ndarray) -> np.ndarray:
         torch.float64).numpy()
 
 
+def gelu_tanh64(g: np.ndarray) -> np.ndarray:
+    """torch's tanh-approximate GELU in float64 (a library routine, not the oracle's formula)."""
+    import torch
+    return torch.nn.functional.gelu(torch.from_numpy(np.asarray(g, np.float64)), approximate="tanh").numpy()
+
+
 def expert_outputs64(spec: LayerSpec, x64: np.ndarray, W) -> np.ndarray:
     """Every expert applied to every token: [T][n_all][D] float64."""
     gate, up, down = W
     g = np.einsum("td,efd->tef", x64, gate)
     u = np.einsum("td,efd->tef", x64, up)
-    if spec.swiglu_round_bf16:
+    if spec.activation == "geglu":
+        if spec.swiglu_round_bf16:
+            g, u = bf16_round64(g), bf16_round64(u)
+            h = bf16_round64(bf16_round64(gelu_tanh64(g)) * u)
+        else:
+            h = gelu_tanh64(g) * u
+    elif spec.swiglu_round_bf16:
         g, u = bf16_round64(g), bf16_round64(u)
         s = bf16_round64(1.0 / (1.0 + np.exp(-g)))
         a = bf16_round64(g * s)

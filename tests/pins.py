@@ -14,7 +14,9 @@ tests swap for builds with planted mistakes.  What pins what:
                           the selected logits; k = 1 gives exactly 1.0.
 * dispatch             -- NumPy stable argsort and the permutation identities.
 * dequantisation       -- bit-exact fp32(s*q + b) from fp64; codes round-trip; the
-                          quantisation error bound against the original draw.
+                          quantisation error bound against the original draw; for
+                          4- and 8-bit codes and groups of 32, 64 and 128.
+* GeGLU                -- torch's tanh-approximate GELU (a library routine) in fp64.
 * expert FFN, layer    -- NumPy fp64 dense brute force; sparse == dense all-experts
                           output masked to the top-k and weighted; k = E equals soft
                           routing; E = k = 1 equals a plain SwiGLU MLP; x = 0 gives
@@ -37,8 +39,8 @@ U = 2.0 ** -24  # unit roundoff of fp32
 
 def desc_of(spec: LayerSpec) -> oracle.Desc:
     return oracle.Desc(spec.d_model, spec.d_ff, spec.n_experts, spec.top_k, spec.n_shared,
-                       spec.act == "bf16", spec.wfmt == "q4", spec.group_size, spec.gate_up_fused,
-                       spec.swiglu_round_bf16, spec.renormalize)
+                       spec.act == "bf16", spec.quantized, spec.group_size, spec.gate_up_fused,
+                       spec.swiglu_round_bf16, spec.renormalize, spec.bits, int(spec.activation == "geglu"))
 
 
 # Small layers spanning every format and flag; d_model 192 and 100 exercise
@@ -55,6 +57,15 @@ SMALL = {
                                 n_shared=2, wfmt="q4", router_bias="zipf", seed=16),
     "bf16-norenorm": LayerSpec("bf16-norenorm", T=6, d_model=64, d_ff=64, n_experts=7, top_k=3,
                                renormalize=False, seed=17),
+    "q8": LayerSpec("q8", T=7, d_model=128, d_ff=128, n_experts=6, top_k=2, wfmt="q8", seed=18),
+    "q4-g32-geglu": LayerSpec("q4-g32-geglu", T=6, d_model=128, d_ff=96, n_experts=5, top_k=2, wfmt="q4",
+                              group_size=32, activation="geglu", seed=19),
+    "q8-g128-fused-round-geglu": LayerSpec("q8-g128-fused-round-geglu", T=6, d_model=256, d_ff=128,
+                                           n_experts=6, top_k=3, wfmt="q8", group_size=128,
+                                           gate_up_fused=True, swiglu_round_bf16=True, activation="geglu",
+                                           seed=20),
+    "bf16-geglu": LayerSpec("bf16-geglu", T=7, d_model=128, d_ff=64, n_experts=5, top_k=2,
+                            activation="geglu", seed=21),
 }
 
 _cache: dict = {}
@@ -204,25 +215,29 @@ def pin_dispatch():
         assert np.all(np.diff(flat[out["order"]]) >= 0)
 
 
-def pin_dequant():
-    spec = SMALL["q4"]
-    L = layer("q4")
+def pin_dequant(name: str = "q4"):
+    spec = SMALL[name]
+    L = layer(name)
     d = desc_of(spec)
-    proj = L["experts"]["gate"]
-    N, K = spec.d_ff, spec.d_model
+    # the gate rows: the first d_ff rows of the fused [gate | up] matrix when fused
+    proj = L["experts"]["gate_up" if spec.gate_up_fused else "gate"]
+    N, K, g, top = spec.d_ff, spec.d_model, spec.group_size, (1 << spec.bits) - 1
+    NS = 2 * N if spec.gate_up_fused else N
+    assert proj["w"].shape[-1] * 32 // spec.bits == K
     raw = inputs._rng(spec.seed, 2, 3).standard_normal((N, K), dtype=np.float32) / np.float32(math.sqrt(K))
-    codes = brute.unpack_codes(proj["w"][3])
-    s = brute.bits_to_f64(proj["scales"][3]).T  # stored [K/64][N]
+    codes = brute.unpack_codes(proj["w"][3], spec.bits)
+    assert codes.max() == top and codes.min() == 0
+    s = brute.bits_to_f64(proj["scales"][3]).T  # stored [K/g][N]
     b = brute.bits_to_f64(proj["biases"][3]).T
     for n in (0, 1, N // 2, N - 1):
-        row = oracle.dequant_row(d, proj, 3, n, N, K)
-        sg, bg = np.repeat(s[n], 64), np.repeat(b[n], 64)
+        row = oracle.dequant_row(d, proj, 3, n, NS, K)
+        sg, bg = np.repeat(s[n], g), np.repeat(b[n], g)
         exact = (sg * codes[n] + bg).astype(np.float32)
         assert np.array_equal(row.view(np.uint32), exact.view(np.uint32)), "dequant is not fp32(s*q+b)"
-        back = np.clip(np.rint((row.astype(np.float64) - bg) / sg), 0, 15)
+        back = np.clip(np.rint((row.astype(np.float64) - bg) / sg), 0, top)
         assert np.array_equal(back, codes[n]), "codes do not round-trip"
         ulp_b = np.abs(bg) * 2.0 ** -8
-        err_bound = sg / 2 + ulp_b + 15 * sg * 2.0 ** -8 + 1e-12
+        err_bound = sg / 2 + ulp_b + top * sg * 2.0 ** -8 + 1e-12
         assert np.all(np.abs(row - raw[n]) <= err_bound), "quantisation error above bound"
 
 
@@ -251,11 +266,44 @@ def pin_expert(name: str):
                 h, _ = oracle.expert_apply(d, L["experts"], e, L["x"][t])
                 g = brute.bf16_round64(gate[e] @ x64[t])
                 u = brute.bf16_round64(up[e] @ x64[t])
-                s = brute.bf16_round64(1.0 / (1.0 + np.exp(-g)))
-                href = brute.bf16_round64(brute.bf16_round64(g * s) * u)
+                href = (_geglu_per_op if spec.activation == "geglu" else _swiglu_per_op)(g, u)
                 hits += int(np.sum(href == h))
                 total += h.size
         assert hits >= 0.97 * total, f"per-op bf16 SwiGLU matches only {hits}/{total}"
+
+
+def _swiglu_per_op(g, u):
+    s = brute.bf16_round64(1.0 / (1.0 + np.exp(-g)))
+    return brute.bf16_round64(brute.bf16_round64(g * s) * u)
+
+
+def _geglu_per_op(g, u):
+    return brute.bf16_round64(brute.bf16_round64(brute.gelu_tanh64(g)) * u)
+
+
+def pin_gelu_special_values():
+    """E = k = 1 GeGLU layer with fp32 weights: x = 0 gives 0; the GLU of a
+    large positive gate is the identity on g*u and of a large negative gate is
+    0 (the tanh form's limits), checked through h on hand-set rows."""
+    spec = LayerSpec("gelu-sv", T=1, d_model=64, d_ff=64, n_experts=1, top_k=1, act="f32",
+                     activation="geglu", seed=22)
+    L = inputs.gen_layer(spec)
+    d = desc_of(spec)
+    D, F = spec.d_model, spec.d_ff
+    gate = np.zeros((1, F, D), np.float32)
+    up = np.zeros((1, F, D), np.float32)
+    gate[0, :, 0] = np.linspace(-12.0, 12.0, F, dtype=np.float32)
+    up[0, :, 0] = 1.0
+    w = {"gate": {"w": gate}, "up": {"w": up}, "down": {"w": L["experts"]["down"]["w"]}}
+    x = np.zeros((D,), np.float32)
+    x[0] = 1.0
+    h, _ = oracle.expert_apply(d, w, 0, x)
+    g = gate[0, :, 0].astype(np.float64)
+    big = np.abs(g) >= 6
+    assert np.allclose(h[big], np.where(g[big] > 0, g[big], 0.0), atol=1e-6)
+    assert np.allclose(h, brute.gelu_tanh64(g), rtol=2e-6, atol=1e-7)
+    h0, _ = oracle.expert_apply(d, w, 0, np.zeros_like(x))
+    assert np.all(h0 == 0.0)
 
 
 def pin_layer(name: str):
@@ -319,7 +367,8 @@ ALL_PINS = [
     ("ties", pin_ties, ()),
     *[(f"weights[{n}]", pin_weights, (n,)) for n in SMALL],
     ("dispatch", pin_dispatch, ()),
-    ("dequant", pin_dequant, ()),
+    *[(f"dequant[{n}]", pin_dequant, (n,)) for n in ("q4", "q8", "q4-g32-geglu", "q8-g128-fused-round-geglu")],
+    ("gelu_special_values", pin_gelu_special_values, ()),
     *[(f"expert[{n}]", pin_expert, (n,)) for n in SMALL],
     *[(f"layer[{n}]", pin_layer, (n,)) for n in SMALL],
     ("soft_routing", pin_soft_routing, ()),

@@ -28,10 +28,10 @@ def test_formats_and_shapes():
         assert L["x"].dtype == (np.float32 if spec.act == "f32" else np.uint16)
         assert L["w_router"].shape == (spec.d_model, spec.n_experts)
         ex = L["experts"]
-        if spec.wfmt == "q4":
-            assert ex["down"]["w"].shape == (n_all, spec.d_model, spec.d_ff // 8)
+        if spec.quantized:
+            assert ex["down"]["w"].shape == (n_all, spec.d_model, spec.d_ff * spec.bits // 32)
             assert ex["down"]["w"].dtype == np.uint32
-            assert ex["down"]["scales"].shape == (n_all, spec.d_ff // 64, spec.d_model)
+            assert ex["down"]["scales"].shape == (n_all, spec.d_ff // spec.group_size, spec.d_model)
         if spec.gate_up_fused:
             assert ex["gate_up"]["w"].shape[1] == 2 * spec.d_ff and "gate" not in ex
 

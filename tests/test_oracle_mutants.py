@@ -21,7 +21,12 @@ MUTANTS = {
     "router_chunk_dropped": ("        acc = acc + p;", "        acc = p;"),
     "renormalise_skipped": ("if (d->renormalize)\n", "if (0)\n"),
     "softmax_wrong_index": ("w[j] = expf(l[idx[j]] - m) / z;", "w[j] = expf(l[j] - m) / z;"),
-    "nibble_order_reversed": ("(4 * (k % 8))", "(4 * (7 - k % 8))"),
+    "nibble_order_reversed": ("(bits * (k % per))", "(bits * (per - 1 - k % per))"),
+    "code_width_fixed_4": ("const int32_t per = 32 / bits;", "const int32_t per = 8;"),
+    "group_size_fixed_64": ("const int32_t G = d->group_size;", "const int32_t G = 64;"),
+    "gelu_cubic_dropped": ("(g + 0.044715f * g * g * g)", "(g)"),
+    "geglu_runs_silu": ("if (d->activation == 1) {", "if (0) {"),
+    "geglu_rounding_skipped": ("h[n] = round_bf16(round_bf16(gelu_tanh(g)) * u);", "h[n] = gelu_tanh(g) * u;"),
     "scale_bias_swapped": ("out[k] = s * (float)q + b;", "out[k] = b * (float)q + s;"),
     "group_index_wrong": ("float s = oracle_bf16_to_f32(sc[(int64_t)(k / G) * N]);", "float s = oracle_bf16_to_f32(sc[0]);"),
     "fused_up_reads_gate": ("oracle_dequant_row(d, &w->gate_up, e, F + n, 2 * F, D, row);",
