@@ -55,44 +55,57 @@ typedef enum {
 } moe_status;
 
 typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
-typedef enum { MOE_WF_DENSE = 0, MOE_WF_AFFINE_Q4 = 1 } moe_wformat;
+typedef enum { MOE_WF_DENSE = 0, MOE_WF_AFFINE_Q4 = 1, MOE_WF_AFFINE_Q8 = 2 } moe_wformat;
+typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GEGLU = 1 } moe_activation;
 
 /*
  * Layer shape and format.
- *  d_model, d_ff  > 0; multiples of 64 when w_format is MOE_WF_AFFINE_Q4
- *                 (the q4 group runs along both reduction dims), multiples of
- *                 8 otherwise.
+ *  d_model, d_ff  > 0; for the affine formats multiples of 64 and of
+ *                 group_size (the groups run along both reduction dims);
+ *                 multiples of 8 otherwise.
  *  n_experts      routed experts E, 1..1024.
  *  top_k          1..min(32, n_experts).
  *  n_shared       always-on shared experts (weight 1.0, not renormalised), 0..8;
  *                 their weights follow the E routed experts in every projection.
  *  act_dtype      moe_dtype of x, W_router and dense expert weights.
- *  w_format       moe_wformat of the expert weights.  MOE_WF_AFFINE_Q4 needs
- *                 act_dtype == MOE_DT_BF16.
- *  group_size     q4 group length along the reduction dim; only 64.
+ *  w_format       moe_wformat of the expert weights.  The affine formats
+ *                 (4- or 8-bit codes: "perf(moe): fused MoE expert decode
+ *                 kernel", "Multi-bit handling"; DS4Server #112, "Native
+ *                 implementation scope") need act_dtype == MOE_DT_BF16.
+ *  group_size     affine group length along the reduction dim: 32, 64 or 128.
  *  gate_up_fused  1: one [2*d_ff][d_model] matrix per expert whose rows are
  *                 [gate | up]; 0: separate gate and up matrices.
  *  swiglu_round_bf16  1: round gate and up to bf16, then sigmoid, g*s and
  *                 (g*s)*u each rounded to bf16 (DS4Server #112, "Kernel
- *                 contract", SwiGLU epilogue); needs act_dtype == BF16.
+ *                 contract", SwiGLU epilogue); for GeGLU gate and up, then
+ *                 gelu(g) and gelu(g)*u, each rounded to bf16.  Needs
+ *                 act_dtype == BF16.
  *  renormalize    1: the k selected weights are divided by their sum.
+ *  activation     moe_activation of the expert GLU: SwiGLU, h = silu(g)*u,
+ *                 or GeGLU with the tanh form of GELU,
+ *                 h = 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))) * u
+ *                 ("SwitchGLU: grouped-expert Metal kernels", "When it
+ *                 applies").
  */
 typedef struct {
   int32_t d_model, d_ff, n_experts, top_k, n_shared;
   int32_t act_dtype, w_format, group_size;
   int32_t gate_up_fused, swiglu_round_bf16, renormalize;
+  int32_t activation;
 } moe_layer_desc;
 
 /*
  * One projection for all experts (routed 0..E-1, then shared E..E+S-1), out-
  * major (the reduction dim contiguous):
  *  dense: w = act_dtype [E+S][N][K]; scales = biases = NULL.
- *  q4:    w = uint32 [E+S][N][K/8], column k of row n is bits [4*(k%8), +4)
- *         of word k/8 (an unsigned code q in 0..15); scales, biases = bf16
- *         [E+S][K/64][N] (group-major: one group's values for consecutive
- *         rows are contiguous); the weight is scale*q + bias of its group ("affine"
- *         4-bit, group 64, with bf16 scales and biases: "SwitchGLU: grouped-
- *         expert Metal kernels" (ml-explore/mlx-lm #2044), "When it applies").
+ *  affine b-bit (b = 4 for Q4, 8 for Q8), group g:
+ *         w = uint32 [E+S][N][K*b/32], column k of row n is bits
+ *         [b*(k%(32/b)), +b) of word k/(32/b) (an unsigned code q in
+ *         0..2^b-1); scales, biases = bf16 [E+S][K/g][N] (group-major: one
+ *         group's values for consecutive rows are contiguous); the weight is
+ *         scale*q + bias of its group ("affine" quantisation with bf16 scales
+ *         and biases: "SwitchGLU: grouped-expert Metal kernels"
+ *         (ml-explore/mlx-lm #2044), "When it applies").
  * gate, up: N = d_ff, K = d_model; gate_up: N = 2*d_ff, K = d_model;
  * down: N = d_model, K = d_ff.
  */

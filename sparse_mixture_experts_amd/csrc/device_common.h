@@ -45,12 +45,22 @@ __device__ __forceinline__ float sigmoid_f32(float g) {
 }
 __device__ __forceinline__ float silu_f32(float g) { return g * sigmoid_f32(g); }
 
-// SwiGLU of one (gate, up) pair.  With per-op rounding: gate and up rounded to
-// bf16, then sigmoid, g*s and (g*s)*u each rounded to bf16.
-__device__ __forceinline__ float swiglu(float g, float u, bool round_ops) {
-  if (!round_ops) return silu_f32(g) * u;
+// tanh-form GELU, 0.5 g (1 + tanh(z)) with z = sqrt(2/pi) (g + 0.044715 g^3),
+// written as g * sigmoid(2z) (the identity 0.5 (1 + tanh z) = 1 / (1 + e^-2z)).
+__device__ __forceinline__ float gelu_tanh_f32(float g) {
+  const float z2 = 1.5957691216057308f * __builtin_fmaf(0.044715f * g, g * g, g);
+  return g * sigmoid_f32(z2);
+}
+
+// The gated unit of one (gate, up) pair: SwiGLU, silu(g) * u, or GeGLU,
+// gelu_tanh(g) * u.  With per-op rounding: gate and up rounded to bf16, then
+// for SwiGLU sigmoid, g*s and (g*s)*u each rounded to bf16; for GeGLU
+// gelu(g) and gelu(g)*u each rounded to bf16.
+__device__ __forceinline__ float glu(float g, float u, bool round_ops, bool geglu) {
+  if (!round_ops) return (geglu ? gelu_tanh_f32(g) : silu_f32(g)) * u;
   g = round_bf16(g);
   u = round_bf16(u);
+  if (geglu) return round_bf16(round_bf16(gelu_tanh_f32(g)) * u);
   float s = round_bf16(sigmoid_f32(g));
   float a = round_bf16(g * s);
   return round_bf16(a * u);

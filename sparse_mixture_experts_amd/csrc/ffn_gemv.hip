@@ -79,7 +79,7 @@ __device__ __forceinline__ void stage_rows(void *xs, const void *__restrict__ sr
 struct GateUpArgs {
   const void *x;
   const int32_t *row_map;
-  int T, N, D, F, E, fused, round_ops, MR;
+  int T, N, D, F, E, fused, round_ops, geglu, MR;
   const void *wg;
   const uint16_t *sg, *bg;
   const void *wu;
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void gateup_gemv_kernel(GateUpArgs a) {
         if (m < mr) {
           const float g = wave_sum(ag[m]), u = wave_sum(au[m]);
           if (lane == 0) {
-            const float hv = swiglu(g, u, a.round_ops);
+            const float hv = glu(g, u, a.round_ops, a.geglu);
             const int64_t o = int64_t(it.row0 + r0 + m) * F + n;
             if constexpr (BF16) static_cast<uint16_t *>(a.h)[o] = uint16_t(f32_to_bf16_bits(hv));
             else static_cast<float *>(a.h)[o] = hv;
@@ -215,7 +215,7 @@ void launch_gemv(const moe_layer_desc *d, int32_t T, const void *x, const int32_
   const int max_items = min(E, N) + S;
   const moe_proj &pg = d->gate_up_fused ? w->gate_up : w->gate;
   GateUpArgs ga{x, row_map, T, N, D, F, E, d->gate_up_fused, d->swiglu_round_bf16,
-                rows_per_pass(D, esz), pg.w, static_cast<const uint16_t *>(pg.scales),
+                d->activation == MOE_ACT_GEGLU, rows_per_pass(D, esz), pg.w, static_cast<const uint16_t *>(pg.scales),
                 static_cast<const uint16_t *>(pg.biases), w->up.w,
                 static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases),
                 counters, items, h};

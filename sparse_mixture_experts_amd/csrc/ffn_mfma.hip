@@ -17,21 +17,22 @@
 //
 // Weight operands come straight from global memory into registers (every
 // weight element is used by exactly one lane), a group ahead of their use.
-// Affine 4-bit weights are dequantised in registers to fp16 with packed
-// math: for each pair of codes the word is shifted and masked into two fp16
-// values 1024+q (exponent 2^10, the code in the low mantissa bits), 1024 is
-// subtracted exactly, and one v_pk_fma_f16 gives s*q + b for both.  The pairs
-// come out as (q_j, q_{j+4}) of a word, so the activations are stored with
-// the same order inside every 8-element block.
+// Affine 4- and 8-bit weights are dequantised in registers to fp16 with
+// packed math: each pair of codes is moved into two fp16 values 1024+q
+// (exponent 2^10, the code in the low mantissa bits; 4-bit codes by shift and
+// mask, 8-bit codes by byte permutes), 1024 is subtracted exactly, and one
+// v_pk_fma_f16 gives s*q + b for both.  The pairs come out as (q_j, q_{j+4})
+// of each 8-code block, so the activations are stored with the same order
+// inside every 8-element block.
 //
-// 4-bit layers keep their activations in fp16 end to end: a small kernel
+// Affine layers keep their activations in fp16 end to end: a small kernel
 // converts x once per token (not once per expert tile) and the gate/up
 // epilogue writes h as fp16, both already in that permuted order, so the
 // GEMMs' LDS staging is a plain copy.  fp16 has the range of neither bf16
 // nor the scales, so values carry power-of-two exponents, used only where
 // needed: one per token row of x (undone in the gate/up epilogue), one per
 // (row, 128-column block) of h, and one per (weight row, slab) for scales
-// whose |s|*15 + |b| is at least 2^15 or below 2^-10.  The main loop runs
+// whose |s|*qmax + |b| (qmax = 15 or 255) is at least 2^15 or below 2^-10.  The main loop runs
 // without any rescaling; if a slab of the tile carries an h or weight
 // exponent, the tile starts over in a loop that brings the accumulators to
 // each such slab's scale and back (exact power-of-two multiplies).  Dense
@@ -60,7 +61,6 @@ constexpr int kNW = kThreads / kWave;
 constexpr int kNT = 4;                     // 16-row weight tiles per wave
 constexpr int kNRows = kNW * kNT * 16;     // weight rows per block (256)
 constexpr int kKS = 128;                   // reduction elements per slab
-constexpr int kGPS = kKS / kGroup;         // groups per slab (2)
 constexpr int kSteps = kKS / 32;           // MFMA reduction steps per slab (4)
 constexpr int kPieces = kKS / 8;           // 16-byte activation pieces per row and slab (16)
 constexpr int kLdsRow = kKS + 8;           // padded LDS row (16-bit elements): spreads rows over banks
@@ -93,6 +93,25 @@ __device__ __forceinline__ f16x8 q4_word_to_f16(uint32_t w, h2 s2, h2 s2_16, h2 
   return __builtin_bit_cast(f16x8, r);
 }
 
+// 8 codes of two words (columns 0-3 in w0, 4-7 in w1) -> 8 fp16 weights s*q + b
+// in the same order q0,q4,q1,q5,q2,q6,q3,q7 as q4_word_to_f16.  One byte
+// permute interleaves the two words' low (high) halves, and one more per pair
+// places two codes under the fp16 exponent bytes of 1024 (held in `mg` as
+// 0x64646464): 1024 + q exactly, for q <= 255.
+__device__ __forceinline__ f16x8 q8_words_to_f16(uint32_t w0, uint32_t w1, h2 s2, h2 b2, uint32_t mg) {
+  const h2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  // __builtin_amdgcn_perm(hi, lo, sel): selector byte i picks byte sel_i of
+  // the 8-byte value hi:lo (0-3 from lo, 4-7 from hi) for result byte i.
+  const uint32_t t0 = __builtin_amdgcn_perm(w1, w0, 0x05010400u);  // q0, q4, q1, q5
+  const uint32_t t1 = __builtin_amdgcn_perm(w1, w0, 0x07030602u);  // q2, q6, q3, q7
+  const uint32_t c[4] = {__builtin_amdgcn_perm(mg, t0, 0x04010400u), __builtin_amdgcn_perm(mg, t0, 0x04030402u),
+                         __builtin_amdgcn_perm(mg, t1, 0x04010400u), __builtin_amdgcn_perm(mg, t1, 0x04030402u)};
+  h2 r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = __builtin_elementwise_fma(__builtin_bit_cast(h2, c[j]) - k1024, s2, b2);
+  return __builtin_bit_cast(f16x8, r);
+}
+
 // x [T][D] bf16 -> fp16 staging copy (row_to_f16), one wave per token.
 __global__ __launch_bounds__(256) void act_f16_kernel(const uint16_t *x, int T, int D, uint16_t *x16,
                                                       int8_t *xsh) {
@@ -102,66 +121,68 @@ __global__ __launch_bounds__(256) void act_f16_kernel(const uint16_t *x, int T, 
 }
 
 struct GemmArgs {
-  const void *act;          // gate/up: x [T][K] (bf16; fp16 copy for 4-bit); down: h [rows][K]
-  const int8_t *act_sh;     // 4-bit: gate/up token exponents [T]; down h exponents [rows][nblk]
-  int8_t *out_sh;           // 4-bit gate/up: h exponents [rows][nblk]
+  const void *act;          // gate/up: x [T][K] (bf16; fp16 copy for affine); down: h [rows][K]
+  const int8_t *act_sh;     // affine: gate/up token exponents [T]; down h exponents [rows][nblk]
+  int8_t *out_sh;           // affine gate/up: h exponents [rows][nblk]
   int nblk;                 // h exponent blocks per row
   const int32_t *row_map;   // gate/up only
   int T, N, K;              // token count, routed rows, reduction length
   int n_out;                // output columns of the projection (F for gate/up, D for down)
   int fused;                // gate/up: [gate | up] in one matrix
-  int round_ops;            // per-op bf16 SwiGLU
+  int round_ops;            // per-op bf16 GLU
+  int geglu;                // gate/up: tanh-GELU gate (else SiLU)
   const void *w0;           // gate (or gate_up) / down weights
   const uint16_t *s0, *b0;
   const void *w1;           // up weights (separate layout)
   const uint16_t *s1, *b1;
   const int32_t *counters;  // [1] = number of tiles
   const PlanItem *tiles;
-  void *out;                // gate/up: h [rows][F] (bf16, or fp16 for 4-bit); down: y [rows][D]
+  void *out;                // gate/up: h [rows][F] (bf16, or fp16 for affine); down: y [rows][D]
   int out_bf16;             // down: y rows as bf16 (else fp32)
 };
 
-template <int RB>
+// GPS: groups per slab (128 / group size; 1 for dense weights).
+template <int RB, int GPS>
 struct Slab {
-  uint16_t a[RB * 16][kLdsRow];   // activations: bf16 (dense) or fp16 in q4 order (q4)
-  uint2 sb[kGPS][kNRows];         // q4: (s,s) and (b,b) as packed fp16, per weight row and group
-  int8_t ash[RB * 16];            // q4 down: h exponents of the slab's rows
-  int8_t wsh[kNRows];             // q4: weight row exponents
+  uint16_t a[RB * 16][kLdsRow];   // activations: bf16 (dense) or fp16 in permuted order (affine)
+  uint2 sb[GPS][kNRows];          // affine: (s,s) and (b,b) as packed fp16, per weight row and group
+  int8_t ash[RB * 16];            // affine down: h exponents of the slab's rows
+  int8_t wsh[kNRows];             // affine: weight row exponents
 };
 
-// Per-lane weight data of one slab: 4-bit -> one uint4 (4 words, 32 codes)
-// per tile; dense -> four uint4 (32 bf16) per tile.
-template <bool Q4>
-struct WSlab;
-template <>
-struct WSlab<true> { uint4 w[kNT]; };
-template <>
-struct WSlab<false> { uint4 w[kNT][kSteps]; };
+// Per-lane weight data of one slab (32 reduction elements per tile): 4-bit
+// -> one uint4 (4 words) per tile; 8-bit -> two; dense bf16 -> four.
+template <int QB>
+struct WSlab { uint4 w[kNT][QB == 0 ? kSteps : QB / 4]; };
 
-// GATEUP: gate/up projection with SwiGLU epilogue writing h, else down
-// projection writing fp32 y rows.  Q4: affine 4-bit weights (fp16 MFMA),
-// else dense bf16 (bf16 MFMA).  RB: 16-row blocks per tile.  Each wave owns
+// GATEUP: gate/up projection with the GLU epilogue writing h, else down
+// projection writing y rows.  QB: affine code width 4 or 8 (fp16 MFMA), or 0
+// for dense bf16 weights (bf16 MFMA).  RB: 16-row blocks per tile.  GPS:
+// affine groups per 128-element slab (4, 2, 1 for groups of 32, 64, 128).  Each wave owns
 // kNT weight tiles of 16 rows; for gate/up the first kNT/2 are gate rows and
 // the last kNT/2 the up rows of the same output columns.
 //
 // Reduction order inside a slab of 128: lane (lr, lg) of an operand holds
 // the 32 slab elements 32*lg .. 32*lg+31 (4-bit: words 4*lg .. 4*lg+3 of the
-// row's slab, one contiguous 16-byte load), and MFMA step j multiplies the 8
-// elements 32*lg + 8*j .. +7 of both operands.  Both operands use the same
-// order, so every step sums over a fixed quarter of the slab and the four
-// steps cover it.  Lanes lg = 0, 1 hold the slab's first group, lg = 2, 3 its
-// second.
-template <bool GATEUP, bool Q4, int RB>
+// row's slab, one contiguous 16-byte load; 8-bit: words 8*lg .. 8*lg+7), and
+// MFMA step j multiplies the 8 elements 32*lg + 8*j .. +7 of both operands.
+// Both operands use the same order, so every step sums over a fixed quarter
+// of the slab and the four steps cover it.  A lane's 32 elements lie in one
+// group: group 32*lg / (128 / GPS) of the slab.
+template <bool GATEUP, int QB, int RB, int GPS>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
+  constexpr bool AFF = QB != 0;                    // affine codes (fp16 path)
+  constexpr int kLPG = 4 / GPS;                   // lanes lg per group
+  constexpr float kQMax = QB == 8 ? 255.0f : 15.0f;
   constexpr int NTH = GATEUP ? kNT / 2 : kNT;   // output-column tiles per wave
   constexpr int kRowsPerPass = kThreads / kPieces;  // activation rows staged per pass (16)
   constexpr int PPT = RB * 16 / kRowsPerPass;     // staging passes (pieces per thread)
   static_assert(PPT * kRowsPerPass == RB * 16, "staging covers the slab");
   static_assert(!GATEUP || kNW * NTH * 16 == kHBlock, "a gate/up block writes one h exponent block");
   static_assert(kKS == kHBlock, "a down slab reads one h exponent block");
-  __shared__ Slab<RB> sm[2];
-  __shared__ float rmax[GATEUP && Q4 ? kNW : 1][RB * 16];  // gate/up 4-bit epilogue: row maxima per wave
-  __shared__ int8_t rsh[RB * 16];                         // gate/up 4-bit: token exponents of the rows
+  __shared__ Slab<RB, GPS> sm[2];
+  __shared__ float rmax[GATEUP && AFF ? kNW : 1][RB * 16];  // gate/up affine epilogue: row maxima per wave
+  __shared__ int8_t rsh[RB * 16];                         // gate/up affine: token exponents of the rows
 
   // XCD-aware order.  Workgroups go to the 8 XCDs round-robin by linear id;
   // the W = tiles * column-blocks work items of this call are cut into 8
@@ -185,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
   const int lr = lane & 15, lg = lane >> 4;  // operand row / reduction quarter of this lane
-  const int K = a.K, KW = K / 8, G = K / kGroup;
+  const int K = a.K, KW = QB == 0 ? 0 : K * QB / 32, G = K / (kKS / GPS);
   const int nslab = (K + kKS - 1) / kKS;
   const int col0 = (bx * kNW + wave) * NTH * 16;  // first output column of this wave
   const bool col_ok = col0 < a.n_out;              // whole wave in or out (n_out % 64 == 0)
@@ -211,19 +232,22 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   for (int nt = 0; nt < kNT; ++nt) {
     const bool up = GATEUP && nt >= NTH;
     const int64_t wr = wrow_of(col_c + (nt % NTH) * 16 + lr, up);
-    wp[nt] = Q4 ? static_cast<const void *>(static_cast<const uint32_t *>(wsrc(up)) + wr * KW)
+    wp[nt] = AFF ? static_cast<const void *>(static_cast<const uint32_t *>(wsrc(up)) + wr * KW)
                 : static_cast<const void *>(static_cast<const uint16_t *>(wsrc(up)) + wr * K);
   }
-  // Slab s of this lane's rows.  The last slab may hold a single group
+  // Slab s of this lane's rows.  The last slab may hold only 64 elements
   // (K = 64 mod 128): its second half is read from a clamped address and
-  // multiplied by zero scales (4-bit) or zeroed activations (dense).
-  auto load_slab = [&](int s, WSlab<Q4> &dst) {
+  // multiplied by zero scales (affine) or zeroed activations (dense).
+  auto load_slab = [&](int s, WSlab<QB> &dst) {
     s = min(s, nslab - 1);
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
-      if constexpr (Q4) {
-        const int w = min(s * (kKS / 8) + lg * 4, KW - 4);
-        dst.w[nt] = *reinterpret_cast<const uint4 *>(static_cast<const uint32_t *>(wp[nt]) + w);
+      if constexpr (AFF) {
+        constexpr int WPL = QB;  // words per lane and slab (32 elements)
+        const int w = min(s * (kKS * QB / 32) + lg * WPL, KW - WPL);
+#pragma unroll
+        for (int v = 0; v < QB / 4; ++v)
+          dst.w[nt][v] = *reinterpret_cast<const uint4 *>(static_cast<const uint32_t *>(wp[nt]) + w + 4 * v);
       } else {
 #pragma unroll
         for (int j = 0; j < kSteps; ++j) {
@@ -256,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     // Rows past the tile (and invalid tokens) read a valid row; their results
     // are never stored.
     src_off[p] = int64_t(r >= 0 ? r : (GATEUP ? 0 : tile.row0)) * K;
-    if constexpr (GATEUP && Q4) {
+    if constexpr (GATEUP && AFF) {
       if (piece == 0) rsh[m] = a.act_sh[src_off[p] / K];  // visible after the first barrier
     }
   }
@@ -272,8 +296,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   const int64_t s_base = int64_t(tile.expert) * G * s_nre + s_rin;
 
   uint4 stg[PPT];
-  uint16_t sraw[kGPS][2];
-  int stg_sh[PPT];  // q4 down: h exponents of the staged rows' slab
+  uint16_t sraw[GPS][2];
+  int stg_sh[PPT];  // affine down: h exponents of the staged rows' slab
   auto stage_load = [&](int s) {
     s = min(s, nslab - 1);
     const int k = s * kKS + piece * 8;
@@ -281,18 +305,18 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     for (int p = 0; p < PPT; ++p) {
       const uint4 v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.act) + src_off[p] +
                                                        min(k, K - 8));
-      if constexpr (Q4) {
+      if constexpr (AFF) {
         stg[p] = v;  // pieces past K meet zero scales
       } else {
         const bool ok = src_row[p] >= 0 && k < K;
         stg[p] = make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
       }
-      if constexpr (Q4 && !GATEUP) stg_sh[p] = a.act_sh[(src_off[p] / K) * a.nblk + s];
+      if constexpr (AFF && !GATEUP) stg_sh[p] = a.act_sh[(src_off[p] / K) * a.nblk + s];
     }
-    if constexpr (Q4) {
+    if constexpr (AFF) {
 #pragma unroll
-      for (int g = 0; g < kGPS; ++g) {
-        const int gg = s * kGPS + g;
+      for (int g = 0; g < GPS; ++g) {
+        const int gg = s * GPS + g;
         const bool ok = s_ok && gg < G;
         const int64_t at = s_base + int64_t(min(gg, G - 1)) * s_nre;
         const uint16_t sv = ssrc(s_up)[at], bv = bsrc(s_up)[at];
@@ -304,30 +328,30 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   // Writes the staged slab to LDS buffer `buf`; returns nonzero when the slab
   // carries an exponent (h rows of the down projection, or weight rows).
   auto stage_write = [&](int buf) -> int {
-    Slab<RB> &S = sm[buf];
+    Slab<RB, GPS> &S = sm[buf];
     int flag = 0;
 #pragma unroll
     for (int p = 0; p < PPT; ++p) {
       const int m = p * kRowsPerPass + tid / kPieces;
       *reinterpret_cast<uint4 *>(&S.a[m][piece * 8]) = stg[p];
-      if constexpr (Q4 && !GATEUP) {
+      if constexpr (AFF && !GATEUP) {
         const int sh = src_row[p] >= 0 ? stg_sh[p] : 0;
         if (piece == 0) S.ash[m] = int8_t(sh);
         flag |= sh;
       }
     }
-    if constexpr (Q4) {
-      float sv[kGPS], bv[kGPS], wm = 0.f;
+    if constexpr (AFF) {
+      float sv[GPS], bv[GPS], wm = 0.f;
 #pragma unroll
-      for (int g = 0; g < kGPS; ++g) {
+      for (int g = 0; g < GPS; ++g) {
         sv[g] = bf16_bits_to_f32(sraw[g][0]);
         bv[g] = bf16_bits_to_f32(sraw[g][1]);
-        wm = fmaxf(wm, __builtin_fmaf(15.0f, fabsf(sv[g]), fabsf(bv[g])));
+        wm = fmaxf(wm, __builtin_fmaf(kQMax, fabsf(sv[g]), fabsf(bv[g])));
       }
       const int wsh = f16_shift(wm);
       const float m = pow2(-wsh);
 #pragma unroll
-      for (int g = 0; g < kGPS; ++g) {
+      for (int g = 0; g < GPS; ++g) {
         const _Float16 sh16 = (_Float16)(sv[g] * m), bh16 = (_Float16)(bv[g] * m);
         const h2 s2 = {sh16, sh16}, b2 = {bh16, bh16};
         S.sb[g][tid] = make_uint2(__builtin_bit_cast(uint32_t, s2), __builtin_bit_cast(uint32_t, b2));
@@ -338,8 +362,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     return flag;
   };
 
-  uint32_t magic = 0x64006400u;  // fp16 exponent of 1024 in both halves
-  asm volatile("" : "+v"(magic));  // kept in a register (see q4_word_to_f16)
+  // fp16 exponent of 1024 in both halves (4-bit), or in every byte (8-bit),
+  // kept in a register (see q4_word_to_f16 and q8_words_to_f16)
+  uint32_t magic = QB == 8 ? 0x64646464u : 0x64006400u;
+  asm volatile("" : "+v"(magic));
   f32x4 acc[kNT][RB];
   auto zero_acc = [&]() {
 #pragma unroll
@@ -352,7 +378,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   // A slab that carries exponents: the accumulators are brought to the slab's
   // scale (times 2^-(h exponent + weight exponent) of each output) before its
   // steps accumulate, and back after, both exact.
-  auto rescale = [&](const Slab<RB> &S, int sign) {
+  auto rescale = [&](const Slab<RB, GPS> &S, int sign) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int ash = GATEUP ? 0 : int(S.ash[rb * 16 + lr]);
@@ -367,13 +393,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   // One slab of every tile of this wave, in kSteps MFMA steps.  Row blocks
   // past the tile's rows are multiplied too (their results are never
   // stored), which keeps the body free of branches.
-  auto compute_slab = [&](const Slab<RB> &S, const WSlab<Q4> &ws) {
-    if constexpr (Q4) {
+  auto compute_slab = [&](const Slab<RB, GPS> &S, const WSlab<QB> &ws) {
+    if constexpr (AFF) {
       const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
       h2 s2[kNT], s2_16[kNT], b2[kNT];
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
-        const uint2 v = S.sb[lg >> 1][(wave * kNT + nt) * 16 + lr];
+        const uint2 v = S.sb[lg / kLPG][(wave * kNT + nt) * 16 + lr];
         s2[nt] = __builtin_bit_cast(h2, v.x);
         s2_16[nt] = s2[nt] * sixteenth;
         b2[nt] = __builtin_bit_cast(h2, v.y);
@@ -386,8 +412,16 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
           bx[rb] = *reinterpret_cast<const f16x8 *>(&S.a[rb * 16 + lr][lg * 32 + j * 8]);
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
-          const uint32_t wd = j == 0 ? ws.w[nt].x : j == 1 ? ws.w[nt].y : j == 2 ? ws.w[nt].z : ws.w[nt].w;
-          const f16x8 aw = q4_word_to_f16(wd, s2[nt], s2_16[nt], b2[nt], magic);
+          f16x8 aw;
+          if constexpr (QB == 4) {
+            const uint4 &q = ws.w[nt][0];
+            const uint32_t wd = j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
+            aw = q4_word_to_f16(wd, s2[nt], s2_16[nt], b2[nt], magic);
+          } else {
+            const uint4 &q = ws.w[nt][j >> 1];  // step j: words 2j, 2j+1 of the lane's 8
+            aw = (j & 1) ? q8_words_to_f16(q.z, q.w, s2[nt], b2[nt], magic)
+                         : q8_words_to_f16(q.x, q.y, s2[nt], b2[nt], magic);
+          }
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) acc[nt][rb] = mfma_f16(aw, bx[rb], acc[nt][rb]);
         }
@@ -411,17 +445,17 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
 
   // ---- pipelined main loop ----
   // Weights run PDS slabs ahead in a ring of register buffers (two slabs for
-  // 4-bit weights; dense slabs are four times larger, so one); the
+  // affine weights; dense slabs are four times the 4-bit size, so one); the
   // activation slab s+1 is loaded before slab s is multiplied and written to
   // the other LDS buffer after it, and the barrier there also reports
   // whether slab s+1 carries exponents.  Steps past the last slab only keep
   // the barrier pattern; their loads are clamped repeats.  SLOW = false: no
   // rescaling, and the loop gives up (returns true) before the first slab
   // with exponents; SLOW = true: rescales around every such slab.
-  constexpr int PDS = Q4 ? 2 : 1;
+  constexpr int PDS = AFF ? 2 : 1;
   auto run = [&](auto slow_tag) __attribute__((always_inline)) -> bool {
     constexpr bool SLOW = decltype(slow_tag)::value;
-    WSlab<Q4> wb[PDS];
+    WSlab<QB> wb[PDS];
     stage_load(0);
     const int f0 = stage_write(0);
 #pragma unroll
@@ -444,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     return false;
   };
   if (run(std::false_type{})) {
-    if constexpr (Q4) {
+    if constexpr (AFF) {
       // Every wave left the fast loop at the same barrier, after its last
       // read of the slab buffers.
       zero_acc();
@@ -452,8 +486,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
     }
   }
 
-  if constexpr (GATEUP && Q4) {
-    // SwiGLU on the true gate/up values (the token exponent undone), then h as
+  if constexpr (GATEUP && AFF) {
+    // The GLU on the true gate/up values (the token exponent undone), then h as
     // fp16 with one exponent per (row, this block's 128 columns), in the
     // permuted staging order.  Lane (lr, lg) holds columns c..c+3,
     // c = col0 + nt*16 + 4*lg, of row m = rb*16 + lr: the lanes lg and lg^1
@@ -469,7 +503,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
       for (int nt = 0; nt < NTH; ++nt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float v = swiglu(acc[nt][rb][i] * xs, acc[nt + NTH][rb][i] * xs, a.round_ops);
+          const float v = glu(acc[nt][rb][i] * xs, acc[nt + NTH][rb][i] * xs, a.round_ops, a.geglu);
           hv[rb][nt][i] = col_ok ? v : 0.f;
           mx = fmaxf(mx, fabsf(hv[rb][nt][i]));
         }
@@ -525,7 +559,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
       if constexpr (GATEUP) {
         uint32_t hb[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16_bits(swiglu(acc[nt][rb][i], acc[nt + NTH][rb][i], a.round_ops));
+        for (int i = 0; i < 4; ++i)
+          hb[i] = f32_to_bf16_bits(glu(acc[nt][rb][i], acc[nt + NTH][rb][i], a.round_ops, a.geglu));
         const uint2 o = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
         *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + row * a.n_out + c) = o;
       } else if (a.out_bf16) {
@@ -545,18 +580,21 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
 // once (one memory round trip), while the workgroup stages the tile's
 // activation rows in LDS once; then the wave runs its K/32 MFMA steps with
 // no further barrier.  Exponents are per row over the whole K (weights: the
-// row's largest 15|s| + |b|; activations: the token's x exponent, or the h
+// row's largest qmax|s| + |b|; activations: the token's x exponent, or the h
 // row's largest value), so they are undone once in the epilogue.
 // gate/up: a wave's rows are 8 gate rows and the 8 up rows of the same
-// columns (the SwiGLU pairs sit 32 lanes apart in the MFMA result), h is
+// columns (the GLU pairs sit 32 lanes apart in the MFMA result), h is
 // written as bf16.  down: 16 output columns, h read as bf16.
 constexpr int kDecMaxK = 2048;
+// Longest reduction held in registers: 16 slabs of 4-bit codes or 8 of
+// 8-bit codes (64 registers of codes per lane either way).
+constexpr int dec_max_k(int qb) { return qb == 8 ? 1024 : kDecMaxK; }
 
 struct DecArgs {
   const void *act;          // gate/up: fp16 staging copy of x [T][K]; down: h bf16 [rows][K]
   const int8_t *act_sh;     // gate/up: token exponents [T]
   const int32_t *row_map;   // gate/up only
-  int T, N, K, n_out, fused, round_ops;
+  int T, N, K, n_out, fused, round_ops, geglu, gsize;
   const uint32_t *w0;       // gate (or gate_up) / down codes
   const uint16_t *s0, *b0;
   const uint32_t *w1;       // up codes (separate layout)
@@ -567,8 +605,10 @@ struct DecArgs {
   int out_bf16;
 };
 
-template <bool GATEUP, int kMaxSlabs>
+template <bool GATEUP, int QB, int kMaxSlabs>
 __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecArgs a) {
+  constexpr float kQMax = QB == 8 ? 255.0f : 15.0f;
+  constexpr int WPL = QB;  // code words per lane and slab
   constexpr int CPW = GATEUP ? 8 : 16;           // output columns per wave
   extern __shared__ uint16_t xs[];               // [16][K + 8] activation rows, fp16 staging order
   __shared__ uint32_t rmax_bits[16];             // down: row maxima of |h| (as float bits)
@@ -590,7 +630,7 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecArgs a) {
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
   const int lr = lane & 15, lg = lane >> 4;
-  const int K = a.K, KW = K / 8, G = K / kGroup, nslab = (K + kKS - 1) / kKS;
+  const int K = a.K, KW = K * QB / 32, G = K / a.gsize, nslab = (K + kKS - 1) / kKS;
   // LDS rows hold whole slabs (K rounded up to 128, the tail zeroed) plus a
   // pad that spreads the 16 rows over banks.
   const int KR = nslab * kKS, XR = KR + 8;
@@ -607,14 +647,18 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecArgs a) {
   const uint32_t *wrow = (second ? a.w1 : a.w0) + (int64_t(tile.expert) * nre + rin) * KW;
   const uint16_t *sp = (second ? a.s1 : a.s0) + int64_t(tile.expert) * G * nre + rin;
   const uint16_t *bp = (second ? a.b1 : a.b0) + int64_t(tile.expert) * G * nre + rin;
-  uint4 wq[kMaxSlabs];
+  uint4 wq[kMaxSlabs][QB / 4];
   uint16_t sr[kMaxSlabs], br[kMaxSlabs];
 #pragma unroll
   for (int s = 0; s < kMaxSlabs; ++s) {
     const int sc = min(s, nslab - 1);
-    wq[s] = *reinterpret_cast<const uint4 *>(wrow + min(sc * (kKS / 8) + lg * 4, KW - 4));
-    const int g = min(2 * sc + (lg >> 1), G - 1);
-    const bool ok = s < nslab && 2 * sc + (lg >> 1) < G;
+    const int w = min(sc * (kKS * QB / 32) + lg * WPL, KW - WPL);
+#pragma unroll
+    for (int v = 0; v < QB / 4; ++v) wq[s][v] = *reinterpret_cast<const uint4 *>(wrow + w + 4 * v);
+    // this lane's 32 elements of the slab lie in one group
+    const int gl = (sc * kKS + lg * 32) / a.gsize;
+    const int g = min(gl, G - 1);
+    const bool ok = s < nslab && gl < G;
     const uint16_t sv = sp[int64_t(g) * nre], bv = bp[int64_t(g) * nre];
     sr[s] = ok ? sv : uint16_t(0);
     br[s] = ok ? bv : uint16_t(0);
@@ -672,14 +716,14 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecArgs a) {
   float wm = 0.f;
 #pragma unroll
   for (int s = 0; s < kMaxSlabs; ++s)
-    wm = fmaxf(wm, __builtin_fmaf(15.0f, fabsf(bf16_bits_to_f32(sr[s])), fabsf(bf16_bits_to_f32(br[s]))));
+    wm = fmaxf(wm, __builtin_fmaf(kQMax, fabsf(bf16_bits_to_f32(sr[s])), fabsf(bf16_bits_to_f32(br[s]))));
   wm = fmaxf(wm, __shfl_xor(wm, 16, kWave));
   wm = fmaxf(wm, __shfl_xor(wm, 32, kWave));
   const int wsh = f16_shift(wm);  // exponent of weight row lr
   const float wmul = pow2(-wsh);
   __syncthreads();  // activation rows staged
 
-  uint32_t magic = 0x64006400u;
+  uint32_t magic = QB == 8 ? 0x64646464u : 0x64006400u;
   asm volatile("" : "+v"(magic));
   const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -689,11 +733,18 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecArgs a) {
       const _Float16 s16 = (_Float16)(bf16_bits_to_f32(sr[s]) * wmul), b16 = (_Float16)(bf16_bits_to_f32(br[s]) * wmul);
       const h2 s2 = {s16, s16}, b2 = {b16, b16};
       const h2 s2_16 = s2 * sixteenth;
-      const uint32_t wd[4] = {wq[s].x, wq[s].y, wq[s].z, wq[s].w};
 #pragma unroll
       for (int j = 0; j < kSteps; ++j) {
         const f16x8 bxv = *reinterpret_cast<const f16x8 *>(&xs[lr * XR + s * kKS + lg * 32 + j * 8]);
-        acc = mfma_f16(q4_word_to_f16(wd[j], s2, s2_16, b2, magic), bxv, acc);
+        f16x8 aw;
+        if constexpr (QB == 4) {
+          const uint4 &q = wq[s][0];
+          aw = q4_word_to_f16(j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w, s2, s2_16, b2, magic);
+        } else {
+          const uint4 &q = wq[s][j >> 1];
+          aw = (j & 1) ? q8_words_to_f16(q.z, q.w, s2, b2, magic) : q8_words_to_f16(q.x, q.y, s2, b2, magic);
+        }
+        acc = mfma_f16(aw, bxv, acc);
       }
     }
   }
@@ -723,7 +774,7 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecArgs a) {
     if (col_ok && lg < 2 && m < tile.rows) {
       uint32_t hb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16_bits(swiglu(v[i], u[i], a.round_ops));
+      for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16_bits(glu(v[i], u[i], a.round_ops, a.geglu));
       *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + row * a.n_out + col0 + 4 * lg) =
           make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
     }
@@ -739,15 +790,28 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecArgs a) {
   }
 }
 
-template <bool GATEUP, bool Q4, int RB>
+template <bool GATEUP, int QB, int RB, int GPS>
 void launch_one(const GemmArgs &ga, int64_t max_tiles, hipStream_t s) {
   constexpr int NTH = GATEUP ? kNT / 2 : kNT;
   const int cols_per_block = kNW * NTH * 16;
   const dim3 grid((ga.n_out + cols_per_block - 1) / cols_per_block, unsigned(max_tiles));
-  hipLaunchKernelGGL((grouped_gemm_kernel<GATEUP, Q4, RB>), grid, dim3(kThreads), 0, s, ga);
+  hipLaunchKernelGGL((grouped_gemm_kernel<GATEUP, QB, RB, GPS>), grid, dim3(kThreads), 0, s, ga);
+}
+// Code width (0: dense bf16) and groups per slab picked at run time.
+template <bool GATEUP, int RB, int QB>
+void launch_groups(const GemmArgs &ga, int gsize, int64_t max_tiles, hipStream_t s) {
+  if (gsize == 32) launch_one<GATEUP, QB, RB, 4>(ga, max_tiles, s);
+  else if (gsize == 128) launch_one<GATEUP, QB, RB, 1>(ga, max_tiles, s);
+  else launch_one<GATEUP, QB, RB, 2>(ga, max_tiles, s);
+}
+template <bool GATEUP, int RB>
+void launch_gemm(const GemmArgs &ga, int qb, int gsize, int64_t max_tiles, hipStream_t s) {
+  if (qb == 4) launch_groups<GATEUP, RB, 4>(ga, gsize, max_tiles, s);
+  else if (qb == 8) launch_groups<GATEUP, RB, 8>(ga, gsize, max_tiles, s);
+  else launch_one<GATEUP, 0, RB, 1>(ga, max_tiles, s);
 }
 
-template <bool GATEUP, int MS>
+template <bool GATEUP, int QB, int MS>
 void launch_decode_ms(const DecArgs &da, int64_t max_tiles, hipStream_t s) {
   constexpr int CPW = GATEUP ? 8 : 16;
   const int cols_per_block = kNW * CPW;
@@ -755,20 +819,21 @@ void launch_decode_ms(const DecArgs &da, int64_t max_tiles, hipStream_t s) {
   if (lds > 64 * 1024) {
     // above the default dynamic-LDS limit (gfx950 has 160 KB per CU): raise it once
     static const bool raised = [] {
-      return hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_gemm_kernel<GATEUP, MS>),
+      return hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_gemm_kernel<GATEUP, QB, MS>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize,
                                  int(16 * (MS * kKS + 8) * sizeof(uint16_t))) == hipSuccess;
     }();
     (void)raised;
   }
   const dim3 grid((da.n_out + cols_per_block - 1) / cols_per_block, unsigned(max_tiles));
-  hipLaunchKernelGGL((decode_gemm_kernel<GATEUP, MS>), grid, dim3(kThreads), lds, s, da);
+  hipLaunchKernelGGL((decode_gemm_kernel<GATEUP, QB, MS>), grid, dim3(kThreads), lds, s, da);
 }
-// K <= 1024: 8 slabs of registers; K <= 2048: 16.
+// K <= 1024: 8 slabs of registers; K <= 2048 (4-bit codes only): 16.
 template <bool GATEUP>
-void launch_decode(const DecArgs &da, int64_t max_tiles, hipStream_t s) {
-  if (da.K <= 8 * kKS) launch_decode_ms<GATEUP, 8>(da, max_tiles, s);
-  else launch_decode_ms<GATEUP, 16>(da, max_tiles, s);
+void launch_decode(const DecArgs &da, int qb, int64_t max_tiles, hipStream_t s) {
+  if (qb == 8) launch_decode_ms<GATEUP, 8, 8>(da, max_tiles, s);
+  else if (da.K <= 8 * kKS) launch_decode_ms<GATEUP, 4, 8>(da, max_tiles, s);
+  else launch_decode_ms<GATEUP, 4, 16>(da, max_tiles, s);
 }
 
 }  // namespace
@@ -791,52 +856,52 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
                             int64_t max_tiles, const FfnScratch &sc, void *y_sorted, bool ys_bf16, void *stream,
                             StageMarker *mk) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool q4 = d->w_format == MOE_WF_AFFINE_Q4;
+  const bool aff = affine(d);
+  const int qb = d->w_format == MOE_WF_AFFINE_Q8 ? 8 : aff ? 4 : 0;
+  const int gs = d->group_size;
+  const int geglu = d->activation == MOE_ACT_GEGLU;
   const int tr = plan_tile_rows(d, T);
   const int nblk = (d->d_ff + kHBlock - 1) / kHBlock;
-  if (q4 && !sc.x16_ready) {
+  if (aff && !sc.x16_ready) {
     hipLaunchKernelGGL(act_f16_kernel, dim3((T + 3) / 4), dim3(256), 0, s, static_cast<const uint16_t *>(x), T,
                        d->d_model, static_cast<uint16_t *>(sc.x16), sc.xsh);
     if (mk) mk->mark("x_f16");
   }
   const moe_proj &pg = d->gate_up_fused ? w->gate_up : w->gate;
-  GemmArgs gu{q4 ? sc.x16 : x, sc.xsh, sc.hsh, nblk, row_map, T, T * d->top_k, d->d_model, d->d_ff,
-              d->gate_up_fused, d->swiglu_round_bf16,
+  GemmArgs gu{aff ? sc.x16 : x, sc.xsh, sc.hsh, nblk, row_map, T, T * d->top_k, d->d_model, d->d_ff,
+              d->gate_up_fused, d->swiglu_round_bf16, geglu,
               pg.w, static_cast<const uint16_t *>(pg.scales), static_cast<const uint16_t *>(pg.biases),
               w->up.w, static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases),
               counters, tiles, sc.h, 0};
-  GemmArgs dn{sc.h, sc.hsh, nullptr, nblk, nullptr, T, T * d->top_k, d->d_ff, d->d_model, 0, 0,
+  GemmArgs dn{sc.h, sc.hsh, nullptr, nblk, nullptr, T, T * d->top_k, d->d_ff, d->d_model, 0, 0, 0,
               w->down.w, static_cast<const uint16_t *>(w->down.scales), static_cast<const uint16_t *>(w->down.biases),
               nullptr, nullptr, nullptr, counters, tiles, y_sorted, ys_bf16};
-  if (tr == 16 && q4 && int64_t(T) * d->top_k <= d->n_experts && d->d_model <= kDecMaxK && d->d_ff <= kDecMaxK) {
+  if (tr == 16 && aff && int64_t(T) * d->top_k <= d->n_experts && d->d_model <= dec_max_k(qb) &&
+      d->d_ff <= dec_max_k(qb)) {
     // at most one routed row per expert on average: whole-K loads per wave
     // (one memory round trip), h as bf16 between the two projections
-    DecArgs dg{q4 ? sc.x16 : x, sc.xsh, row_map, T, T * d->top_k, d->d_model, d->d_ff, d->gate_up_fused,
-               d->swiglu_round_bf16, static_cast<const uint32_t *>(pg.w), static_cast<const uint16_t *>(pg.scales),
-               static_cast<const uint16_t *>(pg.biases), static_cast<const uint32_t *>(w->up.w),
-               static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases), counters,
-               tiles, sc.h, 0};
-    DecArgs dd{sc.h, nullptr, nullptr, T, T * d->top_k, d->d_ff, d->d_model, 0, 0,
+    DecArgs dg{sc.x16, sc.xsh, row_map, T, T * d->top_k, d->d_model, d->d_ff, d->gate_up_fused,
+               d->swiglu_round_bf16, geglu, gs, static_cast<const uint32_t *>(pg.w),
+               static_cast<const uint16_t *>(pg.scales), static_cast<const uint16_t *>(pg.biases),
+               static_cast<const uint32_t *>(w->up.w), static_cast<const uint16_t *>(w->up.scales),
+               static_cast<const uint16_t *>(w->up.biases), counters, tiles, sc.h, 0};
+    DecArgs dd{sc.h, nullptr, nullptr, T, T * d->top_k, d->d_ff, d->d_model, 0, 0, 0, gs,
                static_cast<const uint32_t *>(w->down.w), static_cast<const uint16_t *>(w->down.scales),
                static_cast<const uint16_t *>(w->down.biases), nullptr, nullptr, nullptr, counters, tiles, y_sorted,
                ys_bf16};
-    launch_decode<true>(dg, max_tiles, s);
+    launch_decode<true>(dg, qb, max_tiles, s);
     if (mk) mk->mark("gateup_mfma");
-    launch_decode<false>(dd, max_tiles, s);
+    launch_decode<false>(dd, qb, max_tiles, s);
     if (mk) mk->mark("down_mfma");
   } else if (tr == 16) {
-    if (q4) launch_one<true, true, 1>(gu, max_tiles, s);
-    else launch_one<true, false, 1>(gu, max_tiles, s);
+    launch_gemm<true, 1>(gu, qb, gs, max_tiles, s);
     if (mk) mk->mark("gateup_mfma");
-    if (q4) launch_one<false, true, 1>(dn, max_tiles, s);
-    else launch_one<false, false, 1>(dn, max_tiles, s);
+    launch_gemm<false, 1>(dn, qb, gs, max_tiles, s);
     if (mk) mk->mark("down_mfma");
   } else {
-    if (q4) launch_one<true, true, 4>(gu, max_tiles, s);
-    else launch_one<true, false, 4>(gu, max_tiles, s);
+    launch_gemm<true, 4>(gu, qb, gs, max_tiles, s);
     if (mk) mk->mark("gateup_mfma");
-    if (q4) launch_one<false, true, 4>(dn, max_tiles, s);
-    else launch_one<false, false, 4>(dn, max_tiles, s);
+    launch_gemm<false, 4>(dn, qb, gs, max_tiles, s);
     if (mk) mk->mark("down_mfma");
   }
 }

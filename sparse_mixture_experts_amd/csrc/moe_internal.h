@@ -18,7 +18,6 @@ struct PlanItem {
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxShared = 8;
-constexpr int kGroup = 64;     // q4 group length
 constexpr int kMinTileRows = 16;  // smallest row tile of the grouped MFMA kernels
 
 // Host-side checks (no HIP calls); return a moe_status.
@@ -29,6 +28,10 @@ int validate_weights(const moe_layer_desc *d, const moe_weights *w, bool need_ro
                      bool need_experts);
 
 inline int64_t act_bytes(const moe_layer_desc *d) { return d->act_dtype == MOE_DT_BF16 ? 2 : 4; }
+// Affine 4- or 8-bit expert weights (fp16 matrix-core path with fp16 staging).
+inline bool affine(const moe_layer_desc *d) {
+  return d->w_format == MOE_WF_AFFINE_Q4 || d->w_format == MOE_WF_AFFINE_Q8;
+}
 // Bytes per element of the SwiGLU intermediate h (bf16 for bf16 layers).
 inline int64_t h_bytes(const moe_layer_desc *d) { return d->act_dtype == MOE_DT_BF16 ? 2 : 4; }
 bool use_mfma(const moe_layer_desc *d);
@@ -47,8 +50,8 @@ struct Workspace {
   size_t act_items;                   // [E+S] PlanItem
   size_t tiles;                       // [max_tiles] PlanItem
   size_t h;                           // [N+S*T][d_ff] h_bytes
-  size_t hsh;                         // [N+S*T][ceil(d_ff/128)] int8 (4-bit layers)
-  size_t x16, xsh;                    // [T][d_model] fp16, [T] int8 (4-bit layers)
+  size_t hsh;                         // [N+S*T][ceil(d_ff/128)] int8 (affine layers)
+  size_t x16, xsh;                    // [T][d_model] fp16, [T] int8 (affine layers)
   size_t y_sorted;                    // [N+S*T][d_model] ys_bytes
   size_t total;
   int64_t max_tiles;

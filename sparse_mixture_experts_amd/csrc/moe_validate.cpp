@@ -12,19 +12,23 @@ static bool is_bool(int32_t v) { return v == 0 || v == 1; }
 int validate_desc(const moe_layer_desc *d) {
   if (!d) return MOE_E_INVALID;
   if (d->act_dtype != MOE_DT_F32 && d->act_dtype != MOE_DT_BF16) return MOE_E_INVALID;
-  if (d->w_format != MOE_WF_DENSE && d->w_format != MOE_WF_AFFINE_Q4) return MOE_E_INVALID;
+  if (d->w_format != MOE_WF_DENSE && !affine(d)) return MOE_E_INVALID;
   if (!is_bool(d->gate_up_fused) || !is_bool(d->swiglu_round_bf16) || !is_bool(d->renormalize))
     return MOE_E_INVALID;
+  if (d->activation != MOE_ACT_SWIGLU && d->activation != MOE_ACT_GEGLU) return MOE_E_INVALID;
   if (d->d_model <= 0 || d->d_ff <= 0 || d->d_model > 16384 || d->d_ff > 16384) return MOE_E_INVALID;
   if (d->n_experts < 1 || d->n_experts > kMaxExperts) return MOE_E_INVALID;
   if (d->top_k < 1 || d->top_k > kMaxTopK || d->top_k > d->n_experts) return MOE_E_INVALID;
   if (d->n_shared < 0 || d->n_shared > kMaxShared) return MOE_E_INVALID;
   if (d->swiglu_round_bf16 && d->act_dtype != MOE_DT_BF16) return MOE_E_INVALID;
-  if (d->w_format == MOE_WF_AFFINE_Q4) {
-    // The q4 format carries bf16 scales/biases and feeds bf16 activations.
+  if (affine(d)) {
+    // The affine formats carry bf16 scales/biases and feed bf16 activations;
+    // groups of 32, 64 or 128 along both reduction dims, which the matrix-core
+    // kernels walk in steps of 64.
     if (d->act_dtype != MOE_DT_BF16) return MOE_E_UNSUPPORTED;
-    if (d->group_size != kGroup) return MOE_E_UNSUPPORTED;
-    if (d->d_model % kGroup || d->d_ff % kGroup) return MOE_E_INVALID;
+    const int g = d->group_size;
+    if (g != 32 && g != 64 && g != 128) return MOE_E_UNSUPPORTED;
+    if (d->d_model % 64 || d->d_ff % 64 || d->d_model % g || d->d_ff % g) return MOE_E_INVALID;
   } else {
     if (d->d_model % 8 || d->d_ff % 8) return MOE_E_INVALID;
   }
@@ -46,7 +50,7 @@ int validate_ptr(const void *p, bool may_be_null) {
 static int validate_proj(const moe_layer_desc *d, const moe_proj &p) {
   int s = validate_ptr(p.w);
   if (s) return s;
-  if (d->w_format == MOE_WF_AFFINE_Q4) {
+  if (affine(d)) {
     if ((s = validate_ptr(p.scales))) return s;
     if ((s = validate_ptr(p.biases))) return s;
   }
@@ -101,7 +105,7 @@ Workspace workspace_layout(const moe_layer_desc *d, int32_t T) {
   ws.act_items = take(size_t(E + S) * sizeof(PlanItem));
   ws.tiles = take(size_t(ws.max_tiles) * sizeof(PlanItem));
   ws.h = take(size_t(rows) * d->d_ff * h_bytes(d));
-  const bool q4 = d->w_format == MOE_WF_AFFINE_Q4;
+  const bool q4 = affine(d);
   ws.hsh = take(q4 ? size_t(rows) * ((d->d_ff + kHBlock - 1) / kHBlock) : 0);
   ws.x16 = take(q4 ? size_t(T) * d->d_model * 2 : 0);
   ws.xsh = take(q4 ? size_t(T) : 0);

@@ -358,7 +358,7 @@ int64_t route_scratch_floats(const moe_layer_desc *d, int32_t T) {
 }
 
 bool route_writes_x16(const moe_layer_desc *d) {
-  return d->w_format == MOE_WF_AFFINE_Q4 && d->d_model <= kRowF16MaxD;
+  return affine(d) && d->d_model <= kRowF16MaxD;
 }
 
 bool route_fuses_dispatch(const moe_layer_desc *d, int32_t T) {

@@ -19,7 +19,10 @@ LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
 
 MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = 0, -1, -2, -3, -4
 MOE_DT_F32, MOE_DT_BF16 = 0, 1
-MOE_WF_DENSE, MOE_WF_AFFINE_Q4 = 0, 1
+MOE_WF_DENSE, MOE_WF_AFFINE_Q4, MOE_WF_AFFINE_Q8 = 0, 1, 2
+MOE_ACT_SWIGLU, MOE_ACT_GEGLU = 0, 1
+_WFMT = {"dense": MOE_WF_DENSE, "q4": MOE_WF_AFFINE_Q4, "q8": MOE_WF_AFFINE_Q8}
+_ACT = {"swiglu": MOE_ACT_SWIGLU, "geglu": MOE_ACT_GEGLU}
 
 EXPORTED = ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
             "moe_forward", "moe_forward_timed", "moe_status_string")
@@ -34,7 +37,7 @@ class MoeError(RuntimeError):
 class LayerDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d_model", "d_ff", "n_experts", "top_k", "n_shared", "act_dtype", "w_format", "group_size",
-        "gate_up_fused", "swiglu_round_bf16", "renormalize")]
+        "gate_up_fused", "swiglu_round_bf16", "renormalize", "activation")]
 
 
 class Proj(ctypes.Structure):
@@ -80,17 +83,19 @@ def moe_status_string(status: int) -> str:
 
 
 def make_desc(d_model, d_ff, n_experts, top_k, n_shared=0, act="bf16", wfmt="dense", group_size=64,
-              gate_up_fused=False, swiglu_round_bf16=False, renormalize=True) -> LayerDesc:
+              gate_up_fused=False, swiglu_round_bf16=False, renormalize=True,
+              activation="swiglu") -> LayerDesc:
+    """wfmt: "dense", "q4" or "q8" (affine 4-/8-bit codes); activation: "swiglu" or "geglu"."""
     return LayerDesc(d_model, d_ff, n_experts, top_k, n_shared,
                      MOE_DT_BF16 if act == "bf16" else MOE_DT_F32,
-                     MOE_WF_AFFINE_Q4 if wfmt == "q4" else MOE_WF_DENSE, group_size,
-                     int(gate_up_fused), int(swiglu_round_bf16), int(renormalize))
+                     _WFMT[wfmt], group_size,
+                     int(gate_up_fused), int(swiglu_round_bf16), int(renormalize), _ACT[activation])
 
 
 def desc_from_spec(spec) -> LayerDesc:
     return make_desc(spec.d_model, spec.d_ff, spec.n_experts, spec.top_k, spec.n_shared, spec.act,
                      spec.wfmt, spec.group_size, spec.gate_up_fused, spec.swiglu_round_bf16,
-                     spec.renormalize)
+                     spec.renormalize, spec.activation)
 
 
 def _ptr(t):

@@ -66,9 +66,11 @@ def test_status_strings(lib):
     ("n_experts", 1025, moe.MOE_E_INVALID), ("top_k", 0, moe.MOE_E_INVALID),
     ("top_k", 33, moe.MOE_E_INVALID), ("n_shared", -1, moe.MOE_E_INVALID),
     ("n_shared", 9, moe.MOE_E_INVALID), ("act_dtype", 5, moe.MOE_E_INVALID),
-    ("w_format", 3, moe.MOE_E_INVALID), ("group_size", 32, moe.MOE_E_UNSUPPORTED),
-    ("group_size", 128, moe.MOE_E_UNSUPPORTED), ("act_dtype", moe.MOE_DT_F32, moe.MOE_E_UNSUPPORTED),
+    ("w_format", 3, moe.MOE_E_INVALID), ("group_size", 16, moe.MOE_E_UNSUPPORTED),
+    ("group_size", 96, moe.MOE_E_UNSUPPORTED), ("group_size", 256, moe.MOE_E_UNSUPPORTED),
+    ("act_dtype", moe.MOE_DT_F32, moe.MOE_E_UNSUPPORTED),
     ("renormalize", 2, moe.MOE_E_INVALID), ("gate_up_fused", -1, moe.MOE_E_INVALID),
+    ("activation", 2, moe.MOE_E_INVALID), ("activation", -1, moe.MOE_E_INVALID),
 ])
 def test_descriptor_validation(lib, field, value, status):
     d = good()
@@ -79,6 +81,20 @@ def test_descriptor_validation(lib, field, value, status):
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_route(d, 4, A, A, None, A, A, None, stream=0)
     assert ei.value.status == status
+
+
+def test_affine_formats_and_groups(lib):
+    size = ctypes.c_size_t()
+    for wfmt in ("q4", "q8"):
+        for g in (32, 64, 128):
+            d = moe.make_desc(2048, 768, 128, 8, wfmt=wfmt, group_size=g, activation="geglu")
+            assert lib.moe_workspace_size(ctypes.byref(d), 4, ctypes.byref(size)) == moe.MOE_OK
+    # the group must divide both reduction lengths
+    d = moe.make_desc(2048, 192, 128, 8, wfmt="q8", group_size=128)
+    assert lib.moe_workspace_size(ctypes.byref(d), 4, ctypes.byref(size)) == moe.MOE_E_INVALID
+    # the affine formats feed bf16 activations only
+    d = moe.make_desc(2048, 768, 128, 8, act="f32", wfmt="q8")
+    assert lib.moe_workspace_size(ctypes.byref(d), 4, ctypes.byref(size)) == moe.MOE_E_UNSUPPORTED
 
 
 def test_top_k_above_experts_and_rounding_needs_bf16(lib):

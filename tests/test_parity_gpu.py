@@ -2,7 +2,7 @@
 
 Bit-exact: topk_idx, order, inv_order, row_map, expert_off, tile_off.
 Tolerance: topk_w within 1e-6 absolute; y within 1e-5 * RMS(y_oracle) for the
-fp32 layers and 2e-2 * RMS(y_oracle) for bf16 / 4-bit layers (fp32 output);
+fp32 layers and 2e-2 * RMS(y_oracle) for bf16 / affine 4- and 8-bit layers (fp32 output);
 a bf16 output must equal the nearest-even rounding of the same run's fp32
 output.  Medium layers (several 64-row tiles per expert, ragged tails, empty
 experts) are compared on every token; the five full-size workloads are run
@@ -46,6 +46,30 @@ MID = {
                                   wfmt="q4", seed=28),
     "mid-plain-mlp": LayerSpec("mid-plain-mlp", T=5, d_model=128, d_ff=128, n_experts=1, top_k=1,
                                seed=29),
+    # 8-bit codes, groups of 32 and 128, and the tanh-GELU GLU on every kernel
+    # family: 64-row tiles, 16-row tiles, decode tiles, dense bf16 matrix
+    # cores and the fp32 vector-unit path
+    "mid-q8": LayerSpec("mid-q8", T=200, d_model=512, d_ff=256, n_experts=16, top_k=4, wfmt="q8", seed=32),
+    "mid-q8-g32-geglu-fused-round": LayerSpec("mid-q8-g32-geglu-fused-round", T=150, d_model=256, d_ff=192,
+                                              n_experts=16, top_k=3, wfmt="q8", group_size=32,
+                                              activation="geglu", gate_up_fused=True, swiglu_round_bf16=True,
+                                              seed=33),
+    "mid-q4-g128-shared": LayerSpec("mid-q4-g128-shared", T=120, d_model=384, d_ff=256, n_experts=12, top_k=2,
+                                    n_shared=1, wfmt="q4", group_size=128, router_bias="zipf", seed=34),
+    "mid-q4-g32-geglu-tile16": LayerSpec("mid-q4-g32-geglu-tile16", T=40, d_model=256, d_ff=192, n_experts=32,
+                                         top_k=4, wfmt="q4", group_size=32, activation="geglu", seed=35),
+    "mid-q8-decode-g128-geglu": LayerSpec("mid-q8-decode-g128-geglu", T=3, d_model=512, d_ff=256, n_experts=64,
+                                          top_k=8, wfmt="q8", group_size=128, activation="geglu", seed=36),
+    "mid-q4-decode-g32-geglu-fused-round": LayerSpec("mid-q4-decode-g32-geglu-fused-round", T=4, d_model=320,
+                                                     d_ff=192, n_experts=32, top_k=4, n_shared=1, wfmt="q4",
+                                                     group_size=32, activation="geglu", gate_up_fused=True,
+                                                     swiglu_round_bf16=True, seed=37),
+    "mid-q8-decode-fused": LayerSpec("mid-q8-decode-fused", T=2, d_model=1024, d_ff=320, n_experts=32, top_k=4,
+                                     wfmt="q8", gate_up_fused=True, seed=38),
+    "mid-bf16-geglu": LayerSpec("mid-bf16-geglu", T=100, d_model=192, d_ff=128, n_experts=8, top_k=2,
+                                activation="geglu", seed=39),
+    "mid-f32-geglu": LayerSpec("mid-f32-geglu", T=17, d_model=96, d_ff=64, n_experts=4, top_k=2, act="f32",
+                               activation="geglu", x_scale="fan_in", seed=40),
 }
 FULL = inputs.CONFIGS
 SAMPLE = 48  # tokens compared per full-size layer (all when T is smaller)
@@ -62,7 +86,8 @@ def get(name):
             _host[name] = inputs.gen_layer(spec)
         L = _host[name]
         print(f"[case] {name}: T={spec.T} d={spec.d_model} d_ff={spec.d_ff} E={spec.n_experts} "
-              f"k={spec.top_k} S={spec.n_shared} {spec.act}/{spec.wfmt}", flush=True)
+              f"k={spec.top_k} S={spec.n_shared} {spec.act}/{spec.wfmt} g{spec.group_size} {spec.activation}",
+              flush=True)
         _layers.clear()
         _layers[name] = (L, GpuLayer(L))
     return _layers[name]
@@ -246,15 +271,15 @@ def test_route_exact_ties_and_zero_rows(T):
     assert np.max(np.abs(wt - rw)) <= 1e-6
 
 
-@pytest.mark.parametrize("T", [80, 6])
-def test_fp16_range_shifts(T):
-    """Activations beyond the fp16 range (|x| up to 2^20) and 4-bit scales and
+@pytest.mark.parametrize("T,wfmt,group", [(80, "q4", 64), (6, "q4", 64), (80, "q8", 32), (6, "q8", 128)])
+def test_fp16_range_shifts(T, wfmt, group):
+    """Activations beyond the fp16 range (|x| up to 2^20) and affine scales and
     biases beyond it (x 2^16) take the power-of-two shifted path of the fp16
     MFMA kernels in both projections; each token must still match the oracle
     to the tolerance, relative to that token's own largest output (a few
     columns carry almost all of the output here, so the usual RMS yardstick
     would measure bf16 rounding of h relative to a much smaller number)."""
-    spec = LayerSpec("big", T=T, d_model=256, d_ff=128, n_experts=8, top_k=2, wfmt="q4", seed=41)
+    spec = LayerSpec("big", T=T, d_model=256, d_ff=128, n_experts=8, top_k=2, wfmt=wfmt, group_size=group, seed=41)
     L = inputs.gen_layer(spec)
     x = L["x"].astype(np.uint32)
     x[3::9] += 20 << 7          # those rows times 2^20 (bf16 exponent field)
