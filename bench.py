@@ -74,6 +74,12 @@ def workload_name(spec) -> str:
             f"E={spec.n_experts} top-{spec.top_k}, {spec.act} activations, {w} experts{extra}")
 
 
+def data_note(spec) -> str:
+    w = (f"quantised to affine {spec.bits}-bit g{spec.group_size}" if spec.quantized
+         else f"stored as {spec.act}")
+    return f"synthetic (seeded N(0,1/fan_in) weights {w}, N(0,1) {spec.act} x)"
+
+
 def expert_bytes(spec) -> int:
     """Stored bytes of one expert's gate, up and down weights."""
     n = 3 * spec.d_model * spec.d_ff
@@ -133,7 +139,7 @@ def run_config(name, steps, warmup, use_graph, hip):
     import torch
     from sparse_mixture_experts_amd import inputs, moe
 
-    spec = inputs.CONFIGS[name]
+    spec = inputs.workload(name)
     dev = "cuda:0"
     t0 = time.time()
     host = inputs.gen_layer(spec)
@@ -321,7 +327,7 @@ def cpu_baseline(name, n_tokens):
     import oracle
     from sparse_mixture_experts_amd import inputs
 
-    spec = inputs.CONFIGS[name]
+    spec = inputs.workload(name)
     host = inputs.gen_layer(spec)
     d = oracle.Desc(spec.d_model, spec.d_ff, spec.n_experts, spec.top_k, spec.n_shared, spec.act == "bf16",
                     spec.quantized, spec.group_size, spec.gate_up_fused, spec.swiglu_round_bf16,
@@ -390,7 +396,7 @@ def main():
         "metric": METRIC, "value": round(head["rows_per_s"], 1), "unit": "routed rows/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": path_dtype(spec),
-        "data": "synthetic (seeded N(0,1/fan_in) weights quantised to affine 4-bit g64, N(0,1) bf16 x)",
+        "data": data_note(spec),
         "config": {"workload": workload_name(spec), "T": spec.T, "d_model": spec.d_model, "d_ff": spec.d_ff,
                    "n_experts": spec.n_experts, "top_k": spec.top_k, "n_shared": spec.n_shared,
                    "routed_rows": spec.T * spec.top_k, "weight_copies_rotated": head["weight_copies"],

@@ -170,7 +170,7 @@ struct WSlab { uint4 w[kNT][QB == 0 ? kSteps : QB / 4]; };
 // of the slab and the four steps cover it.  A lane's 32 elements lie in one
 // group: group 32*lg / (128 / GPS) of the slab.
 template <bool GATEUP, int QB, int RB, int GPS>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
+__device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
   constexpr bool AFF = QB != 0;                    // affine codes (fp16 path)
   constexpr int kLPG = 4 / GPS;                   // lanes lg per group
   constexpr float kQMax = QB == 8 ? 255.0f : 15.0f;
@@ -445,14 +445,15 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
 
   // ---- pipelined main loop ----
   // Weights run PDS slabs ahead in a ring of register buffers (two slabs for
-  // affine weights; dense slabs are four times the 4-bit size, so one); the
+  // 4-bit weights; 8-bit and dense slabs are two and four times larger, so
+  // one); the
   // activation slab s+1 is loaded before slab s is multiplied and written to
   // the other LDS buffer after it, and the barrier there also reports
   // whether slab s+1 carries exponents.  Steps past the last slab only keep
   // the barrier pattern; their loads are clamped repeats.  SLOW = false: no
   // rescaling, and the loop gives up (returns true) before the first slab
   // with exponents; SLOW = true: rescales around every such slab.
-  constexpr int PDS = AFF ? 2 : 1;
+  constexpr int PDS = QB == 4 ? 2 : 1;
   auto run = [&](auto slow_tag) __attribute__((always_inline)) -> bool {
     constexpr bool SLOW = decltype(slow_tag)::value;
     WSlab<QB> wb[PDS];
@@ -575,6 +576,22 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   }
 }
 
+// Two entry points over the same body.  The second asks for two waves per
+// SIMD, so that the register allocator keeps within 256 registers
+// (accumulators included) without spilling; it serves the variants that
+// would otherwise need more (8-bit codes, 4-bit down with groups of 32 and
+// dense bf16 with 64-row tiles).  The others allocate on their own, which
+// keeps their accumulators in AGPRs and measured faster.
+template <bool GATEUP, int QB, int RB, int GPS>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
+  grouped_gemm_body<GATEUP, QB, RB, GPS>(a);
+}
+template <bool GATEUP, int QB, int RB, int GPS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void grouped_gemm_kernel_w2(
+    GemmArgs a) {
+  grouped_gemm_body<GATEUP, QB, RB, GPS>(a);
+}
+
 // ---- decode tiles (at most 16 rows of an expert, K <= 2048) ----------------
 // One wave owns 16 weight rows and loads all of their codes and scales at
 // once (one memory round trip), while the workgroup stages the tile's
@@ -585,10 +602,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
 // gate/up: a wave's rows are 8 gate rows and the 8 up rows of the same
 // columns (the GLU pairs sit 32 lanes apart in the MFMA result), h is
 // written as bf16.  down: 16 output columns, h read as bf16.
-constexpr int kDecMaxK = 2048;
-// Longest reduction held in registers: 16 slabs of 4-bit codes or 8 of
-// 8-bit codes (64 registers of codes per lane either way).
-constexpr int dec_max_k(int qb) { return qb == 8 ? 1024 : kDecMaxK; }
+constexpr int kDecMaxK = 2048;  // 16 slabs: 64 (4-bit) or 128 (8-bit) registers of codes per lane
 
 struct DecArgs {
   const void *act;          // gate/up: fp16 staging copy of x [T][K]; down: h bf16 [rows][K]
@@ -795,7 +809,11 @@ void launch_one(const GemmArgs &ga, int64_t max_tiles, hipStream_t s) {
   constexpr int NTH = GATEUP ? kNT / 2 : kNT;
   const int cols_per_block = kNW * NTH * 16;
   const dim3 grid((ga.n_out + cols_per_block - 1) / cols_per_block, unsigned(max_tiles));
-  hipLaunchKernelGGL((grouped_gemm_kernel<GATEUP, QB, RB, GPS>), grid, dim3(kThreads), 0, s, ga);
+  // 4-bit codes with groups of 64 or 128, and every 16-row tile, fit two
+  // waves per SIMD by themselves (4-bit gate/up with groups of 32 too).
+  constexpr bool kFits = RB == 1 || (QB == 4 && (GPS <= 2 || GATEUP));
+  if constexpr (kFits) hipLaunchKernelGGL((grouped_gemm_kernel<GATEUP, QB, RB, GPS>), grid, dim3(kThreads), 0, s, ga);
+  else hipLaunchKernelGGL((grouped_gemm_kernel_w2<GATEUP, QB, RB, GPS>), grid, dim3(kThreads), 0, s, ga);
 }
 // Code width (0: dense bf16) and groups per slab picked at run time.
 template <bool GATEUP, int RB, int QB>
@@ -828,12 +846,17 @@ void launch_decode_ms(const DecArgs &da, int64_t max_tiles, hipStream_t s) {
   const dim3 grid((da.n_out + cols_per_block - 1) / cols_per_block, unsigned(max_tiles));
   hipLaunchKernelGGL((decode_gemm_kernel<GATEUP, QB, MS>), grid, dim3(kThreads), lds, s, da);
 }
-// K <= 1024: 8 slabs of registers; K <= 2048 (4-bit codes only): 16.
+// K <= 1024: 8 slabs of registers; K <= 2048: 16.
 template <bool GATEUP>
 void launch_decode(const DecArgs &da, int qb, int64_t max_tiles, hipStream_t s) {
-  if (qb == 8) launch_decode_ms<GATEUP, 8, 8>(da, max_tiles, s);
-  else if (da.K <= 8 * kKS) launch_decode_ms<GATEUP, 4, 8>(da, max_tiles, s);
-  else launch_decode_ms<GATEUP, 4, 16>(da, max_tiles, s);
+  const bool short_k = da.K <= 8 * kKS;
+  if (qb == 8) {
+    if (short_k) launch_decode_ms<GATEUP, 8, 8>(da, max_tiles, s);
+    else launch_decode_ms<GATEUP, 8, 16>(da, max_tiles, s);
+  } else {
+    if (short_k) launch_decode_ms<GATEUP, 4, 8>(da, max_tiles, s);
+    else launch_decode_ms<GATEUP, 4, 16>(da, max_tiles, s);
+  }
 }
 
 }  // namespace
@@ -876,8 +899,8 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
   GemmArgs dn{sc.h, sc.hsh, nullptr, nblk, nullptr, T, T * d->top_k, d->d_ff, d->d_model, 0, 0, 0,
               w->down.w, static_cast<const uint16_t *>(w->down.scales), static_cast<const uint16_t *>(w->down.biases),
               nullptr, nullptr, nullptr, counters, tiles, y_sorted, ys_bf16};
-  if (tr == 16 && aff && int64_t(T) * d->top_k <= d->n_experts && d->d_model <= dec_max_k(qb) &&
-      d->d_ff <= dec_max_k(qb)) {
+  if (tr == 16 && aff && int64_t(T) * d->top_k <= d->n_experts && d->d_model <= kDecMaxK &&
+      d->d_ff <= kDecMaxK) {
     // at most one routed row per expert on average: whole-K loads per wave
     // (one memory round trip), h as bf16 between the two projections
     DecArgs dg{sc.x16, sc.xsh, row_map, T, T * d->top_k, d->d_model, d->d_ff, d->gate_up_fused,

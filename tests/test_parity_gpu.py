@@ -5,9 +5,10 @@ Tolerance: topk_w within 1e-6 absolute; y within 1e-5 * RMS(y_oracle) for the
 fp32 layers and 2e-2 * RMS(y_oracle) for bf16 / affine 4- and 8-bit layers (fp32 output);
 a bf16 output must equal the nearest-even rounding of the same run's fp32
 output.  Medium layers (several 64-row tiles per expert, ragged tails, empty
-experts) are compared on every token; the five full-size workloads are run
-exactly as the benchmark runs them and compared on sampled tokens (all tokens
-where T is small), with routing compared on every token.
+experts) are compared on every token; the five full-size workloads and their
+8-bit, group-32/128 and GeGLU variants are run exactly as the benchmark runs
+them and compared on sampled tokens (all tokens where T is small), with
+routing compared on every token.
 """
 import math
 
@@ -66,12 +67,16 @@ MID = {
                                                      swiglu_round_bf16=True, seed=37),
     "mid-q8-decode-fused": LayerSpec("mid-q8-decode-fused", T=2, d_model=1024, d_ff=320, n_experts=32, top_k=4,
                                      wfmt="q8", gate_up_fused=True, seed=38),
+    # decode tiles holding more than 1024 8-bit codes per lane row, down's
+    # reduction 64 mod 128
+    "mid-q8-decode-longk": LayerSpec("mid-q8-decode-longk", T=2, d_model=1536, d_ff=1088, n_experts=32, top_k=4,
+                                     wfmt="q8", group_size=32, activation="geglu", seed=42),
     "mid-bf16-geglu": LayerSpec("mid-bf16-geglu", T=100, d_model=192, d_ff=128, n_experts=8, top_k=2,
                                 activation="geglu", seed=39),
     "mid-f32-geglu": LayerSpec("mid-f32-geglu", T=17, d_model=96, d_ff=64, n_experts=4, top_k=2, act="f32",
                                activation="geglu", x_scale="fan_in", seed=40),
 }
-FULL = inputs.CONFIGS
+FULL = {**inputs.CONFIGS, **inputs.VARIANTS}
 SAMPLE = 48  # tokens compared per full-size layer (all when T is smaller)
 
 _host: dict = {}
