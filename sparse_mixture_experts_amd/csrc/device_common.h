@@ -30,13 +30,85 @@ __device__ __forceinline__ float load_act(const void *p, int64_t i) {
   else return static_cast<const float *>(p)[i];
 }
 
+// Wave-wide reductions on DPP lane moves (no LDS round trip): within quads,
+// then mirrored half rows and rows of 16, then two row broadcasts that leave
+// the result in lane 63, read back as a uniform value.  Every lane must be
+// active.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_move(float old, float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+constexpr int kDppQuadSwap1 = 0xb1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4e;   // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppRowMirror = 0x140;  // row_mirror
+constexpr int kDppBcast15 = 0x142;    // row_bcast:15
+constexpr int kDppBcast31 = 0x143;    // row_bcast:31
+
+__device__ __forceinline__ float read_lane(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_move<kDppQuadSwap1>(v, v));
+  v = fmaxf(v, dpp_move<kDppQuadSwap2>(v, v));
+  v = fmaxf(v, dpp_move<kDppHalfMirror>(v, v));
+  v = fmaxf(v, dpp_move<kDppRowMirror>(v, v));
+  v = fmaxf(v, dpp_move<kDppBcast15, 0xa>(v, v));
+  v = fmaxf(v, dpp_move<kDppBcast31, 0xc>(v, v));
+  return read_lane(v, 63);
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_move<kDppQuadSwap1>(0.f, v);
+  v += dpp_move<kDppQuadSwap2>(0.f, v);
+  v += dpp_move<kDppHalfMirror>(0.f, v);
+  v += dpp_move<kDppRowMirror>(0.f, v);
+  v += dpp_move<kDppBcast15, 0xa>(0.f, v);
+  v += dpp_move<kDppBcast31, 0xc>(0.f, v);
+  return read_lane(v, 63);
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Inclusive prefix sum over the wave's lanes on DPP moves: the sums of up to
+// four lanes (row shifts by 1, 2, 3), then row shifts by 4 and 8 on the upper
+// banks, then the two row broadcasts.  Every lane must be active.
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
+__device__ __forceinline__ int dpp_move_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, BANK_MASK, false);
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  int s = v + dpp_move_i<0x111>(v);
+  s += dpp_move_i<0x112>(v);
+  s += dpp_move_i<0x113>(v);
+  s += dpp_move_i<0x114, 0xf, 0xe>(s);
+  s += dpp_move_i<0x118, 0xf, 0xc>(s);
+  s += dpp_move_i<kDppBcast15, 0xa>(s);
+  s += dpp_move_i<kDppBcast31, 0xc>(s);
+  return s;
+}
+__device__ __forceinline__ int read_lane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
+// The entry that ranks first among a wave's MPL values per lane (entry
+// lane + 64*m; larger value first, lower entry number on equal values, -0 ==
+// +0), skipping entries at or past n and those marked in `taken` (bit m).
+// Returns the entry number (uniform) and its value in `best`.
+template <int MPL>
+__device__ __forceinline__ int wave_argmax(const float (&v)[MPL], int n, uint32_t taken, float &best) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int m = 0; m < MPL; ++m)
+    if (lane + kWave * m < n && !((taken >> m) & 1u)) mx = fmaxf(mx, v[m]);
+  mx = wave_max(mx);
+  best = mx;
+#pragma unroll
+  for (int m = 0; m < MPL; ++m) {
+    const uint64_t hit = __ballot(lane + kWave * m < n && !((taken >> m) & 1u) && v[m] == mx);
+    if (hit) return kWave * m + __builtin_ctzll(hit);
+  }
+  return -1;  // only when fewer than one untaken entry remains
+}
 
 // Sigmoid and SiLU on the hardware exp2 and reciprocal (a few ulp of fp32;
 // the per-op bf16 rounding that follows in the rounded SwiGLU hides them).

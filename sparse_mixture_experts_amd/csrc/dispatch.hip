@@ -46,22 +46,12 @@ __device__ int block_exscan(int32_t *a, int n, int32_t *wave_tot) {
   const int b = min(n, tid * chunk), e = min(n, b + chunk);
   int s = 0;
   for (int i = b; i < e; ++i) s += a[i];
-  int v = s;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
+  const int v = wave_incl_scan(s);
   if (lane == 63) wave_tot[w] = v;
   __syncthreads();
   if (w == 0) {
     const int wt = lane < nw ? wave_tot[lane] : 0;
-    int iv = wt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_up(iv, o, 64);
-      if (lane >= o) iv += u;
-    }
+    const int iv = wave_incl_scan(wt);
     if (lane < nw) wave_tot[lane] = iv - wt;
     if (lane == nw - 1) wave_tot[nw] = iv;
   }

@@ -54,20 +54,10 @@ __device__ __forceinline__ void tiny_dispatch(const int32_t *f, int N, int K, in
     ps += (c + tr - 1) / tr;
     as += c > 0;
   }
-  int rx = rs, ux = us, px = ps, ax = as;  // inclusive scans
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int r2 = __shfl_up(rx, o, kWave), u2 = __shfl_up(ux, o, kWave);
-    const int p2 = __shfl_up(px, o, kWave), a2 = __shfl_up(ax, o, kWave);
-    if (lane >= o) {
-      rx += r2;
-      ux += u2;
-      px += p2;
-      ax += a2;
-    }
-  }
-  const int n_utiles = __shfl(ux, kWave - 1, kWave), n_ptiles = __shfl(px, kWave - 1, kWave);
-  const int n_act = __shfl(ax, kWave - 1, kWave);
+  // inclusive scans
+  const int rx = wave_incl_scan(rs), ux = wave_incl_scan(us), px = wave_incl_scan(ps), ax = wave_incl_scan(as);
+  const int n_utiles = read_lane_i(ux, kWave - 1), n_ptiles = read_lane_i(px, kWave - 1);
+  const int n_act = read_lane_i(ax, kWave - 1);
   int r = rx - rs, u = ux - us, pt = px - ps, ac = ax - as;  // exclusive bases of this lane's run
   for (int e = b; e < b1; ++e) {
     const int c = cnt[e];

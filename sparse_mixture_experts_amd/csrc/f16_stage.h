@@ -63,8 +63,7 @@ __device__ __forceinline__ void row_to_f16(const uint16_t *x, int D, uint16_t *o
   const int P = D / 8;
   float mx = 0.f;
   for (int p = lane; p < P; p += kWave) mx = fmaxf(mx, absmax8_bf16(src[p]));
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  mx = wave_max(mx);
   const int sh = f16_shift(mx);
   for (int p = lane; p < P; p += kWave) dst[p] = permute8(bf16x8_to_f16(src[p], sh));
   if (lane == 0) *sh_out = int8_t(sh);
@@ -88,8 +87,7 @@ __device__ __forceinline__ void row_f16_store(const RowF16 &r, int D, uint16_t *
 #pragma unroll
   for (int q = 0; q < 8; ++q)
     if ((q * kWave + lane) * 8 < D) mx = fmaxf(mx, absmax8_bf16(r.v[q]));
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  mx = wave_max(mx);
   const int sh = f16_shift(mx);
 #pragma unroll
   for (int q = 0; q < 8; ++q)

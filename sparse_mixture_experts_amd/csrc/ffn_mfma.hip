@@ -446,23 +446,29 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
   // ---- pipelined main loop ----
   // Weights run PDS slabs ahead in a ring of register buffers (two slabs for
   // 4-bit weights; 8-bit and dense slabs are two and four times larger, so
-  // one); the
-  // activation slab s+1 is loaded before slab s is multiplied and written to
-  // the other LDS buffer after it, and the barrier there also reports
-  // whether slab s+1 carries exponents.  Steps past the last slab only keep
-  // the barrier pattern; their loads are clamped repeats.  SLOW = false: no
-  // rescaling, and the loop gives up (returns true) before the first slab
-  // with exponents; SLOW = true: rescales around every such slab.
+  // one); the activation slab s+1 is loaded before slab s is multiplied and
+  // written to the other LDS buffer after it, behind one barrier per slab.
+  // Steps past the last slab only keep the barrier pattern; their loads are
+  // clamped repeats.  SLOW = true: the barrier also votes on whether the
+  // next slab carries exponents, and such slabs are rescaled.  SLOW = false:
+  // no rescaling; for 64-row tiles each thread notes whether a slab it
+  // staged carries exponents and one vote after the last slab reports
+  // whether any did (the tile's results are then discarded); 16-row tiles
+  // vote at every barrier and give up at the first such slab (fewer
+  // registers live across the loop: three waves per SIMD).
   constexpr int PDS = QB == 4 ? 2 : 1;
+  constexpr bool kLateVote = RB > 1;
   auto run = [&](auto slow_tag) __attribute__((always_inline)) -> bool {
     constexpr bool SLOW = decltype(slow_tag)::value;
+    constexpr bool VOTE = SLOW || !kLateVote;  // vote at every barrier
     WSlab<QB> wb[PDS];
     stage_load(0);
-    const int f0 = stage_write(0);
+    int flag = stage_write(0);
 #pragma unroll
     for (int u = 0; u < PDS; ++u) load_slab(u, wb[u]);
-    int flag = __syncthreads_or(f0);
-    if (!SLOW && flag) return true;
+    if constexpr (VOTE) flag = __syncthreads_or(flag);
+    else __syncthreads();
+    if (!SLOW && VOTE && flag) return true;
     for (int s0 = 0; s0 < nslab; s0 += PDS) {
 #pragma unroll
       for (int u = 0; u < PDS; ++u) {
@@ -472,16 +478,22 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
         if (col_ok && s < nslab) compute_slab(sm[buf], wb[u]);
         load_slab(s + PDS, wb[u]);
         if (SLOW && flag && col_ok) rescale(sm[buf], +1);
-        flag = __syncthreads_or(stage_write(buf ^ 1));
-        if (!SLOW && flag) return true;
+        if constexpr (VOTE) {
+          flag = __syncthreads_or(stage_write(buf ^ 1));
+          if (!SLOW && flag) return true;
+        } else {
+          flag |= stage_write(buf ^ 1);
+          __syncthreads();
+        }
       }
     }
-    return false;
+    if constexpr (VOTE || !AFF) return false;
+    else return __syncthreads_or(flag) != 0;
   };
   if (run(std::false_type{})) {
     if constexpr (AFF) {
-      // Every wave left the fast loop at the same barrier, after its last
-      // read of the slab buffers.
+      // Every wave left the fast loop at the same vote, after its last read
+      // of the slab buffers.
       zero_acc();
       run(std::true_type{});
     }
@@ -577,11 +589,10 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
 }
 
 // Two entry points over the same body.  The second asks for two waves per
-// SIMD, so that the register allocator keeps within 256 registers
-// (accumulators included) without spilling; it serves the variants that
-// would otherwise need more (8-bit codes, 4-bit down with groups of 32 and
-// dense bf16 with 64-row tiles).  The others allocate on their own, which
-// keeps their accumulators in AGPRs and measured faster.
+// SIMD, so that the register allocator keeps the 64-row tiles within 256
+// registers (accumulators included) without spilling; left to itself it
+// gives them one wave per SIMD and moves the accumulators between register
+// files every slab.  16-row tiles allocate on their own.
 template <bool GATEUP, int QB, int RB, int GPS>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
   grouped_gemm_body<GATEUP, QB, RB, GPS>(a);
@@ -809,9 +820,8 @@ void launch_one(const GemmArgs &ga, int64_t max_tiles, hipStream_t s) {
   constexpr int NTH = GATEUP ? kNT / 2 : kNT;
   const int cols_per_block = kNW * NTH * 16;
   const dim3 grid((ga.n_out + cols_per_block - 1) / cols_per_block, unsigned(max_tiles));
-  // 4-bit codes with groups of 64 or 128, and every 16-row tile, fit two
-  // waves per SIMD by themselves (4-bit gate/up with groups of 32 too).
-  constexpr bool kFits = RB == 1 || (QB == 4 && (GPS <= 2 || GATEUP));
+  // 16-row tiles fit two or more waves per SIMD by themselves.
+  constexpr bool kFits = RB == 1;
   if constexpr (kFits) hipLaunchKernelGGL((grouped_gemm_kernel<GATEUP, QB, RB, GPS>), grid, dim3(kThreads), 0, s, ga);
   else hipLaunchKernelGGL((grouped_gemm_kernel_w2<GATEUP, QB, RB, GPS>), grid, dim3(kThreads), 0, s, ga);
 }

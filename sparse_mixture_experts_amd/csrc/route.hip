@@ -43,10 +43,6 @@ __device__ __forceinline__ int xs_at(int k, int t) {
   return (k / kChunk) * (kChunk * TT + kXsPad) + (k % kChunk) * TT + t;
 }
 
-// (v, e) ranks before (bv, be): larger logit first, ties to the lower index.
-__device__ __forceinline__ bool ranks_before(float v, int e, float bv, int be) {
-  return v > bv || (v == bv && e < be);
-}
 
 // Eight consecutive router weights as fp32.
 template <bool BF16>
@@ -245,19 +241,8 @@ __device__ __forceinline__ void select_token(int t, const float *__restrict__ in
   int my_e = 0;
   float my_l = 0.0f, top = 0.0f;
   for (int j = 0; j < K; ++j) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int m = 0; m < MPL; ++m) {
-      const int e = lane + kWave * m;
-      if (e < E && !((taken >> m) & 1u) && ranks_before(l[m], e, bv, be)) { bv = l[m]; be = e; }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oe = __shfl_xor(be, o, kWave);
-      if (ranks_before(ov, oe, bv, be)) { bv = ov; be = oe; }
-    }
+    float bv;
+    const int be = wave_argmax<MPL>(l, E, taken, bv);
     if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
     if (j == 0) top = bv;
     if (lane == j) { my_e = be; my_l = bv; }
@@ -272,7 +257,7 @@ __device__ __forceinline__ void select_token(int t, const float *__restrict__ in
   float w = p;
   if (renorm) {
     float psum = 0.0f;
-    for (int j = 0; j < K; ++j) psum = psum + __shfl(p, j, kWave);
+    for (int j = 0; j < K; ++j) psum = psum + read_lane(p, j);
     w = p / psum;
   }
   if (lane < K) {

@@ -37,9 +37,6 @@ constexpr int kThreads = 256;
 constexpr int kChunk = 64;
 constexpr int kMaxCand = 64;
 
-__device__ __forceinline__ bool ranks_before(float v, int e, float bv, int be) {
-  return v > bv || (v == bv && e < be);
-}
 
 // ---- 1. transpose W [d][E] -> WT [E][d] and squared-norm partials ---------
 // Block (eb, kb): experts eb*64.., columns kb*256..; normp[kb][e] = sum of
@@ -241,11 +238,8 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
     wn = fmaxf(wn, a.wnorm[e]);
     if (a.bias) bmax = fmaxf(bmax, fabsf(a.bias[e]));
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    wn = fmaxf(wn, __shfl_xor(wn, o, kWave));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, o, kWave));
-  }
+  wn = wave_max(wn);
+  bmax = wave_max(bmax);
   const float bound = a.gamma * (sqrtf(xs) * sqrtf(wn) * 1.001f + bmax);
 
   // k-th largest L~ value
@@ -253,21 +247,8 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
   {
     uint32_t taken = 0;
     for (int j = 0; j < K; ++j) {
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int m = 0; m < MPL; ++m) {
-        const int e = lane + kWave * m;
-        if (e < E && !((taken >> m) & 1u) && ranks_before(lv[m], e, bv, be)) { bv = lv[m]; be = e; }
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, kWave);
-        const int oe = __shfl_xor(be, o, kWave);
-        if (ranks_before(ov, oe, bv, be)) { bv = ov; be = oe; }
-      }
+      const int be = wave_argmax<MPL>(lv, E, taken, vk);
       if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
-      vk = bv;
     }
   }
   const float thr = vk - 2.0f * bound;
@@ -355,35 +336,27 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
     __builtin_amdgcn_wave_barrier();
   }
 
-  // top-k over the list
-  int my_e = 0;
+  // top-k over the list.  List positions follow expert order, so the lower
+  // position breaks ties exactly as the lower expert id.
+  int my_p = 0;
   float my_l = 0.f, top = 0.f;
   {
-    uint32_t taken = 0;  // bit q: list entry lane + 64*q taken
-    const int nq = (n + kWave - 1) / kWave;
-    for (int j = 0; j < K; ++j) {
-      float bv = -INFINITY;
-      int be = 0x7fffffff, bp = -1;
-      for (int q = 0; q < nq; ++q) {
-        const int p = lane + kWave * q;
-        if (p < n && !((taken >> q) & 1u)) {
-          const float v = s_l[wv][p];
-          const int e = s_e[wv][p];
-          if (ranks_before(v, e, bv, be)) { bv = v; be = e; bp = p; }
-        }
-      }
+    float ll[MPL];  // list entry lane + 64*q
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, kWave);
-        const int oe = __shfl_xor(be, o, kWave);
-        const int op = __shfl_xor(bp, o, kWave);
-        if (ranks_before(ov, oe, bv, be)) { bv = ov; be = oe; bp = op; }
-      }
+    for (int q = 0; q < MPL; ++q) {
+      const int p = lane + kWave * q;
+      ll[q] = p < n ? s_l[wv][p] : -INFINITY;
+    }
+    uint32_t taken = 0;
+    for (int j = 0; j < K; ++j) {
+      float bv;
+      const int bp = wave_argmax<MPL>(ll, n, taken, bv);
       if ((bp & (kWave - 1)) == lane) taken |= 1u << (bp / kWave);
       if (j == 0) top = bv;
-      if (lane == j) { my_e = be; my_l = bv; }
+      if (lane == j) { my_p = bp; my_l = bv; }
     }
   }
+  const int my_e = s_e[wv][my_p];
 
   // softmax: recomputed logits where listed, L~ elsewhere (cancels when renormalised)
   float z = 0.f;
@@ -395,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
   z = wave_sum(z);
   const float pj = expf(my_l - top) / z;
   float psum = 0.f;
-  for (int j = 0; j < K; ++j) psum = psum + __shfl(pj, j, kWave);
+  for (int j = 0; j < K; ++j) psum = psum + read_lane(pj, j);
   if (lane < K) {
     a.idx_out[int64_t(t) * K + lane] = my_e;
     a.w_out[int64_t(t) * K + lane] = pj / psum;
