@@ -390,10 +390,12 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
     }
   };
 
-  // One slab of every tile of this wave, in kSteps MFMA steps.  Row blocks
-  // past the tile's rows are multiplied too (their results are never
-  // stored), which keeps the body free of branches.
-  auto compute_slab = [&](const Slab<RB, GPS> &S, const WSlab<QB> &ws) {
+  // One slab of every tile of this wave, in kSteps MFMA steps, for the first
+  // NRB row blocks.  Row blocks past the tile's rows but below NRB are
+  // multiplied too (their results are never stored), which keeps the body
+  // free of branches.
+  auto compute_slab = [&](const Slab<RB, GPS> &S, const WSlab<QB> &ws, auto nrb_tag) {
+    constexpr int NRB = decltype(nrb_tag)::value;
     if constexpr (AFF) {
       const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
       h2 s2[kNT], s2_16[kNT], b2[kNT];
@@ -406,9 +408,9 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
       }
 #pragma unroll
       for (int j = 0; j < kSteps; ++j) {
-        f16x8 bx[RB];
+        f16x8 bx[NRB];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+        for (int rb = 0; rb < NRB; ++rb)
           bx[rb] = *reinterpret_cast<const f16x8 *>(&S.a[rb * 16 + lr][lg * 32 + j * 8]);
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
@@ -423,21 +425,21 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
                          : q8_words_to_f16(q.x, q.y, s2[nt], b2[nt], magic);
           }
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) acc[nt][rb] = mfma_f16(aw, bx[rb], acc[nt][rb]);
+          for (int rb = 0; rb < NRB; ++rb) acc[nt][rb] = mfma_f16(aw, bx[rb], acc[nt][rb]);
         }
       }
     } else {
 #pragma unroll
       for (int j = 0; j < kSteps; ++j) {
-        bf16x8 bx[RB];
+        bf16x8 bx[NRB];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+        for (int rb = 0; rb < NRB; ++rb)
           bx[rb] = *reinterpret_cast<const bf16x8 *>(&S.a[rb * 16 + lr][lg * 32 + j * 8]);
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
           const bf16x8 aw = __builtin_bit_cast(bf16x8, ws.w[nt][j]);
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) acc[nt][rb] = mfma_bf16(aw, bx[rb], acc[nt][rb]);
+          for (int rb = 0; rb < NRB; ++rb) acc[nt][rb] = mfma_bf16(aw, bx[rb], acc[nt][rb]);
         }
       }
     }
@@ -458,7 +460,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
   // registers live across the loop: three waves per SIMD).
   constexpr int PDS = QB == 4 ? 2 : 1;
   constexpr bool kLateVote = RB > 1;
-  auto run = [&](auto slow_tag) __attribute__((always_inline)) -> bool {
+  auto run = [&](auto slow_tag, auto nrb_tag) __attribute__((always_inline)) -> bool {
     constexpr bool SLOW = decltype(slow_tag)::value;
     constexpr bool VOTE = SLOW || !kLateVote;  // vote at every barrier
     WSlab<QB> wb[PDS];
@@ -475,7 +477,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
         const int s = s0 + u, buf = s & 1;
         stage_load(s + 1);
         if (SLOW && flag && col_ok) rescale(sm[buf], -1);
-        if (col_ok && s < nslab) compute_slab(sm[buf], wb[u]);
+        if (col_ok && s < nslab) compute_slab(sm[buf], wb[u], nrb_tag);
         load_slab(s + PDS, wb[u]);
         if (SLOW && flag && col_ok) rescale(sm[buf], +1);
         if constexpr (VOTE) {
@@ -490,12 +492,28 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
     if constexpr (VOTE || !AFF) return false;
     else return __syncthreads_or(flag) != 0;
   };
-  if (run(std::false_type{})) {
+  // The fast loop multiplies only the row blocks that hold rows of the tile
+  // (one loop per count for 64-row tiles); the rescaling loop all of them.
+  // 4-bit down with groups of 32 keeps one loop: with four it no longer fits
+  // its registers.
+  using Full = std::integral_constant<int, RB>;
+  constexpr bool kPerCount = RB == 4 && !(QB == 4 && GPS == 4 && !GATEUP);
+  bool redo;
+  if constexpr (kPerCount) {
+    const int nrb = min(RB, (tile.rows + 15) / 16);
+    if (nrb == 4) redo = run(std::false_type{}, Full{});
+    else if (nrb == 3) redo = run(std::false_type{}, std::integral_constant<int, 3>{});
+    else if (nrb == 2) redo = run(std::false_type{}, std::integral_constant<int, 2>{});
+    else redo = run(std::false_type{}, std::integral_constant<int, 1>{});
+  } else {
+    redo = run(std::false_type{}, Full{});
+  }
+  if (redo) {
     if constexpr (AFF) {
       // Every wave left the fast loop at the same vote, after its last read
       // of the slab buffers.
       zero_acc();
-      run(std::true_type{});
+      run(std::true_type{}, Full{});
     }
   }
 
