@@ -14,22 +14,43 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kCols = 8;  // columns per thread (one 16-byte bf16 load, two fp32 ones)
 
-// Eight consecutive expert-output values as fp32.
+// Eight consecutive expert-output values, as loaded (bf16: one 16-byte load;
+// fp32: two) and as fp32.
 template <bool YS_BF16>
-__device__ __forceinline__ void load8(const void *ys, int64_t i, float v[8]) {
+struct Row8 {
+  uint4 u[YS_BF16 ? 1 : 2];
+};
+template <bool YS_BF16>
+__device__ __forceinline__ Row8<YS_BF16> load8(const void *ys, int64_t i) {
+  Row8<YS_BF16> r;
   if constexpr (YS_BF16) {
-    const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(ys) + i);
+    r.u[0] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(ys) + i);
+  } else {
+    const uint4 *q = reinterpret_cast<const uint4 *>(static_cast<const float *>(ys) + i);
+    r.u[0] = q[0];
+    r.u[1] = q[1];
+  }
+  return r;
+}
+template <bool YS_BF16>
+__device__ __forceinline__ void widen8(const Row8<YS_BF16> &r, float v[8]) {
+  if constexpr (YS_BF16) {
+    const uint4 u = r.u[0];
     v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
     v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z); v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
   } else {
-    const float4 *q = reinterpret_cast<const float4 *>(static_cast<const float *>(ys) + i);
-    const float4 a = q[0], b = q[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      v[4 * h] = __uint_as_float(r.u[h].x); v[4 * h + 1] = __uint_as_float(r.u[h].y);
+      v[4 * h + 2] = __uint_as_float(r.u[h].z); v[4 * h + 3] = __uint_as_float(r.u[h].w);
+    }
   }
 }
 
-// Block (t, cb): token t, columns cb*256*8 ..; each thread 8 columns.  All
-// slot rows of a thread are loaded before they are summed (slot order).
+// Block (t, cb): token t, columns cb*256*8 ..; each thread 8 columns.  The
+// token's slot positions and weights are uniform (scalar loads); then all
+// slot rows of a thread (up to 16 bf16 or 8 fp32 rows per round) are in
+// flight together before they are summed in slot order.
 template <bool YS_BF16, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const void *__restrict__ ys,
                                                            const int32_t *__restrict__ inv,
@@ -41,26 +62,30 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void *__restric
   float acc[kCols];
 #pragma unroll
   for (int i = 0; i < kCols; ++i) acc[i] = 0.f;
-  for (int j0 = 0; j0 < K; j0 += 8) {
-    float v[8][kCols], wj[8];
+  constexpr int kSlots = YS_BF16 ? 16 : 8;
+  for (int j0 = 0; j0 < K; j0 += kSlots) {
+    Row8<YS_BF16> r[kSlots];
+    float wj[kSlots];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kSlots; ++u) {
       const int j = min(j0 + u, K - 1);
       const int p = inv[int64_t(t) * K + j];
       const bool ok = j0 + u < K && unsigned(p) < unsigned(N);
       wj[u] = ok ? w[int64_t(t) * K + j] : 0.f;
-      load8<YS_BF16>(ys, int64_t(ok ? p : 0) * D + c, v[u]);
+      r[u] = load8<YS_BF16>(ys, int64_t(ok ? p : 0) * D + c);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < kSlots; ++u)
       if (j0 + u < K) {
+        float v[kCols];
+        widen8<YS_BF16>(r[u], v);
 #pragma unroll
-        for (int i = 0; i < kCols; ++i) acc[i] += wj[u] * v[u][i];
+        for (int i = 0; i < kCols; ++i) acc[i] += wj[u] * v[i];
       }
   }
   for (int s = 0; s < S; ++s) {
     float v[kCols];
-    load8<YS_BF16>(ys, (int64_t(N) + int64_t(s) * T + t) * D + c, v);
+    widen8<YS_BF16>(load8<YS_BF16>(ys, (int64_t(N) + int64_t(s) * T + t) * D + c), v);
 #pragma unroll
     for (int i = 0; i < kCols; ++i) acc[i] += v[i];
   }

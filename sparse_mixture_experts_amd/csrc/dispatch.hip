@@ -323,11 +323,14 @@ __global__ __launch_bounds__(kMbThreads) void dispatch_count_kernel(const int32_
   if (tid == 0) row[E] = bad;
 }
 
-// Each workgroup also forms the global tables it needs from blk: per expert
-// the total over all workgroups (whose exclusive scan gives expert_off) and
-// the sum over earlier workgroups (the start of this workgroup's run), so no
-// separate scan pass is needed; workgroup 0 writes expert_off, tile_off and
-// the work plan.
+// Workgroups 0..B-1 rank their own segments; each forms what it needs from
+// blk: per expert the total over all workgroups (whose exclusive scan gives
+// the expert offsets) and the sum over earlier workgroups (the start of this
+// workgroup's run).  Workgroup B ranks nothing: it writes expert_off,
+// tile_off and the work plan, off the rankers' path.  EPT: experts per
+// thread (E <= EPT * 256); every blk row a thread reads is in flight at once
+// (up to 24 workgroups per round).
+template <int EPT>
 __global__ __launch_bounds__(kMbThreads) void dispatch_rank_kernel(
     const int32_t *__restrict__ f, int N, int K, int E, int S, int T, int seg, int B, int tile_rows, int tr,
     const int32_t *__restrict__ blk, int32_t *__restrict__ order, int32_t *__restrict__ inv_order,
@@ -343,31 +346,32 @@ __global__ __launch_bounds__(kMbThreads) void dispatch_rank_kernel(
   __shared__ int32_t wave_tot[17];
   __shared__ int32_t bad;
   const int tid = threadIdx.x, w = tid >> 6, b = blockIdx.x;
+  const bool planner = b == B;
 
-  int i0, i1;
-  mb_segment(N, seg, i0, i1);
+  int i0 = 0, i1 = 0;
+  if (!planner) mb_segment(N, seg, i0, i1);
   Segment sg;
   seg_load(f, i0, i1, sg);
   for (int q = tid; q < kMbWaves * E; q += kMbThreads) cw[q] = 0;
   if (tid == 0) bad = 0;
-  // column sums of blk, 8 workgroups x up to 4 experts per thread in flight
-  constexpr int kEPT = kMaxExperts / kMbThreads;
-  int ctot[kEPT], cpre[kEPT];
+  // column sums of blk (clamped indices: repeats are loaded but not added)
+  constexpr int kRows = 24;
+  int ctot[EPT], cpre[EPT];
 #pragma unroll
-  for (int i = 0; i < kEPT; ++i) ctot[i] = cpre[i] = 0;
-  for (int b0 = 0; b0 < B; b0 += 8) {
-    int v[kEPT][8];
+  for (int i = 0; i < EPT; ++i) ctot[i] = cpre[i] = 0;
+  for (int b0 = 0; b0 < B; b0 += kRows) {
+    int v[EPT][kRows];
 #pragma unroll
-    for (int i = 0; i < kEPT; ++i)
+    for (int i = 0; i < EPT; ++i)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < kRows; ++u) {
         const int e = min(tid + i * kMbThreads, E - 1);
         v[i][u] = blk[int64_t(min(b0 + u, B - 1)) * (E + 1) + e];
       }
 #pragma unroll
-    for (int i = 0; i < kEPT; ++i)
+    for (int i = 0; i < EPT; ++i)
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < kRows; ++u)
         if (b0 + u < B) {
           ctot[i] += v[i][u];
           if (b0 + u < b) cpre[i] += v[i][u];
@@ -377,7 +381,7 @@ __global__ __launch_bounds__(kMbThreads) void dispatch_rank_kernel(
   for (int q = tid; q < B; q += kMbThreads)
     if (blk[int64_t(q) * (E + 1) + E]) bad = 1;
 #pragma unroll
-  for (int i = 0; i < kEPT; ++i) {
+  for (int i = 0; i < EPT; ++i) {
     const int e = tid + i * kMbThreads;
     if (e < E) {
       tot[e] = off[e] = ctot[i];
@@ -387,21 +391,36 @@ __global__ __launch_bounds__(kMbThreads) void dispatch_rank_kernel(
   }
   __syncthreads();
   if (bad) {
-    // Out-of-range expert id: the -1 result (each workgroup its own positions).
-    const int p0 = b * seg, p1 = min(N, p0 + seg);
-    for (int i = p0 + tid; i < p1; i += kMbThreads) order[i] = inv_order[i] = row_map[i] = -1;
-    if (b == 0) {
+    // Out-of-range expert id: the -1 result (each ranker its own positions).
+    if (planner) {
       for (int e = tid; e <= E; e += kMbThreads) {
         expert_off[e] = e == E ? -1 : 0;
         tile_off[e] = 0;
       }
       if (tid == 0) counters[0] = counters[1] = 0;
+    } else {
+      const int p0 = b * seg, p1 = min(N, p0 + seg);
+      for (int i = p0 + tid; i < p1; i += kMbThreads) order[i] = inv_order[i] = row_map[i] = -1;
     }
     return;
   }
-  seg_count(f, sg, E, cw + w * E, &bad);
   block_exscan(off, E, wave_tot);
-  const int n_utiles = block_exscan(utile, E, wave_tot);
+  if (planner) {
+    const int n_utiles = block_exscan(utile, E, wave_tot);
+    for (int e = tid; e < E; e += kMbThreads) {
+      expert_off[e] = off[e];
+      tile_off[e] = utile[e];
+    }
+    if (tid == 0) {
+      expert_off[E] = N;
+      tile_off[E] = n_utiles;
+    }
+    __syncthreads();
+    emit_plan(off, tot, pre, scr1, wave_tot, E, S, N, T, tr, counters, act_items, tiles);
+    return;
+  }
+  seg_count(f, sg, E, cw + w * E, &bad);
+  __syncthreads();
   for (int e = tid; e < E; e += kMbThreads) {
     int run = off[e] + pre[e];
 #pragma unroll
@@ -413,17 +432,6 @@ __global__ __launch_bounds__(kMbThreads) void dispatch_rank_kernel(
   }
   __syncthreads();
   seg_rank(f, sg, K, E, cw + w * E, order, inv_order, row_map);
-  if (b != 0) return;
-  for (int e = tid; e < E; e += kMbThreads) {
-    expert_off[e] = off[e];
-    tile_off[e] = utile[e];
-  }
-  if (tid == 0) {
-    expert_off[E] = N;
-    tile_off[E] = n_utiles;
-  }
-  __syncthreads();
-  emit_plan(off, tot, pre, scr1, wave_tot, E, S, N, T, tr, counters, act_items, tiles);
 }
 
 // At most 128 slots: one wave does it all.
@@ -485,9 +493,15 @@ void launch_dispatch(const moe_layer_desc *d, int32_t T, const int32_t *idx, int
     const int B = (N + seg - 1) / seg;
     const size_t lds_w = size_t(kMbWaves) * E * sizeof(int32_t);
     hipLaunchKernelGGL(dispatch_count_kernel, dim3(B), dim3(kMbThreads), lds_w, s, idx, N, E, seg, scratch);
-    hipLaunchKernelGGL(dispatch_rank_kernel, dim3(B), dim3(kMbThreads), lds_w + size_t(5 * E) * sizeof(int32_t), s,
-                       idx, N, d->top_k, E, d->n_shared, T, seg, B, tile_rows, tr, scratch, order, inv_order, row_map,
-                       expert_off, tile_off, counters, act_items, tiles);
+    // B ranking workgroups and one planning workgroup
+    auto rank = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(B + 1), dim3(kMbThreads), lds_w + size_t(5 * E) * sizeof(int32_t), s, idx, N,
+                         d->top_k, E, d->n_shared, T, seg, B, tile_rows, tr, scratch, order, inv_order, row_map,
+                         expert_off, tile_off, counters, act_items, tiles);
+    };
+    if (E <= kMbThreads) rank(dispatch_rank_kernel<1>);
+    else if (E <= 2 * kMbThreads) rank(dispatch_rank_kernel<2>);
+    else rank(dispatch_rank_kernel<kMaxExperts / kMbThreads>);
   }
   if (mk) mk->mark("dispatch");
 }
