@@ -331,7 +331,8 @@ def cpu_baseline(name, n_tokens):
     host = inputs.gen_layer(spec)
     d = oracle.Desc(spec.d_model, spec.d_ff, spec.n_experts, spec.top_k, spec.n_shared, spec.act == "bf16",
                     spec.quantized, spec.group_size, spec.gate_up_fused, spec.swiglu_round_bf16,
-                    spec.renormalize, spec.bits, int(spec.activation == "geglu"))
+                    spec.renormalize, spec.bits, int(spec.activation == "geglu"),
+                    spec.act == "f16")
     n = min(n_tokens, spec.T)
     toks = np.linspace(0, spec.T - 1, n).astype(np.int32)
     threads = len(os.sched_getaffinity(0))

@@ -7,9 +7,10 @@ ctypes and NumPy arrays.  It never imports the GPU package, and the GPU
 package never imports it.
 
 Arrays: activations and dense weights are ``float32`` or ``uint16`` holding
-bf16 bits; q4 weights are ``uint32`` words with eight 4-bit codes each (code m
-of a word sits at bits [4m, 4m+4)), scales/biases ``uint16`` bf16 bits stored
-group-major ([..][K/64][N]).
+bf16 (or, with ``act_f16``, fp16) bits; affine weights are ``uint32`` words
+with 32/b b-bit codes each (code m of a word sits at bits [b*m, b*m+b)),
+scales/biases ``uint16`` bits of the 16-bit activation dtype stored
+group-major ([..][K/g][N]).
 """
 from __future__ import annotations
 
@@ -38,7 +39,7 @@ def build() -> str:
 class _Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d_model", "d_ff", "n_experts", "top_k", "n_shared", "act_bf16", "w_q4",
-        "group_size", "gate_up_fused", "swiglu_round_bf16", "renormalize", "w_bits", "activation")]
+        "group_size", "gate_up_fused", "swiglu_round_bf16", "renormalize", "w_bits", "activation", "act_f16")]
 
 
 class _Proj(ctypes.Structure):
@@ -59,6 +60,8 @@ def _open(path: str):
     lib.oracle_bf16_to_f32.restype = ctypes.c_float
     lib.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
     lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_f32.restype = ctypes.c_float
     lib.oracle_router_logits.argtypes = [vp, i32, vp, vp, vp, vp]
     lib.oracle_route.argtypes = [vp, i32, vp, vp, vp, vp, vp]
     lib.oracle_dispatch.argtypes = [i32, i32, i32, vp, i32, vp, vp, vp, vp, vp]
@@ -107,12 +110,17 @@ class Desc:
     renormalize: bool = True
     w_bits: int = 4           # affine code width (4 or 8) when w_q4
     activation: int = 0       # 0: SwiGLU, 1: GeGLU (tanh-GELU)
+    act_f16: bool = False     # fp16 activations, dense weights and scales/biases (act_bf16 False)
+
+    @property
+    def half(self) -> bool:
+        return self.act_bf16 or self.act_f16
 
     def _c(self) -> _Desc:
         return _Desc(self.d_model, self.d_ff, self.n_experts, self.top_k, self.n_shared,
                      int(self.act_bf16), int(self.w_q4), self.group_size,
                      int(self.gate_up_fused), int(self.swiglu_round_bf16), int(self.renormalize),
-                     int(self.w_bits), int(self.activation))
+                     int(self.w_bits), int(self.activation), int(self.act_f16))
 
 
 def _ptr(a):
@@ -124,7 +132,7 @@ def _ptr(a):
 
 def _act(desc: Desc, a):
     a = np.ascontiguousarray(a)
-    want = np.uint16 if desc.act_bf16 else np.float32
+    want = np.uint16 if desc.half else np.float32
     assert a.dtype == want, f"activation array must be {want}, got {a.dtype}"
     return a
 
@@ -142,7 +150,7 @@ def _experts(desc: Desc, w: dict):
         if desc.w_q4:
             assert arrs[0].dtype == np.uint32 and arrs[1].dtype == np.uint16 and arrs[2].dtype == np.uint16
         else:
-            assert arrs[0].dtype == (np.uint16 if desc.act_bf16 else np.float32)
+            assert arrs[0].dtype == (np.uint16 if desc.half else np.float32)
         keep.extend(a for a in arrs if a is not None)
         return _Proj(*[_ptr(a) for a in arrs])
 
@@ -156,6 +164,10 @@ def bf16_to_f32(h: int) -> float:
 
 def f32_to_bf16(f: float) -> int:
     return int(_load().oracle_f32_to_bf16(float(f)))
+
+
+def f16_to_f32(h: int) -> float:
+    return float(_load().oracle_f16_to_f32(int(h)))
 
 
 def router_logits(desc: Desc, x, w_router, router_bias=None) -> np.ndarray:

@@ -44,9 +44,26 @@ uint16_t oracle_f32_to_bf16(float f) {
 
 static float round_bf16(float f) { return oracle_bf16_to_f32(oracle_f32_to_bf16(f)); }
 
+/* IEEE binary16 -> fp32, exact: sign, 5-bit exponent (bias 15), 10-bit
+ * fraction; exponent 0 holds subnormals (fraction * 2^-24), 31 infinities and
+ * NaNs. */
+float oracle_f16_to_f32(uint16_t h) {
+  const uint32_t e = (h >> 10) & 0x1fu, m = h & 0x3ffu;
+  float v;
+  if (e == 0) v = ldexpf((float)m, -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = ldexpf((float)(m | 0x400u), (int)e - 25);
+  return (h & 0x8000u) ? -v : v;
+}
+
+/* A 16-bit value of the activation dtype (bf16, or fp16 with act_f16). */
+static float half_at(const oracle_desc *d, uint16_t h) {
+  return d->act_f16 ? oracle_f16_to_f32(h) : oracle_bf16_to_f32(h);
+}
+
 /* Element i of an activation-dtype array. */
 static float act_at(const oracle_desc *d, const void *p, int64_t i) {
-  if (d->act_bf16) return oracle_bf16_to_f32(((const uint16_t *)p)[i]);
+  if (d->act_bf16 || d->act_f16) return half_at(d, ((const uint16_t *)p)[i]);
   return ((const float *)p)[i];
 }
 
@@ -135,7 +152,7 @@ void oracle_route(const oracle_desc *d, int32_t T, const void *x,
                   const void *w_router, const float *router_bias,
                   int32_t *topk_idx, float *topk_w) {
   const int32_t E = d->n_experts, K = d->top_k;
-  const size_t row_bytes = (size_t)d->d_model * (d->act_bf16 ? 2 : 4);
+  const size_t row_bytes = (size_t)d->d_model * (d->act_bf16 || d->act_f16 ? 2 : 4);
 #pragma omp parallel for schedule(static)
   for (int32_t t = 0; t < T; ++t) {
     float *l = (float *)malloc(sizeof(float) * (size_t)E);
@@ -191,8 +208,12 @@ void oracle_dispatch(int32_t T, int32_t top_k, int32_t n_experts,
  * power-of-two bits 4/8, shift-unpack; DS4Server #112, "Native implementation
  * scope": biases present, 4 or 8 bits, group 32/64/128): w = scale * q + bias,
  * q the unsigned code of the column, scale/bias the bf16 pair of the column's
- * group.  The product of a bf16 scale and a code of at most 8 bits is exact in
- * fp32, so only the addition rounds.
+ * group.  Scales and biases are in the 16-bit activation dtype (bf16, or fp16
+ * for fp16 layers: "SwitchGLU: grouped-expert Metal kernels", "When it
+ * applies", and DS4Server #112, "Current upstream route", both take bf16 or
+ * fp16 activations with scales in the same dtype).  The product of such a scale (at most
+ * 11 significant bits) and a code of at most 8 bits is exact in fp32, so only
+ * the addition rounds.
  */
 void oracle_dequant_row(const oracle_desc *d, const oracle_proj *p, int32_t e,
                         int32_t n, int32_t N, int32_t K, float *out) {
@@ -211,8 +232,8 @@ void oracle_dequant_row(const oracle_desc *d, const oracle_proj *p, int32_t e,
   const uint16_t *bi = p->biases + (int64_t)e * (K / G) * N + n;
   for (int32_t k = 0; k < K; ++k) {
     uint32_t q = (wq[k / per] >> (bits * (k % per))) & mask;
-    float s = oracle_bf16_to_f32(sc[(int64_t)(k / G) * N]);
-    float b = oracle_bf16_to_f32(bi[(int64_t)(k / G) * N]);
+    float s = half_at(d, sc[(int64_t)(k / G) * N]);
+    float b = half_at(d, bi[(int64_t)(k / G) * N]);
     out[k] = s * (float)q + b;
   }
 }
@@ -304,7 +325,7 @@ void oracle_forward_tokens(const oracle_desc *d, int32_t T, const void *x,
                            float *topk_w, int32_t n_threads) {
   (void)T;
   const int32_t D = d->d_model, K = d->top_k, E = d->n_experts;
-  const size_t esz = d->act_bf16 ? 2 : 4;
+  const size_t esz = d->act_bf16 || d->act_f16 ? 2 : 4;
 #ifdef _OPENMP
   if (n_threads > 0) omp_set_num_threads(n_threads);
   g_last_threads = omp_get_max_threads();

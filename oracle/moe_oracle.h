@@ -47,13 +47,16 @@ typedef struct {
   int32_t renormalize;       /* 1: selected weights renormalised to sum to one */
   int32_t w_bits;            /* affine code width: 4 or 8 */
   int32_t activation;        /* 0: SwiGLU (silu(g) * u); 1: GeGLU with tanh-GELU (gelu(g) * u) */
+  int32_t act_f16;           /* 1 (with act_bf16 = 0): x, W_router, dense weights and the
+                                affine scales/biases are fp16 */
 } oracle_desc;
 
 /* One projection for all experts (routed first, then shared).  Dense:
  * w = [n_all][N][K] in the activation dtype.  Affine b-bit (b = 4 or 8):
  * w = uint32 [n_all][N][K*b/32] (32/b codes per word, code m at bits
- * [b*m, b*m+b) holds column (32/b)*word+m), scales/biases = bf16 bits
- * [n_all][K/group][N] (group-major). */
+ * [b*m, b*m+b) holds column (32/b)*word+m), scales/biases = bits of the
+ * 16-bit activation dtype (bf16, or fp16 with act_f16) [n_all][K/group][N]
+ * (group-major). */
 typedef struct {
   const void *w;
   const uint16_t *scales;
@@ -67,6 +70,7 @@ typedef struct {
 /* Conversions (exposed so tests can pin them against a library cast). */
 float oracle_bf16_to_f32(uint16_t h);
 uint16_t oracle_f32_to_bf16(float f);
+float oracle_f16_to_f32(uint16_t h);
 
 /* Router logits [T][E] in the canonical fp32 order. */
 void oracle_router_logits(const oracle_desc *d, int32_t T, const void *x,

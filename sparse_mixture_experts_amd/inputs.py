@@ -1,7 +1,8 @@
 """Seeded synthetic inputs for the sparse MoE layer forward.
 
 This module only draws random numbers and stores them in the layer's input
-formats (fp32, bf16 bits, affine 4-bit codes with bf16 scales/biases).  It
+formats (fp32, bf16 or fp16 bits, affine 4- or 8-bit codes with scales and
+biases in the 16-bit activation dtype).  It
 holds none of the layer's arithmetic; both the GPU tests and the CPU oracle
 consume what it returns.
 
@@ -14,10 +15,12 @@ Recipe (the pages fix the shapes, not the draws):
     router, gate and up; d_ff for down), drawn in stored (out-major) order:
     gate [d_ff][d_model], up [d_ff][d_model], down [d_model][d_ff].
   * x ~ N(0, 1) except for the tiny fp32 layer, where x ~ N(0, 1/d_model).
-  * bf16 storage rounds the fp32 draw to nearest-even (torch's cast).
+  * bf16 storage rounds the fp32 draw to nearest-even (torch's cast); fp16
+    storage likewise (NumPy's cast).
   * b-bit affine storage (b = 4 or 8), per group of g (32, 64 or 128)
     consecutive reduction columns of one row: lo = min, hi = max,
-    scale = bf16((hi - lo) / (2^b - 1)), bias = bf16(lo),
+    scale = half((hi - lo) / (2^b - 1)), bias = half(lo), half = bf16 or fp16
+    (the activation dtype),
     q = clamp(rint((w - bias) / scale), 0, 2^b - 1) (ties to even), q = 0
     where scale == 0.  32/b codes per uint32, code m of a word at bits
     [b*m, b*m + b) holding column (32/b)*word + m.  Codes are stored
@@ -47,7 +50,7 @@ class LayerSpec:
     n_experts: int
     top_k: int
     n_shared: int = 0
-    act: str = "bf16"            # "f32" | "bf16"
+    act: str = "bf16"            # "f32" | "bf16" | "f16"
     wfmt: str = "dense"          # "dense" | "q4" | "q8" (affine 4- or 8-bit codes)
     group_size: int = 64
     gate_up_fused: bool = False
@@ -124,8 +127,27 @@ def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
     return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def quantize_affine(w: np.ndarray, group: int = 64, bits: int = 4):
-    """Encode fp32 rows [N][K] as (uint32 [N][K*bits/32], scales bf16 [N][K/g], biases bf16 [N][K/g])."""
+def to_f16_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 -> IEEE fp16 bit patterns (uint16), round to nearest even, via NumPy."""
+    return np.asarray(a, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    return np.asarray(h, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def to_half_bits(a: np.ndarray, half: str) -> np.ndarray:
+    """fp32 -> bits of the 16-bit dtype `half` ("bf16" or "f16")."""
+    return to_f16_bits(a) if half == "f16" else to_bf16_bits(a)
+
+
+def half_bits_to_f32(h: np.ndarray, half: str) -> np.ndarray:
+    return f16_bits_to_f32(h) if half == "f16" else bf16_bits_to_f32(h)
+
+
+def quantize_affine(w: np.ndarray, group: int = 64, bits: int = 4, half: str = "bf16"):
+    """Encode fp32 rows [N][K] as (uint32 [N][K*bits/32], scales [N][K/g], biases [N][K/g]); scales and
+    biases are bits of the 16-bit dtype `half` ("bf16" or "f16")."""
     N, K = w.shape
     per = 32 // bits
     top = float((1 << bits) - 1)
@@ -133,10 +155,10 @@ def quantize_affine(w: np.ndarray, group: int = 64, bits: int = 4):
     wg = w.reshape(N, K // group, group).astype(np.float32)
     lo = wg.min(axis=-1)
     hi = wg.max(axis=-1)
-    s_bits = to_bf16_bits((hi - lo) / np.float32(top))
-    b_bits = to_bf16_bits(lo)
-    s = bf16_bits_to_f32(s_bits)[..., None]
-    b = bf16_bits_to_f32(b_bits)[..., None]
+    s_bits = to_half_bits((hi - lo) / np.float32(top), half)
+    b_bits = to_half_bits(lo, half)
+    s = half_bits_to_f32(s_bits, half)[..., None]
+    b = half_bits_to_f32(b_bits, half)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
         q = np.rint((wg - b) / s)
     q = np.where(s == 0, 0.0, np.clip(q, 0, top)).astype(np.uint32).reshape(N, K // per, per)
@@ -155,13 +177,13 @@ def gen_x(spec: LayerSpec, x_index: int = 0, T: int | None = None) -> np.ndarray
     T = spec.T if T is None else T
     std = 1.0 / math.sqrt(spec.d_model) if spec.x_scale == "fan_in" else 1.0
     x = _rng(spec.seed, 0, x_index).standard_normal((T, spec.d_model), dtype=np.float32) * np.float32(std)
-    return x if spec.act == "f32" else to_bf16_bits(x)
+    return x if spec.act == "f32" else to_half_bits(x, spec.act)
 
 
 def gen_router(spec: LayerSpec):
     w = _rng(spec.seed, 1).standard_normal((spec.d_model, spec.n_experts), dtype=np.float32)
     w *= np.float32(1.0 / math.sqrt(spec.d_model))
-    w = w if spec.act == "f32" else to_bf16_bits(w)
+    w = w if spec.act == "f32" else to_half_bits(w, spec.act)
     bias = None
     if spec.router_bias == "zipf":
         bias = (-2.2 * np.log(np.arange(1, spec.n_experts + 1, dtype=np.float64))).astype(np.float32)
@@ -170,9 +192,9 @@ def gen_router(spec: LayerSpec):
 
 def _store(spec: LayerSpec, w: np.ndarray):
     if spec.quantized:
-        q, s, b = quantize_affine(w, spec.group_size, spec.bits)
+        q, s, b = quantize_affine(w, spec.group_size, spec.bits, spec.act)
         return {"w": q, "scales": np.ascontiguousarray(s.T), "biases": np.ascontiguousarray(b.T)}
-    return {"w": w if spec.act == "f32" else to_bf16_bits(w)}
+    return {"w": w if spec.act == "f32" else to_half_bits(w, spec.act)}
 
 
 def gen_expert(spec: LayerSpec, e: int) -> dict:

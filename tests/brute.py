@@ -15,8 +15,19 @@ def bits_to_f64(h: np.ndarray) -> np.ndarray:
     return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def f16_bits_to_f64(h: np.ndarray) -> np.ndarray:
+    return np.asarray(h, np.uint16).view(np.float16).astype(np.float64)
+
+
+def half_to_f64(spec: LayerSpec, h: np.ndarray) -> np.ndarray:
+    """Bits of the layer's 16-bit dtype (bf16, or fp16 for fp16 layers) as float64."""
+    return f16_bits_to_f64(h) if spec.act == "f16" else bits_to_f64(h)
+
+
 def widen(spec: LayerSpec, a: np.ndarray) -> np.ndarray:
-    return bits_to_f64(a) if spec.act == "bf16" else np.asarray(a, np.float32).astype(np.float64)
+    if spec.act == "f32":
+        return np.asarray(a, np.float32).astype(np.float64)
+    return half_to_f64(spec, a)
 
 
 def unpack_codes(words: np.ndarray, bits: int = 4) -> np.ndarray:
@@ -33,8 +44,8 @@ def dequant64(spec: LayerSpec, proj: dict) -> np.ndarray:
     q = unpack_codes(proj["w"], spec.bits).astype(np.float64)
     g = spec.group_size
     # scales/biases are stored group-major [..., K/g, N]
-    s = np.repeat(np.swapaxes(bits_to_f64(proj["scales"]), -1, -2), g, axis=-1)
-    b = np.repeat(np.swapaxes(bits_to_f64(proj["biases"]), -1, -2), g, axis=-1)
+    s = np.repeat(np.swapaxes(half_to_f64(spec, proj["scales"]), -1, -2), g, axis=-1)
+    b = np.repeat(np.swapaxes(half_to_f64(spec, proj["biases"]), -1, -2), g, axis=-1)
     return s * q + b
 
 

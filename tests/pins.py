@@ -5,6 +5,7 @@ oracle argument: they call the ``oracle`` package, whose library the mutant
 tests swap for builds with planted mistakes.  What pins what:
 
 * bf16 narrowing       -- torch's bf16 cast (a library routine), incl. ties/inf/NaN.
+* fp16 widening        -- NumPy's fp16 cast on all 65536 bit patterns.
 * router logits        -- NumPy fp64 ``x @ W`` within the closed-form error bound of
                           the chunked fp32 order; one-hot x gives W[i][e] exactly.
 * top-k selection      -- NumPy stable argsort of the same fp32 logits; fp64
@@ -40,7 +41,8 @@ U = 2.0 ** -24  # unit roundoff of fp32
 def desc_of(spec: LayerSpec) -> oracle.Desc:
     return oracle.Desc(spec.d_model, spec.d_ff, spec.n_experts, spec.top_k, spec.n_shared,
                        spec.act == "bf16", spec.quantized, spec.group_size, spec.gate_up_fused,
-                       spec.swiglu_round_bf16, spec.renormalize, spec.bits, int(spec.activation == "geglu"))
+                       spec.swiglu_round_bf16, spec.renormalize, spec.bits, int(spec.activation == "geglu"),
+                       spec.act == "f16")
 
 
 # Small layers spanning every format and flag; d_model 192 and 100 exercise
@@ -66,6 +68,11 @@ SMALL = {
                                            seed=20),
     "bf16-geglu": LayerSpec("bf16-geglu", T=7, d_model=128, d_ff=64, n_experts=5, top_k=2,
                             activation="geglu", seed=21),
+    "f16": LayerSpec("f16", T=7, d_model=128, d_ff=96, n_experts=5, top_k=2, act="f16", seed=23),
+    "f16-q4-shared": LayerSpec("f16-q4-shared", T=6, d_model=128, d_ff=64, n_experts=6, top_k=2, n_shared=1,
+                               act="f16", wfmt="q4", router_bias="zipf", seed=24),
+    "f16-q8-g32-fused": LayerSpec("f16-q8-g32-fused", T=6, d_model=128, d_ff=64, n_experts=4, top_k=2,
+                                  act="f16", wfmt="q8", group_size=32, gate_up_fused=True, seed=25),
 }
 
 _cache: dict = {}
@@ -111,8 +118,8 @@ def pin_router_logits(name: str):
     i = spec.d_model // 3
     xo = np.zeros((1, spec.d_model), np.float32)
     xo[0, i] = 1.0
-    if spec.act == "bf16":
-        xo = inputs.to_bf16_bits(xo)
+    if spec.act != "f32":
+        xo = inputs.to_half_bits(xo, spec.act)
     lo = oracle.router_logits(desc_of(spec), xo, L["w_router"], None)
     assert np.array_equal(lo[0].astype(np.float64), w64[i]), "one-hot logit is not the router row"
 
@@ -227,8 +234,8 @@ def pin_dequant(name: str = "q4"):
     raw = inputs._rng(spec.seed, 2, 3).standard_normal((N, K), dtype=np.float32) / np.float32(math.sqrt(K))
     codes = brute.unpack_codes(proj["w"][3], spec.bits)
     assert codes.max() == top and codes.min() == 0
-    s = brute.bits_to_f64(proj["scales"][3]).T  # stored [K/g][N]
-    b = brute.bits_to_f64(proj["biases"][3]).T
+    s = brute.half_to_f64(spec, proj["scales"][3]).T  # stored [K/g][N]
+    b = brute.half_to_f64(spec, proj["biases"][3]).T
     for n in (0, 1, N // 2, N - 1):
         row = oracle.dequant_row(d, proj, 3, n, NS, K)
         sg, bg = np.repeat(s[n], g), np.repeat(b[n], g)
@@ -279,6 +286,17 @@ def _swiglu_per_op(g, u):
 
 def _geglu_per_op(g, u):
     return brute.bf16_round64(brute.bf16_round64(brute.gelu_tanh64(g)) * u)
+
+
+def pin_f16_decode():
+    """fp16 -> fp32 against NumPy's cast, every one of the 65536 bit patterns
+    (normals, subnormals, both zeros, infinities; NaNs stay NaN)."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    ref = bits.astype(np.uint16).view(np.float16).astype(np.float32)
+    got = np.array([oracle.f16_to_f32(int(b)) for b in bits], np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
 
 
 def pin_gelu_special_values():
@@ -367,7 +385,9 @@ ALL_PINS = [
     ("ties", pin_ties, ()),
     *[(f"weights[{n}]", pin_weights, (n,)) for n in SMALL],
     ("dispatch", pin_dispatch, ()),
-    *[(f"dequant[{n}]", pin_dequant, (n,)) for n in ("q4", "q8", "q4-g32-geglu", "q8-g128-fused-round-geglu")],
+    *[(f"dequant[{n}]", pin_dequant, (n,)) for n in ("q4", "q8", "q4-g32-geglu", "q8-g128-fused-round-geglu",
+                                                     "f16-q4-shared", "f16-q8-g32-fused")],
+    ("f16_decode", pin_f16_decode, ()),
     ("gelu_special_values", pin_gelu_special_values, ()),
     *[(f"expert[{n}]", pin_expert, (n,)) for n in SMALL],
     *[(f"layer[{n}]", pin_layer, (n,)) for n in SMALL],

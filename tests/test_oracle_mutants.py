@@ -28,7 +28,11 @@ MUTANTS = {
     "geglu_runs_silu": ("if (d->activation == 1) {", "if (0) {"),
     "geglu_rounding_skipped": ("h[n] = round_bf16(round_bf16(gelu_tanh(g)) * u);", "h[n] = gelu_tanh(g) * u;"),
     "scale_bias_swapped": ("out[k] = s * (float)q + b;", "out[k] = b * (float)q + s;"),
-    "group_index_wrong": ("float s = oracle_bf16_to_f32(sc[(int64_t)(k / G) * N]);", "float s = oracle_bf16_to_f32(sc[0]);"),
+    "group_index_wrong": ("float s = half_at(d, sc[(int64_t)(k / G) * N]);", "float s = half_at(d, sc[0]);"),
+    "f16_exponent_bias": ("(int)e - 25", "(int)e - 24"),
+    "f16_subnormal_scale": ("ldexpf((float)m, -24)", "ldexpf((float)m, -25)"),
+    "f16_scales_read_as_bf16": ("return d->act_f16 ? oracle_f16_to_f32(h) : oracle_bf16_to_f32(h);",
+                                "return d->act_f16 && 0 ? oracle_f16_to_f32(h) : oracle_bf16_to_f32(h);"),
     "fused_up_reads_gate": ("oracle_dequant_row(d, &w->gate_up, e, F + n, 2 * F, D, row);",
                             "oracle_dequant_row(d, &w->gate_up, e, n, 2 * F, D, row);"),
     "separate_gate_reads_up": ("oracle_dequant_row(d, &w->gate, e, n, F, D, row);",
