@@ -85,7 +85,7 @@ def expert_bytes(spec) -> int:
     n = 3 * spec.d_model * spec.d_ff
     if spec.quantized:
         return n * spec.bits // 8 + (n // spec.group_size) * 4
-    return n * (2 if spec.act == "bf16" else 4)
+    return n * (4 if spec.act == "f32" else 2)
 
 
 def accounting(spec, touched: int):
@@ -96,7 +96,7 @@ def accounting(spec, touched: int):
     intermediate h, the f32 expert outputs and the small index tables.
     """
     T, D, F, E, K, S = spec.T, spec.d_model, spec.d_ff, spec.n_experts, spec.top_k, spec.n_shared
-    esz = 2 if spec.act == "bf16" else 4
+    esz = 4 if spec.act == "f32" else 2
     N, R = T * K, T * K + S * T
     eb = expert_bytes(spec)
     gu_frac, down_frac = 2 / 3, 1 / 3
@@ -152,8 +152,9 @@ def run_config(name, steps, warmup, use_graph, hip):
     n_x = 8
     xs = [moe.to_device(inputs.gen_x(spec, i), dev) for i in range(n_x)]
     T = spec.T
-    out_dt = moe.MOE_DT_BF16 if spec.act == "bf16" else moe.MOE_DT_F32
-    y = torch.empty((T, spec.d_model), device=dev, dtype=torch.bfloat16 if out_dt == moe.MOE_DT_BF16 else torch.float32)
+    out_dt = {"bf16": moe.MOE_DT_BF16, "f16": moe.MOE_DT_F16}.get(spec.act, moe.MOE_DT_F32)
+    y = torch.empty((T, spec.d_model), device=dev,
+                    dtype={moe.MOE_DT_BF16: torch.bfloat16, moe.MOE_DT_F16: torch.float16}.get(out_dt, torch.float32))
     ws = torch.empty(moe.moe_workspace_size(desc, T), dtype=torch.uint8, device=dev)
     idx = torch.empty((T, spec.top_k), dtype=torch.int32, device=dev)
     wt = torch.empty((T, spec.top_k), dtype=torch.float32, device=dev)
@@ -238,14 +239,14 @@ def run_config(name, steps, warmup, use_graph, hip):
 def path_dtype(spec) -> str:
     """Arithmetic type of the expert contractions (they dominate the step).
 
-    4-bit weights are expanded to fp16 and the bf16 activations are staged as
-    fp16 scaled by powers of two, so those products run on fp16 matrix cores;
-    dense bf16 layers use bf16 matrix cores; f32 layers use fp32 FMA.  All of
-    them accumulate in fp32.
+    Affine weights are expanded to fp16 and the 16-bit activations are staged
+    as fp16 scaled by powers of two, so those products run on fp16 matrix
+    cores; dense bf16 / fp16 layers use bf16 / fp16 matrix cores; f32 layers
+    use fp32 FMA.  All of them accumulate in fp32.
     """
-    if spec.act != "bf16":
+    if spec.act == "f32":
         return "f32"
-    return "fp16" if spec.quantized else "bf16"
+    return "fp16" if spec.quantized else ("fp16" if spec.act == "f16" else "bf16")
 
 
 STAGE_SOURCES = {

@@ -54,7 +54,7 @@ typedef enum {
   MOE_E_HIP = -4          /* the HIP runtime reported a launch error */
 } moe_status;
 
-typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
+typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_F16 = 2 } moe_dtype;
 typedef enum { MOE_WF_DENSE = 0, MOE_WF_AFFINE_Q4 = 1, MOE_WF_AFFINE_Q8 = 2 } moe_wformat;
 typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GEGLU = 1 } moe_activation;
 
@@ -67,11 +67,14 @@ typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GEGLU = 1 } moe_activation;
  *  top_k          1..min(32, n_experts).
  *  n_shared       always-on shared experts (weight 1.0, not renormalised), 0..8;
  *                 their weights follow the E routed experts in every projection.
- *  act_dtype      moe_dtype of x, W_router and dense expert weights.
+ *  act_dtype      moe_dtype of x, W_router and dense expert weights (fp32,
+ *                 bf16 or fp16: "SwitchGLU: grouped-expert Metal kernels",
+ *                 "When it applies"; DS4Server #112, "Current upstream route").
  *  w_format       moe_wformat of the expert weights.  The affine formats
  *                 (4- or 8-bit codes: "perf(moe): fused MoE expert decode
  *                 kernel", "Multi-bit handling"; DS4Server #112, "Native
- *                 implementation scope") need act_dtype == MOE_DT_BF16.
+ *                 implementation scope") need a 16-bit act_dtype (bf16 or
+ *                 fp16); their scales and biases are in that dtype.
  *  group_size     affine group length along the reduction dim: 32, 64 or 128.
  *  gate_up_fused  1: one [2*d_ff][d_model] matrix per expert whose rows are
  *                 [gate | up]; 0: separate gate and up matrices.
@@ -101,9 +104,9 @@ typedef struct {
  *  affine b-bit (b = 4 for Q4, 8 for Q8), group g:
  *         w = uint32 [E+S][N][K*b/32], column k of row n is bits
  *         [b*(k%(32/b)), +b) of word k/(32/b) (an unsigned code q in
- *         0..2^b-1); scales, biases = bf16 [E+S][K/g][N] (group-major: one
+ *         0..2^b-1); scales, biases = act_dtype (bf16 or fp16) [E+S][K/g][N] (group-major: one
  *         group's values for consecutive rows are contiguous); the weight is
- *         scale*q + bias of its group ("affine" quantisation with bf16 scales
+ *         scale*q + bias of its group ("affine" quantisation with 16-bit scales
  *         and biases: "SwitchGLU: grouped-expert Metal kernels"
  *         (ml-explore/mlx-lm #2044), "When it applies").
  * gate, up: N = d_ff, K = d_model; gate_up: N = 2*d_ff, K = d_model;
@@ -179,7 +182,7 @@ int moe_expert_ffn(const moe_layer_desc *desc, int32_t T, const void *x,
  *   y[t][:] = sum_{j<k} topk_w[t][j] * y_sorted[inv_order[t*k+j]][:]
  *             + sum_{s<n_shared} y_sorted[N + s*T + t][:],
  * accumulated in fp32 in that order, then stored as out_dtype (moe_dtype;
- * bf16 rounds to nearest even once).
+ * bf16 and fp16 round to nearest even once).
  */
 int moe_combine(const moe_layer_desc *desc, int32_t T, const float *y_sorted,
                 const int32_t *inv_order, const float *topk_w, void *y,

@@ -5,6 +5,8 @@
 // does") gathered through inv_order as in DS4Server #112's _scatter_unsort.
 // A gather per token instead of the PRD's atomic scatter-add keeps the fp32
 // summation order fixed (slot order), so results are deterministic.
+#include <type_traits>
+
 #include "device_common.h"
 #include "moe_internal.h"
 
@@ -51,7 +53,7 @@ __device__ __forceinline__ void widen8(const Row8<YS_BF16> &r, float v[8]) {
 // token's slot positions and weights are uniform (scalar loads); then all
 // slot rows of a thread (up to 16 bf16 or 8 fp32 rows per round) are in
 // flight together before they are summed in slot order.
-template <bool YS_BF16, bool OUT_BF16>
+template <bool YS_BF16, int OUT_DT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const void *__restrict__ ys,
                                                            const int32_t *__restrict__ inv,
                                                            const float *__restrict__ w, int T, int K, int S,
@@ -89,12 +91,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void *__restric
 #pragma unroll
     for (int i = 0; i < kCols; ++i) acc[i] += v[i];
   }
-  if constexpr (OUT_BF16) {
+  if constexpr (OUT_DT != kDtF32) {
     uint4 o;
-    o.x = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
-    o.y = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
-    o.z = f32_to_bf16_bits(acc[4]) | (f32_to_bf16_bits(acc[5]) << 16);
-    o.w = f32_to_bf16_bits(acc[6]) | (f32_to_bf16_bits(acc[7]) << 16);
+    o.x = f32_to_half_bits<OUT_DT>(acc[0]) | (f32_to_half_bits<OUT_DT>(acc[1]) << 16);
+    o.y = f32_to_half_bits<OUT_DT>(acc[2]) | (f32_to_half_bits<OUT_DT>(acc[3]) << 16);
+    o.z = f32_to_half_bits<OUT_DT>(acc[4]) | (f32_to_half_bits<OUT_DT>(acc[5]) << 16);
+    o.w = f32_to_half_bits<OUT_DT>(acc[6]) | (f32_to_half_bits<OUT_DT>(acc[7]) << 16);
     *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(y) + int64_t(t) * D + c) = o;
   } else {
     float4 *q = reinterpret_cast<float4 *>(static_cast<float *>(y) + int64_t(t) * D + c);
@@ -111,13 +113,18 @@ void launch_combine(const moe_layer_desc *d, int32_t T, const void *y_sorted, bo
   const int N = T * d->top_k, D = d->d_model;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(T, (D + kThreads * kCols - 1) / (kThreads * kCols));
-  const bool ob = out_dtype == MOE_DT_BF16;
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, y_sorted, inv_order, topk_w, T, d->top_k, d->n_shared,
                        N, D, y);
   };
-  if (ys_bf16) ob ? go(combine_kernel<true, true>) : go(combine_kernel<true, false>);
-  else ob ? go(combine_kernel<false, true>) : go(combine_kernel<false, false>);
+  auto by_out = [&](auto ys_tag) {
+    constexpr bool YS = decltype(ys_tag)::value;
+    if (out_dtype == MOE_DT_BF16) go(combine_kernel<YS, kDtBF16>);
+    else if (out_dtype == MOE_DT_F16) go(combine_kernel<YS, kDtF16>);
+    else go(combine_kernel<YS, kDtF32>);
+  };
+  if (ys_bf16) by_out(std::true_type{});
+  else by_out(std::false_type{});
   if (mk) mk->mark("combine");
 }
 

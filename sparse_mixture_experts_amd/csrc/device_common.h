@@ -23,11 +23,45 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 }
 __device__ __forceinline__ float round_bf16(float f) { return bf16_bits_to_f32(f32_to_bf16_bits(f)); }
 
-// Activation element i as fp32 (BF16: array of bf16 bits).
-template <bool BF16>
+// Element dtypes as template arguments (the values of moe_dtype).
+constexpr int kDtF32 = 0, kDtBF16 = 1, kDtF16 = 2;
+
+// fp16 bits <-> fp32 (widening exact; narrowing rounds to nearest even).
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return float(__builtin_bit_cast(_Float16, uint16_t(h)));
+}
+__device__ __forceinline__ float f16_lo(uint32_t u) { return f16_bits_to_f32(u & 0xffffu); }
+__device__ __forceinline__ float f16_hi(uint32_t u) { return f16_bits_to_f32(u >> 16); }
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) { return __builtin_bit_cast(uint16_t, _Float16(f)); }
+
+// A 16-bit element (DT = bf16 or fp16) as fp32; the two elements packed in a word.
+template <int DT>
+__device__ __forceinline__ float half_to_f32(uint32_t h) {
+  if constexpr (DT == kDtF16) return f16_bits_to_f32(h);
+  else return bf16_bits_to_f32(h);
+}
+template <int DT>
+__device__ __forceinline__ float half_lo(uint32_t u) {
+  if constexpr (DT == kDtF16) return f16_lo(u);
+  else return bf16_lo(u);
+}
+template <int DT>
+__device__ __forceinline__ float half_hi(uint32_t u) {
+  if constexpr (DT == kDtF16) return f16_hi(u);
+  else return bf16_hi(u);
+}
+// fp32 -> bits of a 16-bit dtype, round to nearest even.
+template <int DT>
+__device__ __forceinline__ uint32_t f32_to_half_bits(float f) {
+  if constexpr (DT == kDtF16) return f32_to_f16_bits(f);
+  else return f32_to_bf16_bits(f);
+}
+
+// Activation element i as fp32 (DT: fp32, or 16-bit bits).
+template <int DT>
 __device__ __forceinline__ float load_act(const void *p, int64_t i) {
-  if constexpr (BF16) return bf16_bits_to_f32(static_cast<const uint16_t *>(p)[i]);
-  else return static_cast<const float *>(p)[i];
+  if constexpr (DT == kDtF32) return static_cast<const float *>(p)[i];
+  else return half_to_f32<DT>(static_cast<const uint16_t *>(p)[i]);
 }
 
 // Wave-wide reductions on DPP lane moves (no LDS round trip): within quads,

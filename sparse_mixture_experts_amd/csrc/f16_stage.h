@@ -1,10 +1,10 @@
 // f16_stage.h -- the fp16 staging format of the 4-bit matrix-core GEMMs.
 //
-// Activations of 4-bit layers are multiplied as fp16.  A row is stored as
+// Activations of affine layers are multiplied as fp16.  A row is stored as
 // fp16 x * 2^-e with one power-of-two exponent e per row (f16_shift), and
 // every 8-element block permuted to e0,e4,e1,e5,e2,e6,e3,e7, the order in
-// which the GEMMs expand a word of eight 4-bit codes.  bf16 -> fp16 is exact
-// for values in fp16's normal range.
+// which the GEMMs expand eight codes.  bf16 -> fp16 is exact for values in
+// fp16's normal range; fp16 rows with no exponent are copied as they are.
 #pragma once
 
 #include "device_common.h"
@@ -35,37 +35,50 @@ __device__ __forceinline__ int f16_shift(float mag) {
 }
 __device__ __forceinline__ float pow2(int e) { return __uint_as_float(uint32_t(127 + e) << 23); }
 
-// Eight bf16 values scaled by 2^-sh as packed fp16 (two per word).
-__device__ __forceinline__ uint4 bf16x8_to_f16(uint4 v, int sh) {
+// Eight 16-bit values (bf16, or fp16 when f16 is set) scaled by 2^-sh as
+// packed fp16 (two per word).
+template <int DT>
+__device__ __forceinline__ uint4 half8_to_f16_t(uint4 v, int sh) {
   const float m = pow2(-sh);
   const uint32_t u[4] = {v.x, v.y, v.z, v.w};
   uint32_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const f16x2_t p = {(_Float16)(bf16_lo(u[i]) * m), (_Float16)(bf16_hi(u[i]) * m)};
+    const f16x2_t p = {(_Float16)(half_lo<DT>(u[i]) * m), (_Float16)(half_hi<DT>(u[i]) * m)};
     o[i] = __builtin_bit_cast(uint32_t, p);
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
-
-__device__ __forceinline__ float absmax8_bf16(uint4 v) {
-  const float a = fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))), fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y))));
-  const float b = fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))), fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w))));
-  return fmaxf(a, b);
+__device__ __forceinline__ uint4 half8_to_f16(uint4 v, int sh, bool f16) {
+  if (!f16) return half8_to_f16_t<kDtBF16>(v, sh);
+  return sh == 0 ? v : half8_to_f16_t<kDtF16>(v, sh);
 }
 
-// One wave converts row x[0..D) (bf16, D a multiple of 8) to out[0..D) in
-// the staging format and writes its exponent to *sh_out (lane 0).
-__device__ __forceinline__ void row_to_f16(const uint16_t *x, int D, uint16_t *out, int8_t *sh_out) {
+template <int DT>
+__device__ __forceinline__ float absmax8_t(uint4 v) {
+  const float a = fmaxf(fmaxf(fabsf(half_lo<DT>(v.x)), fabsf(half_hi<DT>(v.x))),
+                        fmaxf(fabsf(half_lo<DT>(v.y)), fabsf(half_hi<DT>(v.y))));
+  const float b = fmaxf(fmaxf(fabsf(half_lo<DT>(v.z)), fabsf(half_hi<DT>(v.z))),
+                        fmaxf(fabsf(half_lo<DT>(v.w)), fabsf(half_hi<DT>(v.w))));
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float absmax8(uint4 v, bool f16) {
+  return f16 ? absmax8_t<kDtF16>(v) : absmax8_t<kDtBF16>(v);
+}
+
+// One wave converts row x[0..D) (bf16, or fp16 when f16 is set; D a
+// multiple of 8) to out[0..D) in the staging format and writes its exponent
+// to *sh_out (lane 0).
+__device__ __forceinline__ void row_to_f16(const uint16_t *x, int D, uint16_t *out, int8_t *sh_out, bool f16) {
   const int lane = lane_id();
   const uint4 *src = reinterpret_cast<const uint4 *>(x);
   uint4 *dst = reinterpret_cast<uint4 *>(out);
   const int P = D / 8;
   float mx = 0.f;
-  for (int p = lane; p < P; p += kWave) mx = fmaxf(mx, absmax8_bf16(src[p]));
+  for (int p = lane; p < P; p += kWave) mx = fmaxf(mx, absmax8(src[p], f16));
   mx = wave_max(mx);
   const int sh = f16_shift(mx);
-  for (int p = lane; p < P; p += kWave) dst[p] = permute8(bf16x8_to_f16(src[p], sh));
+  for (int p = lane; p < P; p += kWave) dst[p] = permute8(half8_to_f16(src[p], sh, f16));
   if (lane == 0) *sh_out = int8_t(sh);
 }
 
@@ -81,17 +94,18 @@ __device__ __forceinline__ void row_f16_load(const uint16_t *x, int D, RowF16 &r
 #pragma unroll
   for (int q = 0; q < 8; ++q) r.v[q] = reinterpret_cast<const uint4 *>(x)[min(q * kWave + lane, D / 8 - 1)];
 }
-__device__ __forceinline__ void row_f16_store(const RowF16 &r, int D, uint16_t *out, int8_t *sh_out) {
+__device__ __forceinline__ void row_f16_store(const RowF16 &r, int D, uint16_t *out, int8_t *sh_out, bool f16) {
   const int lane = lane_id();
   float mx = 0.f;
 #pragma unroll
   for (int q = 0; q < 8; ++q)
-    if ((q * kWave + lane) * 8 < D) mx = fmaxf(mx, absmax8_bf16(r.v[q]));
+    if ((q * kWave + lane) * 8 < D) mx = fmaxf(mx, absmax8(r.v[q], f16));
   mx = wave_max(mx);
   const int sh = f16_shift(mx);
 #pragma unroll
   for (int q = 0; q < 8; ++q)
-    if ((q * kWave + lane) * 8 < D) reinterpret_cast<uint4 *>(out)[q * kWave + lane] = permute8(bf16x8_to_f16(r.v[q], sh));
+    if ((q * kWave + lane) * 8 < D)
+      reinterpret_cast<uint4 *>(out)[q * kWave + lane] = permute8(half8_to_f16(r.v[q], sh, f16));
   if (lane == 0) *sh_out = int8_t(sh);
 }
 

@@ -1,8 +1,8 @@
 // ffn_gemv.hip -- grouped expert FFN on the vector units, for the layers the
-// matrix-core kernels do not take: fp32 activations, or dense bf16 layers
-// whose d_model or d_ff is not a multiple of 64.  (4-bit layers always have
-// bf16 activations and 64-multiple dims, so they always run on the matrix
-// cores.)
+// matrix-core kernels do not take: fp32 activations, or dense bf16/fp16
+// layers whose d_model or d_ff is not a multiple of 64.  (Affine layers
+// always have 16-bit activations and 64-multiple dims, so they always run on
+// the matrix cores.)
 //
 // "SwitchGLU: grouped-expert Metal kernels" (ml-explore/mlx-lm #2044),
 // section "What": slots are grouped by expert across tokens so each expert's
@@ -23,35 +23,34 @@
 namespace moe {
 namespace {
 
-enum WFmt { W_F32 = 0, W_BF16 = 1 };
 constexpr int kMR = 8;        // rows per pass (register accumulators)
 constexpr int kNB = 16;       // output columns per workgroup (4 per wave)
 constexpr int kThreads = 256;
 
 // Weights k..k+7 of global row `row` (expert-major row index) of a [.][K] matrix.
-template <int WF>
+template <int DT>
 __device__ __forceinline__ void load_w8(const void *__restrict__ w, const uint16_t *__restrict__ sc,
                                         const uint16_t *__restrict__ bi, int64_t row, int K, int k,
                                         float out[8]) {
-  if constexpr (WF == W_F32) {
+  if constexpr (DT == kDtF32) {
     const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(w) + row * K + k);
     const float4 a = p[0], b = p[1];
     out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
     out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
   } else {
     const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(w) + row * K + k);
-    out[0] = bf16_lo(u.x); out[1] = bf16_hi(u.x); out[2] = bf16_lo(u.y); out[3] = bf16_hi(u.y);
-    out[4] = bf16_lo(u.z); out[5] = bf16_hi(u.z); out[6] = bf16_lo(u.w); out[7] = bf16_hi(u.w);
+    out[0] = half_lo<DT>(u.x); out[1] = half_hi<DT>(u.x); out[2] = half_lo<DT>(u.y); out[3] = half_hi<DT>(u.y);
+    out[4] = half_lo<DT>(u.z); out[5] = half_hi<DT>(u.z); out[6] = half_lo<DT>(u.w); out[7] = half_hi<DT>(u.w);
   }
 }
 
-// Eight staged activations (fp32 or bf16 bits in LDS) as fp32.
-template <bool BF16>
+// Eight staged activations (fp32, or 16-bit bits in LDS) as fp32.
+template <int DT>
 __device__ __forceinline__ void lds_x8(const void *xs, int idx, float out[8]) {
-  if constexpr (BF16) {
+  if constexpr (DT != kDtF32) {
     const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(xs) + idx);
-    out[0] = bf16_lo(u.x); out[1] = bf16_hi(u.x); out[2] = bf16_lo(u.y); out[3] = bf16_hi(u.y);
-    out[4] = bf16_lo(u.z); out[5] = bf16_hi(u.z); out[6] = bf16_lo(u.w); out[7] = bf16_hi(u.w);
+    out[0] = half_lo<DT>(u.x); out[1] = half_hi<DT>(u.x); out[2] = half_lo<DT>(u.y); out[3] = half_hi<DT>(u.y);
+    out[4] = half_lo<DT>(u.z); out[5] = half_hi<DT>(u.z); out[6] = half_lo<DT>(u.w); out[7] = half_hi<DT>(u.w);
   } else {
     const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(xs) + idx);
     const float4 a = p[0], b = p[1];
@@ -61,18 +60,19 @@ __device__ __forceinline__ void lds_x8(const void *xs, int idx, float out[8]) {
 }
 
 // Stage `mr` rows of length K into LDS; row m comes from src row src_row(m).
-template <bool BF16, class RowOf>
+template <int DT, class RowOf>
 __device__ __forceinline__ void stage_rows(void *xs, const void *__restrict__ src, int mr, int K,
                                            RowOf src_row) {
-  // 16-byte pieces: 8 bf16 or 4 fp32 elements.
-  constexpr int EPP = BF16 ? 8 : 4;
+  // 16-byte pieces: 8 16-bit or 4 fp32 elements.
+  constexpr int ESZ = DT == kDtF32 ? 4 : 2;  // element bytes
+  constexpr int EPP = 16 / ESZ;
   const int ppr = K / EPP;
   for (int q = threadIdx.x; q < mr * ppr; q += blockDim.x) {
     const int m = q / ppr, c = (q % ppr) * EPP;
     const int64_t r = src_row(m);
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (r >= 0) v = *reinterpret_cast<const uint4 *>(static_cast<const char *>(src) + (r * K + c) * (BF16 ? 2 : 4));
-    *reinterpret_cast<uint4 *>(static_cast<char *>(xs) + (int64_t(m) * K + c) * (BF16 ? 2 : 4)) = v;
+    if (r >= 0) v = *reinterpret_cast<const uint4 *>(static_cast<const char *>(src) + (r * K + c) * ESZ);
+    *reinterpret_cast<uint4 *>(static_cast<char *>(xs) + (int64_t(m) * K + c) * ESZ) = v;
   }
 }
 
@@ -89,7 +89,7 @@ struct GateUpArgs {
   void *h;
 };
 
-template <bool BF16, int WF>
+template <int DT>
 __global__ __launch_bounds__(kThreads) void gateup_gemv_kernel(GateUpArgs a) {
   extern __shared__ uint4 smem_v[];
   void *xs = smem_v;
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void gateup_gemv_kernel(GateUpArgs a) {
   for (int r0 = 0; r0 < it.rows; r0 += a.MR) {
     const int mr = min(a.MR, it.rows - r0);
     __syncthreads();
-    stage_rows<BF16>(xs, a.x, mr, D, [&](int m) -> int64_t {
+    stage_rows<DT>(xs, a.x, mr, D, [&](int m) -> int64_t {
       const int p = it.row0 + r0 + m;
       const int t = p < a.N ? a.row_map[p] : (p - a.N) % a.T;
       return unsigned(t) < unsigned(a.T) ? int64_t(t) : int64_t(-1);
@@ -118,13 +118,13 @@ __global__ __launch_bounds__(kThreads) void gateup_gemv_kernel(GateUpArgs a) {
       for (int m = 0; m < kMR; ++m) ag[m] = au[m] = 0.0f;
       for (int k = lane * 8; k < D; k += 8 * kWave) {
         float wg8[8], wu8[8];
-        load_w8<WF>(a.wg, a.sg, a.bg, rg, D, k, wg8);
-        load_w8<WF>(wu, su, bu, ru, D, k, wu8);
+        load_w8<DT>(a.wg, a.sg, a.bg, rg, D, k, wg8);
+        load_w8<DT>(wu, su, bu, ru, D, k, wu8);
 #pragma unroll
         for (int m = 0; m < kMR; ++m) {
           if (m < mr) {
             float xv[8];
-            lds_x8<BF16>(xs, m * D + k, xv);
+            lds_x8<DT>(xs, m * D + k, xv);
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
               ag[m] += xv[u] * wg8[u];
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void gateup_gemv_kernel(GateUpArgs a) {
           if (lane == 0) {
             const float hv = glu(g, u, a.round_ops, a.geglu);
             const int64_t o = int64_t(it.row0 + r0 + m) * F + n;
-            if constexpr (BF16) static_cast<uint16_t *>(a.h)[o] = uint16_t(f32_to_bf16_bits(hv));
+            if constexpr (DT != kDtF32) static_cast<uint16_t *>(a.h)[o] = uint16_t(f32_to_half_bits<DT>(hv));
             else static_cast<float *>(a.h)[o] = hv;
           }
         }
@@ -159,7 +159,7 @@ struct DownArgs {
   float *y;
 };
 
-template <bool BF16, int WF>
+template <int DT>
 __global__ __launch_bounds__(kThreads) void down_gemv_kernel(DownArgs a) {
   extern __shared__ uint4 smem_v[];
   void *hs = smem_v;
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void down_gemv_kernel(DownArgs a) {
   for (int r0 = 0; r0 < it.rows; r0 += a.MR) {
     const int mr = min(a.MR, it.rows - r0);
     __syncthreads();
-    stage_rows<BF16>(hs, a.h, mr, F, [&](int m) -> int64_t { return it.row0 + r0 + m; });
+    stage_rows<DT>(hs, a.h, mr, F, [&](int m) -> int64_t { return it.row0 + r0 + m; });
     __syncthreads();
     for (int nq = 0; nq < kNB / 4; ++nq) {
       const int n = blockIdx.x * kNB + wave * (kNB / 4) + nq;
@@ -181,12 +181,12 @@ __global__ __launch_bounds__(kThreads) void down_gemv_kernel(DownArgs a) {
       for (int m = 0; m < kMR; ++m) acc[m] = 0.0f;
       for (int k = lane * 8; k < F; k += 8 * kWave) {
         float w8[8];
-        load_w8<WF>(a.wd, a.sd, a.bd, rd, F, k, w8);
+        load_w8<DT>(a.wd, a.sd, a.bd, rd, F, k, w8);
 #pragma unroll
         for (int m = 0; m < kMR; ++m) {
           if (m < mr) {
             float hv[8];
-            lds_x8<BF16>(hs, m * F + k, hv);
+            lds_x8<DT>(hs, m * F + k, hv);
 #pragma unroll
             for (int u = 0; u < 8; ++u) acc[m] += hv[u] * w8[u];
           }
@@ -205,13 +205,13 @@ __global__ __launch_bounds__(kThreads) void down_gemv_kernel(DownArgs a) {
 
 int rows_per_pass(int K, int esz) { return max(1, min(kMR, 65536 / (K * esz))); }
 
-template <bool BF16, int WF>
+template <int DT>
 void launch_gemv(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
                  const moe_weights *w, const int32_t *counters, const PlanItem *items, void *h,
                  float *y, hipStream_t s, StageMarker *mk) {
   const int D = d->d_model, F = d->d_ff, E = d->n_experts, S = d->n_shared;
   const int N = T * d->top_k;
-  const int esz = BF16 ? 2 : 4;
+  const int esz = DT == kDtF32 ? 4 : 2;
   const int max_items = min(E, N) + S;
   const moe_proj &pg = d->gate_up_fused ? w->gate_up : w->gate;
   GateUpArgs ga{x, row_map, T, N, D, F, E, d->gate_up_fused, d->swiglu_round_bf16,
@@ -219,12 +219,12 @@ void launch_gemv(const moe_layer_desc *d, int32_t T, const void *x, const int32_
                 static_cast<const uint16_t *>(pg.biases), w->up.w,
                 static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases),
                 counters, items, h};
-  hipLaunchKernelGGL((gateup_gemv_kernel<BF16, WF>), dim3((F + kNB - 1) / kNB, max_items),
+  hipLaunchKernelGGL((gateup_gemv_kernel<DT>), dim3((F + kNB - 1) / kNB, max_items),
                      dim3(kThreads), size_t(ga.MR) * D * esz, s, ga);
   if (mk) mk->mark("gateup_gemv");
   DownArgs da{h, D, F, rows_per_pass(F, esz), w->down.w, static_cast<const uint16_t *>(w->down.scales),
               static_cast<const uint16_t *>(w->down.biases), counters, items, y};
-  hipLaunchKernelGGL((down_gemv_kernel<BF16, WF>), dim3((D + kNB - 1) / kNB, max_items),
+  hipLaunchKernelGGL((down_gemv_kernel<DT>), dim3((D + kNB - 1) / kNB, max_items),
                      dim3(kThreads), size_t(da.MR) * F * esz, s, da);
   if (mk) mk->mark("down_gemv");
 }
@@ -245,9 +245,11 @@ void launch_expert_ffn(const moe_layer_desc *d, int32_t T, const void *x, const 
   void *h = sc.h;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d->act_dtype == MOE_DT_BF16)
-    launch_gemv<true, W_BF16>(d, T, x, row_map, w, counters, act_items, h, y_sorted, s, mk);
+    launch_gemv<kDtBF16>(d, T, x, row_map, w, counters, act_items, h, y_sorted, s, mk);
+  else if (d->act_dtype == MOE_DT_F16)
+    launch_gemv<kDtF16>(d, T, x, row_map, w, counters, act_items, h, y_sorted, s, mk);
   else
-    launch_gemv<false, W_F32>(d, T, x, row_map, w, counters, act_items, h, y_sorted, s, mk);
+    launch_gemv<kDtF32>(d, T, x, row_map, w, counters, act_items, h, y_sorted, s, mk);
 }
 
 }  // namespace moe

@@ -112,12 +112,13 @@ __device__ __forceinline__ f16x8 q8_words_to_f16(uint32_t w0, uint32_t w1, h2 s2
   return __builtin_bit_cast(f16x8, r);
 }
 
-// x [T][D] bf16 -> fp16 staging copy (row_to_f16), one wave per token.
+// x [T][D] (bf16, or fp16 when x_f16) -> fp16 staging copy (row_to_f16), one
+// wave per token.
 __global__ __launch_bounds__(256) void act_f16_kernel(const uint16_t *x, int T, int D, uint16_t *x16,
-                                                      int8_t *xsh) {
+                                                      int8_t *xsh, int x_f16) {
   const int t = blockIdx.x * (256 / kWave) + int(threadIdx.x) / kWave;
   if (t >= T) return;  // whole waves
-  row_to_f16(x + int64_t(t) * D, D, x16 + int64_t(t) * D, xsh + t);
+  row_to_f16(x + int64_t(t) * D, D, x16 + int64_t(t) * D, xsh + t, x_f16 != 0);
 }
 
 struct GemmArgs {
@@ -131,6 +132,7 @@ struct GemmArgs {
   int fused;                // gate/up: [gate | up] in one matrix
   int round_ops;            // per-op bf16 GLU
   int geglu;                // gate/up: tanh-GELU gate (else SiLU)
+  int half_f16;             // affine scales/biases are fp16 (else bf16)
   const void *w0;           // gate (or gate_up) / down weights
   const uint16_t *s0, *b0;
   const void *w1;           // up weights (separate layout)
@@ -150,14 +152,20 @@ struct Slab {
   int8_t wsh[kNRows];             // affine: weight row exponents
 };
 
+// Weight formats of the grouped GEMM: QB = 4 or 8 (affine codes, fp16
+// MFMA), kDenseBF16 or kDenseF16 (16-bit weights fed to the MFMA as stored).
+constexpr int kDenseBF16 = 0, kDenseF16 = 16;
+constexpr bool is_affine(int qb) { return qb == 4 || qb == 8; }
+
 // Per-lane weight data of one slab (32 reduction elements per tile): 4-bit
-// -> one uint4 (4 words) per tile; 8-bit -> two; dense bf16 -> four.
+// -> one uint4 (4 words) per tile; 8-bit -> two; 16-bit dense -> four.
 template <int QB>
-struct WSlab { uint4 w[kNT][QB == 0 ? kSteps : QB / 4]; };
+struct WSlab { uint4 w[kNT][is_affine(QB) ? QB / 4 : kSteps]; };
 
 // GATEUP: gate/up projection with the GLU epilogue writing h, else down
-// projection writing y rows.  QB: affine code width 4 or 8 (fp16 MFMA), or 0
-// for dense bf16 weights (bf16 MFMA).  RB: 16-row blocks per tile.  GPS:
+// projection writing y rows.  QB: affine code width 4 or 8 (fp16 MFMA), or
+// kDenseBF16 / kDenseF16 for 16-bit dense weights (bf16 / fp16 MFMA; h is
+// written in that dtype).  RB: 16-row blocks per tile.  GPS:
 // affine groups per 128-element slab (4, 2, 1 for groups of 32, 64, 128).  Each wave owns
 // kNT weight tiles of 16 rows; for gate/up the first kNT/2 are gate rows and
 // the last kNT/2 the up rows of the same output columns.
@@ -171,7 +179,7 @@ struct WSlab { uint4 w[kNT][QB == 0 ? kSteps : QB / 4]; };
 // group: group 32*lg / (128 / GPS) of the slab.
 template <bool GATEUP, int QB, int RB, int GPS>
 __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
-  constexpr bool AFF = QB != 0;                    // affine codes (fp16 path)
+  constexpr bool AFF = is_affine(QB);              // affine codes (fp16 path)
   constexpr int kLPG = 4 / GPS;                   // lanes lg per group
   constexpr float kQMax = QB == 8 ? 255.0f : 15.0f;
   constexpr int NTH = GATEUP ? kNT / 2 : kNT;   // output-column tiles per wave
@@ -206,7 +214,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
   const int lr = lane & 15, lg = lane >> 4;  // operand row / reduction quarter of this lane
-  const int K = a.K, KW = QB == 0 ? 0 : K * QB / 32, G = K / (kKS / GPS);
+  const int K = a.K, KW = AFF ? K * QB / 32 : 0, G = K / (kKS / GPS);
   const int nslab = (K + kKS - 1) / kKS;
   const int col0 = (bx * kNW + wave) * NTH * 16;  // first output column of this wave
   const bool col_ok = col0 < a.n_out;              // whole wave in or out (n_out % 64 == 0)
@@ -344,8 +352,8 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
       float sv[GPS], bv[GPS], wm = 0.f;
 #pragma unroll
       for (int g = 0; g < GPS; ++g) {
-        sv[g] = bf16_bits_to_f32(sraw[g][0]);
-        bv[g] = bf16_bits_to_f32(sraw[g][1]);
+        sv[g] = a.half_f16 ? f16_bits_to_f32(sraw[g][0]) : bf16_bits_to_f32(sraw[g][0]);
+        bv[g] = a.half_f16 ? f16_bits_to_f32(sraw[g][1]) : bf16_bits_to_f32(sraw[g][1]);
         wm = fmaxf(wm, __builtin_fmaf(kQMax, fabsf(sv[g]), fabsf(bv[g])));
       }
       const int wsh = f16_shift(wm);
@@ -431,15 +439,21 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
     } else {
 #pragma unroll
       for (int j = 0; j < kSteps; ++j) {
-        bf16x8 bx[NRB];
+        uint4 bx[NRB];
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
-          bx[rb] = *reinterpret_cast<const bf16x8 *>(&S.a[rb * 16 + lr][lg * 32 + j * 8]);
+          bx[rb] = *reinterpret_cast<const uint4 *>(&S.a[rb * 16 + lr][lg * 32 + j * 8]);
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
-          const bf16x8 aw = __builtin_bit_cast(bf16x8, ws.w[nt][j]);
 #pragma unroll
-          for (int rb = 0; rb < NRB; ++rb) acc[nt][rb] = mfma_bf16(aw, bx[rb], acc[nt][rb]);
+          for (int rb = 0; rb < NRB; ++rb) {
+            if constexpr (QB == kDenseF16)
+              acc[nt][rb] = mfma_f16(__builtin_bit_cast(f16x8, ws.w[nt][j]), __builtin_bit_cast(f16x8, bx[rb]),
+                                     acc[nt][rb]);
+            else
+              acc[nt][rb] = mfma_bf16(__builtin_bit_cast(bf16x8, ws.w[nt][j]), __builtin_bit_cast(bf16x8, bx[rb]),
+                                      acc[nt][rb]);
+          }
         }
       }
     }
@@ -590,8 +604,10 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
       if constexpr (GATEUP) {
         uint32_t hb[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          hb[i] = f32_to_bf16_bits(glu(acc[nt][rb][i], acc[nt + NTH][rb][i], a.round_ops, a.geglu));
+        for (int i = 0; i < 4; ++i) {
+          const float v = glu(acc[nt][rb][i], acc[nt + NTH][rb][i], a.round_ops, a.geglu);
+          hb[i] = QB == kDenseF16 ? f32_to_f16_bits(v) : f32_to_bf16_bits(v);
+        }
         const uint2 o = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
         *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + row * a.n_out + c) = o;
       } else if (a.out_bf16) {
@@ -638,6 +654,7 @@ struct DecArgs {
   const int8_t *act_sh;     // gate/up: token exponents [T]
   const int32_t *row_map;   // gate/up only
   int T, N, K, n_out, fused, round_ops, geglu, gsize;
+  int half_f16;             // scales/biases are fp16 (else bf16)
   const uint32_t *w0;       // gate (or gate_up) / down codes
   const uint16_t *s0, *b0;
   const uint32_t *w1;       // up codes (separate layout)
@@ -743,7 +760,7 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int q = q0 + tid + i * kThreads;
-        if (q < nrow * P) atomicMax(&rmax_bits[q / P], __float_as_uint(absmax8_bf16(hv[i])));
+        if (q < nrow * P) atomicMax(&rmax_bits[q / P], __float_as_uint(absmax8(hv[i], false)));
       }
     }
     __syncthreads();
@@ -751,15 +768,19 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecArgs a) {
       const int m = q / P, pc = q % P;
       const int p = tile.row0 + m;
       const uint4 v = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.act) + int64_t(p) * K)[pc];
-      *reinterpret_cast<uint4 *>(&xs[m * XR + pc * 8]) = permute8(bf16x8_to_f16(v, f16_shift(__uint_as_float(rmax_bits[m]))));
+      *reinterpret_cast<uint4 *>(&xs[m * XR + pc * 8]) =
+          permute8(half8_to_f16(v, f16_shift(__uint_as_float(rmax_bits[m])), false));
     }
   }
 
   // ---- weight row exponent over the whole K, fp16 scales ----
-  float wm = 0.f;
+  float sf[kMaxSlabs], bf[kMaxSlabs], wm = 0.f;
 #pragma unroll
-  for (int s = 0; s < kMaxSlabs; ++s)
-    wm = fmaxf(wm, __builtin_fmaf(kQMax, fabsf(bf16_bits_to_f32(sr[s])), fabsf(bf16_bits_to_f32(br[s]))));
+  for (int s = 0; s < kMaxSlabs; ++s) {
+    sf[s] = a.half_f16 ? f16_bits_to_f32(sr[s]) : bf16_bits_to_f32(sr[s]);
+    bf[s] = a.half_f16 ? f16_bits_to_f32(br[s]) : bf16_bits_to_f32(br[s]);
+    wm = fmaxf(wm, __builtin_fmaf(kQMax, fabsf(sf[s]), fabsf(bf[s])));
+  }
   wm = fmaxf(wm, __shfl_xor(wm, 16, kWave));
   wm = fmaxf(wm, __shfl_xor(wm, 32, kWave));
   const int wsh = f16_shift(wm);  // exponent of weight row lr
@@ -773,7 +794,7 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecArgs a) {
 #pragma unroll
   for (int s = 0; s < kMaxSlabs; ++s) {
     if (s < nslab) {
-      const _Float16 s16 = (_Float16)(bf16_bits_to_f32(sr[s]) * wmul), b16 = (_Float16)(bf16_bits_to_f32(br[s]) * wmul);
+      const _Float16 s16 = (_Float16)(sf[s] * wmul), b16 = (_Float16)(bf[s] * wmul);
       const h2 s2 = {s16, s16}, b2 = {b16, b16};
       const h2 s2_16 = s2 * sixteenth;
 #pragma unroll
@@ -854,7 +875,8 @@ template <bool GATEUP, int RB>
 void launch_gemm(const GemmArgs &ga, int qb, int gsize, int64_t max_tiles, hipStream_t s) {
   if (qb == 4) launch_groups<GATEUP, RB, 4>(ga, gsize, max_tiles, s);
   else if (qb == 8) launch_groups<GATEUP, RB, 8>(ga, gsize, max_tiles, s);
-  else launch_one<GATEUP, 0, RB, 1>(ga, max_tiles, s);
+  else if (qb == kDenseF16) launch_one<GATEUP, kDenseF16, RB, 1>(ga, max_tiles, s);
+  else launch_one<GATEUP, kDenseBF16, RB, 1>(ga, max_tiles, s);
 }
 
 template <bool GATEUP, int QB, int MS>
@@ -890,9 +912,10 @@ void launch_decode(const DecArgs &da, int qb, int64_t max_tiles, hipStream_t s) 
 }  // namespace
 
 bool use_mfma(const moe_layer_desc *d) {
-  // bf16 activations with every reduction length a whole number of 64-element
-  // groups; fp32 layers and other shapes take the dequant-GEMV kernels.
-  return d->act_dtype == MOE_DT_BF16 && d->d_model % 64 == 0 && d->d_ff % 64 == 0;
+  // 16-bit activations with every reduction length a whole number of
+  // 64-element groups; fp32 layers and other shapes take the dequant-GEMV
+  // kernels.
+  return d->act_dtype != MOE_DT_F32 && d->d_model % 64 == 0 && d->d_ff % 64 == 0;
 }
 
 int plan_tile_rows(const moe_layer_desc *d, int32_t T) {
@@ -908,23 +931,24 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
                             StageMarker *mk) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool aff = affine(d);
-  const int qb = d->w_format == MOE_WF_AFFINE_Q8 ? 8 : aff ? 4 : 0;
+  const bool f16 = d->act_dtype == MOE_DT_F16;
+  const int qb = d->w_format == MOE_WF_AFFINE_Q8 ? 8 : aff ? 4 : f16 ? kDenseF16 : kDenseBF16;
   const int gs = d->group_size;
   const int geglu = d->activation == MOE_ACT_GEGLU;
   const int tr = plan_tile_rows(d, T);
   const int nblk = (d->d_ff + kHBlock - 1) / kHBlock;
   if (aff && !sc.x16_ready) {
     hipLaunchKernelGGL(act_f16_kernel, dim3((T + 3) / 4), dim3(256), 0, s, static_cast<const uint16_t *>(x), T,
-                       d->d_model, static_cast<uint16_t *>(sc.x16), sc.xsh);
+                       d->d_model, static_cast<uint16_t *>(sc.x16), sc.xsh, int(f16));
     if (mk) mk->mark("x_f16");
   }
   const moe_proj &pg = d->gate_up_fused ? w->gate_up : w->gate;
   GemmArgs gu{aff ? sc.x16 : x, sc.xsh, sc.hsh, nblk, row_map, T, T * d->top_k, d->d_model, d->d_ff,
-              d->gate_up_fused, d->swiglu_round_bf16, geglu,
+              d->gate_up_fused, d->swiglu_round_bf16, geglu, int(f16),
               pg.w, static_cast<const uint16_t *>(pg.scales), static_cast<const uint16_t *>(pg.biases),
               w->up.w, static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases),
               counters, tiles, sc.h, 0};
-  GemmArgs dn{sc.h, sc.hsh, nullptr, nblk, nullptr, T, T * d->top_k, d->d_ff, d->d_model, 0, 0, 0,
+  GemmArgs dn{sc.h, sc.hsh, nullptr, nblk, nullptr, T, T * d->top_k, d->d_ff, d->d_model, 0, 0, 0, int(f16),
               w->down.w, static_cast<const uint16_t *>(w->down.scales), static_cast<const uint16_t *>(w->down.biases),
               nullptr, nullptr, nullptr, counters, tiles, y_sorted, ys_bf16};
   if (tr == 16 && aff && int64_t(T) * d->top_k <= d->n_experts && d->d_model <= kDecMaxK &&
@@ -932,11 +956,11 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
     // at most one routed row per expert on average: whole-K loads per wave
     // (one memory round trip), h as bf16 between the two projections
     DecArgs dg{sc.x16, sc.xsh, row_map, T, T * d->top_k, d->d_model, d->d_ff, d->gate_up_fused,
-               d->swiglu_round_bf16, geglu, gs, static_cast<const uint32_t *>(pg.w),
+               d->swiglu_round_bf16, geglu, gs, int(f16), static_cast<const uint32_t *>(pg.w),
                static_cast<const uint16_t *>(pg.scales), static_cast<const uint16_t *>(pg.biases),
                static_cast<const uint32_t *>(w->up.w), static_cast<const uint16_t *>(w->up.scales),
                static_cast<const uint16_t *>(w->up.biases), counters, tiles, sc.h, 0};
-    DecArgs dd{sc.h, nullptr, nullptr, T, T * d->top_k, d->d_ff, d->d_model, 0, 0, 0, gs,
+    DecArgs dd{sc.h, nullptr, nullptr, T, T * d->top_k, d->d_ff, d->d_model, 0, 0, 0, gs, int(f16),
                static_cast<const uint32_t *>(w->down.w), static_cast<const uint16_t *>(w->down.scales),
                static_cast<const uint16_t *>(w->down.biases), nullptr, nullptr, nullptr, counters, tiles, y_sorted,
                ys_bf16};

@@ -114,7 +114,7 @@ int moe_combine(const moe_layer_desc *desc, int32_t T, const float *y_sorted, co
                 const float *topk_w, void *y, int32_t out_dtype, void *stream) {
   int s;
   if ((s = validate_desc(desc)) || (s = validate_T(T))) return s;
-  if (out_dtype != MOE_DT_F32 && out_dtype != MOE_DT_BF16) return MOE_E_INVALID;
+  if (out_dtype != MOE_DT_F32 && out_dtype != MOE_DT_BF16 && out_dtype != MOE_DT_F16) return MOE_E_INVALID;
   if ((s = validate_ptr(y_sorted)) || (s = validate_ptr(inv_order)) || (s = validate_ptr(topk_w)) ||
       (s = validate_ptr(y)))
     return s;
@@ -128,7 +128,7 @@ static int forward_impl(const moe_layer_desc *desc, int32_t T, const void *x, co
                         size_t ws_bytes, void *stream, StageMarker *mk) {
   int s;
   if ((s = validate_desc(desc)) || (s = validate_T(T))) return s;
-  if (out_dtype != MOE_DT_F32 && out_dtype != MOE_DT_BF16) return MOE_E_INVALID;
+  if (out_dtype != MOE_DT_F32 && out_dtype != MOE_DT_BF16 && out_dtype != MOE_DT_F16) return MOE_E_INVALID;
   if ((s = validate_ptr(x)) || (s = validate_ptr(y)) || (s = validate_ptr(topk_idx_out, true)) ||
       (s = validate_ptr(topk_w_out, true)))
     return s;

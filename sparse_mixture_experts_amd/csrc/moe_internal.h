@@ -27,17 +27,17 @@ int validate_ptr(const void *p, bool may_be_null = false);
 int validate_weights(const moe_layer_desc *d, const moe_weights *w, bool need_router,
                      bool need_experts);
 
-inline int64_t act_bytes(const moe_layer_desc *d) { return d->act_dtype == MOE_DT_BF16 ? 2 : 4; }
+inline int64_t act_bytes(const moe_layer_desc *d) { return d->act_dtype == MOE_DT_F32 ? 4 : 2; }
 // Affine 4- or 8-bit expert weights (fp16 matrix-core path with fp16 staging).
 inline bool affine(const moe_layer_desc *d) {
   return d->w_format == MOE_WF_AFFINE_Q4 || d->w_format == MOE_WF_AFFINE_Q8;
 }
-// Bytes per element of the SwiGLU intermediate h (bf16 for bf16 layers).
-inline int64_t h_bytes(const moe_layer_desc *d) { return d->act_dtype == MOE_DT_BF16 ? 2 : 4; }
+// Bytes per element of the GLU intermediate h (16-bit for bf16 and fp16 layers).
+inline int64_t h_bytes(const moe_layer_desc *d) { return d->act_dtype == MOE_DT_F32 ? 4 : 2; }
 bool use_mfma(const moe_layer_desc *d);
 // Bytes per element of the workspace copy of the expert outputs: bf16 where
-// the matrix-core kernels write them, fp32 on the vector-unit path.
-inline int64_t ys_bytes(const moe_layer_desc *d) { return use_mfma(d) ? 2 : 4; }
+// the matrix-core kernels serve a bf16 layer, fp32 otherwise.
+inline int64_t ys_bytes(const moe_layer_desc *d) { return use_mfma(d) && d->act_dtype == MOE_DT_BF16 ? 2 : 4; }
 
 // Workspace carve-up.  Every section is 256-byte aligned.
 struct Workspace {

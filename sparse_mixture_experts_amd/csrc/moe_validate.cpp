@@ -11,7 +11,8 @@ static bool is_bool(int32_t v) { return v == 0 || v == 1; }
 
 int validate_desc(const moe_layer_desc *d) {
   if (!d) return MOE_E_INVALID;
-  if (d->act_dtype != MOE_DT_F32 && d->act_dtype != MOE_DT_BF16) return MOE_E_INVALID;
+  if (d->act_dtype != MOE_DT_F32 && d->act_dtype != MOE_DT_BF16 && d->act_dtype != MOE_DT_F16)
+    return MOE_E_INVALID;
   if (d->w_format != MOE_WF_DENSE && !affine(d)) return MOE_E_INVALID;
   if (!is_bool(d->gate_up_fused) || !is_bool(d->swiglu_round_bf16) || !is_bool(d->renormalize))
     return MOE_E_INVALID;
@@ -22,10 +23,10 @@ int validate_desc(const moe_layer_desc *d) {
   if (d->n_shared < 0 || d->n_shared > kMaxShared) return MOE_E_INVALID;
   if (d->swiglu_round_bf16 && d->act_dtype != MOE_DT_BF16) return MOE_E_INVALID;
   if (affine(d)) {
-    // The affine formats carry bf16 scales/biases and feed bf16 activations;
+    // The affine formats carry scales/biases in the 16-bit activation dtype;
     // groups of 32, 64 or 128 along both reduction dims, which the matrix-core
     // kernels walk in steps of 64.
-    if (d->act_dtype != MOE_DT_BF16) return MOE_E_UNSUPPORTED;
+    if (d->act_dtype == MOE_DT_F32) return MOE_E_UNSUPPORTED;
     const int g = d->group_size;
     if (g != 32 && g != 64 && g != 128) return MOE_E_UNSUPPORTED;
     if (d->d_model % 64 || d->d_ff % 64 || d->d_model % g || d->d_ff % g) return MOE_E_INVALID;

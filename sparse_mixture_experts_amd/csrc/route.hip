@@ -23,6 +23,7 @@
 // token: it adds any remaining partials in chunk order, then selects the top-k
 // with a butterfly argmax per slot and computes the fp32 softmax weights.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "dispatch_tiny.h"
@@ -45,12 +46,12 @@ __device__ __forceinline__ int xs_at(int k, int t) {
 
 
 // Eight consecutive router weights as fp32.
-template <bool BF16>
+template <int DT>
 __device__ __forceinline__ void load_w8(const void *w, int64_t i, float o[8]) {
-  if constexpr (BF16) {
+  if constexpr (DT != kDtF32) {
     const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(w) + i);
-    o[0] = bf16_lo(u.x); o[1] = bf16_hi(u.x); o[2] = bf16_lo(u.y); o[3] = bf16_hi(u.y);
-    o[4] = bf16_lo(u.z); o[5] = bf16_hi(u.z); o[6] = bf16_lo(u.w); o[7] = bf16_hi(u.w);
+    o[0] = half_lo<DT>(u.x); o[1] = half_hi<DT>(u.x); o[2] = half_lo<DT>(u.y); o[3] = half_hi<DT>(u.y);
+    o[4] = half_lo<DT>(u.z); o[5] = half_hi<DT>(u.z); o[6] = half_lo<DT>(u.w); o[7] = half_hi<DT>(u.w);
   } else {
     const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(w) + i);
     const float4 a = p[0], b = p[1];
@@ -61,7 +62,7 @@ __device__ __forceinline__ void load_w8(const void *w, int64_t i, float o[8]) {
 // Chunk partials.  Block (tb, eb, cb): tokens tb*TT.., experts eb*EPB.., chunks
 // cb*CPB..; thread = (chunk lane tid / EO, expert octet tid % EO).
 // FULL: the block holds all chunks -> logits[T][E]; else partials[C][T][E].
-template <bool BF16, int TT, int CPB>
+template <int DT, int TT, int CPB>
 __global__ __launch_bounds__(kThreads) void route_partials_kernel(
     const void *__restrict__ x, const void *__restrict__ wr, const float *__restrict__ bias, int T, int D,
     int E, int full, float *__restrict__ out) {
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void route_partials_kernel(
 
   for (int q = tid; q < (kend - kbeg) * TT; q += kThreads) {
     const int k = q / TT, t = q % TT;
-    xs[xs_at<TT>(k, t)] = t < nt ? load_act<BF16>(x, int64_t(t0 + t) * D + kbeg + k) : 0.0f;
+    xs[xs_at<TT>(k, t)] = t < nt ? load_act<DT>(x, int64_t(t0 + t) * D + kbeg + k) : 0.0f;
   }
   __syncthreads();
 
@@ -105,10 +106,10 @@ __global__ __launch_bounds__(kThreads) void route_partials_kernel(
       for (int u = 0; u < 8; ++u) {
         const int64_t base = int64_t(kc + k8 + u) * E + e;
         if (k8 + u < n && vec) {
-          load_w8<BF16>(wr, base, w[u]);
+          load_w8<DT>(wr, base, w[u]);
         } else {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) w[u][j] = (k8 + u < n && e + j < E) ? load_act<BF16>(wr, base + j) : 0.0f;
+          for (int j = 0; j < 8; ++j) w[u][j] = (k8 + u < n && e + j < E) ? load_act<DT>(wr, base + j) : 0.0f;
         }
       }
 #pragma unroll
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void route_partials_kernel(
 // expert and TT tokens; a wave's router loads are coalesced (64 consecutive
 // experts of one column) and the token values, staged in LDS, are the same
 // for every lane.  Output partials[C][T][E] (no bias).
-template <bool BF16, int TT>
+template <int DT, int TT>
 __global__ __launch_bounds__(kWave) void route_chunk_kernel(const void *__restrict__ x, const void *__restrict__ wr,
                                                             int T, int D, int E, float *__restrict__ out) {
   __shared__ float xs[kChunk][TT];
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(kWave) void route_chunk_kernel(const void *__restri
   const int kc = c * kChunk, n = min(kChunk, D - kc), nt = min(TT, T - t0);
 #pragma unroll
   for (int t = 0; t < TT; ++t)
-    xs[lane][t] = (lane < n && t < nt) ? load_act<BF16>(x, int64_t(t0 + t) * D + kc + lane) : 0.0f;
+    xs[lane][t] = (lane < n && t < nt) ? load_act<DT>(x, int64_t(t0 + t) * D + kc + lane) : 0.0f;
   __syncthreads();
   const int ec = min(e, E - 1);
   float p[TT];
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(kWave) void route_chunk_kernel(const void *__restri
   // the whole chunk's router column is loaded at once (one memory round trip)
   float w[kChunk];
 #pragma unroll
-  for (int u = 0; u < kChunk; ++u) w[u] = load_act<BF16>(wr, int64_t(kc + min(u, n - 1)) * E + ec);
+  for (int u = 0; u < kChunk; ++u) w[u] = load_act<DT>(wr, int64_t(kc + min(u, n - 1)) * E + ec);
 #pragma unroll
   for (int u = 0; u < kChunk; ++u) {
     if (u < n) {
@@ -197,7 +198,8 @@ template <int MPL>
 __device__ __forceinline__ void select_token(int t, const float *__restrict__ in, int n_chunks,
                                              const float *__restrict__ bias, int T, int E, int K, int renorm,
                                              int32_t *__restrict__ idx_out, float *__restrict__ w_out,
-                                             const uint16_t *x, int D, uint16_t *x16, int8_t *xsh, int32_t *s_f) {
+                                             const uint16_t *x, int D, uint16_t *x16, int8_t *xsh, bool x_f16,
+                                             int32_t *s_f) {
   // chunk partials per load batch: about 64 loads in flight per lane
   constexpr int CB = MPL >= 64 ? 1 : 64 / MPL;
   const int lane = lane_id();
@@ -265,10 +267,10 @@ __device__ __forceinline__ void select_token(int t, const float *__restrict__ in
     w_out[int64_t(t) * K + lane] = w;
     if (s_f) s_f[t * K + lane] = my_e;
   }
-  if (x16) row_f16_store(xr, D, x16 + int64_t(t) * D, xsh + t);
+  if (x16) row_f16_store(xr, D, x16 + int64_t(t) * D, xsh + t, x_f16);
 }
 
-// With x16 set (4-bit layers, d <= 4096), the wave also writes the token's
+// With x16 set (affine layers, d <= 4096), the wave also writes the token's
 // fp16 staging row for the expert GEMMs; its loads go out with the others.
 // With dsp.order set (all tokens in this one workgroup, T*k <= 128), the
 // selected ids also go to LDS and wave 0 then performs the dispatch.
@@ -277,11 +279,12 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(const float *__r
                                                                 const float *__restrict__ bias, int T, int E,
                                                                 int K, int renorm, int32_t *__restrict__ idx_out,
                                                                 float *__restrict__ w_out, const uint16_t *x, int D,
-                                                                uint16_t *x16, int8_t *xsh, FusedDispatch dsp) {
+                                                                uint16_t *x16, int8_t *xsh, int x_f16,
+                                                                FusedDispatch dsp) {
   __shared__ int32_t s_f[kTinyMaxN];
   __shared__ int32_t s_cnt[kMaxExperts];
   const int t = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
-  if (t < T) select_token<MPL>(t, in, n_chunks, bias, T, E, K, renorm, idx_out, w_out, x, D, x16, xsh,
+  if (t < T) select_token<MPL>(t, in, n_chunks, bias, T, E, K, renorm, idx_out, w_out, x, D, x16, xsh, x_f16,
                                dsp.order ? s_f : nullptr);
   if (dsp.order) {
     __syncthreads();
@@ -292,13 +295,14 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(const float *__r
 }
 
 void launch_select(const float *in, int n_chunks, const float *bias, int T, int E, int K, int renorm,
-                   int32_t *idx, float *w, const void *x, int D, void *x16, int8_t *xsh, const FusedDispatch &dsp,
-                   hipStream_t s) {
+                   int32_t *idx, float *w, const void *x, int D, void *x16, int8_t *xsh, bool x_f16,
+                   const FusedDispatch &dsp, hipStream_t s) {
   const dim3 grid((T + kThreads / kWave - 1) / (kThreads / kWave)), block(kThreads);
   const uint16_t *xb = static_cast<const uint16_t *>(x);
   uint16_t *xo = static_cast<uint16_t *>(x16);
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, block, 0, s, in, n_chunks, bias, T, E, K, renorm, idx, w, xb, D, xo, xsh, dsp);
+    hipLaunchKernelGGL(kern, grid, block, 0, s, in, n_chunks, bias, T, E, K, renorm, idx, w, xb, D, xo, xsh,
+                       int(x_f16), dsp);
   };
   if (E <= 64) go(route_select_kernel<1>);
   else if (E <= 128) go(route_select_kernel<2>);
@@ -308,7 +312,7 @@ void launch_select(const float *in, int n_chunks, const float *bias, int T, int 
 }
 
 // Returns true when one block held every chunk (the output is logits).
-template <bool BF16, int TT, int CPB>
+template <int DT, int TT, int CPB>
 bool launch_partials(const void *x, const void *wr, const float *bias, int T, int D, int E, float *out,
                      hipStream_t s) {
   constexpr int EPB = (kThreads / CPB) * 8;
@@ -320,12 +324,12 @@ bool launch_partials(const void *x, const void *wr, const float *bias, int T, in
     // Above the default dynamic-LDS limit (gfx950 has 160 KB per CU): raise it
     // once per process for this kernel.
     static const bool raised = [&] {
-      return hipFuncSetAttribute(reinterpret_cast<const void *>(&route_partials_kernel<BF16, TT, CPB>),
+      return hipFuncSetAttribute(reinterpret_cast<const void *>(&route_partials_kernel<DT, TT, CPB>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) == hipSuccess;
     }();
     (void)raised;
   }
-  hipLaunchKernelGGL((route_partials_kernel<BF16, TT, CPB>), grid, dim3(kThreads), lds, s, x, wr, bias, T, D,
+  hipLaunchKernelGGL((route_partials_kernel<DT, TT, CPB>), grid, dim3(kThreads), lds, s, x, wr, bias, T, D,
                      E, full, out);
   return full;
 }
@@ -363,27 +367,29 @@ void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int D = d->d_model, E = d->n_experts;
   const int C = (D + kChunk - 1) / kChunk;
-  const bool bf16 = d->act_dtype == MOE_DT_BF16;
   // Large T: 8 tokens per block with every chunk of the block on chip.
   // Small T: one wave per (64 experts, chunk, 8 tokens) for many parallel
   // fma chains, the partials summed by the selection kernel.  Large T with
   // d_model > 2048: one token per block, 2 chunks per block.
   int n_chunks = C;
-  if (T < 64) {
-    const dim3 grid((E + kWave - 1) / kWave, C, (T + 7) / 8);
-    if (bf16) hipLaunchKernelGGL((route_chunk_kernel<true, 8>), grid, dim3(kWave), 0, s, x, w_router, T, D, E, scratch);
-    else hipLaunchKernelGGL((route_chunk_kernel<false, 8>), grid, dim3(kWave), 0, s, x, w_router, T, D, E, scratch);
-  } else if (C <= 32) {
-    if (bf16) launch_partials<true, 8, 32>(x, w_router, bias, T, D, E, scratch, s);
-    else launch_partials<false, 8, 32>(x, w_router, bias, T, D, E, scratch, s);
-    n_chunks = 0;
-  } else {
-    const bool full = bf16 ? launch_partials<true, 1, 2>(x, w_router, bias, T, D, E, scratch, s)
-                           : launch_partials<false, 1, 2>(x, w_router, bias, T, D, E, scratch, s);
-    n_chunks = full ? 0 : C;
-  }
+  auto logits = [&](auto dt) {
+    constexpr int DT = decltype(dt)::value;
+    if (T < 64) {
+      const dim3 grid((E + kWave - 1) / kWave, C, (T + 7) / 8);
+      hipLaunchKernelGGL((route_chunk_kernel<DT, 8>), grid, dim3(kWave), 0, s, x, w_router, T, D, E, scratch);
+    } else if (C <= 32) {
+      launch_partials<DT, 8, 32>(x, w_router, bias, T, D, E, scratch, s);
+      n_chunks = 0;
+    } else {
+      n_chunks = launch_partials<DT, 1, 2>(x, w_router, bias, T, D, E, scratch, s) ? 0 : C;
+    }
+  };
+  if (d->act_dtype == MOE_DT_BF16) logits(std::integral_constant<int, kDtBF16>{});
+  else if (d->act_dtype == MOE_DT_F16) logits(std::integral_constant<int, kDtF16>{});
+  else logits(std::integral_constant<int, kDtF32>{});
   if (mk) mk->mark("route_logits");
-  launch_select(scratch, n_chunks, bias, T, E, d->top_k, d->renormalize, idx, w, x, D, x16, xsh, dsp, s);
+  launch_select(scratch, n_chunks, bias, T, E, d->top_k, d->renormalize, idx, w, x, D, x16, xsh,
+                d->act_dtype == MOE_DT_F16, dsp, s);
   if (mk) mk->mark(dsp.order ? "route_select_dispatch" : "route_select");
 }
 

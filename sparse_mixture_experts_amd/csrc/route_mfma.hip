@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
     }
   }
   xs = wave_sum(xs);
-  if (a.x16) row_f16_store(xr, D, a.x16 + int64_t(t) * D, a.xsh + t);  // xr dies here
+  if (a.x16) row_f16_store(xr, D, a.x16 + int64_t(t) * D, a.xsh + t, false);  // xr dies here (bf16 x)
   float wn = 0.f, bmax = 0.f;
 #pragma unroll
   for (int m = 0; m < MPL; ++m) {

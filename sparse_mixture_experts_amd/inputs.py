@@ -96,8 +96,9 @@ CONFIGS = {
 
 
 # The prefill and decode shapes above in the other weight formats and with the
-# tanh-GELU GLU (8-bit codes, groups of 32 and 128): measured beside the
-# headline workload and compared with the oracle at full size.
+# tanh-GELU GLU (8-bit codes, groups of 32 and 128, fp16 activations):
+# measured beside the headline workload and compared with the oracle at full
+# size.
 VARIANTS = {
     "q8-prefill-t2048": CONFIGS["q4-prefill-t2048"].with_(name="q8-prefill-t2048", wfmt="q8"),
     "q4g32-geglu-prefill-t2048": CONFIGS["q4-prefill-t2048"].with_(name="q4g32-geglu-prefill-t2048",
@@ -105,6 +106,9 @@ VARIANTS = {
     "q4g128-prefill-t2048": CONFIGS["q4-prefill-t2048"].with_(name="q4g128-prefill-t2048", group_size=128),
     "q8-decode-t1": CONFIGS["q4-decode-t1"].with_(name="q8-decode-t1", wfmt="q8"),
     "q8-decode-t32": CONFIGS["q4-decode-t32"].with_(name="q8-decode-t32", wfmt="q8"),
+    # per-op bf16 rounding is defined for bf16 activations only
+    "f16-q4-prefill-t2048": CONFIGS["q4-prefill-t2048"].with_(name="f16-q4-prefill-t2048", act="f16",
+                                                              swiglu_round_bf16=False),
 }
 
 

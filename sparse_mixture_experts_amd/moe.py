@@ -18,7 +18,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
 
 MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = 0, -1, -2, -3, -4
-MOE_DT_F32, MOE_DT_BF16 = 0, 1
+MOE_DT_F32, MOE_DT_BF16, MOE_DT_F16 = 0, 1, 2
+_DT = {"f32": MOE_DT_F32, "bf16": MOE_DT_BF16, "f16": MOE_DT_F16}
 MOE_WF_DENSE, MOE_WF_AFFINE_Q4, MOE_WF_AFFINE_Q8 = 0, 1, 2
 MOE_ACT_SWIGLU, MOE_ACT_GEGLU = 0, 1
 _WFMT = {"dense": MOE_WF_DENSE, "q4": MOE_WF_AFFINE_Q4, "q8": MOE_WF_AFFINE_Q8}
@@ -85,9 +86,10 @@ def moe_status_string(status: int) -> str:
 def make_desc(d_model, d_ff, n_experts, top_k, n_shared=0, act="bf16", wfmt="dense", group_size=64,
               gate_up_fused=False, swiglu_round_bf16=False, renormalize=True,
               activation="swiglu") -> LayerDesc:
-    """wfmt: "dense", "q4" or "q8" (affine 4-/8-bit codes); activation: "swiglu" or "geglu"."""
+    """act: "f32", "bf16" or "f16"; wfmt: "dense", "q4" or "q8" (affine 4-/8-bit codes); activation:
+    "swiglu" or "geglu"."""
     return LayerDesc(d_model, d_ff, n_experts, top_k, n_shared,
-                     MOE_DT_BF16 if act == "bf16" else MOE_DT_F32,
+                     _DT[act],
                      _WFMT[wfmt], group_size,
                      int(gate_up_fused), int(swiglu_round_bf16), int(renormalize), _ACT[activation])
 
@@ -180,8 +182,9 @@ def moe_forward_timed(desc, T, x, weights, y, out_dtype, topk_idx_out, topk_w_ou
 # ---- marshalling helpers ----------------------------------------------------
 
 def to_device(a: np.ndarray, device) -> torch.Tensor:
-    """A NumPy array as a device tensor with the matching element type
-    (uint16 bf16 bits -> torch.bfloat16, uint32 codes -> torch.int32)."""
+    """A NumPy array as a device tensor with the matching element size
+    (uint16 bits of a 16-bit dtype -> a torch.bfloat16 tensor holding them;
+    the library reads them by the layer's dtype; uint32 codes -> torch.int32)."""
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)

@@ -10,6 +10,7 @@ import torch
 from sparse_mixture_experts_amd import inputs, moe
 
 DEV = "cuda:0"
+_TORCH_DT = {moe.MOE_DT_F32: torch.float32, moe.MOE_DT_BF16: torch.bfloat16, moe.MOE_DT_F16: torch.float16}
 
 
 class GpuLayer:
@@ -61,7 +62,7 @@ class GpuLayer:
 
     def combine(self, y_sorted: np.ndarray, inv_order: np.ndarray, topk_w: np.ndarray, out_dtype=moe.MOE_DT_F32):
         y = torch.empty((self.T, self.spec.d_model), device=DEV,
-                        dtype=torch.float32 if out_dtype == moe.MOE_DT_F32 else torch.bfloat16)
+                        dtype=_TORCH_DT[out_dtype])
         moe.moe_combine(self.desc, self.T, torch.from_numpy(y_sorted).to(DEV), torch.from_numpy(inv_order).to(DEV),
                         torch.from_numpy(np.ascontiguousarray(topk_w)).to(DEV), y, out_dtype)
         torch.cuda.synchronize()
@@ -69,7 +70,7 @@ class GpuLayer:
 
     def forward(self, out_dtype=moe.MOE_DT_F32, want_routing=True):
         y = torch.empty((self.T, self.spec.d_model), device=DEV,
-                        dtype=torch.float32 if out_dtype == moe.MOE_DT_F32 else torch.bfloat16)
+                        dtype=_TORCH_DT[out_dtype])
         idx = torch.empty((self.T, self.spec.top_k), dtype=torch.int32, device=DEV) if want_routing else None
         w = torch.empty((self.T, self.spec.top_k), dtype=torch.float32, device=DEV) if want_routing else None
         moe.moe_forward(self.desc, self.T, self.x, self.w, y, out_dtype, idx, w, self.ws)
@@ -89,3 +90,7 @@ def rel_err(y: np.ndarray, ref: np.ndarray) -> float:
 
 def bf16_rne(a: np.ndarray) -> np.ndarray:
     return inputs.bf16_bits_to_f32(inputs.to_bf16_bits(a))
+
+
+def f16_rne(a: np.ndarray) -> np.ndarray:
+    return inputs.f16_bits_to_f32(inputs.to_f16_bits(a))

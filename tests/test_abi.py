@@ -92,9 +92,15 @@ def test_affine_formats_and_groups(lib):
     # the group must divide both reduction lengths
     d = moe.make_desc(2048, 192, 128, 8, wfmt="q8", group_size=128)
     assert lib.moe_workspace_size(ctypes.byref(d), 4, ctypes.byref(size)) == moe.MOE_E_INVALID
-    # the affine formats feed bf16 activations only
+    # the affine formats feed 16-bit activations only
     d = moe.make_desc(2048, 768, 128, 8, act="f32", wfmt="q8")
     assert lib.moe_workspace_size(ctypes.byref(d), 4, ctypes.byref(size)) == moe.MOE_E_UNSUPPORTED
+    for act in ("bf16", "f16"):
+        d = moe.make_desc(2048, 768, 128, 8, act=act, wfmt="q4")
+        assert lib.moe_workspace_size(ctypes.byref(d), 4, ctypes.byref(size)) == moe.MOE_OK
+    # per-op bf16 rounding needs bf16 activations
+    d = moe.make_desc(256, 128, 8, 2, act="f16", swiglu_round_bf16=True)
+    assert lib.moe_workspace_size(ctypes.byref(d), 4, ctypes.byref(size)) == moe.MOE_E_INVALID
 
 
 def test_top_k_above_experts_and_rounding_needs_bf16(lib):

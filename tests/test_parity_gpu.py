@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import pins
-from gpu_util import GpuLayer, bf16_rne, rel_err, tol_for
+from gpu_util import GpuLayer, bf16_rne, f16_rne, rel_err, tol_for
 from sparse_mixture_experts_amd import inputs, moe
 from sparse_mixture_experts_amd.inputs import LayerSpec
 
@@ -75,6 +75,19 @@ MID = {
                                 activation="geglu", seed=39),
     "mid-f32-geglu": LayerSpec("mid-f32-geglu", T=17, d_model=96, d_ff=64, n_experts=4, top_k=2, act="f32",
                                activation="geglu", x_scale="fan_in", seed=40),
+    # fp16 activations (fp16 scales/biases, dense fp16 weights) on the dense
+    # matrix cores, the vector-unit path, 64-row, 16-row and decode tiles
+    "mid-f16-dense": LayerSpec("mid-f16-dense", T=120, d_model=256, d_ff=192, n_experts=8, top_k=2, act="f16",
+                               seed=43),
+    "mid-f16-dense-gemv": LayerSpec("mid-f16-dense-gemv", T=20, d_model=96, d_ff=40, n_experts=4, top_k=2,
+                                    act="f16", activation="geglu", seed=44),
+    "mid-f16-q4-shared": LayerSpec("mid-f16-q4-shared", T=150, d_model=256, d_ff=128, n_experts=16, top_k=3,
+                                   n_shared=1, act="f16", wfmt="q4", router_bias="zipf", seed=45),
+    "mid-f16-q4-tile16-fused": LayerSpec("mid-f16-q4-tile16-fused", T=40, d_model=256, d_ff=192, n_experts=32,
+                                         top_k=4, act="f16", wfmt="q4", gate_up_fused=True, seed=46),
+    "mid-f16-q8-decode-geglu": LayerSpec("mid-f16-q8-decode-geglu", T=3, d_model=512, d_ff=256, n_experts=64,
+                                         top_k=8, act="f16", wfmt="q8", group_size=128, activation="geglu",
+                                         seed=47),
 }
 FULL = {**inputs.CONFIGS, **inputs.VARIANTS}
 SAMPLE = 48  # tokens compared per full-size layer (all when T is smaller)
@@ -226,6 +239,9 @@ def _forward_check(name, tokens=None):
     # bf16 output is the nearest-even rounding of the fp32 output; runs repeat bit for bit
     yb, _, _ = g.forward(moe.MOE_DT_BF16, want_routing=False)
     assert np.array_equal(yb.float().cpu().numpy(), bf16_rne(y))
+    if spec.act == "f16":
+        yh, _, _ = g.forward(moe.MOE_DT_F16, want_routing=False)
+        assert np.array_equal(yh.float().cpu().numpy(), f16_rne(y))
     y2, idx2, _ = g.forward()
     assert np.array_equal(y2.cpu().numpy().view(np.uint32), y.view(np.uint32)) and np.array_equal(
         idx2.cpu().numpy(), idx)
