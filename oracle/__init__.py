@@ -68,6 +68,7 @@ def _open(path: str):
     lib.oracle_dequant_row.argtypes = [vp, vp, i32, i32, i32, i32, vp]
     lib.oracle_expert_apply.argtypes = [vp, vp, i32, vp, vp, vp]
     lib.oracle_forward_tokens.argtypes = [vp, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, i32]
+    lib.oracle_backward_tokens.argtypes = [vp, i32, vp, vp, vp, vp, i32, vp, vp, vp, i32]
     lib.oracle_last_threads.restype = i32
     return lib
 
@@ -240,3 +241,22 @@ def forward(desc: Desc, x, w_router, router_bias, weights: dict, tokens=None, n_
                               ctypes.byref(s), n, _ptr(toks), _ptr(y), _ptr(idx), _ptr(w), n_threads)
     del keep
     return y, idx, w, int(lib.oracle_last_threads())
+
+
+def backward(desc: Desc, x, w_router, router_bias, weights: dict, dy, tokens=None, n_threads: int = 0):
+    """dx = dy . dy/dx for `tokens` (default: all); dy is fp32 [n_tok][d_model]
+    with row r for tokens[r].  Returns (dx f32, threads_used)."""
+    lib = _load()
+    x, w_router = _act(desc, x), _act(desc, w_router)
+    T = x.shape[0]
+    toks = np.arange(T, dtype=np.int32) if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
+    bias = None if router_bias is None else np.ascontiguousarray(router_bias, dtype=np.float32)
+    dy = np.ascontiguousarray(dy, dtype=np.float32)
+    n = toks.shape[0]
+    assert dy.shape == (n, desc.d_model)
+    s, keep = _experts(desc, weights)
+    dx = np.empty((n, desc.d_model), np.float32)
+    lib.oracle_backward_tokens(ctypes.byref(desc._c()), T, _ptr(x), _ptr(w_router), _ptr(bias),
+                               ctypes.byref(s), n, _ptr(toks), _ptr(dy), _ptr(dx), n_threads)
+    del keep
+    return dx, int(lib.oracle_last_threads())

@@ -260,6 +260,24 @@ static float gelu_tanh(float g) {
  * The fused [gate | up] matrix holds gate in rows 0..d_ff-1 and up in rows
  * d_ff..2*d_ff-1.
  */
+/* Row n of expert e's gate and up matrices, dequantised.  The fused
+ * [gate | up] matrix holds gate in rows 0..d_ff-1 and up in rows
+ * d_ff..2*d_ff-1. */
+static void gate_row(const oracle_desc *d, const oracle_experts *w, int32_t e, int32_t n, float *row) {
+  const int32_t D = d->d_model, F = d->d_ff;
+  if (d->gate_up_fused)
+    oracle_dequant_row(d, &w->gate_up, e, n, 2 * F, D, row);
+  else
+    oracle_dequant_row(d, &w->gate, e, n, F, D, row);
+}
+static void up_row(const oracle_desc *d, const oracle_experts *w, int32_t e, int32_t n, float *row) {
+  const int32_t D = d->d_model, F = d->d_ff;
+  if (d->gate_up_fused)
+    oracle_dequant_row(d, &w->gate_up, e, F + n, 2 * F, D, row);
+  else
+    oracle_dequant_row(d, &w->up, e, n, F, D, row);
+}
+
 void oracle_expert_apply(const oracle_desc *d, const oracle_experts *w,
                          int32_t e, const void *x_row, float *h_out,
                          float *out) {
@@ -271,15 +289,9 @@ void oracle_expert_apply(const oracle_desc *d, const oracle_experts *w,
 
   for (int32_t n = 0; n < F; ++n) {
     float g = 0.0f, u = 0.0f;
-    if (d->gate_up_fused)
-      oracle_dequant_row(d, &w->gate_up, e, n, 2 * F, D, row);
-    else
-      oracle_dequant_row(d, &w->gate, e, n, F, D, row);
+    gate_row(d, w, e, n, row);
     for (int32_t k = 0; k < D; ++k) g = g + xr[k] * row[k];
-    if (d->gate_up_fused)
-      oracle_dequant_row(d, &w->gate_up, e, F + n, 2 * F, D, row);
-    else
-      oracle_dequant_row(d, &w->up, e, n, F, D, row);
+    up_row(d, w, e, n, row);
     for (int32_t k = 0; k < D; ++k) u = u + xr[k] * row[k];
     if (d->activation == 1) {
       if (d->swiglu_round_bf16) {
@@ -356,6 +368,151 @@ void oracle_forward_tokens(const oracle_desc *d, int32_t T, const void *x,
     free(idx);
     free(wt);
     free(o);
+  }
+}
+
+/*
+ * Backward pass (vector-Jacobian product with respect to x).  "SwitchGLU:
+ * grouped-expert Metal kernels", section "What": the grouped kernels carry a
+ * custom VJP (the gather_qmm math) so that training through the quantised
+ * experts works.  Here, for one token with upstream gradient dy:
+ *   - routing: the selected experts are held at the forward's choice (the
+ *     top-k set is piecewise constant in x); the gradient flows through the
+ *     selected weights w_j;
+ *   - expert j (weight c = w_j; shared experts c = 1): o = Wd h, h = glu(g, u),
+ *     g = Wg x, u = Wu x.  dw_j = dy . o; dh = c Wd^T dy;
+ *     SwiGLU: dg = dh u s (1 + g (1 - s)), s = sigmoid(g); du = dh silu(g);
+ *     GeGLU:  dg = dh u gelu'(g), du = dh gelu(g), with
+ *             gelu'(g) = 0.5 (1 + tanh z) + 0.5 g (1 - tanh^2 z) z',
+ *             z = a (g + b g^3), z' = a (1 + 3 b g^2);
+ *     dx += Wg^T dg + Wu^T du;
+ *   - router: with renormalisation w = softmax over the selected logits, so
+ *     dl_j = w_j (dw_j - sum_i w_i dw_i) on the selected experts only;
+ *     without it w_j = p_{e_j} (softmax over all E), dl_e = p_e (dw(e) -
+ *     sum_j w_j dw_j) for every e (dw(e) = 0 off the selection);
+ *     dx += W_r dl (the bias does not depend on x).
+ * The forward's per-op rounding is not differentiated: g, u and h are the
+ * unrounded fp32 values.  Accumulation: expert parts in slot order, then the
+ * shared experts, then the router part; every sum in ascending index order.
+ */
+static void glu_grad(const oracle_desc *d, float g, float u, float dh, float *dg, float *du) {
+  if (d->activation == 1) {
+    const float a = 0.7978845608028654f, b = 0.044715f;
+    const float z = a * (g + b * g * g * g);
+    const float th = tanhf(z);
+    const float gelu = 0.5f * g * (1.0f + th);
+    const float dgelu = 0.5f * (1.0f + th) + 0.5f * g * (1.0f - th * th) * a * (1.0f + 3.0f * b * g * g);
+    *dg = dh * u * dgelu;
+    *du = dh * gelu;
+  } else {
+    const float s = 1.0f / (1.0f + expf(-g));
+    *dg = dh * u * (s * (1.0f + g * (1.0f - s)));
+    *du = dh * (g * s);
+  }
+}
+
+/* Adds one expert's contribution c * (expert e at x_row) to dx, and returns
+ * dw = dy . (expert e at x_row). */
+static float expert_backward(const oracle_desc *d, const oracle_experts *w, int32_t e, const float *xr,
+                             const float *dyr, float c, float *dxr) {
+  const int32_t D = d->d_model, F = d->d_ff;
+  float *row = (float *)malloc(sizeof(float) * (size_t)(D > F ? D : F));
+  float *g = (float *)malloc(sizeof(float) * (size_t)F);
+  float *u = (float *)malloc(sizeof(float) * (size_t)F);
+  float *h = (float *)malloc(sizeof(float) * (size_t)F);
+  float *dh = (float *)calloc((size_t)F, sizeof(float));
+  for (int32_t n = 0; n < F; ++n) {
+    float gn = 0.0f, un = 0.0f;
+    gate_row(d, w, e, n, row);
+    for (int32_t k = 0; k < D; ++k) gn = gn + xr[k] * row[k];
+    up_row(d, w, e, n, row);
+    for (int32_t k = 0; k < D; ++k) un = un + xr[k] * row[k];
+    g[n] = gn;
+    u[n] = un;
+    h[n] = d->activation == 1 ? gelu_tanh(gn) * un : silu(gn) * un;
+  }
+  /* o = Wd h (for dw) and dh = c Wd^T dy, row m of Wd at a time */
+  float dw = 0.0f;
+  for (int32_t m = 0; m < D; ++m) {
+    oracle_dequant_row(d, &w->down, e, m, D, F, row);
+    float o = 0.0f;
+    for (int32_t n = 0; n < F; ++n) o = o + h[n] * row[n];
+    dw = dw + dyr[m] * o;
+    for (int32_t n = 0; n < F; ++n) dh[n] = dh[n] + dyr[m] * row[n];
+  }
+  for (int32_t n = 0; n < F; ++n) {
+    float dg, du;
+    glu_grad(d, g[n], u[n], c * dh[n], &dg, &du);
+    gate_row(d, w, e, n, row);
+    for (int32_t k = 0; k < D; ++k) dxr[k] = dxr[k] + dg * row[k];
+    up_row(d, w, e, n, row);
+    for (int32_t k = 0; k < D; ++k) dxr[k] = dxr[k] + du * row[k];
+  }
+  free(row);
+  free(g);
+  free(u);
+  free(h);
+  free(dh);
+  return dw;
+}
+
+void oracle_backward_tokens(const oracle_desc *d, int32_t T, const void *x,
+                            const void *w_router, const float *router_bias,
+                            const oracle_experts *w, int32_t n_tok,
+                            const int32_t *tokens, const float *dy, float *dx,
+                            int32_t n_threads) {
+  (void)T;
+  const int32_t D = d->d_model, K = d->top_k, E = d->n_experts;
+  const size_t esz = d->act_bf16 || d->act_f16 ? 2 : 4;
+#ifdef _OPENMP
+  if (n_threads > 0) omp_set_num_threads(n_threads);
+  g_last_threads = omp_get_max_threads();
+#else
+  (void)n_threads;
+  g_last_threads = 1;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int32_t r = 0; r < n_tok; ++r) {
+    const int32_t t = tokens[r];
+    const void *xt = (const char *)x + (size_t)t * D * esz;
+    const float *dyr = dy + (int64_t)r * D;
+    float *dxr = dx + (int64_t)r * D;
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)K);
+    float *wt = (float *)malloc(sizeof(float) * (size_t)K);
+    float *dw = (float *)malloc(sizeof(float) * (size_t)K);
+    float *l = (float *)malloc(sizeof(float) * (size_t)E);
+    float *dl = (float *)calloc((size_t)E, sizeof(float));
+    float *xr = (float *)malloc(sizeof(float) * (size_t)D);
+    for (int32_t k = 0; k < D; ++k) xr[k] = act_at(d, xt, k);
+    oracle_router_logits(d, 1, xt, w_router, router_bias, l);
+    route_one(d, l, idx, wt);
+    for (int32_t k = 0; k < D; ++k) dxr[k] = 0.0f;
+    for (int32_t j = 0; j < K; ++j) dw[j] = expert_backward(d, w, idx[j], xr, dyr, wt[j], dxr);
+    for (int32_t s = 0; s < d->n_shared; ++s) (void)expert_backward(d, w, E + s, xr, dyr, 1.0f, dxr);
+    float dot = 0.0f;
+    for (int32_t j = 0; j < K; ++j) dot = dot + wt[j] * dw[j];
+    if (d->renormalize) {
+      for (int32_t j = 0; j < K; ++j) dl[idx[j]] = wt[j] * (dw[j] - dot);
+    } else {
+      /* the softmax over all E, as route_one forms it */
+      float m = l[0];
+      for (int32_t e = 1; e < E; ++e) m = l[e] > m ? l[e] : m;
+      float z = 0.0f;
+      for (int32_t e = 0; e < E; ++e) z = z + expf(l[e] - m);
+      for (int32_t e = 0; e < E; ++e) dl[e] = -(expf(l[e] - m) / z) * dot;
+      for (int32_t j = 0; j < K; ++j) dl[idx[j]] = dl[idx[j]] + wt[j] * dw[j];
+    }
+    for (int32_t k = 0; k < D; ++k) {
+      float a = 0.0f;
+      for (int32_t e = 0; e < E; ++e) a = a + act_at(d, w_router, (int64_t)k * E + e) * dl[e];
+      dxr[k] = dxr[k] + a;
+    }
+    free(idx);
+    free(wt);
+    free(dw);
+    free(l);
+    free(dl);
+    free(xr);
   }
 }
 

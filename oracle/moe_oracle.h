@@ -108,6 +108,16 @@ void oracle_forward_tokens(const oracle_desc *d, int32_t T, const void *x,
                            const int32_t *tokens, float *y, int32_t *topk_idx,
                            float *topk_w, int32_t n_threads);
 
+/* Backward of the layer with respect to x for the tokens listed in
+ * `tokens`: dy[n_tok][d_model] (fp32, row r belongs to tokens[r]) gives
+ * dx[n_tok][d_model] = dy . dy/dx at x[tokens[r]], weights fixed, routing
+ * fixed at the forward's choice, per-op rounding left out. */
+void oracle_backward_tokens(const oracle_desc *d, int32_t T, const void *x,
+                            const void *w_router, const float *router_bias,
+                            const oracle_experts *w, int32_t n_tok,
+                            const int32_t *tokens, const float *dy, float *dx,
+                            int32_t n_threads);
+
 /* Threads the last oracle_forward_tokens call ran with. */
 int32_t oracle_last_threads(void);
 

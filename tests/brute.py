@@ -118,3 +118,30 @@ def layer_dense_masked64(spec: LayerSpec, layer: dict, topk_idx: np.ndarray, top
     if spec.n_shared:
         y = y + O[:, E:, :].sum(axis=1)
     return y
+
+
+def layer_backward64(spec: LayerSpec, layer: dict, topk_idx: np.ndarray, dy: np.ndarray) -> np.ndarray:
+    """dx = dy . dy/dx by torch's autograd in float64 on the dense formulation
+    of the layer with the routing held at topk_idx (the unrounded forward)."""
+    import torch
+    E, K = spec.n_experts, spec.top_k
+    x = torch.tensor(widen(spec, layer["x"]), dtype=torch.float64, requires_grad=True)
+    wr = torch.tensor(widen(spec, layer["w_router"]), dtype=torch.float64)
+    gate, up, down = (torch.tensor(m, dtype=torch.float64) for m in weights64(spec, layer["experts"]))
+    logits = x @ wr
+    if layer["router_bias"] is not None:
+        logits = logits + torch.tensor(np.asarray(layer["router_bias"], np.float64))
+    p = torch.softmax(logits, dim=-1)
+    idx = torch.tensor(np.asarray(topk_idx, np.int64))
+    w = torch.gather(p, 1, idx)
+    if spec.renormalize:
+        w = w / w.sum(dim=1, keepdim=True)
+    act = ((lambda g: torch.nn.functional.gelu(g, approximate="tanh")) if spec.activation == "geglu"
+           else torch.nn.functional.silu)
+    g = torch.einsum("td,efd->tef", x, gate)
+    u = torch.einsum("td,efd->tef", x, up)
+    o = torch.einsum("tef,edf->ted", act(g) * u, down)  # every expert on every token
+    sel = torch.gather(o[:, :E, :], 1, idx[:, :, None].expand(-1, -1, spec.d_model))
+    y = (w[:, :, None] * sel).sum(dim=1) + o[:, E:, :].sum(dim=1)
+    (y * torch.tensor(np.asarray(dy, np.float64))).sum().backward()
+    return x.grad.numpy()

@@ -18,6 +18,8 @@ tests swap for builds with planted mistakes.  What pins what:
                           quantisation error bound against the original draw; for
                           4- and 8-bit codes and groups of 32, 64 and 128.
 * GeGLU                -- torch's tanh-approximate GELU (a library routine) in fp64.
+* backward (dx)        -- torch autograd in fp64 on the dense formulation with the routing
+                          held; permutation equivariance; linearity in dy.
 * expert FFN, layer    -- NumPy fp64 dense brute force; sparse == dense all-experts
                           output masked to the top-k and weighted; k = E equals soft
                           routing; E = k = 1 equals a plain SwiGLU MLP; x = 0 gives
@@ -324,6 +326,26 @@ def pin_gelu_special_values():
     assert np.all(h0 == 0.0)
 
 
+def pin_backward(name: str):
+    """dx against torch's autograd in fp64 (the dense formulation with the
+    routing held at the oracle's choice, unrounded forward)."""
+    spec, L = SMALL[name], layer(name)
+    d = desc_of(spec)
+    dy = inputs._rng(spec.seed, 9).standard_normal((spec.T, spec.d_model), dtype=np.float32)
+    dx, _ = oracle.backward(d, L["x"], L["w_router"], L["router_bias"], L["experts"], dy)
+    idx, _ = oracle.route(d, L["x"], L["w_router"], L["router_bias"])
+    ref = brute.layer_backward64(spec, L, idx, dy)
+    rms = math.sqrt(float(np.mean(ref ** 2)))
+    assert np.max(np.abs(dx - ref)) <= 2e-5 * rms, (name, np.max(np.abs(dx - ref)) / rms)
+    # token permutation equivariance and linearity in dy
+    perm = np.random.default_rng(5).permutation(spec.T)
+    dxp, _ = oracle.backward(d, L["x"], L["w_router"], L["router_bias"], L["experts"], dy[perm],
+                             tokens=perm.astype(np.int32))
+    assert np.array_equal(dxp, dx[perm])
+    dx2, _ = oracle.backward(d, L["x"], L["w_router"], L["router_bias"], L["experts"], 2 * dy)
+    assert np.array_equal(dx2, 2 * dx)
+
+
 def pin_layer(name: str):
     spec, L = SMALL[name], layer(name)
     d = desc_of(spec)
@@ -391,6 +413,7 @@ ALL_PINS = [
     ("gelu_special_values", pin_gelu_special_values, ()),
     *[(f"expert[{n}]", pin_expert, (n,)) for n in SMALL],
     *[(f"layer[{n}]", pin_layer, (n,)) for n in SMALL],
+    *[(f"backward[{n}]", pin_backward, (n,)) for n in SMALL],
     ("soft_routing", pin_soft_routing, ()),
     ("plain_mlp", pin_plain_mlp, ()),
     *[(f"zero_perm[{n}]", pin_zero_and_permutation, (n,)) for n in SMALL],

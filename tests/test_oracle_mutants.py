@@ -25,11 +25,19 @@ MUTANTS = {
     "code_width_fixed_4": ("const int32_t per = 32 / bits;", "const int32_t per = 8;"),
     "group_size_fixed_64": ("const int32_t G = d->group_size;", "const int32_t G = 64;"),
     "gelu_cubic_dropped": ("(g + 0.044715f * g * g * g)", "(g)"),
-    "geglu_runs_silu": ("if (d->activation == 1) {", "if (0) {"),
+    "geglu_runs_silu": ("    if (d->activation == 1) {\n      if (d->swiglu_round_bf16) {",
+                        "    if (0) {\n      if (d->swiglu_round_bf16) {"),
+    "geglu_grad_runs_silu": ("  if (d->activation == 1) {\n    const float a = 0.7978845608028654f",
+                             "  if (0) {\n    const float a = 0.7978845608028654f"),
     "geglu_rounding_skipped": ("h[n] = round_bf16(round_bf16(gelu_tanh(g)) * u);", "h[n] = gelu_tanh(g) * u;"),
     "scale_bias_swapped": ("out[k] = s * (float)q + b;", "out[k] = b * (float)q + s;"),
     "group_index_wrong": ("float s = half_at(d, sc[(int64_t)(k / G) * N]);", "float s = half_at(d, sc[0]);"),
     "f16_exponent_bias": ("(int)e - 25", "(int)e - 24"),
+    "swiglu_grad_dropped_term": ("*dg = dh * u * (s * (1.0f + g * (1.0f - s)));", "*dg = dh * u * s;"),
+    "gelu_grad_cubic_coeff": ("a * (1.0f + 3.0f * b * g * g)", "a * (1.0f + b * g * g)"),
+    "router_grad_dropped": ("dxr[k] = dxr[k] + a;", "dxr[k] = dxr[k] + 0.0f * a;"),
+    "renorm_grad_mean_dropped": ("dl[idx[j]] = wt[j] * (dw[j] - dot);", "dl[idx[j]] = wt[j] * dw[j];"),
+    "expert_grad_unweighted": ("glu_grad(d, g[n], u[n], c * dh[n], &dg, &du);", "glu_grad(d, g[n], u[n], dh[n], &dg, &du);"),
     "f16_subnormal_scale": ("ldexpf((float)m, -24)", "ldexpf((float)m, -25)"),
     "f16_scales_read_as_bf16": ("return d->act_f16 ? oracle_f16_to_f32(h) : oracle_bf16_to_f32(h);",
                                 "return d->act_f16 && 0 ? oracle_f16_to_f32(h) : oracle_bf16_to_f32(h);"),
@@ -37,6 +45,8 @@ MUTANTS = {
                             "oracle_dequant_row(d, &w->gate_up, e, n, 2 * F, D, row);"),
     "separate_gate_reads_up": ("oracle_dequant_row(d, &w->gate, e, n, F, D, row);",
                                "oracle_dequant_row(d, &w->up, e, n, F, D, row);"),
+    "backward_up_reads_gate": ("    up_row(d, w, e, n, row);\n    for (int32_t k = 0; k < D; ++k) dxr[k]",
+                               "    gate_row(d, w, e, n, row);\n    for (int32_t k = 0; k < D; ++k) dxr[k]"),
     "silu_sign": ("static float silu(float g) { return g / (1.0f + expf(-g)); }",
                   "static float silu(float g) { return g / (1.0f + expf(g)); }"),
     "sigmoid_not_rounded": ("float s = round_bf16(sigmoid(g));", "float s = sigmoid(g);"),
