@@ -213,6 +213,23 @@ int moe_forward_timed(const moe_layer_desc *desc, int32_t T, const void *x,
                       size_t ws_bytes, void *stream, void *const *events,
                       int32_t n_events, char *names, size_t names_len);
 
+/*
+ * Backward of the layer with respect to x ("SwitchGLU: grouped-expert Metal
+ * kernels", section "What": the grouped experts carry a custom VJP for
+ * training through them).  dy[T][d_model] fp32 is the gradient of the loss
+ * with respect to the forward's y; dx[T][d_model] fp32 receives
+ * dy . dy/dx with the weights fixed and the routing held at the forward's
+ * choice: through the selected experts (scaled by their weights), the shared
+ * experts, and the softmax (renormalised or not) that gives the slot weights,
+ * then W_router.  The forward's per-op rounding is not differentiated.  The
+ * router and dispatch run again inside.  ws: moe_backward_workspace_size
+ * bytes (caller-owned, 16-byte aligned).  Errors as for moe_forward.
+ */
+int moe_backward_workspace_size(const moe_layer_desc *desc, int32_t T, size_t *bytes);
+int moe_backward(const moe_layer_desc *desc, int32_t T, const void *x,
+                 const moe_weights *w, const float *dy, float *dx, void *ws,
+                 size_t ws_bytes, void *stream);
+
 /* A static, human-readable name of a moe_status value. */
 const char *moe_status_string(int status);
 

@@ -199,4 +199,40 @@ int moe_forward_timed(const moe_layer_desc *desc, int32_t T, const void *x, cons
   return forward_impl(desc, T, x, w, y, out_dtype, topk_idx_out, topk_w_out, ws, ws_bytes, stream, &mk);
 }
 
+int moe_backward_workspace_size(const moe_layer_desc *desc, int32_t T, size_t *bytes) {
+  int s;
+  if ((s = validate_desc(desc)) || (s = validate_T(T))) return s;
+  if (!bytes) return MOE_E_INVALID;
+  *bytes = backward_workspace_layout(desc, T).total;
+  return MOE_OK;
+}
+
+int moe_backward(const moe_layer_desc *desc, int32_t T, const void *x, const moe_weights *w, const float *dy,
+                 float *dx, void *ws, size_t ws_bytes, void *stream) {
+  int s;
+  if ((s = validate_desc(desc)) || (s = validate_T(T))) return s;
+  if ((s = validate_ptr(x)) || (s = validate_ptr(dy)) || (s = validate_ptr(dx))) return s;
+  if ((s = validate_weights(desc, w, true, true))) return s;
+  if (validate_ptr(ws)) return MOE_E_INVALID;
+  const BwdWorkspace B = backward_workspace_layout(desc, T);
+  if (ws_bytes < B.total) return MOE_E_WORKSPACE;
+  if (T == 0) return MOE_OK;
+  const Workspace &L = B.fwd;
+  // the forward's routing and grouping, again (no staging copy of x)
+  int32_t *idx = at<int32_t>(ws, L.topk_idx);
+  float *wt = at<float>(ws, L.topk_w);
+  launch_route(desc, T, x, w->w_router, w->router_bias, idx, wt, at<float>(ws, L.route), nullptr, nullptr,
+               FusedDispatch{}, stream);
+  launch_dispatch(desc, T, idx, plan_tile_rows(desc, T), at<int32_t>(ws, L.order), at<int32_t>(ws, L.inv_order),
+                  at<int32_t>(ws, L.row_map), at<int32_t>(ws, L.expert_off), at<int32_t>(ws, L.tile_off),
+                  at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles),
+                  at<int32_t>(ws, L.dsp), stream);
+  const BwdScratch sc{at<float>(ws, B.g), at<float>(ws, B.u), at<float>(ws, B.v), at<float>(ws, B.dw),
+                      at<float>(ws, B.dxr)};
+  launch_backward(desc, T, x, w, dy, idx, wt, at<int32_t>(ws, L.order), at<int32_t>(ws, L.inv_order),
+                  at<int32_t>(ws, L.row_map), at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items), sc, dx,
+                  stream);
+  return hip_status();
+}
+
 }  // extern "C"

@@ -130,6 +130,21 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
                             int64_t max_tiles, const FfnScratch &sc, void *y_sorted, bool ys_bf16, void *stream,
                             StageMarker *mk);
 
+// Backward with respect to x (fp32 intermediates in the backward workspace):
+// g and u [R][F] (then dg and du), v = Wd^T dy [R][F], dw [R], dx rows [R][D].
+struct BwdScratch {
+  float *g, *u, *v, *dw, *dxr;
+};
+struct BwdWorkspace {
+  Workspace fwd;  // router and dispatch sections (the forward's layout)
+  size_t g, u, v, dw, dxr, total;
+};
+BwdWorkspace backward_workspace_layout(const moe_layer_desc *d, int32_t T);
+void launch_backward(const moe_layer_desc *d, int32_t T, const void *x, const moe_weights *w, const float *dy,
+                     const int32_t *topk_idx, const float *topk_w, const int32_t *order, const int32_t *inv_order,
+                     const int32_t *row_map, const int32_t *counters, const PlanItem *items, const BwdScratch &sc,
+                     float *dx, void *stream);
+
 // Combine.
 void launch_combine(const moe_layer_desc *d, int32_t T, const void *y_sorted, bool ys_bf16,
                     const int32_t *inv_order, const float *topk_w, void *y, int32_t out_dtype,

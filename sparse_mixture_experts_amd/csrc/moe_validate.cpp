@@ -115,4 +115,23 @@ Workspace workspace_layout(const moe_layer_desc *d, int32_t T) {
   return ws;
 }
 
+BwdWorkspace backward_workspace_layout(const moe_layer_desc *d, int32_t T) {
+  BwdWorkspace b{};
+  b.fwd = workspace_layout(d, T);
+  const int64_t rows = int64_t(T) * d->top_k + int64_t(d->n_shared) * T;
+  size_t o = b.fwd.total;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  b.g = take(size_t(rows) * d->d_ff * 4);
+  b.u = take(size_t(rows) * d->d_ff * 4);
+  b.v = take(size_t(rows) * d->d_ff * 4);
+  b.dw = take(size_t(rows) * 4);
+  b.dxr = take(size_t(rows) * d->d_model * 4);
+  b.total = o;
+  return b;
+}
+
 }  // namespace moe

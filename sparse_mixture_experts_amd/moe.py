@@ -26,7 +26,8 @@ _WFMT = {"dense": MOE_WF_DENSE, "q4": MOE_WF_AFFINE_Q4, "q8": MOE_WF_AFFINE_Q8}
 _ACT = {"swiglu": MOE_ACT_SWIGLU, "geglu": MOE_ACT_GEGLU}
 
 EXPORTED = ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-            "moe_forward", "moe_forward_timed", "moe_status_string")
+            "moe_forward", "moe_forward_timed", "moe_backward_workspace_size", "moe_backward",
+            "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -70,6 +71,8 @@ def load() -> ctypes.CDLL:
         lib.moe_forward.argtypes = [P(LayerDesc), i32, vp, P(Weights), vp, i32, vp, vp, vp, sz, vp]
         lib.moe_forward_timed.argtypes = [P(LayerDesc), i32, vp, P(Weights), vp, i32, vp, vp, vp, sz, vp,
                                           P(vp), i32, ctypes.c_char_p, sz]
+        lib.moe_backward_workspace_size.argtypes = [P(LayerDesc), i32, P(sz)]
+        lib.moe_backward.argtypes = [P(LayerDesc), i32, vp, P(Weights), vp, vp, vp, sz, vp]
         lib.moe_status_string.argtypes = [ctypes.c_int]
         lib.moe_status_string.restype = ctypes.c_char_p
         for name in EXPORTED:
@@ -177,6 +180,18 @@ def moe_forward_timed(desc, T, x, weights, y, out_dtype, topk_idx_out, topk_w_ou
                                     _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws), _nbytes(ws), _stream(stream),
                                     arr, len(events), names, 512), "moe_forward_timed")
     return names.value.decode().split(",") if names.value else []
+
+
+def moe_backward_workspace_size(desc: LayerDesc, T: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().moe_backward_workspace_size(ctypes.byref(desc), T, ctypes.byref(out)), "moe_backward_workspace_size")
+    return out.value
+
+
+def moe_backward(desc, T, x, weights, dy, dx, ws, stream=None):
+    """dx[T][d_model] (fp32) = dy . dy/dx of the layer forward at x (dy fp32)."""
+    _check(load().moe_backward(ctypes.byref(desc), T, _ptr(x), ctypes.byref(weights.c), _ptr(dy), _ptr(dx),
+                               _ptr(ws), _nbytes(ws), _stream(stream)), "moe_backward")
 
 
 # ---- marshalling helpers ----------------------------------------------------

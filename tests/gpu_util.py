@@ -68,6 +68,15 @@ class GpuLayer:
         torch.cuda.synchronize()
         return y
 
+    def backward(self, dy: np.ndarray) -> np.ndarray:
+        """dx (fp32) for the upstream gradient dy [T][d_model] (fp32)."""
+        ws = torch.empty(moe.moe_backward_workspace_size(self.desc, self.T), dtype=torch.uint8, device=DEV)
+        dyd = torch.from_numpy(np.ascontiguousarray(dy, np.float32)).to(DEV)
+        dx = torch.full((self.T, self.spec.d_model), float("nan"), dtype=torch.float32, device=DEV)
+        moe.moe_backward(self.desc, self.T, self.x, self.w, dyd, dx, ws)
+        torch.cuda.synchronize()
+        return dx.cpu().numpy()
+
     def forward(self, out_dtype=moe.MOE_DT_F32, want_routing=True):
         y = torch.empty((self.T, self.spec.d_model), device=DEV,
                         dtype=_TORCH_DT[out_dtype])

@@ -103,6 +103,22 @@ def test_affine_formats_and_groups(lib):
     assert lib.moe_workspace_size(ctypes.byref(d), 4, ctypes.byref(size)) == moe.MOE_E_INVALID
 
 
+def test_backward_validation(lib):
+    d = good()
+    size = ctypes.c_size_t()
+    assert lib.moe_backward_workspace_size(ctypes.byref(d), 4, ctypes.byref(size)) == moe.MOE_OK
+    fwd = ctypes.c_size_t()
+    lib.moe_workspace_size(ctypes.byref(d), 4, ctypes.byref(fwd))
+    assert size.value > fwd.value
+    w = weights()
+    bad = [(None, A, A), (A, None, A), (A, A, None), (A + 4, A, A)]
+    for x, dy, dx in bad:
+        assert lib.moe_backward(ctypes.byref(d), 4, x, ctypes.byref(w), dy, dx, A, size.value, None) == \
+            moe.MOE_E_INVALID
+    assert lib.moe_backward(ctypes.byref(d), 4, A, ctypes.byref(w), A, A, A, size.value - 1, None) == \
+        moe.MOE_E_WORKSPACE
+
+
 def test_top_k_above_experts_and_rounding_needs_bf16(lib):
     d = moe.make_desc(64, 64, 4, 5, act="f32")
     assert lib.moe_workspace_size(ctypes.byref(d), 1, ctypes.byref(ctypes.c_size_t())) == moe.MOE_E_INVALID

@@ -322,3 +322,38 @@ def test_fp16_range_shifts(T, wfmt, group):
         err = np.abs(y[t] - ry[t])
         c = int(np.argmax(err))
         assert err[c] <= 2e-2 * big, (t, ridx[t], c, err[c], big, y[t][c], ry[t][c])
+
+
+def _backward_check(name, tokens=None):
+    L, g = get(name)
+    spec = L["spec"]
+    dy = inputs._rng(spec.seed, 9).standard_normal((g.T, spec.d_model), dtype=np.float32)
+    dx = g.backward(dy)
+    assert np.all(np.isfinite(dx))
+    sel = np.arange(g.T) if tokens is None else tokens
+    ref, _ = oracle.backward(pins.desc_of(spec), L["x"], L["w_router"], L["router_bias"], L["experts"],
+                             np.ascontiguousarray(dy[sel]), tokens=None if tokens is None else tokens)
+    err = rel_err(dx[sel], ref)
+    print(f"[{name}] backward max|err|/RMS = {err:.3g}", flush=True)
+    assert err <= 1e-4, err
+    # the same call twice gives the same bits
+    assert np.array_equal(g.backward(dy).view(np.uint32), dx.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", list(MID))
+def test_backward_mid(name):
+    """dx against the oracle's backward on every token (fp32 arithmetic on
+    both sides; 1e-4 of RMS(dx))."""
+    _backward_check(name)
+
+
+@pytest.mark.parametrize("name", ["q4-decode-t1", "q4-decode-t32", "q4-prefill-t2048"])
+def test_backward_full_size(name):
+    spec = FULL[name]
+    tokens = None
+    if spec.T > SAMPLE:
+        rng = np.random.default_rng(4321)
+        tokens = np.sort(np.concatenate([[0, spec.T - 1], rng.choice(np.arange(1, spec.T - 1), SAMPLE - 2,
+                                                                       replace=False)])).astype(np.int32)
+    _backward_check(name, tokens)
+
