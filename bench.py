@@ -48,6 +48,7 @@ class Hip:
         self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def event(self):
         e = ctypes.c_void_p()
@@ -58,6 +59,9 @@ class Hip:
         ms = ctypes.c_float()
         assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
         return ms.value
+
+    def record(self, e, stream: int):
+        assert self.lib.hipEventRecord(e, stream) == 0
 
     def destroy(self, e):
         self.lib.hipEventDestroy(e)
@@ -236,6 +240,101 @@ def run_config(name, steps, warmup, use_graph, hip):
     return res
 
 
+def backward_accounting(spec, touched: int):
+    """Algorithmic bytes and FLOPs of one backward pass (input gradient).
+
+    Bytes: the touched experts' weights and the router matrix once each, x and
+    dy read, dx written.  FLOPs: g and u recomputed (4 R D F), v = Wd^T dy
+    (2 R D F), dx rows = Wg^T dg + Wu^T du (4 R D F), router logits recomputed
+    (2 T D E) and the router term of dx (2 T D K with renormalisation, else
+    2 T D E).
+    """
+    T, D, F, E, K, S = spec.T, spec.d_model, spec.d_ff, spec.n_experts, spec.top_k, spec.n_shared
+    esz = 4 if spec.act == "f32" else 2
+    R = T * K + S * T
+    w_touched = (touched + S) * expert_bytes(spec)
+    nbytes = w_touched + D * E * esz + T * D * esz + 2 * T * D * 4
+    flops = 10 * R * D * F + 2 * T * D * E + 2 * T * D * (K if spec.renormalize else E)
+    return {"bytes": nbytes, "flops": flops}
+
+
+def run_backward(name, steps, warmup, hip):
+    """K whole backward passes (moe_backward: router and dispatch recomputed,
+    then the gradient kernels) with rotating weights, x and dy."""
+    import torch
+    from sparse_mixture_experts_amd import inputs, moe
+
+    spec = inputs.workload(name)
+    dev = "cuda:0"
+    host = inputs.gen_layer(spec)
+    desc = moe.desc_from_spec(spec)
+    w0 = moe.DeviceWeights.from_layer(host, dev)
+    n_w = max(1, math.ceil(ROTATE_BYTES / max(1, w0.nbytes())))
+    weights = [w0] + [w0.clone() for _ in range(n_w - 1)]
+    n_x = 4
+    xs = [moe.to_device(inputs.gen_x(spec, i), dev) for i in range(n_x)]
+    gen = torch.Generator(device="cpu").manual_seed(1234)
+    dys = [torch.randn((spec.T, spec.d_model), generator=gen, dtype=torch.float32).to(dev) for _ in range(n_x)]
+    T = spec.T
+    dx = torch.empty((T, spec.d_model), dtype=torch.float32, device=dev)
+    ws = torch.empty(moe.moe_backward_workspace_size(desc, T), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    # experts touched by each x (for the algorithmic byte count): one forward each
+    fws = torch.empty(moe.moe_workspace_size(desc, T), dtype=torch.uint8, device=dev)
+    idx = torch.empty((T, spec.top_k), dtype=torch.int32, device=dev)
+    wt = torch.empty((T, spec.top_k), dtype=torch.float32, device=dev)
+    y = torch.empty((T, spec.d_model), dtype=torch.float32, device=dev)
+    touched = []
+    for i in range(n_x):
+        moe.moe_forward(desc, T, xs[i], weights[0], y, moe.MOE_DT_F32, idx, wt, fws, stream)
+        torch.cuda.synchronize()
+        touched.append(len(np.unique(idx.cpu().numpy())))
+    del fws, y
+
+    def step(i):
+        moe.moe_backward(desc, T, xs[i % n_x], weights[i % n_w], dys[i % n_x], dx, ws, stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    ta = time.perf_counter()
+    hip.record(e0, stream.cuda_stream)
+    for i in range(steps):
+        step(i)
+    hip.record(e1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    tb = time.perf_counter()
+    ms = (tb - ta) * 1000.0 / steps
+    ev_ms = hip.elapsed_ms(e0, e1) / steps
+    hip.destroy(e0)
+    hip.destroy(e1)
+    acc = backward_accounting(spec, round(sum(touched) / n_x))
+    t = ev_ms / 1e3
+    tflops = acc["flops"] / t / 1e12
+    gbs = acc["bytes"] / t / 1e9
+    rows = T * spec.top_k
+    # 16-bit layers: the contractions run on the matrix cores (fp16 and bf16
+    # operands, both 2.5 PFLOP/s dense); fp32 layers on the fp32 vector units
+    mc = spec.act != "f32"
+    peak = MFMA_BF16_PEAK_TFLOPS if mc else VALU_F32_PEAK_TFLOPS
+    log(f"[bwd:{name}] {ms * 1e3:.1f} us/step (events {ev_ms * 1e3:.1f} us), {tflops:.2f} TFLOP/s "
+        f"({100 * tflops / peak:.1f}% of {'MFMA' if mc else 'fp32 VALU'}), {gbs:.0f} GB/s")
+    entry = {
+        "workload": "backward (input gradient) of " + workload_name(spec), "value": round(rows / (ms / 1e3), 1),
+        "unit": "routed rows/s", "tokens_per_s": round(T / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
+        "roofline": {"kernel": "whole backward pass", "bound": "mfma" if mc else "alu",
+                     "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": None, "avg_pass_us": round(ev_ms * 1e3, 2),
+                     "algorithmic_flops": acc["flops"], "algorithmic_bytes": acc["bytes"],
+                     "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
+    }
+    del weights, xs, dys, ws
+    torch.cuda.empty_cache()
+    return entry
+
+
 def path_dtype(spec) -> str:
     """Arithmetic type of the expert contractions (they dominate the step).
 
@@ -380,6 +479,9 @@ def main():
     head = run_config(args.config, args.steps, args.warmup, args.graph, hip)
     sweep = []
     for name in [s for s in args.sweep.split(",") if s]:
+        if name.startswith("bwd:"):
+            sweep.append(run_backward(name[4:], args.steps, args.warmup, hip))
+            continue
         r = run_config(name, args.steps, args.warmup, args.graph, hip)
         sweep.append({
             "workload": workload_name(r["spec"]), "value": round(r["rows_per_s"], 1), "unit": "routed rows/s",

@@ -22,7 +22,8 @@ LIB = os.path.join(PKG, "libmoe_mi355x.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["moe_api.cpp", "moe_validate.cpp", "route.hip", "route_mfma.hip", "dispatch.hip", "ffn_gemv.hip",
-           "ffn_mfma.hip", "combine.hip", "backward.hip"]
+           "ffn_mfma.hip", "combine.hip", "backward.hip",
+           "backward_mfma.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}"]

@@ -13,9 +13,10 @@
 //   dx_t = sum of its slots' dx_r in slot order + shared rows + W_r dl, with
 //   dl the softmax backward of the slot weights from dw            (kernel 5)
 // The forward's per-op rounding is not differentiated (the unrounded GLU).
-// All arithmetic is fp32 on the vector units: each weight element is read
-// where its row or column is reduced (down and gate/up twice), for up to
-// kMR routed rows at a time.
+// fp32 layers run kernels 1-4 here, all arithmetic fp32 on the vector units
+// (each weight element is read where its row or column is reduced, for up to
+// kMR routed rows at a time); 16-bit layers run the matrix-core versions of
+// kernels 1-4 (backward_mfma.hip).  Kernel 5 serves both.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -77,9 +78,11 @@ struct BwdArgs {
   const int32_t *counters;
   const PlanItem *items;
   int T, N, K, D, F, E, S, geglu, renorm;
-  const void *w_router;
+  const void *w_router;   // [D][E]
+  const void *wr_t;       // [E][D] (the router matrix transposed)
   const float *router_bias;
   float *g, *u, *v, *dw, *dxr;
+  int dx_splits;          // partial sums of the rows' dx, [dx_splits][R][D]
   float *dx;
   const int32_t *topk_idx;
 };
@@ -175,17 +178,7 @@ __global__ __launch_bounds__(kThreads) void bwd_glu_kernel(BwdArgs a) {
     const int64_t o = int64_t(r) * a.F + f;
     const float g = a.g[o], u = a.u[o], v = a.v[o];
     float act, dact;  // the gate's activation and its derivative
-    if (a.geglu) {
-      const float ca = 0.7978845608028654f, cb = 0.044715f;
-      const float z = ca * __builtin_fmaf(cb * g, g * g, g);
-      const float th = tanhf(z);
-      act = 0.5f * g * (1.0f + th);
-      dact = 0.5f * (1.0f + th) + 0.5f * g * (1.0f - th * th) * ca * __builtin_fmaf(3.0f * cb, g * g, 1.0f);
-    } else {
-      const float s = 1.0f / (1.0f + expf(-g));
-      act = g * s;
-      dact = s * __builtin_fmaf(g, 1.0f - s, 1.0f);
-    }
+    gate_act_grad(g, a.geglu != 0, act, dact);
     dwp = __builtin_fmaf(act * u, v, dwp);
     const float dh = c * v;
     a.g[o] = dh * u * dact;
@@ -231,11 +224,27 @@ __global__ __launch_bounds__(kThreads) void bwd_gate_up_t_kernel(BwdArgs a) {
   }
 }
 
+// Four consecutive elements of a layer-dtype array as fp32.
+template <int DT>
+__device__ __forceinline__ float4 load4(const void *p, int64_t i) {
+  if constexpr (DT == kDtF32) return *reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i);
+  const uint2 u = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p) + i);
+  return make_float4(half_lo<DT>(u.x), half_hi<DT>(u.x), half_lo<DT>(u.y), half_hi<DT>(u.y));
+}
+__device__ __forceinline__ void add4(float4 &a, const float4 &b) {
+  a.x += b.x;
+  a.y += b.y;
+  a.z += b.z;
+  a.w += b.w;
+}
+
 // 5. Per token: router gradient and the sum over its rows.  With
 // renormalisation the slot weights are the softmax of the selected logits,
 // dl_j = w_j (dw_j - sum_i w_i dw_i); without it they are the softmax over all
 // E logits (recomputed here, fp32, ascending d), dl_e = p_e (dw(e) - sum_j
-// w_j dw_j).  dx_t = its slots' rows (slot order) + shared rows + W_r dl.
+// w_j dw_j).  dx_t = its slots' rows (slot order) + shared rows + W_r dl, four
+// columns per thread and step.  DT: the layer's dtype (kDt*).
+template <int DT>
 __global__ __launch_bounds__(kThreads) void bwd_token_kernel(BwdArgs a) {
   __shared__ float dl[kMaxExperts];  // renormalised: per slot; else per expert
   __shared__ float red[kThreads];
@@ -249,8 +258,7 @@ __global__ __launch_bounds__(kThreads) void bwd_token_kernel(BwdArgs a) {
     for (int e = tid; e < a.E; e += kThreads) {
       float l = 0.f;
       for (int d = 0; d < a.D; ++d)
-        l = __builtin_fmaf(act_load(a.fmt.act_dtype, a.x, int64_t(t) * a.D + d),
-                           act_load(a.fmt.act_dtype, a.w_router, int64_t(d) * a.E + e), l);
+        l = __builtin_fmaf(load_act<DT>(a.x, int64_t(t) * a.D + d), load_act<DT>(a.w_router, int64_t(d) * a.E + e), l);
       dl[e] = a.router_bias ? l + a.router_bias[e] : l;
     }
     float mx = -INFINITY;
@@ -278,29 +286,57 @@ __global__ __launch_bounds__(kThreads) void bwd_token_kernel(BwdArgs a) {
       for (int j = 0; j < a.K; ++j) dl[a.topk_idx[s0 + j]] += a.topk_w[s0 + j] * a.dw[a.inv_order[s0 + j]];
   }
   __syncthreads();
-  for (int k = tid; k < a.D; k += kThreads) {
-    float acc = 0.f;
-    for (int j = 0; j < a.K; ++j) acc += a.dxr[int64_t(a.inv_order[s0 + j]) * a.D + k];
-    for (int s = 0; s < a.S; ++s) acc += a.dxr[(int64_t(a.N) + int64_t(s) * a.T + t) * a.D + k];
-    float rg = 0.f;
+  const int64_t R = int64_t(a.N) + int64_t(a.S) * a.T, split = R * a.D;
+  for (int k = 4 * tid; k < a.D; k += 4 * kThreads) {
+    auto row_dx = [&](int64_t r) {  // one row's dx: its split partials in split order
+      const float *p = a.dxr + r * a.D + k;
+      float4 v = *reinterpret_cast<const float4 *>(p);
+      for (int z = 1; z < a.dx_splits; ++z) add4(v, *reinterpret_cast<const float4 *>(p + z * split));
+      return v;
+    };
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+    for (int j = 0; j < a.K; ++j) add4(acc, row_dx(a.inv_order[s0 + j]));
+    for (int s = 0; s < a.S; ++s) add4(acc, row_dx(int64_t(a.N) + int64_t(s) * a.T + t));
+    float4 rg = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto router_row = [&](int e, float c) {  // rg += c * (row e of W_r^T)
+      const float4 w = load4<DT>(a.wr_t, int64_t(e) * a.D + k);
+      rg.x = __builtin_fmaf(w.x, c, rg.x);
+      rg.y = __builtin_fmaf(w.y, c, rg.y);
+      rg.z = __builtin_fmaf(w.z, c, rg.z);
+      rg.w = __builtin_fmaf(w.w, c, rg.w);
+    };
     if (a.renorm) {
-      for (int j = 0; j < a.K; ++j)
-        rg = __builtin_fmaf(act_load(a.fmt.act_dtype, a.w_router, int64_t(k) * a.E + a.topk_idx[s0 + j]), dl[j],
-                            rg);
+#pragma unroll 4
+      for (int j = 0; j < a.K; ++j) router_row(a.topk_idx[s0 + j], dl[j]);
     } else {
-      for (int e = 0; e < a.E; ++e)
-        rg = __builtin_fmaf(act_load(a.fmt.act_dtype, a.w_router, int64_t(k) * a.E + e), dl[e], rg);
+      for (int e = 0; e < a.E; ++e) router_row(e, dl[e]);
     }
-    a.dx[int64_t(t) * a.D + k] = acc + rg;
+    add4(acc, rg);
+    *reinterpret_cast<float4 *>(a.dx + int64_t(t) * a.D + k) = acc;
   }
+}
+
+// The router matrix [D][E] transposed to [E][D] through 32x32 LDS tiles
+// (ESZ-byte elements), so that the per-token kernel reads its rows whole.
+template <typename Elt>
+__global__ __launch_bounds__(256) void transpose_kernel(const Elt *src, int rows, int cols, Elt *dst) {
+  __shared__ Elt tile[32][33];
+  const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+  const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;
+  for (int i = ty; i < 32; i += 8)
+    if (r0 + i < rows && c0 + tx < cols) tile[i][tx] = src[int64_t(r0 + i) * cols + c0 + tx];
+  __syncthreads();
+  for (int i = ty; i < 32; i += 8)
+    if (c0 + i < cols && r0 + tx < rows) dst[int64_t(c0 + i) * rows + r0 + tx] = tile[tx][i];
 }
 
 }  // namespace
 
 void launch_backward(const moe_layer_desc *d, int32_t T, const void *x, const moe_weights *w, const float *dy,
                      const int32_t *topk_idx, const float *topk_w, const int32_t *order, const int32_t *inv_order,
-                     const int32_t *row_map, const int32_t *counters, const PlanItem *items, const BwdScratch &sc,
-                     float *dx, void *stream) {
+                     const int32_t *row_map, const int32_t *counters, const PlanItem *items, const PlanItem *tiles,
+                     int64_t max_tiles, const BwdScratch &sc, float *dx, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int D = d->d_model, F = d->d_ff, E = d->n_experts, S = d->n_shared, K = d->top_k;
   const int N = T * K, R = N + S * T;
@@ -312,17 +348,32 @@ void launch_backward(const moe_layer_desc *d, int32_t T, const void *x, const mo
     return WView{p.w, static_cast<const uint16_t *>(p.scales), static_cast<const uint16_t *>(p.biases), n, k,
                  row_off, nre};
   };
+  const BwdSplits sp = backward_splits(d, T);
   BwdArgs a{WFormat{d->act_dtype, bits, d->group_size},
             view(pg, F, D, 0, fused ? 2 * F : F), view(pu, F, D, fused ? F : 0, fused ? 2 * F : F),
             view(w->down, D, F, 0, D), x, dy, row_map, order, inv_order, topk_w, counters, items,
-            T, N, K, D, F, E, S, d->activation == MOE_ACT_GEGLU, d->renormalize, w->w_router, w->router_bias,
-            sc.g, sc.u, sc.v, sc.dw, sc.dxr, dx, topk_idx};
-  hipLaunchKernelGGL(bwd_gate_up_kernel, dim3((F + 15) / 16, max_items), dim3(kThreads), 0, s, a);
-  hipLaunchKernelGGL(bwd_down_t_kernel, dim3((F + kThreads - 1) / kThreads, max_items), dim3(kThreads), 0, s, a);
-  hipLaunchKernelGGL(bwd_glu_kernel, dim3(R), dim3(kThreads), 0, s, a);
-  hipLaunchKernelGGL(bwd_gate_up_t_kernel, dim3((D + kThreads - 1) / kThreads, max_items), dim3(kThreads), 0, s,
-                     a);
-  hipLaunchKernelGGL(bwd_token_kernel, dim3(T), dim3(kThreads), 0, s, a);
+            T, N, K, D, F, E, S, d->activation == MOE_ACT_GEGLU, d->renormalize, w->w_router, sc.wr_t,
+            w->router_bias, sc.gu, sc.gu + int64_t(R) * F, sc.v, sc.dw, sc.dxr, sp.dx, dx, topk_idx};
+  const dim3 tgrid((E + 31) / 32, (D + 31) / 32);
+  if (d->act_dtype == MOE_DT_F32)
+    hipLaunchKernelGGL(transpose_kernel<float>, tgrid, dim3(256), 0, s, static_cast<const float *>(w->w_router), D,
+                       E, static_cast<float *>(sc.wr_t));
+  else
+    hipLaunchKernelGGL(transpose_kernel<uint16_t>, tgrid, dim3(256), 0, s,
+                       static_cast<const uint16_t *>(w->w_router), D, E, static_cast<uint16_t *>(sc.wr_t));
+  if (use_mfma(d)) {
+    launch_backward_mfma(d, T, x, w, dy, topk_w, order, row_map, counters, tiles, max_tiles, sc, stream);
+  } else {
+    hipLaunchKernelGGL(bwd_gate_up_kernel, dim3((F + 15) / 16, max_items), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(bwd_down_t_kernel, dim3((F + kThreads - 1) / kThreads, max_items), dim3(kThreads), 0, s,
+                       a);
+    hipLaunchKernelGGL(bwd_glu_kernel, dim3(R), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(bwd_gate_up_t_kernel, dim3((D + kThreads - 1) / kThreads, max_items), dim3(kThreads), 0,
+                       s, a);
+  }
+  if (d->act_dtype == MOE_DT_F32) hipLaunchKernelGGL(bwd_token_kernel<kDtF32>, dim3(T), dim3(kThreads), 0, s, a);
+  else if (d->act_dtype == MOE_DT_F16) hipLaunchKernelGGL(bwd_token_kernel<kDtF16>, dim3(T), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(bwd_token_kernel<kDtBF16>, dim3(T), dim3(kThreads), 0, s, a);
 }
 
 }  // namespace moe

@@ -172,4 +172,22 @@ __device__ __forceinline__ float glu(float g, float u, bool round_ops, bool gegl
   return round_bf16(a * u);
 }
 
+
+// The gate's activation a(g) and its derivative a'(g), fp32 with the
+// library's expf / tanhf: SiLU, a = g s with s = sigmoid(g), a' = s (1 + g (1 - s));
+// tanh-GELU, a = g (1 + th) / 2 with th = tanh(z), z = c (g + 0.044715 g^3),
+// a' = (1 + th) / 2 + g (1 - th^2) c (1 + 3 * 0.044715 g^2) / 2, c = sqrt(2/pi).
+__device__ __forceinline__ void gate_act_grad(float g, bool geglu, float &act, float &dact) {
+  if (geglu) {
+    const float ca = 0.7978845608028654f, cb = 0.044715f;
+    const float th = tanhf(ca * __builtin_fmaf(cb * g, g * g, g));
+    act = 0.5f * g * (1.0f + th);
+    dact = 0.5f * (1.0f + th) + 0.5f * g * (1.0f - th * th) * ca * __builtin_fmaf(3.0f * cb, g * g, 1.0f);
+  } else {
+    const float s = 1.0f / (1.0f + expf(-g));
+    act = g * s;
+    dact = s * __builtin_fmaf(g, 1.0f - s, 1.0f);
+  }
+}
+
 }  // namespace moe

@@ -925,6 +925,20 @@ int plan_tile_rows(const moe_layer_desc *d, int32_t T) {
   return N <= 8LL * d->n_experts ? 16 : 64;
 }
 
+void launch_projection_mfma(const moe_layer_desc *d, int32_t T, const void *act, const int8_t *act_sh, int K,
+                            int n_out, const moe_proj &p, const int32_t *counters, const PlanItem *tiles,
+                            int64_t max_tiles, float *out, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool aff = affine(d);
+  const bool f16 = d->act_dtype == MOE_DT_F16;
+  const int qb = d->w_format == MOE_WF_AFFINE_Q8 ? 8 : aff ? 4 : f16 ? kDenseF16 : kDenseBF16;
+  GemmArgs g{act, act_sh, nullptr, (K + kHBlock - 1) / kHBlock, nullptr, T, T * d->top_k, K, n_out, 0, 0, 0,
+             int(f16), p.w, static_cast<const uint16_t *>(p.scales), static_cast<const uint16_t *>(p.biases),
+             nullptr, nullptr, nullptr, counters, tiles, out, 0};
+  if (plan_tile_rows(d, T) == 16) launch_gemm<false, 1>(g, qb, d->group_size, max_tiles, s);
+  else launch_gemm<false, 4>(g, qb, d->group_size, max_tiles, s);
+}
+
 void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
                             const moe_weights *w, const int32_t *counters, const PlanItem *tiles,
                             int64_t max_tiles, const FfnScratch &sc, void *y_sorted, bool ys_bf16, void *stream,

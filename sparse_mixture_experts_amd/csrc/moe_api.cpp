@@ -227,11 +227,12 @@ int moe_backward(const moe_layer_desc *desc, int32_t T, const void *x, const moe
                   at<int32_t>(ws, L.row_map), at<int32_t>(ws, L.expert_off), at<int32_t>(ws, L.tile_off),
                   at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles),
                   at<int32_t>(ws, L.dsp), stream);
-  const BwdScratch sc{at<float>(ws, B.g), at<float>(ws, B.u), at<float>(ws, B.v), at<float>(ws, B.dw),
-                      at<float>(ws, B.dxr)};
+  const BwdScratch sc{at<float>(ws, B.gu),  at<float>(ws, B.v),     at<float>(ws, B.dw),
+                      at<float>(ws, B.dxr), at<void>(ws, B.xs),     at<int8_t>(ws, B.xsh),
+                      at<uint16_t>(ws, B.dgu), at<void>(ws, B.wr_t)};
   launch_backward(desc, T, x, w, dy, idx, wt, at<int32_t>(ws, L.order), at<int32_t>(ws, L.inv_order),
-                  at<int32_t>(ws, L.row_map), at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items), sc, dx,
-                  stream);
+                  at<int32_t>(ws, L.row_map), at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items),
+                  at<PlanItem>(ws, L.tiles), L.max_tiles, sc, dx, stream);
   return hip_status();
 }
 

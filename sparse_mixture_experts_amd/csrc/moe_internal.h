@@ -130,20 +130,47 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
                             int64_t max_tiles, const FfnScratch &sc, void *y_sorted, bool ys_bf16, void *stream,
                             StageMarker *mk);
 
-// Backward with respect to x (fp32 intermediates in the backward workspace):
-// g and u [R][F] (then dg and du), v = Wd^T dy [R][F], dw [R], dx rows [R][D].
+// Backward with respect to x.  Intermediates in the backward workspace (R
+// sorted rows): g and u, v = Wd^T dy (per reduction split), dw, the rows'
+// dx (per split); the matrix-core path adds the gathered x rows, dg | du as
+// bf16, and the router matrix transposed for the per-token kernel.
 struct BwdScratch {
-  float *g, *u, *v, *dw, *dxr;
+  float *gu;      // [R][2F] g | u per row (fused gate/up on the matrix cores), else g [R][F] then u [R][F]
+  float *v;       // [splits.v][R][F]
+  float *dw;      // [R]
+  float *dxr;     // [splits.dx][R][D]
+  void *xs;       // matrix-core path: x of the sorted rows [R][D], 16-bit
+  int8_t *xsh;    // matrix-core path, affine layers: [R][ceil(D/128)] exponents
+  uint16_t *dgu;  // matrix-core path: [R][2F] bf16, dg then du
+  void *wr_t;     // router matrix transposed [E][D] (layer dtype)
 };
+// Reduction splits of the matrix-core backward's transposed products (the
+// partial sums are added in split order by their consumers).
+struct BwdSplits {
+  int v, dx;
+};
+BwdSplits backward_splits(const moe_layer_desc *d, int32_t T);
 struct BwdWorkspace {
   Workspace fwd;  // router and dispatch sections (the forward's layout)
-  size_t g, u, v, dw, dxr, total;
+  size_t gu, v, dw, dxr, xs, xsh, dgu, wr_t, total;
 };
 BwdWorkspace backward_workspace_layout(const moe_layer_desc *d, int32_t T);
 void launch_backward(const moe_layer_desc *d, int32_t T, const void *x, const moe_weights *w, const float *dy,
                      const int32_t *topk_idx, const float *topk_w, const int32_t *order, const int32_t *inv_order,
-                     const int32_t *row_map, const int32_t *counters, const PlanItem *items, const BwdScratch &sc,
-                     float *dx, void *stream);
+                     const int32_t *row_map, const int32_t *counters, const PlanItem *items, const PlanItem *tiles,
+                     int64_t max_tiles, const BwdScratch &sc, float *dx, void *stream);
+// Matrix-core part of the backward (16-bit layers): sc.dw and sc.dxr.
+void launch_backward_mfma(const moe_layer_desc *d, int32_t T, const void *x, const moe_weights *w, const float *dy,
+                          const float *topk_w, const int32_t *order, const int32_t *row_map,
+                          const int32_t *counters, const PlanItem *tiles, int64_t max_tiles, const BwdScratch &sc,
+                          void *stream);
+// The grouped GEMM of the down projection as a plain projection of sorted
+// rows: out[r][n] (fp32, row stride n_out) = sum_k act[r][k] W[n][k] for the
+// rows of the plan's tiles, act in the GEMM's activation format (fp16 with
+// one exponent per (row, 128 columns) on affine layers, else the layer dtype).
+void launch_projection_mfma(const moe_layer_desc *d, int32_t T, const void *act, const int8_t *act_sh, int K,
+                            int n_out, const moe_proj &p, const int32_t *counters, const PlanItem *tiles,
+                            int64_t max_tiles, float *out, void *stream);
 
 // Combine.
 void launch_combine(const moe_layer_desc *d, int32_t T, const void *y_sorted, bool ys_bf16,

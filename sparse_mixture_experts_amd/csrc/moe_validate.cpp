@@ -119,17 +119,22 @@ BwdWorkspace backward_workspace_layout(const moe_layer_desc *d, int32_t T) {
   BwdWorkspace b{};
   b.fwd = workspace_layout(d, T);
   const int64_t rows = int64_t(T) * d->top_k + int64_t(d->n_shared) * T;
+  const BwdSplits sp = backward_splits(d, T);
+  const bool mc = use_mfma(d);
   size_t o = b.fwd.total;
   auto take = [&](size_t bytes) {
     size_t at = o;
     o = align_up(o + bytes);
     return at;
   };
-  b.g = take(size_t(rows) * d->d_ff * 4);
-  b.u = take(size_t(rows) * d->d_ff * 4);
-  b.v = take(size_t(rows) * d->d_ff * 4);
+  b.gu = take(size_t(rows) * 2 * d->d_ff * 4);
+  b.v = take(size_t(sp.v) * rows * d->d_ff * 4);
   b.dw = take(size_t(rows) * 4);
-  b.dxr = take(size_t(rows) * d->d_model * 4);
+  b.dxr = take(size_t(sp.dx) * rows * d->d_model * 4);
+  b.xs = take(mc ? size_t(rows) * d->d_model * 2 : 0);
+  b.xsh = take(mc ? size_t(rows) * ((d->d_model + kHBlock - 1) / kHBlock) : 0);
+  b.dgu = take(mc ? size_t(rows) * 2 * d->d_ff * 2 : 0);
+  b.wr_t = take(size_t(d->n_experts) * d->d_model * act_bytes(d));
   b.total = o;
   return b;
 }

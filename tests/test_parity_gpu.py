@@ -334,16 +334,24 @@ def _backward_check(name, tokens=None):
     ref, _ = oracle.backward(pins.desc_of(spec), L["x"], L["w_router"], L["router_bias"], L["experts"],
                              np.ascontiguousarray(dy[sel]), tokens=None if tokens is None else tokens)
     err = rel_err(dx[sel], ref)
-    print(f"[{name}] backward max|err|/RMS = {err:.3g}", flush=True)
-    assert err <= 1e-4, err
+    rms_err = float(np.sqrt(np.mean((dx[sel].astype(np.float64) - ref) ** 2) / np.mean(ref.astype(np.float64) ** 2)))
+    print(f"[{name}] backward max|err|/RMS = {err:.3g}, RMS err / RMS = {rms_err:.3g}", flush=True)
+    if spec.act == "f32":
+        # fp32 arithmetic on both sides
+        assert err <= 1e-4, err
+    else:
+        # bf16 operands (unit roundoff 2^-8) in the three transposed and GLU
+        # products: about 3.5e-3 relative RMS error predicted, 5 sigma at most
+        assert rms_err <= 1e-2, rms_err
+        assert err <= 5e-2, err
     # the same call twice gives the same bits
     assert np.array_equal(g.backward(dy).view(np.uint32), dx.view(np.uint32))
 
 
 @pytest.mark.parametrize("name", list(MID))
 def test_backward_mid(name):
-    """dx against the oracle's backward on every token (fp32 arithmetic on
-    both sides; 1e-4 of RMS(dx))."""
+    """dx against the oracle's backward on every token (fp32 layers: fp32
+    arithmetic, 1e-4 of RMS(dx); 16-bit layers: bf16 matrix-core operands)."""
     _backward_check(name)
 
 
