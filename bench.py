@@ -7,8 +7,9 @@ A step is one whole layer forward (router, dispatch, expert FFN, combine)
 through the C ABI (moe_forward) over one batch of synthetic input that is
 already resident in HBM.  The headline workload is the 2048-token prefill
 chunk (T=2048, d_model=2048, d_ff=512, E=512, top-10, affine 4-bit g64, fused
-gate|up); the decode layer at T=1 and T=32 is measured in the same run and
-reported under "sweep".  Weight copies and x copies rotate from step to step
+gate|up); the decode layer at T=1 and T=32, and the backward pass with respect
+to x (moe_backward) of all three, are measured in the same run and reported
+under "sweep".  Weight copies and x copies rotate from step to step
 so that the bytes between two reuses of the same buffer exceed the 256 MB
 Infinity Cache: every step streams its weights from HBM.
 
@@ -452,7 +453,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="q4-prefill-t2048")
-    ap.add_argument("--sweep", default="q4-decode-t1,q4-decode-t32")
+    ap.add_argument("--sweep", default="q4-decode-t1,q4-decode-t32,bwd:q4-decode-t1,bwd:q4-decode-t32,"
+                                       "bwd:q4-prefill-t2048",
+                    help="further workloads; a bwd: prefix times the backward pass (moe_backward) instead")
     ap.add_argument("--graph", action="store_true", help="replay captured HIP graphs in the timed loop")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of the headline workload the oracle runs for cpu_baseline (default: all)")

@@ -222,8 +222,12 @@ int moe_forward_timed(const moe_layer_desc *desc, int32_t T, const void *x,
  * choice: through the selected experts (scaled by their weights), the shared
  * experts, and the softmax (renormalised or not) that gives the slot weights,
  * then W_router.  The forward's per-op rounding is not differentiated.  The
- * router and dispatch run again inside.  ws: moe_backward_workspace_size
- * bytes (caller-owned, 16-byte aligned).  Errors as for moe_forward.
+ * router and dispatch run again inside.  fp32 layers compute in fp32 on the
+ * vector units; 16-bit layers run the contractions on the matrix cores (the
+ * gate/up recomputation as in the forward, the transposed products with
+ * bf16 operands and fp32 accumulation).  Repeated calls give identical bits.
+ * ws: moe_backward_workspace_size bytes (caller-owned, 16-byte aligned).
+ * Errors as for moe_forward.
  */
 int moe_backward_workspace_size(const moe_layer_desc *desc, int32_t T, size_t *bytes);
 int moe_backward(const moe_layer_desc *desc, int32_t T, const void *x,
