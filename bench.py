@@ -68,14 +68,14 @@ class Hip:
         self.lib.hipEventDestroy(e)
 
 
-def workload_name(spec) -> str:
+def workload_name(spec, what: str = "forward") -> str:
     w = f"affine {spec.bits}-bit g{spec.group_size}" if spec.quantized else f"dense {spec.act}"
     extra = (", fused gate|up" if spec.gate_up_fused else "") + (
         ", GeGLU (tanh-GELU gate)" if spec.activation == "geglu" else "") + (
         ", per-op bf16 GLU rounding" if spec.swiglu_round_bf16 else "") + (
         f", {spec.n_shared} shared experts" if spec.n_shared else "") + (
         ", Zipf-skewed router bias" if spec.router_bias == "zipf" else "")
-    return (f"{spec.name}: MoE layer forward T={spec.T} d_model={spec.d_model} d_ff={spec.d_ff} "
+    return (f"{spec.name}: MoE layer {what} T={spec.T} d_model={spec.d_model} d_ff={spec.d_ff} "
             f"E={spec.n_experts} top-{spec.top_k}, {spec.act} activations, {w} experts{extra}")
 
 
@@ -317,19 +317,27 @@ def run_backward(name, steps, warmup, hip):
     gbs = acc["bytes"] / t / 1e9
     rows = T * spec.top_k
     # 16-bit layers: the contractions run on the matrix cores (fp16 and bf16
-    # operands, both 2.5 PFLOP/s dense); fp32 layers on the fp32 vector units
+    # operands, both 2.5 PFLOP/s dense); fp32 layers on the fp32 vector units.
+    # The roofline is whichever of compute and HBM bytes takes longer at peak.
     mc = spec.act != "f32"
-    peak = MFMA_BF16_PEAK_TFLOPS if mc else VALU_F32_PEAK_TFLOPS
+    fpeak = MFMA_BF16_PEAK_TFLOPS if mc else VALU_F32_PEAK_TFLOPS
+    t_flop, t_hbm = acc["flops"] / (fpeak * 1e12), acc["bytes"] / (HBM_PEAK_GBS * 1e9)
+    if t_hbm >= t_flop:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma" if mc else "alu", "achieved": round(tflops, 3), "peak": fpeak, "unit": "TFLOP/s",
+                "frac": round(tflops / fpeak, 4)}
     log(f"[bwd:{name}] {ms * 1e3:.1f} us/step (events {ev_ms * 1e3:.1f} us), {tflops:.2f} TFLOP/s "
-        f"({100 * tflops / peak:.1f}% of {'MFMA' if mc else 'fp32 VALU'}), {gbs:.0f} GB/s")
+        f"({100 * tflops / fpeak:.1f}% of {'MFMA' if mc else 'fp32 VALU'}), {gbs:.0f} GB/s "
+        f"({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM)")
     entry = {
-        "workload": "backward (input gradient) of " + workload_name(spec), "value": round(rows / (ms / 1e3), 1),
+        "workload": workload_name(spec, "backward (dx)"), "value": round(rows / (ms / 1e3), 1),
         "unit": "routed rows/s", "tokens_per_s": round(T / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
-        "roofline": {"kernel": "whole backward pass", "bound": "mfma" if mc else "alu",
-                     "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": None, "avg_pass_us": round(ev_ms * 1e3, 2),
-                     "algorithmic_flops": acc["flops"], "algorithmic_bytes": acc["bytes"],
-                     "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
+        "roofline": {"kernel": "whole backward pass", **roof, "traffic": None,
+                     "avg_pass_us": round(ev_ms * 1e3, 2), "algorithmic_flops": acc["flops"],
+                     "algorithmic_bytes": acc["bytes"], "flop_frac": round(tflops / fpeak, 4),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
     }
     del weights, xs, dys, ws
     torch.cuda.empty_cache()

@@ -13,16 +13,16 @@
 // Transposed use.  The stored matrices keep the forward's reduction dimension
 // contiguous (codes packed and quantised in groups along a row), so v and
 // dx_r reduce over the stored row index.  A workgroup owns one plan tile (up
-// to 16*RB rows of one expert), 128 output columns (stored columns) and a
-// range of the reduction.  Per slab of 64 reduction rows the 256 threads load
-// the codes, dequantise them in fp32 (s*q + b), round to bf16 and write each
-// pair of consecutive reduction rows of one column as one dword, so LDS holds
-// [32 row pairs][128 columns]; an MFMA operand (8 consecutive reduction rows
-// of one column) is then four dword reads.  The activations (dy gathered by
-// token and rounded to bf16, or the bf16 dg|du rows) are staged as
-// [rows][64].  v_mfma_f32_16x16x32_bf16 takes 16 weight columns as operand A
-// and 16 rows as operand B; fp32 accumulation.  bf16 operands keep every
-// value in range without exponent bookkeeping (dy is arbitrary fp32).
+// to 16*RB rows of one expert), 256 output columns (stored columns, 64 per
+// wave) and a range of the reduction.  Each lane loads, straight into
+// registers, the words of eight consecutive reduction rows that hold its
+// columns, and builds from them operand A of v_mfma_f32_16x16x32_bf16 one
+// column at a time: eight values of one column, dequantised in fp32
+// (s*q + b) and rounded to bf16 (see tgemm_kernel for the lane mapping).
+// The activations (dy gathered by token and rounded to bf16, or the bf16
+// dg|du rows) are staged in LDS as [rows][64] and read as operand B; fp32
+// accumulation.  bf16 operands keep every value in range without exponent
+// bookkeeping (dy is arbitrary fp32).
 //
 // Small row counts split the reduction over several workgroups; each split
 // writes its own partial sums and the consumers (the GLU kernel for v, the
@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "f16_stage.h"
@@ -45,11 +46,10 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kTN = 128;              // output columns per workgroup
-constexpr int kTK = 64;               // reduction rows per slab
-constexpr int kPairs = kTK / 2;       // LDS row pairs per slab
-constexpr int kPairStride = kTN + 4;  // dwords per LDS pair row: the four lane groups of a read hit different banks
-constexpr int kARow = kTK + 8;        // bf16 elements per LDS activation row
+constexpr int kWaveCols = 64;                        // output columns per wave
+constexpr int kTN = kThreads / kWave * kWaveCols;    // output columns per workgroup (256)
+constexpr int kTK = 64;                              // reduction rows per activation slab (two k-blocks of 32)
+constexpr int kARow = kTK + 8;                       // bf16 elements per LDS activation row
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   const f32x2 v = {lo, hi};
@@ -104,18 +104,28 @@ struct TArgs {
 // QB: 4 or 8 (affine codes) or 16 (dense 16-bit weights).  RB: 16-row blocks
 // per tile.  ASRC: activation source (see TArgs::act).  HF: scales/biases or
 // dense weights are fp16 (else bf16).
+//
+// A wave owns 64 output columns and computes them as four MFMA column sets
+// of 16.  Lane (m = lane % 16, lg = lane / 16) loads, for each k-block of 32
+// reduction rows, the 32-bit word (dword for dense weights) of rows
+// 8*lg .. 8*lg+7 that holds its columns, and column set s takes from each of
+// those words the value of one column:
+//   4-bit: word m % 8 of the wave, nibble 4*(m / 8) + s   (column 8*(m%8) + 4*(m/8) + s)
+//   8-bit: word m, byte s                                  (column 4*m + s)
+//   dense: dword m + 16*(s/2), half s % 2                  (column 2*(m + 16*(s/2)) + s%2)
+// so every lane's operand A of set s is the eight values of one column for
+// its eight rows, dequantised in fp32 and rounded to bf16, with no transpose
+// through LDS.  (For 4-bit codes lanes m and m + 8 load the same word and
+// use its two halves.)  The activations of the tile are staged in LDS per
+// slab of 64 reduction rows and read as operand B.
 template <int QB, int RB, int ASRC, bool HF>
-__global__ __launch_bounds__(kThreads) void tgemm_kernel(TArgs a) {
+__device__ __forceinline__ void tgemm_body(const TArgs &a) {
   constexpr bool AFF = QB != 16;
-  constexpr int VPW = 32 / QB;         // values per 32-bit word (8, 4, 2)
-  constexpr int WPR = kTN / VPW;       // words per slab row and column block (16, 32, 64)
-  constexpr int PPP = kThreads / WPR;  // row pairs per staging pass (16, 8, 4)
-  constexpr int NPASS = kPairs / PPP;  // staging passes (2, 4, 8)
-  constexpr int PPR = kTK / 8;         // 8-element activation pieces per row (8)
-  constexpr int RPP = kThreads / PPR;  // activation rows per staging pass (32)
+  constexpr int VPW = 32 / QB;   // values per 32-bit word (8, 4, 2)
+  constexpr int NWL = AFF ? 1 : 2;  // distinct words per row and lane
+  constexpr int PPR = kTK / 8;    // 8-element activation pieces per row and slab
+  constexpr int RPP = kThreads / PPR;
   constexpr int APASS = (RB * 16 + RPP - 1) / RPP;
-  static_assert(kThreads % WPR == 0 && kPairs % PPP == 0, "weight staging covers the slab");
-  __shared__ uint32_t bt[2][kPairs * kPairStride];
   __shared__ uint16_t as[2][RB * 16 * kARow];
 
   // XCD-aware order: consecutive linear ids go to the 8 XCDs in turn; the
@@ -136,102 +146,78 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(TArgs a) {
   const int ncb = (a.n_cols + kTN - 1) / kTN;
   const int tile_id = item / nbx, bx = item % nbx;
   const int cb = bx % ncb, z = bx / ncb;
-  const PlanItem tile = a.tiles[tile_id];
-  const int n0 = cb * kTN;
+  PlanItem tile = a.tiles[tile_id];
+  // uniform across the workgroup: kept in scalar registers
+  tile.expert = __builtin_amdgcn_readfirstlane(tile.expert);
+  tile.row0 = __builtin_amdgcn_readfirstlane(tile.row0);
+  tile.rows = __builtin_amdgcn_readfirstlane(tile.rows);
   const int ks = a.K / a.ksplit;  // whole slabs (the host picks the split)
-  const int k_begin = z * ks, nsl = ks / kTK;
+  const int k_begin = z * ks, nsl = ks / kTK, nkb = ks / 32;
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
   const int lr = lane & 15, lg = lane >> 4;
+  const int wc0 = cb * kTN + wave * kWaveCols;  // first column of this wave
 
-  // Weight staging role: word column wc of the block, row pairs pr + i*PPP
-  // of every slab.  Per matrix, this thread's word (and scale pair) of row 0
-  // of the slab; a slab adds its first row, a pass 2*PPP rows.
-  const int wc = tid % WPR, pr = tid / WPR;
-  const int wpr_row = a.n_cols / VPW;                 // words per stored row
-  const int wcol = min(n0 / VPW + wc, wpr_row - 1);   // clamped (columns past n_cols are never stored)
+  // this lane's word column(s) and bit shift per column set
+  const int wpr_row = a.n_cols / VPW;  // words per stored row
+  int wcol[NWL];
+  if constexpr (QB == 4) wcol[0] = wc0 / 8 + (lr & 7);
+  else if constexpr (QB == 8) wcol[0] = wc0 / 4 + lr;
+  else {
+    wcol[0] = wc0 / 2 + lr;
+    wcol[1] = wc0 / 2 + lr + 16;
+  }
+#pragma unroll
+  for (int v = 0; v < NWL; ++v) wcol[v] = min(wcol[v], wpr_row - 1);  // columns past n_cols are never stored
+  const int half_sel = QB == 4 ? 16 * (lr >> 3) : 0;  // 4-bit: this lane's half of the word
   const int ngrp = AFF ? a.n_cols / a.group : 1;
-  const int grp = AFF ? wcol * VPW / a.group : 0;
+  const int grp = AFF ? wcol[0] * VPW / a.group : 0;
+  // Addresses: a base common to the workgroup (the expert's matrix, or its
+  // scale rows) plus 32-bit per-lane offsets, so that the loads take the
+  // scalar-base form.
   const uint32_t *wbase[2];
   const uint32_t *sbase[2], *bbase[2];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    wbase[m] = static_cast<const uint32_t *>(a.w[m]) + (int64_t(tile.expert) * a.nre[m] + 2 * pr) * wpr_row + wcol;
+  for (int mt = 0; mt < 2; ++mt) {
+    wbase[mt] = static_cast<const uint32_t *>(a.w[mt]) + int64_t(tile.expert) * a.nre[mt] * wpr_row;
     if constexpr (AFF) {
-      const int64_t si = (int64_t(tile.expert) * ngrp + grp) * a.nre[m] + 2 * pr;
-      sbase[m] = reinterpret_cast<const uint32_t *>(a.sc[m] + si);  // (row, row + 1) scale pair
-      bbase[m] = reinterpret_cast<const uint32_t *>(a.bi[m] + si);
+      sbase[mt] = reinterpret_cast<const uint32_t *>(a.sc[mt] + int64_t(tile.expert) * ngrp * a.nre[mt]);
+      bbase[mt] = reinterpret_cast<const uint32_t *>(a.bi[mt] + int64_t(tile.expert) * ngrp * a.nre[mt]);
     }
   }
-  const int pass_w = 2 * PPP * wpr_row;
-
-  uint32_t wr[NPASS][2];
-  uint32_t sr[NPASS], br[NPASS];
-  auto load_w = [&](int slab) {
-    const int k = k_begin + slab * kTK;  // the slab lies in one matrix (k_second is a multiple of kTK)
-    const int m = k >= a.k_second ? 1 : 0;
-    const int row = k - (m ? a.k_second : 0);
-    const uint32_t *wp = (m ? wbase[1] : wbase[0]) + row * wpr_row;
+  uint32_t woff[NWL];  // byte offset of this lane's word in row 8*lg
 #pragma unroll
-    for (int i = 0; i < NPASS; ++i) {
-      wr[i][0] = wp[i * pass_w];
-      wr[i][1] = wp[i * pass_w + wpr_row];
-    }
-    if constexpr (AFF) {
-      const uint32_t *sp = (m ? sbase[1] : sbase[0]) + row / 2;
-      const uint32_t *bp = (m ? bbase[1] : bbase[0]) + row / 2;
+  for (int v = 0; v < NWL; ++v) woff[v] = uint32_t(8 * lg * wpr_row + wcol[v]) * 4u;
+  // byte offset of the scale pair (rows 8*lg, 8*lg + 1) of this lane's group, per matrix
+  uint32_t soff[2];
 #pragma unroll
-      for (int i = 0; i < NPASS; ++i) {
-        sr[i] = sp[i * PPP];
-        br[i] = bp[i * PPP];
-      }
-    }
+  for (int mt = 0; mt < 2; ++mt) soff[mt] = uint32_t(grp * a.nre[mt] + 8 * lg) * 2u;
+  auto ld = [](const void *base, uint32_t byte_off) {
+    return *reinterpret_cast<const uint32_t *>(static_cast<const char *>(base) + byte_off);
   };
-  auto write_w = [&](uint32_t *dst) {
+
+  // One k-block's weights in registers: eight rows' words and four
+  // (row, row + 1) scale and bias pairs.
+  struct WBlock {
+    uint32_t w[8][NWL];
+    uint32_t s[4], b[4];
+  };
+  auto load_block = [&](int kb, WBlock &wb) {
+    const int k = k_begin + 32 * kb;  // a k-block lies in one matrix (k_second is a multiple of 64)
+    const int mt = k >= a.k_second ? 1 : 0;
+    const int row = k - (mt ? a.k_second : 0);
+    const uint32_t *wp = (mt ? wbase[1] : wbase[0]) + row * wpr_row;  // uniform
 #pragma unroll
-    for (int i = 0; i < NPASS; ++i) {
-      uint32_t o[VPW];
-      if constexpr (AFF) {
-        const float s0 = HF ? f16_lo(sr[i]) : bf16_lo(sr[i]), s1 = HF ? f16_hi(sr[i]) : bf16_hi(sr[i]);
-        const float b0 = HF ? f16_lo(br[i]) : bf16_lo(br[i]), b1 = HF ? f16_hi(br[i]) : bf16_hi(br[i]);
-        float q0[VPW], q1[VPW];
-        if constexpr (QB == 4) {
-          // even codes in the low nibbles of the four bytes, odd codes in the
-          // high ones: eight byte-to-float conversions per word
-          uint32_t e0 = wr[i][0] & 0x0f0f0f0fu, o0 = (wr[i][0] >> 4) & 0x0f0f0f0fu;
-          uint32_t e1 = wr[i][1] & 0x0f0f0f0fu, o1 = (wr[i][1] >> 4) & 0x0f0f0f0fu;
-          asm volatile("" : "+v"(e0), "+v"(o0), "+v"(e1), "+v"(o1));  // keep whole-byte conversions
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            q0[2 * b] = float((e0 >> (8 * b)) & 0xffu);
-            q0[2 * b + 1] = float((o0 >> (8 * b)) & 0xffu);
-            q1[2 * b] = float((e1 >> (8 * b)) & 0xffu);
-            q1[2 * b + 1] = float((o1 >> (8 * b)) & 0xffu);
-          }
-        } else {
+      for (int v = 0; v < NWL; ++v) wb.w[i][v] = ld(wp + i * wpr_row, woff[v]);
+    if constexpr (AFF) {
+      const uint32_t *sp = (mt ? sbase[1] : sbase[0]) + row / 2, *bp = (mt ? bbase[1] : bbase[0]) + row / 2;
+      const uint32_t so = mt ? soff[1] : soff[0];
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            q0[b] = float((wr[i][0] >> (8 * b)) & 0xffu);
-            q1[b] = float((wr[i][1] >> (8 * b)) & 0xffu);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < VPW; ++j) o[j] = pack_bf16(__builtin_fmaf(s0, q0[j], b0), __builtin_fmaf(s1, q1[j], b1));
-      } else if constexpr (HF) {
-        o[0] = pack_bf16(f16_lo(wr[i][0]), f16_lo(wr[i][1]));
-        o[1] = pack_bf16(f16_hi(wr[i][0]), f16_hi(wr[i][1]));
-      } else {
-        o[0] = (wr[i][0] & 0xffffu) | (wr[i][1] << 16);
-        o[1] = (wr[i][0] >> 16) | (wr[i][1] & 0xffff0000u);
-      }
-      uint32_t *d = dst + (pr + i * PPP) * kPairStride + wc * VPW;
-      if constexpr (VPW == 8) {
-        reinterpret_cast<uint4 *>(d)[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        reinterpret_cast<uint4 *>(d)[1] = make_uint4(o[4], o[5], o[6], o[7]);
-      } else if constexpr (VPW == 4) {
-        *reinterpret_cast<uint4 *>(d) = make_uint4(o[0], o[1], o[2], o[3]);
-      } else {
-        *reinterpret_cast<uint2 *>(d) = make_uint2(o[0], o[1]);
+      for (int p = 0; p < 4; ++p) {
+        wb.s[p] = ld(sp + p, so);
+        wb.b[p] = ld(bp + p, so);
       }
     }
   };
@@ -249,32 +235,34 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(TArgs a) {
     if constexpr (ASRC == 0) src = q < a.N ? a.row_map[q] : (q - a.N) % a.T;
     aoff[i] = int64_t(src) * a.K + pc * 8;
   }
-  float4 af[APASS][2];
-  uint4 ab[APASS];
-  auto load_a = [&](int slab) {
+  struct AStage {
+    float4 f[APASS][2];
+    uint4 h[APASS];
+  };
+  auto load_a = [&](int slab, AStage &st) {
     const int k = k_begin + slab * kTK;
 #pragma unroll
     for (int i = 0; i < APASS; ++i) {
       if constexpr (ASRC == 0) {
         const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(a.act) + aoff[i] + k);
-        af[i][0] = p[0];
-        af[i][1] = p[1];
+        st.f[i][0] = p[0];
+        st.f[i][1] = p[1];
       } else {
-        ab[i] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.act) + aoff[i] + k);
+        st.h[i] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.act) + aoff[i] + k);
       }
     }
   };
-  auto write_a = [&](uint16_t *dst) {
+  auto write_a = [&](const AStage &st, uint16_t *dst) {
 #pragma unroll
     for (int i = 0; i < APASS; ++i) {
       const int m = rr + i * RPP;
       if (m < RB * 16) {
         uint4 v;
         if constexpr (ASRC == 0) {
-          v = make_uint4(pack_bf16(af[i][0].x, af[i][0].y), pack_bf16(af[i][0].z, af[i][0].w),
-                         pack_bf16(af[i][1].x, af[i][1].y), pack_bf16(af[i][1].z, af[i][1].w));
+          v = make_uint4(pack_bf16(st.f[i][0].x, st.f[i][0].y), pack_bf16(st.f[i][0].z, st.f[i][0].w),
+                         pack_bf16(st.f[i][1].x, st.f[i][1].y), pack_bf16(st.f[i][1].z, st.f[i][1].w));
         } else {
-          v = ab[i];
+          v = st.h[i];
         }
         if (!aok[i]) v = make_uint4(0u, 0u, 0u, 0u);
         *reinterpret_cast<uint4 *>(dst + m * kARow + pc * 8) = v;
@@ -282,74 +270,139 @@ __global__ __launch_bounds__(kThreads) void tgemm_kernel(TArgs a) {
     }
   };
 
-  f32x4 acc[2][RB];
+  f32x4 acc[4][RB];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct)
+  for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) acc[ct][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < RB; ++rb) acc[s2][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int cw = wave * 32 + lr;  // this lane's operand-A column (plus 16 for the second tile)
-  auto compute = [&](const uint32_t *bsl, const uint16_t *asl) {
+  // One k-block: operand B of every row block from LDS, then per column set
+  // the dequantised operand A and its MFMAs.
+  auto compute = [&](const WBlock &wb, const uint16_t *asl, int kbl, auto nrb_tag) {
+    constexpr int NRB = decltype(nrb_tag)::value;
+    uint4 xv[NRB];
 #pragma unroll
-    for (int j = 0; j < kTK / 32; ++j) {
-      bf16x8 wa[2];
+    for (int rb = 0; rb < NRB; ++rb)
+      xv[rb] = *reinterpret_cast<const uint4 *>(asl + (rb * 16 + lr) * kARow + 32 * kbl + 8 * lg);
+    float sv[8], bv[8];
+    if constexpr (AFF) {
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const uint32_t *p = bsl + (16 * j + 4 * lg) * kPairStride + cw + 16 * ct;
-        const uint4 v = make_uint4(p[0], p[kPairStride], p[2 * kPairStride], p[3 * kPairStride]);
-        wa[ct] = __builtin_bit_cast(bf16x8, v);
+      for (int p = 0; p < 4; ++p) {
+        sv[2 * p] = HF ? f16_lo(wb.s[p]) : bf16_lo(wb.s[p]);
+        sv[2 * p + 1] = HF ? f16_hi(wb.s[p]) : bf16_hi(wb.s[p]);
+        bv[2 * p] = HF ? f16_lo(wb.b[p]) : bf16_lo(wb.b[p]);
+        bv[2 * p + 1] = HF ? f16_hi(wb.b[p]) : bf16_hi(wb.b[p]);
       }
+    }
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        if (rb * 16 < tile.rows) {  // uniform
-          const uint4 v = *reinterpret_cast<const uint4 *>(asl + (rb * 16 + lr) * kARow + 32 * j + 8 * lg);
-          const bf16x8 xb = __builtin_bit_cast(bf16x8, v);
+    for (int st = 0; st < 4; ++st) {
+      uint32_t o[4];
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct)
-            acc[ct][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ct], xb, acc[ct][rb], 0, 0, 0);
+      for (int p = 0; p < 4; ++p) {
+        if constexpr (QB == 4) {
+          const int sh = half_sel + 4 * st;
+          const float q0 = float((wb.w[2 * p][0] >> sh) & 15u), q1 = float((wb.w[2 * p + 1][0] >> sh) & 15u);
+          o[p] = pack_bf16(__builtin_fmaf(sv[2 * p], q0, bv[2 * p]), __builtin_fmaf(sv[2 * p + 1], q1, bv[2 * p + 1]));
+        } else if constexpr (QB == 8) {
+          const float q0 = float((wb.w[2 * p][0] >> (8 * st)) & 255u);
+          const float q1 = float((wb.w[2 * p + 1][0] >> (8 * st)) & 255u);
+          o[p] = pack_bf16(__builtin_fmaf(sv[2 * p], q0, bv[2 * p]), __builtin_fmaf(sv[2 * p + 1], q1, bv[2 * p + 1]));
+        } else {
+          const uint32_t w0 = wb.w[2 * p][st >> 1], w1 = wb.w[2 * p + 1][st >> 1];
+          if constexpr (HF) {
+            o[p] = (st & 1) ? pack_bf16(f16_hi(w0), f16_hi(w1)) : pack_bf16(f16_lo(w0), f16_lo(w1));
+          } else {
+            o[p] = (st & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u)) : ((w0 & 0xffffu) | (w1 << 16));
+          }
         }
       }
+      const bf16x8 wa = __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+        acc[st][rb] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, xv[rb]), acc[st][rb], 0, 0, 0);
     }
   };
 
-  // Double buffer: slab i is multiplied from LDS while slab i+1 waits in
-  // registers to be written to the other buffer and slab i+2 is in flight.
-  load_w(0);
-  load_a(0);
-  write_w(bt[0]);
-  write_a(as[0]);
-  if (nsl > 1) {
-    load_w(1);
-    load_a(1);
-  }
-  __syncthreads();
-  for (int i = 0; i < nsl; ++i) {
-    compute(bt[i & 1], as[i & 1]);
-    if (i + 1 < nsl) {
-      write_w(bt[(i + 1) & 1]);
-      write_a(as[(i + 1) & 1]);
-    }
-    if (i + 2 < nsl) {
-      load_w(i + 2);
-      load_a(i + 2);
-    }
+  // Activations: two LDS buffers, one slab (two k-blocks) ahead in
+  // registers.  Weights: a ring of four k-block register sets, loaded two
+  // k-blocks ahead of their use (loads past the end repeat the last block).
+  // The loop runs for the number of row blocks that hold rows (NRB), so the
+  // MFMAs carry no branches.
+  auto run = [&](auto nrb_tag) {
+    WBlock wb[4];
+    AStage ast;
+    load_block(0, wb[0]);
+    load_block(min(1, nkb - 1), wb[1]);
+    load_a(0, ast);
+    write_a(ast, as[0]);
+    if (nsl > 1) load_a(1, ast);
     __syncthreads();
+    for (int i = 0; i < nsl; i += 2) {
+      // slab i in buffer 0: k-blocks 2i, 2i+1 in wb[0], wb[1]
+      load_block(min(2 * i + 2, nkb - 1), wb[2]);
+      compute(wb[0], as[0], 0, nrb_tag);
+      load_block(min(2 * i + 3, nkb - 1), wb[3]);
+      compute(wb[1], as[0], 1, nrb_tag);
+      if (i + 1 < nsl) write_a(ast, as[1]);
+      if (i + 2 < nsl) load_a(i + 2, ast);
+      __syncthreads();
+      if (i + 1 >= nsl) break;
+      // slab i+1 in buffer 1: k-blocks 2i+2, 2i+3 in wb[2], wb[3]
+      load_block(min(2 * i + 4, nkb - 1), wb[0]);
+      compute(wb[2], as[1], 0, nrb_tag);
+      load_block(min(2 * i + 5, nkb - 1), wb[1]);
+      compute(wb[3], as[1], 1, nrb_tag);
+      if (i + 2 < nsl) write_a(ast, as[0]);
+      if (i + 3 < nsl) load_a(i + 3, ast);
+      __syncthreads();
+    }
+  };
+  if constexpr (RB == 4) {
+    const int nrb = (tile.rows + 15) / 16;
+    if (nrb >= 4) run(std::integral_constant<int, 4>{});
+    else if (nrb == 3) run(std::integral_constant<int, 3>{});
+    else if (nrb == 2) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 1>{});
+  } else {
+    run(std::integral_constant<int, RB>{});
   }
 
-  // lane holds outputs n = column + 4*lg + e (e = 0..3) of tile row rb*16 + lr
+  // Lane holds, per column set st and row block rb, outputs of tile row
+  // rb*16 + lr at the columns of A rows m' = 4*lg + e (e = 0..3).
   float *out = a.out + int64_t(z) * a.split_stride;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int m = rb * 16 + lr;
     if (m >= tile.rows) continue;
+    float *orow = out + int64_t(tile.row0 + m) * a.n_cols;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const int n = n0 + wave * 32 + 16 * ct + 4 * lg;
-      if (n < a.n_cols)
-        *reinterpret_cast<float4 *>(out + int64_t(tile.row0 + m) * a.n_cols + n) =
-            make_float4(acc[ct][rb][0], acc[ct][rb][1], acc[ct][rb][2], acc[ct][rb][3]);
+    for (int e = 0; e < 4; ++e) {
+      const int mp = 4 * lg + e;
+      if constexpr (QB == 4 || QB == 8) {
+        const int c = wc0 + (QB == 4 ? 8 * (mp & 7) + 4 * (mp >> 3) : 4 * mp);
+        if (c < a.n_cols)
+          *reinterpret_cast<float4 *>(orow + c) = make_float4(acc[0][rb][e], acc[1][rb][e], acc[2][rb][e], acc[3][rb][e]);
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int c = wc0 + 2 * (mp + 16 * h);
+          if (c < a.n_cols) *reinterpret_cast<float2 *>(orow + c) = make_float2(acc[2 * h][rb][e], acc[2 * h + 1][rb][e]);
+        }
+      }
     }
   }
+}
+
+// 64-row tiles ask for two waves per SIMD (the register budget of the
+// accumulators and the weight ring); 16-row tiles allocate on their own.
+template <int QB, int RB, int ASRC, bool HF>
+__global__ __launch_bounds__(kThreads) void tgemm_kernel(TArgs a) {
+  tgemm_body<QB, RB, ASRC, HF>(a);
+}
+template <int QB, int RB, int ASRC, bool HF>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void tgemm_kernel_w2(TArgs a) {
+  tgemm_body<QB, RB, ASRC, HF>(a);
 }
 
 // ---- GLU backward per sorted row ---------------------------------------------
@@ -392,8 +445,13 @@ __global__ __launch_bounds__(256) void glu_bf16_kernel(GluArgs a) {
 template <int QB, int RB, bool HF>
 void launch_t_src(const TArgs &t, int asrc, int64_t max_tiles, hipStream_t s) {
   const dim3 grid(unsigned(((t.n_cols + kTN - 1) / kTN) * t.ksplit), unsigned(max_tiles));
-  if (asrc == 0) hipLaunchKernelGGL((tgemm_kernel<QB, RB, 0, HF>), grid, dim3(kThreads), 0, s, t);
-  else hipLaunchKernelGGL((tgemm_kernel<QB, RB, 1, HF>), grid, dim3(kThreads), 0, s, t);
+  if constexpr (RB == 1) {
+    if (asrc == 0) hipLaunchKernelGGL((tgemm_kernel<QB, RB, 0, HF>), grid, dim3(kThreads), 0, s, t);
+    else hipLaunchKernelGGL((tgemm_kernel<QB, RB, 1, HF>), grid, dim3(kThreads), 0, s, t);
+  } else {
+    if (asrc == 0) hipLaunchKernelGGL((tgemm_kernel_w2<QB, RB, 0, HF>), grid, dim3(kThreads), 0, s, t);
+    else hipLaunchKernelGGL((tgemm_kernel_w2<QB, RB, 1, HF>), grid, dim3(kThreads), 0, s, t);
+  }
 }
 template <int QB, int RB>
 void launch_t_hf(const TArgs &t, int asrc, int64_t max_tiles, hipStream_t s) {
