@@ -9,7 +9,10 @@
 //      contiguous rows) and the per-expert squared norms are formed;
 //   2. L~ = x . W + bias on the bf16 matrix cores (exact bf16 products, fp32
 //      sums: two MFMAs per 64-column chunk from zero, chunk results added in
-//      fp32);
+//      fp32).  fp16 layers split every value exactly into a bf16 head and a
+//      bf16 tail (fp16's 11 significant bits fit in two bf16 parts, and
+//      bf16's exponent range holds fp16's subnormals) and take all four
+//      head/tail products, so L~ is again a sum of exact products;
 //   3. per token, with B = gamma * ||x_t|| * max_e ||W_e|| + gamma * max|bias|
 //      a bound on |L~ - L| for every expert (Cauchy-Schwarz bounds the sum of
 //      |x_i W_ie|; gamma covers the rounding of both summation orders), every
@@ -31,7 +34,27 @@ namespace moe {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+// Eight fp16 values -> head and tail bf16 vectors with head + tail exact.
+__device__ __forceinline__ void f16x8_split(uint4 v, bf16x8 &hd, bf16x8 &tl) {
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  uint32_t h[4], t[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float a = f16_lo(u[p]), b = f16_hi(u[p]);
+    h[p] = pack_bf16(a, b);
+    t[p] = pack_bf16(a - bf16_lo(h[p]), b - bf16_hi(h[p]));
+  }
+  hd = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+  tl = __builtin_bit_cast(bf16x8, make_uint4(t[0], t[1], t[2], t[3]));
+}
 
 constexpr int kThreads = 256;
 constexpr int kChunk = 64;
@@ -41,6 +64,7 @@ constexpr int kMaxCand = 64;
 // ---- 1. transpose W [d][E] -> WT [E][d] and squared-norm partials ---------
 // Block (eb, kb): experts eb*64.., columns kb*256..; normp[kb][e] = sum of
 // squares of W[kb*256 .. +256][e].
+template <int DT>
 __global__ __launch_bounds__(kThreads) void router_transpose_kernel(const uint16_t *__restrict__ w, int D, int E,
                                                                     uint16_t *__restrict__ wt,
                                                                     float *__restrict__ normp) {
@@ -74,8 +98,8 @@ __global__ __launch_bounds__(kThreads) void router_transpose_kernel(const uint16
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     const uint4 v = *reinterpret_cast<const uint4 *>(&tile[el][q * 64 + c * 8]);
-    const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                        bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    const float f[8] = {half_lo<DT>(v.x), half_hi<DT>(v.x), half_lo<DT>(v.y), half_hi<DT>(v.y),
+                        half_lo<DT>(v.z), half_hi<DT>(v.z), half_lo<DT>(v.w), half_hi<DT>(v.w)};
 #pragma unroll
     for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(f[i], f[i], ss);
     const int k = k0 + q * 64 + c * 8;
@@ -94,6 +118,7 @@ __global__ __launch_bounds__(kThreads) void router_transpose_kernel(const uint16
 // their 64 experts: normp[n_kb][e] -> normp[n_kb + 0 * E + e] (the row after
 // the partials).
 constexpr int kMfThreads = 512;
+template <int DT>
 __global__ __launch_bounds__(kMfThreads) void router_mfma_kernel(const uint16_t *__restrict__ x,
                                                                  const uint16_t *__restrict__ wt,
                                                                  const float *__restrict__ bias,
@@ -144,20 +169,46 @@ __global__ __launch_bounds__(kMfThreads) void router_mfma_kernel(const uint16_t 
   // buffer, whose last readers (chunk c-1) are past the previous barrier, and
   // chunk c+3 into nx.
   auto step = [&](int c, int buf, Stage &nx) __attribute__((always_inline)) {
-    bf16x8 av[2][2], bv[2];
+    if constexpr (DT == kDtBF16) {
+      bf16x8 av[2][2], bv[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          av[i][j] = *reinterpret_cast<const bf16x8 *>(&sab[buf][0][we * 32 + i * 16 + lr][lg * 16 + j * 8]);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        av[i][j] = *reinterpret_cast<const bf16x8 *>(&sab[buf][0][we * 32 + i * 16 + lr][lg * 16 + j * 8]);
+        bv[j] = *reinterpret_cast<const bf16x8 *>(&sab[buf][1][wtk * 16 + lr][lg * 16 + j * 8]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      bv[j] = *reinterpret_cast<const bf16x8 *>(&sab[buf][1][wtk * 16 + lr][lg * 16 + j * 8]);
+      for (int i = 0; i < 2; ++i) {
+        f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i][0], bv[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i][1], bv[1], d, 0, 0, 0);
+        acc[i] += d;
+      }
+    } else {
+      // fp16: head/tail split of both operands, four products per pair
+      bf16x8 ah[2][2], at[2][2], bh[2], bt[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i][0], bv[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i][1], bv[1], d, 0, 0, 0);
-      acc[i] += d;
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          f16x8_split(*reinterpret_cast<const uint4 *>(&sab[buf][0][we * 32 + i * 16 + lr][lg * 16 + j * 8]),
+                      ah[i][j], at[i][j]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        f16x8_split(*reinterpret_cast<const uint4 *>(&sab[buf][1][wtk * 16 + lr][lg * 16 + j * 8]), bh[j], bt[j]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i][j], bh[j], d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i][j], bt[j], d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(at[i][j], bh[j], d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(at[i][j], bt[j], d, 0, 0, 0);
+        }
+        acc[i] += d;
+      }
     }
     store(buf ^ 1, nx);
     load(c + 3, nx);
@@ -193,7 +244,7 @@ struct CertArgs {
 };
 
 // One wave per token; each lane keeps L~ of experts lane + 64*m, m < MPL.
-template <int MPL>
+template <int MPL, int DT>
 __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
   constexpr int kNW = kThreads / kWave;
   constexpr int kBatch = 32;  // candidates recomputed per batch
@@ -222,15 +273,15 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
     for (int q = 0; q < 8; ++q) {
       if ((q * kWave + lane) * 8 < D) {
         const uint4 v = xr.v[q];
-        const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                            bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+        const float f[8] = {half_lo<DT>(v.x), half_hi<DT>(v.x), half_lo<DT>(v.y), half_hi<DT>(v.y),
+                            half_lo<DT>(v.z), half_hi<DT>(v.z), half_lo<DT>(v.w), half_hi<DT>(v.w)};
 #pragma unroll
         for (int i = 0; i < 8; ++i) xs = __builtin_fmaf(f[i], f[i], xs);
       }
     }
   }
   xs = wave_sum(xs);
-  if (a.x16) row_f16_store(xr, D, a.x16 + int64_t(t) * D, a.xsh + t, false);  // xr dies here (bf16 x)
+  if (a.x16) row_f16_store(xr, D, a.x16 + int64_t(t) * D, a.xsh + t, DT == kDtF16);  // xr dies here
   float wn = 0.f, bmax = 0.f;
 #pragma unroll
   for (int m = 0; m < MPL; ++m) {
@@ -285,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
   const int slots = kWave / C;
   const int slot = lane / C, ch = lane % C;
   const bool lane_on = slot < slots;
-  uint32_t xw[32];  // this lane's x chunk as packed bf16 (64 values)
+  uint32_t xw[32];  // this lane's x chunk as packed 16-bit values (64)
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const uint4 v = *reinterpret_cast<const uint4 *>(a.x + int64_t(t) * D + ch * kChunk + q * 8);
@@ -305,8 +356,8 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
       const uint32_t wv4[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        part = __builtin_fmaf(bf16_lo(xw[4 * q + h]), bf16_lo(wv4[h]), part);
-        part = __builtin_fmaf(bf16_hi(xw[4 * q + h]), bf16_hi(wv4[h]), part);
+        part = __builtin_fmaf(half_lo<DT>(xw[4 * q + h]), half_lo<DT>(wv4[h]), part);
+        part = __builtin_fmaf(half_hi<DT>(xw[4 * q + h]), half_hi<DT>(wv4[h]), part);
       }
     }
     return part;
@@ -378,11 +429,11 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
 }  // namespace
 
 bool route_mfma_applies(const moe_layer_desc *d, int32_t T) {
-  return d->act_dtype == MOE_DT_BF16 && d->renormalize && d->d_model % kChunk == 0 &&
+  return d->act_dtype != MOE_DT_F32 && d->renormalize && d->d_model % kChunk == 0 &&
          d->d_model <= kWave * kChunk && T >= 64;
 }
 
-// Scratch: L~ [T][E] f32, then WT [E][D] bf16, then norm partials [D/256][E]
+// Scratch: L~ [T][E] f32, then WT [E][D] (16-bit), then norm partials [D/256][E]
 // f32, each part starting on a 16-byte boundary (offsets in floats).
 static int64_t align4(int64_t v) { return (v + 3) & ~int64_t(3); }
 
@@ -391,33 +442,48 @@ int64_t route_mfma_scratch_floats(const moe_layer_desc *d, int32_t T) {
   return align4(int64_t(T) * E) + align4((E * D + 1) / 2) + (nkb + 1) * E;
 }
 
-void launch_route_mfma(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router, const float *bias,
-                       int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh, void *stream,
-                       StageMarker *mk) {
-  hipStream_t s = static_cast<hipStream_t>(stream);
+namespace {
+template <int DT>
+void launch_route_mfma_t(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router, const float *bias,
+                         int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh, hipStream_t s,
+                         StageMarker *mk) {
   const int D = d->d_model, E = d->n_experts, nkb = (D + 255) / 256, C = D / kChunk;
   float *lt = scratch;
   const int64_t o_wt = align4(int64_t(T) * E), o_np = o_wt + align4((int64_t(E) * D + 1) / 2);
   uint16_t *wt = reinterpret_cast<uint16_t *>(scratch + o_wt);
   float *normp = scratch + o_np;
-  hipLaunchKernelGGL(router_transpose_kernel, dim3((E + 63) / 64, nkb), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL(router_transpose_kernel<DT>, dim3((E + 63) / 64, nkb), dim3(kThreads), 0, s,
                      static_cast<const uint16_t *>(w_router), D, E, wt, normp);
-  hipLaunchKernelGGL(router_mfma_kernel, dim3((E + 63) / 64, (T + 63) / 64), dim3(kMfThreads), 0, s,
+  hipLaunchKernelGGL(router_mfma_kernel<DT>, dim3((E + 63) / 64, (T + 63) / 64), dim3(kMfThreads), 0, s,
                      static_cast<const uint16_t *>(x), wt, bias, normp, nkb, T, D, E, lt);
   if (mk) mk->mark("route_mfma");
-  // |L~ - L| <= gamma * S: two MFMAs per chunk counted as 128 sequential
-  // roundings, C chunk additions, and the fixed order's 64 + C + 1 roundings,
-  // with a margin: (256 + 2C) units of 2^-24.
-  const float gamma = float(256 + 2 * C) * 5.9604645e-8f;
+  // |L~ - L| <= gamma * S: the MFMAs of a chunk counted as 32 sequential
+  // roundings each (two per chunk for bf16, eight for the fp16 head/tail
+  // products), C chunk additions, and the fixed order's 64 + C + 1
+  // roundings, with a margin: (256 + 2C) units of 2^-24 for bf16, (384 + 2C)
+  // for fp16.
+  const float gamma = float((DT == kDtF16 ? 384 : 256) + 2 * C) * 5.9604645e-8f;
   CertArgs ca{static_cast<const uint16_t *>(x), wt, bias, lt, normp + int64_t(nkb) * E, T, D, E, d->top_k, gamma,
               idx, w, static_cast<uint16_t *>(x16), xsh};
   const dim3 grid((T + kThreads / kWave - 1) / (kThreads / kWave)), block(kThreads);
-  if (E <= 64) hipLaunchKernelGGL(router_certify_kernel<1>, grid, block, 0, s, ca);
-  else if (E <= 128) hipLaunchKernelGGL(router_certify_kernel<2>, grid, block, 0, s, ca);
-  else if (E <= 256) hipLaunchKernelGGL(router_certify_kernel<4>, grid, block, 0, s, ca);
-  else if (E <= 512) hipLaunchKernelGGL(router_certify_kernel<8>, grid, block, 0, s, ca);
-  else hipLaunchKernelGGL(router_certify_kernel<16>, grid, block, 0, s, ca);
+  if (E <= 64) hipLaunchKernelGGL((router_certify_kernel<1, DT>), grid, block, 0, s, ca);
+  else if (E <= 128) hipLaunchKernelGGL((router_certify_kernel<2, DT>), grid, block, 0, s, ca);
+  else if (E <= 256) hipLaunchKernelGGL((router_certify_kernel<4, DT>), grid, block, 0, s, ca);
+  else if (E <= 512) hipLaunchKernelGGL((router_certify_kernel<8, DT>), grid, block, 0, s, ca);
+  else hipLaunchKernelGGL((router_certify_kernel<16, DT>), grid, block, 0, s, ca);
   if (mk) mk->mark("route_certify");
+}
+
+}  // namespace
+
+void launch_route_mfma(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router, const float *bias,
+                       int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh, void *stream,
+                       StageMarker *mk) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d->act_dtype == MOE_DT_F16)
+    launch_route_mfma_t<kDtF16>(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, s, mk);
+  else
+    launch_route_mfma_t<kDtBF16>(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, s, mk);
 }
 
 }  // namespace moe

@@ -271,11 +271,15 @@ def test_zero_input_gives_zero_output():
     _layers.clear()  # the cached device layer no longer holds the generated x
 
 
+@pytest.mark.parametrize("act", ["bf16", "f16"])
 @pytest.mark.parametrize("T", [9, 96])
-def test_route_exact_ties_and_zero_rows(T):
+def test_route_exact_ties_and_zero_rows(T, act):
     """Duplicated router columns tie exactly and zero rows tie everywhere: the
-    lower expert index must win, on both the small-T and the large-T router."""
-    spec = LayerSpec("ties", T=T, d_model=256, d_ff=64, n_experts=16, top_k=4, seed=31)
+    lower expert index must win, on both the small-T and the large-T router.
+    fp16 layers also get rows of fp16 subnormals (x * 2^-20) and rows near
+    fp16's largest values (x * 2^12), which the large-T router splits into
+    bf16 head and tail parts."""
+    spec = LayerSpec("ties", T=T, d_model=256, d_ff=64, n_experts=16, top_k=4, act=act, seed=31)
     L = inputs.gen_layer(spec)
     w = L["w_router"].copy()
     w[:, 5] = w[:, 2]
@@ -283,6 +287,10 @@ def test_route_exact_ties_and_zero_rows(T):
     w[:, 15] = w[:, 0]
     L["w_router"] = w
     x = L["x"].copy()
+    if act == "f16":
+        xf = inputs.f16_bits_to_f32(x)
+        x[3::7] = inputs.to_f16_bits(xf[3::7] * np.float32(2.0 ** -20))
+        x[5::7] = inputs.to_f16_bits(xf[5::7] * np.float32(2.0 ** 12))
     x[::7] = 0  # every 7th token: all logits 0
     L["x"] = x
     g = GpuLayer(L)
