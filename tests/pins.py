@@ -75,6 +75,8 @@ SMALL = {
                                act="f16", wfmt="q4", router_bias="zipf", seed=24),
     "f16-q8-g32-fused": LayerSpec("f16-q8-g32-fused", T=6, d_model=128, d_ff=64, n_experts=4, top_k=2,
                                   act="f16", wfmt="q8", group_size=32, gate_up_fused=True, seed=25),
+    "f32-fused-shared": LayerSpec("f32-fused-shared", T=5, d_model=96, d_ff=40, n_experts=4, top_k=2, n_shared=1,
+                                  act="f32", gate_up_fused=True, seed=26),
 }
 
 _cache: dict = {}

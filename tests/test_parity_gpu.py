@@ -85,6 +85,12 @@ MID = {
                                    n_shared=1, act="f16", wfmt="q4", router_bias="zipf", seed=45),
     "mid-f16-q4-tile16-fused": LayerSpec("mid-f16-q4-tile16-fused", T=40, d_model=256, d_ff=192, n_experts=32,
                                          top_k=4, act="f16", wfmt="q4", gate_up_fused=True, seed=46),
+    # fused gate|up on the vector-unit kernels: fp32, and bf16 with a d_model
+    # that is not a multiple of 64
+    "mid-f32-fused-shared": LayerSpec("mid-f32-fused-shared", T=23, d_model=96, d_ff=80, n_experts=6, top_k=2,
+                                      n_shared=1, act="f32", gate_up_fused=True, x_scale="fan_in", seed=48),
+    "mid-bf16-gemv-fused": LayerSpec("mid-bf16-gemv-fused", T=30, d_model=96, d_ff=72, n_experts=5, top_k=2,
+                                     gate_up_fused=True, activation="geglu", seed=49),
     "mid-f16-q8-decode-geglu": LayerSpec("mid-f16-q8-decode-geglu", T=3, d_model=512, d_ff=256, n_experts=64,
                                          top_k=8, act="f16", wfmt="q8", group_size=128, activation="geglu",
                                          seed=47),
@@ -363,8 +369,10 @@ def test_backward_mid(name):
     _backward_check(name)
 
 
-@pytest.mark.parametrize("name", ["q4-decode-t1", "q4-decode-t32", "q4-prefill-t2048"])
+@pytest.mark.parametrize("name", list(FULL))
 def test_backward_full_size(name):
+    """dx at every workload's full size, in the launch configuration the
+    benchmark times (48 sampled tokens where T is larger)."""
     spec = FULL[name]
     tokens = None
     if spec.T > SAMPLE:
