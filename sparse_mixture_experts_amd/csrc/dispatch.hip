@@ -434,14 +434,15 @@ __global__ __launch_bounds__(kMbThreads) void dispatch_rank_kernel(
   seg_rank(f, sg, K, E, cw + w * E, order, inv_order, row_map);
 }
 
-// At most 128 slots: one wave does it all.
+// At most 64*SPL slots: one wave does it all.
+template <int SPL>
 __global__ __launch_bounds__(kWave) void dispatch_tiny_kernel(
     const int32_t *__restrict__ f, int N, int K, int E, int S, int T, int tile_rows, int tr, int32_t *order,
     int32_t *inv_order, int32_t *row_map, int32_t *expert_off, int32_t *tile_off, int32_t *counters,
     PlanItem *act_items, PlanItem *tiles) {
   __shared__ int32_t cnt[kMaxExperts];
-  tiny_dispatch(f, N, K, E, S, T, tile_rows, tr, order, inv_order, row_map, expert_off, tile_off, counters,
-                act_items, tiles, cnt);
+  tiny_dispatch<SPL>(f, N, K, E, S, T, tile_rows, tr, order, inv_order, row_map, expert_off, tile_off, counters,
+                     act_items, tiles, cnt);
 }
 
 __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *__restrict__ expert_off,
@@ -480,8 +481,13 @@ void launch_dispatch(const moe_layer_desc *d, int32_t T, const int32_t *idx, int
   const int tr = plan_tile_rows(d, T);
   const int E = d->n_experts, N = T * d->top_k;
   if (N <= kTinyMaxN) {
-    hipLaunchKernelGGL(dispatch_tiny_kernel, dim3(1), dim3(kWave), 0, s, idx, N, d->top_k, E, d->n_shared, T,
-                       tile_rows, tr, order, inv_order, row_map, expert_off, tile_off, counters, act_items, tiles);
+    auto tiny = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(1), dim3(kWave), 0, s, idx, N, d->top_k, E, d->n_shared, T, tile_rows, tr, order,
+                         inv_order, row_map, expert_off, tile_off, counters, act_items, tiles);
+    };
+    if (N <= 2 * kWave) tiny(dispatch_tiny_kernel<2>);
+    else if (N <= 4 * kWave) tiny(dispatch_tiny_kernel<4>);
+    else tiny(dispatch_tiny_kernel<8>);
   } else if (N <= kSingleBlockMax) {
     const int nw = kThreads / 64;
     const size_t lds = size_t(nw * E + 5 * E) * sizeof(int32_t);

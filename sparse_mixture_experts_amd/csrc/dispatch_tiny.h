@@ -2,11 +2,11 @@
 //
 // The same outputs as the workgroup dispatch (DS4Server issue #112, "Current
 // upstream route": order, inv_order, row_map; "Kernel contract": per-expert
-// row and tile prefix tables; plus the internal work plan) for N <= 128 flat
-// slots, computed by a single wave so that no workgroup barrier or second
-// kernel is needed: used by the dispatch entry point for small N and by the
-// router's selection kernel when every token of the call is in one
-// workgroup (decode).
+// row and tile prefix tables; plus the internal work plan) for N <= 64*SPL
+// flat slots (SPL slots per lane, at most 8), computed by a single wave so
+// that no workgroup barrier or second kernel is needed: used by the dispatch
+// entry point for small N and by the router's selection kernel when every
+// token of the call is in one workgroup (decode).
 #pragma once
 
 #include "device_common.h"
@@ -14,18 +14,26 @@
 
 namespace moe {
 
-constexpr int kTinyMaxN = 2 * kWave;
+constexpr int kTinyMaxN = 8 * kWave;        // the dispatch entry point's one-wave path
+constexpr int kTinyFusedMaxN = 2 * kWave;   // dispatch inside the router's selection kernel
 
 // f: the N expert ids (flat slot i = t*K + j), global or LDS.  cnt: LDS
 // scratch of E ints owned by this wave.  tile_rows: the caller's tile_off
 // granularity; tr: the row-tile height of the internal plan.
+template <int SPL>
 __device__ __forceinline__ void tiny_dispatch(const int32_t *f, int N, int K, int E, int S, int T, int tile_rows,
                                               int tr, int32_t *order, int32_t *inv_order, int32_t *row_map,
                                               int32_t *expert_off, int32_t *tile_off, int32_t *counters,
                                               PlanItem *act_items, PlanItem *tiles, int32_t *cnt) {
   const int lane = lane_id();
-  const int e0 = lane < N ? f[lane] : 0, e1 = lane + kWave < N ? f[lane + kWave] : 0;
-  const bool bad = (lane < N && unsigned(e0) >= unsigned(E)) || (lane + kWave < N && unsigned(e1) >= unsigned(E));
+  int ev[SPL];  // expert of slot h*64 + lane
+  bool bad = false;
+#pragma unroll
+  for (int h = 0; h < SPL; ++h) {
+    const int i = h * kWave + lane;
+    ev[h] = i < N ? f[i] : 0;
+    bad |= i < N && unsigned(ev[h]) >= unsigned(E);
+  }
   if (__ballot(bad)) {
     // Out-of-range expert id: an empty, in-bounds result with expert_off[E] = -1.
     for (int i = lane; i < N; i += kWave) order[i] = inv_order[i] = row_map[i] = -1;
@@ -38,8 +46,9 @@ __device__ __forceinline__ void tiny_dispatch(const int32_t *f, int N, int K, in
   }
   for (int e = lane; e < E; e += kWave) cnt[e] = 0;
   __builtin_amdgcn_wave_barrier();
-  if (lane < N) atomicAdd(&cnt[e0], 1);
-  if (lane + kWave < N) atomicAdd(&cnt[e1], 1);
+#pragma unroll
+  for (int h = 0; h < SPL; ++h)
+    if (h * kWave + lane < N) atomicAdd(&cnt[ev[h]], 1);
   __builtin_amdgcn_wave_barrier();
 
   // Each lane owns a contiguous run of experts; exclusive scans of the rows,
@@ -91,10 +100,10 @@ __device__ __forceinline__ void tiny_dispatch(const int32_t *f, int N, int K, in
   const uint64_t lt_mask = lane ? (~0ull >> (kWave - lane)) : 0ull;
   volatile int32_t *base = cnt;
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int i = half * kWave + lane;
+  for (int h = 0; h < SPL; ++h) {
+    const int i = h * kWave + lane;
     const bool valid = i < N;
-    const int e = half ? e1 : e0;
+    const int e = ev[h];
     uint64_t peers = __ballot(valid);
     for (int bit = 0; bit < nbits; ++bit) {
       const bool on = (e >> bit) & 1;

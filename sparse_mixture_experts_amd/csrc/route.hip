@@ -281,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(const float *__r
                                                                 float *__restrict__ w_out, const uint16_t *x, int D,
                                                                 uint16_t *x16, int8_t *xsh, int x_f16,
                                                                 FusedDispatch dsp) {
-  __shared__ int32_t s_f[kTinyMaxN];
+  __shared__ int32_t s_f[kTinyFusedMaxN];
   __shared__ int32_t s_cnt[kMaxExperts];
   const int t = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
   if (t < T) select_token<MPL>(t, in, n_chunks, bias, T, E, K, renorm, idx_out, w_out, x, D, x16, xsh, x_f16,
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(const float *__r
   if (dsp.order) {
     __syncthreads();
     if (threadIdx.x < kWave)
-      tiny_dispatch(s_f, T * K, K, E, dsp.S, T, dsp.tile_rows, dsp.tr, dsp.order, dsp.inv_order, dsp.row_map,
+      tiny_dispatch<kTinyFusedMaxN / kWave>(s_f, T * K, K, E, dsp.S, T, dsp.tile_rows, dsp.tr, dsp.order, dsp.inv_order, dsp.row_map,
                     dsp.expert_off, dsp.tile_off, dsp.counters, dsp.act_items, dsp.tiles, s_cnt);
   }
 }
@@ -351,7 +351,7 @@ bool route_writes_x16(const moe_layer_desc *d) {
 }
 
 bool route_fuses_dispatch(const moe_layer_desc *d, int32_t T) {
-  return T <= kThreads / kWave && int64_t(T) * d->top_k <= kTinyMaxN && !route_mfma_applies(d, T);
+  return T <= kThreads / kWave && int64_t(T) * d->top_k <= kTinyFusedMaxN && !route_mfma_applies(d, T);
 }
 
 void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router,

@@ -147,9 +147,13 @@ def test_dispatch_edge_cases():
              np.full((1, 8), E - 1, np.int32),
              rng.integers(0, E, (1000, 8), dtype=np.int32),               # duplicates within a token
              np.arange(8, dtype=np.int32).reshape(1, 8),
-             rng.integers(0, E, (16, 8), dtype=np.int32),                 # 128 slots: the one-wave dispatch
+             rng.integers(0, E, (16, 8), dtype=np.int32),                 # 128 slots: one wave, 2 per lane
              rng.integers(0, 3, (16, 8), dtype=np.int32),                 # ... with heavy repeats
-             rng.integers(0, E, (17, 8), dtype=np.int32),                 # 136 slots: one workgroup
+             rng.integers(0, E, (17, 8), dtype=np.int32),                 # 136 slots: one wave, 4 per lane
+             rng.integers(0, 2, (32, 8), dtype=np.int32),                 # 256 slots, two experts
+             rng.integers(0, E, (33, 8), dtype=np.int32),                 # 264 slots: one wave, 8 per lane
+             np.full((64, 8), 7, np.int32),                               # 512 slots, one expert
+             rng.integers(0, E, (65, 8), dtype=np.int32),                 # 520 slots: one workgroup
              rng.integers(0, E, (3, 8), dtype=np.int32)]
     for idx in cases:
         for tr in (1, 64, 1000):
@@ -157,10 +161,11 @@ def test_dispatch_edge_cases():
             ref = oracle.dispatch(idx, E, tr)
             for k in ref:
                 assert np.array_equal(got[k], ref[k]), (k, idx.shape, tr)
-    bad = rng.integers(0, E, (4, 8), dtype=np.int32)
-    bad[2, 3] = E  # out of range
-    got = g.dispatch(bad, 64)
-    assert got["expert_off"][E] == -1 and np.all(got["order"] == -1) and np.all(got["expert_off"][:E] == 0)
+    for shape in ((4, 8), (40, 8)):  # 2 and 8 slots per lane
+        bad = rng.integers(0, E, shape, dtype=np.int32)
+        bad[2, 3] = E  # out of range
+        got = g.dispatch(bad, 64)
+        assert got["expert_off"][E] == -1 and np.all(got["order"] == -1) and np.all(got["expert_off"][:E] == 0)
 
 
 def test_dispatch_many_workgroups():
