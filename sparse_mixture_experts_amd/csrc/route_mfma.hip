@@ -388,10 +388,27 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
   }
 
   // top-k over the list.  List positions follow expert order, so the lower
-  // position breaks ties exactly as the lower expert id.
+  // position breaks ties exactly as the lower expert id.  A list of at most
+  // 64 (the usual case) is ranked in one pass: lane p counts the entries that
+  // come before its own (larger, or equal at a lower position).
   int my_p = 0;
   float my_l = 0.f, top = 0.f;
-  {
+  if (n <= kWave) {
+    __shared__ int32_t s_rank[kNW][kMaxTopK];  // list position of the rank-j entry
+    const float mine = lane < n ? s_l[wv][lane] : -INFINITY;
+    int rank = 0;
+    for (int q = 0; q < n; ++q) {
+      const float o = s_l[wv][q];
+      rank += (o > mine || (o == mine && q < lane)) ? 1 : 0;
+    }
+    if (lane < n && rank < K) s_rank[wv][rank] = lane;
+    __builtin_amdgcn_wave_barrier();
+    top = s_l[wv][s_rank[wv][0]];
+    if (lane < K) {
+      my_p = s_rank[wv][lane];
+      my_l = s_l[wv][my_p];
+    }
+  } else {
     float ll[MPL];  // list entry lane + 64*q
 #pragma unroll
     for (int q = 0; q < MPL; ++q) {
