@@ -112,7 +112,9 @@ __global__ __launch_bounds__(kThreads) void router_transpose_kernel(const uint16
 
 // ---- 2. L~ = x . W + bias on MFMA ------------------------------------------
 // Block tile 64 experts x 64 tokens, 8 waves; wave (we, wt) owns 32 experts x
-// 16 tokens = 2 MFMA tiles.  Operand A = WT rows (experts), operand B = x rows
+// 16 tokens = 2 MFMA tiles.  blockIdx.z takes one of gridDim.z equal runs of
+// the 64-column chunks and writes its own partial L~ (lt + z*T*E); the
+// certification adds the partials in z order.  Operand A = WT rows (experts), operand B = x rows
 // (tokens); a lane's 4 results are 4 consecutive experts of one token.
 // The blocks of the first token tile also add up the squared-norm partials of
 // their 64 experts: normp[n_kb][e] -> normp[n_kb + 0 * E + e] (the row after
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(kMfThreads) void router_mfma_kernel(const uint16_t 
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
   const int lr = lane & 15, lg = lane >> 4;
   const int e0 = blockIdx.x * 64, t0 = blockIdx.y * 64;
-  if (blockIdx.y == 0 && tid < 64 && e0 + tid < E) {
+  if (blockIdx.y == 0 && blockIdx.z == 0 && tid < 64 && e0 + tid < E) {
     float s = 0.f;
     for (int kb = 0; kb < n_kb; ++kb) s += normp[int64_t(kb) * E + e0 + tid];
     normp[int64_t(n_kb) * E + e0 + tid] = s;
@@ -146,10 +148,12 @@ __global__ __launch_bounds__(kMfThreads) void router_mfma_kernel(const uint16_t 
   const int64_t src = which == 0 ? int64_t(min(e0 + sr, E - 1)) * D : int64_t(min(t0 + sr, T - 1)) * D;
   const uint16_t *sbase = which == 0 ? wt : x;
   const bool ok = which == 0 ? e0 + sr < E : t0 + sr < T;
-  const int C = D / kChunk;
+  const int C = D / kChunk / gridDim.z;  // chunks of this block's run
+  const int c_base = blockIdx.z * C;
+  lt += int64_t(blockIdx.z) * T * E;
   struct Stage { uint4 v0, v1; };
   auto load = [&](int c, Stage &st) __attribute__((always_inline)) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(sbase + src + min(c, C - 1) * kChunk + sc);
+    const uint4 *p = reinterpret_cast<const uint4 *>(sbase + src + (c_base + min(c, C - 1)) * kChunk + sc);
     st.v0 = p[0];
     st.v1 = p[1];
   };
@@ -226,7 +230,7 @@ __global__ __launch_bounds__(kMfThreads) void router_mfma_kernel(const uint16_t 
     if (t < T) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (eb + q < E) lt[int64_t(t) * E + eb + q] = v[q] + (bias ? bias[eb + q] : 0.0f);
+        if (eb + q < E) lt[int64_t(t) * E + eb + q] = v[q] + (bias && blockIdx.z == 0 ? bias[eb + q] : 0.0f);
     }
   }
 }
@@ -236,6 +240,7 @@ struct CertArgs {
   const uint16_t *x, *wt;
   const float *bias, *lt, *wnorm;
   int T, D, E, K;
+  int n_lt;  // partial L~ arrays, [n_lt][T][E] (1 or 2)
   float gamma;
   int32_t *idx_out;
   float *w_out;
@@ -261,7 +266,12 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
 #pragma unroll
   for (int m = 0; m < MPL; ++m) {
     const int e = lane + kWave * m;
-    lv[m] = e < E ? a.lt[int64_t(t) * E + e] : -INFINITY;
+    // both partials loaded unconditionally (the second from the first array
+    // when there is one) so that all loads of the row are in flight together
+    const int ec = min(e, E - 1);
+    const float l0 = a.lt[int64_t(t) * E + ec];
+    const float l1 = a.lt[(int64_t(a.n_lt > 1 ? a.T : 0) + t) * E + ec];
+    lv[m] = e < E ? (a.n_lt > 1 ? l0 + l1 : l0) : -INFINITY;
   }
   // ||x_t||^2: d <= 64 * 64 gives at most 8 pieces of 8 per lane, all loaded
   // together; the same registers give the fp16 staging row when asked.
@@ -454,9 +464,13 @@ bool route_mfma_applies(const moe_layer_desc *d, int32_t T) {
 // f32, each part starting on a 16-byte boundary (offsets in floats).
 static int64_t align4(int64_t v) { return (v + 3) & ~int64_t(3); }
 
+// Chunk runs of the matrix-core logits: two when the chunk count is even
+// (more workgroups in flight; partial sums added by the certification).
+static int route_mfma_splits(const moe_layer_desc *d) { return (d->d_model / kChunk) % 2 == 0 ? 2 : 1; }
+
 int64_t route_mfma_scratch_floats(const moe_layer_desc *d, int32_t T) {
   const int64_t E = d->n_experts, D = d->d_model, nkb = (D + 255) / 256;
-  return align4(int64_t(T) * E) + align4((E * D + 1) / 2) + (nkb + 1) * E;
+  return align4(route_mfma_splits(d) * int64_t(T) * E) + align4((E * D + 1) / 2) + (nkb + 1) * E;
 }
 
 namespace {
@@ -466,12 +480,13 @@ void launch_route_mfma_t(const moe_layer_desc *d, int32_t T, const void *x, cons
                          StageMarker *mk) {
   const int D = d->d_model, E = d->n_experts, nkb = (D + 255) / 256, C = D / kChunk;
   float *lt = scratch;
-  const int64_t o_wt = align4(int64_t(T) * E), o_np = o_wt + align4((int64_t(E) * D + 1) / 2);
+  const int nz = route_mfma_splits(d);
+  const int64_t o_wt = align4(nz * int64_t(T) * E), o_np = o_wt + align4((int64_t(E) * D + 1) / 2);
   uint16_t *wt = reinterpret_cast<uint16_t *>(scratch + o_wt);
   float *normp = scratch + o_np;
   hipLaunchKernelGGL(router_transpose_kernel<DT>, dim3((E + 63) / 64, nkb), dim3(kThreads), 0, s,
                      static_cast<const uint16_t *>(w_router), D, E, wt, normp);
-  hipLaunchKernelGGL(router_mfma_kernel<DT>, dim3((E + 63) / 64, (T + 63) / 64), dim3(kMfThreads), 0, s,
+  hipLaunchKernelGGL(router_mfma_kernel<DT>, dim3((E + 63) / 64, (T + 63) / 64, nz), dim3(kMfThreads), 0, s,
                      static_cast<const uint16_t *>(x), wt, bias, normp, nkb, T, D, E, lt);
   if (mk) mk->mark("route_mfma");
   // |L~ - L| <= gamma * S: the MFMAs of a chunk counted as 32 sequential
@@ -480,8 +495,8 @@ void launch_route_mfma_t(const moe_layer_desc *d, int32_t T, const void *x, cons
   // roundings, with a margin: (256 + 2C) units of 2^-24 for bf16, (384 + 2C)
   // for fp16.
   const float gamma = float((DT == kDtF16 ? 384 : 256) + 2 * C) * 5.9604645e-8f;
-  CertArgs ca{static_cast<const uint16_t *>(x), wt, bias, lt, normp + int64_t(nkb) * E, T, D, E, d->top_k, gamma,
-              idx, w, static_cast<uint16_t *>(x16), xsh};
+  CertArgs ca{static_cast<const uint16_t *>(x), wt, bias, lt, normp + int64_t(nkb) * E, T, D, E, d->top_k, nz,
+              gamma, idx, w, static_cast<uint16_t *>(x16), xsh};
   const dim3 grid((T + kThreads / kWave - 1) / (kThreads / kWave)), block(kThreads);
   if (E <= 64) hipLaunchKernelGGL((router_certify_kernel<1, DT>), grid, block, 0, s, ca);
   else if (E <= 128) hipLaunchKernelGGL((router_certify_kernel<2, DT>), grid, block, 0, s, ca);
