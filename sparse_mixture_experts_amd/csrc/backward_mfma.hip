@@ -4,8 +4,8 @@
 // section "What": the grouped expert kernels carry a custom VJP.  The pass is
 // the chain of contractions of the fp32 vector-unit kernels, over the same
 // grouping of sorted rows by expert (the forward's plan tiles):
-//   g | u = x Wgu^T     the forward's grouped GEMM, run as a plain projection
-//                       on a gathered copy of the sorted rows' x
+//   g | u = x Wgu^T     the forward's grouped gate/up GEMM without its GLU
+//                       epilogue (x read through row_map, g and u out as fp32)
 //   v     = dy Wd       transposed use of the down weights
 //   dw, dg | du         per row, from g, u, v and the slot weight (GLU derivative)
 //   dx_r  = [dg|du] Wgu transposed use of the gate/up weights
@@ -54,31 +54,6 @@ constexpr int kARow = kTK + 8;                       // bf16 elements per LDS ac
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   const f32x2 v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-
-// ---- gathered x ------------------------------------------------------------
-// Sorted row r of x (token row_map[r], or (r - N) % T for shared rows) in the
-// activation format of the grouped GEMM: affine layers fp16 with the row's
-// exponent repeated for each 128-column block; dense layers a plain copy.
-// One wave per row.
-__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *x, const int32_t *row_map, int T, int N,
-                                                          int R, int D, int nblk, int aff, int x_f16, uint16_t *xs,
-                                                          int8_t *xsh) {
-  const int r = blockIdx.x * (256 / kWave) + int(threadIdx.x) / kWave;
-  if (r >= R) return;  // whole waves
-  const int tok = r < N ? row_map[r] : (r - N) % T;
-  const uint16_t *src = x + int64_t(tok) * D;
-  uint16_t *dst = xs + int64_t(r) * D;
-  if (aff) {
-    row_to_f16(src, D, dst, xsh + int64_t(r) * nblk, x_f16 != 0);
-    if (lane_id() == 0) {
-      const int8_t e = xsh[int64_t(r) * nblk];  // written by this lane just above
-      for (int b = 1; b < nblk; ++b) xsh[int64_t(r) * nblk + b] = e;
-    }
-  } else {
-    for (int p = lane_id(); p < D / 8; p += kWave)
-      reinterpret_cast<uint4 *>(dst)[p] = reinterpret_cast<const uint4 *>(src)[p];
-  }
 }
 
 // ---- transposed grouped GEMM -------------------------------------------------
@@ -498,19 +473,10 @@ void launch_backward_mfma(const moe_layer_desc *d, int32_t T, const void *x, con
   const int qb = d->w_format == MOE_WF_AFFINE_Q8 ? 8 : aff ? 4 : 16;
   const int tr = plan_tile_rows(d, T);
   const BwdSplits sp = backward_splits(d, T);
-  const int nblk = (D + kHBlock - 1) / kHBlock;
   const bool fused = d->gate_up_fused;
 
-  // 1. g | u on the forward's grouped GEMM, from the sorted rows of x
-  hipLaunchKernelGGL(gather_rows_kernel, dim3((R + 3) / 4), dim3(256), 0, s, static_cast<const uint16_t *>(x),
-                     row_map, T, N, R, D, nblk, int(aff), f16, static_cast<uint16_t *>(sc.xs), sc.xsh);
-  if (fused) {
-    launch_projection_mfma(d, T, sc.xs, sc.xsh, D, 2 * F, w->gate_up, counters, tiles, max_tiles, sc.gu, stream);
-  } else {
-    launch_projection_mfma(d, T, sc.xs, sc.xsh, D, F, w->gate, counters, tiles, max_tiles, sc.gu, stream);
-    launch_projection_mfma(d, T, sc.xs, sc.xsh, D, F, w->up, counters, tiles, max_tiles, sc.gu + int64_t(R) * F,
-                           stream);
-  }
+  // 1. g | u on the forward's grouped gate/up GEMM ([gate | up] per row)
+  launch_gate_up_raw_mfma(d, T, x, row_map, w, counters, tiles, max_tiles, sc.ffn, sc.gu, stream);
 
   // 2. v = dy Wd (down weights [E+S][D][F]: reduction over d, columns f)
   const moe_proj &dn = w->down;
@@ -521,8 +487,8 @@ void launch_backward_mfma(const moe_layer_desc *d, int32_t T, const void *x, con
   launch_t(tv, qb, tr, 0, max_tiles, s);
 
   // 3. dw and dg | du per row
-  GluArgs ga{sc.gu, fused ? sc.gu + F : sc.gu + int64_t(R) * F, fused ? 2 * F : F, sc.v, sp.v, int64_t(R) * F,
-             topk_w, order, N, F, d->activation == MOE_ACT_GEGLU, sc.dw, sc.dgu};
+  GluArgs ga{sc.gu, sc.gu + F, 2 * F, sc.v, sp.v, int64_t(R) * F, topk_w, order, N, F,
+             d->activation == MOE_ACT_GEGLU, sc.dw, sc.dgu};
   hipLaunchKernelGGL(glu_bf16_kernel, dim3(R), dim3(256), 0, s, ga);
 
   // 4. dx_r = [dg | du] Wgu (gate rows then up rows: reduction over 2F, columns d)

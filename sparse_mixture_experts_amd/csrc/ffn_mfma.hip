@@ -157,6 +157,12 @@ struct Slab {
 constexpr int kDenseBF16 = 0, kDenseF16 = 16;
 constexpr bool is_affine(int qb) { return qb == 4 || qb == 8; }
 
+// Projections of the grouped GEMM: down (sorted h rows -> y rows), gate/up
+// with the GLU epilogue (x rows through row_map -> h), and gate/up with the
+// gate and up values written as they are (fp32 rows [gate | up], for the
+// backward pass).
+constexpr int kDown = 0, kGateUp = 1, kGateUpRaw = 2;
+
 // Per-lane weight data of one slab (32 reduction elements per tile): 4-bit
 // -> one uint4 (4 words) per tile; 8-bit -> two; 16-bit dense -> four.
 template <int QB>
@@ -177,8 +183,10 @@ struct WSlab { uint4 w[kNT][is_affine(QB) ? QB / 4 : kSteps]; };
 // Both operands use the same order, so every step sums over a fixed quarter
 // of the slab and the four steps cover it.  A lane's 32 elements lie in one
 // group: group 32*lg / (128 / GPS) of the slab.
-template <bool GATEUP, int QB, int RB, int GPS>
+template <int MODE, int QB, int RB, int GPS>
 __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
+  constexpr bool GATEUP = MODE != kDown;  // gate/up rows (two weight matrices per column)
+  constexpr bool RAW = MODE == kGateUpRaw;  // g and u out as fp32, no GLU
   constexpr bool AFF = is_affine(QB);              // affine codes (fp16 path)
   constexpr int kLPG = 4 / GPS;                   // lanes lg per group
   constexpr float kQMax = QB == 8 ? 255.0f : 15.0f;
@@ -531,7 +539,28 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
     }
   }
 
-  if constexpr (GATEUP && AFF) {
+  if constexpr (RAW) {
+    // gate and up values (the token exponent undone) as fp32: row r holds
+    // gate columns 0..n_out-1 then up columns n_out..2*n_out-1
+    if (!col_ok) return;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int m = rb * 16 + lr;
+      if (m >= tile.rows) continue;
+      const float xs = AFF ? pow2(rsh[m]) : 1.0f;
+      float *orow = static_cast<float *>(a.out) + (tile.row0 + m) * int64_t(2 * a.n_out);
+#pragma unroll
+      for (int nt = 0; nt < NTH; ++nt) {
+        const int c = col0 + nt * 16 + lg * 4;
+        *reinterpret_cast<float4 *>(orow + c) = make_float4(acc[nt][rb][0] * xs, acc[nt][rb][1] * xs,
+                                                            acc[nt][rb][2] * xs, acc[nt][rb][3] * xs);
+        *reinterpret_cast<float4 *>(orow + a.n_out + c) =
+            make_float4(acc[nt + NTH][rb][0] * xs, acc[nt + NTH][rb][1] * xs, acc[nt + NTH][rb][2] * xs,
+                        acc[nt + NTH][rb][3] * xs);
+      }
+    }
+    return;
+  } else if constexpr (GATEUP && AFF) {
     // The GLU on the true gate/up values (the token exponent undone), then h as
     // fp16 with one exponent per (row, this block's 128 columns), in the
     // permuted staging order.  Lane (lr, lg) holds columns c..c+3,
@@ -627,14 +656,14 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
 // registers (accumulators included) without spilling; left to itself it
 // gives them one wave per SIMD and moves the accumulators between register
 // files every slab.  16-row tiles allocate on their own.
-template <bool GATEUP, int QB, int RB, int GPS>
+template <int MODE, int QB, int RB, int GPS>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs a) {
-  grouped_gemm_body<GATEUP, QB, RB, GPS>(a);
+  grouped_gemm_body<MODE, QB, RB, GPS>(a);
 }
-template <bool GATEUP, int QB, int RB, int GPS>
+template <int MODE, int QB, int RB, int GPS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void grouped_gemm_kernel_w2(
     GemmArgs a) {
-  grouped_gemm_body<GATEUP, QB, RB, GPS>(a);
+  grouped_gemm_body<MODE, QB, RB, GPS>(a);
 }
 
 // ---- decode tiles (at most 16 rows of an expert, K <= 2048) ----------------
@@ -854,29 +883,29 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecArgs a) {
   }
 }
 
-template <bool GATEUP, int QB, int RB, int GPS>
+template <int MODE, int QB, int RB, int GPS>
 void launch_one(const GemmArgs &ga, int64_t max_tiles, hipStream_t s) {
-  constexpr int NTH = GATEUP ? kNT / 2 : kNT;
+  constexpr int NTH = MODE != kDown ? kNT / 2 : kNT;
   const int cols_per_block = kNW * NTH * 16;
   const dim3 grid((ga.n_out + cols_per_block - 1) / cols_per_block, unsigned(max_tiles));
   // 16-row tiles fit two or more waves per SIMD by themselves.
   constexpr bool kFits = RB == 1;
-  if constexpr (kFits) hipLaunchKernelGGL((grouped_gemm_kernel<GATEUP, QB, RB, GPS>), grid, dim3(kThreads), 0, s, ga);
-  else hipLaunchKernelGGL((grouped_gemm_kernel_w2<GATEUP, QB, RB, GPS>), grid, dim3(kThreads), 0, s, ga);
+  if constexpr (kFits) hipLaunchKernelGGL((grouped_gemm_kernel<MODE, QB, RB, GPS>), grid, dim3(kThreads), 0, s, ga);
+  else hipLaunchKernelGGL((grouped_gemm_kernel_w2<MODE, QB, RB, GPS>), grid, dim3(kThreads), 0, s, ga);
 }
 // Code width (0: dense bf16) and groups per slab picked at run time.
-template <bool GATEUP, int RB, int QB>
+template <int MODE, int RB, int QB>
 void launch_groups(const GemmArgs &ga, int gsize, int64_t max_tiles, hipStream_t s) {
-  if (gsize == 32) launch_one<GATEUP, QB, RB, 4>(ga, max_tiles, s);
-  else if (gsize == 128) launch_one<GATEUP, QB, RB, 1>(ga, max_tiles, s);
-  else launch_one<GATEUP, QB, RB, 2>(ga, max_tiles, s);
+  if (gsize == 32) launch_one<MODE, QB, RB, 4>(ga, max_tiles, s);
+  else if (gsize == 128) launch_one<MODE, QB, RB, 1>(ga, max_tiles, s);
+  else launch_one<MODE, QB, RB, 2>(ga, max_tiles, s);
 }
-template <bool GATEUP, int RB>
+template <int MODE, int RB>
 void launch_gemm(const GemmArgs &ga, int qb, int gsize, int64_t max_tiles, hipStream_t s) {
-  if (qb == 4) launch_groups<GATEUP, RB, 4>(ga, gsize, max_tiles, s);
-  else if (qb == 8) launch_groups<GATEUP, RB, 8>(ga, gsize, max_tiles, s);
-  else if (qb == kDenseF16) launch_one<GATEUP, kDenseF16, RB, 1>(ga, max_tiles, s);
-  else launch_one<GATEUP, kDenseBF16, RB, 1>(ga, max_tiles, s);
+  if (qb == 4) launch_groups<MODE, RB, 4>(ga, gsize, max_tiles, s);
+  else if (qb == 8) launch_groups<MODE, RB, 8>(ga, gsize, max_tiles, s);
+  else if (qb == kDenseF16) launch_one<MODE, kDenseF16, RB, 1>(ga, max_tiles, s);
+  else launch_one<MODE, kDenseBF16, RB, 1>(ga, max_tiles, s);
 }
 
 template <bool GATEUP, int QB, int MS>
@@ -925,18 +954,24 @@ int plan_tile_rows(const moe_layer_desc *d, int32_t T) {
   return N <= 8LL * d->n_experts ? 16 : 64;
 }
 
-void launch_projection_mfma(const moe_layer_desc *d, int32_t T, const void *act, const int8_t *act_sh, int K,
-                            int n_out, const moe_proj &p, const int32_t *counters, const PlanItem *tiles,
-                            int64_t max_tiles, float *out, void *stream) {
+void launch_gate_up_raw_mfma(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
+                             const moe_weights *w, const int32_t *counters, const PlanItem *tiles, int64_t max_tiles,
+                             const FfnScratch &sc, float *gu, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool aff = affine(d);
   const bool f16 = d->act_dtype == MOE_DT_F16;
   const int qb = d->w_format == MOE_WF_AFFINE_Q8 ? 8 : aff ? 4 : f16 ? kDenseF16 : kDenseBF16;
-  GemmArgs g{act, act_sh, nullptr, (K + kHBlock - 1) / kHBlock, nullptr, T, T * d->top_k, K, n_out, 0, 0, 0,
-             int(f16), p.w, static_cast<const uint16_t *>(p.scales), static_cast<const uint16_t *>(p.biases),
-             nullptr, nullptr, nullptr, counters, tiles, out, 0};
-  if (plan_tile_rows(d, T) == 16) launch_gemm<false, 1>(g, qb, d->group_size, max_tiles, s);
-  else launch_gemm<false, 4>(g, qb, d->group_size, max_tiles, s);
+  if (aff && !sc.x16_ready)
+    hipLaunchKernelGGL(act_f16_kernel, dim3((T + 3) / 4), dim3(256), 0, s, static_cast<const uint16_t *>(x), T,
+                       d->d_model, static_cast<uint16_t *>(sc.x16), sc.xsh, int(f16));
+  const moe_proj &pg = d->gate_up_fused ? w->gate_up : w->gate;
+  GemmArgs g{aff ? sc.x16 : x, sc.xsh, nullptr, 0, row_map, T, T * d->top_k, d->d_model, d->d_ff,
+             d->gate_up_fused, 0, 0, int(f16),
+             pg.w, static_cast<const uint16_t *>(pg.scales), static_cast<const uint16_t *>(pg.biases),
+             w->up.w, static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases),
+             counters, tiles, gu, 0};
+  if (plan_tile_rows(d, T) == 16) launch_gemm<kGateUpRaw, 1>(g, qb, d->group_size, max_tiles, s);
+  else launch_gemm<kGateUpRaw, 4>(g, qb, d->group_size, max_tiles, s);
 }
 
 void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
@@ -983,14 +1018,14 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
     launch_decode<false>(dd, qb, max_tiles, s);
     if (mk) mk->mark("down_mfma");
   } else if (tr == 16) {
-    launch_gemm<true, 1>(gu, qb, gs, max_tiles, s);
+    launch_gemm<kGateUp, 1>(gu, qb, gs, max_tiles, s);
     if (mk) mk->mark("gateup_mfma");
-    launch_gemm<false, 1>(dn, qb, gs, max_tiles, s);
+    launch_gemm<kDown, 1>(dn, qb, gs, max_tiles, s);
     if (mk) mk->mark("down_mfma");
   } else {
-    launch_gemm<true, 4>(gu, qb, gs, max_tiles, s);
+    launch_gemm<kGateUp, 4>(gu, qb, gs, max_tiles, s);
     if (mk) mk->mark("gateup_mfma");
-    launch_gemm<false, 4>(dn, qb, gs, max_tiles, s);
+    launch_gemm<kDown, 4>(dn, qb, gs, max_tiles, s);
     if (mk) mk->mark("down_mfma");
   }
 }

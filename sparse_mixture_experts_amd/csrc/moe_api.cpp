@@ -218,18 +218,18 @@ int moe_backward(const moe_layer_desc *desc, int32_t T, const void *x, const moe
   if (ws_bytes < B.total) return MOE_E_WORKSPACE;
   if (T == 0) return MOE_OK;
   const Workspace &L = B.fwd;
-  // the forward's routing and grouping, again (no staging copy of x)
+  // the forward's routing and grouping, again (and the fp16 staging copy of x)
   int32_t *idx = at<int32_t>(ws, L.topk_idx);
   float *wt = at<float>(ws, L.topk_w);
-  launch_route(desc, T, x, w->w_router, w->router_bias, idx, wt, at<float>(ws, L.route), nullptr, nullptr,
-               FusedDispatch{}, stream);
+  launch_route(desc, T, x, w->w_router, w->router_bias, idx, wt, at<float>(ws, L.route), at<void>(ws, L.x16),
+               at<int8_t>(ws, L.xsh), FusedDispatch{}, stream);
   launch_dispatch(desc, T, idx, plan_tile_rows(desc, T), at<int32_t>(ws, L.order), at<int32_t>(ws, L.inv_order),
                   at<int32_t>(ws, L.row_map), at<int32_t>(ws, L.expert_off), at<int32_t>(ws, L.tile_off),
                   at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles),
                   at<int32_t>(ws, L.dsp), stream);
-  const BwdScratch sc{at<float>(ws, B.gu),  at<float>(ws, B.v),     at<float>(ws, B.dw),
-                      at<float>(ws, B.dxr), at<void>(ws, B.xs),     at<int8_t>(ws, B.xsh),
-                      at<uint16_t>(ws, B.dgu), at<void>(ws, B.wr_t)};
+  const BwdScratch sc{at<float>(ws, B.gu),    at<float>(ws, B.v),    at<float>(ws, B.dw),
+                      at<float>(ws, B.dxr),   at<uint16_t>(ws, B.dgu), at<void>(ws, B.wr_t),
+                      ffn_scratch(ws, L, route_writes_x16(desc))};
   launch_backward(desc, T, x, w, dy, idx, wt, at<int32_t>(ws, L.order), at<int32_t>(ws, L.inv_order),
                   at<int32_t>(ws, L.row_map), at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items),
                   at<PlanItem>(ws, L.tiles), L.max_tiles, sc, dx, stream);

@@ -132,17 +132,16 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
 
 // Backward with respect to x.  Intermediates in the backward workspace (R
 // sorted rows): g and u, v = Wd^T dy (per reduction split), dw, the rows'
-// dx (per split); the matrix-core path adds the gathered x rows, dg | du as
-// bf16, and the router matrix transposed for the per-token kernel.
+// dx (per split), the router matrix transposed for the per-token kernel;
+// the matrix-core path adds dg | du as bf16.
 struct BwdScratch {
-  float *gu;      // [R][2F] g | u per row (fused gate/up on the matrix cores), else g [R][F] then u [R][F]
+  float *gu;      // matrix cores: [R][2F] g | u per row; vector units: g [R][F] then u [R][F]
   float *v;       // [splits.v][R][F]
   float *dw;      // [R]
   float *dxr;     // [splits.dx][R][D]
-  void *xs;       // matrix-core path: x of the sorted rows [R][D], 16-bit
-  int8_t *xsh;    // matrix-core path, affine layers: [R][ceil(D/128)] exponents
   uint16_t *dgu;  // matrix-core path: [R][2F] bf16, dg then du
   void *wr_t;     // router matrix transposed [E][D] (layer dtype)
+  FfnScratch ffn; // matrix-core path: the fp16 staging copy of x (affine layers)
 };
 // Reduction splits of the matrix-core backward's transposed products (the
 // partial sums are added in split order by their consumers).
@@ -152,7 +151,7 @@ struct BwdSplits {
 BwdSplits backward_splits(const moe_layer_desc *d, int32_t T);
 struct BwdWorkspace {
   Workspace fwd;  // router and dispatch sections (the forward's layout)
-  size_t gu, v, dw, dxr, xs, xsh, dgu, wr_t, total;
+  size_t gu, v, dw, dxr, dgu, wr_t, total;
 };
 BwdWorkspace backward_workspace_layout(const moe_layer_desc *d, int32_t T);
 void launch_backward(const moe_layer_desc *d, int32_t T, const void *x, const moe_weights *w, const float *dy,
@@ -164,13 +163,13 @@ void launch_backward_mfma(const moe_layer_desc *d, int32_t T, const void *x, con
                           const float *topk_w, const int32_t *order, const int32_t *row_map,
                           const int32_t *counters, const PlanItem *tiles, int64_t max_tiles, const BwdScratch &sc,
                           void *stream);
-// The grouped GEMM of the down projection as a plain projection of sorted
-// rows: out[r][n] (fp32, row stride n_out) = sum_k act[r][k] W[n][k] for the
-// rows of the plan's tiles, act in the GEMM's activation format (fp16 with
-// one exponent per (row, 128 columns) on affine layers, else the layer dtype).
-void launch_projection_mfma(const moe_layer_desc *d, int32_t T, const void *act, const int8_t *act_sh, int K,
-                            int n_out, const moe_proj &p, const int32_t *counters, const PlanItem *tiles,
-                            int64_t max_tiles, float *out, void *stream);
+// The grouped gate/up GEMM without the GLU: gu[r] = [x Wg^T | x Wu^T] for
+// every sorted row r (fp32, row stride 2*d_ff), x read through row_map as in
+// the forward (the fp16 staging copy for affine layers, written here unless
+// sc.x16_ready).
+void launch_gate_up_raw_mfma(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
+                             const moe_weights *w, const int32_t *counters, const PlanItem *tiles, int64_t max_tiles,
+                             const FfnScratch &sc, float *gu, void *stream);
 
 // Combine.
 void launch_combine(const moe_layer_desc *d, int32_t T, const void *y_sorted, bool ys_bf16,
