@@ -111,6 +111,7 @@ def accounting(spec, touched: int):
     ysz = 2 if spec.act == "bf16" and D % 64 == 0 and F % 64 == 0 else 4
     # the router's per-token kernel writes the fp16 staging copy of x (and reads x) for 4-bit layers
     x16_bytes = (T * D * 2 + T) if spec.quantized and D <= 4096 else 0
+    lt_parts = 2 if (D // 64) % 2 == 0 else 1
     gateup = {"bound": "hbm", "bytes": int(w_touched * gu_frac) + T * D * esz + R * F * esz,
               "flops": 2 * R * 2 * D * F}
     down = {"bound": "hbm", "bytes": int(w_touched * down_frac) + R * F * esz + R * D * ysz, "flops": 2 * R * D * F}
@@ -122,11 +123,13 @@ def accounting(spec, touched: int):
             # VALU router: canonical-order logits (fp32 FMA chains), then top-k
             "route_logits": {"bound": "alu", "flops": 2 * T * D * E, "bytes": T * D * esz + router + T * E * 4},
             "route_select": {"bound": "hbm", "bytes": T * E * 4 + N * 8 + x16_bytes},
-            # matrix-core router: W transposed (read + write + read), x read, logits written
-            "route_mfma": {"bound": "hbm", "bytes": 3 * router + T * D * esz + T * E * 4, "flops": 2 * T * D * E},
+            # matrix-core router: W transposed (read + write + read), x read,
+            # logits written (two partial sums when the 64-column chunks split evenly)
+            "route_mfma": {"bound": "hbm", "bytes": 3 * router + T * D * esz + lt_parts * T * E * 4,
+                           "flops": 2 * T * D * E},
             # certification: logits and x read, the k winners written (and the
             # fp16 staging copy of x for 4-bit layers)
-            "route_certify": {"bound": "hbm", "bytes": T * E * 4 + T * D * esz + N * 8 + x16_bytes},
+            "route_certify": {"bound": "hbm", "bytes": lt_parts * T * E * 4 + T * D * esz + N * 8 + x16_bytes},
             "dispatch": {"bound": "hbm", "bytes": N * 4 * 4},
             # selection with the dispatch of a handful of slots folded in
             "route_select_dispatch": {"bound": "hbm", "bytes": T * E * 4 + N * 8 + x16_bytes + N * 4 * 4},
