@@ -141,6 +141,7 @@ struct GemmArgs {
   const PlanItem *tiles;
   void *out;                // gate/up: h [rows][F] (bf16, or fp16 for affine); down: y [rows][D]
   int out_bf16;             // down: y rows as bf16 (else fp32)
+  int bx_major;             // work order: column block major (experts with several tiles), else tile major
 };
 
 // GPS: groups per slab (128 / group size; 1 for dense weights).
@@ -217,7 +218,11 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
     item = (lin % 8) * per + slot;
   }
   if (item >= work) return;
-  const int tile_id = item / nbx, bx = item % nbx;
+  // Tile-major order puts the column blocks of a tile next to each other
+  // (they stage the same activation rows); column-block-major order puts the
+  // tiles of one expert next to each other (they read the same weights).
+  const int n_tiles = a.counters[1];
+  const int tile_id = a.bx_major ? item % n_tiles : item / nbx, bx = a.bx_major ? item / n_tiles : item % nbx;
   const PlanItem tile = a.tiles[tile_id];
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
@@ -947,6 +952,13 @@ bool use_mfma(const moe_layer_desc *d) {
   return d->act_dtype != MOE_DT_F32 && d->d_model % 64 == 0 && d->d_ff % 64 == 0;
 }
 
+// Experts with two or more row tiles on average: their tiles run next to
+// each other for each column block, so the second reads the weights from L2.
+static int use_bx_major(const moe_layer_desc *d, int32_t T) {
+  const int64_t rows_per_expert = int64_t(T) * d->top_k / d->n_experts;
+  return rows_per_expert >= 2 * plan_tile_rows(d, T) ? 1 : 0;
+}
+
 int plan_tile_rows(const moe_layer_desc *d, int32_t T) {
   // Decode-sized groups (T*k/E <= 8 rows per expert on average, the pages'
   // small-group regime) use 16-row tiles; larger groups 64-row tiles.
@@ -969,7 +981,7 @@ void launch_gate_up_raw_mfma(const moe_layer_desc *d, int32_t T, const void *x, 
              d->gate_up_fused, 0, 0, int(f16),
              pg.w, static_cast<const uint16_t *>(pg.scales), static_cast<const uint16_t *>(pg.biases),
              w->up.w, static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases),
-             counters, tiles, gu, 0};
+             counters, tiles, gu, 0, use_bx_major(d, T)};
   if (plan_tile_rows(d, T) == 16) launch_gemm<kGateUpRaw, 1>(g, qb, d->group_size, max_tiles, s);
   else launch_gemm<kGateUpRaw, 4>(g, qb, d->group_size, max_tiles, s);
 }
@@ -986,6 +998,7 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
   const int geglu = d->activation == MOE_ACT_GEGLU;
   const int tr = plan_tile_rows(d, T);
   const int nblk = (d->d_ff + kHBlock - 1) / kHBlock;
+  const int bx_major = use_bx_major(d, T);
   if (aff && !sc.x16_ready) {
     hipLaunchKernelGGL(act_f16_kernel, dim3((T + 3) / 4), dim3(256), 0, s, static_cast<const uint16_t *>(x), T,
                        d->d_model, static_cast<uint16_t *>(sc.x16), sc.xsh, int(f16));
@@ -996,10 +1009,10 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
               d->gate_up_fused, d->swiglu_round_bf16, geglu, int(f16),
               pg.w, static_cast<const uint16_t *>(pg.scales), static_cast<const uint16_t *>(pg.biases),
               w->up.w, static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases),
-              counters, tiles, sc.h, 0};
+              counters, tiles, sc.h, 0, bx_major};
   GemmArgs dn{sc.h, sc.hsh, nullptr, nblk, nullptr, T, T * d->top_k, d->d_ff, d->d_model, 0, 0, 0, int(f16),
               w->down.w, static_cast<const uint16_t *>(w->down.scales), static_cast<const uint16_t *>(w->down.biases),
-              nullptr, nullptr, nullptr, counters, tiles, y_sorted, ys_bf16};
+              nullptr, nullptr, nullptr, counters, tiles, y_sorted, ys_bf16, bx_major};
   if (tr == 16 && aff && int64_t(T) * d->top_k <= d->n_experts && d->d_model <= kDecMaxK &&
       d->d_ff <= kDecMaxK) {
     // at most one routed row per expert on average: whole-K loads per wave

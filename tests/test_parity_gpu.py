@@ -91,6 +91,11 @@ MID = {
                                       n_shared=1, act="f32", gate_up_fused=True, x_scale="fan_in", seed=48),
     "mid-bf16-gemv-fused": LayerSpec("mid-bf16-gemv-fused", T=30, d_model=96, d_ff=72, n_experts=5, top_k=2,
                                      gate_up_fused=True, activation="geglu", seed=49),
+    # experts with several 64-row tiles each (column-block-major work order)
+    "mid-bf16-many-tiles": LayerSpec("mid-bf16-many-tiles", T=600, d_model=256, d_ff=192, n_experts=4, top_k=2,
+                                     seed=50),
+    "mid-q4-many-tiles-shared": LayerSpec("mid-q4-many-tiles-shared", T=520, d_model=256, d_ff=128, n_experts=4,
+                                          top_k=1, n_shared=1, wfmt="q4", gate_up_fused=True, seed=51),
     "mid-f16-q8-decode-geglu": LayerSpec("mid-f16-q8-decode-geglu", T=3, d_model=512, d_ff=256, n_experts=64,
                                          top_k=8, act="f16", wfmt="q8", group_size=128, activation="geglu",
                                          seed=47),
