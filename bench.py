@@ -93,12 +93,33 @@ def expert_bytes(spec) -> int:
     return n * (4 if spec.act == "f32" else 2)
 
 
+def expert_output_bytes(spec) -> float:
+    """Bytes per expert-output element between the down projection and the
+    combine, in the format moe_forward picks (the library's rule restated):
+    fp16 plus one exponent byte per 64 columns on the 16-bit matrix-core
+    tiles; fp32 on the vector-unit and decode kernels and when the down
+    reduction is split into fp32 partial rows (counted once here)."""
+    T, D, F, E, K, S = spec.T, spec.d_model, spec.d_ff, spec.n_experts, spec.top_k, spec.n_shared
+    if spec.act == "f32" or D % 64 or F % 64:
+        return 4
+    N = T * K
+    tr = 16 if N <= 8 * E else 64
+    if tr == 16 and spec.quantized and N <= E and D <= 2048 and F <= 2048:
+        return 4  # decode kernel
+    R = N + S * T
+    tiles, nbx, nslab = max(min(R, E + S), -(-R // tr)), -(-D // 256), -(-F // 128)
+    kz = 1
+    while tiles * nbx * kz < 512 and kz < 8 and nslab >= 4 * kz:
+        kz *= 2
+    return 4 if kz > 1 else 2 + 1 / 64
+
+
 def accounting(spec, touched: int):
     """Algorithmic bytes and FLOPs of one forward, and per kernel.
 
     Bytes count each tensor a kernel must read or write once: weights of the
     experts the batch touches (plus shared experts), activations, the routed
-    intermediate h, the f32 expert outputs and the small index tables.
+    intermediate h, the expert outputs (as stored) and the small index tables.
     """
     T, D, F, E, K, S = spec.T, spec.d_model, spec.d_ff, spec.n_experts, spec.top_k, spec.n_shared
     esz = 4 if spec.act == "f32" else 2
@@ -107,14 +128,14 @@ def accounting(spec, touched: int):
     gu_frac, down_frac = 2 / 3, 1 / 3
     w_touched = (touched + S) * eb
     router = D * E * esz
-    # expert outputs: bf16 where the matrix-core kernels write them, else fp32
-    ysz = 2 if spec.act == "bf16" and D % 64 == 0 and F % 64 == 0 else 4
+    ysz = expert_output_bytes(spec)
     # the router's per-token kernel writes the fp16 staging copy of x (and reads x) for 4-bit layers
     x16_bytes = (T * D * 2 + T) if spec.quantized and D <= 4096 else 0
     lt_parts = 2 if (D // 64) % 2 == 0 else 1
     gateup = {"bound": "hbm", "bytes": int(w_touched * gu_frac) + T * D * esz + R * F * esz,
               "flops": 2 * R * 2 * D * F}
-    down = {"bound": "hbm", "bytes": int(w_touched * down_frac) + R * F * esz + R * D * ysz, "flops": 2 * R * D * F}
+    down = {"bound": "hbm", "bytes": int(w_touched * down_frac) + R * F * esz + int(R * D * ysz),
+            "flops": 2 * R * D * F}
     acc = {
         "layer_bytes": w_touched + router + T * D * esz + T * D * esz,
         "expert_flops": 2 * R * 3 * D * F,
@@ -137,7 +158,7 @@ def accounting(spec, touched: int):
             "x_f16": {"bound": "hbm", "bytes": 2 * T * D * esz + T},
             "gateup_gemv": gateup, "down_gemv": down,
             "gateup_mfma": gateup, "down_mfma": down,
-            "combine": {"bound": "hbm", "bytes": R * D * ysz + T * D * esz + N * 8},
+            "combine": {"bound": "hbm", "bytes": int(R * D * ysz) + T * D * esz + N * 8},
         },
     }
     return acc

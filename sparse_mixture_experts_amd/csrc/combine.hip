@@ -4,7 +4,11 @@
 // the weighted sum of "perf(moe): fused MoE expert decode kernel" ("What it
 // does") gathered through inv_order as in DS4Server #112's _scatter_unsort.
 // A gather per token instead of the PRD's atomic scatter-add keeps the fp32
-// summation order fixed (slot order), so results are deterministic.
+// summation order fixed (slot order), so results are deterministic.  Expert
+// outputs arrive as fp32 rows, as fp16 rows with one power-of-two exponent
+// per 64 columns, or (down reduction split) as fp32 partial rows that are
+// first summed in part order.
+#include <stdexcept>
 #include <type_traits>
 
 #include "device_common.h"
@@ -14,32 +18,40 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kCols = 8;  // columns per thread (one 16-byte bf16 load, two fp32 ones)
+constexpr int kCols = 8;  // columns per thread (one 16-byte fp16 load, two fp32 ones)
 
-// Eight consecutive expert-output values, as loaded (bf16: one 16-byte load;
-// fp32: two) and as fp32.
-template <bool YS_BF16>
+// Eight consecutive expert-output values, as loaded (fp16: one 16-byte load
+// and the row's exponent for these columns; fp32: two 16-byte loads) and as
+// fp32.
+template <bool F16E>
 struct Row8 {
-  uint4 u[YS_BF16 ? 1 : 2];
+  uint4 u[F16E ? 1 : 2];
+  int sh;
 };
-template <bool YS_BF16>
-__device__ __forceinline__ Row8<YS_BF16> load8(const void *ys, int64_t i) {
-  Row8<YS_BF16> r;
-  if constexpr (YS_BF16) {
+template <bool F16E>
+__device__ __forceinline__ Row8<F16E> load8(const void *ys, const int8_t *ys_sh, int64_t row, int D, int c) {
+  Row8<F16E> r;
+  const int64_t i = row * D + c;
+  if constexpr (F16E) {
     r.u[0] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(ys) + i);
+    r.sh = ys_sh[row * (D / kYsBlock) + c / kYsBlock];
   } else {
     const uint4 *q = reinterpret_cast<const uint4 *>(static_cast<const float *>(ys) + i);
     r.u[0] = q[0];
     r.u[1] = q[1];
+    r.sh = 0;
   }
   return r;
 }
-template <bool YS_BF16>
-__device__ __forceinline__ void widen8(const Row8<YS_BF16> &r, float v[8]) {
-  if constexpr (YS_BF16) {
+__device__ __forceinline__ float f16_lo(uint32_t u) { return float(__builtin_bit_cast(_Float16, uint16_t(u))); }
+__device__ __forceinline__ float f16_hi(uint32_t u) { return float(__builtin_bit_cast(_Float16, uint16_t(u >> 16))); }
+template <bool F16E>
+__device__ __forceinline__ void widen8(const Row8<F16E> &r, float v[8]) {
+  if constexpr (F16E) {
     const uint4 u = r.u[0];
-    v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
-    v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z); v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+    const float m = __uint_as_float(uint32_t(127 + r.sh) << 23);  // 2^sh
+    v[0] = f16_lo(u.x) * m; v[1] = f16_hi(u.x) * m; v[2] = f16_lo(u.y) * m; v[3] = f16_hi(u.y) * m;
+    v[4] = f16_lo(u.z) * m; v[5] = f16_hi(u.z) * m; v[6] = f16_lo(u.w) * m; v[7] = f16_hi(u.w) * m;
   } else {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -49,45 +61,64 @@ __device__ __forceinline__ void widen8(const Row8<YS_BF16> &r, float v[8]) {
   }
 }
 
+// Adds the partial rows 1 .. parts-1 of the fp32 row `row`, columns c .. c+7.
+__device__ __forceinline__ void add_parts(const void *ys, int64_t row, int D, int c, int parts,
+                                          int64_t part_rows, float v[8]) {
+  for (int z = 1; z < parts; ++z) {
+    float q[kCols];
+    widen8<false>(load8<false>(ys, nullptr, z * part_rows + row, D, c), q);
+#pragma unroll
+    for (int i = 0; i < kCols; ++i) v[i] += q[i];
+  }
+}
+
 // Block (t, cb): token t, columns cb*256*8 ..; each thread 8 columns.  The
 // token's slot positions and weights are uniform (scalar loads); then all
-// slot rows of a thread (up to 16 bf16 or 8 fp32 rows per round) are in
-// flight together before they are summed in slot order.
-template <bool YS_BF16, int OUT_DT>
+// slot rows of a thread (up to 16 fp16 or 8 fp32 rows per round) are in
+// flight together before they are summed in slot order.  parts > 1 (fp32
+// rows only): partial rows part_rows rows apart.
+template <bool F16E, int OUT_DT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const void *__restrict__ ys,
+                                                           const int8_t *__restrict__ ys_sh,
                                                            const int32_t *__restrict__ inv,
                                                            const float *__restrict__ w, int T, int K, int S,
-                                                           int N, int D, void *__restrict__ y) {
+                                                           int N, int D, int parts, int64_t part_rows,
+                                                           void *__restrict__ y) {
   const int t = blockIdx.x;
   const int c = (blockIdx.y * kThreads + threadIdx.x) * kCols;
   if (c >= D) return;
   float acc[kCols];
 #pragma unroll
   for (int i = 0; i < kCols; ++i) acc[i] = 0.f;
-  constexpr int kSlots = YS_BF16 ? 16 : 8;
+  constexpr int kSlots = F16E ? 16 : 8;
   for (int j0 = 0; j0 < K; j0 += kSlots) {
-    Row8<YS_BF16> r[kSlots];
+    Row8<F16E> r[kSlots];
     float wj[kSlots];
+    int rowj[kSlots];
 #pragma unroll
     for (int u = 0; u < kSlots; ++u) {
       const int j = min(j0 + u, K - 1);
       const int p = inv[int64_t(t) * K + j];
       const bool ok = j0 + u < K && unsigned(p) < unsigned(N);
       wj[u] = ok ? w[int64_t(t) * K + j] : 0.f;
-      r[u] = load8<YS_BF16>(ys, int64_t(ok ? p : 0) * D + c);
+      rowj[u] = ok ? p : 0;
+      r[u] = load8<F16E>(ys, ys_sh, rowj[u], D, c);
     }
 #pragma unroll
     for (int u = 0; u < kSlots; ++u)
       if (j0 + u < K) {
         float v[kCols];
-        widen8<YS_BF16>(r[u], v);
+        widen8<F16E>(r[u], v);
+        if constexpr (!F16E) add_parts(ys, rowj[u], D, c, parts, part_rows, v);
 #pragma unroll
         for (int i = 0; i < kCols; ++i) acc[i] += wj[u] * v[i];
       }
   }
   for (int s = 0; s < S; ++s) {
     float v[kCols];
-    widen8<YS_BF16>(load8<YS_BF16>(ys, (int64_t(N) + int64_t(s) * T + t) * D + c), v);
+    const int64_t row = int64_t(N) + int64_t(s) * T + t;
+    widen8<F16E>(load8<F16E>(ys, ys_sh, row, D, c), v);
+    if constexpr (!F16E) add_parts(ys, row, D, c, parts, part_rows, v);
 #pragma unroll
     for (int i = 0; i < kCols; ++i) acc[i] += v[i];
   }
@@ -107,23 +138,26 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void *__restric
 
 }  // namespace
 
-void launch_combine(const moe_layer_desc *d, int32_t T, const void *y_sorted, bool ys_bf16,
+void launch_combine(const moe_layer_desc *d, int32_t T, const void *y_sorted, const int8_t *ys_sh,
                     const int32_t *inv_order, const float *topk_w, void *y, int32_t out_dtype,
-                    void *stream, StageMarker *mk) {
+                    void *stream, StageMarker *mk, int parts) {
   const int N = T * d->top_k, D = d->d_model;
+  if (parts > 1 && ys_sh) throw std::invalid_argument("combine: partial rows are fp32");
+  if (ys_sh && D % kYsBlock) throw std::invalid_argument("combine: fp16 rows need d_model % 64 == 0");
+  const int64_t part_rows = int64_t(N) + int64_t(d->n_shared) * T;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(T, (D + kThreads * kCols - 1) / (kThreads * kCols));
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, y_sorted, inv_order, topk_w, T, d->top_k, d->n_shared,
-                       N, D, y);
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, y_sorted, ys_sh, inv_order, topk_w, T, d->top_k,
+                       d->n_shared, N, D, parts, part_rows, y);
   };
   auto by_out = [&](auto ys_tag) {
-    constexpr bool YS = decltype(ys_tag)::value;
-    if (out_dtype == MOE_DT_BF16) go(combine_kernel<YS, kDtBF16>);
-    else if (out_dtype == MOE_DT_F16) go(combine_kernel<YS, kDtF16>);
-    else go(combine_kernel<YS, kDtF32>);
+    constexpr bool F16E = decltype(ys_tag)::value;
+    if (out_dtype == MOE_DT_BF16) go(combine_kernel<F16E, kDtBF16>);
+    else if (out_dtype == MOE_DT_F16) go(combine_kernel<F16E, kDtF16>);
+    else go(combine_kernel<F16E, kDtF32>);
   };
-  if (ys_bf16) by_out(std::true_type{});
+  if (ys_sh) by_out(std::true_type{});
   else by_out(std::false_type{});
   if (mk) mk->mark("combine");
 }

@@ -234,9 +234,10 @@ void launch_gemv(const moe_layer_desc *d, int32_t T, const void *x, const int32_
 void launch_expert_ffn(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
                        const moe_weights *w, const int32_t *counters, const PlanItem *act_items,
                        const PlanItem *tiles, int64_t max_tiles, const FfnScratch &sc, void *ys,
-                       bool ys_bf16, void *stream, StageMarker *mk) {
+                       int8_t *ys_sh, void *stream, StageMarker *mk, int down_parts) {
   if (use_mfma(d)) {
-    launch_expert_ffn_mfma(d, T, x, row_map, w, counters, tiles, max_tiles, sc, ys, ys_bf16, stream, mk);
+    launch_expert_ffn_mfma(d, T, x, row_map, w, counters, tiles, max_tiles, sc, ys, ys_sh, stream, mk,
+                           down_parts);
     return;
   }
   // The vector-unit kernels write fp32 rows (the workspace copy is fp32 for

@@ -41,6 +41,7 @@
 // Activations and scales are staged in LDS in slabs of 128 reduction
 // elements, double buffered: the global loads of slab s+1 are in flight in
 // registers while slab s is multiplied.
+#include <stdexcept>
 #include <type_traits>
 
 #include "device_common.h"
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(256) void act_f16_kernel(const uint16_t *x, int T, 
 struct GemmArgs {
   const void *act;          // gate/up: x [T][K] (bf16; fp16 copy for affine); down: h [rows][K]
   const int8_t *act_sh;     // affine: gate/up token exponents [T]; down h exponents [rows][nblk]
-  int8_t *out_sh;           // affine gate/up: h exponents [rows][nblk]
+  int8_t *out_sh;           // affine gate/up: h exponents [rows][nblk]; down: y exponents [rows][n_out/64] (or null)
   int nblk;                 // h exponent blocks per row
   const int32_t *row_map;   // gate/up only
   int T, N, K;              // token count, routed rows, reduction length
@@ -139,9 +140,11 @@ struct GemmArgs {
   const uint16_t *s1, *b1;
   const int32_t *counters;  // [1] = number of tiles
   const PlanItem *tiles;
-  void *out;                // gate/up: h [rows][F] (bf16, or fp16 for affine); down: y [rows][D]
-  int out_bf16;             // down: y rows as bf16 (else fp32)
+  void *out;                // gate/up: h [rows][F] (bf16, or fp16 for affine); down: y [rows][D], fp16 with
+                            // exponents when out_sh is set, else fp32
   int bx_major;             // work order: column block major (experts with several tiles), else tile major
+  int kz;                   // down: reduction parts (fp32 partial rows at out + z * part_stride), else 1
+  int64_t part_stride;
 };
 
 // GPS: groups per slab (128 / group size; 1 for dense weights).
@@ -207,9 +210,10 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
   // stage the same activation rows) share an L2 and every XCD gets an equal
   // share.  Linear ids past the 8 ranges exit.
   const int nbx = gridDim.x;
-  const int total = nbx * gridDim.y;
-  const int work = a.counters[1] * nbx;
-  const int lin = blockIdx.y * nbx + blockIdx.x;
+  const int total = nbx * gridDim.y * gridDim.z;
+  const int n_tiles = a.counters[1];
+  const int work = n_tiles * nbx * a.kz;
+  const int lin = (blockIdx.z * gridDim.y + blockIdx.y) * nbx + blockIdx.x;
   const int per = (work + 7) / 8;
   int item = lin;
   if (8 * per <= total) {
@@ -218,17 +222,21 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
     item = (lin % 8) * per + slot;
   }
   if (item >= work) return;
-  // Tile-major order puts the column blocks of a tile next to each other
-  // (they stage the same activation rows); column-block-major order puts the
-  // tiles of one expert next to each other (they read the same weights).
-  const int n_tiles = a.counters[1];
+  // reduction part (outermost), then the tile and column block.  Tile-major
+  // order puts the column blocks of a tile next to each other (they stage
+  // the same activation rows); column-block-major order puts the tiles of one
+  // expert next to each other (they read the same weights).
+  const int z = item / (n_tiles * nbx);
+  item -= z * n_tiles * nbx;
   const int tile_id = a.bx_major ? item % n_tiles : item / nbx, bx = a.bx_major ? item / n_tiles : item % nbx;
   const PlanItem tile = a.tiles[tile_id];
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
   const int lr = lane & 15, lg = lane >> 4;  // operand row / reduction quarter of this lane
   const int K = a.K, KW = AFF ? K * QB / 32 : 0, G = K / (kKS / GPS);
-  const int nslab = (K + kKS - 1) / kKS;
+  // this part's slabs: sbeg .. sbeg + nslab - 1 (the host keeps every part non-empty)
+  const int nslab_all = (K + kKS - 1) / kKS, ns = (nslab_all + a.kz - 1) / a.kz;
+  const int sbeg = z * ns, nslab = min(ns, nslab_all - sbeg);
   const int col0 = (bx * kNW + wave) * NTH * 16;  // first output column of this wave
   const bool col_ok = col0 < a.n_out;              // whole wave in or out (n_out % 64 == 0)
 
@@ -260,7 +268,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
   // (K = 64 mod 128): its second half is read from a clamped address and
   // multiplied by zero scales (affine) or zeroed activations (dense).
   auto load_slab = [&](int s, WSlab<QB> &dst) {
-    s = min(s, nslab - 1);
+    s = sbeg + min(s, nslab - 1);
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
       if constexpr (AFF) {
@@ -320,7 +328,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
   uint16_t sraw[GPS][2];
   int stg_sh[PPT];  // affine down: h exponents of the staged rows' slab
   auto stage_load = [&](int s) {
-    s = min(s, nslab - 1);
+    s = sbeg + min(s, nslab - 1);
     const int k = s * kKS + piece * 8;
 #pragma unroll
     for (int p = 0; p < PPT; ++p) {
@@ -627,6 +635,28 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
   if (!col_ok) return;
 
   // Epilogue: lane holds outputs n = col + lg*4 + i of tile row m = rb*16 + lr.
+  // down with fp16 outputs: one exponent per (row, this wave's 64 columns),
+  // from the row's largest magnitude over the four lanes lg that hold it.
+  int ysh[RB] = {};
+  if constexpr (!GATEUP) {
+    static_assert(kNT * 16 == kYsBlock, "a wave writes one exponent block of each row");
+    if (a.out_sh) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float mx = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NTH; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[nt][rb][i]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        ysh[rb] = f16_shift(mx);
+        const int m = rb * 16 + lr;
+        if (lg == 0 && m < tile.rows)
+          a.out_sh[(tile.row0 + m) * (a.n_out / kYsBlock) + col0 / kYsBlock] = int8_t(ysh[rb]);
+      }
+    }
+  }
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int m = rb * 16 + lr;
@@ -644,12 +674,14 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
         }
         const uint2 o = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
         *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + row * a.n_out + c) = o;
-      } else if (a.out_bf16) {
-        const uint2 o = make_uint2(f32_to_bf16_bits(acc[nt][rb][0]) | (f32_to_bf16_bits(acc[nt][rb][1]) << 16),
-                                   f32_to_bf16_bits(acc[nt][rb][2]) | (f32_to_bf16_bits(acc[nt][rb][3]) << 16));
-        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + row * a.n_out + c) = o;
+      } else if (a.out_sh) {
+        const float sc = pow2(-ysh[rb]);
+        const h2 v01 = {(_Float16)(acc[nt][rb][0] * sc), (_Float16)(acc[nt][rb][1] * sc)};
+        const h2 v23 = {(_Float16)(acc[nt][rb][2] * sc), (_Float16)(acc[nt][rb][3] * sc)};
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + row * a.n_out + c) =
+            make_uint2(__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23));
       } else {
-        *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + row * a.n_out + c) =
+        *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + z * a.part_stride + row * a.n_out + c) =
             make_float4(acc[nt][rb][0], acc[nt][rb][1], acc[nt][rb][2], acc[nt][rb][3]);
       }
     }
@@ -695,8 +727,7 @@ struct DecArgs {
   const uint16_t *s1, *b1;
   const int32_t *counters;
   const PlanItem *tiles;
-  void *out;                // gate/up: h bf16 [rows][F]; down: y [rows][D]
-  int out_bf16;
+  void *out;                // gate/up: h bf16 [rows][F]; down: y fp32 [rows][D]
 };
 
 template <bool GATEUP, int QB, int kMaxSlabs>
@@ -878,13 +909,7 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(DecArgs a) {
     }
   } else if (col_ok && m < tile.rows) {
     const int c = col0 + 4 * lg;
-    if (a.out_bf16) {
-      *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + row * a.n_out + c) =
-          make_uint2(f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
-                     f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16));
-    } else {
-      *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + row * a.n_out + c) = make_float4(v[0], v[1], v[2], v[3]);
-    }
+    *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + row * a.n_out + c) = make_float4(v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -892,7 +917,7 @@ template <int MODE, int QB, int RB, int GPS>
 void launch_one(const GemmArgs &ga, int64_t max_tiles, hipStream_t s) {
   constexpr int NTH = MODE != kDown ? kNT / 2 : kNT;
   const int cols_per_block = kNW * NTH * 16;
-  const dim3 grid((ga.n_out + cols_per_block - 1) / cols_per_block, unsigned(max_tiles));
+  const dim3 grid((ga.n_out + cols_per_block - 1) / cols_per_block, unsigned(max_tiles), unsigned(ga.kz));
   // 16-row tiles fit two or more waves per SIMD by themselves.
   constexpr bool kFits = RB == 1;
   if constexpr (kFits) hipLaunchKernelGGL((grouped_gemm_kernel<MODE, QB, RB, GPS>), grid, dim3(kThreads), 0, s, ga);
@@ -959,6 +984,33 @@ static int use_bx_major(const moe_layer_desc *d, int32_t T) {
   return rows_per_expert >= 2 * plan_tile_rows(d, T) ? 1 : 0;
 }
 
+// The decode tiles: 16-row tiles of affine layers with at most one routed
+// row per expert on average and both reduction lengths within kDecMaxK.
+static bool decode_tiles(const moe_layer_desc *d, int32_t T) {
+  return use_mfma(d) && plan_tile_rows(d, T) == 16 && affine(d) && int64_t(T) * d->top_k <= d->n_experts &&
+         d->d_model <= kDecMaxK && d->d_ff <= kDecMaxK;
+}
+
+int ffn_down_parts(const moe_layer_desc *d, int32_t T) {
+  // Few workgroups in the down projection (few tiles, long reduction, as in a
+  // dense layer with 8 experts): split the reduction until about 512
+  // workgroups, at least two slabs per part.
+  if (T <= 0 || !use_mfma(d) || decode_tiles(d, T)) return 1;
+  const int64_t R = int64_t(T) * d->top_k + int64_t(d->n_shared) * T;
+  const int tr = plan_tile_rows(d, T);
+  const int64_t tiles = std::max<int64_t>(std::min<int64_t>(R, d->n_experts + d->n_shared), (R + tr - 1) / tr);
+  const int64_t nbx = (d->d_model + kNRows - 1) / kNRows;
+  const int nslab = (d->d_ff + kKS - 1) / kKS;
+  int kz = 1;
+  while (tiles * nbx * kz < 512 && kz < 8 && nslab >= 4 * kz) kz *= 2;
+  const int ns = (nslab + kz - 1) / kz;
+  return (nslab + ns - 1) / ns;  // every part non-empty
+}
+
+bool ys_f16e(const moe_layer_desc *d, int32_t T) {
+  return use_mfma(d) && !decode_tiles(d, T) && ffn_down_parts(d, T) == 1;
+}
+
 int plan_tile_rows(const moe_layer_desc *d, int32_t T) {
   // Decode-sized groups (T*k/E <= 8 rows per expert on average, the pages'
   // small-group regime) use 16-row tiles; larger groups 64-row tiles.
@@ -981,15 +1033,15 @@ void launch_gate_up_raw_mfma(const moe_layer_desc *d, int32_t T, const void *x, 
              d->gate_up_fused, 0, 0, int(f16),
              pg.w, static_cast<const uint16_t *>(pg.scales), static_cast<const uint16_t *>(pg.biases),
              w->up.w, static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases),
-             counters, tiles, gu, 0, use_bx_major(d, T)};
+             counters, tiles, gu, use_bx_major(d, T), 1, 0};
   if (plan_tile_rows(d, T) == 16) launch_gemm<kGateUpRaw, 1>(g, qb, d->group_size, max_tiles, s);
   else launch_gemm<kGateUpRaw, 4>(g, qb, d->group_size, max_tiles, s);
 }
 
 void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
                             const moe_weights *w, const int32_t *counters, const PlanItem *tiles,
-                            int64_t max_tiles, const FfnScratch &sc, void *y_sorted, bool ys_bf16, void *stream,
-                            StageMarker *mk) {
+                            int64_t max_tiles, const FfnScratch &sc, void *y_sorted, int8_t *ys_sh, void *stream,
+                            StageMarker *mk, int down_parts) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool aff = affine(d);
   const bool f16 = d->act_dtype == MOE_DT_F16;
@@ -1009,23 +1061,24 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
               d->gate_up_fused, d->swiglu_round_bf16, geglu, int(f16),
               pg.w, static_cast<const uint16_t *>(pg.scales), static_cast<const uint16_t *>(pg.biases),
               w->up.w, static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases),
-              counters, tiles, sc.h, 0, bx_major};
-  GemmArgs dn{sc.h, sc.hsh, nullptr, nblk, nullptr, T, T * d->top_k, d->d_ff, d->d_model, 0, 0, 0, int(f16),
+              counters, tiles, sc.h, bx_major, 1, 0};
+  if (ys_sh && (down_parts > 1 || decode_tiles(d, T)))
+    throw std::invalid_argument("expert ffn: fp16 outputs need the 64- or 16-row tiles without a reduction split");
+  GemmArgs dn{sc.h, sc.hsh, ys_sh, nblk, nullptr, T, T * d->top_k, d->d_ff, d->d_model, 0, 0, 0, int(f16),
               w->down.w, static_cast<const uint16_t *>(w->down.scales), static_cast<const uint16_t *>(w->down.biases),
-              nullptr, nullptr, nullptr, counters, tiles, y_sorted, ys_bf16, bx_major};
-  if (tr == 16 && aff && int64_t(T) * d->top_k <= d->n_experts && d->d_model <= kDecMaxK &&
-      d->d_ff <= kDecMaxK) {
+              nullptr, nullptr, nullptr, counters, tiles, y_sorted, bx_major, down_parts,
+              (int64_t(T) * d->top_k + int64_t(d->n_shared) * T) * d->d_model};
+  if (decode_tiles(d, T)) {
     // at most one routed row per expert on average: whole-K loads per wave
     // (one memory round trip), h as bf16 between the two projections
     DecArgs dg{sc.x16, sc.xsh, row_map, T, T * d->top_k, d->d_model, d->d_ff, d->gate_up_fused,
                d->swiglu_round_bf16, geglu, gs, int(f16), static_cast<const uint32_t *>(pg.w),
                static_cast<const uint16_t *>(pg.scales), static_cast<const uint16_t *>(pg.biases),
                static_cast<const uint32_t *>(w->up.w), static_cast<const uint16_t *>(w->up.scales),
-               static_cast<const uint16_t *>(w->up.biases), counters, tiles, sc.h, 0};
+               static_cast<const uint16_t *>(w->up.biases), counters, tiles, sc.h};
     DecArgs dd{sc.h, nullptr, nullptr, T, T * d->top_k, d->d_ff, d->d_model, 0, 0, 0, gs, int(f16),
                static_cast<const uint32_t *>(w->down.w), static_cast<const uint16_t *>(w->down.scales),
-               static_cast<const uint16_t *>(w->down.biases), nullptr, nullptr, nullptr, counters, tiles, y_sorted,
-               ys_bf16};
+               static_cast<const uint16_t *>(w->down.biases), nullptr, nullptr, nullptr, counters, tiles, y_sorted};
     launch_decode<true>(dg, qb, max_tiles, s);
     if (mk) mk->mark("gateup_mfma");
     launch_decode<false>(dd, qb, max_tiles, s);

@@ -106,7 +106,7 @@ int moe_expert_ffn(const moe_layer_desc *desc, int32_t T, const void *x, const i
   launch_plan(desc, T, expert_off, at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items),
               at<PlanItem>(ws, L.tiles), stream);
   launch_expert_ffn(desc, T, x, row_map, w, at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items),
-                    at<PlanItem>(ws, L.tiles), L.max_tiles, ffn_scratch(ws, L, false), y_sorted, false, stream);
+                    at<PlanItem>(ws, L.tiles), L.max_tiles, ffn_scratch(ws, L, false), y_sorted, nullptr, stream);
   return hip_status();
 }
 
@@ -119,7 +119,7 @@ int moe_combine(const moe_layer_desc *desc, int32_t T, const float *y_sorted, co
       (s = validate_ptr(y)))
     return s;
   if (T == 0) return MOE_OK;
-  launch_combine(desc, T, y_sorted, false, inv_order, topk_w, y, out_dtype, stream);
+  launch_combine(desc, T, y_sorted, nullptr, inv_order, topk_w, y, out_dtype, stream);
   return hip_status();
 }
 
@@ -149,11 +149,13 @@ static int forward_impl(const moe_layer_desc *desc, int32_t T, const void *x, co
   if (!route_fuses_dispatch(desc, T))
     launch_dispatch(desc, T, idx, 64, dsp.order, dsp.inv_order, dsp.row_map, dsp.expert_off, dsp.tile_off,
                     dsp.counters, dsp.act_items, dsp.tiles, at<int32_t>(ws, L.dsp), stream, mk);
+  const int parts = ffn_down_parts(desc, T);
+  int8_t *ys_sh = ys_f16e(desc, T) ? at<int8_t>(ws, L.ys_sh) : nullptr;
   launch_expert_ffn(desc, T, x, at<int32_t>(ws, L.row_map), w, at<int32_t>(ws, L.counters),
                     at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles), L.max_tiles,
-                    ffn_scratch(ws, L, x16_ready), at<void>(ws, L.y_sorted), ys_bytes(desc) == 2, stream, mk);
-  launch_combine(desc, T, at<void>(ws, L.y_sorted), ys_bytes(desc) == 2, at<int32_t>(ws, L.inv_order), wt, y, out_dtype,
-                 stream, mk);
+                    ffn_scratch(ws, L, x16_ready), at<void>(ws, L.y_sorted), ys_sh, stream, mk, parts);
+  launch_combine(desc, T, at<void>(ws, L.y_sorted), ys_sh, at<int32_t>(ws, L.inv_order), wt, y, out_dtype, stream,
+                 mk, parts);
   return hip_status();
 }
 

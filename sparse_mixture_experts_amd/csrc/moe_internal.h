@@ -37,7 +37,6 @@ inline int64_t h_bytes(const moe_layer_desc *d) { return d->act_dtype == MOE_DT_
 bool use_mfma(const moe_layer_desc *d);
 // Bytes per element of the workspace copy of the expert outputs: bf16 where
 // the matrix-core kernels serve a bf16 layer, fp32 otherwise.
-inline int64_t ys_bytes(const moe_layer_desc *d) { return use_mfma(d) && d->act_dtype == MOE_DT_BF16 ? 2 : 4; }
 
 // Workspace carve-up.  Every section is 256-byte aligned.
 struct Workspace {
@@ -52,7 +51,8 @@ struct Workspace {
   size_t h;                           // [N+S*T][d_ff] h_bytes
   size_t hsh;                         // [N+S*T][ceil(d_ff/128)] int8 (affine layers)
   size_t x16, xsh;                    // [T][d_model] fp16, [T] int8 (affine layers)
-  size_t y_sorted;                    // [N+S*T][d_model] ys_bytes
+  size_t y_sorted;                    // [N+S*T][d_model]: fp16 (ys_f16e), fp32, or [parts] fp32 partial rows
+  size_t ys_sh;                       // [N+S*T][d_model/64] int8 exponents (ys_f16e)
   size_t total;
   int64_t max_tiles;
 };
@@ -116,19 +116,31 @@ struct FfnScratch {
 };
 constexpr int kHBlock = 128;  // h columns per exponent block
 
-// Expert FFN over the plan: y_sorted rows for all routed and shared rows.
+// Reduction parts of the down projection inside moe_forward (1: none).  With
+// more, the expert outputs are fp32 partial rows [parts][N+S*T][d_model]
+// that the combine adds in part order.
+int ffn_down_parts(const moe_layer_desc *d, int32_t T);
+// Expert outputs inside moe_forward as fp16 values v with one power-of-two
+// exponent e per (row, 64 columns), y = v * 2^e: on the 16-bit matrix-core
+// tiles when the down reduction is not split.  Otherwise fp32.
+bool ys_f16e(const moe_layer_desc *d, int32_t T);
+constexpr int kYsBlock = 64;  // expert-output columns per exponent
+
+// Expert FFN over the plan: y_sorted rows for all routed and shared rows,
+// fp32 (ys_sh null), fp16 with exponents in ys_sh (ys_f16e layers), or fp32
+// partial rows (down_parts > 1).
 void launch_expert_ffn(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
                        const moe_weights *w, const int32_t *counters, const PlanItem *act_items,
                        const PlanItem *tiles, int64_t max_tiles, const FfnScratch &sc, void *y_sorted,
-                       bool ys_bf16, void *stream, StageMarker *mk = nullptr);
+                       int8_t *ys_sh, void *stream, StageMarker *mk = nullptr, int down_parts = 1);
 
 // Row-tile height of the work plan for this layer and token count, and
 // whether the grouped MFMA kernels serve the layer (else dequant-GEMV).
 int plan_tile_rows(const moe_layer_desc *d, int32_t T);
 void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
                             const moe_weights *w, const int32_t *counters, const PlanItem *tiles,
-                            int64_t max_tiles, const FfnScratch &sc, void *y_sorted, bool ys_bf16, void *stream,
-                            StageMarker *mk);
+                            int64_t max_tiles, const FfnScratch &sc, void *y_sorted, int8_t *ys_sh, void *stream,
+                            StageMarker *mk, int down_parts = 1);
 
 // Backward with respect to x.  Intermediates in the backward workspace (R
 // sorted rows): g and u, v = Wd^T dy (per reduction split), dw, the rows'
@@ -172,8 +184,10 @@ void launch_gate_up_raw_mfma(const moe_layer_desc *d, int32_t T, const void *x, 
                              const FfnScratch &sc, float *gu, void *stream);
 
 // Combine.
-void launch_combine(const moe_layer_desc *d, int32_t T, const void *y_sorted, bool ys_bf16,
+// Combine of fp32 rows (ys_sh null), fp16 rows with exponents ys_sh, or
+// parts > 1 fp32 partial rows added in part order.
+void launch_combine(const moe_layer_desc *d, int32_t T, const void *y_sorted, const int8_t *ys_sh,
                     const int32_t *inv_order, const float *topk_w, void *y, int32_t out_dtype,
-                    void *stream, StageMarker *mk = nullptr);
+                    void *stream, StageMarker *mk = nullptr, int parts = 1);
 
 }  // namespace moe

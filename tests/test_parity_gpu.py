@@ -99,6 +99,13 @@ MID = {
     "mid-f16-q8-decode-geglu": LayerSpec("mid-f16-q8-decode-geglu", T=3, d_model=512, d_ff=256, n_experts=64,
                                          top_k=8, act="f16", wfmt="q8", group_size=128, activation="geglu",
                                          seed=47),
+    # long down reductions over few tiles: the down projection splits its
+    # reduction into fp32 partial rows (4 parts, the last one short and ending
+    # in a half slab; 8 parts of two slabs with a shared expert)
+    "mid-bf16-long-down": LayerSpec("mid-bf16-long-down", T=64, d_model=256, d_ff=2624, n_experts=4, top_k=2,
+                                    seed=52),
+    "mid-q4-long-down-shared": LayerSpec("mid-q4-long-down-shared", T=8, d_model=256, d_ff=2048, n_experts=8,
+                                         top_k=2, n_shared=1, wfmt="q4", gate_up_fused=True, seed=53),
 }
 FULL = {**inputs.CONFIGS, **inputs.VARIANTS}
 SAMPLE = 48  # tokens compared per full-size layer (all when T is smaller)
