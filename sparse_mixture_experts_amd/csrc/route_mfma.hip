@@ -112,10 +112,11 @@ __global__ __launch_bounds__(kThreads) void router_transpose_kernel(const uint16
 
 // ---- 2. L~ = x . W + bias on MFMA ------------------------------------------
 // Block tile 64 experts x 64 tokens, 8 waves; wave (we, wt) owns 32 experts x
-// 16 tokens = 2 MFMA tiles.  blockIdx.z takes one of gridDim.z equal runs of
-// the 64-column chunks and writes its own partial L~ (lt + z*T*E); the
-// certification adds the partials in z order.  Operand A = WT rows (experts), operand B = x rows
-// (tokens); a lane's 4 results are 4 consecutive experts of one token.
+// 16 tokens = 2 MFMA tiles.  The grid is (expert tiles, token tiles, runs):
+// run z takes one of gridDim.z equal runs of the 64-column chunks and writes
+// its own partial L~ (lt + z*T*E); the certification adds the partials in z
+// order.  Operand A = WT rows (experts), operand B = x rows (tokens); a
+// lane's 4 results are 4 consecutive experts of one token.
 // The blocks of the first token tile also add up the squared-norm partials of
 // their 64 experts: normp[n_kb][e] -> normp[n_kb + 0 * E + e] (the row after
 // the partials).
@@ -129,8 +130,17 @@ __global__ __launch_bounds__(kMfThreads) void router_mfma_kernel(const uint16_t 
   __shared__ uint16_t sab[2][2][64][kChunk + 8];  // [buffer][expert tile, token tile][row][col]
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
   const int lr = lane & 15, lg = lane >> 4;
-  const int e0 = blockIdx.x * 64, t0 = blockIdx.y * 64;
-  if (blockIdx.y == 0 && blockIdx.z == 0 && tid < 64 && e0 + tid < E) {
+  // XCD-aware order.  Workgroups go to the 8 XCDs round-robin by linear id;
+  // each XCD takes a contiguous range of (expert tile fastest, token tile,
+  // chunk run) items, so the expert tiles of a token tile run on one XCD and
+  // read that token tile through the same L2 (x is then fetched once, not
+  // once per XCD).
+  const int nbx = gridDim.x, nby = gridDim.y, total = nbx * nby * gridDim.z;
+  const int lin = (blockIdx.z * nby + blockIdx.y) * nbx + blockIdx.x;
+  const int item = total % 8 == 0 ? (lin % 8) * (total / 8) + lin / 8 : lin;
+  const int bx = item % nbx, by = (item / nbx) % nby, bz = item / (nbx * nby);
+  const int e0 = bx * 64, t0 = by * 64;
+  if (by == 0 && bz == 0 && tid < 64 && e0 + tid < E) {
     float s = 0.f;
     for (int kb = 0; kb < n_kb; ++kb) s += normp[int64_t(kb) * E + e0 + tid];
     normp[int64_t(n_kb) * E + e0 + tid] = s;
@@ -140,17 +150,19 @@ __global__ __launch_bounds__(kMfThreads) void router_mfma_kernel(const uint16_t 
   acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // staging: threads 0..255 fill the expert tile, 256..511 the token tile;
-  // thread -> (row (tid % 256) / 4, 16 columns (tid % 4) * 16).  Chunk c+2 is
-  // loaded into registers while chunk c is multiplied from one LDS buffer and
-  // chunk c+1 is written to the other.
+  // thread -> (row (tid % 256) / 4, 16 columns (tid % 4) * 16).  kRing chunks
+  // are in flight in registers: while chunk c is multiplied from one LDS
+  // buffer, chunk c+1 is written to the other and chunk c+1+kRing is loaded
+  // into the register slot it leaves.  Each chunk is a short step, so a deep
+  // ring is what keeps the memory round trips overlapped.
   const int which = tid / 256;  // 0: experts, 1: tokens
   const int sr = (tid % 256) / 4, sc = (tid % 4) * 16;
   const int64_t src = which == 0 ? int64_t(min(e0 + sr, E - 1)) * D : int64_t(min(t0 + sr, T - 1)) * D;
   const uint16_t *sbase = which == 0 ? wt : x;
   const bool ok = which == 0 ? e0 + sr < E : t0 + sr < T;
   const int C = D / kChunk / gridDim.z;  // chunks of this block's run
-  const int c_base = blockIdx.z * C;
-  lt += int64_t(blockIdx.z) * T * E;
+  const int c_base = bz * C;
+  lt += int64_t(bz) * T * E;
   struct Stage { uint4 v0, v1; };
   auto load = [&](int c, Stage &st) __attribute__((always_inline)) {
     const uint4 *p = reinterpret_cast<const uint4 *>(sbase + src + (c_base + min(c, C - 1)) * kChunk + sc);
@@ -163,15 +175,16 @@ __global__ __launch_bounds__(kMfThreads) void router_mfma_kernel(const uint16_t 
     *reinterpret_cast<uint4 *>(&sab[buf][which][sr][sc]) = keep(st.v0);
     *reinterpret_cast<uint4 *>(&sab[buf][which][sr][sc + 8]) = keep(st.v1);
   };
-  Stage ring[2];
-  load(0, ring[0]);
-  load(1, ring[1]);
+  constexpr int kRing = 2;  // even: LDS buffer of chunk c is c % 2
+  Stage ring[kRing];  // slot c % kRing holds chunk c until it is written to LDS
+#pragma unroll
+  for (int u = 0; u < kRing; ++u) load(u, ring[u]);
   store(0, ring[0]);
-  load(2, ring[0]);
+  load(kRing, ring[0]);
   __syncthreads();
   // chunk c from LDS buffer buf; then chunk c+1 (held in nx) to the other
   // buffer, whose last readers (chunk c-1) are past the previous barrier, and
-  // chunk c+3 into nx.
+  // chunk c+1+kRing into nx.
   auto step = [&](int c, int buf, Stage &nx) __attribute__((always_inline)) {
     if constexpr (DT == kDtBF16) {
       bf16x8 av[2][2], bv[2];
@@ -215,12 +228,13 @@ __global__ __launch_bounds__(kMfThreads) void router_mfma_kernel(const uint16_t 
       }
     }
     store(buf ^ 1, nx);
-    load(c + 3, nx);
+    load(c + 1 + kRing, nx);
     __syncthreads();
   };
-  for (int c = 0; c < C; c += 2) {
-    step(c, 0, ring[1]);
-    if (c + 1 < C) step(c + 1, 1, ring[0]);
+  for (int c = 0; c < C; c += kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u)
+      if (c + u < C) step(c + u, u & 1, ring[(u + 1) % kRing]);
   }
   const int t = t0 + wtk * 16 + lr;
 #pragma unroll
@@ -230,7 +244,7 @@ __global__ __launch_bounds__(kMfThreads) void router_mfma_kernel(const uint16_t 
     if (t < T) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (eb + q < E) lt[int64_t(t) * E + eb + q] = v[q] + (bias && blockIdx.z == 0 ? bias[eb + q] : 0.0f);
+        if (eb + q < E) lt[int64_t(t) * E + eb + q] = v[q] + (bias && bz == 0 ? bias[eb + q] : 0.0f);
     }
   }
 }
@@ -273,6 +287,14 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
     const float l1 = a.lt[(int64_t(a.n_lt > 1 ? a.T : 0) + t) * E + ec];
     lv[m] = e < E ? (a.n_lt > 1 ? l0 + l1 : l0) : -INFINITY;
   }
+  // max_e ||W_e|| and max |bias| (loads in flight with those of x)
+  float wn = 0.f, bmax = 0.f;
+#pragma unroll
+  for (int m = 0; m < MPL; ++m) {
+    const int e = min(lane + kWave * m, E - 1);  // repeats of expert E-1 do not change a max
+    wn = fmaxf(wn, a.wnorm[e]);
+    if (a.bias) bmax = fmaxf(bmax, fabsf(a.bias[e]));
+  }
   // ||x_t||^2: d <= 64 * 64 gives at most 8 pieces of 8 per lane, all loaded
   // together; the same registers give the fp16 staging row when asked.
   float xs = 0.f;
@@ -292,13 +314,6 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
   }
   xs = wave_sum(xs);
   if (a.x16) row_f16_store(xr, D, a.x16 + int64_t(t) * D, a.xsh + t, DT == kDtF16);  // xr dies here
-  float wn = 0.f, bmax = 0.f;
-#pragma unroll
-  for (int m = 0; m < MPL; ++m) {
-    const int e = min(lane + kWave * m, E - 1);  // repeats of expert E-1 do not change a max
-    wn = fmaxf(wn, a.wnorm[e]);
-    if (a.bias) bmax = fmaxf(bmax, fabsf(a.bias[e]));
-  }
   wn = wave_max(wn);
   bmax = wave_max(bmax);
   const float bound = a.gamma * (sqrtf(xs) * sqrtf(wn) * 1.001f + bmax);
@@ -346,11 +361,16 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
   const int slots = kWave / C;
   const int slot = lane / C, ch = lane % C;
   const bool lane_on = slot < slots;
-  uint32_t xw[32];  // this lane's x chunk as packed 16-bit values (64)
+  float xf[kChunk];  // this lane's x chunk as fp32, widened once for all its chains
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const uint4 v = *reinterpret_cast<const uint4 *>(a.x + int64_t(t) * D + ch * kChunk + q * 8);
-    xw[4 * q] = v.x; xw[4 * q + 1] = v.y; xw[4 * q + 2] = v.z; xw[4 * q + 3] = v.w;
+    const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      xf[8 * q + 2 * h] = half_lo<DT>(vw[h]);
+      xf[8 * q + 2 * h + 1] = half_hi<DT>(vw[h]);
+    }
   }
   // Lane (slot, ch) takes candidates slot, slot + slots, ...; the router row
   // chunk of the next one is loaded while the current chain runs.
@@ -366,8 +386,8 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
       const uint32_t wv4[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        part = __builtin_fmaf(half_lo<DT>(xw[4 * q + h]), half_lo<DT>(wv4[h]), part);
-        part = __builtin_fmaf(half_hi<DT>(xw[4 * q + h]), half_hi<DT>(wv4[h]), part);
+        part = __builtin_fmaf(xf[8 * q + 2 * h], half_lo<DT>(wv4[h]), part);
+        part = __builtin_fmaf(xf[8 * q + 2 * h + 1], half_hi<DT>(wv4[h]), part);
       }
     }
     return part;
