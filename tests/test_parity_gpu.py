@@ -275,6 +275,43 @@ def test_forward_mid(name):
     _forward_check(name)
 
 
+def _scaled_bf16_bits(bits: np.ndarray, shift: int) -> np.ndarray:
+    """bf16 bit patterns times 2^shift, exactly (asserted)."""
+    f = inputs.bf16_bits_to_f32(bits).astype(np.float64) * 2.0 ** shift
+    out = inputs.to_bf16_bits(f.astype(np.float32)).reshape(bits.shape)
+    assert np.array_equal(inputs.bf16_bits_to_f32(out).astype(np.float64), f)
+    return out
+
+
+@pytest.mark.parametrize("name,shift", [("mid-bf16", 24), ("mid-bf16", -24), ("mid-q4", 20), ("mid-q4", -20),
+                                        ("mid-q4-g32-geglu-tile16", 20), ("mid-q4-decode", -20),
+                                        ("mid-bf16-long-down", 24)])
+def test_forward_output_magnitudes(name, shift):
+    """Expert outputs far above fp16's range (2^+20 and more) and far below its
+    normal range: the down weights, or their affine scales and biases, times
+    2^shift exactly.  Expert-output rows stored as fp16 then need nonzero
+    exponents; the result must still be the oracle's within tolerance."""
+    spec = MID[name]
+    L = inputs.gen_layer(spec)
+    down = dict(L["experts"]["down"])
+    for k in (("scales", "biases") if spec.quantized else ("w",)):
+        down[k] = _scaled_bf16_bits(down[k], shift)
+    L = {**L, "experts": {**L["experts"], "down": down}}
+    print(f"[case] {name} down x 2^{shift}", flush=True)
+    g = GpuLayer(L)
+    y, idx, w = g.forward()
+    y, idx = y.cpu().numpy(), idx.cpu().numpy()
+    assert np.all(np.isfinite(y))
+    ry, ridx, _, _ = oracle.forward(pins.desc_of(spec), L["x"], L["w_router"], L["router_bias"], L["experts"])
+    assert np.array_equal(idx, ridx)
+    err = rel_err(y, ry)
+    print(f"[{name} x 2^{shift}] max|err|/RMS = {err:.3g}, RMS(y) = {np.sqrt(np.mean(ry.astype(np.float64) ** 2)):.3g}",
+          flush=True)
+    assert err <= tol_for(spec), err
+    del g
+    _layers.clear()
+
+
 @pytest.mark.parametrize("name", list(FULL))
 def test_forward_full_size(name):
     spec = FULL[name]
