@@ -35,8 +35,6 @@ inline bool affine(const moe_layer_desc *d) {
 // Bytes per element of the GLU intermediate h (16-bit for bf16 and fp16 layers).
 inline int64_t h_bytes(const moe_layer_desc *d) { return d->act_dtype == MOE_DT_F32 ? 4 : 2; }
 bool use_mfma(const moe_layer_desc *d);
-// Bytes per element of the workspace copy of the expert outputs: bf16 where
-// the matrix-core kernels serve a bf16 layer, fp32 otherwise.
 
 // Workspace carve-up.  Every section is 256-byte aligned.
 struct Workspace {
