@@ -106,6 +106,12 @@ MID = {
                                     seed=52),
     "mid-q4-long-down-shared": LayerSpec("mid-q4-long-down-shared", T=8, d_model=256, d_ff=2048, n_experts=8,
                                          top_k=2, n_shared=1, wfmt="q4", gate_up_fused=True, seed=53),
+    # one token (fp16 with router bias and a short last chunk; 256 experts
+    # with the dispatch folded into the selection kernel)
+    "mid-one-token-f16-bias": LayerSpec("mid-one-token-f16-bias", T=1, d_model=352, d_ff=128, n_experts=16, top_k=4,
+                                        act="f16", router_bias="zipf", seed=54),
+    "mid-q4-one-token-e256": LayerSpec("mid-q4-one-token-e256", T=1, d_model=512, d_ff=256, n_experts=256, top_k=8,
+                                       wfmt="q4", seed=55),
 }
 FULL = {**inputs.CONFIGS, **inputs.VARIANTS}
 SAMPLE = 48  # tokens compared per full-size layer (all when T is smaller)
@@ -332,13 +338,14 @@ def test_zero_input_gives_zero_output():
 
 
 @pytest.mark.parametrize("act", ["bf16", "f16"])
-@pytest.mark.parametrize("T", [9, 96])
+@pytest.mark.parametrize("T", [1, 9, 96])
 def test_route_exact_ties_and_zero_rows(T, act):
     """Duplicated router columns tie exactly and zero rows tie everywhere: the
-    lower expert index must win, on both the small-T and the large-T router.
-    fp16 layers also get rows of fp16 subnormals (x * 2^-20) and rows near
-    fp16's largest values (x * 2^12), which the large-T router splits into
-    bf16 head and tail parts."""
+    lower expert index must win, for one token and on the small-T and
+    large-T routers (one token: a zero row for bf16, the duplicated columns
+    alone for fp16).  fp16 layers also get rows of fp16 subnormals (x * 2^-20) and rows
+    near fp16's largest values (x * 2^12), which the large-T router splits
+    into bf16 head and tail parts."""
     spec = LayerSpec("ties", T=T, d_model=256, d_ff=64, n_experts=16, top_k=4, act=act, seed=31)
     L = inputs.gen_layer(spec)
     w = L["w_router"].copy()
@@ -351,7 +358,8 @@ def test_route_exact_ties_and_zero_rows(T, act):
         xf = inputs.f16_bits_to_f32(x)
         x[3::7] = inputs.to_f16_bits(xf[3::7] * np.float32(2.0 ** -20))
         x[5::7] = inputs.to_f16_bits(xf[5::7] * np.float32(2.0 ** 12))
-    x[::7] = 0  # every 7th token: all logits 0
+    if T > 1 or act == "bf16":
+        x[::7] = 0  # every 7th token: all logits 0
     L["x"] = x
     g = GpuLayer(L)
     idx, wt = g.route()
