@@ -165,18 +165,19 @@ __global__ __launch_bounds__(kWave) void route_chunk_kernel(const void *__restri
   __shared__ float xs[kChunk][TT];
   const int lane = threadIdx.x, e = blockIdx.x * kWave + lane, c = blockIdx.y, t0 = blockIdx.z * TT;
   const int kc = c * kChunk, n = min(kChunk, D - kc), nt = min(TT, T - t0);
+  const int ec = min(e, E - 1);
+  // the whole chunk's router column is loaded at once, in flight together
+  // with the token values (one memory round trip)
+  float w[kChunk];
+#pragma unroll
+  for (int u = 0; u < kChunk; ++u) w[u] = load_act<DT>(wr, int64_t(kc + min(u, n - 1)) * E + ec);
 #pragma unroll
   for (int t = 0; t < TT; ++t)
     xs[lane][t] = (lane < n && t < nt) ? load_act<DT>(x, int64_t(t0 + t) * D + kc + lane) : 0.0f;
   __syncthreads();
-  const int ec = min(e, E - 1);
   float p[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t) p[t] = 0.0f;
-  // the whole chunk's router column is loaded at once (one memory round trip)
-  float w[kChunk];
-#pragma unroll
-  for (int u = 0; u < kChunk; ++u) w[u] = load_act<DT>(wr, int64_t(kc + min(u, n - 1)) * E + ec);
 #pragma unroll
   for (int u = 0; u < kChunk; ++u) {
     if (u < n) {
@@ -374,7 +375,11 @@ void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void 
   int n_chunks = C;
   auto logits = [&](auto dt) {
     constexpr int DT = decltype(dt)::value;
-    if (T < 64) {
+    if (T == 1) {
+      // one token: one chain per lane (no idle token slots)
+      const dim3 grid((E + kWave - 1) / kWave, C, 1);
+      hipLaunchKernelGGL((route_chunk_kernel<DT, 1>), grid, dim3(kWave), 0, s, x, w_router, T, D, E, scratch);
+    } else if (T < 64) {
       const dim3 grid((E + kWave - 1) / kWave, C, (T + 7) / 8);
       hipLaunchKernelGGL((route_chunk_kernel<DT, 8>), grid, dim3(kWave), 0, s, x, w_router, T, D, E, scratch);
     } else if (C <= 32) {
