@@ -112,6 +112,9 @@ MID = {
                                         act="f16", router_bias="zipf", seed=54),
     "mid-q4-one-token-e256": LayerSpec("mid-q4-one-token-e256", T=1, d_model=512, d_ff=256, n_experts=256, top_k=8,
                                        wfmt="q4", seed=55),
+    # 32 tokens x 12 slots: the one-wave dispatch at 8 slots per lane
+    "mid-q4-t32-k12": LayerSpec("mid-q4-t32-k12", T=32, d_model=256, d_ff=128, n_experts=64, top_k=12, wfmt="q4",
+                                seed=56),
 }
 FULL = {**inputs.CONFIGS, **inputs.VARIANTS}
 SAMPLE = 48  # tokens compared per full-size layer (all when T is smaller)
