@@ -1007,6 +1007,23 @@ int ffn_down_parts(const moe_layer_desc *d, int32_t T) {
   return (nslab + ns - 1) / ns;  // every part non-empty
 }
 
+int64_t ys_workspace_bytes(const moe_layer_desc *d, int32_t T) {
+  // fp32 rows bound fp16 ones.  Partial rows: a split into p > 1 parts
+  // stopped doubling with tiles * nbx * p < 1024, and R <= 64 * tiles, so
+  // p * R < 1024 * 64 / nbx; p is at most the largest split the reduction
+  // length allows.  Both bounds grow with T, so the size also covers every
+  // smaller T.
+  const int64_t R = int64_t(T) * d->top_k + int64_t(d->n_shared) * T, D = d->d_model;
+  int64_t rows = R;
+  if (use_mfma(d)) {
+    const int nslab = (d->d_ff + kKS - 1) / kKS;
+    const int64_t kzmax = nslab >= 16 ? 8 : nslab >= 8 ? 4 : nslab >= 4 ? 2 : 1;
+    const int64_t nbx = (D + kNRows - 1) / kNRows;
+    rows = std::max(R, std::min(kzmax * R, 1024 * 64 / nbx));
+  }
+  return rows * D * 4;
+}
+
 bool ys_f16e(const moe_layer_desc *d, int32_t T) {
   return use_mfma(d) && !decode_tiles(d, T) && ffn_down_parts(d, T) == 1;
 }

@@ -122,6 +122,8 @@ int ffn_down_parts(const moe_layer_desc *d, int32_t T);
 // exponent e per (row, 64 columns), y = v * 2^e: on the 16-bit matrix-core
 // tiles when the down reduction is not split.  Otherwise fp32.
 bool ys_f16e(const moe_layer_desc *d, int32_t T);
+// Workspace bytes for the expert outputs of any call with at most T tokens.
+int64_t ys_workspace_bytes(const moe_layer_desc *d, int32_t T);
 constexpr int kYsBlock = 64;  // expert-output columns per exponent
 
 // Expert FFN over the plan: y_sorted rows for all routed and shared rows,

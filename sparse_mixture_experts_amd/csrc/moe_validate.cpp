@@ -110,9 +110,8 @@ Workspace workspace_layout(const moe_layer_desc *d, int32_t T) {
   ws.hsh = take(q4 ? size_t(rows) * ((d->d_ff + kHBlock - 1) / kHBlock) : 0);
   ws.x16 = take(q4 ? size_t(T) * d->d_model * 2 : 0);
   ws.xsh = take(q4 ? size_t(T) : 0);
-  const bool f16e = ys_f16e(d, T);
-  ws.y_sorted = take(size_t(rows) * d->d_model * (f16e ? 2 : size_t(4) * ffn_down_parts(d, T)));
-  ws.ys_sh = take(f16e ? size_t(rows) * (d->d_model / kYsBlock) : 0);
+  ws.y_sorted = take(size_t(ys_workspace_bytes(d, T)));
+  ws.ys_sh = take(use_mfma(d) ? size_t(rows) * (d->d_model / kYsBlock) : 0);
   ws.total = o;
   return ws;
 }

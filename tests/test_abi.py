@@ -165,3 +165,25 @@ def test_zero_tokens_is_a_no_op(lib):
     assert lib.moe_combine(ctypes.byref(d), 0, A, A, A, A, 0, None) == moe.MOE_OK
     assert lib.moe_forward(ctypes.byref(d), 0, A, ctypes.byref(weights()), A, 1, None, None, A, need,
                            None) == moe.MOE_OK
+
+
+@pytest.mark.parametrize("shape", [
+    dict(d_model=2048, d_ff=5632, n_experts=8, top_k=2),                        # dense: split down reductions
+    dict(d_model=2048, d_ff=768, n_experts=128, top_k=8, wfmt="q4"),            # decode tiles, then 16-row tiles
+    dict(d_model=2048, d_ff=512, n_experts=512, top_k=10, wfmt="q4"),           # prefill shape
+    dict(d_model=2048, d_ff=1408, n_experts=64, top_k=6, n_shared=2, wfmt="q4"),
+    dict(d_model=256, d_ff=2624, n_experts=4, top_k=2, act="f16"),
+    dict(d_model=64, d_ff=128, n_experts=8, top_k=2, act="f32"),
+])
+def test_workspace_covers_smaller_T(shape):
+    """The header promises that the workspace for T tokens also serves every
+    smaller T: the size must not decrease as T grows, although the layout of
+    the expert outputs changes with T (fp32 rows on decode tiles, fp16 rows
+    with exponents on the 64- and 16-row tiles, fp32 partial rows when the
+    down reduction is split)."""
+    desc = moe.make_desc(**shape)
+    prev = 0
+    for T in range(0, 2200):
+        size = moe.moe_workspace_size(desc, T)
+        assert size >= prev, (T, size, prev)
+        prev = size
