@@ -75,9 +75,10 @@ __device__ __forceinline__ void add_parts(const void *ys, int64_t row, int D, in
 // Block (t, cb): token t, columns cb*256*8 ..; each thread 8 columns.  The
 // token's slot positions and weights are uniform (scalar loads); then all
 // slot rows of a thread (up to 16 fp16 or 8 fp32 rows per round) are in
-// flight together before they are summed in slot order.  parts > 1 (fp32
-// rows only): partial rows part_rows rows apart.
-template <bool F16E, int OUT_DT>
+// flight together before they are summed in slot order; SL slots per round
+// (the launch picks the smallest that covers k, up to 16 fp16 or 8 fp32
+// rows).  parts > 1 (fp32 rows only): partial rows part_rows rows apart.
+template <bool F16E, int OUT_DT, int SL>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const void *__restrict__ ys,
                                                            const int8_t *__restrict__ ys_sh,
                                                            const int32_t *__restrict__ inv,
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void *__restric
   float acc[kCols];
 #pragma unroll
   for (int i = 0; i < kCols; ++i) acc[i] = 0.f;
-  constexpr int kSlots = F16E ? 16 : 8;
+  constexpr int kSlots = SL;
   for (int j0 = 0; j0 < K; j0 += kSlots) {
     Row8<F16E> r[kSlots];
     float wj[kSlots];
@@ -151,14 +152,27 @@ void launch_combine(const moe_layer_desc *d, int32_t T, const void *y_sorted, co
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, y_sorted, ys_sh, inv_order, topk_w, T, d->top_k,
                        d->n_shared, N, D, parts, part_rows, y);
   };
-  auto by_out = [&](auto ys_tag) {
+  const int K = d->top_k;
+  auto by_out = [&](auto ys_tag, auto sl_tag) {
     constexpr bool F16E = decltype(ys_tag)::value;
-    if (out_dtype == MOE_DT_BF16) go(combine_kernel<F16E, kDtBF16>);
-    else if (out_dtype == MOE_DT_F16) go(combine_kernel<F16E, kDtF16>);
-    else go(combine_kernel<F16E, kDtF32>);
+    constexpr int SL = decltype(sl_tag)::value;
+    if (out_dtype == MOE_DT_BF16) go(combine_kernel<F16E, kDtBF16, SL>);
+    else if (out_dtype == MOE_DT_F16) go(combine_kernel<F16E, kDtF16, SL>);
+    else go(combine_kernel<F16E, kDtF32, SL>);
   };
-  if (ys_sh) by_out(std::true_type{});
-  else by_out(std::false_type{});
+  using S4 = std::integral_constant<int, 4>;
+  using S8 = std::integral_constant<int, 8>;
+  using S12 = std::integral_constant<int, 12>;
+  using S16 = std::integral_constant<int, 16>;
+  if (ys_sh) {
+    if (K <= 4) by_out(std::true_type{}, S4{});
+    else if (K <= 8) by_out(std::true_type{}, S8{});
+    else if (K <= 12) by_out(std::true_type{}, S12{});
+    else by_out(std::true_type{}, S16{});
+  } else {
+    if (K <= 4) by_out(std::false_type{}, S4{});
+    else by_out(std::false_type{}, S8{});
+  }
   if (mk) mk->mark("combine");
 }
 
