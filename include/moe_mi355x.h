@@ -224,8 +224,10 @@ int moe_forward_timed(const moe_layer_desc *desc, int32_t T, const void *x,
  * then W_router.  The forward's per-op rounding is not differentiated.  The
  * router and dispatch run again inside.  fp32 layers compute in fp32 on the
  * vector units; 16-bit layers run the contractions on the matrix cores (the
- * gate/up recomputation as in the forward, the transposed products with
- * bf16 operands and fp32 accumulation).  Repeated calls give identical bits.
+ * gate/up recomputation as in the forward; the transposed products on fp16
+ * operands with power-of-two exponents, or for dense bf16 weights on the
+ * exact weights against a bf16 head/tail split of the activations; fp32
+ * accumulation).  Repeated calls give identical bits.
  * ws: moe_backward_workspace_size bytes (caller-owned, 16-byte aligned).
  * Errors as for moe_forward.
  */

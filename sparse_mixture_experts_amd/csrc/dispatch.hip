@@ -1,11 +1,12 @@
 // dispatch.hip -- groups the T*k routed rows by expert.
 //
-// DS4Server issue #112 ("Current upstream route", sort_rows): order is the
-// argsort of the flattened expert ids, inv_order its inverse, row_map =
-// order / k, and x is read in place through row_map instead of being copied;
-// "Kernel contract": per-expert row and tile prefix tables.  The PRD "5.5 real
-// sparse MoE kernels (Metal)" names this step ("Expert-dispatch ... the hard
-// part").
+// DS4Server issue #112, "Current upstream route" (sort_rows) and "Kernel
+// contract": the routed slots are ordered by their expert id (a stable
+// sort), with the inverse permutation and the token of every sorted row kept
+// beside it, so the expert kernels can read x rows where they lie; the same
+// section asks for per-expert row and tile prefix tables.  The PRD "5.5 real
+// sparse MoE kernels (Metal)", "Acceptance criteria", names this step as the
+// difficult one of the layer.
 //
 // A counting sort, stable and deterministic, in one workgroup:
 //   1. each wave owns a contiguous segment of slots and counts its experts

@@ -229,9 +229,9 @@ int moe_backward(const moe_layer_desc *desc, int32_t T, const void *x, const moe
                   at<int32_t>(ws, L.row_map), at<int32_t>(ws, L.expert_off), at<int32_t>(ws, L.tile_off),
                   at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles),
                   at<int32_t>(ws, L.dsp), stream);
-  const BwdScratch sc{at<float>(ws, B.gu),    at<float>(ws, B.v),    at<float>(ws, B.dw),
-                      at<float>(ws, B.dxr),   at<uint16_t>(ws, B.dgu), at<void>(ws, B.wr_t),
-                      ffn_scratch(ws, L, route_writes_x16(desc))};
+  const BwdScratch sc{at<float>(ws, B.gu),     at<float>(ws, B.v),       at<float>(ws, B.dw),
+                      at<float>(ws, B.dxr),    at<float>(ws, B.dgu),     at<int8_t>(ws, B.dgu_sh),
+                      at<int8_t>(ws, B.dy_sh), at<void>(ws, B.wr_t),     ffn_scratch(ws, L, route_writes_x16(desc))};
   launch_backward(desc, T, x, w, dy, idx, wt, at<int32_t>(ws, L.order), at<int32_t>(ws, L.inv_order),
                   at<int32_t>(ws, L.row_map), at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items),
                   at<PlanItem>(ws, L.tiles), L.max_tiles, sc, dx, stream);

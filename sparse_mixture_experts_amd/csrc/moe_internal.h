@@ -145,13 +145,16 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
 // Backward with respect to x.  Intermediates in the backward workspace (R
 // sorted rows): g and u, v = Wd^T dy (per reduction split), dw, the rows'
 // dx (per split), the router matrix transposed for the per-token kernel;
-// the matrix-core path adds dg | du as bf16.
+// the matrix-core path adds dg | du and the power-of-two exponents of its
+// fp16 operands (per dg|du row and per dy row).
 struct BwdScratch {
   float *gu;      // matrix cores: [R][2F] g | u per row; vector units: g [R][F] then u [R][F]
   float *v;       // [splits.v][R][F]
   float *dw;      // [R]
   float *dxr;     // [splits.dx][R][D]
-  uint16_t *dgu;  // matrix-core path: [R][2F] bf16, dg then du
+  float *dgu;     // matrix-core path: [R][2F] fp32, dg then du
+  int8_t *dgu_sh; // matrix-core path: [R] exponent of each dg|du row
+  int8_t *dy_sh;  // matrix-core path: [T] exponent of each dy row
   void *wr_t;     // router matrix transposed [E][D] (layer dtype)
   FfnScratch ffn; // matrix-core path: the fp16 staging copy of x (affine layers)
 };
@@ -163,7 +166,7 @@ struct BwdSplits {
 BwdSplits backward_splits(const moe_layer_desc *d, int32_t T);
 struct BwdWorkspace {
   Workspace fwd;  // router and dispatch sections (the forward's layout)
-  size_t gu, v, dw, dxr, dgu, wr_t, total;
+  size_t gu, v, dw, dxr, dgu, dgu_sh, dy_sh, wr_t, total;
 };
 BwdWorkspace backward_workspace_layout(const moe_layer_desc *d, int32_t T);
 void launch_backward(const moe_layer_desc *d, int32_t T, const void *x, const moe_weights *w, const float *dy,

@@ -132,7 +132,9 @@ BwdWorkspace backward_workspace_layout(const moe_layer_desc *d, int32_t T) {
   b.v = take(size_t(sp.v) * rows * d->d_ff * 4);
   b.dw = take(size_t(rows) * 4);
   b.dxr = take(size_t(sp.dx) * rows * d->d_model * 4);
-  b.dgu = take(mc ? size_t(rows) * 2 * d->d_ff * 2 : 0);
+  b.dgu = take(mc ? size_t(rows) * 2 * d->d_ff * 4 : 0);
+  b.dgu_sh = take(mc ? size_t(rows) : 0);
+  b.dy_sh = take(mc ? size_t(T) : 0);
   b.wr_t = take(size_t(d->n_experts) * d->d_model * act_bytes(d));
   b.total = o;
   return b;

@@ -5,10 +5,9 @@ Tolerance: topk_w within 1e-6 absolute; y within 1e-5 * RMS(y_oracle) for the
 fp32 layers and 2e-2 * RMS(y_oracle) for bf16 / affine 4- and 8-bit layers (fp32 output);
 a bf16 output must equal the nearest-even rounding of the same run's fp32
 output.  Medium layers (several 64-row tiles per expert, ragged tails, empty
-experts) are compared on every token; the five full-size workloads and their
-8-bit, group-32/128 and GeGLU variants are run exactly as the benchmark runs
-them and compared on sampled tokens (all tokens where T is small), with
-routing compared on every token.
+experts) and the five full-size workloads with their 8-bit, group-32/128,
+GeGLU and fp16 variants (run exactly as the benchmark runs them) are all
+compared on every token, forward and backward.
 """
 import math
 
@@ -115,9 +114,17 @@ MID = {
     # 32 tokens x 12 slots: the one-wave dispatch at 8 slots per lane
     "mid-q4-t32-k12": LayerSpec("mid-q4-t32-k12", T=32, d_model=256, d_ff=128, n_experts=64, top_k=12, wfmt="q4",
                                 seed=56),
+    # more than 12 slots per token: the combine's 16-row slot rounds on fp16
+    # expert outputs (64-row tiles), and more than 8 slots on fp32 expert
+    # outputs (vector-unit kernels and decode tiles)
+    "mid-q4-k16": LayerSpec("mid-q4-k16", T=100, d_model=256, d_ff=128, n_experts=32, top_k=16, wfmt="q4",
+                            seed=57),
+    "mid-f32-k10": LayerSpec("mid-f32-k10", T=24, d_model=96, d_ff=64, n_experts=16, top_k=10, act="f32",
+                             x_scale="fan_in", seed=58),
+    "mid-q4-decode-k12": LayerSpec("mid-q4-decode-k12", T=2, d_model=256, d_ff=192, n_experts=64, top_k=12,
+                                   wfmt="q4", seed=59),
 }
 FULL = {**inputs.CONFIGS, **inputs.VARIANTS}
-SAMPLE = 48  # tokens compared per full-size layer (all when T is smaller)
 
 _host: dict = {}
 _layers: dict = {}
@@ -148,7 +155,7 @@ def test_route(name):
     assert np.max(np.abs(w - rw)) <= 1e-6
 
 
-@pytest.mark.parametrize("name", list(MID) + ["q4-decode-t32", "q4-prefill-t2048", "q4-skewed-t256"])
+@pytest.mark.parametrize("name", list(MID) + list(inputs.CONFIGS))
 @pytest.mark.parametrize("tile_rows", [1, 7, 64])
 def test_dispatch(name, tile_rows):
     L, g = get(name)
@@ -323,13 +330,9 @@ def test_forward_output_magnitudes(name, shift):
 
 @pytest.mark.parametrize("name", list(FULL))
 def test_forward_full_size(name):
-    spec = FULL[name]
-    tokens = None
-    if spec.T > SAMPLE:
-        rng = np.random.default_rng(1234)
-        tokens = np.sort(np.concatenate([[0, spec.T - 1], rng.choice(np.arange(1, spec.T - 1), SAMPLE - 2,
-                                                                       replace=False)])).astype(np.int32)
-    _forward_check(name, tokens)
+    """Every token of every workload and variant at full size, in the launch
+    configuration the benchmark times (the oracle runs on all host cores)."""
+    _forward_check(name)
 
 
 def test_zero_input_gives_zero_output():
@@ -419,10 +422,11 @@ def _backward_check(name, tokens=None):
         # fp32 arithmetic on both sides
         assert err <= 1e-4, err
     else:
-        # bf16 operands (unit roundoff 2^-8) in the three transposed and GLU
-        # products: about 3.5e-3 relative RMS error predicted, 5 sigma at most
-        assert rms_err <= 1e-2, rms_err
-        assert err <= 5e-2, err
+        # the 16-bit layers' tolerance, as for the forward output; fp16
+        # operands (unit roundoff 2^-11) in the transposed products keep the
+        # RMS error near 3e-4 of RMS(dx)
+        assert rms_err <= 2e-3, rms_err
+        assert err <= 2e-2, err
     # the same call twice gives the same bits
     assert np.array_equal(g.backward(dy).view(np.uint32), dx.view(np.uint32))
 
@@ -430,19 +434,13 @@ def _backward_check(name, tokens=None):
 @pytest.mark.parametrize("name", list(MID))
 def test_backward_mid(name):
     """dx against the oracle's backward on every token (fp32 layers: fp32
-    arithmetic, 1e-4 of RMS(dx); 16-bit layers: bf16 matrix-core operands)."""
+    arithmetic, 1e-4 of RMS(dx); 16-bit layers: 2e-2 of RMS(dx))."""
     _backward_check(name)
 
 
 @pytest.mark.parametrize("name", list(FULL))
 def test_backward_full_size(name):
-    """dx at every workload's full size, in the launch configuration the
-    benchmark times (48 sampled tokens where T is larger)."""
-    spec = FULL[name]
-    tokens = None
-    if spec.T > SAMPLE:
-        rng = np.random.default_rng(4321)
-        tokens = np.sort(np.concatenate([[0, spec.T - 1], rng.choice(np.arange(1, spec.T - 1), SAMPLE - 2,
-                                                                       replace=False)])).astype(np.int32)
-    _backward_check(name, tokens)
+    """dx on every token at every workload's full size, in the launch
+    configuration the benchmark times."""
+    _backward_check(name)
 
