@@ -236,6 +236,25 @@ int moe_backward(const moe_layer_desc *desc, int32_t T, const void *x,
                  const moe_weights *w, const float *dy, float *dx, void *ws,
                  size_t ws_bytes, void *stream);
 
+/*
+ * moe_forward without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace is a device array of
+ * MOE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends; the call itself allocates nothing.  Layers whose
+ * moe_workspace_size(desc, T) exceeds MOE_NOALLOC_SCRATCH_BYTES get
+ * MOE_E_WORKSPACE and nothing is enqueued (the one-token and 32-token decode
+ * layers need well under 8 MiB, a 512-token dense layer with 8 experts about
+ * 75 MiB).  The work runs on the device current at the call, which must be
+ * the device of `stream`.  Every call on one GPU shares that GPU's array, so
+ * calls that overlap on one GPU (other streams, other host threads) race:
+ * serialise them.  Other arguments and results as for moe_forward.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (96u * 1024u * 1024u)
+int moe_forward_noalloc(const moe_layer_desc *desc, int32_t T, const void *x,
+                        const moe_weights *w, void *y, int32_t out_dtype,
+                        int32_t *topk_idx_out, float *topk_w_out, void *stream);
+
 /* A static, human-readable name of a moe_status value. */
 const char *moe_status_string(int status);
 

@@ -27,7 +27,8 @@ _ACT = {"swiglu": MOE_ACT_SWIGLU, "geglu": MOE_ACT_GEGLU}
 
 EXPORTED = ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
             "moe_forward", "moe_forward_timed", "moe_backward_workspace_size", "moe_backward",
-            "moe_status_string")
+            "moe_status_string", "moe_forward_noalloc")
+NOALLOC_SCRATCH_BYTES = 96 * 1024 * 1024  # MOE_NOALLOC_SCRATCH_BYTES
 
 
 class MoeError(RuntimeError):
@@ -71,6 +72,7 @@ def load() -> ctypes.CDLL:
         lib.moe_forward.argtypes = [P(LayerDesc), i32, vp, P(Weights), vp, i32, vp, vp, vp, sz, vp]
         lib.moe_forward_timed.argtypes = [P(LayerDesc), i32, vp, P(Weights), vp, i32, vp, vp, vp, sz, vp,
                                           P(vp), i32, ctypes.c_char_p, sz]
+        lib.moe_forward_noalloc.argtypes = [P(LayerDesc), i32, vp, P(Weights), vp, i32, vp, vp, vp]
         lib.moe_backward_workspace_size.argtypes = [P(LayerDesc), i32, P(sz)]
         lib.moe_backward.argtypes = [P(LayerDesc), i32, vp, P(Weights), vp, vp, vp, sz, vp]
         lib.moe_status_string.argtypes = [ctypes.c_int]
@@ -169,6 +171,11 @@ def moe_forward(desc, T, x, weights, y, out_dtype, topk_idx_out, topk_w_out, ws,
     _check(load().moe_forward(ctypes.byref(desc), T, _ptr(x), ctypes.byref(weights.c), _ptr(y), out_dtype,
                               _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws), _nbytes(ws),
                               _stream(stream)), "moe_forward")
+
+
+def moe_forward_noalloc(desc, T, x, weights, y, out_dtype, topk_idx_out, topk_w_out, stream=None):
+    _check(load().moe_forward_noalloc(ctypes.byref(desc), T, _ptr(x), ctypes.byref(weights.c), _ptr(y), out_dtype,
+                                      _ptr(topk_idx_out), _ptr(topk_w_out), _stream(stream)), "moe_forward_noalloc")
 
 
 def moe_forward_timed(desc, T, x, weights, y, out_dtype, topk_idx_out, topk_w_out, ws, events, stream=None):
