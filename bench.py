@@ -7,11 +7,14 @@ A step is one whole layer forward (router, dispatch, expert FFN, combine)
 through the C ABI (moe_forward) over one batch of synthetic input that is
 already resident in HBM.  The headline workload is the 2048-token prefill
 chunk (T=2048, d_model=2048, d_ff=512, E=512, top-10, affine 4-bit g64, fused
-gate|up); the decode layer at T=1 and T=32, and the backward pass with respect
-to x (moe_backward) of all three, are measured in the same run and reported
-under "sweep".  Weight copies and x copies rotate from step to step
-so that the bytes between two reuses of the same buffer exceed the 256 MB
-Infinity Cache: every step streams its weights from HBM.
+gate|up).  Every other workload runs in the same process and is reported
+under "sweep": the tiny fp32 layer, the dense bf16 layer at T=512, the decode
+layer at T=1 and T=32 and the skewed layer at T=256, each with its own
+roofline and oracle timing, plus the backward pass with respect to x
+(moe_backward) of the decode and prefill layers.  Weight copies and x copies
+rotate from step to step so that the bytes between two reuses of the same
+buffer exceed the 256 MB Infinity Cache: every step streams its weights from
+HBM.
 
 Prints ONE JSON line on stdout (everything else goes to stderr).
 """
@@ -32,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, TFLOP/s
-VALU_F32_PEAK_TFLOPS = 78.6     # fp32 FMA without packed instructions: 256 CU * 64 lanes * 2 * 2.4 GHz
+VALU_F32_PEAK_TFLOPS = 157.3    # MI355X published fp32 vector peak
 METRIC = "MoE layer routed rows/s at T=1/32/2048; % of HBM or MFMA roofline"
 ROTATE_BYTES = 1 << 30          # reuse distance of weight buffers
 
@@ -117,51 +120,64 @@ def expert_output_bytes(spec) -> float:
 def accounting(spec, touched: int):
     """Algorithmic bytes and FLOPs of one forward, and per kernel.
 
-    Bytes count each tensor a kernel must read or write once: weights of the
-    experts the batch touches (plus shared experts), activations, the routed
-    intermediate h, the expert outputs (as stored) and the small index tables.
+    The layer's bytes are the stored weights of the experts the batch touches
+    (plus shared experts), the router matrix, x and y.  Per kernel, the
+    roofline counts what the step cannot avoid moving: the gate/up launch the
+    gate and up weights of the touched experts and x; the down launch the down
+    weights; the router launches the router matrix and x.  The intermediates a
+    fused implementation need not move (h between the projections, the
+    expert outputs between down and combine) are reported beside them, as
+    stored by this library, under "intermediate_bytes".
     """
     T, D, F, E, K, S = spec.T, spec.d_model, spec.d_ff, spec.n_experts, spec.top_k, spec.n_shared
     esz = 4 if spec.act == "f32" else 2
     N, R = T * K, T * K + S * T
     eb = expert_bytes(spec)
-    gu_frac, down_frac = 2 / 3, 1 / 3
     w_touched = (touched + S) * eb
     router = D * E * esz
-    ysz = expert_output_bytes(spec)
-    # the router's per-token kernel writes the fp16 staging copy of x (and reads x) for 4-bit layers
-    x16_bytes = (T * D * 2 + T) if spec.quantized and D <= 4096 else 0
-    lt_parts = 2 if (D // 64) % 2 == 0 else 1
-    gateup = {"bound": "hbm", "bytes": int(w_touched * gu_frac) + T * D * esz + R * F * esz,
-              "flops": 2 * R * 2 * D * F}
-    down = {"bound": "hbm", "bytes": int(w_touched * down_frac) + R * F * esz + int(R * D * ysz),
-            "flops": 2 * R * D * F}
+    x_bytes = y_bytes = T * D * esz
+    h_bytes = R * F * esz
+    ys_bytes = int(R * D * expert_output_bytes(spec))
+    gateup = {"bound": "hbm", "bytes": int(w_touched * 2 / 3) + x_bytes, "flops": 2 * R * 2 * D * F,
+              "intermediate_bytes": {"h_written": h_bytes}}
+    down = {"bound": "hbm", "bytes": int(w_touched / 3), "flops": 2 * R * D * F,
+            "intermediate_bytes": {"h_read": h_bytes, "expert_outputs_written": ys_bytes}}
+    route = {"bound": "hbm", "bytes": router + x_bytes, "flops": 2 * T * D * E}
     acc = {
-        "layer_bytes": w_touched + router + T * D * esz + T * D * esz,
+        "layer_bytes": w_touched + router + x_bytes + y_bytes,
         "expert_flops": 2 * R * 3 * D * F,
         "router_flops": 2 * T * D * E,
+        # FLOPs of the sparse layer over those of the dense all-experts layer
+        "sparse_dense_flop_ratio": (K + S) / (E + S),
         "kernels": {
-            # VALU router: canonical-order logits (fp32 FMA chains), then top-k
-            "route_logits": {"bound": "alu", "flops": 2 * T * D * E, "bytes": T * D * esz + router + T * E * 4},
-            "route_select": {"bound": "hbm", "bytes": T * E * 4 + N * 8 + x16_bytes},
-            # matrix-core router: W transposed (read + write + read), x read,
-            # logits written (two partial sums when the 64-column chunks split evenly)
-            "route_mfma": {"bound": "hbm", "bytes": 3 * router + T * D * esz + lt_parts * T * E * 4,
-                           "flops": 2 * T * D * E},
-            # certification: logits and x read, the k winners written (and the
-            # fp16 staging copy of x for 4-bit layers)
-            "route_certify": {"bound": "hbm", "bytes": lt_parts * T * E * 4 + T * D * esz + N * 8 + x16_bytes},
+            # vector-unit router: canonical-order logits (fp32 FMA chains)
+            "route_logits": {"bound": "alu", "flops": 2 * T * D * E, "bytes": router + x_bytes},
+            "route_select": {"bound": "hbm", "bytes": N * 8},
+            "route_mfma": route,
+            "route_certify": {"bound": "hbm", "bytes": N * 8},
             "dispatch": {"bound": "hbm", "bytes": N * 4 * 4},
-            # selection with the dispatch of a handful of slots folded in
-            "route_select_dispatch": {"bound": "hbm", "bytes": T * E * 4 + N * 8 + x16_bytes + N * 4 * 4},
-            # fp16 copy of x for the 4-bit GEMMs: x read, copy and token exponents written
-            "x_f16": {"bound": "hbm", "bytes": 2 * T * D * esz + T},
+            "route_select_dispatch": {"bound": "hbm", "bytes": N * 8 + N * 4 * 4},
+            "x_f16": {"bound": "hbm", "bytes": 2 * x_bytes},
             "gateup_gemv": gateup, "down_gemv": down,
             "gateup_mfma": gateup, "down_mfma": down,
-            "combine": {"bound": "hbm", "bytes": int(R * D * ysz) + T * D * esz + N * 8},
+            "combine": {"bound": "hbm", "bytes": y_bytes + N * 8,
+                        "intermediate_bytes": {"expert_outputs_read": ys_bytes}},
         },
     }
     return acc
+
+
+_HOST = {}
+
+
+def host_layer(name):
+    """The seeded synthetic layer of a workload (generated once per process)."""
+    from sparse_mixture_experts_amd import inputs
+    if name not in _HOST:
+        t0 = time.time()
+        _HOST[name] = inputs.gen_layer(inputs.workload(name))
+        log(f"[{name}] generated in {time.time() - t0:.1f}s")
+    return _HOST[name]
 
 
 def run_config(name, steps, warmup, use_graph, hip):
@@ -170,9 +186,7 @@ def run_config(name, steps, warmup, use_graph, hip):
 
     spec = inputs.workload(name)
     dev = "cuda:0"
-    t0 = time.time()
-    host = inputs.gen_layer(spec)
-    log(f"[{name}] generated in {time.time() - t0:.1f}s")
+    host = host_layer(name)
     desc = moe.desc_from_spec(spec)
     w0 = moe.DeviceWeights.from_layer(host, dev)
     wbytes = w0.nbytes()
@@ -291,7 +305,7 @@ def run_backward(name, steps, warmup, hip):
 
     spec = inputs.workload(name)
     dev = "cuda:0"
-    host = inputs.gen_layer(spec)
+    host = host_layer(name)
     desc = moe.desc_from_spec(spec)
     w0 = moe.DeviceWeights.from_layer(host, dev)
     n_w = max(1, math.ceil(ROTATE_BYTES / max(1, w0.nbytes())))
@@ -436,9 +450,12 @@ def calibrate_copy(mib: int):
 
 
 def roofline(res):
+    """Roofline of the step's dominant kernel (the longest average launch):
+    algorithmic bytes (or FLOPs for the vector-unit router) per launch over the
+    launch's average duration from HIP events on the launch stream."""
     km = res["kernel_ms"]
-    traffic = measured_traffic(res["name"], max(km, key=km.get))
     dom = max(km, key=km.get)
+    traffic = measured_traffic(res["name"], dom)
     kacc = res["acc"]["kernels"].get(dom)
     t = km[dom] / 1e3
     if kacc is None:
@@ -448,35 +465,53 @@ def roofline(res):
         a = kacc["flops"] / t / 1e12
         return {"kernel": dom, "bound": "alu", "achieved": round(a, 3), "peak": VALU_F32_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(a / VALU_F32_PEAK_TFLOPS, 4), "traffic": traffic,
-                "avg_launch_us": round(km[dom] * 1e3, 2)}
+                "avg_launch_us": round(km[dom] * 1e3, 2), "algorithmic_flops_per_launch": kacc["flops"]}
     a = kacc["bytes"] / t / 1e9
-    return {"kernel": dom, "bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic, "avg_launch_us": round(km[dom] * 1e3, 2),
-            "algorithmic_bytes_per_launch": kacc["bytes"]}
+    out = {"kernel": dom, "bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic, "avg_launch_us": round(km[dom] * 1e3, 2),
+           "algorithmic_bytes_per_launch": kacc["bytes"]}
+    if "flops" in kacc:
+        out["mfma_frac"] = round(kacc["flops"] / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+    if "intermediate_bytes" in kacc:
+        out["intermediate_bytes_per_launch"] = kacc["intermediate_bytes"]
+    return out
 
 
-def cpu_baseline(name, n_tokens):
-    """The oracle, as it stands, on the host cores over a bounded token sample."""
+def cpu_baseline(name, n_tokens, threads=None):
+    """The oracle, as it stands, on the host cores over a bounded token sample
+    (evenly spaced tokens of the workload, each routed over all experts and run
+    through its selected experts); threads=None uses every core available to
+    the process."""
     import oracle
     from sparse_mixture_experts_amd import inputs
 
     spec = inputs.workload(name)
-    host = inputs.gen_layer(spec)
+    host = host_layer(name)
     d = oracle.Desc(spec.d_model, spec.d_ff, spec.n_experts, spec.top_k, spec.n_shared, spec.act == "bf16",
                     spec.quantized, spec.group_size, spec.gate_up_fused, spec.swiglu_round_bf16,
                     spec.renormalize, spec.bits, int(spec.activation == "geglu"),
                     spec.act == "f16")
     n = min(n_tokens, spec.T)
     toks = np.linspace(0, spec.T - 1, n).astype(np.int32)
-    threads = len(os.sched_getaffinity(0))
+    threads = threads or len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
     _, _, _, used = oracle.forward(d, host["x"], host["w_router"], host["router_bias"], host["experts"],
                                    tokens=toks, n_threads=threads)
     dt = time.perf_counter() - t0
     rows = n * spec.top_k
     return {"value": round(rows / dt, 2), "unit": "routed rows/s", "cores": used, "kind": "oracle",
+            "tokens_per_s": round(n / dt, 3),
             "sample": f"{n} of {spec.T} tokens ({rows} routed rows) of {name}, each routed and run through "
                       f"its {spec.top_k} experts; {dt:.2f} s wall on {used} threads"}
+
+
+# Oracle sample per workload for the sweep's cpu_baseline (tokens), and the
+# workloads also timed on one thread (tokens).
+CPU_SAMPLE = {"tiny-f32": 16, "dense-bf16-t512": 512, "q4-decode-t1": 1, "q4-decode-t32": 32,
+              "q4-skewed-t256": 256, "q4-prefill-t2048": 256}
+CPU_ONE_THREAD = {"tiny-f32": 16, "q4-decode-t1": 1, "q4-decode-t32": 8}
+DEFAULT_SWEEP = ("tiny-f32,dense-bf16-t512,q4-decode-t1,q4-decode-t32,q4-skewed-t256,"
+                 "bwd:q4-decode-t1,bwd:q4-decode-t32,bwd:q4-prefill-t2048")
 
 
 def main():
@@ -485,8 +520,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="q4-prefill-t2048")
-    ap.add_argument("--sweep", default="q4-decode-t1,q4-decode-t32,bwd:q4-decode-t1,bwd:q4-decode-t32,"
-                                       "bwd:q4-prefill-t2048",
+    ap.add_argument("--sweep", default=DEFAULT_SWEEP,
                     help="further workloads; a bwd: prefix times the backward pass (moe_backward) instead")
     ap.add_argument("--graph", action="store_true", help="replay captured HIP graphs in the timed loop")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
@@ -518,12 +552,20 @@ def main():
             sweep.append(run_backward(name[4:], args.steps, args.warmup, hip))
             continue
         r = run_config(name, args.steps, args.warmup, args.graph, hip)
-        sweep.append({
+        entry = {
             "workload": workload_name(r["spec"]), "value": round(r["rows_per_s"], 1), "unit": "routed rows/s",
             "tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 5),
             "layer_gbs": round(r["layer_gbs"], 1), "layer_hbm_frac": round(r["layer_hbm_frac"], 4),
+            "layer_mfma_frac": round(r["layer_mfma_frac"], 4),
+            "sparse_dense_flop_ratio": round(r["acc"]["sparse_dense_flop_ratio"], 5),
             "kernel_us": {k: round(v * 1e3, 2) for k, v in r["kernel_ms"].items()},
-            "roofline": roofline(r)})
+            "roofline": roofline(r)}
+        if not args.no_cpu_baseline and name in CPU_SAMPLE:
+            entry["cpu_baseline"] = cpu_baseline(name, CPU_SAMPLE[name])
+            if name in CPU_ONE_THREAD:
+                entry["cpu_baseline_1thread"] = cpu_baseline(name, CPU_ONE_THREAD[name], threads=1)
+            log(f"[cpu baseline {name}] {entry['cpu_baseline']}")
+        sweep.append(entry)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -546,6 +588,7 @@ def main():
                            "expert_flops": head["acc"]["expert_flops"],
                            "mfma_frac": round(head["layer_mfma_frac"], 4),
                            "touched_experts": head["touched"]},
+        "sparse_dense_flop_ratio": round(head["acc"]["sparse_dense_flop_ratio"], 5),
         "kernel_us": {k: round(v * 1e3, 2) for k, v in head["kernel_ms"].items()},
         "roofline": roofline(head),
         "cpu_baseline": cpu,

@@ -139,6 +139,14 @@ static int forward_impl(const moe_layer_desc *desc, int32_t T, const void *x, co
   if (mk) mk->mark(nullptr);
   int32_t *idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.topk_idx);
   float *wt = topk_w_out ? topk_w_out : at<float>(ws, L.topk_w);
+  if (t1_fused_applies(desc, T)) {
+    // one token: router chunk partials, then selection + gate/up, then down +
+    // combine (no dispatch: slot j of the token is its j-th expert)
+    const int C = launch_route_chunks_t1(desc, x, w->w_router, at<float>(ws, L.route), stream, mk);
+    launch_t1_layer(desc, x, w, at<float>(ws, L.route), C, idx, wt, at<float>(ws, L.h), at<float>(ws, L.y_sorted), y,
+                    out_dtype, stream, mk);
+    return hip_status();
+  }
   const bool x16_ready = route_writes_x16(desc);
   const FusedDispatch dsp{at<int32_t>(ws, L.order), at<int32_t>(ws, L.inv_order), at<int32_t>(ws, L.row_map),
                           at<int32_t>(ws, L.expert_off), at<int32_t>(ws, L.tile_off), at<int32_t>(ws, L.counters),

@@ -46,7 +46,7 @@ struct Workspace {
   size_t dsp;                         // dispatch scratch (dispatch_scratch_ints)
   size_t act_items;                   // [E+S] PlanItem
   size_t tiles;                       // [max_tiles] PlanItem
-  size_t h;                           // [N+S*T][d_ff] h_bytes
+  size_t h;                           // [N+S*T][d_ff] h_bytes (one token: [k+S][d_ff] fp32)
   size_t hsh;                         // [N+S*T][ceil(d_ff/128)] int8 (affine layers)
   size_t x16, xsh;                    // [T][d_model] fp16, [T] int8 (affine layers)
   size_t y_sorted;                    // [N+S*T][d_model]: fp16 (ys_f16e), fp32, or [parts] fp32 partial rows
@@ -88,6 +88,19 @@ bool route_fuses_dispatch(const moe_layer_desc *d, int32_t T);
 void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router,
                   const float *bias, int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh,
                   const FusedDispatch &dsp, void *stream, StageMarker *mk = nullptr);
+
+// One-token router logits as canonical-order chunk partials [C][1][E] (no
+// selection); returns C.
+int launch_route_chunks_t1(const moe_layer_desc *d, const void *x, const void *w_router, float *partials,
+                           void *stream, StageMarker *mk = nullptr);
+// The one-token layer after the router's chunk partials, in two launches:
+// selection fused with gate/up (h [k+S][d_ff] fp32), then down fused with
+// the weighted combine into y.  idx/wt receive the routing.
+bool t1_fused_applies(const moe_layer_desc *d, int32_t T);
+// hmax: [k+S][d_ff/8] fp32 scratch.
+void launch_t1_layer(const moe_layer_desc *d, const void *x, const moe_weights *w, const float *partials,
+                     int n_chunks, int32_t *idx, float *wt, float *h, float *hmax, void *y, int32_t out_dtype,
+                     void *stream, StageMarker *mk = nullptr);
 
 // Dispatch: stable counting sort + prefix tables + the internal work plan.
 // scratch holds dispatch_scratch_ints ints (per-workgroup counts for large N).

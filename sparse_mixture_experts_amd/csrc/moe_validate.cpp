@@ -105,7 +105,10 @@ Workspace workspace_layout(const moe_layer_desc *d, int32_t T) {
   ws.dsp = take(size_t(dispatch_scratch_ints(d, T)) * 4);
   ws.act_items = take(size_t(E + S) * sizeof(PlanItem));
   ws.tiles = take(size_t(ws.max_tiles) * sizeof(PlanItem));
-  ws.h = take(size_t(rows) * d->d_ff * h_bytes(d));
+  // h rows; the one-token layer keeps them as fp32 ([k+S][d_ff]), which the
+  // 16-bit rows of two tokens already cover, so the size stays non-decreasing in T
+  const int64_t h_one_token = T >= 1 ? (int64_t(d->top_k) + S) * d->d_ff * 4 : 0;
+  ws.h = take(size_t(std::max<int64_t>(rows * d->d_ff * h_bytes(d), h_one_token)));
   const bool q4 = affine(d);
   ws.hsh = take(q4 ? size_t(rows) * ((d->d_ff + kHBlock - 1) / kHBlock) : 0);
   ws.x16 = take(q4 ? size_t(T) * d->d_model * 2 : 0);

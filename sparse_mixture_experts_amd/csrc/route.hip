@@ -29,6 +29,7 @@
 #include "dispatch_tiny.h"
 #include "f16_stage.h"
 #include "moe_internal.h"
+#include "select_token.h"
 
 namespace moe {
 namespace {
@@ -192,85 +193,6 @@ __global__ __launch_bounds__(kWave) void route_chunk_kernel(const void *__restri
   }
 }
 
-// One wave per token: logits (summing chunk partials when n_chunks > 0),
-// top-k, softmax.  Each lane keeps the logits of experts lane + 64*m, m < MPL.
-// The per-token part of the selection kernel (one wave).
-template <int MPL>
-__device__ __forceinline__ void select_token(int t, const float *__restrict__ in, int n_chunks,
-                                             const float *__restrict__ bias, int T, int E, int K, int renorm,
-                                             int32_t *__restrict__ idx_out, float *__restrict__ w_out,
-                                             const uint16_t *x, int D, uint16_t *x16, int8_t *xsh, bool x_f16,
-                                             int32_t *s_f) {
-  // chunk partials per load batch: about 64 loads in flight per lane
-  constexpr int CB = MPL >= 64 ? 1 : 64 / MPL;
-  const int lane = lane_id();
-  RowF16 xr;
-  if (x16) row_f16_load(x + int64_t(t) * D, D, xr);
-  float l[MPL];
-  if (n_chunks == 0) {
-#pragma unroll
-    for (int m = 0; m < MPL; ++m) {
-      const int e = lane + kWave * m;
-      l[m] = e < E ? in[int64_t(t) * E + e] : -INFINITY;
-    }
-  } else {
-    float acc[MPL];
-#pragma unroll
-    for (int m = 0; m < MPL; ++m) acc[m] = 0.0f;
-    for (int c0 = 0; c0 < n_chunks; c0 += CB) {
-      float pv[CB][MPL];
-#pragma unroll
-      for (int u = 0; u < CB; ++u)
-#pragma unroll
-        for (int m = 0; m < MPL; ++m) {
-          const int e = min(lane + kWave * m, E - 1), c = min(c0 + u, n_chunks - 1);
-          pv[u][m] = in[(int64_t(c) * T + t) * E + e];
-        }
-      // chunk order
-#pragma unroll
-      for (int u = 0; u < CB; ++u)
-        if (c0 + u < n_chunks) {
-#pragma unroll
-          for (int m = 0; m < MPL; ++m) acc[m] = acc[m] + pv[u][m];
-        }
-    }
-#pragma unroll
-    for (int m = 0; m < MPL; ++m) {
-      const int e = lane + kWave * m;
-      l[m] = e < E ? (bias ? acc[m] + bias[e] : acc[m]) : -INFINITY;
-    }
-  }
-  uint32_t taken = 0;
-  int my_e = 0;
-  float my_l = 0.0f, top = 0.0f;
-  for (int j = 0; j < K; ++j) {
-    float bv;
-    const int be = wave_argmax<MPL>(l, E, taken, bv);
-    if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
-    if (j == 0) top = bv;
-    if (lane == j) { my_e = be; my_l = bv; }
-  }
-  // fp32 softmax over all E logits (the top-1 logit is the maximum).
-  float z = 0.0f;
-#pragma unroll
-  for (int m = 0; m < MPL; ++m)
-    if (lane + kWave * m < E) z += expf(l[m] - top);
-  z = wave_sum(z);
-  const float p = expf(my_l - top) / z;
-  float w = p;
-  if (renorm) {
-    float psum = 0.0f;
-    for (int j = 0; j < K; ++j) psum = psum + read_lane(p, j);
-    w = p / psum;
-  }
-  if (lane < K) {
-    idx_out[int64_t(t) * K + lane] = my_e;
-    w_out[int64_t(t) * K + lane] = w;
-    if (s_f) s_f[t * K + lane] = my_e;
-  }
-  if (x16) row_f16_store(xr, D, x16 + int64_t(t) * D, xsh + t, x_f16);
-}
-
 // With x16 set (affine layers, d <= 4096), the wave also writes the token's
 // fp16 staging row for the expert GEMMs; its loads go out with the others.
 // With dsp.order set (all tokens in this one workgroup, T*k <= 128), the
@@ -353,6 +275,21 @@ bool route_writes_x16(const moe_layer_desc *d) {
 
 bool route_fuses_dispatch(const moe_layer_desc *d, int32_t T) {
   return T <= kThreads / kWave && int64_t(T) * d->top_k <= kTinyFusedMaxN && !route_mfma_applies(d, T);
+}
+
+int launch_route_chunks_t1(const moe_layer_desc *d, const void *x, const void *w_router, float *partials,
+                           void *stream, StageMarker *mk) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int D = d->d_model, E = d->n_experts, C = (D + kChunk - 1) / kChunk;
+  const dim3 grid((E + kWave - 1) / kWave, C, 1);
+  if (d->act_dtype == MOE_DT_BF16)
+    hipLaunchKernelGGL((route_chunk_kernel<kDtBF16, 1>), grid, dim3(kWave), 0, s, x, w_router, 1, D, E, partials);
+  else if (d->act_dtype == MOE_DT_F16)
+    hipLaunchKernelGGL((route_chunk_kernel<kDtF16, 1>), grid, dim3(kWave), 0, s, x, w_router, 1, D, E, partials);
+  else
+    hipLaunchKernelGGL((route_chunk_kernel<kDtF32, 1>), grid, dim3(kWave), 0, s, x, w_router, 1, D, E, partials);
+  if (mk) mk->mark("route_logits");
+  return C;
 }
 
 void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router,

@@ -123,6 +123,18 @@ MID = {
                              x_scale="fan_in", seed=58),
     "mid-q4-decode-k12": LayerSpec("mid-q4-decode-k12", T=2, d_model=256, d_ff=192, n_experts=64, top_k=12,
                                    wfmt="q4", seed=59),
+    # one-token layers on the fused one-token kernels: reduction lengths of 64
+    # mod 128, a shared expert, fused gate|up with per-op rounding and a router
+    # bias; 8-bit g32 GeGLU with fp16 activations; 14 slots (two per down
+    # wave) with groups of 128
+    "mid-t1-q4-shared-fused-round": LayerSpec("mid-t1-q4-shared-fused-round", T=1, d_model=320, d_ff=192,
+                                              n_experts=32, top_k=4, n_shared=1, wfmt="q4", gate_up_fused=True,
+                                              swiglu_round_bf16=True, router_bias="zipf", seed=60),
+    "mid-t1-f16-q8-g32-geglu": LayerSpec("mid-t1-f16-q8-g32-geglu", T=1, d_model=512, d_ff=256, n_experts=64,
+                                         top_k=8, act="f16", wfmt="q8", group_size=32, activation="geglu",
+                                         seed=61),
+    "mid-t1-q4-k12-s2-g128": LayerSpec("mid-t1-q4-k12-s2-g128", T=1, d_model=256, d_ff=384, n_experts=64,
+                                       top_k=12, n_shared=2, wfmt="q4", group_size=128, seed=62),
 }
 FULL = {**inputs.CONFIGS, **inputs.VARIANTS}
 
