@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the sparse MoE layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--sweep A,B] [--graph]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--sweep A,B] [--no-graph]
 
 A step is one whole layer forward (router, dispatch, expert FFN, combine)
 through the C ABI (moe_forward) over one batch of synthetic input that is
@@ -14,7 +14,9 @@ roofline and oracle timing, plus the backward pass with respect to x
 (moe_backward) of the decode and prefill layers.  Weight copies and x copies
 rotate from step to step so that the bytes between two reuses of the same
 buffer exceed the 256 MB Infinity Cache: every step streams its weights from
-HBM.
+HBM.  Each workload's K steps are timed twice, launched eagerly from Python
+and as one captured HIP graph of the same K forwards; the faster of the two
+is the reported step time ("launch" says which), both are in the line.
 
 Prints ONE JSON line on stdout (everything else goes to stderr).
 """
@@ -216,34 +218,38 @@ def run_config(name, steps, warmup, use_graph, hip):
         step(i)
     torch.cuda.synchronize()
 
-    graph = None
-    if use_graph:
-        # one graph per (x, weights) pair in the rotation
-        graph = []
-        cap = torch.cuda.Stream()
-        cap.wait_stream(stream)
-        with torch.cuda.stream(cap):
-            for i in range(n_x * n_w // math.gcd(n_x, n_w)):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=cap):
-                    moe.moe_forward(desc, T, xs[i % n_x], weights[i % n_w], y, out_dt, idx, wt, ws, cap)
-                graph.append(g)
-        stream.wait_stream(cap)
-        for g in graph[:2]:
-            g.replay()
-        torch.cuda.synchronize()
-
-    # timed region: K whole forwards
+    # timed region, eager: K whole forwards launched one by one from Python
     torch.cuda.synchronize()
     ta = time.perf_counter()
     for i in range(steps):
-        if graph:
-            graph[i % len(graph)].replay()
-        else:
-            step(i)
+        step(i)
     torch.cuda.synchronize()
     tb = time.perf_counter()
-    ms = (tb - ta) * 1000.0 / steps
+    eager_ms = (tb - ta) * 1000.0 / steps
+
+    # timed region, graph: the same K forwards (same rotation) captured into
+    # one HIP graph and replayed once, so the host's per-call cost (Python,
+    # ctypes, launch calls) is out of the measurement
+    graph_ms = None
+    if use_graph:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(steps):
+                    moe.moe_forward(desc, T, xs[i % n_x], weights[i % n_w], y, out_dt, idx, wt, ws, cap)
+        stream.wait_stream(cap)
+        g.replay()
+        torch.cuda.synchronize()
+        ta = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        tb = time.perf_counter()
+        graph_ms = (tb - ta) * 1000.0 / steps
+        del g
+    launch = "graph" if graph_ms is not None and graph_ms < eager_ms else "eager"
+    ms = graph_ms if launch == "graph" else eager_ms
 
     # per-kernel durations on the launch stream: events around every kernel
     kernel_ms, names = {}, []
@@ -265,7 +271,7 @@ def run_config(name, steps, warmup, use_graph, hip):
     res = {
         "name": name, "spec": spec, "ms_per_step": ms, "rows_per_s": rows / (ms / 1e3),
         "tokens_per_s": T / (ms / 1e3), "kernel_ms": kernel_ms, "acc": acc, "touched": avg_touched,
-        "weight_copies": n_w, "x_copies": n_x, "graph": bool(graph),
+        "weight_copies": n_w, "x_copies": n_x, "launch": launch, "eager_ms": eager_ms, "graph_ms": graph_ms,
     }
     lb = acc["layer_bytes"]
     res["layer_gbs"] = lb / (ms / 1e3) / 1e9
@@ -522,7 +528,8 @@ def main():
     ap.add_argument("--config", default="q4-prefill-t2048")
     ap.add_argument("--sweep", default=DEFAULT_SWEEP,
                     help="further workloads; a bwd: prefix times the backward pass (moe_backward) instead")
-    ap.add_argument("--graph", action="store_true", help="replay captured HIP graphs in the timed loop")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (default: also one HIP graph of the K steps; the faster is reported)")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of the headline workload the oracle runs for cpu_baseline (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -545,18 +552,20 @@ def main():
     moe.load()
     hip = Hip()
 
-    head = run_config(args.config, args.steps, args.warmup, args.graph, hip)
+    head = run_config(args.config, args.steps, args.warmup, not args.no_graph, hip)
     sweep = []
     for name in [s for s in args.sweep.split(",") if s]:
         if name.startswith("bwd:"):
             sweep.append(run_backward(name[4:], args.steps, args.warmup, hip))
             continue
-        r = run_config(name, args.steps, args.warmup, args.graph, hip)
+        r = run_config(name, args.steps, args.warmup, not args.no_graph, hip)
         entry = {
             "workload": workload_name(r["spec"]), "value": round(r["rows_per_s"], 1), "unit": "routed rows/s",
             "tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 5),
             "layer_gbs": round(r["layer_gbs"], 1), "layer_hbm_frac": round(r["layer_hbm_frac"], 4),
-            "layer_mfma_frac": round(r["layer_mfma_frac"], 4),
+            "layer_mfma_frac": round(r["layer_mfma_frac"], 4), "launch": r["launch"],
+            "eager_ms_per_step": round(r["eager_ms"], 5),
+            "graph_ms_per_step": None if r["graph_ms"] is None else round(r["graph_ms"], 5),
             "sparse_dense_flop_ratio": round(r["acc"]["sparse_dense_flop_ratio"], 5),
             "kernel_us": {k: round(v * 1e3, 2) for k, v in r["kernel_ms"].items()},
             "roofline": roofline(r)}
@@ -581,7 +590,9 @@ def main():
         "config": {"workload": workload_name(spec), "T": spec.T, "d_model": spec.d_model, "d_ff": spec.d_ff,
                    "n_experts": spec.n_experts, "top_k": spec.top_k, "n_shared": spec.n_shared,
                    "routed_rows": spec.T * spec.top_k, "weight_copies_rotated": head["weight_copies"],
-                   "graph_replay": head["graph"]},
+                   "launch": head["launch"]},
+        "eager_ms_per_step": round(head["eager_ms"], 5),
+        "graph_ms_per_step": None if head["graph_ms"] is None else round(head["graph_ms"], 5),
         "tokens_per_s": round(head["tokens_per_s"], 1),
         "layer_roofline": {"algorithmic_bytes": head["acc"]["layer_bytes"], "gbs": round(head["layer_gbs"], 1),
                            "hbm_frac": round(head["layer_hbm_frac"], 4),
