@@ -653,6 +653,267 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   grouped_gemm_body<MODE, QB, RB, GPS>(a);
 }
 
+// ---- down projection with the tile's h rows resident in LDS ---------------
+// When a tile's h rows fit in LDS whole (the down reduction is d_ff), one
+// workgroup stages them once and then runs several 256-column blocks of the
+// output over them: the weights stream through a register ring two slabs
+// ahead across column-block boundaries, each lane loads its own scales, and
+// the main loop has no barrier.  (The slab-pipelined kernel above stages the
+// same h rows again for every column block, with a barrier per slab.)
+// Exponents: the h rows carry one per (row, 128 columns), the weights one
+// per (row, slab) from |s|*qmax + |b| of the lane's group; a ballot finds the
+// usual case where all are zero, otherwise the accumulators are brought to
+// the slab's scale and back as in the slab-pipelined kernel (exact).
+constexpr int kResMaxLds = 80 * 1024;  // bytes of resident h per workgroup
+
+template <int QB, int RB, int GPS>
+__device__ __forceinline__ void down_resident_body(const GemmArgs &a, int cbpw) {
+  constexpr int NT = kNT;                   // 16-row weight tiles per wave (64 output columns)
+  constexpr int PDS = (QB == 8 && RB == 4) ? 1 : 2;  // weight slabs in flight ahead (8-bit 64-row: registers)
+  constexpr int NR = PDS + 1;               // ring size
+  constexpr float kQMax = QB == 8 ? 255.0f : 15.0f;
+  extern __shared__ __align__(16) uint16_t hs[];  // [RB*16][XR] h rows, then [RB*16][nslab] int8 exponents
+
+  const int n_cb = (a.n_out + kNRows - 1) / kNRows;
+  const int nbx = gridDim.x, total = nbx * gridDim.y;
+  const int n_tiles = a.counters[1];
+  const int work = n_tiles * nbx;
+  const int lin = blockIdx.y * nbx + blockIdx.x;
+  const int per = (work + 7) / 8;
+  int item = lin;
+  if (8 * per <= total) {
+    const int slot = lin / 8;
+    if (slot >= per) return;
+    item = (lin % 8) * per + slot;
+  }
+  if (item >= work) return;
+  const int tile_id = item / nbx, grp = item % nbx;
+  PlanItem tile = a.tiles[tile_id];
+  tile.expert = __builtin_amdgcn_readfirstlane(tile.expert);
+  tile.row0 = __builtin_amdgcn_readfirstlane(tile.row0);
+  tile.rows = __builtin_amdgcn_readfirstlane(tile.rows);
+  const int cb0 = grp * cbpw, ncb = min(cbpw, n_cb - cb0);
+
+  const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+  const int lr = lane & 15, lg = lane >> 4;
+  const int K = a.K, KW = K * QB / 32, G = K / (kKS / GPS);
+  const int nslab = (K + kKS - 1) / kKS, KR = nslab * kKS, XR = KR + 8;
+  int8_t *ash = reinterpret_cast<int8_t *>(hs + RB * 16 * XR);
+
+  // ---- h rows of the tile (already fp16 in the staging order) and their exponents
+  int hflag = 0;
+  {
+    const int P = KR / 8;  // 16-byte pieces per LDS row
+    for (int q = tid; q < RB * 16 * P; q += kThreads) {
+      const int m = q / P, pc = q % P;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (m < tile.rows && pc * 8 < K)
+        v = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.act) + int64_t(tile.row0 + m) * K)[pc];
+      *reinterpret_cast<uint4 *>(&hs[m * XR + pc * 8]) = v;
+    }
+    for (int q = tid; q < RB * 16 * nslab; q += kThreads) {
+      const int m = q / nslab, sl = q % nslab;
+      const int e = m < tile.rows ? a.act_sh[int64_t(tile.row0 + m) * a.nblk + sl] : 0;
+      ash[q] = int8_t(e);
+      hflag |= e;
+    }
+  }
+  hflag = __syncthreads_or(hflag);
+
+  // ---- weights: step q = (column block j = q / nslab, slab s = q % nslab)
+  const int Q = ncb * nslab;
+  struct WStep {
+    uint4 w[NT][QB / 4];
+    uint16_t sv[NT], bv[NT];
+  };
+  const uint32_t *wbase = static_cast<const uint32_t *>(a.w0) + int64_t(tile.expert) * a.n_out * KW;
+  const uint16_t *sbase = a.s0 + int64_t(tile.expert) * G * a.n_out;
+  const uint16_t *bbase = a.b0 + int64_t(tile.expert) * G * a.n_out;
+  auto load_step = [&](int q, WStep &st) {
+    q = min(q, Q - 1);
+    const int j = q / nslab, sl = q % nslab;
+    const int colw = (cb0 + j) * kNRows + wave * NT * 16;  // first column of this wave
+    const int w = min(sl * (kKS * QB / 32) + lg * QB, KW - QB);
+    const int gl = (sl * kKS + lg * 32) / (kKS / GPS);
+    const int g = min(gl, G - 1);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = min(colw + nt * 16 + lr, a.n_out - 1);
+      const uint32_t *wr = wbase + int64_t(n) * KW + w;
+#pragma unroll
+      for (int v = 0; v < QB / 4; ++v) st.w[nt][v] = *reinterpret_cast<const uint4 *>(wr + 4 * v);
+      const uint16_t s = sbase[int64_t(g) * a.n_out + n], b = bbase[int64_t(g) * a.n_out + n];
+      st.sv[nt] = gl < G ? s : uint16_t(0);
+      st.bv[nt] = gl < G ? b : uint16_t(0);
+    }
+  };
+
+  uint32_t magic = QB == 8 ? 0x64646464u : 0x64006400u;
+  asm volatile("" : "+v"(magic));
+  f32x4 acc[NT][RB];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) acc[nt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  zero_acc();
+
+  auto epilogue = [&](int j) {
+    const int col0 = (cb0 + j) * kNRows + wave * NT * 16;
+    if (col0 >= a.n_out) return;
+    int ysh[RB] = {};
+    if (a.out_sh) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float mx = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[nt][rb][i]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        ysh[rb] = f16_shift(mx);
+        const int m = rb * 16 + lr;
+        if (lg == 0 && m < tile.rows)
+          a.out_sh[(tile.row0 + m) * (a.n_out / kYsBlock) + col0 / kYsBlock] = int8_t(ysh[rb]);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int m = rb * 16 + lr;
+      if (m >= tile.rows) continue;
+      const int64_t row = tile.row0 + m;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int c = col0 + nt * 16 + lg * 4;
+        if (a.out_sh) {
+          const float sc = pow2(-ysh[rb]);
+          const h2 v01 = {(_Float16)(acc[nt][rb][0] * sc), (_Float16)(acc[nt][rb][1] * sc)};
+          const h2 v23 = {(_Float16)(acc[nt][rb][2] * sc), (_Float16)(acc[nt][rb][3] * sc)};
+          *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + row * a.n_out + c) =
+              make_uint2(__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23));
+        } else {
+          *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + row * a.n_out + c) =
+              make_float4(acc[nt][rb][0], acc[nt][rb][1], acc[nt][rb][2], acc[nt][rb][3]);
+        }
+      }
+    }
+  };
+
+  // One step's MFMAs over the first NRB row blocks.
+  auto compute = [&](const WStep &st, int q, auto nrb_tag) {
+    constexpr int NRB = decltype(nrb_tag)::value;
+    const int sl = q % nslab;
+    float sv[NT], bv[NT];
+    bool need = false;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      sv[nt] = a.half_f16 ? f16_bits_to_f32(st.sv[nt]) : bf16_bits_to_f32(st.sv[nt]);
+      bv[nt] = a.half_f16 ? f16_bits_to_f32(st.bv[nt]) : bf16_bits_to_f32(st.bv[nt]);
+      need |= f16_shift(__builtin_fmaf(kQMax, fabsf(sv[nt]), fabsf(bv[nt]))) != 0;
+    }
+    const bool wexp = __ballot(need) != 0;  // uniform
+    int wsh[NT] = {};
+    if (wexp) {
+      // the exponent of each weight row over its four lanes lg
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float wm = __builtin_fmaf(kQMax, fabsf(sv[nt]), fabsf(bv[nt]));
+        wm = fmaxf(wm, __shfl_xor(wm, 16, kWave));
+        wm = fmaxf(wm, __shfl_xor(wm, 32, kWave));
+        wsh[nt] = f16_shift(wm);
+      }
+    }
+    const bool rescale = wexp || hflag;
+    auto scale_acc = [&](int sign) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const int hsh = ash[(rb * 16 + lr) * nslab + sl];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[nt][rb][i] *= pow2(sign * (hsh + __shfl(wsh[nt], 4 * lg + i, kWave)));
+      }
+    };
+    if (rescale) scale_acc(-1);
+    const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    h2 s2[NT], s2_16[NT], b2[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float m = pow2(-wsh[nt]);
+      const _Float16 s16 = (_Float16)(sv[nt] * m), b16 = (_Float16)(bv[nt] * m);
+      s2[nt] = h2{s16, s16};
+      b2[nt] = h2{b16, b16};
+      s2_16[nt] = s2[nt] * sixteenth;
+    }
+    const uint16_t *hrow = hs + sl * kKS + lg * 32;
+#pragma unroll
+    for (int jj = 0; jj < kSteps; ++jj) {
+      f16x8 bx[NRB];
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) bx[rb] = *reinterpret_cast<const f16x8 *>(hrow + (rb * 16 + lr) * XR + jj * 8);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        f16x8 aw;
+        if constexpr (QB == 4) {
+          const uint4 &qv = st.w[nt][0];
+          aw = q4_word_to_f16(jj == 0 ? qv.x : jj == 1 ? qv.y : jj == 2 ? qv.z : qv.w, s2[nt], s2_16[nt], b2[nt],
+                              magic);
+        } else {
+          const uint4 &qv = st.w[nt][jj >> 1];
+          aw = (jj & 1) ? q8_words_to_f16(qv.z, qv.w, s2[nt], b2[nt], magic)
+                        : q8_words_to_f16(qv.x, qv.y, s2[nt], b2[nt], magic);
+        }
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) acc[nt][rb] = mfma_f16(aw, bx[rb], acc[nt][rb]);
+      }
+    }
+    if (rescale) scale_acc(+1);
+  };
+
+  auto run = [&](auto nrb_tag) {
+    WStep ring[NR];
+#pragma unroll
+    for (int u = 0; u < PDS; ++u) load_step(u, ring[u]);
+    for (int q0 = 0; q0 < Q; q0 += NR) {
+#pragma unroll
+      for (int u = 0; u < NR; ++u) {
+        const int q = q0 + u;
+        if (q < Q) {
+          load_step(q + PDS, ring[(u + PDS) % NR]);
+          compute(ring[u], q, nrb_tag);
+          if (q % nslab == nslab - 1) {
+            epilogue(q / nslab);
+            zero_acc();
+          }
+        }
+      }
+    }
+  };
+  const int nrb = min(RB, (tile.rows + 15) / 16);
+  if constexpr (RB == 4) {
+    if (nrb == 4) run(std::integral_constant<int, 4>{});
+    else if (nrb == 3) run(std::integral_constant<int, 3>{});
+    else if (nrb == 2) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 1>{});
+  } else {
+    run(std::integral_constant<int, RB>{});
+  }
+}
+// 64-row tiles ask for two waves per SIMD (accumulators and the weight ring
+// within 256 registers); 16-row tiles allocate on their own.
+template <int QB, int RB, int GPS>
+__global__ __launch_bounds__(kThreads) void down_resident_kernel(GemmArgs a, int cbpw) {
+  down_resident_body<QB, RB, GPS>(a, cbpw);
+}
+template <int QB, int RB, int GPS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void down_resident_kernel_w2(
+    GemmArgs a, int cbpw) {
+  down_resident_body<QB, RB, GPS>(a, cbpw);
+}
+
 // ---- decode tiles (at most 16 rows of an expert, K <= 2048) ----------------
 // One wave owns 16 weight rows and loads all of their codes and scales at
 // once (one memory round trip), while the workgroup stages the tile's
@@ -888,6 +1149,41 @@ void launch_gemm(const GemmArgs &ga, int qb, int gsize, int64_t max_tiles, hipSt
   else launch_one<MODE, kDenseBF16, RB, 1>(ga, max_tiles, s);
 }
 
+// Bytes of dynamic LDS of the resident-h down kernel for RB row blocks.
+inline size_t down_resident_lds(int RB, int K) {
+  const int nslab = (K + kKS - 1) / kKS;
+  return size_t(RB) * 16 * (nslab * kKS + 8) * sizeof(uint16_t) + size_t(RB) * 16 * nslab;
+}
+template <int QB, int RB>
+void launch_down_resident(const GemmArgs &ga, int gsize, int64_t max_tiles, int64_t est_tiles, hipStream_t s) {
+  const int n_cb = (ga.n_out + kNRows - 1) / kNRows;
+  // column blocks per workgroup: about four workgroups per CU over the
+  // expected tiles, each staging its tile's h once
+  const int64_t want = (est_tiles * n_cb + 1023) / 1024;
+  const int cbpw = int(std::max<int64_t>(1, std::min<int64_t>(n_cb, want)));
+  const dim3 grid((n_cb + cbpw - 1) / cbpw, unsigned(max_tiles));
+  const size_t lds = down_resident_lds(RB, ga.K);
+  auto go = [&](auto kern) {
+    if (lds > 64 * 1024) {
+      static const bool raised = [&] {
+        return hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   kResMaxLds) == hipSuccess;
+      }();
+      (void)raised;
+    }
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, ga, cbpw);
+  };
+  if constexpr (RB == 1) {
+    if (gsize == 32) go(down_resident_kernel<QB, RB, 4>);
+    else if (gsize == 128) go(down_resident_kernel<QB, RB, 1>);
+    else go(down_resident_kernel<QB, RB, 2>);
+  } else {
+    if (gsize == 32) go(down_resident_kernel_w2<QB, RB, 4>);
+    else if (gsize == 128) go(down_resident_kernel_w2<QB, RB, 1>);
+    else go(down_resident_kernel_w2<QB, RB, 2>);
+  }
+}
+
 template <bool GATEUP, int QB, int MS>
 void launch_decode_ms(const DecArgs &da, int64_t max_tiles, hipStream_t s) {
   constexpr int CPW = GATEUP ? 8 : 16;
@@ -1050,15 +1346,25 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
     if (mk) mk->mark("gateup_mfma");
     launch_decode<false>(dd, qb, max_tiles, s);
     if (mk) mk->mark("down_mfma");
-  } else if (tr == 16) {
-    launch_gemm<kGateUp, 1>(gu, qb, gs, max_tiles, s);
-    if (mk) mk->mark("gateup_mfma");
-    launch_gemm<kDown, 1>(dn, qb, gs, max_tiles, s);
-    if (mk) mk->mark("down_mfma");
   } else {
-    launch_gemm<kGateUp, 4>(gu, qb, gs, max_tiles, s);
+    // the down projection keeps each tile's h rows resident in LDS when they fit
+    const bool resident = aff && down_parts == 1 && down_resident_lds(tr == 16 ? 1 : 4, d->d_ff) <= kResMaxLds;
+    const int64_t R = int64_t(T) * d->top_k + int64_t(d->n_shared) * T;
+    const int64_t est_tiles = std::max<int64_t>(std::min<int64_t>(R, d->n_experts + d->n_shared), (R + tr - 1) / tr);
+    if (tr == 16) launch_gemm<kGateUp, 1>(gu, qb, gs, max_tiles, s);
+    else launch_gemm<kGateUp, 4>(gu, qb, gs, max_tiles, s);
     if (mk) mk->mark("gateup_mfma");
-    launch_gemm<kDown, 4>(dn, qb, gs, max_tiles, s);
+    if (resident && tr == 16) {
+      if (qb == 8) launch_down_resident<8, 1>(dn, gs, max_tiles, est_tiles, s);
+      else launch_down_resident<4, 1>(dn, gs, max_tiles, est_tiles, s);
+    } else if (resident) {
+      if (qb == 8) launch_down_resident<8, 4>(dn, gs, max_tiles, est_tiles, s);
+      else launch_down_resident<4, 4>(dn, gs, max_tiles, est_tiles, s);
+    } else if (tr == 16) {
+      launch_gemm<kDown, 1>(dn, qb, gs, max_tiles, s);
+    } else {
+      launch_gemm<kDown, 4>(dn, qb, gs, max_tiles, s);
+    }
     if (mk) mk->mark("down_mfma");
   }
 }
