@@ -77,7 +77,7 @@ def workload_name(spec, what: str = "forward") -> str:
     w = f"affine {spec.bits}-bit g{spec.group_size}" if spec.quantized else f"dense {spec.act}"
     extra = (", fused gate|up" if spec.gate_up_fused else "") + (
         ", GeGLU (tanh-GELU gate)" if spec.activation == "geglu" else "") + (
-        ", per-op bf16 GLU rounding" if spec.swiglu_round_bf16 else "") + (
+        ", per-op bf16 GLU rounding" if spec.glu_round else "") + (
         f", {spec.n_shared} shared experts" if spec.n_shared else "") + (
         ", Zipf-skewed router bias" if spec.router_bias == "zipf" else "")
     return (f"{spec.name}: MoE layer {what} T={spec.T} d_model={spec.d_model} d_ff={spec.d_ff} "
@@ -494,7 +494,7 @@ def cpu_baseline(name, n_tokens, threads=None):
     spec = inputs.workload(name)
     host = host_layer(name)
     d = oracle.Desc(spec.d_model, spec.d_ff, spec.n_experts, spec.top_k, spec.n_shared, spec.act == "bf16",
-                    spec.quantized, spec.group_size, spec.gate_up_fused, spec.swiglu_round_bf16,
+                    spec.quantized, spec.group_size, spec.gate_up_fused, spec.glu_round,
                     spec.renormalize, spec.bits, int(spec.activation == "geglu"),
                     spec.act == "f16")
     n = min(n_tokens, spec.T)

@@ -78,7 +78,7 @@ typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GEGLU = 1 } moe_activation;
  *  group_size     affine group length along the reduction dim: 32, 64 or 128.
  *  gate_up_fused  1: one [2*d_ff][d_model] matrix per expert whose rows are
  *                 [gate | up]; 0: separate gate and up matrices.
- *  swiglu_round_bf16  1: round gate and up to bf16, then sigmoid, g*s and
+ *  glu_round  1: round gate and up to bf16, then sigmoid, g*s and
  *                 (g*s)*u each rounded to bf16 (DS4Server #112, "Kernel
  *                 contract", SwiGLU epilogue); for GeGLU gate and up, then
  *                 gelu(g) and gelu(g)*u, each rounded to bf16.  Needs
@@ -93,7 +93,7 @@ typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GEGLU = 1 } moe_activation;
 typedef struct {
   int32_t d_model, d_ff, n_experts, top_k, n_shared;
   int32_t act_dtype, w_format, group_size;
-  int32_t gate_up_fused, swiglu_round_bf16, renormalize;
+  int32_t gate_up_fused, glu_round, renormalize;
   int32_t activation;
 } moe_layer_desc;
 

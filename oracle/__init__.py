@@ -39,7 +39,7 @@ def build() -> str:
 class _Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d_model", "d_ff", "n_experts", "top_k", "n_shared", "act_bf16", "w_q4",
-        "group_size", "gate_up_fused", "swiglu_round_bf16", "renormalize", "w_bits", "activation", "act_f16")]
+        "group_size", "gate_up_fused", "glu_round", "renormalize", "w_bits", "activation", "act_f16")]
 
 
 class _Proj(ctypes.Structure):
@@ -62,6 +62,8 @@ def _open(path: str):
     lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
     lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
     lib.oracle_f16_to_f32.restype = ctypes.c_float
+    lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_f16.restype = ctypes.c_uint16
     lib.oracle_router_logits.argtypes = [vp, i32, vp, vp, vp, vp]
     lib.oracle_route.argtypes = [vp, i32, vp, vp, vp, vp, vp]
     lib.oracle_dispatch.argtypes = [i32, i32, i32, vp, i32, vp, vp, vp, vp, vp]
@@ -107,7 +109,7 @@ class Desc:
     w_q4: bool = False
     group_size: int = 64
     gate_up_fused: bool = False
-    swiglu_round_bf16: bool = False
+    glu_round: bool = False
     renormalize: bool = True
     w_bits: int = 4           # affine code width (4 or 8) when w_q4
     activation: int = 0       # 0: SwiGLU, 1: GeGLU (tanh-GELU)
@@ -120,7 +122,7 @@ class Desc:
     def _c(self) -> _Desc:
         return _Desc(self.d_model, self.d_ff, self.n_experts, self.top_k, self.n_shared,
                      int(self.act_bf16), int(self.w_q4), self.group_size,
-                     int(self.gate_up_fused), int(self.swiglu_round_bf16), int(self.renormalize),
+                     int(self.gate_up_fused), int(self.glu_round), int(self.renormalize),
                      int(self.w_bits), int(self.activation), int(self.act_f16))
 
 
@@ -169,6 +171,10 @@ def f32_to_bf16(f: float) -> int:
 
 def f16_to_f32(h: int) -> float:
     return float(_load().oracle_f16_to_f32(int(h)))
+
+
+def f32_to_f16(f: float) -> int:
+    return int(_load().oracle_f32_to_f16(float(f)))
 
 
 def router_logits(desc: Desc, x, w_router, router_bias=None) -> np.ndarray:

@@ -56,6 +56,52 @@ float oracle_f16_to_f32(uint16_t h) {
   return (h & 0x8000u) ? -v : v;
 }
 
+/* fp32 -> IEEE binary16, round to nearest, ties to even.  The value is
+ * scaled into binary16's grid by its exponent: normal results keep 11
+ * significant bits (1 implicit + 10 stored), results below 2^-14 are
+ * multiples of 2^-24 (subnormals), results at or above 65520 overflow to
+ * infinity; NaN stays a quiet NaN.  The rounding is done on the exact fp32
+ * bits: the kept part and the discarded remainder are compared with half a
+ * unit of the last kept place. */
+uint16_t oracle_f32_to_f16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  const uint32_t ex = (u >> 23) & 0xffu, man = u & 0x7fffffu;
+  if (ex == 0xffu) return (uint16_t)(sign | 0x7c00u | (man ? 0x200u : 0u)); /* inf / NaN */
+  if (ex == 0 && man == 0) return sign;                                   /* +-0 (fp32 subnormals below too) */
+  /* the value is sig * 2^(e - 23) with sig the 24-bit significand */
+  const uint32_t sig = ex ? (man | 0x800000u) : man;
+  const int32_t e = ex ? (int32_t)ex - 127 : -126;
+  /* binary16 keeps bits down to 2^(max(e, -14) - 10): drop `sh` low bits of sig */
+  const int32_t keep_exp = (e < -14 ? -14 : e) - 10;
+  const int32_t sh = keep_exp - (e - 23);
+  uint32_t q;
+  if (sh >= 32) {
+    q = 0; /* far below half of the smallest subnormal */
+  } else {
+    q = sig >> sh;
+    const uint32_t rem = sig & ((1u << sh) - 1u), half = 1u << (sh - 1);
+    if (rem > half || (rem == half && (q & 1u))) q += 1u;
+  }
+  /* q counts units of 2^keep_exp; rebuild the binary16 fields */
+  if (e < -14) return (uint16_t)(sign | q); /* subnormal (q = 1024 carries into the smallest normal) */
+  int32_t be = e + 15;
+  if (q == 2048u) { /* rounding carried into the next binade */
+    q = 1024u;
+    be += 1;
+  }
+  if (be >= 31) return (uint16_t)(sign | 0x7c00u); /* overflow */
+  return (uint16_t)(sign | ((uint32_t)be << 10) | (q & 0x3ffu));
+}
+
+static float round_f16(float f) { return oracle_f16_to_f32(oracle_f32_to_f16(f)); }
+
+/* Per-op rounding of the gated epilogue to the layer's 16-bit activation
+ * dtype (DS4Server #112, "Kernel contract": the SwiGLU accumulators are
+ * rounded to the activation dtype, bf16 or fp16). */
+static float round_act(const oracle_desc *d, float f) { return d->act_f16 ? round_f16(f) : round_bf16(f); }
+
 /* A 16-bit value of the activation dtype (bf16, or fp16 with act_f16). */
 static float half_at(const oracle_desc *d, uint16_t h) {
   return d->act_f16 ? oracle_f16_to_f32(h) : oracle_bf16_to_f32(h);
@@ -294,19 +340,19 @@ void oracle_expert_apply(const oracle_desc *d, const oracle_experts *w,
     up_row(d, w, e, n, row);
     for (int32_t k = 0; k < D; ++k) u = u + xr[k] * row[k];
     if (d->activation == 1) {
-      if (d->swiglu_round_bf16) {
-        g = round_bf16(g);
-        u = round_bf16(u);
-        h[n] = round_bf16(round_bf16(gelu_tanh(g)) * u);
+      if (d->glu_round) {
+        g = round_act(d, g);
+        u = round_act(d, u);
+        h[n] = round_act(d, round_act(d, gelu_tanh(g)) * u);
       } else {
         h[n] = gelu_tanh(g) * u;
       }
-    } else if (d->swiglu_round_bf16) {
-      g = round_bf16(g);
-      u = round_bf16(u);
-      float s = round_bf16(sigmoid(g));
-      float a = round_bf16(g * s);
-      h[n] = round_bf16(a * u);
+    } else if (d->glu_round) {
+      g = round_act(d, g);
+      u = round_act(d, u);
+      float s = round_act(d, sigmoid(g));
+      float a = round_act(d, g * s);
+      h[n] = round_act(d, a * u);
     } else {
       h[n] = silu(g) * u;
     }

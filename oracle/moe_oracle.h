@@ -43,7 +43,7 @@ typedef struct {
   int32_t w_q4;              /* 0: dense weights in the activation dtype; 1: affine quantised */
   int32_t group_size;        /* quantisation group length along the reduction dim (32, 64, 128) */
   int32_t gate_up_fused;     /* 1: one [2*d_ff][d] matrix per expert, rows = [gate | up] */
-  int32_t swiglu_round_bf16; /* 1: per-op bf16 rounding in the gated epilogue */
+  int32_t glu_round; /* 1: per-op rounding to the activation dtype (bf16 or fp16) in the gated epilogue */
   int32_t renormalize;       /* 1: selected weights renormalised to sum to one */
   int32_t w_bits;            /* affine code width: 4 or 8 */
   int32_t activation;        /* 0: SwiGLU (silu(g) * u); 1: GeGLU with tanh-GELU (gelu(g) * u) */
@@ -71,6 +71,8 @@ typedef struct {
 float oracle_bf16_to_f32(uint16_t h);
 uint16_t oracle_f32_to_bf16(float f);
 float oracle_f16_to_f32(uint16_t h);
+/* fp32 -> binary16 bits, round to nearest even (subnormals, overflow to inf). */
+uint16_t oracle_f32_to_f16(float f);
 
 /* Router logits [T][E] in the canonical fp32 order. */
 void oracle_router_logits(const oracle_desc *d, int32_t T, const void *x,

@@ -382,7 +382,7 @@ void launch_t1_layer(const moe_layer_desc *d, const void *x, const moe_weights *
   const moe_proj &pg = d->gate_up_fused ? w->gate_up : w->gate;
   T1Args a{partials, n_chunks, w->router_bias, d->n_experts, d->top_k, d->n_shared, d->renormalize,
            static_cast<const uint16_t *>(x), d->act_dtype == MOE_DT_F16, d->d_model, d->d_ff, d->gate_up_fused,
-           d->swiglu_round_bf16, d->activation == MOE_ACT_GEGLU, d->group_size, d->act_dtype == MOE_DT_F16,
+           d->glu_round, d->activation == MOE_ACT_GEGLU, d->group_size, d->act_dtype == MOE_DT_F16,
            static_cast<const uint32_t *>(pg.w), static_cast<const uint16_t *>(pg.scales),
            static_cast<const uint16_t *>(pg.biases), static_cast<const uint32_t *>(w->up.w),
            static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases),

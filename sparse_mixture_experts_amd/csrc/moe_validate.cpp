@@ -14,14 +14,14 @@ int validate_desc(const moe_layer_desc *d) {
   if (d->act_dtype != MOE_DT_F32 && d->act_dtype != MOE_DT_BF16 && d->act_dtype != MOE_DT_F16)
     return MOE_E_INVALID;
   if (d->w_format != MOE_WF_DENSE && !affine(d)) return MOE_E_INVALID;
-  if (!is_bool(d->gate_up_fused) || !is_bool(d->swiglu_round_bf16) || !is_bool(d->renormalize))
+  if (!is_bool(d->gate_up_fused) || !is_bool(d->glu_round) || !is_bool(d->renormalize))
     return MOE_E_INVALID;
   if (d->activation != MOE_ACT_SWIGLU && d->activation != MOE_ACT_GEGLU) return MOE_E_INVALID;
   if (d->d_model <= 0 || d->d_ff <= 0 || d->d_model > 16384 || d->d_ff > 16384) return MOE_E_INVALID;
   if (d->n_experts < 1 || d->n_experts > kMaxExperts) return MOE_E_INVALID;
   if (d->top_k < 1 || d->top_k > kMaxTopK || d->top_k > d->n_experts) return MOE_E_INVALID;
   if (d->n_shared < 0 || d->n_shared > kMaxShared) return MOE_E_INVALID;
-  if (d->swiglu_round_bf16 && d->act_dtype != MOE_DT_BF16) return MOE_E_INVALID;
+  if (d->glu_round && d->act_dtype != MOE_DT_BF16) return MOE_E_INVALID;
   if (affine(d)) {
     // The affine formats carry scales/biases in the 16-bit activation dtype;
     // groups of 32, 64 or 128 along both reduction dims, which the matrix-core

@@ -54,7 +54,7 @@ class LayerSpec:
     wfmt: str = "dense"          # "dense" | "q4" | "q8" (affine 4- or 8-bit codes)
     group_size: int = 64
     gate_up_fused: bool = False
-    swiglu_round_bf16: bool = False
+    glu_round: bool = False
     renormalize: bool = True
     router_bias: str = "none"    # "none" | "zipf"
     x_scale: str = "unit"        # "unit" | "fan_in"
@@ -88,7 +88,7 @@ CONFIGS = {
     "q4-decode-t32": LayerSpec("q4-decode-t32", T=32, d_model=2048, d_ff=768, n_experts=128,
                                top_k=8, wfmt="q4", seed=3),
     "q4-prefill-t2048": LayerSpec("q4-prefill-t2048", T=2048, d_model=2048, d_ff=512, n_experts=512,
-                                  top_k=10, wfmt="q4", gate_up_fused=True, swiglu_round_bf16=True,
+                                  top_k=10, wfmt="q4", gate_up_fused=True, glu_round=True,
                                   seed=4),
     "q4-skewed-t256": LayerSpec("q4-skewed-t256", T=256, d_model=2048, d_ff=1408, n_experts=64,
                                 top_k=6, n_shared=2, wfmt="q4", router_bias="zipf", seed=5),
@@ -108,7 +108,7 @@ VARIANTS = {
     "q8-decode-t32": CONFIGS["q4-decode-t32"].with_(name="q8-decode-t32", wfmt="q8"),
     # per-op bf16 rounding is defined for bf16 activations only
     "f16-q4-prefill-t2048": CONFIGS["q4-prefill-t2048"].with_(name="f16-q4-prefill-t2048", act="f16",
-                                                              swiglu_round_bf16=False),
+                                                              glu_round=False),
 }
 
 

@@ -40,7 +40,7 @@ class MoeError(RuntimeError):
 class LayerDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d_model", "d_ff", "n_experts", "top_k", "n_shared", "act_dtype", "w_format", "group_size",
-        "gate_up_fused", "swiglu_round_bf16", "renormalize", "activation")]
+        "gate_up_fused", "glu_round", "renormalize", "activation")]
 
 
 class Proj(ctypes.Structure):
@@ -89,19 +89,19 @@ def moe_status_string(status: int) -> str:
 
 
 def make_desc(d_model, d_ff, n_experts, top_k, n_shared=0, act="bf16", wfmt="dense", group_size=64,
-              gate_up_fused=False, swiglu_round_bf16=False, renormalize=True,
+              gate_up_fused=False, glu_round=False, renormalize=True,
               activation="swiglu") -> LayerDesc:
     """act: "f32", "bf16" or "f16"; wfmt: "dense", "q4" or "q8" (affine 4-/8-bit codes); activation:
     "swiglu" or "geglu"."""
     return LayerDesc(d_model, d_ff, n_experts, top_k, n_shared,
                      _DT[act],
                      _WFMT[wfmt], group_size,
-                     int(gate_up_fused), int(swiglu_round_bf16), int(renormalize), _ACT[activation])
+                     int(gate_up_fused), int(glu_round), int(renormalize), _ACT[activation])
 
 
 def desc_from_spec(spec) -> LayerDesc:
     return make_desc(spec.d_model, spec.d_ff, spec.n_experts, spec.top_k, spec.n_shared, spec.act,
-                     spec.wfmt, spec.group_size, spec.gate_up_fused, spec.swiglu_round_bf16,
+                     spec.wfmt, spec.group_size, spec.gate_up_fused, spec.glu_round,
                      spec.renormalize, spec.activation)
 
 

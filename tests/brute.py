@@ -67,6 +67,16 @@ def bf16_round64(v: np.ndarray) -> np.ndarray:
         torch.float64).numpy()
 
 
+def f16_round64(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest IEEE binary16 (ties to even), via float32 first."""
+    return np.asarray(v, np.float64).astype(np.float32).astype(np.float16).astype(np.float64)
+
+
+def act_round64(spec: LayerSpec, v: np.ndarray) -> np.ndarray:
+    """Per-op rounding of the gated epilogue: to the layer's 16-bit activation dtype."""
+    return f16_round64(v) if spec.act == "f16" else bf16_round64(v)
+
+
 def gelu_tanh64(g: np.ndarray) -> np.ndarray:
     """torch's tanh-approximate GELU in float64 (a library routine, not the oracle's formula)."""
     import torch
@@ -78,17 +88,18 @@ def expert_outputs64(spec: LayerSpec, x64: np.ndarray, W) -> np.ndarray:
     gate, up, down = W
     g = np.einsum("td,efd->tef", x64, gate)
     u = np.einsum("td,efd->tef", x64, up)
+    r = lambda v: act_round64(spec, v)  # noqa: E731
     if spec.activation == "geglu":
-        if spec.swiglu_round_bf16:
-            g, u = bf16_round64(g), bf16_round64(u)
-            h = bf16_round64(bf16_round64(gelu_tanh64(g)) * u)
+        if spec.glu_round:
+            g, u = r(g), r(u)
+            h = r(r(gelu_tanh64(g)) * u)
         else:
             h = gelu_tanh64(g) * u
-    elif spec.swiglu_round_bf16:
-        g, u = bf16_round64(g), bf16_round64(u)
-        s = bf16_round64(1.0 / (1.0 + np.exp(-g)))
-        a = bf16_round64(g * s)
-        h = bf16_round64(a * u)
+    elif spec.glu_round:
+        g, u = r(g), r(u)
+        s = r(1.0 / (1.0 + np.exp(-g)))
+        a = r(g * s)
+        h = r(a * u)
     else:
         h = g / (1.0 + np.exp(-g)) * u
     return np.einsum("tef,edf->ted", h, down)

@@ -43,7 +43,7 @@ U = 2.0 ** -24  # unit roundoff of fp32
 def desc_of(spec: LayerSpec) -> oracle.Desc:
     return oracle.Desc(spec.d_model, spec.d_ff, spec.n_experts, spec.top_k, spec.n_shared,
                        spec.act == "bf16", spec.quantized, spec.group_size, spec.gate_up_fused,
-                       spec.swiglu_round_bf16, spec.renormalize, spec.bits, int(spec.activation == "geglu"),
+                       spec.glu_round, spec.renormalize, spec.bits, int(spec.activation == "geglu"),
                        spec.act == "f16")
 
 
@@ -56,7 +56,7 @@ SMALL = {
     "bf16": LayerSpec("bf16", T=9, d_model=128, d_ff=96, n_experts=5, top_k=2, seed=13),
     "q4": LayerSpec("q4", T=7, d_model=128, d_ff=128, n_experts=6, top_k=2, wfmt="q4", seed=14),
     "q4-fused-round": LayerSpec("q4-fused-round", T=7, d_model=128, d_ff=64, n_experts=8, top_k=3,
-                                wfmt="q4", gate_up_fused=True, swiglu_round_bf16=True, seed=15),
+                                wfmt="q4", gate_up_fused=True, glu_round=True, seed=15),
     "q4-shared-bias": LayerSpec("q4-shared-bias", T=6, d_model=128, d_ff=64, n_experts=4, top_k=2,
                                 n_shared=2, wfmt="q4", router_bias="zipf", seed=16),
     "bf16-norenorm": LayerSpec("bf16-norenorm", T=6, d_model=64, d_ff=64, n_experts=7, top_k=3,
@@ -66,7 +66,7 @@ SMALL = {
                               group_size=32, activation="geglu", seed=19),
     "q8-g128-fused-round-geglu": LayerSpec("q8-g128-fused-round-geglu", T=6, d_model=256, d_ff=128,
                                            n_experts=6, top_k=3, wfmt="q8", group_size=128,
-                                           gate_up_fused=True, swiglu_round_bf16=True, activation="geglu",
+                                           gate_up_fused=True, glu_round=True, activation="geglu",
                                            seed=20),
     "bf16-geglu": LayerSpec("bf16-geglu", T=7, d_model=128, d_ff=64, n_experts=5, top_k=2,
                             activation="geglu", seed=21),
@@ -77,6 +77,11 @@ SMALL = {
                                   act="f16", wfmt="q8", group_size=32, gate_up_fused=True, seed=25),
     "f32-fused-shared": LayerSpec("f32-fused-shared", T=5, d_model=96, d_ff=40, n_experts=4, top_k=2, n_shared=1,
                                   act="f32", gate_up_fused=True, seed=26),
+    # per-op rounding to fp16 (the activation dtype), SwiGLU and GeGLU
+    "f16-q4-fused-round": LayerSpec("f16-q4-fused-round", T=7, d_model=128, d_ff=64, n_experts=8, top_k=3,
+                                    act="f16", wfmt="q4", gate_up_fused=True, glu_round=True, seed=27),
+    "f16-dense-round-geglu": LayerSpec("f16-dense-round-geglu", T=6, d_model=128, d_ff=64, n_experts=5, top_k=2,
+                                       act="f16", glu_round=True, activation="geglu", seed=28),
 }
 
 _cache: dict = {}
@@ -263,33 +268,57 @@ def pin_expert(name: str):
             h, o = oracle.expert_apply(d, L["experts"], e, L["x"][t])
             ref = O[t, e]
             rms = math.sqrt(float(np.mean(ref ** 2)))
-            if spec.swiglu_round_bf16:
-                assert np.array_equal(brute.bf16_round64(h), h.astype(np.float64)), "h is not bf16"
+            if spec.glu_round:
+                assert np.array_equal(brute.act_round64(spec, h), h.astype(np.float64)), "h is not in the act dtype"
                 assert np.max(np.abs(o - ref)) <= 2e-2 * rms
             else:
                 assert np.max(np.abs(o - ref)) <= 1e-5 * rms, (t, e, np.max(np.abs(o - ref)) / rms)
-    if spec.swiglu_round_bf16:
+    if spec.glu_round:
         # per-op rounding reproduced element by element from fp64 gate/up
         gate, up, _ = brute.weights64(spec, L["experts"])
         hits = total = 0
         for t in range(spec.T):
             for e in range(spec.n_experts):
                 h, _ = oracle.expert_apply(d, L["experts"], e, L["x"][t])
-                g = brute.bf16_round64(gate[e] @ x64[t])
-                u = brute.bf16_round64(up[e] @ x64[t])
-                href = (_geglu_per_op if spec.activation == "geglu" else _swiglu_per_op)(g, u)
+                g = brute.act_round64(spec, gate[e] @ x64[t])
+                u = brute.act_round64(spec, up[e] @ x64[t])
+                href = (_geglu_per_op if spec.activation == "geglu" else _swiglu_per_op)(spec, g, u)
                 hits += int(np.sum(href == h))
                 total += h.size
         assert hits >= 0.97 * total, f"per-op bf16 SwiGLU matches only {hits}/{total}"
 
 
-def _swiglu_per_op(g, u):
-    s = brute.bf16_round64(1.0 / (1.0 + np.exp(-g)))
-    return brute.bf16_round64(brute.bf16_round64(g * s) * u)
+def _swiglu_per_op(spec, g, u):
+    r = lambda v: brute.act_round64(spec, v)  # noqa: E731
+    s = r(1.0 / (1.0 + np.exp(-g)))
+    return r(r(g * s) * u)
 
 
-def _geglu_per_op(g, u):
-    return brute.bf16_round64(brute.bf16_round64(brute.gelu_tanh64(g)) * u)
+def _geglu_per_op(spec, g, u):
+    r = lambda v: brute.act_round64(spec, v)  # noqa: E731
+    return r(r(brute.gelu_tanh64(g)) * u)
+
+
+def pin_f16_cast():
+    """fp32 -> binary16 (round to nearest even) against NumPy's cast: values
+    across the whole range, exact ties between neighbours, the subnormal range
+    (including half of the smallest subnormal), the largest finite values and
+    overflow to infinity, both zeros."""
+    rng = np.random.default_rng(3)
+    vals = [rng.standard_normal(3000).astype(np.float32) * np.float32(2.0 ** e) for e in (-30, -20, -14, -8, 0, 8, 15)]
+    # exact ties: an fp16 value plus half its unit in the last place
+    h = rng.integers(0, 0x7bff, 3000, dtype=np.uint16).view(np.float16).astype(np.float32)
+    ulp = np.spacing(h.astype(np.float16)).astype(np.float32)
+    ties = h + ulp / np.float32(2)
+    special = np.array([0.0, -0.0, np.inf, -np.inf, 65504.0, 65519.996, 65520.0, -65520.0, 1e9, 2.0 ** -24,
+                        2.0 ** -25, 2.0 ** -25 * 1.0001, 3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 * (1 - 2.0 ** -11),
+                        1e-40], np.float32)
+    v = np.concatenate(vals + [ties, -ties, special])
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.f32_to_f16(float(a)) for a in v], np.uint16)
+    assert np.array_equal(got, ref), f"fp16 narrowing differs at {v[np.flatnonzero(got != ref)[:5]]}"
+    assert math.isnan(oracle.f16_to_f32(oracle.f32_to_f16(float("nan"))))
 
 
 def pin_f16_decode():
@@ -356,7 +385,7 @@ def pin_layer(name: str):
     assert np.array_equal(idx, idx_r) and np.array_equal(w, w_r)
     ref = brute.layer_dense_masked64(spec, L, idx, w)
     rms = math.sqrt(float(np.mean(ref ** 2)))
-    tol = 2e-2 if spec.swiglu_round_bf16 else 1e-5
+    tol = 2e-2 if spec.glu_round else 1e-5
     assert np.max(np.abs(y - ref)) <= tol * rms, (name, np.max(np.abs(y - ref)) / rms)
     assert np.all(np.isfinite(y))
 
@@ -411,6 +440,7 @@ ALL_PINS = [
     ("dispatch", pin_dispatch, ()),
     *[(f"dequant[{n}]", pin_dequant, (n,)) for n in ("q4", "q8", "q4-g32-geglu", "q8-g128-fused-round-geglu",
                                                      "f16-q4-shared", "f16-q8-g32-fused")],
+    ("f16_cast", pin_f16_cast, ()),
     ("f16_decode", pin_f16_decode, ()),
     ("gelu_special_values", pin_gelu_special_values, ()),
     *[(f"expert[{n}]", pin_expert, (n,)) for n in SMALL],

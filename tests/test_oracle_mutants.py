@@ -25,11 +25,11 @@ MUTANTS = {
     "code_width_fixed_4": ("const int32_t per = 32 / bits;", "const int32_t per = 8;"),
     "group_size_fixed_64": ("const int32_t G = d->group_size;", "const int32_t G = 64;"),
     "gelu_cubic_dropped": ("(g + 0.044715f * g * g * g)", "(g)"),
-    "geglu_runs_silu": ("    if (d->activation == 1) {\n      if (d->swiglu_round_bf16) {",
-                        "    if (0) {\n      if (d->swiglu_round_bf16) {"),
+    "geglu_runs_silu": ("    if (d->activation == 1) {\n      if (d->glu_round) {",
+                        "    if (0) {\n      if (d->glu_round) {"),
     "geglu_grad_runs_silu": ("  if (d->activation == 1) {\n    const float a = 0.7978845608028654f",
                              "  if (0) {\n    const float a = 0.7978845608028654f"),
-    "geglu_rounding_skipped": ("h[n] = round_bf16(round_bf16(gelu_tanh(g)) * u);", "h[n] = gelu_tanh(g) * u;"),
+    "geglu_rounding_skipped": ("h[n] = round_act(d, round_act(d, gelu_tanh(g)) * u);", "h[n] = gelu_tanh(g) * u;"),
     "scale_bias_swapped": ("out[k] = s * (float)q + b;", "out[k] = b * (float)q + s;"),
     "group_index_wrong": ("float s = half_at(d, sc[(int64_t)(k / G) * N]);", "float s = half_at(d, sc[0]);"),
     "f16_exponent_bias": ("(int)e - 25", "(int)e - 24"),
@@ -49,7 +49,10 @@ MUTANTS = {
                                "    gate_row(d, w, e, n, row);\n    for (int32_t k = 0; k < D; ++k) dxr[k]"),
     "silu_sign": ("static float silu(float g) { return g / (1.0f + expf(-g)); }",
                   "static float silu(float g) { return g / (1.0f + expf(g)); }"),
-    "sigmoid_not_rounded": ("float s = round_bf16(sigmoid(g));", "float s = sigmoid(g);"),
+    "sigmoid_not_rounded": ("float s = round_act(d, sigmoid(g));", "float s = sigmoid(g);"),
+    "f16_layers_round_to_bf16": ("return d->act_f16 ? round_f16(f) : round_bf16(f);", "return round_bf16(f);"),
+    "f16_ties_away": ("if (rem > half || (rem == half && (q & 1u))) q += 1u;", "if (rem >= half) q += 1u;"),
+    "f16_subnormals_flushed": ("if (e < -14) return (uint16_t)(sign | q);", "if (e < -14) return sign;"),
     "dispatch_unstable": ("return i < j ? -1 : (i > j);", "return i < j ? 1 : -(i > j);"),
     "row_map_modulo": ("row_map[p] = order[p] / top_k;", "row_map[p] = order[p] % top_k;"),
     "tile_off_floor": ("(cnt + tile_rows - 1) / tile_rows", "cnt / tile_rows"),

@@ -29,7 +29,7 @@ MID = {
     "mid-bf16": LayerSpec("mid-bf16", T=300, d_model=256, d_ff=320, n_experts=8, top_k=2, seed=22),
     "mid-q4": LayerSpec("mid-q4", T=200, d_model=512, d_ff=256, n_experts=16, top_k=4, wfmt="q4", seed=23),
     "mid-q4-fused-round": LayerSpec("mid-q4-fused-round", T=257, d_model=256, d_ff=128, n_experts=32,
-                                    top_k=6, wfmt="q4", gate_up_fused=True, swiglu_round_bf16=True,
+                                    top_k=6, wfmt="q4", gate_up_fused=True, glu_round=True,
                                     seed=24),
     "mid-q4-shared-skew": LayerSpec("mid-q4-shared-skew", T=130, d_model=256, d_ff=192, n_experts=16,
                                     top_k=3, n_shared=2, wfmt="q4", router_bias="zipf", seed=25),
@@ -39,7 +39,7 @@ MID = {
     # per-op rounding and a shared expert
     "mid-q4-decode-fused": LayerSpec("mid-q4-decode-fused", T=5, d_model=320, d_ff=192, n_experts=32,
                                      top_k=4, n_shared=1, wfmt="q4", gate_up_fused=True,
-                                     swiglu_round_bf16=True, router_bias="zipf", seed=30),
+                                     glu_round=True, router_bias="zipf", seed=30),
     "mid-bf16-norenorm": LayerSpec("mid-bf16-norenorm", T=20, d_model=192, d_ff=64, n_experts=5, top_k=3,
                                    renormalize=False, seed=27),
     "mid-soft-routing": LayerSpec("mid-soft-routing", T=9, d_model=128, d_ff=64, n_experts=4, top_k=4,
@@ -52,7 +52,7 @@ MID = {
     "mid-q8": LayerSpec("mid-q8", T=200, d_model=512, d_ff=256, n_experts=16, top_k=4, wfmt="q8", seed=32),
     "mid-q8-g32-geglu-fused-round": LayerSpec("mid-q8-g32-geglu-fused-round", T=150, d_model=256, d_ff=192,
                                               n_experts=16, top_k=3, wfmt="q8", group_size=32,
-                                              activation="geglu", gate_up_fused=True, swiglu_round_bf16=True,
+                                              activation="geglu", gate_up_fused=True, glu_round=True,
                                               seed=33),
     "mid-q4-g128-shared": LayerSpec("mid-q4-g128-shared", T=120, d_model=384, d_ff=256, n_experts=12, top_k=2,
                                     n_shared=1, wfmt="q4", group_size=128, router_bias="zipf", seed=34),
@@ -63,7 +63,7 @@ MID = {
     "mid-q4-decode-g32-geglu-fused-round": LayerSpec("mid-q4-decode-g32-geglu-fused-round", T=4, d_model=320,
                                                      d_ff=192, n_experts=32, top_k=4, n_shared=1, wfmt="q4",
                                                      group_size=32, activation="geglu", gate_up_fused=True,
-                                                     swiglu_round_bf16=True, seed=37),
+                                                     glu_round=True, seed=37),
     "mid-q8-decode-fused": LayerSpec("mid-q8-decode-fused", T=2, d_model=1024, d_ff=320, n_experts=32, top_k=4,
                                      wfmt="q8", gate_up_fused=True, seed=38),
     # decode tiles holding more than 1024 8-bit codes per lane row, down's
@@ -129,7 +129,7 @@ MID = {
     # wave) with groups of 128
     "mid-t1-q4-shared-fused-round": LayerSpec("mid-t1-q4-shared-fused-round", T=1, d_model=320, d_ff=192,
                                               n_experts=32, top_k=4, n_shared=1, wfmt="q4", gate_up_fused=True,
-                                              swiglu_round_bf16=True, router_bias="zipf", seed=60),
+                                              glu_round=True, router_bias="zipf", seed=60),
     "mid-t1-f16-q8-g32-geglu": LayerSpec("mid-t1-f16-q8-g32-geglu", T=1, d_model=512, d_ff=256, n_experts=64,
                                          top_k=8, act="f16", wfmt="q8", group_size=32, activation="geglu",
                                          seed=61),
