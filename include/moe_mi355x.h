@@ -78,11 +78,12 @@ typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GEGLU = 1 } moe_activation;
  *  group_size     affine group length along the reduction dim: 32, 64 or 128.
  *  gate_up_fused  1: one [2*d_ff][d_model] matrix per expert whose rows are
  *                 [gate | up]; 0: separate gate and up matrices.
- *  glu_round  1: round gate and up to bf16, then sigmoid, g*s and
- *                 (g*s)*u each rounded to bf16 (DS4Server #112, "Kernel
- *                 contract", SwiGLU epilogue); for GeGLU gate and up, then
- *                 gelu(g) and gelu(g)*u, each rounded to bf16.  Needs
- *                 act_dtype == BF16.
+ *  glu_round      1: per-op rounding of the gated unit to the activation
+ *                 dtype (bf16 or fp16, nearest even; DS4Server #112, "Kernel
+ *                 contract", SwiGLU epilogue): gate and up rounded, then
+ *                 sigmoid, g*s and (g*s)*u each rounded; for GeGLU gate and
+ *                 up, then gelu(g) and gelu(g)*u each rounded.  Needs a
+ *                 16-bit act_dtype.
  *  renormalize    1: the k selected weights are divided by their sum.
  *  activation     moe_activation of the expert GLU: SwiGLU, h = silu(g)*u,
  *                 or GeGLU with the tanh form of GELU,

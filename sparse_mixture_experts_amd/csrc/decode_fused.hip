@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256) void t1_gateup_kernel(T1Args a) {
         g += part[w][lane];
         u += part[w][8 + lane];
       }
-      hv = glu(g, u, a.round_ops != 0, a.geglu != 0);
+      hv = glu(g, u, a.round_ops, a.geglu != 0);
       a.h[int64_t(slot) * F + cb * 8 + lane] = hv;
     }
     float m = fabsf(hv);
@@ -382,7 +382,7 @@ void launch_t1_layer(const moe_layer_desc *d, const void *x, const moe_weights *
   const moe_proj &pg = d->gate_up_fused ? w->gate_up : w->gate;
   T1Args a{partials, n_chunks, w->router_bias, d->n_experts, d->top_k, d->n_shared, d->renormalize,
            static_cast<const uint16_t *>(x), d->act_dtype == MOE_DT_F16, d->d_model, d->d_ff, d->gate_up_fused,
-           d->glu_round, d->activation == MOE_ACT_GEGLU, d->group_size, d->act_dtype == MOE_DT_F16,
+           glu_round_mode(d), d->activation == MOE_ACT_GEGLU, d->group_size, d->act_dtype == MOE_DT_F16,
            static_cast<const uint32_t *>(pg.w), static_cast<const uint16_t *>(pg.scales),
            static_cast<const uint16_t *>(pg.biases), static_cast<const uint32_t *>(w->up.w),
            static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases),

@@ -158,18 +158,27 @@ __device__ __forceinline__ float gelu_tanh_f32(float g) {
   return g * sigmoid_f32(z2);
 }
 
+// Per-op rounding modes of the gated unit: none, or to the layer's 16-bit
+// activation dtype.
+constexpr int kRoundNone = 0, kRoundBF16 = 1, kRoundF16 = 2;
+__device__ __forceinline__ float round_f16(float f) { return float(_Float16(f)); }
+__device__ __forceinline__ float round_mode(float f, int mode) {
+  return mode == kRoundF16 ? round_f16(f) : round_bf16(f);
+}
+
 // The gated unit of one (gate, up) pair: SwiGLU, silu(g) * u, or GeGLU,
-// gelu_tanh(g) * u.  With per-op rounding: gate and up rounded to bf16, then
-// for SwiGLU sigmoid, g*s and (g*s)*u each rounded to bf16; for GeGLU
-// gelu(g) and gelu(g)*u each rounded to bf16.
-__device__ __forceinline__ float glu(float g, float u, bool round_ops, bool geglu) {
-  if (!round_ops) return (geglu ? gelu_tanh_f32(g) : silu_f32(g)) * u;
-  g = round_bf16(g);
-  u = round_bf16(u);
-  if (geglu) return round_bf16(round_bf16(gelu_tanh_f32(g)) * u);
-  float s = round_bf16(sigmoid_f32(g));
-  float a = round_bf16(g * s);
-  return round_bf16(a * u);
+// gelu_tanh(g) * u.  With per-op rounding (mode bf16 or fp16): gate and up
+// rounded, then for SwiGLU sigmoid, g*s and (g*s)*u each rounded; for GeGLU
+// gelu(g) and gelu(g)*u each rounded (round to nearest even).
+__device__ __forceinline__ float glu(float g, float u, int round_mode_, bool geglu) {
+  if (round_mode_ == kRoundNone) return (geglu ? gelu_tanh_f32(g) : silu_f32(g)) * u;
+  auto r = [&](float v) { return round_mode(v, round_mode_); };
+  g = r(g);
+  u = r(u);
+  if (geglu) return r(r(gelu_tanh_f32(g)) * u);
+  float s = r(sigmoid_f32(g));
+  float a = r(g * s);
+  return r(a * u);
 }
 
 

@@ -214,7 +214,7 @@ void launch_gemv(const moe_layer_desc *d, int32_t T, const void *x, const int32_
   const int esz = DT == kDtF32 ? 4 : 2;
   const int max_items = min(E, N) + S;
   const moe_proj &pg = d->gate_up_fused ? w->gate_up : w->gate;
-  GateUpArgs ga{x, row_map, T, N, D, F, E, d->gate_up_fused, d->glu_round,
+  GateUpArgs ga{x, row_map, T, N, D, F, E, d->gate_up_fused, glu_round_mode(d),
                 d->activation == MOE_ACT_GEGLU, rows_per_pass(D, esz), pg.w, static_cast<const uint16_t *>(pg.scales),
                 static_cast<const uint16_t *>(pg.biases), w->up.w,
                 static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases),

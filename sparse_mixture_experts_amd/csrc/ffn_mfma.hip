@@ -81,7 +81,7 @@ struct GemmArgs {
   int T, N, K;              // token count, routed rows, reduction length
   int n_out;                // output columns of the projection (F for gate/up, D for down)
   int fused;                // gate/up: [gate | up] in one matrix
-  int round_ops;            // per-op bf16 GLU
+  int round_ops;            // per-op GLU rounding mode (kRoundNone / BF16 / F16)
   int geglu;                // gate/up: tanh-GELU gate (else SiLU)
   int half_f16;             // affine scales/biases are fp16 (else bf16)
   const void *w0;           // gate (or gate_up) / down weights
@@ -1321,7 +1321,7 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
   }
   const moe_proj &pg = d->gate_up_fused ? w->gate_up : w->gate;
   GemmArgs gu{aff ? sc.x16 : x, sc.xsh, sc.hsh, nblk, row_map, T, T * d->top_k, d->d_model, d->d_ff,
-              d->gate_up_fused, d->glu_round, geglu, int(f16),
+              d->gate_up_fused, glu_round_mode(d), geglu, int(f16),
               pg.w, static_cast<const uint16_t *>(pg.scales), static_cast<const uint16_t *>(pg.biases),
               w->up.w, static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases),
               counters, tiles, sc.h, bx_major, 1, 0};
@@ -1335,7 +1335,7 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
     // at most one routed row per expert on average: whole-K loads per wave
     // (one memory round trip), h as bf16 between the two projections
     DecArgs dg{sc.x16, sc.xsh, row_map, T, T * d->top_k, d->d_model, d->d_ff, d->gate_up_fused,
-               d->glu_round, geglu, gs, int(f16), static_cast<const uint32_t *>(pg.w),
+               glu_round_mode(d), geglu, gs, int(f16), static_cast<const uint32_t *>(pg.w),
                static_cast<const uint16_t *>(pg.scales), static_cast<const uint16_t *>(pg.biases),
                static_cast<const uint32_t *>(w->up.w), static_cast<const uint16_t *>(w->up.scales),
                static_cast<const uint16_t *>(w->up.biases), counters, tiles, sc.h};

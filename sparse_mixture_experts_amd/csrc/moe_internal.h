@@ -35,6 +35,11 @@ inline bool affine(const moe_layer_desc *d) {
 // Bytes per element of the GLU intermediate h (16-bit for bf16 and fp16 layers).
 inline int64_t h_bytes(const moe_layer_desc *d) { return d->act_dtype == MOE_DT_F32 ? 4 : 2; }
 bool use_mfma(const moe_layer_desc *d);
+// Per-op GLU rounding mode of the layer: 0 none, 1 bf16, 2 fp16 (the layer's
+// activation dtype).
+inline int glu_round_mode(const moe_layer_desc *d) {
+  return d->glu_round ? (d->act_dtype == MOE_DT_F16 ? 2 : 1) : 0;
+}
 
 // Workspace carve-up.  Every section is 256-byte aligned.
 struct Workspace {

@@ -21,7 +21,7 @@ int validate_desc(const moe_layer_desc *d) {
   if (d->n_experts < 1 || d->n_experts > kMaxExperts) return MOE_E_INVALID;
   if (d->top_k < 1 || d->top_k > kMaxTopK || d->top_k > d->n_experts) return MOE_E_INVALID;
   if (d->n_shared < 0 || d->n_shared > kMaxShared) return MOE_E_INVALID;
-  if (d->glu_round && d->act_dtype != MOE_DT_BF16) return MOE_E_INVALID;
+  if (d->glu_round && d->act_dtype == MOE_DT_F32) return MOE_E_INVALID;  // rounds to a 16-bit dtype
   if (affine(d)) {
     // The affine formats carry scales/biases in the 16-bit activation dtype;
     // groups of 32, 64 or 128 along both reduction dims, which the matrix-core

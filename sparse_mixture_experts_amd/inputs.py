@@ -106,9 +106,8 @@ VARIANTS = {
     "q4g128-prefill-t2048": CONFIGS["q4-prefill-t2048"].with_(name="q4g128-prefill-t2048", group_size=128),
     "q8-decode-t1": CONFIGS["q4-decode-t1"].with_(name="q8-decode-t1", wfmt="q8"),
     "q8-decode-t32": CONFIGS["q4-decode-t32"].with_(name="q8-decode-t32", wfmt="q8"),
-    # per-op bf16 rounding is defined for bf16 activations only
-    "f16-q4-prefill-t2048": CONFIGS["q4-prefill-t2048"].with_(name="f16-q4-prefill-t2048", act="f16",
-                                                              glu_round=False),
+    # fp16 activations, scales and biases; the per-op GLU rounding is to fp16
+    "f16-q4-prefill-t2048": CONFIGS["q4-prefill-t2048"].with_(name="f16-q4-prefill-t2048", act="f16"),
 }
 
 

@@ -98,9 +98,10 @@ def test_affine_formats_and_groups(lib):
     for act in ("bf16", "f16"):
         d = moe.make_desc(2048, 768, 128, 8, act=act, wfmt="q4")
         assert lib.moe_workspace_size(ctypes.byref(d), 4, ctypes.byref(size)) == moe.MOE_OK
-    # per-op bf16 rounding needs bf16 activations
-    d = moe.make_desc(256, 128, 8, 2, act="f16", glu_round=True)
-    assert lib.moe_workspace_size(ctypes.byref(d), 4, ctypes.byref(size)) == moe.MOE_E_INVALID
+    # per-op GLU rounding goes to the 16-bit activation dtype: bf16 or fp16
+    for act in ("bf16", "f16"):
+        d = moe.make_desc(256, 128, 8, 2, act=act, glu_round=True)
+        assert lib.moe_workspace_size(ctypes.byref(d), 4, ctypes.byref(size)) == moe.MOE_OK
 
 
 def test_backward_validation(lib):
@@ -119,7 +120,7 @@ def test_backward_validation(lib):
         moe.MOE_E_WORKSPACE
 
 
-def test_top_k_above_experts_and_rounding_needs_bf16(lib):
+def test_top_k_above_experts_and_rounding_needs_16bit(lib):
     d = moe.make_desc(64, 64, 4, 5, act="f32")
     assert lib.moe_workspace_size(ctypes.byref(d), 1, ctypes.byref(ctypes.c_size_t())) == moe.MOE_E_INVALID
     d = moe.make_desc(64, 64, 4, 2, act="f32", glu_round=True)

@@ -135,6 +135,25 @@ MID = {
                                          seed=61),
     "mid-t1-q4-k12-s2-g128": LayerSpec("mid-t1-q4-k12-s2-g128", T=1, d_model=256, d_ff=384, n_experts=64,
                                        top_k=12, n_shared=2, wfmt="q4", group_size=128, seed=62),
+    # per-op GLU rounding to fp16 on fp16 layers: 64-row and 16-row affine
+    # tiles, decode tiles, the one-token kernels, dense fp16 matrix cores with
+    # GeGLU and the dense vector-unit path
+    "mid-f16-q4-fused-round": LayerSpec("mid-f16-q4-fused-round", T=257, d_model=256, d_ff=128, n_experts=32,
+                                        top_k=6, act="f16", wfmt="q4", gate_up_fused=True, glu_round=True,
+                                        seed=63),
+    "mid-f16-q8-tile16-round-geglu": LayerSpec("mid-f16-q8-tile16-round-geglu", T=40, d_model=256, d_ff=192,
+                                               n_experts=32, top_k=4, act="f16", wfmt="q8", glu_round=True,
+                                               activation="geglu", seed=64),
+    "mid-f16-q4-decode-round": LayerSpec("mid-f16-q4-decode-round", T=3, d_model=512, d_ff=256, n_experts=64,
+                                         top_k=8, act="f16", wfmt="q4", glu_round=True, seed=65),
+    "mid-t1-f16-q4-round": LayerSpec("mid-t1-f16-q4-round", T=1, d_model=512, d_ff=256, n_experts=64, top_k=8,
+                                     n_shared=1, act="f16", wfmt="q4", gate_up_fused=True, glu_round=True,
+                                     seed=66),
+    "mid-f16-dense-round-geglu": LayerSpec("mid-f16-dense-round-geglu", T=120, d_model=256, d_ff=192,
+                                           n_experts=8, top_k=2, act="f16", glu_round=True, activation="geglu",
+                                           seed=67),
+    "mid-f16-gemv-round": LayerSpec("mid-f16-gemv-round", T=20, d_model=96, d_ff=40, n_experts=4, top_k=2,
+                                    act="f16", glu_round=True, seed=68),
 }
 FULL = {**inputs.CONFIGS, **inputs.VARIANTS}
 
