@@ -73,11 +73,17 @@ __device__ int block_exscan(int32_t *a, int n, int32_t *wave_tot) {
 __device__ void emit_plan(const int32_t *off, const int32_t *cnt, int32_t *act_flag,
                           int32_t *tile_cnt, int32_t *wave_tot, int E, int S, int N, int T, int tr,
                           int32_t *counters, PlanItem *act_items, PlanItem *tiles) {
+  __shared__ int32_t s_multi;  // tiles that belong to experts with two or more tiles
   const int tid = threadIdx.x, nth = blockDim.x;
+  if (tid == 0) s_multi = 0;
+  __syncthreads();
+  int multi = 0;
   for (int e = tid; e < E; e += nth) {
     act_flag[e] = cnt[e] > 0;
     tile_cnt[e] = (cnt[e] + tr - 1) / tr;
+    if (tile_cnt[e] >= 2) multi += tile_cnt[e];
   }
+  if (multi) atomicAdd(&s_multi, multi);
   __syncthreads();
   const int n_act = block_exscan(act_flag, E, wave_tot);
   const int n_tiles = block_exscan(tile_cnt, E, wave_tot);
@@ -96,6 +102,7 @@ __device__ void emit_plan(const int32_t *off, const int32_t *cnt, int32_t *act_f
   if (tid == 0) {
     counters[0] = n_act + S;
     counters[1] = n_tiles + S * shared_tiles;
+    counters[2] = plan_multi_tile(s_multi + (shared_tiles >= 2 ? S * shared_tiles : 0), counters[1]);
   }
 }
 
@@ -215,7 +222,7 @@ __device__ void write_bad(int N, int E, int32_t *order, int32_t *inv_order, int3
     expert_off[e] = e == E ? -1 : 0;
     tile_off[e] = 0;
   }
-  if (tid == 0) counters[0] = counters[1] = 0;
+  if (tid == 0) counters[0] = counters[1] = counters[2] = 0;
 }
 
 // Whole dispatch in one workgroup (small N).
@@ -398,7 +405,7 @@ __global__ __launch_bounds__(kMbThreads) void dispatch_rank_kernel(
         expert_off[e] = e == E ? -1 : 0;
         tile_off[e] = 0;
       }
-      if (tid == 0) counters[0] = counters[1] = 0;
+      if (tid == 0) counters[0] = counters[1] = counters[2] = 0;
     } else {
       const int p0 = b * seg, p1 = min(N, p0 + seg);
       for (int i = p0 + tid; i < p1; i += kMbThreads) order[i] = inv_order[i] = row_map[i] = -1;

@@ -41,7 +41,7 @@ __device__ __forceinline__ void tiny_dispatch(const int32_t *f, int N, int K, in
       expert_off[e] = e == E ? -1 : 0;
       tile_off[e] = 0;
     }
-    if (lane == 0) counters[0] = counters[1] = 0;
+    if (lane == 0) counters[0] = counters[1] = counters[2] = 0;
     return;
   }
   for (int e = lane; e < E; e += kWave) cnt[e] = 0;
@@ -55,14 +55,16 @@ __device__ __forceinline__ void tiny_dispatch(const int32_t *f, int N, int K, in
   // caller tiles, plan tiles and active experts of the runs.
   const int chunk = (E + kWave - 1) / kWave;
   const int b = min(E, lane * chunk), b1 = min(E, b + chunk);
-  int rs = 0, us = 0, ps = 0, as = 0;
+  int rs = 0, us = 0, ps = 0, as = 0, ms = 0;
   for (int e = b; e < b1; ++e) {
     const int c = cnt[e];
     rs += c;
     us += (c + tile_rows - 1) / tile_rows;
     ps += (c + tr - 1) / tr;
     as += c > 0;
+    if (c > tr) ms += (c + tr - 1) / tr;  // tiles of experts with two or more
   }
+  const int multi = wave_incl_scan(ms);
   // inclusive scans
   const int rx = wave_incl_scan(rs), ux = wave_incl_scan(us), px = wave_incl_scan(ps), ax = wave_incl_scan(as);
   const int n_utiles = read_lane_i(ux, kWave - 1), n_ptiles = read_lane_i(px, kWave - 1);
@@ -91,6 +93,8 @@ __device__ __forceinline__ void tiny_dispatch(const int32_t *f, int N, int K, in
     tile_off[E] = n_utiles;
     counters[0] = n_act + S;
     counters[1] = n_ptiles + S * shared_tiles;
+    counters[2] = plan_multi_tile(read_lane_i(multi, kWave - 1) + (shared_tiles >= 2 ? S * shared_tiles : 0),
+                                  counters[1]);
   }
   __builtin_amdgcn_wave_barrier();
 

@@ -178,7 +178,8 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
   // expert next to each other (they read the same weights).
   const int z = item / (n_tiles * nbx);
   item -= z * n_tiles * nbx;
-  const int tile_id = a.bx_major ? item % n_tiles : item / nbx, bx = a.bx_major ? item / n_tiles : item % nbx;
+  const bool bxm = a.bx_major | a.counters[2];  // host layer shape, or the plan's multi-tile experts
+  const int tile_id = bxm ? item % n_tiles : item / nbx, bx = bxm ? item / n_tiles : item % nbx;
   const PlanItem tile = a.tiles[tile_id];
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
@@ -687,7 +688,8 @@ __device__ __forceinline__ void down_resident_body(const GemmArgs &a, int cbpw) 
     item = (lin % 8) * per + slot;
   }
   if (item >= work) return;
-  const int tile_id = item / nbx, grp = item % nbx;
+  const bool bxm = a.bx_major | a.counters[2];  // the tiles of one expert back to back per column group
+  const int tile_id = bxm ? item % n_tiles : item / nbx, grp = bxm ? item / n_tiles : item % nbx;
   PlanItem tile = a.tiles[tile_id];
   tile.expert = __builtin_amdgcn_readfirstlane(tile.expert);
   tile.row0 = __builtin_amdgcn_readfirstlane(tile.row0);

@@ -15,6 +15,13 @@ struct PlanItem {
   int32_t expert, row0, rows, pad;
 };
 
+// Work-plan counters (int32 in the workspace): [0] active items, [1] row
+// tiles, [2] 1 when at least a quarter of the tiles belong to experts (or
+// shared experts) with two or more tiles: the grouped GEMMs then run the
+// tiles of one expert back to back for each column block, so its weights are
+// read from L2 by all but the first.
+__host__ __device__ inline int plan_multi_tile(int multi_tiles, int tiles) { return 4 * multi_tiles >= tiles ? 1 : 0; }
+
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxShared = 8;
@@ -47,7 +54,7 @@ struct Workspace {
   size_t route;                       // router logits / chunk partials (f32)
   size_t order, inv_order, row_map;   // [N] int32
   size_t expert_off, tile_off;        // [E+1] int32
-  size_t counters;                    // 64 int32: [0] active items, [1] tiles
+  size_t counters;                    // 64 int32: [0] active items, [1] tiles, [2] multi-tile experts
   size_t dsp;                         // dispatch scratch (dispatch_scratch_ints)
   size_t act_items;                   // [E+S] PlanItem
   size_t tiles;                       // [max_tiles] PlanItem

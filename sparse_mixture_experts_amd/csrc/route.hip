@@ -38,6 +38,9 @@ constexpr int kThreads = 256;
 constexpr int kChunk = 64;
 
 constexpr int kXsPad = 8;
+// Up to this many tokens the logits run as chunk partials (one wave per (64
+// experts, chunk, 8 tokens)), summed in chunk order by the selection kernel.
+constexpr int kChunkRouterMaxT = 512;
 
 // LDS index of staged column k (relative to the block's first column), token t.
 template <int TT>
@@ -263,7 +266,7 @@ int64_t route_scratch_floats(const moe_layer_desc *d, int32_t T) {
   // Covers every T' <= T: below 64 tokens (and at any T when C > 32) the
   // chunk partials, C per (token, expert), go through the workspace.
   const int64_t C = (d->d_model + kChunk - 1) / kChunk;
-  const int64_t t_split = C <= 32 ? std::min<int64_t>(T, 63) : int64_t(T);
+  const int64_t t_split = C <= 32 ? std::min<int64_t>(T, kChunkRouterMaxT) : int64_t(T);
   int64_t n = std::max<int64_t>(int64_t(T) * d->n_experts, C * t_split * d->n_experts);
   if (route_mfma_applies(d, T)) n = std::max(n, route_mfma_scratch_floats(d, T));
   return n;
@@ -305,10 +308,11 @@ void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int D = d->d_model, E = d->n_experts;
   const int C = (D + kChunk - 1) / kChunk;
-  // Large T: 8 tokens per block with every chunk of the block on chip.
-  // Small T: one wave per (64 experts, chunk, 8 tokens) for many parallel
-  // fma chains, the partials summed by the selection kernel.  Large T with
-  // d_model > 2048: one token per block, 2 chunks per block.
+  // Up to 512 tokens: one wave per (64 experts, chunk, 8 tokens) for many
+  // parallel fma chains, the partials summed by the selection kernel.  Beyond
+  // (when the matrix-core router does not apply): 8 tokens per block with
+  // every chunk of the block on chip; with d_model > 2048 one token per
+  // block, 2 chunks per block.
   int n_chunks = C;
   auto logits = [&](auto dt) {
     constexpr int DT = decltype(dt)::value;
@@ -316,7 +320,7 @@ void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void 
       // one token: one chain per lane (no idle token slots)
       const dim3 grid((E + kWave - 1) / kWave, C, 1);
       hipLaunchKernelGGL((route_chunk_kernel<DT, 1>), grid, dim3(kWave), 0, s, x, w_router, T, D, E, scratch);
-    } else if (T < 64) {
+    } else if (T <= kChunkRouterMaxT) {
       const dim3 grid((E + kWave - 1) / kWave, C, (T + 7) / 8);
       hipLaunchKernelGGL((route_chunk_kernel<DT, 8>), grid, dim3(kWave), 0, s, x, w_router, T, D, E, scratch);
     } else if (C <= 32) {

@@ -476,8 +476,10 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
 }  // namespace
 
 bool route_mfma_applies(const moe_layer_desc *d, int32_t T) {
+  // Below 64K (token, expert) logits the per-chunk vector router is faster:
+  // the matrix-core router's three launches cost more than its fma chains.
   return d->act_dtype != MOE_DT_F32 && d->renormalize && d->d_model % kChunk == 0 &&
-         d->d_model <= kWave * kChunk && T >= 64;
+         d->d_model <= kWave * kChunk && T >= 64 && int64_t(T) * d->n_experts >= 65536;
 }
 
 // Scratch: L~ [T][E] f32, then WT [E][D] (16-bit), then norm partials [D/256][E]

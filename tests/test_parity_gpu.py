@@ -375,15 +375,17 @@ def test_zero_input_gives_zero_output():
 
 
 @pytest.mark.parametrize("act", ["bf16", "f16"])
-@pytest.mark.parametrize("T", [1, 9, 96])
+@pytest.mark.parametrize("T", [1, 9, 96, 160])
 def test_route_exact_ties_and_zero_rows(T, act):
     """Duplicated router columns tie exactly and zero rows tie everywhere: the
-    lower expert index must win, for one token and on the small-T and
-    large-T routers (one token: a zero row for bf16, the duplicated columns
+    lower expert index must win, for one token and on the chunk and
+    matrix-core routers (one token: a zero row for bf16, the duplicated columns
     alone for fp16).  fp16 layers also get rows of fp16 subnormals (x * 2^-20) and rows
-    near fp16's largest values (x * 2^12), which the large-T router splits
+    near fp16's largest values (x * 2^12), which the matrix-core router splits
     into bf16 head and tail parts."""
-    spec = LayerSpec("ties", T=T, d_model=256, d_ff=64, n_experts=16, top_k=4, act=act, seed=31)
+    # 160 tokens x 512 experts take the matrix-core router, the others the chunk router
+    spec = LayerSpec("ties", T=T, d_model=256, d_ff=64, n_experts=512 if T == 160 else 16, top_k=4, act=act,
+                     seed=31)
     L = inputs.gen_layer(spec)
     w = L["w_router"].copy()
     w[:, 5] = w[:, 2]
