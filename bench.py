@@ -51,14 +51,19 @@ class Hip:
 
     def __init__(self):
         self.lib = ctypes.CDLL("libamdhip64.so")
-        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
+    # Timing-only events: recording one performs no system-scope fence (no
+    # L2 write-back and invalidate between the kernels it separates), so the
+    # kernels run as they do untimed and the bracket adds little of its own.
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
     def event(self):
         e = ctypes.c_void_p()
-        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        assert self.lib.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE) == 0
         return e.value
 
     def elapsed_ms(self, a, b) -> float:
@@ -73,11 +78,32 @@ class Hip:
         self.lib.hipEventDestroy(e)
 
 
+_SLEEP_CYCLES_PER_MS = None
+
+
+def hold_stream(ms: float):
+    """Enqueue a spin kernel of about `ms` milliseconds on torch's current
+    stream, so that the host enqueues the launches that follow before the GPU
+    reaches them: events recorded between those kernels then time them back to
+    back, as a kernel trace does, rather than the host's launch gaps."""
+    global _SLEEP_CYCLES_PER_MS
+    import torch
+    if _SLEEP_CYCLES_PER_MS is None:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        a.record()
+        torch.cuda._sleep(1 << 22)
+        b.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_MS = (1 << 22) / max(a.elapsed_time(b), 1e-3)
+    torch.cuda._sleep(int(min(ms, 1000.0) * _SLEEP_CYCLES_PER_MS))
+
+
 def workload_name(spec, what: str = "forward") -> str:
     w = f"affine {spec.bits}-bit g{spec.group_size}" if spec.quantized else f"dense {spec.act}"
     extra = (", fused gate|up" if spec.gate_up_fused else "") + (
         ", GeGLU (tanh-GELU gate)" if spec.activation == "geglu" else "") + (
-        ", per-op bf16 GLU rounding" if spec.glu_round else "") + (
+        f", per-op {spec.act} GLU rounding" if spec.glu_round else "") + (
         f", {spec.n_shared} shared experts" if spec.n_shared else "") + (
         ", Zipf-skewed router bias" if spec.router_bias == "zipf" else "")
     return (f"{spec.name}: MoE layer {what} T={spec.T} d_model={spec.d_model} d_ff={spec.d_ff} "
@@ -144,7 +170,11 @@ def accounting(spec, touched: int):
               "intermediate_bytes": {"h_written": h_bytes}}
     down = {"bound": "hbm", "bytes": int(w_touched / 3), "flops": 2 * R * D * F,
             "intermediate_bytes": {"h_read": h_bytes, "expert_outputs_written": ys_bytes}}
-    route = {"bound": "hbm", "bytes": router + x_bytes, "flops": 2 * T * D * E}
+    chunks = -(-D // 64)
+    part_bytes = chunks * T * E * 4      # vector-unit router: per-chunk logit partials
+    lt_bytes = 2 * T * E * 4             # matrix-core router: two partial logit arrays
+    route = {"bound": "hbm", "bytes": router + x_bytes, "flops": 2 * T * D * E,
+             "intermediate_bytes": {"router_transposed_written": router, "logit_partials_written": lt_bytes}}
     acc = {
         "layer_bytes": w_touched + router + x_bytes + y_bytes,
         "expert_flops": 2 * R * 3 * D * F,
@@ -153,17 +183,28 @@ def accounting(spec, touched: int):
         "sparse_dense_flop_ratio": (K + S) / (E + S),
         "kernels": {
             # vector-unit router: canonical-order logits (fp32 FMA chains)
-            "route_logits": {"bound": "alu", "flops": 2 * T * D * E, "bytes": router + x_bytes},
-            "route_select": {"bound": "hbm", "bytes": N * 8},
+            "route_logits": {"bound": "alu", "flops": 2 * T * D * E, "bytes": router + x_bytes,
+                             "intermediate_bytes": {"chunk_partials_written": part_bytes}},
+            "route_select": {"bound": "hbm", "bytes": N * 8,
+                             "intermediate_bytes": {"chunk_partials_read": part_bytes}},
             "route_mfma": route,
-            "route_certify": {"bound": "hbm", "bytes": N * 8},
+            # candidates' exact chains re-read x and router rows; the fp16 staging copy of x is written here
+            "route_certify": {"bound": "hbm", "bytes": N * 8,
+                              "intermediate_bytes": {"logit_partials_read": lt_bytes, "x_read": x_bytes,
+                                                     "x16_written": T * D * 2}},
             "dispatch": {"bound": "hbm", "bytes": N * 4 * 4},
-            "route_select_dispatch": {"bound": "hbm", "bytes": N * 8 + N * 4 * 4},
+            "route_select_dispatch": {"bound": "hbm", "bytes": N * 8 + N * 4 * 4,
+                                      "intermediate_bytes": {"chunk_partials_read": part_bytes}},
             "x_f16": {"bound": "hbm", "bytes": 2 * x_bytes},
             "gateup_gemv": gateup, "down_gemv": down,
             "gateup_mfma": gateup, "down_mfma": down,
             "combine": {"bound": "hbm", "bytes": y_bytes + N * 8,
                         "intermediate_bytes": {"expert_outputs_read": ys_bytes}},
+            # one token: selection fused with gate/up, down fused with the combine
+            "select_gateup": {**gateup, "bytes": gateup["bytes"] + N * 8,
+                              "intermediate_bytes": {"chunk_partials_read": part_bytes, "h_written": R * F * 4}},
+            "down_combine": {**down, "bytes": down["bytes"] + y_bytes,
+                             "intermediate_bytes": {"h_read": R * F * 4}},
         },
     }
     return acc
@@ -251,16 +292,22 @@ def run_config(name, steps, warmup, use_graph, hip):
     launch = "graph" if graph_ms is not None and graph_ms < eager_ms else "eager"
     ms = graph_ms if launch == "graph" else eager_ms
 
-    # per-kernel durations on the launch stream: events around every kernel
+    # per-kernel durations on the launch stream: each kernel launched with a
+    # start and a stop event of its own execution (summed per stage), with the
+    # GPU held until the host has enqueued the K steps, so that no kernel
+    # waits on the host
     kernel_ms, names = {}, []
-    evs = [[hip.event() for _ in range(16)] for _ in range(steps)]
+    evs = [[hip.event() for _ in range(32)] for _ in range(steps)]
     torch.cuda.synchronize()
+    hold_stream(2.0 + 2.0 * steps * eager_ms)
     for i in range(steps):
         names = moe.moe_forward_timed(desc, T, xs[i % n_x], weights[i % n_w], y, out_dt, idx, wt, ws,
                                       evs[i], stream)
     torch.cuda.synchronize()
+    assert 0 < len(names) <= 16, names
     for j, nm in enumerate(names):
-        kernel_ms[nm] = sum(hip.elapsed_ms(evs[i][j], evs[i][j + 1]) for i in range(steps)) / steps
+        kernel_ms[nm] = kernel_ms.get(nm, 0.0) + sum(
+            hip.elapsed_ms(evs[i][2 * j], evs[i][2 * j + 1]) for i in range(steps)) / steps
     for row in evs:
         for e in row:
             hip.destroy(e)
@@ -345,13 +392,19 @@ def run_backward(name, steps, warmup, hip):
     torch.cuda.synchronize()
     e0, e1 = hip.event(), hip.event()
     ta = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    tb = time.perf_counter()
+    ms = (tb - ta) * 1000.0 / steps
+    # GPU time per pass: the same K passes again between two events, with the
+    # GPU held until the host has enqueued them
+    hold_stream(2.0 + 2.0 * steps * ms)
     hip.record(e0, stream.cuda_stream)
     for i in range(steps):
         step(i)
     hip.record(e1, stream.cuda_stream)
     torch.cuda.synchronize()
-    tb = time.perf_counter()
-    ms = (tb - ta) * 1000.0 / steps
     ev_ms = hip.elapsed_ms(e0, e1) / steps
     hip.destroy(e0)
     hip.destroy(e1)
@@ -378,7 +431,7 @@ def run_backward(name, steps, warmup, hip):
     entry = {
         "workload": workload_name(spec, "backward (dx)"), "value": round(rows / (ms / 1e3), 1),
         "unit": "routed rows/s", "tokens_per_s": round(T / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
-        "roofline": {"kernel": "whole backward pass", **roof, "traffic": None,
+        "roofline": {"kernel": "whole backward pass", **roof, "traffic": measured_traffic(f"bwd_{name}", "backward"),
                      "avg_pass_us": round(ev_ms * 1e3, 2), "algorithmic_flops": acc["flops"],
                      "algorithmic_bytes": acc["bytes"], "flop_frac": round(tflops / fpeak, 4),
                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
@@ -405,7 +458,10 @@ STAGE_SOURCES = {
     "route_logits": "route.hip", "route_select": "route.hip", "route_mfma": "route_mfma.hip",
     "route_certify": "route_mfma.hip", "route_select_dispatch": "route.hip", "dispatch": "dispatch.hip", "x_f16": "ffn_mfma.hip", "gateup_gemv": "ffn_gemv.hip",
     "down_gemv": "ffn_gemv.hip", "gateup_mfma": "ffn_mfma.hip", "down_mfma": "ffn_mfma.hip",
-    "combine": "combine.hip",
+    "combine": "combine.hip", "select_gateup": "decode_fused.hip", "down_combine": "decode_fused.hip",
+    # the whole backward pass: routing and dispatch recomputed, then the gradient kernels
+    "backward": ("backward.hip", "backward_mfma.hip", "route.hip", "route_mfma.hip", "dispatch.hip",
+                 "ffn_mfma.hip"),
 }
 
 
@@ -417,7 +473,8 @@ def kernel_sources_digest(kernel: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_mixture_experts_amd", "csrc")
     headers = sorted(os.path.basename(p) for p in glob.glob(os.path.join(csrc, "*.h")))
-    for f in [STAGE_SOURCES[kernel]] + headers:
+    src = STAGE_SOURCES[kernel]
+    for f in (list(src) if isinstance(src, tuple) else [src]) + headers:
         with open(os.path.join(ROOT, "sparse_mixture_experts_amd", "csrc", f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()

@@ -201,12 +201,16 @@ int moe_forward(const moe_layer_desc *desc, int32_t T, const void *x,
                 size_t ws_bytes, void *stream);
 
 /*
- * moe_forward for profiling: the same work, plus a stream event recorded
- * before the first kernel (events[0]) and after each kernel i (events[i+1]),
- * for as many as n_events events (hipEvent_t handles created by the caller).
- * names (nullable, names_len bytes) receives the comma-separated kernel names
- * in launch order, truncated to fit.  Kernel durations are the elapsed times
- * between consecutive events.
+ * moe_forward for profiling: the same work, with kernel i of the call (in
+ * launch order) launched through hipExtLaunchKernel with events[2i] and
+ * events[2i+1] as its start and stop events, for as many kernels as
+ * n_events / 2 covers (hipEvent_t handles created by the caller; kernels past
+ * them launch plainly).  The elapsed time between a kernel's two events is
+ * that kernel's own execution, with no launch gap inside.  names (nullable,
+ * names_len bytes) receives one comma-separated stage name per kernel, in
+ * launch order, truncated to fit (a stage such as "dispatch" or "route_mfma"
+ * may run two kernels).  Only the calling host thread's launches inside this
+ * call are affected.
  */
 int moe_forward_timed(const moe_layer_desc *desc, int32_t T, const void *x,
                       const moe_weights *w, void *y, int32_t out_dtype,

@@ -12,6 +12,7 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "launch.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -149,7 +150,7 @@ void launch_combine(const moe_layer_desc *d, int32_t T, const void *y_sorted, co
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(T, (D + kThreads * kCols - 1) / (kThreads * kCols));
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, y_sorted, ys_sh, inv_order, topk_w, T, d->top_k,
+    launch(kern, grid, dim3(kThreads), 0, s, y_sorted, ys_sh, inv_order, topk_w, T, d->top_k,
                        d->n_shared, N, D, parts, part_rows, y);
   };
   const int K = d->top_k;

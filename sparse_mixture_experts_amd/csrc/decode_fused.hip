@@ -31,6 +31,7 @@
 #include "dequant_f16.h"
 #include "device_common.h"
 #include "f16_stage.h"
+#include "launch.h"
 #include "moe_internal.h"
 #include "select_token.h"
 
@@ -127,7 +128,11 @@ __global__ __launch_bounds__(256) void t1_gateup_kernel(T1Args a) {
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
   const int lr = lane & 15, lg = lane >> 4;
-  const int slot = blockIdx.y, cb = blockIdx.x;
+  // one XCD per range of consecutive (slot, column block) pairs: the 8 column
+  // blocks whose scales and biases share a cache line share an L2
+  const int nx = gridDim.x;
+  const int item = xcd_contiguous(blockIdx.y * nx + blockIdx.x, nx * gridDim.y);
+  const int slot = item / nx, cb = item % nx;
   const int D = a.D, F = a.F, nslab = (D + kSlab - 1) / kSlab;
 
   // the token's experts (wave 0) and the fp16 staging row of x (wave 1)
@@ -234,7 +239,8 @@ __global__ __launch_bounds__(512) void t1_down_combine_kernel(T1Args a) {
   const int lr = lane & 15, lg = lane >> 4;
   const int D = a.D, F = a.F, nslab = (F + kSlab - 1) / kSlab, FR = nslab * kSlab;
   const int R = a.K + a.S;
-  const int c0 = blockIdx.x * 16;
+  // consecutive 16-column blocks (whose scales share cache lines) on one XCD
+  const int c0 = xcd_contiguous(blockIdx.x, gridDim.x) * 16;
 
   // weights of this wave's first slot, issued before the h rows are staged
   auto slot_expert = [&](int j) { return j < a.K ? a.idx[j] : a.E + (j - a.K); };
@@ -343,11 +349,11 @@ void launch_t1_qb(const T1Args &a, hipStream_t s) {
   const dim3 g1(a.F / 8, a.K + a.S);
   auto gu = [&](auto msw) {
     constexpr int MSW = decltype(msw)::value;
-    if (a.E <= 64) hipLaunchKernelGGL((t1_gateup_kernel<QB, MSW, 1>), g1, dim3(256), 0, s, a);
-    else if (a.E <= 128) hipLaunchKernelGGL((t1_gateup_kernel<QB, MSW, 2>), g1, dim3(256), 0, s, a);
-    else if (a.E <= 256) hipLaunchKernelGGL((t1_gateup_kernel<QB, MSW, 4>), g1, dim3(256), 0, s, a);
-    else if (a.E <= 512) hipLaunchKernelGGL((t1_gateup_kernel<QB, MSW, 8>), g1, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((t1_gateup_kernel<QB, MSW, 16>), g1, dim3(256), 0, s, a);
+    if (a.E <= 64) launch((t1_gateup_kernel<QB, MSW, 1>), g1, dim3(256), 0, s, a);
+    else if (a.E <= 128) launch((t1_gateup_kernel<QB, MSW, 2>), g1, dim3(256), 0, s, a);
+    else if (a.E <= 256) launch((t1_gateup_kernel<QB, MSW, 4>), g1, dim3(256), 0, s, a);
+    else if (a.E <= 512) launch((t1_gateup_kernel<QB, MSW, 8>), g1, dim3(256), 0, s, a);
+    else launch((t1_gateup_kernel<QB, MSW, 16>), g1, dim3(256), 0, s, a);
   };
   if (nsw <= 4) gu(std::integral_constant<int, 4>{});
   else gu(std::integral_constant<int, 8>{});
@@ -358,8 +364,8 @@ void launch_t1_down(const T1Args &a, hipStream_t s) {
   const int nslab = (a.F + kSlab - 1) / kSlab;
   const size_t lds = size_t(a.K + a.S) * nslab * kSlab * sizeof(uint16_t);
   const dim3 g2(a.D / 16);
-  if (QB == 8 || nslab <= 8) hipLaunchKernelGGL((t1_down_combine_kernel<QB, 8>), g2, dim3(512), lds, s, a);
-  else hipLaunchKernelGGL((t1_down_combine_kernel<QB, QB == 8 ? 8 : 16>), g2, dim3(512), lds, s, a);
+  if (QB == 8 || nslab <= 8) launch((t1_down_combine_kernel<QB, 8>), g2, dim3(512), lds, s, a);
+  else launch((t1_down_combine_kernel<QB, QB == 8 ? 8 : 16>), g2, dim3(512), lds, s, a);
 }
 
 }  // namespace

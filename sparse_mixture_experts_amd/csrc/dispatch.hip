@@ -23,6 +23,7 @@
 
 #include "device_common.h"
 #include "dispatch_tiny.h"
+#include "launch.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -490,7 +491,7 @@ void launch_dispatch(const moe_layer_desc *d, int32_t T, const int32_t *idx, int
   const int E = d->n_experts, N = T * d->top_k;
   if (N <= kTinyMaxN) {
     auto tiny = [&](auto kern) {
-      hipLaunchKernelGGL(kern, dim3(1), dim3(kWave), 0, s, idx, N, d->top_k, E, d->n_shared, T, tile_rows, tr, order,
+      launch(kern, dim3(1), dim3(kWave), 0, s, idx, N, d->top_k, E, d->n_shared, T, tile_rows, tr, order,
                          inv_order, row_map, expert_off, tile_off, counters, act_items, tiles);
     };
     if (N <= 2 * kWave) tiny(dispatch_tiny_kernel<2>);
@@ -499,17 +500,17 @@ void launch_dispatch(const moe_layer_desc *d, int32_t T, const int32_t *idx, int
   } else if (N <= kSingleBlockMax) {
     const int nw = kThreads / 64;
     const size_t lds = size_t(nw * E + 5 * E) * sizeof(int32_t);
-    hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kThreads), lds, s, idx, N, d->top_k, E, d->n_shared, T,
+    launch(dispatch_kernel, dim3(1), dim3(kThreads), lds, s, idx, N, d->top_k, E, d->n_shared, T,
                        tile_rows, tr, order, inv_order, row_map, expert_off, tile_off, counters, act_items, tiles);
   } else {
     // Scattered writes of order and row_map are spread over many CUs.
     const int seg = int(dispatch_segment(N));
     const int B = (N + seg - 1) / seg;
     const size_t lds_w = size_t(kMbWaves) * E * sizeof(int32_t);
-    hipLaunchKernelGGL(dispatch_count_kernel, dim3(B), dim3(kMbThreads), lds_w, s, idx, N, E, seg, scratch);
+    launch(dispatch_count_kernel, dim3(B), dim3(kMbThreads), lds_w, s, idx, N, E, seg, scratch);
     // B ranking workgroups and one planning workgroup
     auto rank = [&](auto kern) {
-      hipLaunchKernelGGL(kern, dim3(B + 1), dim3(kMbThreads), lds_w + size_t(5 * E) * sizeof(int32_t), s, idx, N,
+      launch(kern, dim3(B + 1), dim3(kMbThreads), lds_w + size_t(5 * E) * sizeof(int32_t), s, idx, N,
                          d->top_k, E, d->n_shared, T, seg, B, tile_rows, tr, scratch, order, inv_order, row_map,
                          expert_off, tile_off, counters, act_items, tiles);
     };
@@ -525,7 +526,7 @@ void launch_plan(const moe_layer_desc *d, int32_t T, const int32_t *expert_off, 
   const int E = d->n_experts;
   const int tr = plan_tile_rows(d, T);
   const size_t lds = size_t(4 * E) * sizeof(int32_t);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), lds, static_cast<hipStream_t>(stream),
+  launch(plan_kernel, dim3(1), dim3(kThreads), lds, static_cast<hipStream_t>(stream),
                      expert_off, T * d->top_k, E, d->n_shared, T, tr, counters, act_items, tiles);
 }
 

@@ -18,6 +18,7 @@
 // bytes of a weight row per step), dequantises once, and applies the piece to
 // all staged rows; a butterfly sum finishes each dot product.
 #include "device_common.h"
+#include "launch.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -219,12 +220,12 @@ void launch_gemv(const moe_layer_desc *d, int32_t T, const void *x, const int32_
                 static_cast<const uint16_t *>(pg.biases), w->up.w,
                 static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases),
                 counters, items, h};
-  hipLaunchKernelGGL((gateup_gemv_kernel<DT>), dim3((F + kNB - 1) / kNB, max_items),
+  launch((gateup_gemv_kernel<DT>), dim3((F + kNB - 1) / kNB, max_items),
                      dim3(kThreads), size_t(ga.MR) * D * esz, s, ga);
   if (mk) mk->mark("gateup_gemv");
   DownArgs da{h, D, F, rows_per_pass(F, esz), w->down.w, static_cast<const uint16_t *>(w->down.scales),
               static_cast<const uint16_t *>(w->down.biases), counters, items, y};
-  hipLaunchKernelGGL((down_gemv_kernel<DT>), dim3((D + kNB - 1) / kNB, max_items),
+  launch((down_gemv_kernel<DT>), dim3((D + kNB - 1) / kNB, max_items),
                      dim3(kThreads), size_t(da.MR) * F * esz, s, da);
   if (mk) mk->mark("down_gemv");
 }

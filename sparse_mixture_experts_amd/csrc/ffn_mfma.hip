@@ -47,6 +47,7 @@
 #include "device_common.h"
 #include "dequant_f16.h"
 #include "f16_stage.h"
+#include "launch.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -96,6 +97,18 @@ struct GemmArgs {
   int kz;                   // down: reduction parts (fp32 partial rows at out + z * part_stride), else 1
   int64_t part_stride;
 };
+
+// Column blocks per group of the work order (item_tile_block): whole rows of
+// blocks (tile-major) when every expert has about one tile; groups of
+// kColGroup blocks when the plan finds experts with several tiles (the skewed
+// 256-token layer: down read 1.84x its bytes tile-major, 1.18x in groups);
+// single blocks (column-block-major: every tile for one block of columns,
+// then the next) when the host's layer shape gives every expert two or more
+// tiles (the dense 512-token layer: gate/up read 1.22x its bytes this way,
+// 1.48x in groups of 8).
+__device__ __forceinline__ int col_group(const GemmArgs &a, int nbx) {
+  return a.bx_major ? 1 : a.counters[2] ? min(nbx, kColGroup) : nbx;
+}
 
 // GPS: groups per slab (128 / group size; 1 for dense weights).
 template <int RB, int GPS>
@@ -174,12 +187,13 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
   if (item >= work) return;
   // reduction part (outermost), then the tile and column block.  Tile-major
   // order puts the column blocks of a tile next to each other (they stage
-  // the same activation rows); column-block-major order puts the tiles of one
-  // expert next to each other (they read the same weights).
+  // the same activation rows); with experts of several tiles, groups of 8
+  // column blocks also put the tiles of one expert together (they read the
+  // same weights).
   const int z = item / (n_tiles * nbx);
   item -= z * n_tiles * nbx;
-  const bool bxm = a.bx_major | a.counters[2];  // host layer shape, or the plan's multi-tile experts
-  const int tile_id = bxm ? item % n_tiles : item / nbx, bx = bxm ? item / n_tiles : item % nbx;
+  int tile_id, bx;
+  item_tile_block(item, n_tiles, nbx, col_group(a, nbx), tile_id, bx);
   const PlanItem tile = a.tiles[tile_id];
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
@@ -688,8 +702,8 @@ __device__ __forceinline__ void down_resident_body(const GemmArgs &a, int cbpw) 
     item = (lin % 8) * per + slot;
   }
   if (item >= work) return;
-  const bool bxm = a.bx_major | a.counters[2];  // the tiles of one expert back to back per column group
-  const int tile_id = bxm ? item % n_tiles : item / nbx, grp = bxm ? item / n_tiles : item % nbx;
+  int tile_id, grp;
+  item_tile_block(item, n_tiles, nbx, col_group(a, nbx), tile_id, grp);
   PlanItem tile = a.tiles[tile_id];
   tile.expert = __builtin_amdgcn_readfirstlane(tile.expert);
   tile.row0 = __builtin_amdgcn_readfirstlane(tile.row0);
@@ -1133,8 +1147,8 @@ void launch_one(const GemmArgs &ga, int64_t max_tiles, hipStream_t s) {
   const dim3 grid((ga.n_out + cols_per_block - 1) / cols_per_block, unsigned(max_tiles), unsigned(ga.kz));
   // 16-row tiles fit two or more waves per SIMD by themselves.
   constexpr bool kFits = RB == 1;
-  if constexpr (kFits) hipLaunchKernelGGL((grouped_gemm_kernel<MODE, QB, RB, GPS>), grid, dim3(kThreads), 0, s, ga);
-  else hipLaunchKernelGGL((grouped_gemm_kernel_w2<MODE, QB, RB, GPS>), grid, dim3(kThreads), 0, s, ga);
+  if constexpr (kFits) launch((grouped_gemm_kernel<MODE, QB, RB, GPS>), grid, dim3(kThreads), 0, s, ga);
+  else launch((grouped_gemm_kernel_w2<MODE, QB, RB, GPS>), grid, dim3(kThreads), 0, s, ga);
 }
 // Code width (0: dense bf16) and groups per slab picked at run time.
 template <int MODE, int RB, int QB>
@@ -1173,7 +1187,7 @@ void launch_down_resident(const GemmArgs &ga, int gsize, int64_t max_tiles, int6
       }();
       (void)raised;
     }
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, ga, cbpw);
+    launch(kern, grid, dim3(kThreads), lds, s, ga, cbpw);
   };
   if constexpr (RB == 1) {
     if (gsize == 32) go(down_resident_kernel<QB, RB, 4>);
@@ -1201,7 +1215,7 @@ void launch_decode_ms(const DecArgs &da, int64_t max_tiles, hipStream_t s) {
     (void)raised;
   }
   const dim3 grid((da.n_out + cols_per_block - 1) / cols_per_block, unsigned(max_tiles));
-  hipLaunchKernelGGL((decode_gemm_kernel<GATEUP, QB, MS>), grid, dim3(kThreads), lds, s, da);
+  launch((decode_gemm_kernel<GATEUP, QB, MS>), grid, dim3(kThreads), lds, s, da);
 }
 // K <= 1024: 8 slabs of registers; K <= 2048: 16.
 template <bool GATEUP>
@@ -1225,8 +1239,9 @@ bool use_mfma(const moe_layer_desc *d) {
   return d->act_dtype != MOE_DT_F32 && d->d_model % 64 == 0 && d->d_ff % 64 == 0;
 }
 
-// Experts with two or more row tiles on average: their tiles run next to
-// each other for each column block, so the second reads the weights from L2.
+// Experts with two or more row tiles on average: the work runs in groups of
+// 8 column blocks with an expert's tiles together, so all but the first tile
+// read the weights from L2.
 static int use_bx_major(const moe_layer_desc *d, int32_t T) {
   const int64_t rows_per_expert = int64_t(T) * d->top_k / d->n_experts;
   return rows_per_expert >= 2 * plan_tile_rows(d, T) ? 1 : 0;
@@ -1291,7 +1306,7 @@ void launch_gate_up_raw_mfma(const moe_layer_desc *d, int32_t T, const void *x, 
   const bool f16 = d->act_dtype == MOE_DT_F16;
   const int qb = d->w_format == MOE_WF_AFFINE_Q8 ? 8 : aff ? 4 : f16 ? kDenseF16 : kDenseBF16;
   if (aff && !sc.x16_ready)
-    hipLaunchKernelGGL(act_f16_kernel, dim3((T + 3) / 4), dim3(256), 0, s, static_cast<const uint16_t *>(x), T,
+    launch(act_f16_kernel, dim3((T + 3) / 4), dim3(256), 0, s, static_cast<const uint16_t *>(x), T,
                        d->d_model, static_cast<uint16_t *>(sc.x16), sc.xsh, int(f16));
   const moe_proj &pg = d->gate_up_fused ? w->gate_up : w->gate;
   GemmArgs g{aff ? sc.x16 : x, sc.xsh, nullptr, 0, row_map, T, T * d->top_k, d->d_model, d->d_ff,
@@ -1317,7 +1332,7 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
   const int nblk = (d->d_ff + kHBlock - 1) / kHBlock;
   const int bx_major = use_bx_major(d, T);
   if (aff && !sc.x16_ready) {
-    hipLaunchKernelGGL(act_f16_kernel, dim3((T + 3) / 4), dim3(256), 0, s, static_cast<const uint16_t *>(x), T,
+    launch(act_f16_kernel, dim3((T + 3) / 4), dim3(256), 0, s, static_cast<const uint16_t *>(x), T,
                        d->d_model, static_cast<uint16_t *>(sc.x16), sc.xsh, int(f16));
     if (mk) mk->mark("x_f16");
   }

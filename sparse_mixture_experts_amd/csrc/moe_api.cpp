@@ -7,9 +7,17 @@
 // entry point here only enqueues.
 #include <hip/hip_runtime.h>
 
+#include "launch.h"
 #include "moe_internal.h"
 
 using namespace moe;
+
+namespace moe {
+KernelTimer *&kernel_timer() {
+  static thread_local KernelTimer *t = nullptr;
+  return t;
+}
+}  // namespace moe
 
 namespace {
 
@@ -175,22 +183,35 @@ int moe_forward(const moe_layer_desc *desc, int32_t T, const void *x, const moe_
 }
 
 namespace {
-// Records events[0] before the first kernel and events[i] after kernel i, and
-// collects the kernel names.
-struct EventMarker : StageMarker {
+// Hands each kernel of the call a (start, stop) event pair and names every
+// kernel after the stage it belongs to.
+struct EventMarker : StageMarker, KernelTimer {
   void *const *events;
-  int32_t n_events, used = 0;
-  hipStream_t stream;
+  int32_t n_events, kernels = 0, named = 0;
   char *names;
   size_t names_len, pos = 0;
-  void mark(const char *stage) override {
-    if (used < n_events) (void)hipEventRecord(static_cast<hipEvent_t>(events[used]), stream);
-    ++used;
-    if (!stage || !names || names_len == 0) return;
-    for (const char *p = (pos ? "," : ""); *p && pos + 1 < names_len; ++p) names[pos++] = *p;
-    for (const char *p = stage; *p && pos + 1 < names_len; ++p) names[pos++] = *p;
-    names[pos] = 0;
+  bool next_events(hipEvent_t *start, hipEvent_t *stop) override {
+    const int32_t k = kernels++;
+    if (2 * k + 1 >= n_events) return false;
+    *start = static_cast<hipEvent_t>(events[2 * k]);
+    *stop = static_cast<hipEvent_t>(events[2 * k + 1]);
+    return true;
   }
+  void mark(const char *stage) override {
+    for (; named < kernels; ++named) {
+      if (!stage || !names || names_len == 0) continue;
+      for (const char *p = (pos ? "," : ""); *p && pos + 1 < names_len; ++p) names[pos++] = *p;
+      for (const char *p = stage; *p && pos + 1 < names_len; ++p) names[pos++] = *p;
+      names[pos] = 0;
+    }
+  }
+};
+
+// Installs a kernel timer on this thread for one scope.
+struct TimerScope {
+  KernelTimer *saved;
+  explicit TimerScope(KernelTimer *t) : saved(kernel_timer()) { kernel_timer() = t; }
+  ~TimerScope() { kernel_timer() = saved; }
 };
 }  // namespace
 
@@ -203,9 +224,9 @@ int moe_forward_timed(const moe_layer_desc *desc, int32_t T, const void *x, cons
   EventMarker mk;
   mk.events = events;
   mk.n_events = n_events;
-  mk.stream = static_cast<hipStream_t>(stream);
   mk.names = names;
   mk.names_len = names_len;
+  TimerScope scope(&mk);
   return forward_impl(desc, T, x, w, y, out_dtype, topk_idx_out, topk_w_out, ws, ws_bytes, stream, &mk);
 }
 

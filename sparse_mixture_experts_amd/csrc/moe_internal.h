@@ -17,10 +17,39 @@ struct PlanItem {
 
 // Work-plan counters (int32 in the workspace): [0] active items, [1] row
 // tiles, [2] 1 when at least a quarter of the tiles belong to experts (or
-// shared experts) with two or more tiles: the grouped GEMMs then run the
-// tiles of one expert back to back for each column block, so its weights are
-// read from L2 by all but the first.
+// shared experts) with two or more tiles: the grouped GEMMs then order their
+// work in column groups (below), so the tiles of one expert read its weights
+// together and all but the first find them in L2.
 __host__ __device__ inline int plan_multi_tile(int multi_tiles, int tiles) { return 4 * multi_tiles >= tiles ? 1 : 0; }
+
+// Workgroups go to the 8 XCDs round-robin by linear id.  This maps linear
+// id `lin` of `total` to a work index such that each XCD takes one
+// contiguous range of work indices (ranges differ in length by at most one):
+// neighbouring work that shares cache lines then shares an L2.  A bijection
+// on [0, total).
+__host__ __device__ inline int xcd_contiguous(int lin, int total) {
+  const int xcd = lin & 7, base = total >> 3, rem = total & 7;
+  return xcd * base + (xcd < rem ? xcd : rem) + (lin >> 3);
+}
+
+// Columns blocks per group in that order.
+constexpr int kColGroup = 8;
+
+// Work item -> (row tile, column block) of a grouped GEMM with n_tiles tiles
+// and nbx column blocks, in groups of gc column blocks (the last group may be
+// narrower): item = ((group * n_tiles) + tile) * width + block in group.
+// The workgroups that an XCD runs at once take consecutive items, so they
+// cover every tile of a few experts for the same gc column blocks (the
+// tiles of an expert read the same weights, the blocks of a tile stage the
+// same activation rows).  gc = nbx is plain tile-major order.  Every item
+// below n_tiles * nbx maps to a distinct (tile, block).
+__host__ __device__ inline void item_tile_block(int item, int n_tiles, int nbx, int gc, int &tile, int &bx) {
+  const int span = n_tiles * gc, full = nbx / gc, g = item / span;
+  const int width = g < full ? gc : nbx - full * gc;
+  const int r = item - g * span;
+  tile = r / width;
+  bx = g * gc + r % width;
+}
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;

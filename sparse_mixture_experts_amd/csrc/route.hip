@@ -28,6 +28,7 @@
 #include "device_common.h"
 #include "dispatch_tiny.h"
 #include "f16_stage.h"
+#include "launch.h"
 #include "moe_internal.h"
 #include "select_token.h"
 
@@ -227,7 +228,7 @@ void launch_select(const float *in, int n_chunks, const float *bias, int T, int 
   const uint16_t *xb = static_cast<const uint16_t *>(x);
   uint16_t *xo = static_cast<uint16_t *>(x16);
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, block, 0, s, in, n_chunks, bias, T, E, K, renorm, idx, w, xb, D, xo, xsh,
+    launch(kern, grid, block, 0, s, in, n_chunks, bias, T, E, K, renorm, idx, w, xb, D, xo, xsh,
                        int(x_f16), dsp);
   };
   if (E <= 64) go(route_select_kernel<1>);
@@ -255,7 +256,7 @@ bool launch_partials(const void *x, const void *wr, const float *bias, int T, in
     }();
     (void)raised;
   }
-  hipLaunchKernelGGL((route_partials_kernel<DT, TT, CPB>), grid, dim3(kThreads), lds, s, x, wr, bias, T, D,
+  launch((route_partials_kernel<DT, TT, CPB>), grid, dim3(kThreads), lds, s, x, wr, bias, T, D,
                      E, full, out);
   return full;
 }
@@ -286,11 +287,11 @@ int launch_route_chunks_t1(const moe_layer_desc *d, const void *x, const void *w
   const int D = d->d_model, E = d->n_experts, C = (D + kChunk - 1) / kChunk;
   const dim3 grid((E + kWave - 1) / kWave, C, 1);
   if (d->act_dtype == MOE_DT_BF16)
-    hipLaunchKernelGGL((route_chunk_kernel<kDtBF16, 1>), grid, dim3(kWave), 0, s, x, w_router, 1, D, E, partials);
+    launch((route_chunk_kernel<kDtBF16, 1>), grid, dim3(kWave), 0, s, x, w_router, 1, D, E, partials);
   else if (d->act_dtype == MOE_DT_F16)
-    hipLaunchKernelGGL((route_chunk_kernel<kDtF16, 1>), grid, dim3(kWave), 0, s, x, w_router, 1, D, E, partials);
+    launch((route_chunk_kernel<kDtF16, 1>), grid, dim3(kWave), 0, s, x, w_router, 1, D, E, partials);
   else
-    hipLaunchKernelGGL((route_chunk_kernel<kDtF32, 1>), grid, dim3(kWave), 0, s, x, w_router, 1, D, E, partials);
+    launch((route_chunk_kernel<kDtF32, 1>), grid, dim3(kWave), 0, s, x, w_router, 1, D, E, partials);
   if (mk) mk->mark("route_logits");
   return C;
 }
@@ -319,10 +320,10 @@ void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void 
     if (T == 1) {
       // one token: one chain per lane (no idle token slots)
       const dim3 grid((E + kWave - 1) / kWave, C, 1);
-      hipLaunchKernelGGL((route_chunk_kernel<DT, 1>), grid, dim3(kWave), 0, s, x, w_router, T, D, E, scratch);
+      launch((route_chunk_kernel<DT, 1>), grid, dim3(kWave), 0, s, x, w_router, T, D, E, scratch);
     } else if (T <= kChunkRouterMaxT) {
       const dim3 grid((E + kWave - 1) / kWave, C, (T + 7) / 8);
-      hipLaunchKernelGGL((route_chunk_kernel<DT, 8>), grid, dim3(kWave), 0, s, x, w_router, T, D, E, scratch);
+      launch((route_chunk_kernel<DT, 8>), grid, dim3(kWave), 0, s, x, w_router, T, D, E, scratch);
     } else if (C <= 32) {
       launch_partials<DT, 8, 32>(x, w_router, bias, T, D, E, scratch, s);
       n_chunks = 0;

@@ -28,6 +28,7 @@
 // Architecture": router matmul, softmax and top-K all on the GPU.)
 #include "device_common.h"
 #include "f16_stage.h"
+#include "launch.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -506,9 +507,9 @@ void launch_route_mfma_t(const moe_layer_desc *d, int32_t T, const void *x, cons
   const int64_t o_wt = align4(nz * int64_t(T) * E), o_np = o_wt + align4((int64_t(E) * D + 1) / 2);
   uint16_t *wt = reinterpret_cast<uint16_t *>(scratch + o_wt);
   float *normp = scratch + o_np;
-  hipLaunchKernelGGL(router_transpose_kernel<DT>, dim3((E + 63) / 64, nkb), dim3(kThreads), 0, s,
+  launch(router_transpose_kernel<DT>, dim3((E + 63) / 64, nkb), dim3(kThreads), 0, s,
                      static_cast<const uint16_t *>(w_router), D, E, wt, normp);
-  hipLaunchKernelGGL(router_mfma_kernel<DT>, dim3((E + 63) / 64, (T + 63) / 64, nz), dim3(kMfThreads), 0, s,
+  launch(router_mfma_kernel<DT>, dim3((E + 63) / 64, (T + 63) / 64, nz), dim3(kMfThreads), 0, s,
                      static_cast<const uint16_t *>(x), wt, bias, normp, nkb, T, D, E, lt);
   if (mk) mk->mark("route_mfma");
   // |L~ - L| <= gamma * S: the MFMAs of a chunk counted as 32 sequential
@@ -520,11 +521,11 @@ void launch_route_mfma_t(const moe_layer_desc *d, int32_t T, const void *x, cons
   CertArgs ca{static_cast<const uint16_t *>(x), wt, bias, lt, normp + int64_t(nkb) * E, T, D, E, d->top_k, nz,
               gamma, idx, w, static_cast<uint16_t *>(x16), xsh};
   const dim3 grid((T + kThreads / kWave - 1) / (kThreads / kWave)), block(kThreads);
-  if (E <= 64) hipLaunchKernelGGL((router_certify_kernel<1, DT>), grid, block, 0, s, ca);
-  else if (E <= 128) hipLaunchKernelGGL((router_certify_kernel<2, DT>), grid, block, 0, s, ca);
-  else if (E <= 256) hipLaunchKernelGGL((router_certify_kernel<4, DT>), grid, block, 0, s, ca);
-  else if (E <= 512) hipLaunchKernelGGL((router_certify_kernel<8, DT>), grid, block, 0, s, ca);
-  else hipLaunchKernelGGL((router_certify_kernel<16, DT>), grid, block, 0, s, ca);
+  if (E <= 64) launch((router_certify_kernel<1, DT>), grid, block, 0, s, ca);
+  else if (E <= 128) launch((router_certify_kernel<2, DT>), grid, block, 0, s, ca);
+  else if (E <= 256) launch((router_certify_kernel<4, DT>), grid, block, 0, s, ca);
+  else if (E <= 512) launch((router_certify_kernel<8, DT>), grid, block, 0, s, ca);
+  else launch((router_certify_kernel<16, DT>), grid, block, 0, s, ca);
   if (mk) mk->mark("route_certify");
 }
 

@@ -179,8 +179,9 @@ def moe_forward_noalloc(desc, T, x, weights, y, out_dtype, topk_idx_out, topk_w_
 
 
 def moe_forward_timed(desc, T, x, weights, y, out_dtype, topk_idx_out, topk_w_out, ws, events, stream=None):
-    """moe_forward recording `events` (raw hipEvent_t handles) around each kernel;
-    returns the kernel names in launch order."""
+    """moe_forward with kernel i launched between events[2i] and events[2i+1]
+    (raw hipEvent_t handles: its start and its end); returns one stage name
+    per kernel, in launch order."""
     arr = (ctypes.c_void_p * len(events))(*events)
     names = ctypes.create_string_buffer(512)
     _check(load().moe_forward_timed(ctypes.byref(desc), T, _ptr(x), ctypes.byref(weights.c), _ptr(y), out_dtype,
