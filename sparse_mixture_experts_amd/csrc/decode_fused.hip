@@ -23,9 +23,14 @@
 //      runs the down rows of its slots (all slots in flight at once) and
 //      scales them by the slot weight; the waves' sums are added in wave
 //      order and y is written in the output dtype.
-// Expert weights are expanded to fp16 in registers as on the other matrix-
-// core kernels (dequant_f16.h) with a power-of-two exponent per weight row
-// and wave, undone before any sum across waves.
+// At one token the matrix cores would multiply 16 rows for one: both kernels
+// are dequant-GEMVs instead (slab_dot): code pairs under the fp16 exponent
+// of 1024 meet activation pairs in v_dot2_f32_f16, the affine scale and bias
+// are applied per slab in fp32, and the row's four lanes are summed with
+// cross-lane swaps.  (Measured against the same kernels on 16x16x32 MFMA
+// slabs, 4-bit codes: selection + gate/up 10.4 -> 10.2 us, down + combine
+// 10.6 -> 9.7 us; the one-token layer 23.7 -> 22.6 us, and 28.6 -> 26.3 us
+// with 8-bit codes.)
 #include <hip/hip_runtime.h>
 
 #include "dequant_f16.h"
@@ -87,28 +92,52 @@ __device__ __forceinline__ void load_row_slab(const uint32_t *wrow, const uint16
   br = ok ? bv : uint16_t(0);
 }
 
-// One slab's four MFMA steps: operand A = 16 weight rows expanded to fp16
-// (this lane's row, 32 elements), operand B = the activation row (the same
-// 8 values for every column, from LDS in the staging order).
+// Dequant-GEMV of one slab: this lane's 32 codes of its weight row against
+// the 32 staged activations (staging order e0,e4,e1,e5,e2,e6,e3,e7 in every
+// block of 8).  Each code pair goes under the fp16 exponent of 1024 (1024 + q
+// exact, or 1024 + 16q for the 4-bit codes in bits 4-7 of a byte) and meets
+// its activation pair in v_dot2_f32_f16; returns sum q*x in `qx` and sum x in
+// `sx`, so that the slab's share of the row's dot product is s*qx + b*sx
+// with the group's scale and bias in fp32.
 template <int QB>
-__device__ __forceinline__ f32x4 slab_mfma(const uint4 (&wq)[QB / 4], h2 s2, h2 b2, const uint16_t *act, int lg,
-                                           uint32_t magic, f32x4 acc) {
-  const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const h2 s2_16 = s2 * sixteenth;
+__device__ __forceinline__ void slab_dot(const uint4 (&wq)[QB / 4], const uint16_t *act, uint32_t magic, float &qx,
+                                         float &sx) {
+  const h2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+  float a1 = 0.f, a16 = 0.f, s1 = 0.f, s16 = 0.f;  // code pairs taken as 1024 + q / 1024 + 16q, and their x sums
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const f16x8 bx = *reinterpret_cast<const f16x8 *>(act + lg * 32 + j * 8);
-    f16x8 aw;
+    const uint4 xv = *reinterpret_cast<const uint4 *>(act + j * 8);
+    const h2 X0 = __builtin_bit_cast(h2, xv.x), X1 = __builtin_bit_cast(h2, xv.y);
+    const h2 X2 = __builtin_bit_cast(h2, xv.z), X3 = __builtin_bit_cast(h2, xv.w);
     if constexpr (QB == 4) {
-      const uint4 &q = wq[0];
-      aw = q4_word_to_f16(j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w, s2, s2_16, b2, magic);
+      const uint32_t w = j == 0 ? wq[0].x : j == 1 ? wq[0].y : j == 2 ? wq[0].z : wq[0].w;
+      const uint32_t w8 = w >> 8;
+      a1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, (w & 0x000f000fu) | magic), X0, a1, false);
+      a1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, (w8 & 0x000f000fu) | magic), X2, a1, false);
+      a16 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, (w & 0x00f000f0u) | magic), X1, a16, false);
+      a16 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, (w8 & 0x00f000f0u) | magic), X3, a16, false);
+      s1 = __builtin_amdgcn_fdot2(X0, one2, s1, false);
+      s1 = __builtin_amdgcn_fdot2(X2, one2, s1, false);
+      s16 = __builtin_amdgcn_fdot2(X1, one2, s16, false);
+      s16 = __builtin_amdgcn_fdot2(X3, one2, s16, false);
     } else {
+      // two words hold the block's 8 codes (see q8_words_to_f16)
       const uint4 &q = wq[j >> 1];
-      aw = (j & 1) ? q8_words_to_f16(q.z, q.w, s2, b2, magic) : q8_words_to_f16(q.x, q.y, s2, b2, magic);
+      const uint32_t w0 = (j & 1) ? q.z : q.x, w1 = (j & 1) ? q.w : q.y;
+      const uint32_t t0 = __builtin_amdgcn_perm(w1, w0, 0x05010400u);  // q0, q4, q1, q5
+      const uint32_t t1 = __builtin_amdgcn_perm(w1, w0, 0x07030602u);  // q2, q6, q3, q7
+      a1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, __builtin_amdgcn_perm(magic, t0, 0x04010400u)), X0, a1, false);
+      a1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, __builtin_amdgcn_perm(magic, t0, 0x04030402u)), X1, a1, false);
+      a1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, __builtin_amdgcn_perm(magic, t1, 0x04010400u)), X2, a1, false);
+      a1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, __builtin_amdgcn_perm(magic, t1, 0x04030402u)), X3, a1, false);
+      s1 = __builtin_amdgcn_fdot2(X0, one2, s1, false);
+      s1 = __builtin_amdgcn_fdot2(X1, one2, s1, false);
+      s1 = __builtin_amdgcn_fdot2(X2, one2, s1, false);
+      s1 = __builtin_amdgcn_fdot2(X3, one2, s1, false);
     }
-    acc = mfma_f16(aw, bx, acc);
   }
-  return acc;
+  qx = (a1 - 1024.0f * s1) + (QB == 4 ? (a16 - 1024.0f * s16) * 0.0625f : 0.0f);
+  sx = s1 + s16;
 }
 
 __device__ __forceinline__ float half_bits(uint16_t v, int half_f16) {
@@ -119,7 +148,6 @@ __device__ __forceinline__ float half_bits(uint16_t v, int half_f16) {
 // split in four); MPL: router logits per lane in the selection (E <= 64*MPL).
 template <int QB, int MSW, int MPL>
 __global__ __launch_bounds__(256) void t1_gateup_kernel(T1Args a) {
-  constexpr float kQMax = QB == 8 ? 255.0f : 15.0f;
   __shared__ __align__(16) uint16_t xs[kT1MaxD];  // fp16 staging row of x (zero past D to whole slabs)
   __shared__ int8_t s_xsh;
   __shared__ int32_t s_idx[kMaxTopK];
@@ -171,41 +199,21 @@ __global__ __launch_bounds__(256) void t1_gateup_kernel(T1Args a) {
   for (int s = 0; s < MSW; ++s)
     load_row_slab<QB>(wrow, sp, bp, nre, D, a.gsize, min(s0 + s, nslab - 1), lg, s < ns, wq[s], sr[s], br[s]);
 
-  // weight row exponent over this wave's slabs (the row's four lanes lg)
-  float wm = 0.f;
-#pragma unroll
-  for (int s = 0; s < MSW; ++s)
-    wm = fmaxf(wm, __builtin_fmaf(kQMax, fabsf(half_bits(sr[s], a.half_f16)), fabsf(half_bits(br[s], a.half_f16))));
-  wm = fmaxf(wm, __shfl_xor(wm, 16, kWave));
-  wm = fmaxf(wm, __shfl_xor(wm, 32, kWave));
-  const int wsh = f16_shift(wm);
-  const float wmul = pow2(-wsh);
-
   uint32_t magic = QB == 8 ? 0x64646464u : 0x64006400u;
   asm volatile("" : "+v"(magic));
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
 #pragma unroll
   for (int s = 0; s < MSW; ++s) {
     if (s < ns) {
-      const _Float16 s16 = (_Float16)(half_bits(sr[s], a.half_f16) * wmul);
-      const _Float16 b16 = (_Float16)(half_bits(br[s], a.half_f16) * wmul);
-      acc = slab_mfma<QB>(wq[s], h2{s16, s16}, h2{b16, b16}, xs + (s0 + s) * kSlab, lg, magic, acc);
+      float qx, sx;
+      slab_dot<QB>(wq[s], xs + (s0 + s) * kSlab + lg * 32, magic, qx, sx);
+      tot = __builtin_fmaf(half_bits(sr[s], a.half_f16), qx, __builtin_fmaf(half_bits(br[s], a.half_f16), sx, tot));
     }
   }
-  // lane holds rows 4*lg + i (every column alike): true values, then the
-  // waves' partial sums in LDS
-  if (lr == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) part[wave][4 * lg + i] = 0.f;
-  }
-  const int xsh = s_xsh;
-  float v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = acc[i] * pow2(__shfl(wsh, 4 * lg + i, kWave) + xsh);
-  if (lr == 0 && ns > 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) part[wave][4 * lg + i] = v[i];
-  }
+  // the row's four lanes lg, then the waves' partial sums in LDS (true values)
+  tot += __shfl_xor(tot, 16, kWave);
+  tot += __shfl_xor(tot, 32, kWave);
+  if (lane < 16) part[wave][lane] = ns > 0 ? tot * pow2(int(s_xsh)) : 0.f;
   __syncthreads();
   if (wave == 0) {
     float hv = 0.f;
@@ -230,7 +238,6 @@ __global__ __launch_bounds__(256) void t1_gateup_kernel(T1Args a) {
 // Grid d_model / 16, 512 threads.  MS: slabs of d_ff held per wave.
 template <int QB, int MS>
 __global__ __launch_bounds__(512) void t1_down_combine_kernel(T1Args a) {
-  constexpr float kQMax = QB == 8 ? 255.0f : 15.0f;
   extern __shared__ __align__(16) uint16_t hs[];  // [k + S][FR] fp16 h rows (staging order, zero to whole slabs)
   __shared__ uint32_t rmax_bits[kMaxTopK + kMaxShared];
   __shared__ float part[kDNWaves][16];
@@ -303,35 +310,24 @@ __global__ __launch_bounds__(512) void t1_down_combine_kernel(T1Args a) {
 
   uint32_t magic = QB == 8 ? 0x64646464u : 0x64006400u;
   asm volatile("" : "+v"(magic));
-  float ysum[4] = {0.f, 0.f, 0.f, 0.f};
+  float ysum = 0.f;  // output column c0 + lr, this lane's quarter lg of every slab
   for (int j = wave; j < R; j += kDNWaves) {
     if (j != wave) load_slot(j);
-    float wm = 0.f;
-#pragma unroll
-    for (int s = 0; s < MS; ++s)
-      wm = fmaxf(wm, __builtin_fmaf(kQMax, fabsf(half_bits(sr[s], a.half_f16)), fabsf(half_bits(br[s], a.half_f16))));
-    wm = fmaxf(wm, __shfl_xor(wm, 16, kWave));
-    wm = fmaxf(wm, __shfl_xor(wm, 32, kWave));
-    const int wsh = f16_shift(wm);
-    const float wmul = pow2(-wsh);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float tot = 0.f;
 #pragma unroll
     for (int s = 0; s < MS; ++s) {
       if (s < nslab) {
-        const _Float16 s16 = (_Float16)(half_bits(sr[s], a.half_f16) * wmul);
-        const _Float16 b16 = (_Float16)(half_bits(br[s], a.half_f16) * wmul);
-        acc = slab_mfma<QB>(wq[s], h2{s16, s16}, h2{b16, b16}, hs + j * FR + s * kSlab, lg, magic, acc);
+        float qx, sx;
+        slab_dot<QB>(wq[s], hs + j * FR + s * kSlab + lg * 32, magic, qx, sx);
+        tot = __builtin_fmaf(half_bits(sr[s], a.half_f16), qx, __builtin_fmaf(half_bits(br[s], a.half_f16), sx, tot));
       }
     }
     const float c = j < a.K ? a.wt[j] : 1.0f;
-    const int hsh = f16_shift(__uint_as_float(rmax_bits[j]));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ysum[i] += c * (acc[i] * pow2(__shfl(wsh, 4 * lg + i, kWave) + hsh));
+    ysum += c * (tot * pow2(f16_shift(__uint_as_float(rmax_bits[j]))));
   }
-  if (lr == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) part[wave][4 * lg + i] = ysum[i];
-  }
+  ysum += __shfl_xor(ysum, 16, kWave);
+  ysum += __shfl_xor(ysum, 32, kWave);
+  if (lane < 16) part[wave][lane] = ysum;
   __syncthreads();
   if (tid < 16) {
     float y = 0.f;
