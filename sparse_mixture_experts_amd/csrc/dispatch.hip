@@ -475,6 +475,11 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t *__restric
 
 }  // namespace
 
+int64_t dispatch_segment_slots(const moe_layer_desc *d, int32_t T) {
+  const int64_t N = int64_t(T) * d->top_k;
+  return N <= kSingleBlockMax ? 0 : dispatch_segment(N);
+}
+
 int64_t dispatch_scratch_ints(const moe_layer_desc *d, int32_t T) {
   const int64_t N = int64_t(T) * d->top_k;
   if (N <= kSingleBlockMax) return 0;
@@ -485,7 +490,7 @@ int64_t dispatch_scratch_ints(const moe_layer_desc *d, int32_t T) {
 void launch_dispatch(const moe_layer_desc *d, int32_t T, const int32_t *idx, int32_t tile_rows,
                      int32_t *order, int32_t *inv_order, int32_t *row_map, int32_t *expert_off,
                      int32_t *tile_off, int32_t *counters, PlanItem *act_items, PlanItem *tiles,
-                     int32_t *scratch, void *stream, StageMarker *mk) {
+                     int32_t *scratch, void *stream, StageMarker *mk, bool counts_ready) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int tr = plan_tile_rows(d, T);
   const int E = d->n_experts, N = T * d->top_k;
@@ -507,7 +512,7 @@ void launch_dispatch(const moe_layer_desc *d, int32_t T, const int32_t *idx, int
     const int seg = int(dispatch_segment(N));
     const int B = (N + seg - 1) / seg;
     const size_t lds_w = size_t(kMbWaves) * E * sizeof(int32_t);
-    launch(dispatch_count_kernel, dim3(B), dim3(kMbThreads), lds_w, s, idx, N, E, seg, scratch);
+    if (!counts_ready) launch(dispatch_count_kernel, dim3(B), dim3(kMbThreads), lds_w, s, idx, N, E, seg, scratch);
     // B ranking workgroups and one planning workgroup
     auto rank = [&](auto kern) {
       launch(kern, dim3(B + 1), dim3(kMbThreads), lds_w + size_t(5 * E) * sizeof(int32_t), s, idx, N,

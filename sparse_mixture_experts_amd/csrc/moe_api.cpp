@@ -159,12 +159,13 @@ static int forward_impl(const moe_layer_desc *desc, int32_t T, const void *x, co
   const FusedDispatch dsp{at<int32_t>(ws, L.order), at<int32_t>(ws, L.inv_order), at<int32_t>(ws, L.row_map),
                           at<int32_t>(ws, L.expert_off), at<int32_t>(ws, L.tile_off), at<int32_t>(ws, L.counters),
                           at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles), 64,
-                          plan_tile_rows(desc, T), desc->n_shared};
+                          plan_tile_rows(desc, T), desc->n_shared, at<int32_t>(ws, L.dsp)};
   launch_route(desc, T, x, w->w_router, w->router_bias, idx, wt, at<float>(ws, L.route), at<void>(ws, L.x16),
                at<int8_t>(ws, L.xsh), dsp, stream, mk);
   if (!route_fuses_dispatch(desc, T))
     launch_dispatch(desc, T, idx, 64, dsp.order, dsp.inv_order, dsp.row_map, dsp.expert_off, dsp.tile_off,
-                    dsp.counters, dsp.act_items, dsp.tiles, at<int32_t>(ws, L.dsp), stream, mk);
+                    dsp.counters, dsp.act_items, dsp.tiles, at<int32_t>(ws, L.dsp), stream, mk,
+                    route_counts_dispatch(desc, T));
   const int parts = ffn_down_parts(desc, T);
   int8_t *ys_sh = ys_f16e(desc, T) ? at<int8_t>(ws, L.ys_sh) : nullptr;
   launch_expert_ffn(desc, T, x, at<int32_t>(ws, L.row_map), w, at<int32_t>(ws, L.counters),
@@ -252,12 +253,14 @@ int moe_backward(const moe_layer_desc *desc, int32_t T, const void *x, const moe
   // the forward's routing and grouping, again (and the fp16 staging copy of x)
   int32_t *idx = at<int32_t>(ws, L.topk_idx);
   float *wt = at<float>(ws, L.topk_w);
+  FusedDispatch counts_only{};
+  counts_only.counts = at<int32_t>(ws, L.dsp);
   launch_route(desc, T, x, w->w_router, w->router_bias, idx, wt, at<float>(ws, L.route), at<void>(ws, L.x16),
-               at<int8_t>(ws, L.xsh), FusedDispatch{}, stream);
+               at<int8_t>(ws, L.xsh), counts_only, stream);
   launch_dispatch(desc, T, idx, plan_tile_rows(desc, T), at<int32_t>(ws, L.order), at<int32_t>(ws, L.inv_order),
                   at<int32_t>(ws, L.row_map), at<int32_t>(ws, L.expert_off), at<int32_t>(ws, L.tile_off),
                   at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles),
-                  at<int32_t>(ws, L.dsp), stream);
+                  at<int32_t>(ws, L.dsp), stream, nullptr, route_counts_dispatch(desc, T));
   const BwdScratch sc{at<float>(ws, B.gu),     at<float>(ws, B.v),       at<float>(ws, B.dw),
                       at<float>(ws, B.dxr),    at<float>(ws, B.dgu),     at<int8_t>(ws, B.dgu_sh),
                       at<int8_t>(ws, B.dy_sh), at<void>(ws, B.wr_t),     ffn_scratch(ws, L, route_writes_x16(desc))};

@@ -111,15 +111,22 @@ int64_t route_scratch_floats(const moe_layer_desc *d, int32_t T);
 // Matrix-core router with exact recomputation of the candidates (large T).
 bool route_mfma_applies(const moe_layer_desc *d, int32_t T);
 int64_t route_mfma_scratch_floats(const moe_layer_desc *d, int32_t T);
+// counts (nullable): the dispatch's per-segment expert counts [B][E+1] for
+// segments of seg slots, zeroed and then written here (integer atomics).
 void launch_route_mfma(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router, const float *bias,
                        int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh, void *stream,
-                       StageMarker *mk);
+                       StageMarker *mk, int32_t *counts = nullptr, int seg = 0);
 // Outputs of a dispatch that the router's selection kernel performs itself
 // (order == nullptr: none).
 struct FusedDispatch {
   int32_t *order, *inv_order, *row_map, *expert_off, *tile_off, *counters;
   PlanItem *act_items, *tiles;
   int tile_rows, tr, S;
+  // Nullable: the multi-workgroup dispatch's per-segment expert counts
+  // ([B][E+1], see dispatch_segment_slots), which the matrix-core router
+  // writes with integer atomics when route_counts_dispatch holds; the
+  // dispatch then skips its counting pass.
+  int32_t *counts = nullptr;
 };
 // x16/xsh (nullable): the router's per-token kernel also writes the fp16
 // staging copy of x for the 4-bit GEMMs when route_writes_x16 holds.  With
@@ -146,10 +153,17 @@ void launch_t1_layer(const moe_layer_desc *d, const void *x, const moe_weights *
 // Dispatch: stable counting sort + prefix tables + the internal work plan.
 // scratch holds dispatch_scratch_ints ints (per-workgroup counts for large N).
 int64_t dispatch_scratch_ints(const moe_layer_desc *d, int32_t T);
+// counts_ready: the per-segment counts in `scratch` were written by the
+// router (route_counts_dispatch), so the counting pass is skipped.
 void launch_dispatch(const moe_layer_desc *d, int32_t T, const int32_t *idx, int32_t tile_rows,
                      int32_t *order, int32_t *inv_order, int32_t *row_map, int32_t *expert_off,
                      int32_t *tile_off, int32_t *counters, PlanItem *act_items, PlanItem *tiles,
-                     int32_t *scratch, void *stream, StageMarker *mk = nullptr);
+                     int32_t *scratch, void *stream, StageMarker *mk = nullptr, bool counts_ready = false);
+// Slots per segment of the multi-workgroup dispatch (0 when T*k is small
+// enough for one workgroup).
+int64_t dispatch_segment_slots(const moe_layer_desc *d, int32_t T);
+// The matrix-core router writes the multi-workgroup dispatch's counts.
+bool route_counts_dispatch(const moe_layer_desc *d, int32_t T);
 
 // Work plan from caller-supplied expert offsets (standalone moe_expert_ffn).
 void launch_plan(const moe_layer_desc *d, int32_t T, const int32_t *expert_off, int32_t *counters,

@@ -303,7 +303,9 @@ void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void 
   FusedDispatch dsp = dsp_in;
   if (!route_fuses_dispatch(d, T)) dsp.order = nullptr;
   if (route_mfma_applies(d, T)) {
-    launch_route_mfma(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, stream, mk);
+    const bool counts = dsp.counts && route_counts_dispatch(d, T);
+    launch_route_mfma(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, stream, mk, counts ? dsp.counts : nullptr,
+                      counts ? int(dispatch_segment_slots(d, T)) : 0);
     return;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -68,9 +68,14 @@ constexpr int kMaxCand = 64;
 template <int DT>
 __global__ __launch_bounds__(kThreads) void router_transpose_kernel(const uint16_t *__restrict__ w, int D, int E,
                                                                     uint16_t *__restrict__ wt,
-                                                                    float *__restrict__ normp) {
+                                                                    float *__restrict__ normp,
+                                                                    int32_t *__restrict__ counts, int n_counts) {
   __shared__ uint16_t tile[64][256 + 8];
   const int tid = threadIdx.x;
+  // the dispatch counts that the certification adds to start from zero
+  for (int i = (blockIdx.y * gridDim.x + blockIdx.x) * kThreads + tid; i < n_counts;
+       i += gridDim.x * gridDim.y * kThreads)
+    counts[i] = 0;
   const int e0 = blockIdx.x * 64, k0 = blockIdx.y * 256;
   {
     const int k = k0 + tid;  // one router row per thread, 64 experts
@@ -261,6 +266,8 @@ struct CertArgs {
   float *w_out;
   uint16_t *x16;  // nullable: fp16 staging copy of x for the 4-bit GEMMs
   int8_t *xsh;
+  int32_t *counts;  // nullable: dispatch counts [N / seg][E + 1] of the slots' experts, per segment of seg slots
+  int seg;
 };
 
 // One wave per token; each lane keeps L~ of experts lane + 64*m, m < MPL.
@@ -471,6 +478,8 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
   if (lane < K) {
     a.idx_out[int64_t(t) * K + lane] = my_e;
     a.w_out[int64_t(t) * K + lane] = pj / psum;
+    // integer sums: the same counts whatever the order of the additions
+    if (a.counts) atomicAdd(&a.counts[((int64_t(t) * K + lane) / a.seg) * (E + 1) + my_e], 1);
   }
 }
 
@@ -481,6 +490,10 @@ bool route_mfma_applies(const moe_layer_desc *d, int32_t T) {
   // the matrix-core router's three launches cost more than its fma chains.
   return d->act_dtype != MOE_DT_F32 && d->renormalize && d->d_model % kChunk == 0 &&
          d->d_model <= kWave * kChunk && T >= 64 && int64_t(T) * d->n_experts >= 65536;
+}
+
+bool route_counts_dispatch(const moe_layer_desc *d, int32_t T) {
+  return route_mfma_applies(d, T) && dispatch_segment_slots(d, T) > 0;
 }
 
 // Scratch: L~ [T][E] f32, then WT [E][D] (16-bit), then norm partials [D/256][E]
@@ -500,15 +513,17 @@ namespace {
 template <int DT>
 void launch_route_mfma_t(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router, const float *bias,
                          int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh, hipStream_t s,
-                         StageMarker *mk) {
+                         StageMarker *mk, int32_t *counts, int seg) {
   const int D = d->d_model, E = d->n_experts, nkb = (D + 255) / 256, C = D / kChunk;
+  const int64_t N = int64_t(T) * d->top_k;
+  const int n_counts = counts ? int((N + seg - 1) / seg * (E + 1)) : 0;
   float *lt = scratch;
   const int nz = route_mfma_splits(d);
   const int64_t o_wt = align4(nz * int64_t(T) * E), o_np = o_wt + align4((int64_t(E) * D + 1) / 2);
   uint16_t *wt = reinterpret_cast<uint16_t *>(scratch + o_wt);
   float *normp = scratch + o_np;
   launch(router_transpose_kernel<DT>, dim3((E + 63) / 64, nkb), dim3(kThreads), 0, s,
-                     static_cast<const uint16_t *>(w_router), D, E, wt, normp);
+                     static_cast<const uint16_t *>(w_router), D, E, wt, normp, counts, n_counts);
   launch(router_mfma_kernel<DT>, dim3((E + 63) / 64, (T + 63) / 64, nz), dim3(kMfThreads), 0, s,
                      static_cast<const uint16_t *>(x), wt, bias, normp, nkb, T, D, E, lt);
   if (mk) mk->mark("route_mfma");
@@ -519,7 +534,7 @@ void launch_route_mfma_t(const moe_layer_desc *d, int32_t T, const void *x, cons
   // for fp16.
   const float gamma = float((DT == kDtF16 ? 384 : 256) + 2 * C) * 5.9604645e-8f;
   CertArgs ca{static_cast<const uint16_t *>(x), wt, bias, lt, normp + int64_t(nkb) * E, T, D, E, d->top_k, nz,
-              gamma, idx, w, static_cast<uint16_t *>(x16), xsh};
+              gamma, idx, w, static_cast<uint16_t *>(x16), xsh, counts, seg};
   const dim3 grid((T + kThreads / kWave - 1) / (kThreads / kWave)), block(kThreads);
   if (E <= 64) launch((router_certify_kernel<1, DT>), grid, block, 0, s, ca);
   else if (E <= 128) launch((router_certify_kernel<2, DT>), grid, block, 0, s, ca);
@@ -533,12 +548,13 @@ void launch_route_mfma_t(const moe_layer_desc *d, int32_t T, const void *x, cons
 
 void launch_route_mfma(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router, const float *bias,
                        int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh, void *stream,
-                       StageMarker *mk) {
+                       StageMarker *mk, int32_t *counts, int seg) {
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (counts && seg <= 0) counts = nullptr;
   if (d->act_dtype == MOE_DT_F16)
-    launch_route_mfma_t<kDtF16>(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, s, mk);
+    launch_route_mfma_t<kDtF16>(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, s, mk, counts, seg);
   else
-    launch_route_mfma_t<kDtBF16>(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, s, mk);
+    launch_route_mfma_t<kDtBF16>(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, s, mk, counts, seg);
 }
 
 }  // namespace moe

@@ -119,6 +119,11 @@ MID = {
     # outputs (vector-unit kernels and decode tiles)
     "mid-q4-k16": LayerSpec("mid-q4-k16", T=100, d_model=256, d_ff=128, n_experts=32, top_k=16, wfmt="q4",
                             seed=57),
+    # the matrix-core router over more than 4096 slots: its certification
+    # also counts the slots of every dispatch segment, and the multi-
+    # workgroup dispatch ranks from those counts
+    "mid-q4-t512-k10-counts": LayerSpec("mid-q4-t512-k10-counts", T=512, d_model=256, d_ff=128, n_experts=128,
+                                        top_k=10, wfmt="q4", seed=70),
     "mid-f32-k10": LayerSpec("mid-f32-k10", T=24, d_model=96, d_ff=64, n_experts=16, top_k=10, act="f32",
                              x_scale="fan_in", seed=58),
     "mid-q4-decode-k12": LayerSpec("mid-q4-decode-k12", T=2, d_model=256, d_ff=192, n_experts=64, top_k=12,
