@@ -1173,9 +1173,11 @@ inline size_t down_resident_lds(int RB, int K) {
 template <int QB, int RB>
 void launch_down_resident(const GemmArgs &ga, int gsize, int64_t max_tiles, int64_t est_tiles, hipStream_t s) {
   const int n_cb = (ga.n_out + kNRows - 1) / kNRows;
-  // column blocks per workgroup: about four workgroups per CU over the
-  // expected tiles, each staging its tile's h once
-  const int64_t want = (est_tiles * n_cb + 1023) / 1024;
+  // column blocks per workgroup: about two workgroups per CU over the
+  // expected tiles, each staging its tile's h once (prefill: all 8 blocks,
+  // 125.6 us against 128.5 us with 5 and 169.8 us with 1; 32-token decode:
+  // 2 blocks, 33.5 us against 35.3 us with 1)
+  const int64_t want = (est_tiles * n_cb + 511) / 512;
   const int cbpw = int(std::max<int64_t>(1, std::min<int64_t>(n_cb, want)));
   const dim3 grid((n_cb + cbpw - 1) / cbpw, unsigned(max_tiles));
   const size_t lds = down_resident_lds(RB, ga.K);
