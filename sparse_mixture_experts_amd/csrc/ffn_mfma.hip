@@ -96,6 +96,9 @@ struct GemmArgs {
   int bx_major;             // work order: column block major (experts with several tiles), else tile major
   int kz;                   // down: reduction parts (fp32 partial rows at out + z * part_stride), else 1
   int64_t part_stride;
+  // affine: tile-packed copies of w0 / w1 (moe_pack_weights), or null; set
+  // together (w1's when gate and up are separate)
+  const uint32_t *wp0 = nullptr, *wp1 = nullptr;
 };
 
 // Column blocks per group of the work order (item_tile_block): whole rows of
@@ -221,13 +224,22 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
   const int col_c = col_ok ? col0 : a.n_out - NTH * 16;  // in-range columns for idle waves
 
   // This lane's weight row (operand A row lr) of each tile.
+  // With a tile-packed copy, a lane's row of a slab sits at (tile of 16
+  // rows, slab, row in tile): the 16 rows of a slab are one contiguous block.
+  constexpr int SW = kKS * QB / 32;  // affine: words of one row's slab
+  const bool packed = AFF && a.wp0 != nullptr;
   const void *wp[kNT];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
     const bool up = GATEUP && nt >= NTH;
     const int64_t wr = wrow_of(col_c + (nt % NTH) * 16 + lr, up);
-    wp[nt] = AFF ? static_cast<const void *>(static_cast<const uint32_t *>(wsrc(up)) + wr * KW)
-                : static_cast<const void *>(static_cast<const uint16_t *>(wsrc(up)) + wr * K);
+    if (packed) {
+      const uint32_t *pb = (GATEUP && !a.fused && up) ? a.wp1 : a.wp0;
+      wp[nt] = pb + (wr >> 4) * (int64_t((K + kKS - 1) / kKS) * 16 * SW) + (wr & 15) * SW;
+    } else {
+      wp[nt] = AFF ? static_cast<const void *>(static_cast<const uint32_t *>(wsrc(up)) + wr * KW)
+                  : static_cast<const void *>(static_cast<const uint16_t *>(wsrc(up)) + wr * K);
+    }
   }
   // Slab s of this lane's rows.  The last slab may hold only 64 elements
   // (K = 64 mod 128): its second half is read from a clamped address and
@@ -238,7 +250,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
     for (int nt = 0; nt < kNT; ++nt) {
       if constexpr (AFF) {
         constexpr int WPL = QB;  // words per lane and slab (32 elements)
-        const int w = min(s * (kKS * QB / 32) + lg * WPL, KW - WPL);
+        const int w = packed ? s * 16 * SW + lg * WPL : min(s * SW + lg * WPL, KW - WPL);
 #pragma unroll
         for (int v = 0; v < QB / 4; ++v)
           dst.w[nt][v] = *reinterpret_cast<const uint4 *>(static_cast<const uint32_t *>(wp[nt]) + w + 4 * v);
@@ -743,6 +755,9 @@ __device__ __forceinline__ void down_resident_body(const GemmArgs &a, int cbpw) 
     uint16_t sv[NT], bv[NT];
   };
   const uint32_t *wbase = static_cast<const uint32_t *>(a.w0) + int64_t(tile.expert) * a.n_out * KW;
+  // tile-packed copy (or null): the 16 rows of a slab in one block
+  constexpr int SW = kKS * QB / 32;
+  const uint32_t *pbase = a.wp0 ? a.wp0 + int64_t(tile.expert) * a.n_out * nslab * SW : nullptr;
   const uint16_t *sbase = a.s0 + int64_t(tile.expert) * G * a.n_out;
   const uint16_t *bbase = a.b0 + int64_t(tile.expert) * G * a.n_out;
   auto load_step = [&](int q, WStep &st) {
@@ -755,7 +770,8 @@ __device__ __forceinline__ void down_resident_body(const GemmArgs &a, int cbpw) 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int n = min(colw + nt * 16 + lr, a.n_out - 1);
-      const uint32_t *wr = wbase + int64_t(n) * KW + w;
+      const uint32_t *wr = pbase ? pbase + (int64_t(n >> 4) * nslab + sl) * 16 * SW + (n & 15) * SW + lg * QB
+                                 : wbase + int64_t(n) * KW + w;
 #pragma unroll
       for (int v = 0; v < QB / 4; ++v) st.w[nt][v] = *reinterpret_cast<const uint4 *>(wr + 4 * v);
       const uint16_t s = sbase[int64_t(g) * a.n_out + n], b = bbase[int64_t(g) * a.n_out + n];
@@ -1300,6 +1316,15 @@ int plan_tile_rows(const moe_layer_desc *d, int32_t T) {
   return N <= 8LL * d->n_experts ? 16 : 64;
 }
 
+// The tile-packed copies, when the caller gave every one the projection
+// needs (gate and up both, when separate).
+// p1: the up projection when gate and up are separate, else null.
+static void set_packed(const moe_layer_desc *d, GemmArgs &g, const moe_proj &p0, const moe_proj *p1) {
+  if (!affine(d) || !p0.w_packed || (p1 && !p1->w_packed)) return;
+  g.wp0 = static_cast<const uint32_t *>(p0.w_packed);
+  g.wp1 = p1 ? static_cast<const uint32_t *>(p1->w_packed) : nullptr;
+}
+
 void launch_gate_up_raw_mfma(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
                              const moe_weights *w, const int32_t *counters, const PlanItem *tiles, int64_t max_tiles,
                              const FfnScratch &sc, float *gu, void *stream) {
@@ -1316,6 +1341,7 @@ void launch_gate_up_raw_mfma(const moe_layer_desc *d, int32_t T, const void *x, 
              pg.w, static_cast<const uint16_t *>(pg.scales), static_cast<const uint16_t *>(pg.biases),
              w->up.w, static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases),
              counters, tiles, gu, use_bx_major(d, T), 1, 0};
+  set_packed(d, g, pg, d->gate_up_fused ? nullptr : &w->up);
   if (plan_tile_rows(d, T) == 16) launch_gemm<kGateUpRaw, 1>(g, qb, d->group_size, max_tiles, s);
   else launch_gemm<kGateUpRaw, 4>(g, qb, d->group_size, max_tiles, s);
 }
@@ -1350,6 +1376,8 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
               w->down.w, static_cast<const uint16_t *>(w->down.scales), static_cast<const uint16_t *>(w->down.biases),
               nullptr, nullptr, nullptr, counters, tiles, y_sorted, bx_major, down_parts,
               (int64_t(T) * d->top_k + int64_t(d->n_shared) * T) * d->d_model};
+  set_packed(d, gu, pg, d->gate_up_fused ? nullptr : &w->up);
+  set_packed(d, dn, w->down, nullptr);
   if (decode_tiles(d, T)) {
     // at most one routed row per expert on average: whole-K loads per wave
     // (one memory round trip), h as bf16 between the two projections

@@ -231,6 +231,26 @@ int moe_forward_timed(const moe_layer_desc *desc, int32_t T, const void *x, cons
   return forward_impl(desc, T, x, w, y, out_dtype, topk_idx_out, topk_w_out, ws, ws_bytes, stream, &mk);
 }
 
+int moe_packed_bytes(const moe_layer_desc *desc, int32_t proj, size_t *bytes) {
+  int s;
+  if ((s = validate_desc(desc))) return s;
+  if (!bytes) return MOE_E_INVALID;
+  if (!affine(desc)) return MOE_E_UNSUPPORTED;
+  const int64_t words = packed_words(desc, proj);
+  if (words < 0) return MOE_E_INVALID;
+  *bytes = size_t(words) * 4;
+  return MOE_OK;
+}
+
+int moe_pack_weights(const moe_layer_desc *desc, int32_t proj, const void *w, void *w_packed, void *stream) {
+  size_t bytes = 0;
+  int s;
+  if ((s = moe_packed_bytes(desc, proj, &bytes))) return s;
+  if ((s = validate_ptr(w)) || (s = validate_ptr(w_packed))) return s;
+  launch_pack(desc, proj, static_cast<const uint32_t *>(w), static_cast<uint32_t *>(w_packed), stream);
+  return hip_status();
+}
+
 int moe_backward_workspace_size(const moe_layer_desc *desc, int32_t T, size_t *bytes) {
   int s;
   if ((s = validate_desc(desc)) || (s = validate_T(T))) return s;

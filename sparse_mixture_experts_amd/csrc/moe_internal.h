@@ -62,6 +62,14 @@ int validate_T(int32_t T);
 int validate_ptr(const void *p, bool may_be_null = false);
 int validate_weights(const moe_layer_desc *d, const moe_weights *w, bool need_router,
                      bool need_experts);
+// Rows N and reduction K of a moe_projection (false: not used by the layer),
+// and the uint32 words of its tile-packed copy for all E+S matrices (-1:
+// not used).
+bool proj_shape(const moe_layer_desc *d, int32_t proj, int *N, int *K);
+int64_t packed_words(const moe_layer_desc *d, int32_t proj);
+// Repack the codes w[E+S][N][K*b/32] of one projection into the tile-packed
+// layout (see moe_pack_weights).
+void launch_pack(const moe_layer_desc *d, int32_t proj, const uint32_t *w, uint32_t *w_packed, void *stream);
 
 inline int64_t act_bytes(const moe_layer_desc *d) { return d->act_dtype == MOE_DT_F32 ? 4 : 2; }
 // Affine 4- or 8-bit expert weights (fp16 matrix-core path with fp16 staging).

@@ -54,8 +54,40 @@ static int validate_proj(const moe_layer_desc *d, const moe_proj &p) {
   if (affine(d)) {
     if ((s = validate_ptr(p.scales))) return s;
     if ((s = validate_ptr(p.biases))) return s;
+    if ((s = validate_ptr(p.w_packed, true))) return s;
+  } else if (p.w_packed) {
+    return MOE_E_INVALID;  // the packed copy exists for affine codes only
   }
   return MOE_OK;
+}
+
+// Rows N and reduction K of projection `proj` (moe_projection); false when
+// the descriptor does not use it.
+bool proj_shape(const moe_layer_desc *d, int32_t proj, int *N, int *K) {
+  switch (proj) {
+    case MOE_PROJ_GATE:
+    case MOE_PROJ_UP:
+      if (d->gate_up_fused) return false;
+      *N = d->d_ff, *K = d->d_model;
+      return true;
+    case MOE_PROJ_GATE_UP:
+      if (!d->gate_up_fused) return false;
+      *N = 2 * d->d_ff, *K = d->d_model;
+      return true;
+    case MOE_PROJ_DOWN:
+      *N = d->d_model, *K = d->d_ff;
+      return true;
+    default:
+      return false;
+  }
+}
+
+int64_t packed_words(const moe_layer_desc *d, int32_t proj) {
+  int N = 0, K = 0;
+  if (!proj_shape(d, proj, &N, &K)) return -1;
+  const int b = d->w_format == MOE_WF_AFFINE_Q8 ? 8 : 4;
+  const int64_t nslab = (K + 127) / 128, sw = 128 * b / 32;
+  return int64_t(d->n_experts + d->n_shared) * N * nslab * sw;
 }
 
 int validate_weights(const moe_layer_desc *d, const moe_weights *w, bool need_router,

@@ -27,7 +27,9 @@ _ACT = {"swiglu": MOE_ACT_SWIGLU, "geglu": MOE_ACT_GEGLU}
 
 EXPORTED = ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
             "moe_forward", "moe_forward_timed", "moe_backward_workspace_size", "moe_backward",
-            "moe_status_string", "moe_forward_noalloc")
+            "moe_status_string", "moe_forward_noalloc", "moe_packed_bytes", "moe_pack_weights")
+MOE_PROJ_GATE, MOE_PROJ_UP, MOE_PROJ_GATE_UP, MOE_PROJ_DOWN = 0, 1, 2, 3
+_PROJ = {"gate": MOE_PROJ_GATE, "up": MOE_PROJ_UP, "gate_up": MOE_PROJ_GATE_UP, "down": MOE_PROJ_DOWN}
 NOALLOC_SCRATCH_BYTES = 96 * 1024 * 1024  # MOE_NOALLOC_SCRATCH_BYTES
 
 
@@ -44,7 +46,8 @@ class LayerDesc(ctypes.Structure):
 
 
 class Proj(ctypes.Structure):
-    _fields_ = [("w", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
+    _fields_ = [("w", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
+                ("w_packed", ctypes.c_void_p)]
 
 
 class Weights(ctypes.Structure):
@@ -75,6 +78,8 @@ def load() -> ctypes.CDLL:
         lib.moe_forward_noalloc.argtypes = [P(LayerDesc), i32, vp, P(Weights), vp, i32, vp, vp, vp]
         lib.moe_backward_workspace_size.argtypes = [P(LayerDesc), i32, P(sz)]
         lib.moe_backward.argtypes = [P(LayerDesc), i32, vp, P(Weights), vp, vp, vp, sz, vp]
+        lib.moe_packed_bytes.argtypes = [P(LayerDesc), i32, P(sz)]
+        lib.moe_pack_weights.argtypes = [P(LayerDesc), i32, vp, vp, vp]
         lib.moe_status_string.argtypes = [ctypes.c_int]
         lib.moe_status_string.restype = ctypes.c_char_p
         for name in EXPORTED:
@@ -202,6 +207,18 @@ def moe_backward(desc, T, x, weights, dy, dx, ws, stream=None):
                                _ptr(ws), _nbytes(ws), _stream(stream)), "moe_backward")
 
 
+def moe_packed_bytes(desc: LayerDesc, proj: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().moe_packed_bytes(ctypes.byref(desc), proj, ctypes.byref(out)), "moe_packed_bytes")
+    return out.value
+
+
+def moe_pack_weights(desc, proj: int, w, w_packed, stream=None):
+    """Enqueue the tile-packed copy of projection `proj`'s codes `w` into `w_packed`."""
+    _check(load().moe_pack_weights(ctypes.byref(desc), proj, _ptr(w), _ptr(w_packed), _stream(stream)),
+           "moe_pack_weights")
+
+
 # ---- marshalling helpers ----------------------------------------------------
 
 def to_device(a: np.ndarray, device) -> torch.Tensor:
@@ -226,7 +243,7 @@ class DeviceWeights:
             p = experts.get(name)
             if p is None:
                 return Proj(None, None, None)
-            return Proj(_ptr(p["w"]), _ptr(p.get("scales")), _ptr(p.get("biases")))
+            return Proj(_ptr(p["w"]), _ptr(p.get("scales")), _ptr(p.get("biases")), _ptr(p.get("w_packed")))
 
         self.c = Weights(_ptr(w_router), _ptr(router_bias), proj("gate"), proj("up"), proj("gate_up"),
                          proj("down"))
@@ -236,6 +253,20 @@ class DeviceWeights:
         experts = {name: {k: to_device(v, device) for k, v in p.items()} for name, p in layer["experts"].items()}
         bias = None if layer["router_bias"] is None else to_device(layer["router_bias"], device)
         return cls(to_device(layer["w_router"], device), bias, experts)
+
+    def with_packed(self, desc: LayerDesc, stream=None) -> "DeviceWeights":
+        """The same weights plus a tile-packed copy of every affine projection's
+        codes (moe_pack_weights), which the grouped kernels then read."""
+        experts = {}
+        for name, p in self.experts.items():
+            q = dict(p)
+            q.pop("w_packed", None)
+            n = moe_packed_bytes(desc, _PROJ[name])
+            m = p["w"].shape[0]  # matrices (experts, routed then shared)
+            q["w_packed"] = torch.empty((m, n // 4 // m), dtype=torch.int32, device=p["w"].device)
+            moe_pack_weights(desc, _PROJ[name], p["w"], q["w_packed"], stream)
+            experts[name] = q
+        return DeviceWeights(self.w_router, self.router_bias, experts)
 
     def clone(self) -> "DeviceWeights":
         """A byte-identical copy at new device addresses."""

@@ -188,3 +188,34 @@ def test_workspace_covers_smaller_T(shape):
         size = moe.moe_workspace_size(desc, T)
         assert size >= prev, (T, size, prev)
         prev = size
+
+
+def test_packed_bytes_and_validation(lib):
+    size = ctypes.c_size_t()
+    d = moe.make_desc(2048, 768, 128, 8, n_shared=2, wfmt="q4")
+    # [E+S][N/16 tiles][ceil(K/128) slabs][16 rows][16 words] = (E+S) * N * slabs * 16 words
+    assert lib.moe_packed_bytes(ctypes.byref(d), moe.MOE_PROJ_GATE, ctypes.byref(size)) == moe.MOE_OK
+    assert size.value == 130 * 768 * 16 * 16 * 4
+    assert lib.moe_packed_bytes(ctypes.byref(d), moe.MOE_PROJ_DOWN, ctypes.byref(size)) == moe.MOE_OK
+    assert size.value == 130 * 2048 * 6 * 16 * 4
+    # 8-bit codes, a reduction of 64 mod 128 padded to a whole slab
+    d8 = moe.make_desc(320, 192, 4, 2, wfmt="q8", group_size=32, gate_up_fused=True)
+    assert lib.moe_packed_bytes(ctypes.byref(d8), moe.MOE_PROJ_GATE_UP, ctypes.byref(size)) == moe.MOE_OK
+    assert size.value == 4 * 384 * 3 * 32 * 4
+    # a projection the layer does not use, dense weights, bad arguments
+    assert lib.moe_packed_bytes(ctypes.byref(d), moe.MOE_PROJ_GATE_UP, ctypes.byref(size)) == moe.MOE_E_INVALID
+    assert lib.moe_packed_bytes(ctypes.byref(d), 7, ctypes.byref(size)) == moe.MOE_E_INVALID
+    dd = moe.make_desc(2048, 768, 128, 8)
+    assert lib.moe_packed_bytes(ctypes.byref(dd), moe.MOE_PROJ_DOWN, ctypes.byref(size)) == moe.MOE_E_UNSUPPORTED
+    assert lib.moe_pack_weights(ctypes.byref(d), moe.MOE_PROJ_DOWN, A + 4, A, None) == moe.MOE_E_INVALID
+    assert lib.moe_pack_weights(ctypes.byref(d), moe.MOE_PROJ_DOWN, A, None, None) == moe.MOE_E_INVALID
+    # a packed copy on a dense layer, or misaligned, is refused before anything runs
+    w = weights()
+    w.down = moe.Proj(A, None, None, A)
+    need = ws_size(dd, 0)
+    assert lib.moe_forward(ctypes.byref(dd), 0, A, ctypes.byref(w), A, 1, None, None, A, need, None) == \
+        moe.MOE_E_INVALID
+    w = weights()
+    w.down = moe.Proj(A, A, A, A + 4)
+    assert lib.moe_forward(ctypes.byref(d), 0, A, ctypes.byref(w), A, 1, None, None, A, ws_size(d, 0), None) == \
+        moe.MOE_E_INVALID
