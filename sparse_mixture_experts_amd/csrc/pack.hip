@@ -10,6 +10,8 @@
 // zero where SW s + j is past the row (a last slab of 64 columns).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "launch.h"
 #include "moe_internal.h"
 
@@ -18,24 +20,25 @@ namespace {
 
 constexpr int kPackThreads = 256;
 
-// One thread per 16-byte piece of the packed copy.
+// 16-byte pieces of the packed copy, grid-stride over all of them.
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(const uint32_t *__restrict__ w,
                                                             uint32_t *__restrict__ out, int64_t pieces, int KW,
                                                             int nslab, int SW) {
-  const int64_t q = int64_t(blockIdx.x) * kPackThreads + threadIdx.x;
-  if (q >= pieces) return;
   const int per_row = SW / 4;                       // pieces per (row, slab)
   const int64_t per_tile = int64_t(nslab) * 16 * per_row;
-  const int64_t mt = q / per_tile;                  // matrix * (N / 16) + tile
-  int64_t rem = q - mt * per_tile;
-  const int s = int(rem / (16 * per_row));
-  rem -= int64_t(s) * 16 * per_row;
-  const int r = int(rem / per_row), j = int(rem % per_row) * 4;
-  const int64_t row = mt * 16 + r;                  // row over all matrices (N % 16 == 0)
-  const int col = s * SW + j;
-  uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (col < KW) v = *reinterpret_cast<const uint4 *>(w + row * KW + col);
-  reinterpret_cast<uint4 *>(out)[q] = v;
+  for (int64_t q = int64_t(blockIdx.x) * kPackThreads + threadIdx.x; q < pieces;
+       q += int64_t(gridDim.x) * kPackThreads) {
+    const int64_t mt = q / per_tile;                // matrix * (N / 16) + tile
+    int64_t rem = q - mt * per_tile;
+    const int s = int(rem / (16 * per_row));
+    rem -= int64_t(s) * 16 * per_row;
+    const int r = int(rem / per_row), j = int(rem % per_row) * 4;
+    const int64_t row = mt * 16 + r;                // row over all matrices (N % 16 == 0)
+    const int col = s * SW + j;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (col < KW) v = *reinterpret_cast<const uint4 *>(w + row * KW + col);
+    reinterpret_cast<uint4 *>(out)[q] = v;
+  }
 }
 
 }  // namespace
@@ -47,7 +50,7 @@ void launch_pack(const moe_layer_desc *d, int32_t proj, const uint32_t *w, uint3
   const int KW = K * b / 32, SW = 128 * b / 32, nslab = (K + 127) / 128;
   const int64_t pieces = packed_words(d, proj) / 4;
   if (pieces <= 0) return;
-  const int64_t blocks = (pieces + kPackThreads - 1) / kPackThreads;
+  const int64_t blocks = std::min<int64_t>((pieces + kPackThreads - 1) / kPackThreads, 1 << 20);
   launch(pack_kernel, dim3(unsigned(blocks)), dim3(kPackThreads), 0, static_cast<hipStream_t>(stream), w, w_packed,
          pieces, KW, nslab, SW);
 }
