@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace moe {
 
 constexpr int kWave = 64;
@@ -14,12 +16,11 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) { return __uint_
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.  gfx950
+// converts in one instruction (v_cvt_pk_bf16_f32, under the default
+// round-to-nearest-even mode, subnormals kept).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 __device__ __forceinline__ float round_bf16(float f) { return bf16_bits_to_f32(f32_to_bf16_bits(f)); }
 
@@ -170,15 +171,43 @@ __device__ __forceinline__ float round_mode(float f, int mode) {
 // gelu_tanh(g) * u.  With per-op rounding (mode bf16 or fp16): gate and up
 // rounded, then for SwiGLU sigmoid, g*s and (g*s)*u each rounded; for GeGLU
 // gelu(g) and gelu(g)*u each rounded (round to nearest even).
+template <int MODE, bool GEGLU>
+__device__ __forceinline__ float glu_t(float g, float u) {
+  if constexpr (MODE == kRoundNone) {
+    return (GEGLU ? gelu_tanh_f32(g) : silu_f32(g)) * u;
+  } else {
+    auto r = [](float v) { return MODE == kRoundF16 ? round_f16(v) : round_bf16(v); };
+    g = r(g);
+    u = r(u);
+    if constexpr (GEGLU) return r(r(gelu_tanh_f32(g)) * u);
+    const float s = r(sigmoid_f32(g));
+    const float a = r(g * s);
+    return r(a * u);
+  }
+}
 __device__ __forceinline__ float glu(float g, float u, int round_mode_, bool geglu) {
-  if (round_mode_ == kRoundNone) return (geglu ? gelu_tanh_f32(g) : silu_f32(g)) * u;
-  auto r = [&](float v) { return round_mode(v, round_mode_); };
-  g = r(g);
-  u = r(u);
-  if (geglu) return r(r(gelu_tanh_f32(g)) * u);
-  float s = r(sigmoid_f32(g));
-  float a = r(g * s);
-  return r(a * u);
+  if (round_mode_ == kRoundNone) return geglu ? glu_t<kRoundNone, true>(g, u) : glu_t<kRoundNone, false>(g, u);
+  if (round_mode_ == kRoundF16) return geglu ? glu_t<kRoundF16, true>(g, u) : glu_t<kRoundF16, false>(g, u);
+  return geglu ? glu_t<kRoundBF16, true>(g, u) : glu_t<kRoundBF16, false>(g, u);
+}
+
+// Calls f(std::integral_constant<int, mode>, std::integral_constant<bool, geglu>)
+// for the run-time rounding mode and gate function, so that a loop over many
+// outputs is compiled once per case instead of selecting per value.
+template <typename F>
+__device__ __forceinline__ void with_glu(int round_mode_, bool geglu, F &&f) {
+  using N = std::integral_constant<int, kRoundNone>;
+  using B = std::integral_constant<int, kRoundBF16>;
+  using H = std::integral_constant<int, kRoundF16>;
+  using T = std::true_type;
+  using Fl = std::false_type;
+  if (round_mode_ == kRoundBF16) {
+    if (geglu) f(B{}, T{}); else f(B{}, Fl{});
+  } else if (round_mode_ == kRoundF16) {
+    if (geglu) f(H{}, T{}); else f(H{}, Fl{});
+  } else {
+    if (geglu) f(N{}, T{}); else f(N{}, Fl{});
+  }
 }
 
 

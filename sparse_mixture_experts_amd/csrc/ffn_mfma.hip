@@ -558,23 +558,26 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
     // hold the two halves of an 8-column block and swap a pair of values so
     // that each stores 4 contiguous permuted elements.
     float hv[RB][NTH][4];
+    with_glu(a.round_ops, a.geglu != 0, [&](auto mode, auto gelu) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      if (rb * 16 >= tile.rows) break;  // row blocks past the tile (uniform)
-      const float xs = pow2(rsh[rb * 16 + lr]);
-      float mx = 0.f;
+      for (int rb = 0; rb < RB; ++rb) {
+        if (rb * 16 >= tile.rows) break;  // row blocks past the tile (uniform)
+        const float xs = pow2(rsh[rb * 16 + lr]);
+        float mx = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < NTH; ++nt)
+        for (int nt = 0; nt < NTH; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = glu(acc[nt][rb][i] * xs, acc[nt + NTH][rb][i] * xs, a.round_ops, a.geglu);
-          hv[rb][nt][i] = col_ok ? v : 0.f;
-          mx = fmaxf(mx, fabsf(hv[rb][nt][i]));
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      if (lg == 0) rmax[wave][rb * 16 + lr] = mx;
-    }
+          for (int i = 0; i < 4; ++i) {
+            const float v = glu_t<decltype(mode)::value, decltype(gelu)::value>(acc[nt][rb][i] * xs,
+                                                                              acc[nt + NTH][rb][i] * xs);
+            hv[rb][nt][i] = col_ok ? v : 0.f;
+            mx = fmaxf(mx, fabsf(hv[rb][nt][i]));
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        if (lg == 0) rmax[wave][rb * 16 + lr] = mx;
+      }
+    });
     __syncthreads();
     if (!col_ok) return;
 #pragma unroll
