@@ -117,11 +117,14 @@ typedef struct {
   const void *w;
   const void *scales;
   const void *biases;
-  /* Optional (NULL: none), affine formats only: the same codes in the
-   * tile-packed layout that moe_pack_weights writes.  When set, the grouped
-   * matrix-core kernels of moe_forward, moe_expert_ffn and moe_backward read
-   * their weights from here (the same bytes in another order: results are
-   * bit-identical); w is still required, for the other kernels. */
+  /* Optional (NULL: none), affine formats only: the tile-packed copy that
+   * moe_pack_weights writes (codes, scales and biases rearranged).  When
+   * set, the grouped matrix-core kernels of moe_forward, moe_expert_ffn and
+   * moe_backward read their codes from here; the forward's gate/up kernel
+   * also takes its scales and group terms from it for the matrices whose
+   * flag is set (see moe_pack_weights), which changes the rounding (not the
+   * bound) of its results.  w, scales and biases are still required, for
+   * the other kernels. */
   const void *w_packed;
 } moe_proj;
 
@@ -142,29 +145,44 @@ typedef enum {
 } moe_projection;
 
 /*
- * Tile-packed copy of an affine projection's codes.  The grouped kernels
- * multiply tiles of 16 weight rows and stream the reduction in slabs of 128
- * columns; in the stored layout a slab of a tile is 16 pieces of 64 (4-bit)
- * or 128 (8-bit) bytes, one per row, 1 KB or more apart.  The packed layout
- * puts each (tile, slab) in one contiguous block:
- *   packed[m][t][s][r][j] = w[m][16 t + r][SW s + j]   (uint32 words)
- * for matrix m < E+S, tile t < N/16, slab s < ceil(K/128), row r < 16 and
- * j < SW = 128*b/32 (16 words for 4-bit, 32 for 8-bit codes), zero where
- * SW s + j >= K*b/32 (a last slab of 64 columns).  N and K as in moe_proj.
- * It is an addition for callers that keep a second copy of the codes (on a
- * 288 GB device the copy is cheap next to the time it saves: the 2048-token
- * prefill layer 412.6 -> 393.9 us, the 32-token decode 111.7 -> 106.6 us).
+ * Tile-packed copy of an affine projection.  The grouped kernels multiply
+ * tiles of 16 weight rows and stream the reduction in slabs of 128 columns;
+ * in the stored layout a slab of a tile is 16 pieces of 64 (4-bit) or 128
+ * (8-bit) bytes, one per row, 1 KB or more apart.  The packed copy holds four
+ * regions, each starting at a multiple of 256 bytes, in this order (M = E+S
+ * matrices, N and K as in moe_proj, G = K/group_size groups per row,
+ * nslab = ceil(K/128), SW = 128*b/32 words, GPS = 128/group_size,
+ * GP = G rounded up to a multiple of 32, z = 8 for 4-bit and 128 for 8-bit
+ * codes):
+ *   codes[m][t][s][r][j] = w[m][16 t + r][SW s + j]   uint32, zero past the row;
+ *   scales[m][t][s][r][i] = fp16(s), s the scale of row 16 t + r, group GPS s + i;
+ *   groups[m][t][r][g]    = fp16((b - 1024 s - n2) * group_size) for row
+ *                           16 t + r and group g (scale s, bias b), with
+ *                           n2 = fp16(-(1024 + z) s);
+ *   flags[m]  int32 1 when every scale of matrix m is 0 or an fp16 value in
+ *             [2^-14, 32] and every group term is finite and below 2^15 in
+ *             magnitude, else 0
+ * (scales and group terms zero past the last group).  For matrices with the
+ * flag set, the forward's gate/up kernel expands a code q to
+ * fp16(s*(1024 + q) + n2) = fp16(s*(q - z) + delta), which is one fma and
+ * keeps the rounding error of s*q + b, and adds the rest of every weight of
+ * the group, b - 1024 s - n2, as one fp16 matrix-core product of the group
+ * terms with the group means of x.  The sum is the same
+ * (scale*q + bias) * x, rounded in other places.  The copy is an addition for
+ * callers that keep a second copy of the weights (on a 288 GB device it is
+ * cheap next to the time it saves).
  *
  * moe_packed_bytes: *bytes = size of the packed copy of projection `proj`
  * for all E+S matrices.  MOE_E_UNSUPPORTED for dense weights, MOE_E_INVALID
  * for a bad descriptor or a projection the descriptor does not use.
- * moe_pack_weights: enqueue the repacking of `w` (device, the stored layout)
- * into `w_packed` (device, moe_packed_bytes bytes, 16-byte aligned) on
- * `stream`; no host wait, no allocation.
+ * moe_pack_weights: enqueue the packing of `w`, `scales` and `biases`
+ * (device, the stored layouts of that projection) into `w_packed` (device,
+ * moe_packed_bytes bytes, 16-byte aligned) on `stream`; no host wait, no
+ * allocation.  MOE_E_INVALID for a null or misaligned pointer.
  */
 int moe_packed_bytes(const moe_layer_desc *desc, int32_t proj, size_t *bytes);
-int moe_pack_weights(const moe_layer_desc *desc, int32_t proj, const void *w, void *w_packed,
-                     void *stream);
+int moe_pack_weights(const moe_layer_desc *desc, int32_t proj, const void *w, const void *scales,
+                     const void *biases, void *w_packed, void *stream);
 
 /* Bytes of workspace that moe_dispatch, moe_expert_ffn and moe_forward need
  * for this layer at T tokens (also valid for any smaller T).  Returns

@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void t1_gateup_kernel(T1Args a) {
   // the token's experts (wave 0) and the fp16 staging row of x (wave 1)
   if (wave == 0) {
     select_token<MPL>(0, a.partials, a.n_chunks, a.bias, 1, a.E, a.K, a.renorm, s_idx, s_w, nullptr, D, nullptr,
-                      nullptr, false, nullptr);
+                      nullptr, false, XgOut{nullptr, 0, 0}, nullptr);
   } else if (wave == 1) {
     row_to_f16(a.x, D, xs, &s_xsh, a.x_f16 != 0);
   } else {

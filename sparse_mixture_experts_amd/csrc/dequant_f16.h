@@ -62,4 +62,32 @@ __device__ __forceinline__ f16x8 q8_words_to_f16(uint32_t w0, uint32_t w1, h2 s2
   return __builtin_bit_cast(f16x8, r);
 }
 
+// The expansions of the tile-packed fast path: 8 fp16 values
+// round(s*(q - z) + delta), z = 8 (4-bit) or 128 (8-bit), each from one fma
+// on 1024 + q with the addend n2 = round(-(1024 + z) s) (one pk_mul of s by
+// the exact constant); the fma forms s*(1024 + q) + n2 = s*(q - z) + delta
+// exactly (delta = n2 + (1024 + z) s, |delta| <= |s|) and rounds once.  The
+// rest of each weight, b - 1024 s - n2, is the same for the whole group and
+// enters as a separate product with the group sums of the activations.
+// Order q0,q4,q1,q5,q2,q6,q3,q7 as above; every 4-bit code is shifted to the
+// low nibble of its half (three shifts), so that all use the same n2.
+__device__ __forceinline__ f16x8 q4_word_to_f16_c(uint32_t w, h2 s2, h2 n2, uint32_t magic) {
+  const uint32_t c[4] = {(w & 0x000f000fu) | magic, ((w >> 4) & 0x000f000fu) | magic,
+                         ((w >> 8) & 0x000f000fu) | magic, ((w >> 12) & 0x000f000fu) | magic};
+  h2 r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = __builtin_elementwise_fma(__builtin_bit_cast(h2, c[j]), s2, n2);
+  return __builtin_bit_cast(f16x8, r);
+}
+__device__ __forceinline__ f16x8 q8_words_to_f16_c(uint32_t w0, uint32_t w1, h2 s2, h2 n2, uint32_t mg) {
+  const uint32_t t0 = __builtin_amdgcn_perm(w1, w0, 0x05010400u);  // q0, q4, q1, q5
+  const uint32_t t1 = __builtin_amdgcn_perm(w1, w0, 0x07030602u);  // q2, q6, q3, q7
+  const uint32_t c[4] = {__builtin_amdgcn_perm(mg, t0, 0x04010400u), __builtin_amdgcn_perm(mg, t0, 0x04030402u),
+                         __builtin_amdgcn_perm(mg, t1, 0x04010400u), __builtin_amdgcn_perm(mg, t1, 0x04030402u)};
+  h2 r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = __builtin_elementwise_fma(__builtin_bit_cast(h2, c[j]), s2, n2);
+  return __builtin_bit_cast(f16x8, r);
+}
+
 }  // namespace moe

@@ -8,6 +8,7 @@
 #pragma once
 
 #include "device_common.h"
+#include "moe_internal.h"
 
 namespace moe {
 
@@ -66,10 +67,39 @@ __device__ __forceinline__ float absmax8(uint4 v, bool f16) {
   return f16 ? absmax8_t<kDtF16>(v) : absmax8_t<kDtBF16>(v);
 }
 
+// The group means (XgOut): each group's sum in fp32 over its fp16 staged
+// values, so |mean| stays within the row's largest |value|.
+// Called by every lane of the wave at once: lane's piece p (8 staged values
+// in any order; valid false: past the row) goes into its group's sum over the
+// gs / 8 lanes that hold the group, and the group's first lane writes the mean.
+__device__ __forceinline__ void group_mean_piece(uint4 o, bool valid, int p, const XgOut &xo, uint16_t *row) {
+  const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+  float s = 0.f;
+  if (valid) {
+    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, o.x), one2, s, false);
+    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, o.y), one2, s, false);
+    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, o.z), one2, s, false);
+    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, o.w), one2, s, false);
+  }
+  const int lpg = xo.gs / 8;  // lanes per group: 4, 8 or 16 (groups never straddle a pass)
+  s += __shfl_xor(s, 1, kWave);
+  s += __shfl_xor(s, 2, kWave);
+  if (lpg >= 8) s += __shfl_xor(s, 4, kWave);
+  if (lpg >= 16) s += __shfl_xor(s, 8, kWave);
+  if (valid && (lane_id() & (lpg - 1)) == 0) {
+    const _Float16 m = static_cast<_Float16>(s * (1.0f / float(xo.gs)));
+    row[p * 8 / xo.gs] = __builtin_bit_cast(uint16_t, m);
+  }
+}
+__device__ __forceinline__ void group_mean_pad(int D, const XgOut &xo, uint16_t *row) {
+  for (int g = D / xo.gs + lane_id(); g < xo.gp; g += kWave) row[g] = 0;
+}
+
 // One wave converts row x[0..D) (bf16, or fp16 when f16 is set; D a
 // multiple of 8) to out[0..D) in the staging format and writes its exponent
-// to *sh_out (lane 0).
-__device__ __forceinline__ void row_to_f16(const uint16_t *x, int D, uint16_t *out, int8_t *sh_out, bool f16) {
+// to *sh_out (lane 0), and the row's group means to row t of xo when set.
+__device__ __forceinline__ void row_to_f16(const uint16_t *x, int D, uint16_t *out, int8_t *sh_out, bool f16,
+                                           XgOut xo = {nullptr, 0, 0}, int t = 0) {
   const int lane = lane_id();
   const uint4 *src = reinterpret_cast<const uint4 *>(x);
   uint4 *dst = reinterpret_cast<uint4 *>(out);
@@ -78,7 +108,18 @@ __device__ __forceinline__ void row_to_f16(const uint16_t *x, int D, uint16_t *o
   for (int p = lane; p < P; p += kWave) mx = fmaxf(mx, absmax8(src[p], f16));
   mx = wave_max(mx);
   const int sh = f16_shift(mx);
-  for (int p = lane; p < P; p += kWave) dst[p] = permute8(half8_to_f16(src[p], sh, f16));
+  uint16_t *xrow = xo.xg ? xo.xg + int64_t(t) * xo.gp : nullptr;
+  for (int p0 = 0; p0 < P; p0 += kWave) {  // the same trip count on every lane
+    const int p = p0 + lane;
+    const bool ok = p < P;
+    uint4 o = make_uint4(0u, 0u, 0u, 0u);
+    if (ok) {
+      o = permute8(half8_to_f16(src[p], sh, f16));
+      dst[p] = o;
+    }
+    if (xrow) group_mean_piece(o, ok, p, xo, xrow);
+  }
+  if (xrow) group_mean_pad(D, xo, xrow);
   if (lane == 0) *sh_out = int8_t(sh);
 }
 
@@ -94,7 +135,8 @@ __device__ __forceinline__ void row_f16_load(const uint16_t *x, int D, RowF16 &r
 #pragma unroll
   for (int q = 0; q < 8; ++q) r.v[q] = reinterpret_cast<const uint4 *>(x)[min(q * kWave + lane, D / 8 - 1)];
 }
-__device__ __forceinline__ void row_f16_store(const RowF16 &r, int D, uint16_t *out, int8_t *sh_out, bool f16) {
+__device__ __forceinline__ void row_f16_store(const RowF16 &r, int D, uint16_t *out, int8_t *sh_out, bool f16,
+                                              XgOut xo = {nullptr, 0, 0}, int t = 0) {
   const int lane = lane_id();
   float mx = 0.f;
 #pragma unroll
@@ -102,10 +144,19 @@ __device__ __forceinline__ void row_f16_store(const RowF16 &r, int D, uint16_t *
     if ((q * kWave + lane) * 8 < D) mx = fmaxf(mx, absmax8(r.v[q], f16));
   mx = wave_max(mx);
   const int sh = f16_shift(mx);
+  uint16_t *xrow = xo.xg ? xo.xg + int64_t(t) * xo.gp : nullptr;
 #pragma unroll
-  for (int q = 0; q < 8; ++q)
-    if ((q * kWave + lane) * 8 < D)
-      reinterpret_cast<uint4 *>(out)[q * kWave + lane] = permute8(half8_to_f16(r.v[q], sh, f16));
+  for (int q = 0; q < 8; ++q) {
+    if (q * kWave * 8 >= D) break;  // the same on every lane
+    const bool ok = (q * kWave + lane) * 8 < D;
+    uint4 o = make_uint4(0u, 0u, 0u, 0u);
+    if (ok) {
+      o = permute8(half8_to_f16(r.v[q], sh, f16));
+      reinterpret_cast<uint4 *>(out)[q * kWave + lane] = o;
+    }
+    if (xrow) group_mean_piece(o, ok, q * kWave + lane, xo, xrow);
+  }
+  if (xrow) group_mean_pad(D, xo, xrow);
   if (lane == 0) *sh_out = int8_t(sh);
 }
 

@@ -64,13 +64,13 @@ constexpr int kLdsRow = kKS + 8;           // padded LDS row (16-bit elements): 
 static_assert(kNRows == kThreads, "one scale row per thread");
 static_assert(kKS == 32 * 4, "a lane's 4 reduction blocks of 32 span the slab");
 
-// x [T][D] (bf16, or fp16 when x_f16) -> fp16 staging copy (row_to_f16), one
-// wave per token.
+// x [T][D] (bf16, or fp16 when x_f16) -> fp16 staging copy (row_to_f16) and
+// its group means when xo.xg is set, one wave per token.
 __global__ __launch_bounds__(256) void act_f16_kernel(const uint16_t *x, int T, int D, uint16_t *x16,
-                                                      int8_t *xsh, int x_f16) {
+                                                      int8_t *xsh, int x_f16, XgOut xo) {
   const int t = blockIdx.x * (256 / kWave) + int(threadIdx.x) / kWave;
   if (t >= T) return;  // whole waves
-  row_to_f16(x + int64_t(t) * D, D, x16 + int64_t(t) * D, xsh + t, x_f16 != 0);
+  row_to_f16(x + int64_t(t) * D, D, x16 + int64_t(t) * D, xsh + t, x_f16 != 0, xo, t);
 }
 
 struct GemmArgs {
@@ -99,6 +99,13 @@ struct GemmArgs {
   // affine: tile-packed copies of w0 / w1 (moe_pack_weights), or null; set
   // together (w1's when gate and up are separate)
   const uint32_t *wp0 = nullptr, *wp1 = nullptr;
+  // gate/up on packed copies: their fp16 scales, group terms and flags, and
+  // the group means of the staged token rows ([T][gp] fp16); xg null: the
+  // fast path is off
+  const uint16_t *sp0 = nullptr, *sp1 = nullptr, *bp0 = nullptr, *bp1 = nullptr;
+  const int32_t *fl0 = nullptr, *fl1 = nullptr;
+  const uint16_t *xg = nullptr;
+  int gp = 0;
 };
 
 // Column blocks per group of the work order (item_tile_block): whole rows of
@@ -136,7 +143,10 @@ constexpr int kDown = 0, kGateUp = 1, kGateUpRaw = 2;
 // Per-lane weight data of one slab (32 reduction elements per tile): 4-bit
 // -> one uint4 (4 words) per tile; 8-bit -> two; 16-bit dense -> four.
 template <int QB>
-struct WSlab { uint4 w[kNT][is_affine(QB) ? QB / 4 : kSteps]; };
+struct WSlab {
+  uint4 w[kNT][is_affine(QB) ? QB / 4 : kSteps];
+  uint32_t s[kNT];  // fast path: the lane's fp16 scale of each tile
+};
 
 // GATEUP: gate/up projection with the GLU epilogue writing h, else down
 // projection writing y rows.  QB: affine code width 4 or 8 (fp16 MFMA), or
@@ -241,6 +251,35 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
                   : static_cast<const void *>(static_cast<const uint16_t *>(wsrc(up)) + wr * K);
     }
   }
+  // The fast path: gate/up on packed copies whose matrices all
+  // carry the flag (and with the token group sums at hand).  Each wave's
+  // tiles are addressed through their wave-uniform tile index, so only the
+  // lane's offset inside a (tile, slab) block lives in a vector register.
+  bool fast = false;
+  if constexpr (AFF && GATEUP) {
+    if (packed && a.xg)
+      fast = __builtin_amdgcn_readfirstlane(a.fl0[tile.expert] != 0 && (a.fused || a.fl1[tile.expert] != 0));
+  }
+  int ptile[kNT];
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt)
+    ptile[nt] = __builtin_amdgcn_readfirstlane(int(wrow_of(col_c + (nt % NTH) * 16, GATEUP && nt >= NTH) >> 4));
+  constexpr int kGPS = GPS;
+  const uint32_t lane_w = uint32_t(lr * SW + lg * (AFF ? QB : 0));  // words
+  const uint32_t lane_s = uint32_t(lr * kGPS + lg / kLPG);          // fp16 scales
+  auto load_slab_fast = [&](int s, WSlab<QB> &dst) {
+    s = sbeg + min(s, nslab - 1);
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      const bool second = GATEUP && !a.fused && nt >= NTH;
+      const int64_t blk = int64_t(ptile[nt]) * nslab_all + s;
+      const uint32_t *cb = (second ? a.wp1 : a.wp0) + blk * (16 * SW);
+#pragma unroll
+      for (int v = 0; v < (AFF ? QB / 4 : 1); ++v) dst.w[nt][v] = *reinterpret_cast<const uint4 *>(cb + lane_w + 4 * v);
+      dst.s[nt] = (second ? a.sp1 : a.sp0)[blk * (16 * kGPS) + lane_s];
+    }
+  };
+
   // Slab s of this lane's rows.  The last slab may hold only 64 elements
   // (K = 64 mod 128): its second half is read from a clamped address and
   // multiplied by zero scales (affine) or zeroed activations (dense).
@@ -304,7 +343,8 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
   uint4 stg[PPT];
   uint16_t sraw[GPS][2];
   int stg_sh[PPT];  // affine down: h exponents of the staged rows' slab
-  auto stage_load = [&](int s) {
+  auto stage_load = [&](int s, auto fast_tag) {
+    constexpr bool FAST = decltype(fast_tag)::value;
     s = sbeg + min(s, nslab - 1);
     const int k = s * kKS + piece * 8;
 #pragma unroll
@@ -319,7 +359,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
       }
       if constexpr (AFF && !GATEUP) stg_sh[p] = a.act_sh[(src_off[p] / K) * a.nblk + s];
     }
-    if constexpr (AFF) {
+    if constexpr (AFF && !FAST) {
 #pragma unroll
       for (int g = 0; g < GPS; ++g) {
         const int gg = s * GPS + g;
@@ -333,7 +373,8 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
   };
   // Writes the staged slab to LDS buffer `buf`; returns nonzero when the slab
   // carries an exponent (h rows of the down projection, or weight rows).
-  auto stage_write = [&](int buf) -> int {
+  auto stage_write = [&](int buf, auto fast_tag) -> int {
+    constexpr bool FAST = decltype(fast_tag)::value;
     Slab<RB, GPS> &S = sm[buf];
     int flag = 0;
 #pragma unroll
@@ -346,7 +387,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
         flag |= sh;
       }
     }
-    if constexpr (AFF) {
+    if constexpr (AFF && !FAST) {
       float sv[GPS], bv[GPS], wm = 0.f;
 #pragma unroll
       for (int g = 0; g < GPS; ++g) {
@@ -400,9 +441,44 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
   // NRB row blocks.  Row blocks past the tile's rows but below NRB are
   // multiplied too (their results are never stored), which keeps the body
   // free of branches.
-  auto compute_slab = [&](const Slab<RB, GPS> &S, const WSlab<QB> &ws, auto nrb_tag) {
+  auto compute_slab = [&](const Slab<RB, GPS> &S, const WSlab<QB> &ws, auto nrb_tag, auto fast_tag) {
     constexpr int NRB = decltype(nrb_tag)::value;
-    if constexpr (AFF) {
+    constexpr bool FAST = decltype(fast_tag)::value;
+    if constexpr (AFF && FAST) {
+      // round(s*(q - z) + delta) per weight (the rest of each weight was
+      // added by bias_term)
+      constexpr float kOff = QB == 8 ? -1152.0f : -1032.0f;  // -(1024 + z), exact in fp16
+      const h2 moff = {(_Float16)kOff, (_Float16)kOff};
+      h2 s2[kNT], n2[kNT];
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        const _Float16 sv = __builtin_bit_cast(_Float16, uint16_t(ws.s[nt]));
+        s2[nt] = h2{sv, sv};
+        n2[nt] = s2[nt] * moff;
+      }
+#pragma unroll
+      for (int j = 0; j < kSteps; ++j) {
+        f16x8 bx[NRB];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+          bx[rb] = *reinterpret_cast<const f16x8 *>(&S.a[rb * 16 + lr][lg * 32 + j * 8]);
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+          f16x8 aw;
+          if constexpr (QB == 4) {
+            const uint4 &q = ws.w[nt][0];
+            const uint32_t wd = j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
+            aw = q4_word_to_f16_c(wd, s2[nt], n2[nt], magic);
+          } else {
+            const uint4 &q = ws.w[nt][j >> 1];
+            aw = (j & 1) ? q8_words_to_f16_c(q.z, q.w, s2[nt], n2[nt], magic)
+                         : q8_words_to_f16_c(q.x, q.y, s2[nt], n2[nt], magic);
+          }
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) acc[nt][rb] = mfma_f16(aw, bx[rb], acc[nt][rb]);
+        }
+      }
+    } else if constexpr (AFF) {
       const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
       h2 s2[kNT], s2_16[kNT], b2[kNT];
 #pragma unroll
@@ -470,16 +546,68 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
   // whether any did (the tile's results are then discarded); 16-row tiles
   // vote at every barrier and give up at the first such slab (fewer
   // registers live across the loop: three waves per SIMD).
+  // The fast path's group term, added to the (zero) accumulators before the
+  // slabs: for every output (weight row n, token row m) the sum over groups g
+  // of c_g(n) X_g(m), c_g = b - 1024 s - n2 the part of the group's weights
+  // left out of the expansion and X_g the group sum of the staged token row,
+  // as one fp16 matrix-core product of c_g * group (packed) with X_g / group
+  // (the x group sums), both rounded once to fp16.
+  auto bias_term = [&]() {
+    int btok[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int m = rb * 16 + lr;
+      int tk = 0;  // rows past the tile read token 0 (never stored)
+      if (m < tile.rows) {
+        const int q = tile.row0 + m;
+        const int t = q < a.N ? a.row_map[q] : (q - a.N) % a.T;
+        tk = unsigned(t) < unsigned(a.T) ? t : 0;
+      }
+      btok[rb] = tk;
+    }
+    const int gp = a.gp;
+    for (int c = 0; c < gp; c += 32) {
+      // every load of the chunk first (one memory round trip), then the products
+      f16x8 xb[RB], av[kNT];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        xb[rb] = *reinterpret_cast<const f16x8 *>(a.xg + int64_t(btok[rb]) * gp + c + 8 * lg);
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        const bool second = GATEUP && !a.fused && nt >= NTH;
+        av[nt] = *reinterpret_cast<const f16x8 *>((second ? a.bp1 : a.bp0) + (int64_t(ptile[nt]) * 16 + lr) * gp +
+                                                  c + 8 * lg);
+      }
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[nt][rb] = mfma_f16(av[nt], xb[rb], acc[nt][rb]);
+    }
+  };
+
   constexpr int PDS = QB == 4 ? 2 : 1;
   constexpr bool kLateVote = RB > 1;
-  auto run = [&](auto slow_tag, auto nrb_tag) __attribute__((always_inline)) -> bool {
+  auto run = [&](auto slow_tag, auto nrb_tag, auto fast_tag) __attribute__((always_inline)) -> bool {
     constexpr bool SLOW = decltype(slow_tag)::value;
-    constexpr bool VOTE = SLOW || !kLateVote;  // vote at every barrier
+    constexpr bool FAST = decltype(fast_tag)::value;  // no exponents: no votes
+    constexpr bool VOTE = !FAST && (SLOW || !kLateVote);  // vote at every barrier
     WSlab<QB> wb[PDS];
-    stage_load(0);
-    int flag = stage_write(0);
+    auto load_w = [&](int s, WSlab<QB> &dst) {
+      if constexpr (FAST) load_slab_fast(s, dst);
+      else load_slab(s, dst);
+    };
+    stage_load(0, fast_tag);
+    int flag;
+    if constexpr (FAST) {
 #pragma unroll
-    for (int u = 0; u < PDS; ++u) load_slab(u, wb[u]);
+      for (int u = 0; u < PDS; ++u) load_w(u, wb[u]);
+      bias_term();
+      flag = stage_write(0, fast_tag);
+    } else {
+      flag = stage_write(0, fast_tag);
+#pragma unroll
+      for (int u = 0; u < PDS; ++u) load_w(u, wb[u]);
+    }
     if constexpr (VOTE) flag = __syncthreads_or(flag);
     else __syncthreads();
     if (!SLOW && VOTE && flag) return true;
@@ -487,21 +615,21 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
 #pragma unroll
       for (int u = 0; u < PDS; ++u) {
         const int s = s0 + u, buf = s & 1;
-        stage_load(s + 1);
+        stage_load(s + 1, fast_tag);
         if (SLOW && flag && col_ok) rescale(sm[buf], -1);
-        if (col_ok && s < nslab) compute_slab(sm[buf], wb[u], nrb_tag);
-        load_slab(s + PDS, wb[u]);
+        if (col_ok && s < nslab) compute_slab(sm[buf], wb[u], nrb_tag, fast_tag);
+        load_w(s + PDS, wb[u]);
         if (SLOW && flag && col_ok) rescale(sm[buf], +1);
         if constexpr (VOTE) {
-          flag = __syncthreads_or(stage_write(buf ^ 1));
+          flag = __syncthreads_or(stage_write(buf ^ 1, fast_tag));
           if (!SLOW && flag) return true;
         } else {
-          flag |= stage_write(buf ^ 1);
+          flag |= stage_write(buf ^ 1, fast_tag);
           __syncthreads();
         }
       }
     }
-    if constexpr (VOTE || !AFF) return false;
+    if constexpr (VOTE || !AFF || FAST) return false;
     else return __syncthreads_or(flag) != 0;
   };
   // The fast loop multiplies only the row blocks that hold rows of the tile
@@ -510,22 +638,30 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs &a) {
   // its registers.
   using Full = std::integral_constant<int, RB>;
   constexpr bool kPerCount = RB == 4 && !(QB == 4 && GPS == 4 && !GATEUP);
-  bool redo;
-  if constexpr (kPerCount) {
-    const int nrb = min(RB, (tile.rows + 15) / 16);
-    if (nrb == 4) redo = run(std::false_type{}, Full{});
-    else if (nrb == 3) redo = run(std::false_type{}, std::integral_constant<int, 3>{});
-    else if (nrb == 2) redo = run(std::false_type{}, std::integral_constant<int, 2>{});
-    else redo = run(std::false_type{}, std::integral_constant<int, 1>{});
+  auto run_counts = [&](auto fast_tag) -> bool {
+    if constexpr (kPerCount) {
+      const int nrb = min(RB, (tile.rows + 15) / 16);
+      if (nrb == 4) return run(std::false_type{}, Full{}, fast_tag);
+      if (nrb == 3) return run(std::false_type{}, std::integral_constant<int, 3>{}, fast_tag);
+      if (nrb == 2) return run(std::false_type{}, std::integral_constant<int, 2>{}, fast_tag);
+      return run(std::false_type{}, std::integral_constant<int, 1>{}, fast_tag);
+    } else {
+      return run(std::false_type{}, Full{}, fast_tag);
+    }
+  };
+  bool redo = false;
+  if constexpr (AFF && GATEUP) {
+    if (fast) run_counts(std::true_type{});
+    else redo = run_counts(std::false_type{});
   } else {
-    redo = run(std::false_type{}, Full{});
+    redo = run_counts(std::false_type{});
   }
   if (redo) {
     if constexpr (AFF) {
       // Every wave left the fast loop at the same vote, after its last read
       // of the slab buffers.
       zero_acc();
-      run(std::true_type{}, Full{});
+      run(std::true_type{}, Full{}, std::false_type{});
     }
   }
 
@@ -1322,10 +1458,27 @@ int plan_tile_rows(const moe_layer_desc *d, int32_t T) {
 // The tile-packed copies, when the caller gave every one the projection
 // needs (gate and up both, when separate).
 // p1: the up projection when gate and up are separate, else null.
-static void set_packed(const moe_layer_desc *d, GemmArgs &g, const moe_proj &p0, const moe_proj *p1) {
+// proj0/proj1: their moe_projection values.  xg (nullable): the token group
+// means (XgOut), which turn on the fast path of gate/up.
+static void set_packed(const moe_layer_desc *d, GemmArgs &g, const moe_proj &p0, const moe_proj *p1, int proj0,
+                       int proj1, const uint16_t *xg = nullptr) {
   if (!affine(d) || !p0.w_packed || (p1 && !p1->w_packed)) return;
-  g.wp0 = static_cast<const uint32_t *>(p0.w_packed);
-  g.wp1 = p1 ? static_cast<const uint32_t *>(p1->w_packed) : nullptr;
+  PackedLayout L0, L1;
+  if (!packed_layout(d, proj0, &L0) || (p1 && !packed_layout(d, proj1, &L1))) return;
+  auto at = [](const void *base, size_t off) { return static_cast<const unsigned char *>(base) + off; };
+  g.wp0 = reinterpret_cast<const uint32_t *>(at(p0.w_packed, L0.codes));
+  g.wp1 = p1 ? reinterpret_cast<const uint32_t *>(at(p1->w_packed, L1.codes)) : nullptr;
+  if (!xg || L0.GP != xg_groups_padded(d)) return;
+  g.sp0 = reinterpret_cast<const uint16_t *>(at(p0.w_packed, L0.scales));
+  g.bp0 = reinterpret_cast<const uint16_t *>(at(p0.w_packed, L0.biases));
+  g.fl0 = reinterpret_cast<const int32_t *>(at(p0.w_packed, L0.flags));
+  if (p1) {
+    g.sp1 = reinterpret_cast<const uint16_t *>(at(p1->w_packed, L1.scales));
+    g.bp1 = reinterpret_cast<const uint16_t *>(at(p1->w_packed, L1.biases));
+    g.fl1 = reinterpret_cast<const int32_t *>(at(p1->w_packed, L1.flags));
+  }
+  g.xg = xg;
+  g.gp = L0.GP;
 }
 
 void launch_gate_up_raw_mfma(const moe_layer_desc *d, int32_t T, const void *x, const int32_t *row_map,
@@ -1337,14 +1490,15 @@ void launch_gate_up_raw_mfma(const moe_layer_desc *d, int32_t T, const void *x, 
   const int qb = d->w_format == MOE_WF_AFFINE_Q8 ? 8 : aff ? 4 : f16 ? kDenseF16 : kDenseBF16;
   if (aff && !sc.x16_ready)
     launch(act_f16_kernel, dim3((T + 3) / 4), dim3(256), 0, s, static_cast<const uint16_t *>(x), T,
-                       d->d_model, static_cast<uint16_t *>(sc.x16), sc.xsh, int(f16));
+                       d->d_model, static_cast<uint16_t *>(sc.x16), sc.xsh, int(f16), XgOut{nullptr, 0, 0});
   const moe_proj &pg = d->gate_up_fused ? w->gate_up : w->gate;
   GemmArgs g{aff ? sc.x16 : x, sc.xsh, nullptr, 0, row_map, T, T * d->top_k, d->d_model, d->d_ff,
              d->gate_up_fused, 0, 0, int(f16),
              pg.w, static_cast<const uint16_t *>(pg.scales), static_cast<const uint16_t *>(pg.biases),
              w->up.w, static_cast<const uint16_t *>(w->up.scales), static_cast<const uint16_t *>(w->up.biases),
              counters, tiles, gu, use_bx_major(d, T), 1, 0};
-  set_packed(d, g, pg, d->gate_up_fused ? nullptr : &w->up);
+  set_packed(d, g, pg, d->gate_up_fused ? nullptr : &w->up, d->gate_up_fused ? MOE_PROJ_GATE_UP : MOE_PROJ_GATE,
+             MOE_PROJ_UP);
   if (plan_tile_rows(d, T) == 16) launch_gemm<kGateUpRaw, 1>(g, qb, d->group_size, max_tiles, s);
   else launch_gemm<kGateUpRaw, 4>(g, qb, d->group_size, max_tiles, s);
 }
@@ -1362,9 +1516,12 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
   const int tr = plan_tile_rows(d, T);
   const int nblk = (d->d_ff + kHBlock - 1) / kHBlock;
   const int bx_major = use_bx_major(d, T);
+  // the group means of x for the fast gate/up path: written with the fp16
+  // staging copy, by the router (x16_ready) or here
+  const XgOut xo = xg_out(d, sc.xg);
   if (aff && !sc.x16_ready) {
     launch(act_f16_kernel, dim3((T + 3) / 4), dim3(256), 0, s, static_cast<const uint16_t *>(x), T,
-                       d->d_model, static_cast<uint16_t *>(sc.x16), sc.xsh, int(f16));
+                       d->d_model, static_cast<uint16_t *>(sc.x16), sc.xsh, int(f16), xo);
     if (mk) mk->mark("x_f16");
   }
   const moe_proj &pg = d->gate_up_fused ? w->gate_up : w->gate;
@@ -1379,8 +1536,9 @@ void launch_expert_ffn_mfma(const moe_layer_desc *d, int32_t T, const void *x, c
               w->down.w, static_cast<const uint16_t *>(w->down.scales), static_cast<const uint16_t *>(w->down.biases),
               nullptr, nullptr, nullptr, counters, tiles, y_sorted, bx_major, down_parts,
               (int64_t(T) * d->top_k + int64_t(d->n_shared) * T) * d->d_model};
-  set_packed(d, gu, pg, d->gate_up_fused ? nullptr : &w->up);
-  set_packed(d, dn, w->down, nullptr);
+  set_packed(d, gu, pg, d->gate_up_fused ? nullptr : &w->up, d->gate_up_fused ? MOE_PROJ_GATE_UP : MOE_PROJ_GATE,
+             MOE_PROJ_UP, xo.xg);
+  set_packed(d, dn, w->down, nullptr, MOE_PROJ_DOWN, MOE_PROJ_DOWN);
   if (decode_tiles(d, T)) {
     // at most one routed row per expert on average: whole-K loads per wave
     // (one memory round trip), h as bf16 between the two projections

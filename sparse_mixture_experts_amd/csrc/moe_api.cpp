@@ -32,7 +32,7 @@ T *at(void *ws, size_t off) {
 
 FfnScratch ffn_scratch(void *ws, const Workspace &L, bool x16_ready) {
   return FfnScratch{at<void>(ws, L.h), at<int8_t>(ws, L.hsh), at<void>(ws, L.x16), at<int8_t>(ws, L.xsh),
-                    x16_ready};
+                    x16_ready, at<uint16_t>(ws, L.xg)};
 }
 
 int check_ws(const moe_layer_desc *d, int32_t T, const void *ws, size_t ws_bytes, Workspace *out) {
@@ -77,7 +77,7 @@ int moe_route(const moe_layer_desc *desc, int32_t T, const void *x, const void *
   if ((s = check_ws(desc, T, ws, ws_bytes, &L))) return s;
   if (T == 0) return MOE_OK;
   launch_route(desc, T, x, w_router, router_bias, topk_idx, topk_w, at<float>(ws, L.route), nullptr, nullptr,
-               FusedDispatch{}, stream);
+               nullptr, FusedDispatch{}, stream);
   return hip_status();
 }
 
@@ -161,7 +161,7 @@ static int forward_impl(const moe_layer_desc *desc, int32_t T, const void *x, co
                           at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles), 64,
                           plan_tile_rows(desc, T), desc->n_shared, at<int32_t>(ws, L.dsp)};
   launch_route(desc, T, x, w->w_router, w->router_bias, idx, wt, at<float>(ws, L.route), at<void>(ws, L.x16),
-               at<int8_t>(ws, L.xsh), dsp, stream, mk);
+               at<int8_t>(ws, L.xsh), at<uint16_t>(ws, L.xg), dsp, stream, mk);
   if (!route_fuses_dispatch(desc, T))
     launch_dispatch(desc, T, idx, 64, dsp.order, dsp.inv_order, dsp.row_map, dsp.expert_off, dsp.tile_off,
                     dsp.counters, dsp.act_items, dsp.tiles, at<int32_t>(ws, L.dsp), stream, mk,
@@ -236,18 +236,22 @@ int moe_packed_bytes(const moe_layer_desc *desc, int32_t proj, size_t *bytes) {
   if ((s = validate_desc(desc))) return s;
   if (!bytes) return MOE_E_INVALID;
   if (!affine(desc)) return MOE_E_UNSUPPORTED;
-  const int64_t words = packed_words(desc, proj);
-  if (words < 0) return MOE_E_INVALID;
-  *bytes = size_t(words) * 4;
+  PackedLayout L;
+  if (!packed_layout(desc, proj, &L)) return MOE_E_INVALID;
+  *bytes = L.total;
   return MOE_OK;
 }
 
-int moe_pack_weights(const moe_layer_desc *desc, int32_t proj, const void *w, void *w_packed, void *stream) {
+int moe_pack_weights(const moe_layer_desc *desc, int32_t proj, const void *w, const void *scales,
+                     const void *biases, void *w_packed, void *stream) {
   size_t bytes = 0;
   int s;
   if ((s = moe_packed_bytes(desc, proj, &bytes))) return s;
-  if ((s = validate_ptr(w)) || (s = validate_ptr(w_packed))) return s;
-  launch_pack(desc, proj, static_cast<const uint32_t *>(w), static_cast<uint32_t *>(w_packed), stream);
+  if ((s = validate_ptr(w)) || (s = validate_ptr(scales)) || (s = validate_ptr(biases)) ||
+      (s = validate_ptr(w_packed)))
+    return s;
+  launch_pack(desc, proj, static_cast<const uint32_t *>(w), static_cast<const uint16_t *>(scales),
+              static_cast<const uint16_t *>(biases), w_packed, stream);
   return hip_status();
 }
 
@@ -276,7 +280,7 @@ int moe_backward(const moe_layer_desc *desc, int32_t T, const void *x, const moe
   FusedDispatch counts_only{};
   counts_only.counts = at<int32_t>(ws, L.dsp);
   launch_route(desc, T, x, w->w_router, w->router_bias, idx, wt, at<float>(ws, L.route), at<void>(ws, L.x16),
-               at<int8_t>(ws, L.xsh), counts_only, stream);
+               at<int8_t>(ws, L.xsh), nullptr, counts_only, stream);
   launch_dispatch(desc, T, idx, plan_tile_rows(desc, T), at<int32_t>(ws, L.order), at<int32_t>(ws, L.inv_order),
                   at<int32_t>(ws, L.row_map), at<int32_t>(ws, L.expert_off), at<int32_t>(ws, L.tile_off),
                   at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles),

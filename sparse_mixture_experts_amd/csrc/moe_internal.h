@@ -62,14 +62,46 @@ int validate_T(int32_t T);
 int validate_ptr(const void *p, bool may_be_null = false);
 int validate_weights(const moe_layer_desc *d, const moe_weights *w, bool need_router,
                      bool need_experts);
-// Rows N and reduction K of a moe_projection (false: not used by the layer),
-// and the uint32 words of its tile-packed copy for all E+S matrices (-1:
-// not used).
+// Rows N and reduction K of a moe_projection (false: not used by the layer).
 bool proj_shape(const moe_layer_desc *d, int32_t proj, int *N, int *K);
-int64_t packed_words(const moe_layer_desc *d, int32_t proj);
-// Repack the codes w[E+S][N][K*b/32] of one projection into the tile-packed
-// layout (see moe_pack_weights).
-void launch_pack(const moe_layer_desc *d, int32_t proj, const uint32_t *w, uint32_t *w_packed, void *stream);
+// The tile-packed copy of one projection for all M = E+S matrices, in four
+// 256-byte aligned regions (byte offsets from its start):
+//   codes   [M][N/16][nslab][16][SW] uint32: the codes of each (16-row tile,
+//           128-column slab) in one block (zero past the row);
+//   scales  [M][N/16][nslab][16][GPS] fp16: the scale s of each (row, group
+//           of the slab), converted exactly (zero past the last group);
+//   groups  [M][N/16][16][GP] fp16: each row's group terms in tile blocks,
+//           round((b - 1024 s - n2) * group), n2 = round(-(1024 + z) s) with
+//           z = 8 (4-bit) or 128 (8-bit) (zero past the last group);
+//   flags   [M] int32: 1 when every scale of the matrix is 0 or an fp16
+//           value in [2^-14, 32] and every group term is finite and below
+//           2^15 in magnitude before rounding.
+// nslab = ceil(K/128), SW = 128*b/32, GPS = 128/group, GP = G rounded up to
+// a multiple of 32 (G = K/group).  For matrices with the flag set the
+// gate/up kernel expands codes to round(s (q - z) + delta) and adds the
+// group terms as one fp16 matrix-core product with the group means of x.
+struct PackedLayout {
+  int N, K, nslab, SW, GPS, G, GP;
+  size_t codes, scales, biases, flags, total;
+};
+bool packed_layout(const moe_layer_desc *d, int32_t proj, PackedLayout *out);
+// Write the tile-packed copy of one projection (codes w[E+S][N][K*b/32],
+// scales and biases [E+S][G][N]) into w_packed (see moe_pack_weights).
+void launch_pack(const moe_layer_desc *d, int32_t proj, const uint32_t *w, const uint16_t *scales,
+                 const uint16_t *biases, void *w_packed, void *stream);
+// Group entries per token row of the x group means (G rounded up to 32).
+int xg_groups_padded(const moe_layer_desc *d);
+// Where the kernels that write the fp16 staging copy of x also put its group
+// means, for the fast gate/up path: row t of xg (gp entries) holds, for each
+// group of gs staged values, fp16(sum / gs), and zero past the last group.
+// xg null: not written.
+struct XgOut {
+  uint16_t *xg;
+  int gs, gp;
+};
+// The destination for this layer (xg null unless the layer is affine on the
+// matrix cores and xg is given).
+XgOut xg_out(const moe_layer_desc *d, uint16_t *xg);
 
 inline int64_t act_bytes(const moe_layer_desc *d) { return d->act_dtype == MOE_DT_F32 ? 4 : 2; }
 // Affine 4- or 8-bit expert weights (fp16 matrix-core path with fp16 staging).
@@ -98,6 +130,7 @@ struct Workspace {
   size_t h;                           // [N+S*T][d_ff] h_bytes (one token: [k+S][d_ff] fp32)
   size_t hsh;                         // [N+S*T][ceil(d_ff/128)] int8 (affine layers)
   size_t x16, xsh;                    // [T][d_model] fp16, [T] int8 (affine layers)
+  size_t xg;                          // [T][GP] fp16 group means of x16 (affine matrix-core layers)
   size_t y_sorted;                    // [N+S*T][d_model]: fp16 (ys_f16e), fp32, or [parts] fp32 partial rows
   size_t ys_sh;                       // [N+S*T][d_model/64] int8 exponents (ys_f16e)
   size_t total;
@@ -122,7 +155,7 @@ int64_t route_mfma_scratch_floats(const moe_layer_desc *d, int32_t T);
 // counts (nullable): the dispatch's per-segment expert counts [B][E+1] for
 // segments of seg slots, zeroed and then written here (integer atomics).
 void launch_route_mfma(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router, const float *bias,
-                       int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh, void *stream,
+                       int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh, XgOut xo, void *stream,
                        StageMarker *mk, int32_t *counts = nullptr, int seg = 0);
 // Outputs of a dispatch that the router's selection kernel performs itself
 // (order == nullptr: none).
@@ -141,9 +174,10 @@ struct FusedDispatch {
 // dsp.order set and route_fuses_dispatch true it also does the dispatch.
 bool route_writes_x16(const moe_layer_desc *d);
 bool route_fuses_dispatch(const moe_layer_desc *d, int32_t T);
+// xg (nullable): the group means of the staging rows go there too.
 void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router,
                   const float *bias, int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh,
-                  const FusedDispatch &dsp, void *stream, StageMarker *mk = nullptr);
+                  uint16_t *xg, const FusedDispatch &dsp, void *stream, StageMarker *mk = nullptr);
 
 // One-token router logits as canonical-order chunk partials [C][1][E] (no
 // selection); returns C.
@@ -187,6 +221,7 @@ struct FfnScratch {
   void *x16;
   int8_t *xsh;
   bool x16_ready;  // x16/xsh already written (by the router)
+  uint16_t *xg = nullptr;  // group means of x16 (written by the expert FFN when the packed weights allow)
 };
 constexpr int kHBlock = 128;  // h columns per exponent block
 

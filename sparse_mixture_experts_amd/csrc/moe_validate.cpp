@@ -82,12 +82,41 @@ bool proj_shape(const moe_layer_desc *d, int32_t proj, int *N, int *K) {
   }
 }
 
-int64_t packed_words(const moe_layer_desc *d, int32_t proj) {
-  int N = 0, K = 0;
-  if (!proj_shape(d, proj, &N, &K)) return -1;
+static size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+bool packed_layout(const moe_layer_desc *d, int32_t proj, PackedLayout *out) {
+  PackedLayout L{};
+  if (!affine(d) || !proj_shape(d, proj, &L.N, &L.K)) return false;
   const int b = d->w_format == MOE_WF_AFFINE_Q8 ? 8 : 4;
-  const int64_t nslab = (K + 127) / 128, sw = 128 * b / 32;
-  return int64_t(d->n_experts + d->n_shared) * N * nslab * sw;
+  const int64_t M = int64_t(d->n_experts) + d->n_shared;
+  L.nslab = (L.K + 127) / 128;
+  L.SW = 128 * b / 32;
+  L.GPS = 128 / d->group_size;
+  L.G = L.K / d->group_size;
+  L.GP = (L.G + 31) / 32 * 32;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L.codes = take(size_t(M) * L.N * L.nslab * L.SW * 4);
+  L.scales = take(size_t(M) * L.N * L.nslab * L.GPS * 2);
+  L.biases = take(size_t(M) * L.N * L.GP * 2);
+  L.flags = take(size_t(M) * 4);
+  L.total = o;
+  *out = L;
+  return true;
+}
+
+int xg_groups_padded(const moe_layer_desc *d) {
+  const int G = d->d_model / d->group_size;
+  return (G + 31) / 32 * 32;
+}
+
+XgOut xg_out(const moe_layer_desc *d, uint16_t *xg) {
+  if (!xg || !affine(d) || !use_mfma(d)) return XgOut{nullptr, 0, 0};
+  return XgOut{xg, d->group_size, xg_groups_padded(d)};
 }
 
 int validate_weights(const moe_layer_desc *d, const moe_weights *w, bool need_router,
@@ -109,8 +138,6 @@ int validate_weights(const moe_layer_desc *d, const moe_weights *w, bool need_ro
   }
   return MOE_OK;
 }
-
-static size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 Workspace workspace_layout(const moe_layer_desc *d, int32_t T) {
   Workspace ws{};
@@ -145,6 +172,7 @@ Workspace workspace_layout(const moe_layer_desc *d, int32_t T) {
   ws.hsh = take(q4 ? size_t(rows) * ((d->d_ff + kHBlock - 1) / kHBlock) : 0);
   ws.x16 = take(q4 ? size_t(T) * d->d_model * 2 : 0);
   ws.xsh = take(q4 ? size_t(T) : 0);
+  ws.xg = take(q4 && use_mfma(d) ? size_t(T) * xg_groups_padded(d) * 2 : 0);
   ws.y_sorted = take(size_t(ys_workspace_bytes(d, T)));
   ws.ys_sh = take(use_mfma(d) ? size_t(rows) * (d->d_model / kYsBlock) : 0);
   ws.total = o;

@@ -206,13 +206,13 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(const float *__r
                                                                 const float *__restrict__ bias, int T, int E,
                                                                 int K, int renorm, int32_t *__restrict__ idx_out,
                                                                 float *__restrict__ w_out, const uint16_t *x, int D,
-                                                                uint16_t *x16, int8_t *xsh, int x_f16,
+                                                                uint16_t *x16, int8_t *xsh, int x_f16, XgOut xo,
                                                                 FusedDispatch dsp) {
   __shared__ int32_t s_f[kTinyFusedMaxN];
   __shared__ int32_t s_cnt[kMaxExperts];
   const int t = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
   if (t < T) select_token<MPL>(t, in, n_chunks, bias, T, E, K, renorm, idx_out, w_out, x, D, x16, xsh, x_f16,
-                               dsp.order ? s_f : nullptr);
+                               xo, dsp.order ? s_f : nullptr);
   if (dsp.order) {
     __syncthreads();
     if (threadIdx.x < kWave)
@@ -222,14 +222,14 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(const float *__r
 }
 
 void launch_select(const float *in, int n_chunks, const float *bias, int T, int E, int K, int renorm,
-                   int32_t *idx, float *w, const void *x, int D, void *x16, int8_t *xsh, bool x_f16,
+                   int32_t *idx, float *w, const void *x, int D, void *x16, int8_t *xsh, bool x_f16, XgOut xo,
                    const FusedDispatch &dsp, hipStream_t s) {
   const dim3 grid((T + kThreads / kWave - 1) / (kThreads / kWave)), block(kThreads);
   const uint16_t *xb = static_cast<const uint16_t *>(x);
-  uint16_t *xo = static_cast<uint16_t *>(x16);
+  uint16_t *x16o = static_cast<uint16_t *>(x16);
   auto go = [&](auto kern) {
-    launch(kern, grid, block, 0, s, in, n_chunks, bias, T, E, K, renorm, idx, w, xb, D, xo, xsh,
-                       int(x_f16), dsp);
+    launch(kern, grid, block, 0, s, in, n_chunks, bias, T, E, K, renorm, idx, w, xb, D, x16o, xsh,
+                       int(x_f16), xo, dsp);
   };
   if (E <= 64) go(route_select_kernel<1>);
   else if (E <= 128) go(route_select_kernel<2>);
@@ -298,13 +298,14 @@ int launch_route_chunks_t1(const moe_layer_desc *d, const void *x, const void *w
 
 void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router,
                   const float *bias, int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh,
-                  const FusedDispatch &dsp_in, void *stream, StageMarker *mk) {
+                  uint16_t *xg, const FusedDispatch &dsp_in, void *stream, StageMarker *mk) {
   if (!route_writes_x16(d)) x16 = nullptr, xsh = nullptr;
+  const XgOut xo = xg_out(d, x16 ? xg : nullptr);
   FusedDispatch dsp = dsp_in;
   if (!route_fuses_dispatch(d, T)) dsp.order = nullptr;
   if (route_mfma_applies(d, T)) {
     const bool counts = dsp.counts && route_counts_dispatch(d, T);
-    launch_route_mfma(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, stream, mk, counts ? dsp.counts : nullptr,
+    launch_route_mfma(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, xo, stream, mk, counts ? dsp.counts : nullptr,
                       counts ? int(dispatch_segment_slots(d, T)) : 0);
     return;
   }
@@ -347,7 +348,7 @@ void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void 
   else logits(std::integral_constant<int, kDtF32>{});
   if (mk) mk->mark("route_logits");
   launch_select(scratch, n_chunks, bias, T, E, d->top_k, d->renormalize, idx, w, x, D, x16, xsh,
-                d->act_dtype == MOE_DT_F16, dsp, s);
+                d->act_dtype == MOE_DT_F16, xo, dsp, s);
   if (mk) mk->mark(dsp.order ? "route_select_dispatch" : "route_select");
 }
 

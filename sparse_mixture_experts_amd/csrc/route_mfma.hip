@@ -266,6 +266,7 @@ struct CertArgs {
   float *w_out;
   uint16_t *x16;  // nullable: fp16 staging copy of x for the 4-bit GEMMs
   int8_t *xsh;
+  XgOut xo;       // and its group means (xo.xg nullable)
   int32_t *counts;  // nullable: dispatch counts [N / seg][E + 1] of the slots' experts, per segment of seg slots
   int seg;
 };
@@ -321,7 +322,7 @@ __global__ __launch_bounds__(kThreads) void router_certify_kernel(CertArgs a) {
     }
   }
   xs = wave_sum(xs);
-  if (a.x16) row_f16_store(xr, D, a.x16 + int64_t(t) * D, a.xsh + t, DT == kDtF16);  // xr dies here
+  if (a.x16) row_f16_store(xr, D, a.x16 + int64_t(t) * D, a.xsh + t, DT == kDtF16, a.xo, t);  // xr dies here
   wn = wave_max(wn);
   bmax = wave_max(bmax);
   const float bound = a.gamma * (sqrtf(xs) * sqrtf(wn) * 1.001f + bmax);
@@ -512,7 +513,7 @@ int64_t route_mfma_scratch_floats(const moe_layer_desc *d, int32_t T) {
 namespace {
 template <int DT>
 void launch_route_mfma_t(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router, const float *bias,
-                         int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh, hipStream_t s,
+                         int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh, XgOut xo, hipStream_t s,
                          StageMarker *mk, int32_t *counts, int seg) {
   const int D = d->d_model, E = d->n_experts, nkb = (D + 255) / 256, C = D / kChunk;
   const int64_t N = int64_t(T) * d->top_k;
@@ -534,7 +535,7 @@ void launch_route_mfma_t(const moe_layer_desc *d, int32_t T, const void *x, cons
   // for fp16.
   const float gamma = float((DT == kDtF16 ? 384 : 256) + 2 * C) * 5.9604645e-8f;
   CertArgs ca{static_cast<const uint16_t *>(x), wt, bias, lt, normp + int64_t(nkb) * E, T, D, E, d->top_k, nz,
-              gamma, idx, w, static_cast<uint16_t *>(x16), xsh, counts, seg};
+              gamma, idx, w, static_cast<uint16_t *>(x16), xsh, xo, counts, seg};
   const dim3 grid((T + kThreads / kWave - 1) / (kThreads / kWave)), block(kThreads);
   if (E <= 64) launch((router_certify_kernel<1, DT>), grid, block, 0, s, ca);
   else if (E <= 128) launch((router_certify_kernel<2, DT>), grid, block, 0, s, ca);
@@ -547,14 +548,14 @@ void launch_route_mfma_t(const moe_layer_desc *d, int32_t T, const void *x, cons
 }  // namespace
 
 void launch_route_mfma(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router, const float *bias,
-                       int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh, void *stream,
+                       int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh, XgOut xo, void *stream,
                        StageMarker *mk, int32_t *counts, int seg) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (counts && seg <= 0) counts = nullptr;
   if (d->act_dtype == MOE_DT_F16)
-    launch_route_mfma_t<kDtF16>(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, s, mk, counts, seg);
+    launch_route_mfma_t<kDtF16>(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, xo, s, mk, counts, seg);
   else
-    launch_route_mfma_t<kDtBF16>(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, s, mk, counts, seg);
+    launch_route_mfma_t<kDtBF16>(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, xo, s, mk, counts, seg);
 }
 
 }  // namespace moe

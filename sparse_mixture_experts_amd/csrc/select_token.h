@@ -18,7 +18,7 @@ __device__ __forceinline__ void select_token(int t, const float *__restrict__ in
                                              const float *__restrict__ bias, int T, int E, int K, int renorm,
                                              int32_t *__restrict__ idx_out, float *__restrict__ w_out,
                                              const uint16_t *x, int D, uint16_t *x16, int8_t *xsh, bool x_f16,
-                                             int32_t *s_f) {
+                                             XgOut xo, int32_t *s_f) {
   // chunk partials per load batch: about 64 loads in flight per lane
   constexpr int CB = MPL >= 64 ? 1 : 64 / MPL;
   const int lane = lane_id();
@@ -86,7 +86,7 @@ __device__ __forceinline__ void select_token(int t, const float *__restrict__ in
     w_out[int64_t(t) * K + lane] = w;
     if (s_f) s_f[t * K + lane] = my_e;
   }
-  if (x16) row_f16_store(xr, D, x16 + int64_t(t) * D, xsh + t, x_f16);
+  if (x16) row_f16_store(xr, D, x16 + int64_t(t) * D, xsh + t, x_f16, xo, t);
 }
 
 }  // namespace

@@ -79,7 +79,7 @@ def load() -> ctypes.CDLL:
         lib.moe_backward_workspace_size.argtypes = [P(LayerDesc), i32, P(sz)]
         lib.moe_backward.argtypes = [P(LayerDesc), i32, vp, P(Weights), vp, vp, vp, sz, vp]
         lib.moe_packed_bytes.argtypes = [P(LayerDesc), i32, P(sz)]
-        lib.moe_pack_weights.argtypes = [P(LayerDesc), i32, vp, vp, vp]
+        lib.moe_pack_weights.argtypes = [P(LayerDesc), i32, vp, vp, vp, vp, vp]
         lib.moe_status_string.argtypes = [ctypes.c_int]
         lib.moe_status_string.restype = ctypes.c_char_p
         for name in EXPORTED:
@@ -213,10 +213,11 @@ def moe_packed_bytes(desc: LayerDesc, proj: int) -> int:
     return out.value
 
 
-def moe_pack_weights(desc, proj: int, w, w_packed, stream=None):
-    """Enqueue the tile-packed copy of projection `proj`'s codes `w` into `w_packed`."""
-    _check(load().moe_pack_weights(ctypes.byref(desc), proj, _ptr(w), _ptr(w_packed), _stream(stream)),
-           "moe_pack_weights")
+def moe_pack_weights(desc, proj: int, w, scales, biases, w_packed, stream=None):
+    """Enqueue the tile-packed copy of projection `proj` (codes `w`, `scales`,
+    `biases`) into `w_packed` (moe_packed_bytes bytes)."""
+    _check(load().moe_pack_weights(ctypes.byref(desc), proj, _ptr(w), _ptr(scales), _ptr(biases), _ptr(w_packed),
+                                   _stream(stream)), "moe_pack_weights")
 
 
 # ---- marshalling helpers ----------------------------------------------------
@@ -255,16 +256,15 @@ class DeviceWeights:
         return cls(to_device(layer["w_router"], device), bias, experts)
 
     def with_packed(self, desc: LayerDesc, stream=None) -> "DeviceWeights":
-        """The same weights plus a tile-packed copy of every affine projection's
-        codes (moe_pack_weights), which the grouped kernels then read."""
+        """The same weights plus the tile-packed copy of every affine projection
+        (moe_pack_weights), which the grouped kernels then read."""
         experts = {}
         for name, p in self.experts.items():
             q = dict(p)
             q.pop("w_packed", None)
             n = moe_packed_bytes(desc, _PROJ[name])
-            m = p["w"].shape[0]  # matrices (experts, routed then shared)
-            q["w_packed"] = torch.empty((m, n // 4 // m), dtype=torch.int32, device=p["w"].device)
-            moe_pack_weights(desc, _PROJ[name], p["w"], q["w_packed"], stream)
+            q["w_packed"] = torch.empty((n,), dtype=torch.uint8, device=p["w"].device)
+            moe_pack_weights(desc, _PROJ[name], p["w"], p["scales"], p["biases"], q["w_packed"], stream)
             experts[name] = q
         return DeviceWeights(self.w_router, self.router_bias, experts)
 
@@ -275,10 +275,16 @@ class DeviceWeights:
         return DeviceWeights(self.w_router.clone(), bias, experts)
 
     def nbytes(self, experts=None) -> int:
-        """Bytes of all weights, or of the listed expert ids only."""
+        """Bytes held for all weights, or for the listed expert ids only (a
+        packed copy counted in proportion)."""
         total = 0
         for p in self.experts.values():
-            for v in p.values():
-                per = v.numel() * v.element_size() // v.shape[0]
+            m = p["w"].shape[0]
+            for k, v in p.items():
+                size = v.numel() * v.element_size()
+                if k == "w_packed":  # one flat buffer for all m matrices
+                    total += size if experts is None else size * len(experts) // m
+                    continue
+                per = size // v.shape[0]
                 total += per * (v.shape[0] if experts is None else len(experts))
         return total

@@ -14,13 +14,19 @@ _TORCH_DT = {moe.MOE_DT_F32: torch.float32, moe.MOE_DT_BF16: torch.bfloat16, moe
 
 
 class GpuLayer:
-    def __init__(self, layer: dict):
+    """packed: give affine layers the tile-packed copy of their weights, as the
+    benchmark does (default), or only the stored layouts (False)."""
+
+    def __init__(self, layer: dict, packed: bool = True):
         self.spec = layer["spec"]
         self.layer = layer
         self.desc = moe.desc_from_spec(self.spec)
         self.x = moe.to_device(layer["x"], DEV)
         self.T = self.x.shape[0]
         self.w = moe.DeviceWeights.from_layer(layer, DEV)
+        if packed and self.spec.quantized:
+            self.w = self.w.with_packed(self.desc)
+            torch.cuda.synchronize()
         self.ws = torch.empty(moe.moe_workspace_size(self.desc, self.T), dtype=torch.uint8, device=DEV)
 
     @property

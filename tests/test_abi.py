@@ -190,25 +190,37 @@ def test_workspace_covers_smaller_T(shape):
         prev = size
 
 
+def _packed_size(M, N, K, bits, group):
+    """The documented regions, each rounded up to 256 bytes: codes
+    [M][N/16][slabs][16][SW] words, fp16 scales [M][N/16][slabs][16][128/group],
+    fp16 group terms [M][N/16][16][G rounded up to 32], int32 flags [M]."""
+    up = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    slabs = -(-K // 128)
+    G = K // group
+    return (up(M * N * slabs * (128 * bits // 32) * 4) + up(M * N * slabs * (128 // group) * 2)
+            + up(M * N * (-(-G // 32) * 32) * 2) + up(M * 4))
+
+
 def test_packed_bytes_and_validation(lib):
     size = ctypes.c_size_t()
     d = moe.make_desc(2048, 768, 128, 8, n_shared=2, wfmt="q4")
-    # [E+S][N/16 tiles][ceil(K/128) slabs][16 rows][16 words] = (E+S) * N * slabs * 16 words
     assert lib.moe_packed_bytes(ctypes.byref(d), moe.MOE_PROJ_GATE, ctypes.byref(size)) == moe.MOE_OK
-    assert size.value == 130 * 768 * 16 * 16 * 4
+    assert size.value == _packed_size(130, 768, 2048, 4, 64) == 115016448
     assert lib.moe_packed_bytes(ctypes.byref(d), moe.MOE_PROJ_DOWN, ctypes.byref(size)) == moe.MOE_OK
-    assert size.value == 130 * 2048 * 6 * 16 * 4
-    # 8-bit codes, a reduction of 64 mod 128 padded to a whole slab
-    d8 = moe.make_desc(320, 192, 4, 2, wfmt="q8", group_size=32, gate_up_fused=True)
+    assert size.value == _packed_size(130, 2048, 768, 4, 64)
+    # 8-bit codes, a reduction of 64 mod 128 padded to a whole slab, fp16
+    d8 = moe.make_desc(320, 192, 4, 2, act="f16", wfmt="q8", group_size=32, gate_up_fused=True)
     assert lib.moe_packed_bytes(ctypes.byref(d8), moe.MOE_PROJ_GATE_UP, ctypes.byref(size)) == moe.MOE_OK
-    assert size.value == 4 * 384 * 3 * 32 * 4
+    assert size.value == _packed_size(4, 384, 320, 8, 32)
     # a projection the layer does not use, dense weights, bad arguments
     assert lib.moe_packed_bytes(ctypes.byref(d), moe.MOE_PROJ_GATE_UP, ctypes.byref(size)) == moe.MOE_E_INVALID
     assert lib.moe_packed_bytes(ctypes.byref(d), 7, ctypes.byref(size)) == moe.MOE_E_INVALID
     dd = moe.make_desc(2048, 768, 128, 8)
     assert lib.moe_packed_bytes(ctypes.byref(dd), moe.MOE_PROJ_DOWN, ctypes.byref(size)) == moe.MOE_E_UNSUPPORTED
-    assert lib.moe_pack_weights(ctypes.byref(d), moe.MOE_PROJ_DOWN, A + 4, A, None) == moe.MOE_E_INVALID
-    assert lib.moe_pack_weights(ctypes.byref(d), moe.MOE_PROJ_DOWN, A, None, None) == moe.MOE_E_INVALID
+    assert lib.moe_pack_weights(ctypes.byref(d), moe.MOE_PROJ_DOWN, A + 4, A, A, A, None) == moe.MOE_E_INVALID
+    assert lib.moe_pack_weights(ctypes.byref(d), moe.MOE_PROJ_DOWN, A, A, A, None, None) == moe.MOE_E_INVALID
+    assert lib.moe_pack_weights(ctypes.byref(d), moe.MOE_PROJ_DOWN, A, None, A, A, None) == moe.MOE_E_INVALID
+    assert lib.moe_pack_weights(ctypes.byref(d), moe.MOE_PROJ_DOWN, A, A, A + 8, A, None) == moe.MOE_E_INVALID
     # a packed copy on a dense layer, or misaligned, is refused before anything runs
     w = weights()
     w.down = moe.Proj(A, None, None, A)
