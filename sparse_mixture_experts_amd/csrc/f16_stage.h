@@ -81,11 +81,14 @@ __device__ __forceinline__ void group_mean_piece(uint4 o, bool valid, int p, con
     s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, o.z), one2, s, false);
     s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, o.w), one2, s, false);
   }
-  const int lpg = xo.gs / 8;  // lanes per group: 4, 8 or 16 (groups never straddle a pass)
-  s += __shfl_xor(s, 1, kWave);
-  s += __shfl_xor(s, 2, kWave);
-  if (lpg >= 8) s += __shfl_xor(s, 4, kWave);
-  if (lpg >= 16) s += __shfl_xor(s, 8, kWave);
+  // sums over the gs / 8 lanes of the group (4, 8 or 16; groups never
+  // straddle a pass), on DPP lane moves: quads, then mirrored half rows, then
+  // mirrored rows
+  const int lpg = xo.gs / 8;
+  s += dpp_move<kDppQuadSwap1>(0.f, s);
+  s += dpp_move<kDppQuadSwap2>(0.f, s);
+  if (lpg >= 8) s += dpp_move<kDppHalfMirror>(0.f, s);
+  if (lpg >= 16) s += dpp_move<kDppRowMirror>(0.f, s);
   if (valid && (lane_id() & (lpg - 1)) == 0) {
     const _Float16 m = static_cast<_Float16>(s * (1.0f / float(xo.gs)));
     row[p * 8 / xo.gs] = __builtin_bit_cast(uint16_t, m);
