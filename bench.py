@@ -525,7 +525,55 @@ def calibrate_copy(mib: int):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
 
 
-def roofline(res):
+def measured_peaks():
+    """What this GPU reaches on plain streaming and dense work, measured in the
+    same run (context for the published peaks the rooflines use): the
+    library's streaming-read kernel over 1 GiB (8192 workgroups of 16-byte
+    loads) and over 600 MiB (one launch's size at the prefill gate/up), torch's
+    device copy of 1 GiB (read + write bytes), and a bf16 8192^3 matrix
+    product (torch.matmul on the vendor GEMM library); each the best of 3
+    timed rounds of 5 launches."""
+    import torch
+    from sparse_mixture_experts_amd import moe
+    dev = "cuda:0"
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+
+    def best_ms(fn, reps=5, rounds=3):
+        fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(rounds):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / reps)
+        return best
+
+    blocks = 8192
+    words = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    n600 = 600 << 20
+    read_ms = best_ms(lambda: moe.moe_stream_read(src, n, words, blocks))
+    read600_ms = best_ms(lambda: moe.moe_stream_read(src, n600, words, blocks))
+    copy_ms = best_ms(lambda: dst.copy_(src))
+    gemm_ms = best_ms(lambda: torch.matmul(a, b))
+    out = {"read_GBs": round(n / read_ms / 1e6, 1), "read_600MiB_GBs": round(n600 / read600_ms / 1e6, 1),
+           "copy_GBs": round(2 * n / copy_ms / 1e6, 1),
+           "bf16_gemm_TFLOPs": round(2 * 8192 ** 3 / gemm_ms / 1e9, 1),
+           "how": "moe_stream_read over 1 GiB and over 600 MiB (8192 workgroups, 16-byte loads), torch device "
+                  "copy of 1 GiB (read + write bytes), torch.matmul bf16 8192^3; best of 3 rounds of 5 launches"}
+    del src, dst, a, b, words
+    torch.cuda.empty_cache()
+    return out
+
+
+def roofline(res, peaks=None):
     """Roofline of the step's dominant kernel (the longest average launch):
     algorithmic bytes (or FLOPs for the vector-unit router) per launch over the
     launch's average duration from HIP events on the launch stream."""
@@ -546,6 +594,9 @@ def roofline(res):
     out = {"kernel": dom, "bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic, "avg_launch_us": round(km[dom] * 1e3, 2),
            "algorithmic_bytes_per_launch": kacc["bytes"]}
+    if peaks and peaks.get("read_GBs"):
+        # the same rate against what a plain streaming read reaches on this GPU
+        out["frac_of_measured_read"] = round(a / peaks["read_GBs"], 4)
     if "flops" in kacc:
         out["mfma_frac"] = round(kacc["flops"] / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
     if "intermediate_bytes" in kacc:
@@ -621,6 +672,8 @@ def main():
     from sparse_mixture_experts_amd import moe
     moe.load()
     hip = Hip()
+    peaks = measured_peaks()
+    log(f"[measured peaks] {peaks}")
 
     head = run_config(args.config, args.steps, args.warmup, not args.no_graph, hip)
     sweep = []
@@ -638,7 +691,7 @@ def main():
             "graph_ms_per_step": None if r["graph_ms"] is None else round(r["graph_ms"], 5),
             "sparse_dense_flop_ratio": round(r["acc"]["sparse_dense_flop_ratio"], 5),
             "kernel_us": {k: round(v * 1e3, 2) for k, v in r["kernel_ms"].items()},
-            "roofline": roofline(r)}
+            "roofline": roofline(r, peaks)}
         if not args.no_cpu_baseline and name in CPU_SAMPLE:
             entry["cpu_baseline"] = cpu_baseline(name, CPU_SAMPLE[name])
             if name in CPU_ONE_THREAD:
@@ -672,7 +725,8 @@ def main():
                            "touched_experts": head["touched"]},
         "sparse_dense_flop_ratio": round(head["acc"]["sparse_dense_flop_ratio"], 5),
         "kernel_us": {k: round(v * 1e3, 2) for k, v in head["kernel_ms"].items()},
-        "roofline": roofline(head),
+        "roofline": roofline(head, peaks),
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
         "sweep": sweep,
     }

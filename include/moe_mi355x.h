@@ -317,6 +317,19 @@ int moe_forward_noalloc(const moe_layer_desc *desc, int32_t T, const void *x,
                         const moe_weights *w, void *y, int32_t out_dtype,
                         int32_t *topk_idx_out, float *topk_w_out, void *stream);
 
+/*
+ * A plain streaming read, outside the layer: the rate a kernel of this
+ * library reaches when it only reads, the scale for the HBM rooflines of the
+ * weight-streaming kernels.  blocks workgroups of 256 threads read the
+ * `bytes` at src (device memory, 16-byte aligned, bytes a multiple of 16)
+ * with 16-byte loads, grid-stride, and each thread writes the XOR of the
+ * words it read to out[blocks * 256] (device memory, caller-owned).  Enqueued
+ * on `stream`; MOE_E_INVALID for a null pointer, a misaligned src, a size
+ * that is 0 or not a multiple of 16, or blocks outside [1, 65536];
+ * MOE_E_HIP if the launch fails.
+ */
+int moe_stream_read(const void *src, size_t bytes, uint32_t *out, int32_t blocks, void *stream);
+
 /* A static, human-readable name of a moe_status value. */
 const char *moe_status_string(int status);
 

@@ -23,7 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["moe_api.cpp", "moe_validate.cpp", "route.hip", "route_mfma.hip", "dispatch.hip", "ffn_gemv.hip",
            "ffn_mfma.hip", "combine.hip", "backward.hip",
-           "backward_mfma.hip", "forward_noalloc.hip", "decode_fused.hip", "pack.hip"]
+           "backward_mfma.hip", "forward_noalloc.hip", "decode_fused.hip", "pack.hip", "probe.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}"]

@@ -80,6 +80,7 @@ def load() -> ctypes.CDLL:
         lib.moe_backward.argtypes = [P(LayerDesc), i32, vp, P(Weights), vp, vp, vp, sz, vp]
         lib.moe_packed_bytes.argtypes = [P(LayerDesc), i32, P(sz)]
         lib.moe_pack_weights.argtypes = [P(LayerDesc), i32, vp, vp, vp, vp, vp]
+        lib.moe_stream_read.argtypes = [vp, sz, vp, i32, vp]
         lib.moe_status_string.argtypes = [ctypes.c_int]
         lib.moe_status_string.restype = ctypes.c_char_p
         for name in EXPORTED:
@@ -181,6 +182,12 @@ def moe_forward(desc, T, x, weights, y, out_dtype, topk_idx_out, topk_w_out, ws,
 def moe_forward_noalloc(desc, T, x, weights, y, out_dtype, topk_idx_out, topk_w_out, stream=None):
     _check(load().moe_forward_noalloc(ctypes.byref(desc), T, _ptr(x), ctypes.byref(weights.c), _ptr(y), out_dtype,
                                       _ptr(topk_idx_out), _ptr(topk_w_out), _stream(stream)), "moe_forward_noalloc")
+
+
+def moe_stream_read(src, nbytes, out, blocks, stream=None):
+    """The library's plain streaming read of nbytes of src (a measurement
+    kernel outside the layer); out holds blocks * 256 uint32 words."""
+    _check(load().moe_stream_read(_ptr(src), nbytes, _ptr(out), blocks, _stream(stream)), "moe_stream_read")
 
 
 def moe_forward_timed(desc, T, x, weights, y, out_dtype, topk_idx_out, topk_w_out, ws, events, stream=None):

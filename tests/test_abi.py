@@ -231,3 +231,15 @@ def test_packed_bytes_and_validation(lib):
     w.down = moe.Proj(A, A, A, A + 4)
     assert lib.moe_forward(ctypes.byref(d), 0, A, ctypes.byref(w), A, 1, None, None, A, ws_size(d, 0), None) == \
         moe.MOE_E_INVALID
+
+
+def test_stream_read_validation(lib):
+    # every case is rejected on the host before any launch
+    bad = moe.MOE_E_INVALID
+    assert lib.moe_stream_read(None, 16, ctypes.c_void_p(64), 1, None) == bad
+    assert lib.moe_stream_read(ctypes.c_void_p(64), 16, None, 1, None) == bad
+    assert lib.moe_stream_read(ctypes.c_void_p(64), 0, ctypes.c_void_p(64), 1, None) == bad
+    assert lib.moe_stream_read(ctypes.c_void_p(64), 24, ctypes.c_void_p(64), 1, None) == bad
+    assert lib.moe_stream_read(ctypes.c_void_p(72), 16, ctypes.c_void_p(64), 1, None) == bad
+    assert lib.moe_stream_read(ctypes.c_void_p(64), 16, ctypes.c_void_p(64), 0, None) == bad
+    assert lib.moe_stream_read(ctypes.c_void_p(64), 16, ctypes.c_void_p(64), 65537, None) == bad
