@@ -335,6 +335,33 @@ def _scaled_bf16_bits(bits: np.ndarray, shift: int) -> np.ndarray:
     return out
 
 
+@pytest.mark.parametrize("shift", [16, -16, 0])
+def test_one_token_h_range(shift):
+    """One-token layer with the up projection's affine scales and biases
+    times 2^shift exactly: h rows far above fp16's range (2^16 times their
+    usual size) or far below its normal range, which the down kernel stages
+    with nonzero per-row exponents; shift 0 as stored.  All must match the
+    oracle within tolerance."""
+    spec = MID["mid-q4-one-token-e256"]
+    L = inputs.gen_layer(spec)
+    up = dict(L["experts"]["up"])
+    for k in ("scales", "biases"):
+        up[k] = _scaled_bf16_bits(up[k], shift)
+    L = {**L, "experts": {**L["experts"], "up": up}}
+    print(f"[case] one token, up x 2^{shift}", flush=True)
+    g = GpuLayer(L)
+    y, idx, w = g.forward()
+    y, idx = y.cpu().numpy(), idx.cpu().numpy()
+    assert np.all(np.isfinite(y))
+    ry, ridx, _, _ = oracle.forward(pins.desc_of(spec), L["x"], L["w_router"], L["router_bias"], L["experts"])
+    assert np.array_equal(idx, ridx)
+    err = rel_err(y, ry)
+    print(f"[one token, up x 2^{shift}] max|err|/RMS = {err:.3g}", flush=True)
+    assert err <= tol_for(spec), err
+    del g
+    _layers.clear()
+
+
 @pytest.mark.parametrize("name,shift", [("mid-bf16", 24), ("mid-bf16", -24), ("mid-q4", 20), ("mid-q4", -20),
                                         ("mid-q4-g32-geglu-tile16", 20), ("mid-q4-decode", -20),
                                         ("mid-bf16-long-down", 24)])
