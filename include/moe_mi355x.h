@@ -134,6 +134,12 @@ typedef struct {
   moe_proj gate, up;         /* used when gate_up_fused == 0 */
   moe_proj gate_up;          /* used when gate_up_fused == 1 */
   moe_proj down;
+  /* Optional (NULL: none): the prepared router that moe_pack_router wrote
+   * from w_router.  When set, the matrix-core router (16-bit layers, T >= 64
+   * with T * n_experts >= 65536) reads it instead of transposing w_router
+   * on every call; routing results are the same.  w_router is still
+   * required. */
+  const void *w_router_packed;
 } moe_weights;
 
 /* Projections, for moe_packed_bytes and moe_pack_weights. */
@@ -183,6 +189,26 @@ typedef enum {
 int moe_packed_bytes(const moe_layer_desc *desc, int32_t proj, size_t *bytes);
 int moe_pack_weights(const moe_layer_desc *desc, int32_t proj, const void *w, const void *scales,
                      const void *biases, void *w_packed, void *stream);
+
+/*
+ * Prepared router ("MoE Optimization COMPLETE", "Optimization Technique": the
+ * router matmul on the GPU).  The matrix-core router multiplies the rows of
+ * the transposed router weight and bounds its rounding with the experts'
+ * weight norms; both depend on the weights only, so a caller whose router
+ * does not change can prepare them once.  The prepared router holds
+ *   wt[e][i]   = w_router[i][e], act_dtype, [n_experts][d_model];
+ *   then, from a multiple of 256 bytes, normp[kb][e] = sum of squares of
+ *   w_router[256 kb .. 256 kb + 255][e] (fp32, kb < ceil(d_model/256)), and
+ *   norms[e] = those partials summed in kb order (fp32).
+ * moe_router_packed_bytes: *bytes = its size; MOE_E_UNSUPPORTED for fp32
+ * layers and for d_model not a multiple of 64 or above 4096 (the layers the
+ * matrix-core router does not take), MOE_E_INVALID for a bad descriptor.
+ * moe_pack_router: enqueue its writing from `w_router` (device) into `out`
+ * (device, moe_router_packed_bytes bytes, 16-byte aligned) on `stream`; no
+ * host wait, no allocation; MOE_E_INVALID for a null or misaligned pointer.
+ */
+int moe_router_packed_bytes(const moe_layer_desc *desc, size_t *bytes);
+int moe_pack_router(const moe_layer_desc *desc, const void *w_router, void *out, void *stream);
 
 /* Bytes of workspace that moe_dispatch, moe_expert_ffn and moe_forward need
  * for this layer at T tokens (also valid for any smaller T).  Returns

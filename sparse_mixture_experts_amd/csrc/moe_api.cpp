@@ -161,7 +161,7 @@ static int forward_impl(const moe_layer_desc *desc, int32_t T, const void *x, co
                           at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles), 64,
                           plan_tile_rows(desc, T), desc->n_shared, at<int32_t>(ws, L.dsp)};
   launch_route(desc, T, x, w->w_router, w->router_bias, idx, wt, at<float>(ws, L.route), at<void>(ws, L.x16),
-               at<int8_t>(ws, L.xsh), at<uint16_t>(ws, L.xg), dsp, stream, mk);
+               at<int8_t>(ws, L.xsh), at<uint16_t>(ws, L.xg), dsp, stream, mk, w->w_router_packed);
   if (!route_fuses_dispatch(desc, T))
     launch_dispatch(desc, T, idx, 64, dsp.order, dsp.inv_order, dsp.row_map, dsp.expert_off, dsp.tile_off,
                     dsp.counters, dsp.act_items, dsp.tiles, at<int32_t>(ws, L.dsp), stream, mk,
@@ -231,6 +231,24 @@ int moe_forward_timed(const moe_layer_desc *desc, int32_t T, const void *x, cons
   return forward_impl(desc, T, x, w, y, out_dtype, topk_idx_out, topk_w_out, ws, ws_bytes, stream, &mk);
 }
 
+int moe_router_packed_bytes(const moe_layer_desc *desc, size_t *bytes) {
+  int s;
+  if ((s = validate_desc(desc))) return s;
+  if (!bytes) return MOE_E_INVALID;
+  if (!router_pack_applies(desc)) return MOE_E_UNSUPPORTED;
+  *bytes = router_packed_bytes(desc);
+  return MOE_OK;
+}
+
+int moe_pack_router(const moe_layer_desc *desc, const void *w_router, void *out, void *stream) {
+  size_t bytes = 0;
+  int s;
+  if ((s = moe_router_packed_bytes(desc, &bytes))) return s;
+  if ((s = validate_ptr(w_router)) || (s = validate_ptr(out))) return s;
+  launch_pack_router(desc, w_router, out, stream);
+  return hip_status();
+}
+
 int moe_packed_bytes(const moe_layer_desc *desc, int32_t proj, size_t *bytes) {
   int s;
   if ((s = validate_desc(desc))) return s;
@@ -280,7 +298,7 @@ int moe_backward(const moe_layer_desc *desc, int32_t T, const void *x, const moe
   FusedDispatch counts_only{};
   counts_only.counts = at<int32_t>(ws, L.dsp);
   launch_route(desc, T, x, w->w_router, w->router_bias, idx, wt, at<float>(ws, L.route), at<void>(ws, L.x16),
-               at<int8_t>(ws, L.xsh), nullptr, counts_only, stream);
+               at<int8_t>(ws, L.xsh), nullptr, counts_only, stream, nullptr, w->w_router_packed);
   launch_dispatch(desc, T, idx, plan_tile_rows(desc, T), at<int32_t>(ws, L.order), at<int32_t>(ws, L.inv_order),
                   at<int32_t>(ws, L.row_map), at<int32_t>(ws, L.expert_off), at<int32_t>(ws, L.tile_off),
                   at<int32_t>(ws, L.counters), at<PlanItem>(ws, L.act_items), at<PlanItem>(ws, L.tiles),

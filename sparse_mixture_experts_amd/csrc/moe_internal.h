@@ -151,12 +151,18 @@ struct StageMarker {
 int64_t route_scratch_floats(const moe_layer_desc *d, int32_t T);
 // Matrix-core router with exact recomputation of the candidates (large T).
 bool route_mfma_applies(const moe_layer_desc *d, int32_t T);
+// Prepared router for the matrix-core router (moe_pack_router): whether the
+// layer can use one, its size, where its norms start, and its packing.
+bool router_pack_applies(const moe_layer_desc *d);
+size_t router_packed_bytes(const moe_layer_desc *d);
+size_t router_packed_norms_offset(const moe_layer_desc *d);
+void launch_pack_router(const moe_layer_desc *d, const void *w_router, void *out, void *stream);
 int64_t route_mfma_scratch_floats(const moe_layer_desc *d, int32_t T);
 // counts (nullable): the dispatch's per-segment expert counts [B][E+1] for
 // segments of seg slots, zeroed and then written here (integer atomics).
 void launch_route_mfma(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router, const float *bias,
                        int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh, XgOut xo, void *stream,
-                       StageMarker *mk, int32_t *counts = nullptr, int seg = 0);
+                       StageMarker *mk, int32_t *counts = nullptr, int seg = 0, const void *packed = nullptr);
 // Outputs of a dispatch that the router's selection kernel performs itself
 // (order == nullptr: none).
 struct FusedDispatch {
@@ -177,7 +183,8 @@ bool route_fuses_dispatch(const moe_layer_desc *d, int32_t T);
 // xg (nullable): the group means of the staging rows go there too.
 void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router,
                   const float *bias, int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh,
-                  uint16_t *xg, const FusedDispatch &dsp, void *stream, StageMarker *mk = nullptr);
+                  uint16_t *xg, const FusedDispatch &dsp, void *stream, StageMarker *mk = nullptr,
+                  const void *router_packed = nullptr);
 
 // One-token router logits as canonical-order chunk partials [C][1][E] (no
 // selection); returns C.

@@ -126,6 +126,9 @@ int validate_weights(const moe_layer_desc *d, const moe_weights *w, bool need_ro
   if (need_router) {
     if ((s = validate_ptr(w->w_router))) return s;
     if ((s = validate_ptr(w->router_bias, true))) return s;
+    if ((s = validate_ptr(w->w_router_packed, true))) return s;
+    // a prepared router only where the matrix-core router can use one
+    if (w->w_router_packed && !router_pack_applies(d)) return MOE_E_INVALID;
   }
   if (need_experts) {
     if (d->gate_up_fused) {

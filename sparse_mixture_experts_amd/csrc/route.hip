@@ -298,7 +298,8 @@ int launch_route_chunks_t1(const moe_layer_desc *d, const void *x, const void *w
 
 void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router,
                   const float *bias, int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh,
-                  uint16_t *xg, const FusedDispatch &dsp_in, void *stream, StageMarker *mk) {
+                  uint16_t *xg, const FusedDispatch &dsp_in, void *stream, StageMarker *mk,
+                  const void *router_packed) {
   if (!route_writes_x16(d)) x16 = nullptr, xsh = nullptr;
   const XgOut xo = xg_out(d, x16 ? xg : nullptr);
   FusedDispatch dsp = dsp_in;
@@ -306,7 +307,7 @@ void launch_route(const moe_layer_desc *d, int32_t T, const void *x, const void 
   if (route_mfma_applies(d, T)) {
     const bool counts = dsp.counts && route_counts_dispatch(d, T);
     launch_route_mfma(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, xo, stream, mk, counts ? dsp.counts : nullptr,
-                      counts ? int(dispatch_segment_slots(d, T)) : 0);
+                      counts ? int(dispatch_segment_slots(d, T)) : 0, router_packed);
     return;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);

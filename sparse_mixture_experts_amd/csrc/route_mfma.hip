@@ -132,7 +132,9 @@ __global__ __launch_bounds__(kMfThreads) void router_mfma_kernel(const uint16_t 
                                                                  const uint16_t *__restrict__ wt,
                                                                  const float *__restrict__ bias,
                                                                  float *__restrict__ normp, int n_kb, int T,
-                                                                 int D, int E, float *__restrict__ lt) {
+                                                                 int D, int E, float *__restrict__ lt,
+                                                                 int norms_ready, int32_t *__restrict__ counts,
+                                                                 int n_counts) {
   __shared__ uint16_t sab[2][2][64][kChunk + 8];  // [buffer][expert tile, token tile][row][col]
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
   const int lr = lane & 15, lg = lane >> 4;
@@ -146,7 +148,11 @@ __global__ __launch_bounds__(kMfThreads) void router_mfma_kernel(const uint16_t 
   const int item = total % 8 == 0 ? (lin % 8) * (total / 8) + lin / 8 : lin;
   const int bx = item % nbx, by = (item / nbx) % nby, bz = item / (nbx * nby);
   const int e0 = bx * 64, t0 = by * 64;
-  if (by == 0 && bz == 0 && tid < 64 && e0 + tid < E) {
+  // with a prepared router the transpose kernel does not run: its other
+  // job, zeroing the dispatch counts that the certification adds to, is done
+  // here
+  for (int i = lin * kMfThreads + tid; i < n_counts; i += total * kMfThreads) counts[i] = 0;
+  if (!norms_ready && by == 0 && bz == 0 && tid < 64 && e0 + tid < E) {
     float s = 0.f;
     for (int kb = 0; kb < n_kb; ++kb) s += normp[int64_t(kb) * E + e0 + tid];
     normp[int64_t(n_kb) * E + e0 + tid] = s;
@@ -497,6 +503,46 @@ bool route_counts_dispatch(const moe_layer_desc *d, int32_t T) {
   return route_mfma_applies(d, T) && dispatch_segment_slots(d, T) > 0;
 }
 
+// Prepared router: WT [E][D] (16-bit), then, from router_packed_norms_offset,
+// the squared-norm partials [D/256][E] and their sums [E] (fp32), as the
+// transpose kernel and the logit kernel leave them in the scratch.
+bool router_pack_applies(const moe_layer_desc *d) {
+  return d->act_dtype != MOE_DT_F32 && d->d_model % kChunk == 0 && d->d_model <= kWave * kChunk;
+}
+size_t router_packed_norms_offset(const moe_layer_desc *d) {
+  return (size_t(d->n_experts) * d->d_model * 2 + 255) / 256 * 256;
+}
+size_t router_packed_bytes(const moe_layer_desc *d) {
+  const size_t nkb = (d->d_model + 255) / 256;
+  return router_packed_norms_offset(d) + (nkb + 1) * size_t(d->n_experts) * 4;
+}
+
+namespace {
+// The sums of the squared-norm partials, in partial order (the order the
+// logit kernel uses).
+__global__ __launch_bounds__(kThreads) void router_norm_sum_kernel(float *normp, int n_kb, int E) {
+  const int e = blockIdx.x * kThreads + threadIdx.x;
+  if (e >= E) return;
+  float s = 0.f;
+  for (int kb = 0; kb < n_kb; ++kb) s += normp[int64_t(kb) * E + e];
+  normp[int64_t(n_kb) * E + e] = s;
+}
+}  // namespace
+
+void launch_pack_router(const moe_layer_desc *d, const void *w_router, void *out, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int D = d->d_model, E = d->n_experts, nkb = (D + 255) / 256;
+  uint16_t *wt = static_cast<uint16_t *>(out);
+  float *normp = reinterpret_cast<float *>(static_cast<char *>(out) + router_packed_norms_offset(d));
+  if (d->act_dtype == MOE_DT_F16)
+    launch(router_transpose_kernel<kDtF16>, dim3((E + 63) / 64, nkb), dim3(kThreads), 0, s,
+           static_cast<const uint16_t *>(w_router), D, E, wt, normp, static_cast<int32_t *>(nullptr), 0);
+  else
+    launch(router_transpose_kernel<kDtBF16>, dim3((E + 63) / 64, nkb), dim3(kThreads), 0, s,
+           static_cast<const uint16_t *>(w_router), D, E, wt, normp, static_cast<int32_t *>(nullptr), 0);
+  launch(router_norm_sum_kernel, dim3((E + kThreads - 1) / kThreads), dim3(kThreads), 0, s, normp, nkb, E);
+}
+
 // Scratch: L~ [T][E] f32, then WT [E][D] (16-bit), then norm partials [D/256][E]
 // f32, each part starting on a 16-byte boundary (offsets in floats).
 static int64_t align4(int64_t v) { return (v + 3) & ~int64_t(3); }
@@ -514,19 +560,29 @@ namespace {
 template <int DT>
 void launch_route_mfma_t(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router, const float *bias,
                          int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh, XgOut xo, hipStream_t s,
-                         StageMarker *mk, int32_t *counts, int seg) {
+                         StageMarker *mk, int32_t *counts, int seg, const void *packed) {
   const int D = d->d_model, E = d->n_experts, nkb = (D + 255) / 256, C = D / kChunk;
   const int64_t N = int64_t(T) * d->top_k;
   const int n_counts = counts ? int((N + seg - 1) / seg * (E + 1)) : 0;
   float *lt = scratch;
   const int nz = route_mfma_splits(d);
   const int64_t o_wt = align4(nz * int64_t(T) * E), o_np = o_wt + align4((int64_t(E) * D + 1) / 2);
-  uint16_t *wt = reinterpret_cast<uint16_t *>(scratch + o_wt);
+  const uint16_t *wt = reinterpret_cast<uint16_t *>(scratch + o_wt);
   float *normp = scratch + o_np;
-  launch(router_transpose_kernel<DT>, dim3((E + 63) / 64, nkb), dim3(kThreads), 0, s,
-                     static_cast<const uint16_t *>(w_router), D, E, wt, normp, counts, n_counts);
-  launch(router_mfma_kernel<DT>, dim3((E + 63) / 64, (T + 63) / 64, nz), dim3(kMfThreads), 0, s,
-                     static_cast<const uint16_t *>(x), wt, bias, normp, nkb, T, D, E, lt);
+  if (packed) {
+    // the prepared router (moe_pack_router): the transposed weight and its
+    // summed norms, read in place; no transpose kernel
+    wt = static_cast<const uint16_t *>(packed);
+    normp = reinterpret_cast<float *>(const_cast<char *>(static_cast<const char *>(packed)) +
+                                      router_packed_norms_offset(d));
+    launch(router_mfma_kernel<DT>, dim3((E + 63) / 64, (T + 63) / 64, nz), dim3(kMfThreads), 0, s,
+           static_cast<const uint16_t *>(x), wt, bias, normp, nkb, T, D, E, lt, 1, counts, n_counts);
+  } else {
+    launch(router_transpose_kernel<DT>, dim3((E + 63) / 64, nkb), dim3(kThreads), 0, s,
+           static_cast<const uint16_t *>(w_router), D, E, const_cast<uint16_t *>(wt), normp, counts, n_counts);
+    launch(router_mfma_kernel<DT>, dim3((E + 63) / 64, (T + 63) / 64, nz), dim3(kMfThreads), 0, s,
+           static_cast<const uint16_t *>(x), wt, bias, normp, nkb, T, D, E, lt, 0, nullptr, 0);
+  }
   if (mk) mk->mark("route_mfma");
   // |L~ - L| <= gamma * S: the MFMAs of a chunk counted as 32 sequential
   // roundings each (two per chunk for bf16, eight for the fp16 head/tail
@@ -549,13 +605,14 @@ void launch_route_mfma_t(const moe_layer_desc *d, int32_t T, const void *x, cons
 
 void launch_route_mfma(const moe_layer_desc *d, int32_t T, const void *x, const void *w_router, const float *bias,
                        int32_t *idx, float *w, float *scratch, void *x16, int8_t *xsh, XgOut xo, void *stream,
-                       StageMarker *mk, int32_t *counts, int seg) {
+                       StageMarker *mk, int32_t *counts, int seg, const void *packed) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (counts && seg <= 0) counts = nullptr;
   if (d->act_dtype == MOE_DT_F16)
-    launch_route_mfma_t<kDtF16>(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, xo, s, mk, counts, seg);
+    launch_route_mfma_t<kDtF16>(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, xo, s, mk, counts, seg, packed);
   else
-    launch_route_mfma_t<kDtBF16>(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, xo, s, mk, counts, seg);
+    launch_route_mfma_t<kDtBF16>(d, T, x, w_router, bias, idx, w, scratch, x16, xsh, xo, s, mk, counts, seg,
+                                 packed);
 }
 
 }  // namespace moe

@@ -52,7 +52,7 @@ class Proj(ctypes.Structure):
 
 class Weights(ctypes.Structure):
     _fields_ = [("w_router", ctypes.c_void_p), ("router_bias", ctypes.c_void_p), ("gate", Proj),
-                ("up", Proj), ("gate_up", Proj), ("down", Proj)]
+                ("up", Proj), ("gate_up", Proj), ("down", Proj), ("w_router_packed", ctypes.c_void_p)]
 
 
 _lib = None
@@ -81,6 +81,8 @@ def load() -> ctypes.CDLL:
         lib.moe_packed_bytes.argtypes = [P(LayerDesc), i32, P(sz)]
         lib.moe_pack_weights.argtypes = [P(LayerDesc), i32, vp, vp, vp, vp, vp]
         lib.moe_stream_read.argtypes = [vp, sz, vp, i32, vp]
+        lib.moe_router_packed_bytes.argtypes = [P(LayerDesc), P(sz)]
+        lib.moe_pack_router.argtypes = [P(LayerDesc), vp, vp, vp]
         lib.moe_status_string.argtypes = [ctypes.c_int]
         lib.moe_status_string.restype = ctypes.c_char_p
         for name in EXPORTED:
@@ -184,6 +186,11 @@ def moe_forward_noalloc(desc, T, x, weights, y, out_dtype, topk_idx_out, topk_w_
                                       _ptr(topk_idx_out), _ptr(topk_w_out), _stream(stream)), "moe_forward_noalloc")
 
 
+def moe_pack_router(desc, w_router, out, stream=None):
+    """The prepared router of w_router into out (moe_router_packed_bytes bytes)."""
+    _check(load().moe_pack_router(ctypes.byref(desc), _ptr(w_router), _ptr(out), _stream(stream)), "moe_pack_router")
+
+
 def moe_stream_read(src, nbytes, out, blocks, stream=None):
     """The library's plain streaming read of nbytes of src (a measurement
     kernel outside the layer); out holds blocks * 256 uint32 words."""
@@ -244,8 +251,9 @@ def to_device(a: np.ndarray, device) -> torch.Tensor:
 class DeviceWeights:
     """Device copies of a layer's weights plus the C weight table pointing at them."""
 
-    def __init__(self, w_router: torch.Tensor, router_bias, experts: dict):
+    def __init__(self, w_router: torch.Tensor, router_bias, experts: dict, router_packed=None):
         self.w_router, self.router_bias, self.experts = w_router, router_bias, experts
+        self.router_packed = router_packed
 
         def proj(name):
             p = experts.get(name)
@@ -254,7 +262,7 @@ class DeviceWeights:
             return Proj(_ptr(p["w"]), _ptr(p.get("scales")), _ptr(p.get("biases")), _ptr(p.get("w_packed")))
 
         self.c = Weights(_ptr(w_router), _ptr(router_bias), proj("gate"), proj("up"), proj("gate_up"),
-                         proj("down"))
+                         proj("down"), _ptr(router_packed))
 
     @classmethod
     def from_layer(cls, layer: dict, device="cuda") -> "DeviceWeights":
@@ -264,7 +272,22 @@ class DeviceWeights:
 
     def with_packed(self, desc: LayerDesc, stream=None) -> "DeviceWeights":
         """The same weights plus the tile-packed copy of every affine projection
-        (moe_pack_weights), which the grouped kernels then read."""
+        (moe_pack_weights), which the grouped kernels then read, and the
+        prepared router (moe_pack_router) where the layer can use one."""
+        return self.with_packed_experts(desc, stream).with_packed_router(desc, stream)
+
+    def with_packed_router(self, desc: LayerDesc, stream=None) -> "DeviceWeights":
+        """The same weights plus the prepared router, or as they are when the
+        layer's router takes none."""
+        n = ctypes.c_size_t(0)
+        if load().moe_router_packed_bytes(ctypes.byref(desc), ctypes.byref(n)) != MOE_OK:
+            return self
+        packed = torch.empty((n.value,), dtype=torch.uint8, device=self.w_router.device)
+        moe_pack_router(desc, self.w_router, packed, stream)
+        return DeviceWeights(self.w_router, self.router_bias, self.experts, packed)
+
+    def with_packed_experts(self, desc: LayerDesc, stream=None) -> "DeviceWeights":
+        """The same weights plus the tile-packed copy of every affine projection."""
         experts = {}
         for name, p in self.experts.items():
             q = dict(p)
@@ -273,13 +296,14 @@ class DeviceWeights:
             q["w_packed"] = torch.empty((n,), dtype=torch.uint8, device=p["w"].device)
             moe_pack_weights(desc, _PROJ[name], p["w"], p["scales"], p["biases"], q["w_packed"], stream)
             experts[name] = q
-        return DeviceWeights(self.w_router, self.router_bias, experts)
+        return DeviceWeights(self.w_router, self.router_bias, experts, self.router_packed)
 
     def clone(self) -> "DeviceWeights":
         """A byte-identical copy at new device addresses."""
         experts = {n: {k: v.clone() for k, v in p.items()} for n, p in self.experts.items()}
         bias = None if self.router_bias is None else self.router_bias.clone()
-        return DeviceWeights(self.w_router.clone(), bias, experts)
+        rp = None if self.router_packed is None else self.router_packed.clone()
+        return DeviceWeights(self.w_router.clone(), bias, experts, rp)
 
     def nbytes(self, experts=None) -> int:
         """Bytes held for all weights, or for the listed expert ids only (a

@@ -243,3 +243,31 @@ def test_stream_read_validation(lib):
     assert lib.moe_stream_read(ctypes.c_void_p(72), 16, ctypes.c_void_p(64), 1, None) == bad
     assert lib.moe_stream_read(ctypes.c_void_p(64), 16, ctypes.c_void_p(64), 0, None) == bad
     assert lib.moe_stream_read(ctypes.c_void_p(64), 16, ctypes.c_void_p(64), 65537, None) == bad
+
+
+def test_router_packed_bytes_and_validation(lib):
+    size = ctypes.c_size_t()
+    d = moe.make_desc(2048, 512, 512, 10, wfmt="q4")
+    assert lib.moe_router_packed_bytes(ctypes.byref(d), ctypes.byref(size)) == moe.MOE_OK
+    wt = 512 * 2048 * 2                                    # [E][d] 16-bit, a multiple of 256 bytes here
+    assert size.value == wt + (2048 // 256 + 1) * 512 * 4  # norm partials [d/256][E] and their sums [E]
+    d6 = moe.make_desc(320, 128, 6, 2, act="f16")          # 6*320*2 = 3840 bytes (15 * 256), 2 partial rows
+    assert lib.moe_router_packed_bytes(ctypes.byref(d6), ctypes.byref(size)) == moe.MOE_OK
+    assert size.value == 3840 + 3 * 6 * 4
+    d32 = moe.make_desc(64, 128, 8, 2, act="f32")
+    assert lib.moe_router_packed_bytes(ctypes.byref(d32), ctypes.byref(size)) == moe.MOE_E_UNSUPPORTED
+    assert lib.moe_pack_router(ctypes.byref(d), None, A, None) == moe.MOE_E_INVALID
+    assert lib.moe_pack_router(ctypes.byref(d), A, A + 4, None) == moe.MOE_E_INVALID
+    # a prepared router where the layer's router takes none, or misaligned
+    w = moe.Weights(A, None, moe.Proj(A, None, None), moe.Proj(A, None, None), moe.Proj(None, None, None),
+                    moe.Proj(A, None, None), A)
+    need = ws_size(d32, 0)
+    assert lib.moe_forward(ctypes.byref(d32), 0, A, ctypes.byref(w), A, 0, None, None, A, need, None) == \
+        moe.MOE_E_INVALID
+    w = weights()
+    w.w_router_packed = A + 8
+    assert lib.moe_forward(ctypes.byref(d), 0, A, ctypes.byref(w), A, 1, None, None, A, ws_size(d, 0), None) == \
+        moe.MOE_E_INVALID
+    w.w_router_packed = A
+    assert lib.moe_forward(ctypes.byref(d), 0, A, ctypes.byref(w), A, 1, None, None, A, ws_size(d, 0), None) == \
+        moe.MOE_OK

@@ -172,3 +172,38 @@ def test_packed_layout(name):
         want_f = ok.reshape(M, -1).all(axis=1).astype(np.int32)
         assert np.array_equal(raw[o_fl:o_fl + M * 4].view(np.int32), want_f), proj
         assert want_f.any(), "the generated layers exercise the flagged path"
+
+
+# the matrix-core router at its smallest (T x E = 65536), with a router bias
+ROUTER_CASES = {
+    "mid-q4-t128-e512": LayerSpec("mid-q4-t128-e512", T=128, d_model=256, d_ff=128, n_experts=512, top_k=6,
+                                  wfmt="q4", router_bias="zipf", seed=87),
+}
+
+
+@pytest.mark.parametrize("name", ["q4-prefill-t2048", "f16-q4-prefill-t2048", "mid-q4-t128-e512"])
+def test_prepared_router_same_results(name):
+    """moe_forward with the prepared router (moe_pack_router) and without it:
+    the same routing, weights and output, bit for bit (the logit kernel reads
+    the same transposed rows and norms either way)."""
+    spec = ROUTER_CASES[name] if name in ROUTER_CASES else inputs.workload(name)
+    L = inputs.gen_layer(spec)
+    desc = moe.desc_from_spec(spec)
+    base = moe.DeviceWeights.from_layer(L, "cuda:0").with_packed_experts(desc)
+    prep = base.with_packed_router(desc)
+    assert prep.router_packed is not None
+    x = moe.to_device(L["x"], "cuda:0")
+    T = spec.T
+    ws = torch.empty(moe.moe_workspace_size(desc, T), dtype=torch.uint8, device="cuda:0")
+    outs = []
+    for w in (base, prep, base):
+        y = torch.empty((T, spec.d_model), dtype=torch.float32, device="cuda:0")
+        idx = torch.empty((T, spec.top_k), dtype=torch.int32, device="cuda:0")
+        wt = torch.empty((T, spec.top_k), dtype=torch.float32, device="cuda:0")
+        moe.moe_forward(desc, T, x, w, y, moe.MOE_DT_F32, idx, wt, ws)
+        torch.cuda.synchronize()
+        outs.append((y.cpu().numpy(), idx.cpu().numpy(), wt.cpu().numpy()))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), name
+    for a, b in zip(outs[0], outs[2]):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), name
