@@ -137,8 +137,9 @@ typedef struct {
   /* Optional (NULL: none): the prepared router that moe_pack_router wrote
    * from w_router.  When set, the matrix-core router (16-bit layers, T >= 64
    * with T * n_experts >= 65536) reads it instead of transposing w_router
-   * on every call; routing results are the same.  w_router is still
-   * required. */
+   * on every call; routing results are the same.  It is a copy: after
+   * w_router changes, write it again (a stale copy routes by the old
+   * weights).  w_router is still required. */
   const void *w_router_packed;
 } moe_weights;
 
@@ -206,6 +207,8 @@ int moe_pack_weights(const moe_layer_desc *desc, int32_t proj, const void *w, co
  * moe_pack_router: enqueue its writing from `w_router` (device) into `out`
  * (device, moe_router_packed_bytes bytes, 16-byte aligned) on `stream`; no
  * host wait, no allocation; MOE_E_INVALID for a null or misaligned pointer.
+ * The copy does not follow later changes to w_router: write it again after
+ * each change, before the next call that is given it.
  */
 int moe_router_packed_bytes(const moe_layer_desc *desc, size_t *bytes);
 int moe_pack_router(const moe_layer_desc *desc, const void *w_router, void *out, void *stream);
