@@ -12,6 +12,10 @@ C ABI.
   bit for bit the stored layout's dx; so does the forward of a layer whose
   matrices all fail the flag's test (every tile then takes the stored
   layout's expansion).
+- The prepared router (moe_pack_router) holds its documented layout (the
+  transposed router bit for bit, the squared-norm partials and sums within
+  fp32 summation error), and a forward given it routes and weighs exactly as
+  one without it.
 """
 import numpy as np
 import pytest
@@ -207,3 +211,34 @@ def test_prepared_router_same_results(name):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), name
     for a, b in zip(outs[0], outs[2]):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), name
+
+
+@pytest.mark.parametrize("spec", [
+    inputs.workload("q4-prefill-t2048").with_(T=1),
+    LayerSpec("rp-f16-e6", T=1, d_model=320, d_ff=64, n_experts=6, top_k=2, act="f16", seed=91),
+    LayerSpec("rp-bf16-e72", T=1, d_model=576, d_ff=64, n_experts=72, top_k=4, seed=92),
+], ids=lambda s: s.name)
+def test_prepared_router_layout(spec):
+    """The prepared router holds what its documented layout says: the router
+    transposed bit for bit, then (from a 256-byte multiple) the squared-norm
+    partials of each 256-row block and their sums, within fp32 summation
+    error of the fp64 values."""
+    desc = moe.desc_from_spec(spec)
+    w, _ = inputs.gen_router(spec)
+    D, E = spec.d_model, spec.n_experts
+    n = moe.ctypes.c_size_t(0)
+    assert moe.load().moe_router_packed_bytes(moe.ctypes.byref(desc), moe.ctypes.byref(n)) == moe.MOE_OK
+    nkb = (D + 255) // 256
+    off = (E * D * 2 + 255) // 256 * 256
+    assert n.value == off + (nkb + 1) * E * 4
+    out = torch.full((n.value,), 0x5A, dtype=torch.uint8, device="cuda:0")
+    moe.moe_pack_router(desc, moe.to_device(w, "cuda:0"), out)
+    torch.cuda.synchronize()
+    raw = out.cpu().numpy()
+    assert np.array_equal(raw[:E * D * 2].view(np.uint16).reshape(E, D), w.T)
+    wf = inputs.half_bits_to_f32(w, spec.act).astype(np.float64)
+    sq = wf * wf
+    want_p = np.stack([sq[256 * kb:256 * (kb + 1)].sum(axis=0) for kb in range(nkb)])
+    got = raw[off:off + (nkb + 1) * E * 4].view(np.float32).reshape(nkb + 1, E).astype(np.float64)
+    assert np.allclose(got[:nkb], want_p, rtol=1e-5, atol=0), spec.name
+    assert np.allclose(got[nkb], sq.sum(axis=0), rtol=1e-5, atol=0), spec.name
